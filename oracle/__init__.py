@@ -1,0 +1,189 @@
+"""fp64 CPU oracle for circulant softmax attention -- TEST INFRASTRUCTURE.
+
+Only the test suite, `__graft_entry__.smoke()` and the CPU-baseline leg of
+`bench.py` may import this package.  The GPU library neither imports nor
+links it, and this package imports nothing from the GPU library: the only
+module both sides share is the seeded input generator, which holds none of
+the method's arithmetic.
+
+The heavy loops live in `cat_oracle.c` (plain direct sums in double
+precision, no FFT); this module marshals numpy arrays into it and composes
+the steps in the order the pages give:
+
+  CAT (CAT: Circular-Convolutional Attention for Sub-Quadratic Transformers,
+  "Method details / Overall framework" and "Key designs"):
+      Z = X W_A  ->  Z* = softmax over the N tokens, per head
+      V = X W_V  ->  O_h = circ(Z*_h) V_h,  C[i][j] = Z*[(i - j) mod N]
+
+  2D circulant attention (Vision Transformers are Circulant Attention
+  Learners, "Circulant Attention: attention rebuilt with the FFT"):
+      Q, K, V = X W_Q, X W_K, X W_V
+      a_h = circular cross-correlation of Q_h and K_h on the token grid,
+            summed over the head's channels, times 1/sqrt(d)
+      O_h = BCCB(softmax(a_h)) V_h  (2D circular convolution)
+
+Every function here is pinned by `tests/test_oracle.py` to something other
+than itself (library routines on a different route, closed forms,
+invariants, hand-computed fixtures in `tests/golden/`).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+
+from . import build as _build
+
+_lib = None
+_P = ctypes.POINTER(ctypes.c_double)
+_I64P = ctypes.POINTER(ctypes.c_int64)
+_i64 = ctypes.c_int64
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if _build.needs_build():
+            _build.build()
+        lib = ctypes.CDLL(_build.LIB)
+        lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_matmul.argtypes = [_P, _P, _P, _i64, _i64, _i64]
+        lib.oracle_scores_1d.argtypes = [_P, _P, _P, _i64, _i64, _i64, _i64]
+        lib.oracle_softmax_rows.argtypes = [_P, _P, _i64, _i64]
+        lib.oracle_circulant_1d.argtypes = [_P, _P, _P, _i64, _i64, _i64, _i64, _I64P, _i64]
+        lib.oracle_scores_bccb_2d.argtypes = [_P, _P, _P, _i64, _i64, _i64, _i64, _i64,
+                                              ctypes.c_double]
+        lib.oracle_bccb_2d.argtypes = [_P, _P, _P, _i64, _i64, _i64, _i64, _i64, _I64P, _i64]
+        for f in ("oracle_matmul", "oracle_scores_1d", "oracle_softmax_rows",
+                  "oracle_circulant_1d", "oracle_scores_bccb_2d", "oracle_bccb_2d"):
+            getattr(lib, f).restype = None
+        _lib = lib
+    return _lib
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(_P)
+
+
+def _rows(rows: Optional[Sequence[int]]):
+    if rows is None:
+        return None, None, 0
+    r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    return r, r.ctypes.data_as(_I64P), int(r.size)
+
+
+def num_threads() -> int:
+    """Threads the oracle's OpenMP loops use (OMP_NUM_THREADS or all cores)."""
+    return int(_load().oracle_num_threads())
+
+
+# ---------------------------------------------------------------- primitives
+def matmul(X, W) -> np.ndarray:
+    """[..., K] x [K, Nc] -> [..., Nc] in fp64 (X W, as the pages write it)."""
+    X = _f64(X)
+    W = _f64(W)
+    K, Nc = W.shape
+    assert X.shape[-1] == K
+    M = X.size // K
+    Y = np.empty(X.shape[:-1] + (Nc,), dtype=np.float64)
+    _load().oracle_matmul(_ptr(X), _ptr(W), _ptr(Y), M, K, Nc)
+    return Y
+
+
+def scores_1d(X, W_A) -> np.ndarray:
+    """z[b, h, n] = sum_k X[b, n, k] W_A[k, h]  ->  [B, H, N]."""
+    X = _f64(X)
+    W_A = _f64(W_A)
+    B, N, D = X.shape
+    H = W_A.shape[1]
+    assert W_A.shape[0] == D
+    z = np.empty((B, H, N), dtype=np.float64)
+    _load().oracle_scores_1d(_ptr(X), _ptr(W_A), _ptr(z), B, N, D, H)
+    return z
+
+
+def softmax(z) -> np.ndarray:
+    """Softmax over the last axis (max-subtracted)."""
+    z = _f64(z)
+    L = z.shape[-1]
+    out = np.empty_like(z)
+    _load().oracle_softmax_rows(_ptr(z), _ptr(out), z.size // max(L, 1), L)
+    return out
+
+
+def circulant_1d(w, V, rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """O[b, i, c] = sum_j w[b, h(c), (i - j) mod N] V[b, j, c].
+
+    w: [B, H, N]; V: [B, N, D].  Returns [B, N, D], or [len(rows), D] when
+    `rows` (flattened b * N + i) is given.
+    """
+    w = _f64(w)
+    V = _f64(V)
+    B, H, N = w.shape
+    assert V.shape[:2] == (B, N) and V.shape[2] % H == 0
+    D = V.shape[2]
+    r, rp, nr = _rows(rows)
+    O = np.empty(((nr,) if r is not None else (B, N)) + (D,), dtype=np.float64)
+    _load().oracle_circulant_1d(_ptr(w), _ptr(V), _ptr(O), B, N, D, H, rp, nr)
+    return O
+
+
+def scores_bccb_2d(Q, K, Hg: int, Wg: int, H: int, scale: Optional[float] = None) -> np.ndarray:
+    """a[b, h, s1, s2]: circular cross-correlation of Q_h and K_h on the grid,
+    summed over the head's d channels, times `scale` (default 1/sqrt(d))."""
+    Q = _f64(Q)
+    K = _f64(K)
+    B, N, D = Q.shape
+    assert K.shape == Q.shape and N == Hg * Wg and D % H == 0
+    if scale is None:
+        scale = 1.0 / math.sqrt(D // H)
+    a = np.empty((B, H, Hg, Wg), dtype=np.float64)
+    _load().oracle_scores_bccb_2d(_ptr(Q), _ptr(K), _ptr(a), B, Hg, Wg, D, H, float(scale))
+    return a
+
+
+def bccb_2d(w, V, rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """O[b, (i1,i2), c] = sum_j w[b, h(c), (i1-j1) mod Hg, (i2-j2) mod Wg] V[b, j, c].
+
+    w: [B, H, Hg, Wg]; V: [B, Hg*Wg, D]."""
+    w = _f64(w)
+    V = _f64(V)
+    B, H, Hg, Wg = w.shape
+    N = Hg * Wg
+    assert V.shape[:2] == (B, N) and V.shape[2] % H == 0
+    D = V.shape[2]
+    r, rp, nr = _rows(rows)
+    O = np.empty(((nr,) if r is not None else (B, N)) + (D,), dtype=np.float64)
+    _load().oracle_bccb_2d(_ptr(w), _ptr(V), _ptr(O), B, Hg, Wg, D, H, rp, nr)
+    return O
+
+
+# ---------------------------------------------------------------- composites
+def cat_forward_1d(X, W_A, W_V, rows: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
+    """CAT forward: returns z (logits [B,H,N]), zstar (softmax), V (= X W_V) and O."""
+    z = scores_1d(X, W_A)
+    zstar = softmax(z)
+    V = matmul(X, W_V)
+    O = circulant_1d(zstar, V, rows=rows)
+    return {"z": z, "zstar": zstar, "V": V, "O": O}
+
+
+def cat_forward_bccb_2d(X, W_Q, W_K, W_V, Hg: int, Wg: int, H: int,
+                        rows: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
+    """2D circulant attention forward: returns Q, K, V, a (scaled logits
+    [B,H,Hg,Wg]), astar (softmax over all Hg*Wg positions) and O."""
+    Q = matmul(X, W_Q)
+    K = matmul(X, W_K)
+    V = matmul(X, W_V)
+    a = scores_bccb_2d(Q, K, Hg, Wg, H)
+    B = a.shape[0]
+    astar = softmax(a.reshape(B, H, Hg * Wg)).reshape(a.shape)
+    O = bccb_2d(astar, V, rows=rows)
+    return {"Q": Q, "K": K, "V": V, "a": a, "astar": astar, "O": O}

@@ -1,0 +1,297 @@
+#!/usr/bin/env python3
+"""Throughput of the circulant softmax attention forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one whole forward pass (projection MFMA GEMM, softmax + filter
+spectrum, fused FFT-convolution; in 2D also the score correlation) over one
+batch of seeded synthetic input already resident in device memory.  The
+default workload is CAT 1D at N=1024, D=768 (B=16, H=12, bf16 storage, fp32
+compute).  Input/output/workspace buffers are rotated over enough sets to
+exceed the 256 MB Infinity Cache, so every step reads its inputs from HBM.
+
+Rank 0 prints one JSON line on stdout; progress goes to stderr.  The line
+carries the headline metric, a roofline entry for the slowest kernel (its
+algorithmic bytes or flops per launch over its average launch time, measured
+with HIP events recorded by the library around each kernel in an
+instrumented pass of the same K steps) and the fp64 CPU oracle timed on a
+bounded sample of the same workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+PEAK_TFLOPS = {"mfma_bf16": 2500.0, "mfma_f32": 157.3, "valu_f32": 78.6}
+MALL_BYTES = 256 << 20
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def fft_flops(L: int) -> float:
+    """Conventional flop count of one complex transform of L points."""
+    return 5.0 * L * math.log2(L) if L > 1 else 0.0
+
+
+def kernel_model(wl, L: int, ngrp: int):
+    """Algorithmic bytes and flops of each kernel of one forward call."""
+    s = 4 if wl.dtype == "f32" else 2
+    B, N, D, H, d = wl.B, wl.N, wl.D, wl.H, wl.d
+    T = B * N
+    BH = B * H
+    lines = BH * (d // 2)
+    spec_bytes = BH * L * 8
+    m = {}
+    if wl.kind == "1d":
+        m["project"] = dict(bytes=T * D * s + D * (D + H) * s + T * D * s + BH * N * 4,
+                            flops=2.0 * T * D * (D + H), unit="mfma_bf16" if s == 2 else "mfma_f32")
+        m["spectrum"] = dict(bytes=BH * N * 4 + spec_bytes, flops=BH * (fft_flops(L) + 4.0 * N), unit="valu_f32")
+    else:
+        m["project"] = dict(bytes=T * D * s + 3 * D * D * s + 2 * T * D * 4 + T * D * s,
+                            flops=2.0 * T * D * 3 * D, unit="mfma_bf16" if s == 2 else "mfma_f32")
+        m["scores"] = dict(bytes=2 * T * D * 4 + BH * ngrp * L * 8,
+                           flops=lines * (2 * fft_flops(L) + 8.0 * L), unit="valu_f32")
+        m["spectrum"] = dict(bytes=BH * ngrp * L * 8 + spec_bytes,
+                             flops=BH * (2 * fft_flops(L) + 4.0 * N), unit="valu_f32")
+    m["fftconv"] = dict(bytes=2 * T * D * s + spec_bytes, flops=lines * (2 * fft_flops(L) + 6.0 * L), unit="valu_f32")
+    return m
+
+
+def source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = {
+    "fftconv": ["circulant_softmax_attention_amd/csrc/cat_fftconv.hpp", "circulant_softmax_attention_amd/csrc/cat_fft.hpp",
+                "circulant_softmax_attention_amd/csrc/cat_common.hpp"],
+    "project": ["circulant_softmax_attention_amd/csrc/cat_gemm.hip"],
+}
+KERNEL_SOURCES["spectrum"] = KERNEL_SOURCES["fftconv"]
+KERNEL_SOURCES["scores"] = KERNEL_SOURCES["fftconv"]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from a committed counter summary, if it was taken
+    on the current sources of that kernel; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        if rec.get("source_hash") != source_hash(KERNEL_SOURCES[kernel]):
+            return None
+        return rec.get("hbm_bytes_per_launch")
+    except Exception:
+        return None
+
+
+def cpu_baseline(wl, inp, target_s: float):
+    """The fp64 oracle, as it stands, on a bounded sample of the workload."""
+    import numpy as np
+
+    import oracle
+    threads = oracle.num_threads()
+    if wl.kind == "1d":
+        t0 = time.perf_counter()
+        oracle.cat_forward_1d(inp.X[:1], inp.W_A, inp.W_V)
+        t1 = time.perf_counter() - t0
+        n = int(max(1, min(wl.B - 1, round((target_s - t1) / max(t1, 1e-9)))))
+        t0 = time.perf_counter()
+        oracle.cat_forward_1d(inp.X[1:1 + n], inp.W_A, inp.W_V)
+        tn = time.perf_counter() - t0
+        imgs, secs = 1 + n, t1 + tn
+        return dict(value=imgs * wl.N / secs, unit="tokens/s", cores=threads, kind="oracle",
+                    sample=f"{imgs} of {wl.B} sequences ({imgs * wl.N} tokens), fp64 direct O(N^2 d) sums, "
+                           f"{secs:.1f} s")
+    # 2D: one (image, head) slice end to end; a whole image is H such slices
+    d = wl.d
+    t0 = time.perf_counter()
+    hs = slice(0, d)
+    oracle.cat_forward_bccb_2d(inp.X[:1], inp.W_Q[:, hs], inp.W_K[:, hs], inp.W_V[:, hs], wl.Hg, wl.Wg, 1)
+    secs = time.perf_counter() - t0
+    per_image = secs * wl.H
+    return dict(value=wl.N / per_image, unit="tokens/s", cores=threads, kind="oracle",
+                sample=f"one head of one image (1/{wl.H} of an image, {wl.N} tokens) in {secs:.1f} s, "
+                       f"scaled by {wl.H} heads per image; fp64 direct O(N^2 d) sums")
+
+
+def run(args):
+    import numpy as np
+    import torch
+
+    from circulant_softmax_attention_amd import workloads as W
+    lib_path = os.path.join(ROOT, "circulant_softmax_attention_amd", "libcat.so")
+    if not os.path.exists(lib_path):
+        from circulant_softmax_attention_amd import build
+        build.build(verbose=False)
+    from circulant_softmax_attention_amd import cat
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a ROCm GPU")
+    wl = W.WORKLOADS[args.workload]
+    log("workload", wl.name, wl.note)
+    inp = W.make_inputs(wl)
+    dt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dt).cuda()
+
+    if wl.kind == "1d":
+        plan = cat.cat_plan_create("1d", wl.dtype, wl.B, wl.N, wl.D, wl.H)
+        weights = [dev(inp.W_A), dev(inp.W_V)]
+    else:
+        plan = cat.cat_plan_create("2d", wl.dtype, wl.B, wl.N, wl.D, wl.H, wl.Hg, wl.Wg)
+        weights = [dev(inp.W_Q), dev(inp.W_K), dev(inp.W_V)]
+    L, L1, L2 = plan.geometry()
+    ws_bytes = plan.workspace_size()
+    x0 = dev(inp.X)
+    esz = 4 if wl.dtype == "f32" else 2
+    set_bytes = 2 * x0.numel() * esz + ws_bytes
+    nsets = max(1, math.ceil(args.rotate_bytes / set_bytes))
+    X = [x0] + [x0.clone() for _ in range(nsets - 1)]
+    O = [torch.empty_like(x0) for _ in range(nsets)]
+    WS = [cat.alloc_workspace(plan) for _ in range(nsets)]
+    log(f"transform {L} = {L1} x {L2}; {nsets} buffer sets of {set_bytes / 2**20:.1f} MiB")
+
+    fwd = cat.cat_forward_1d if wl.kind == "1d" else cat.cat_forward_bccb_2d
+
+    def step(i):
+        k = i % nsets
+        fwd(plan, X[k], *weights, O=O[k], workspace=WS[k])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: K steps between synchronisations
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for i in range(args.steps):
+        step(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1000.0 / args.steps
+    gpu_ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    log(f"{args.steps} steps: {ms_per_step * 1000:.1f} us/step wall, {gpu_ms_per_step * 1000:.1f} us/step events")
+
+    # instrumented pass: the library records events around each kernel
+    cat.cat_plan_set_timing(plan, True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    inst_ms = (time.perf_counter() - t0) * 1000.0 / args.steps
+    ktimes = cat.cat_plan_kernel_times(plan)
+    cat.cat_plan_set_timing(plan, False)
+    for k, (ms, n) in ktimes.items():
+        log(f"  kernel {k:9s} {ms * 1000:9.2f} us avg over {n} launches")
+
+    ngrp = (wl.d // 2 + 3) // 4
+    model = kernel_model(wl, L, ngrp)
+    kernels = {}
+    for k, (ms, n) in ktimes.items():
+        mm = model[k]
+        sec = ms / 1000.0
+        gbs = mm["bytes"] / sec / 1e9
+        tfl = mm["flops"] / sec / 1e12
+        kernels[k] = dict(us=round(ms * 1000, 3), bytes=int(mm["bytes"]), flops=float(mm["flops"]),
+                          hbm_frac=round(gbs / HBM_PEAK_GBS, 4),
+                          compute_frac=round(tfl / PEAK_TFLOPS[mm["unit"]], 4), compute_unit=mm["unit"])
+    dom = max(ktimes, key=lambda k: ktimes[k][0])
+    kd = kernels[dom]
+    sec = ktimes[dom][0] / 1000.0
+    if kd["compute_unit"].startswith("mfma"):
+        bound = "mfma"
+    else:
+        bound = "hbm" if kd["hbm_frac"] >= kd["compute_frac"] else "alu"
+    if bound == "hbm":
+        achieved, peak, unit = kd["bytes"] / sec / 1e9, HBM_PEAK_GBS, "GB/s"
+    else:
+        achieved, peak, unit = kd["flops"] / sec / 1e12, PEAK_TFLOPS[kd["compute_unit"]], "TFLOP/s"
+    roofline = dict(kernel=dom, bound=bound, achieved=round(achieved, 2), peak=peak, unit=unit,
+                    frac=round(achieved / peak, 4), traffic=measured_traffic(dom, wl.name),
+                    hbm_frac=kd["hbm_frac"], compute_frac=kd["compute_frac"], us=kd["us"])
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        cpu = cpu_baseline(wl, inp, args.cpu_seconds)
+        log("cpu baseline:", cpu)
+
+    tokens = wl.B * wl.N
+    value = tokens / (ms_per_step / 1000.0)
+    line = {
+        "metric": "circulant-attention tokens/s at N=1024,D=768; % of HBM roofline (1 GPU)"
+        if wl.name == W.HEADLINE else f"circulant-attention tokens/s ({wl.name})",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if wl.dtype == "f32" else "bf16-storage/f32-compute",
+        "data": "synthetic (seeded PCG64: X~N(0,1), W~N(0,1/D))",
+        "config": {"workload": wl.name, "kind": wl.kind, "B": wl.B, "N": wl.N, "D": wl.D, "H": wl.H,
+                   "grid": [wl.Hg, wl.Wg] if wl.kind == "2d" else None, "storage": wl.dtype,
+                   "transform": [L, L1, L2], "global_batch": wl.B, "seq_len": wl.N, "parallelism": "none"},
+        "e2e_hbm_frac": round(((2 * tokens * wl.D * esz) + sum(w.numel() * esz for w in weights))
+                              / (ms_per_step / 1000.0) / 1e9 / HBM_PEAK_GBS, 4),
+        "gpu_event_ms_per_step": round(gpu_ms_per_step, 5),
+        "instrumented_ms_per_step": round(inst_ms, 5),
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    return line
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None, help="workload name (default: the N=1024, D=768 one)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rotate-bytes", type=float, default=2.5 * MALL_BYTES,
+                    help="total bytes of rotated buffer sets (defeats the Infinity Cache)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path has no multi-GPU mode. "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if args.steps > 512:
+        print("--steps is limited to 512 (per-kernel timing slots)", file=sys.stderr)
+        sys.exit(2)
+    from circulant_softmax_attention_amd import workloads as W
+    if args.workload is None:
+        args.workload = W.HEADLINE
+    line = run(args)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,601 @@
+// cat_api.cpp -- the C ABI (include/cat.h): validation, plans, workspace
+// layout and the launch sequences of the forward paths.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/cat.h"
+#include "cat_internal.hpp"
+
+using namespace cat;
+
+struct cat_plan_s {
+  cat_problem p;
+  int d;
+  int et;            // ElemType of the storage dtype
+  size_t esz;        // storage bytes per element
+  LineGeom geom;
+  int L;
+  int G;             // complex lines per transform workgroup
+  int ng;            // line groups per head (d / 2 / G)
+  int Gs;            // lines per spectrum workgroup
+  int npair, ngrp, ppg;  // 2D score partials
+  float2* d_tw;      // 1D inter-pass twiddles, L entries (null in 2D)
+  size_t off_V, off_z, off_Q, off_K, off_part, off_spec, ws_bytes;
+  bool debug_sync;
+  // per-kernel timing slots: ev[slot][kernel][start/stop]
+  static constexpr int kSlots = 512, kMaxK = 4;
+  bool timing = false;
+  hipEvent_t* ev = nullptr;
+  int64_t calls = 0;
+  int nk = 0;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+cat_status fail(cat_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+cat_status hip_fail(hipError_t e, const char* what) {
+  g_err = std::string(what) + ": " + hipGetErrorString(e);
+  return CAT_ERR_HIP;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t up256(size_t v) { return (v + 255) & ~size_t(255); }
+
+bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+// Split a power-of-two length into L1 x L2 with L2 | L1, as balanced as possible.
+void split_pow2(int L, int* L1, int* L2) {
+  int e = 0;
+  while ((1 << e) < L) ++e;
+  *L2 = 1 << (e / 2);
+  *L1 = L / *L2;
+}
+
+cat_status check_sync(const cat_plan_s* pl, const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, what);
+  if (pl->debug_sync) {
+    e = hipDeviceSynchronize();
+    if (e != hipSuccess) return hip_fail(e, what);
+  }
+  return CAT_OK;
+}
+
+char* ws_at(void* ws, size_t off) { return reinterpret_cast<char*>(ws) + off; }
+
+void free_events(cat_plan_s* pl) {
+  if (!pl->ev) return;
+  for (int i = 0; i < cat_plan_s::kSlots * cat_plan_s::kMaxK * 2; ++i)
+    if (pl->ev[i]) (void)hipEventDestroy(pl->ev[i]);
+  delete[] pl->ev;
+  pl->ev = nullptr;
+}
+
+// Records around kernel `k` of the current call when timing is on.
+struct KernelMark {
+  cat_plan_s* pl;
+  hipStream_t s;
+  hipEvent_t* slot;
+  KernelMark(cat_plan_s* p, hipStream_t st) : pl(p), s(st), slot(nullptr) {
+    if (pl->timing) {
+      slot = pl->ev + (size_t)(pl->calls % cat_plan_s::kSlots) * cat_plan_s::kMaxK * 2;
+      ++pl->calls;
+    }
+  }
+  void begin(int k) {
+    if (slot) (void)hipEventRecord(slot[2 * k], s);
+  }
+  void end(int k) {
+    if (slot) (void)hipEventRecord(slot[2 * k + 1], s);
+  }
+};
+
+}  // namespace
+
+extern "C" {
+
+const char* cat_status_string(cat_status s) {
+  switch (s) {
+    case CAT_OK: return "CAT_OK";
+    case CAT_ERR_INVALID_ARG: return "CAT_ERR_INVALID_ARG";
+    case CAT_ERR_UNSUPPORTED: return "CAT_ERR_UNSUPPORTED";
+    case CAT_ERR_HIP: return "CAT_ERR_HIP";
+    case CAT_ERR_ALLOC: return "CAT_ERR_ALLOC";
+    case CAT_ERR_PLAN_MISMATCH: return "CAT_ERR_PLAN_MISMATCH";
+  }
+  return "CAT_ERR_UNKNOWN";
+}
+
+const char* cat_last_error(void) { return g_err.c_str(); }
+
+cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
+  if (out == nullptr) return fail(CAT_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (p == nullptr) return fail(CAT_ERR_INVALID_ARG, "problem is NULL");
+  if (p->kind != CAT_1D && p->kind != CAT_BCCB_2D) return fail(CAT_ERR_INVALID_ARG, "unknown kind");
+  if (p->dtype != CAT_F32 && p->dtype != CAT_BF16) return fail(CAT_ERR_INVALID_ARG, "unknown dtype");
+  if (p->B < 0 || p->N < 1 || p->D < 1 || p->H < 1)
+    return fail(CAT_ERR_INVALID_ARG, "B must be >= 0 and N, D, H >= 1");
+  if (p->D % p->H != 0) return fail(CAT_ERR_INVALID_ARG, "D must be a multiple of H");
+  const int64_t d = p->D / p->H;
+  if (d % 2 != 0) return fail(CAT_ERR_INVALID_ARG, "head width d = D/H must be even");
+  if (p->D % 8 != 0) return fail(CAT_ERR_INVALID_ARG, "D must be a multiple of 8");
+  if (p->B * p->N * p->D >= (int64_t(1) << 31) || p->B * p->H > (int64_t(1) << 24))
+    return fail(CAT_ERR_UNSUPPORTED, "problem too large (B*N*D must be < 2^31)");
+
+  LineGeom g{};
+  if (p->kind == CAT_1D) {
+    int L = 0;
+    if (is_pow2(p->N) && p->N <= 4096) {
+      L = (int)p->N;
+    } else if (2 * p->N - 1 <= 4096) {
+      L = 1;
+      while (L < 2 * p->N - 1) L <<= 1;
+    } else {
+      return fail(CAT_ERR_UNSUPPORTED, "1D N beyond the single-workgroup transform (pow2 <= 4096, other <= 2048)");
+    }
+    split_pow2(L, &g.L1, &g.L2);
+    g.twiddled = 1;
+  } else {
+    if (p->Hg < 1 || p->Wg < 1 || p->Hg * p->Wg != p->N)
+      return fail(CAT_ERR_INVALID_ARG, "2D needs Hg, Wg >= 1 and Hg*Wg == N");
+    g.L1 = (int)p->Hg;
+    g.L2 = (int)p->Wg;
+    g.twiddled = 0;
+  }
+  if (!geom_supported(g)) return fail(CAT_ERR_UNSUPPORTED, "transform length / grid not instantiated");
+
+  cat_plan_s* pl = new (std::nothrow) cat_plan_s();
+  if (!pl) return fail(CAT_ERR_ALLOC, "host allocation failed");
+  pl->p = *p;
+  pl->d = (int)d;
+  pl->et = p->dtype == CAT_F32 ? ET_F32 : ET_BF16;
+  pl->esz = p->dtype == CAT_F32 ? 4 : 2;
+  pl->geom = g;
+  pl->L = g.L1 * g.L2;
+  const int T = line_threads(g);
+  const size_t line_bytes = line_lds_bytes(g);
+  const int d2 = (int)d / 2;
+  // lines per transform workgroup: power of two dividing d/2, <= 256 threads
+  int G = 1;
+  const size_t lds_cap = p->kind == CAT_1D ? 96 * 1024 : 152 * 1024;
+  while (G < 8 && d2 % (2 * G) == 0 && (2 * G) * T <= 256 && (2 * G) * line_bytes <= lds_cap) G *= 2;
+  pl->G = G;
+  pl->ng = d2 / G;
+  int Gs = 1;
+  while ((2 * Gs) * T <= 128 && (2 * Gs) * (line_bytes + T * sizeof(float)) <= 96 * 1024) Gs *= 2;
+  pl->Gs = Gs;
+  pl->npair = d2;
+  pl->ppg = 4;
+  pl->ngrp = (d2 + pl->ppg - 1) / pl->ppg;
+  const char* ds = std::getenv("CAT_DEBUG_SYNC");
+  pl->debug_sync = ds && ds[0] == '1';
+
+  const size_t BND = (size_t)p->B * p->N * p->D;
+  const size_t BH = (size_t)p->B * p->H;
+  size_t off = 0;
+  pl->off_V = off;
+  off = up256(off + BND * pl->esz);
+  pl->off_spec = off;
+  off = up256(off + BH * pl->L * sizeof(float2));
+  if (p->kind == CAT_1D) {
+    pl->off_z = off;
+    off = up256(off + BH * p->N * sizeof(float));
+    pl->off_Q = pl->off_K = pl->off_part = 0;
+  } else {
+    pl->off_z = 0;
+    pl->off_Q = off;
+    off = up256(off + BND * sizeof(float));
+    pl->off_K = off;
+    off = up256(off + BND * sizeof(float));
+    pl->off_part = off;
+    off = up256(off + BH * pl->ngrp * pl->L * sizeof(float2));
+  }
+  pl->ws_bytes = off;
+
+  // device tables and kernel attributes (first HIP calls)
+  pl->d_tw = nullptr;
+  if (g.twiddled) {
+    std::vector<float2> tw((size_t)pl->L);
+    const double two_pi = 6.283185307179586476925286766559;
+    for (int n2 = 0; n2 < g.L2; ++n2)
+      for (int k1 = 0; k1 < g.L1; ++k1) {
+        const long e = ((long)n2 * k1) % pl->L;
+        const double ang = two_pi * (double)e / (double)pl->L;
+        tw[(size_t)n2 * g.L1 + k1] = make_float2((float)std::cos(ang), (float)(-std::sin(ang)));
+      }
+    hipError_t e = hipMalloc(&pl->d_tw, tw.size() * sizeof(float2));
+    if (e != hipSuccess) {
+      delete pl;
+      return hip_fail(e, "hipMalloc(twiddles)");
+    }
+    e = hipMemcpy(pl->d_tw, tw.data(), tw.size() * sizeof(float2), hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+      (void)hipFree(pl->d_tw);
+      delete pl;
+      return hip_fail(e, "hipMemcpy(twiddles)");
+    }
+  }
+  hipError_t e = prepare_kernels(g, (size_t)G * line_bytes, (size_t)Gs * (line_bytes + T * sizeof(float)),
+                                 2 * line_bytes);
+  if (e != hipSuccess) {
+    if (pl->d_tw) (void)hipFree(pl->d_tw);
+    delete pl;
+    return hip_fail(e, "hipFuncSetAttribute");
+  }
+  *out = pl;
+  g_err.clear();
+  return CAT_OK;
+}
+
+cat_status cat_plan_destroy(cat_plan plan) {
+  if (plan == nullptr) return CAT_OK;
+  if (plan->d_tw) (void)hipFree(plan->d_tw);
+  free_events(plan);
+  delete plan;
+  return CAT_OK;
+}
+
+cat_status cat_plan_set_timing(cat_plan plan, int enable) {
+  if (!plan) return fail(CAT_ERR_INVALID_ARG, "NULL plan");
+  plan->timing = false;
+  plan->calls = 0;
+  if (!enable) return CAT_OK;
+  if (!plan->ev) {
+    const int n = cat_plan_s::kSlots * cat_plan_s::kMaxK * 2;
+    plan->ev = new (std::nothrow) hipEvent_t[n]();
+    if (!plan->ev) return fail(CAT_ERR_ALLOC, "event table allocation failed");
+    for (int i = 0; i < n; ++i) {
+      hipError_t e = hipEventCreate(&plan->ev[i]);
+      if (e != hipSuccess) {
+        free_events(plan);
+        return hip_fail(e, "hipEventCreate");
+      }
+    }
+  }
+  plan->timing = true;
+  return CAT_OK;
+}
+
+cat_status cat_plan_kernel_times(cat_plan plan, double* total_ms, int64_t* calls, int* nkernels) {
+  if (!plan || !total_ms || !calls || !nkernels) return fail(CAT_ERR_INVALID_ARG, "NULL argument");
+  const int nk = plan->p.kind == CAT_1D ? 3 : 4;
+  *nkernels = nk;
+  for (int k = 0; k < 8; ++k) {
+    total_ms[k] = 0.0;
+    calls[k] = 0;
+  }
+  if (!plan->ev || plan->calls == 0) return CAT_OK;
+  const int64_t n = plan->calls < cat_plan_s::kSlots ? plan->calls : cat_plan_s::kSlots;
+  for (int64_t c = 0; c < n; ++c) {
+    hipEvent_t* slot = plan->ev + (size_t)c * cat_plan_s::kMaxK * 2;
+    for (int k = 0; k < nk; ++k) {
+      hipError_t e = hipEventSynchronize(slot[2 * k + 1]);
+      if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+      float ms = 0.f;
+      e = hipEventElapsedTime(&ms, slot[2 * k], slot[2 * k + 1]);
+      if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+      total_ms[k] += ms;
+      calls[k] += 1;
+    }
+  }
+  return CAT_OK;
+}
+
+cat_status cat_plan_workspace_size(cat_plan plan, size_t* bytes) {
+  if (!plan || !bytes) return fail(CAT_ERR_INVALID_ARG, "NULL argument");
+  *bytes = plan->ws_bytes;
+  return CAT_OK;
+}
+
+cat_status cat_plan_geometry(cat_plan plan, int64_t* L, int64_t* L1, int64_t* L2) {
+  if (!plan) return fail(CAT_ERR_INVALID_ARG, "NULL plan");
+  if (L) *L = plan->L;
+  if (L1) *L1 = plan->geom.L1;
+  if (L2) *L2 = plan->geom.L2;
+  return CAT_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+cat_status check_ptrs(std::initializer_list<const void*> ps) {
+  for (const void* q : ps) {
+    if (q == nullptr) return fail(CAT_ERR_INVALID_ARG, "NULL buffer");
+    if (!aligned16(q)) return fail(CAT_ERR_INVALID_ARG, "buffer not 16-byte aligned");
+  }
+  return CAT_OK;
+}
+
+GemmArgs gemm_base(const cat_plan_s* pl, const void* X) {
+  GemmArgs a{};
+  a.X = X;
+  a.M = (int)(pl->p.B * pl->p.N);
+  a.K = (int)pl->p.D;
+  a.Ntok = (int)pl->p.N;
+  a.H = (int)pl->p.H;
+  a.d = pl->d;
+  return a;
+}
+
+GemmSeg seg(const void* W, void* out, int ncols, int out_f32, int layout, int cg) {
+  GemmSeg s{};
+  s.W = W;
+  s.out = out;
+  s.ncols = ncols;
+  s.out_f32 = out_f32;
+  s.layout = layout;
+  s.cg = cg;
+  return s;
+}
+
+SpecArgs spec_base(const cat_plan_s* pl, void* ws) {
+  SpecArgs a{};
+  a.spec = reinterpret_cast<float2*>(ws_at(ws, pl->off_spec));
+  a.tw = pl->d_tw;
+  a.BH = (int)(pl->p.B * pl->p.H);
+  a.N = (int)pl->p.N;
+  a.scale = 1.0f;
+  a.G = pl->Gs;
+  return a;
+}
+
+ConvArgs conv_base(const cat_plan_s* pl, const void* Vblk, const float2* spec, void* O) {
+  ConvArgs a{};
+  a.V = Vblk;
+  a.spec = spec;
+  a.tw = pl->d_tw;
+  a.O = O;
+  a.B = (int)pl->p.B;
+  a.H = (int)pl->p.H;
+  a.D = (int)pl->p.D;
+  a.N = (int)pl->p.N;
+  a.d = pl->d;
+  a.G = pl->G;
+  a.ng = pl->ng;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+cat_status cat_forward_1d(cat_plan plan, const void* X, const void* W_A, const void* W_V, void* O,
+                          void* workspace, void* stream) {
+  if (!plan) return fail(CAT_ERR_INVALID_ARG, "NULL plan");
+  if (plan->p.kind != CAT_1D) return fail(CAT_ERR_PLAN_MISMATCH, "plan is not 1D");
+  if (plan->p.B == 0) return CAT_OK;  // empty batch: nothing to do
+  cat_status st = check_ptrs({X, W_A, W_V, O, workspace});
+  if (st != CAT_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  void* Vb = ws_at(workspace, plan->off_V);
+  float* z = reinterpret_cast<float*>(ws_at(workspace, plan->off_z));
+  KernelMark mk(plan, s);
+
+  GemmArgs ga = gemm_base(plan, X);
+  ga.nseg = 2;
+  ga.seg[0] = seg(W_V, Vb, (int)plan->p.D, 0, OUT_BLOCKED, 2 * plan->G);
+  ga.seg[1] = seg(W_A, z, (int)plan->p.H, 1, OUT_HEADMAJOR, 1);
+  mk.begin(0);
+  hipError_t e = launch_gemm(plan->et, ga, s);
+  mk.end(0);
+  if (e != hipSuccess) return hip_fail(e, "projection launch");
+  if ((st = check_sync(plan, "projection")) != CAT_OK) return st;
+
+  SpecArgs sa = spec_base(plan, workspace);
+  sa.logits = z;
+  mk.begin(1);
+  e = launch_spectrum(plan->geom, 0, sa, s);
+  mk.end(1);
+  if (e != hipSuccess) return hip_fail(e, "spectrum launch");
+  if ((st = check_sync(plan, "spectrum")) != CAT_OK) return st;
+
+  ConvArgs ca = conv_base(plan, Vb, sa.spec, O);
+  mk.begin(2);
+  e = launch_conv(plan->geom, plan->et, ca, s);
+  mk.end(2);
+  if (e != hipSuccess) return hip_fail(e, "fft-conv launch");
+  return check_sync(plan, "fft-conv");
+}
+
+cat_status cat_forward_bccb_2d(cat_plan plan, const void* X, const void* W_Q, const void* W_K,
+                               const void* W_V, void* O, void* workspace, void* stream) {
+  if (!plan) return fail(CAT_ERR_INVALID_ARG, "NULL plan");
+  if (plan->p.kind != CAT_BCCB_2D) return fail(CAT_ERR_PLAN_MISMATCH, "plan is not 2D");
+  if (plan->p.B == 0) return CAT_OK;  // empty batch: nothing to do
+  cat_status st = check_ptrs({X, W_Q, W_K, W_V, O, workspace});
+  if (st != CAT_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  void* Vb = ws_at(workspace, plan->off_V);
+  float* Qb = reinterpret_cast<float*>(ws_at(workspace, plan->off_Q));
+  float* Kb = reinterpret_cast<float*>(ws_at(workspace, plan->off_K));
+  float2* part = reinterpret_cast<float2*>(ws_at(workspace, plan->off_part));
+  const int D = (int)plan->p.D;
+  KernelMark mk(plan, s);
+
+  GemmArgs ga = gemm_base(plan, X);
+  ga.nseg = 3;
+  ga.seg[0] = seg(W_Q, Qb, D, 1, OUT_BLOCKED, 2);
+  ga.seg[1] = seg(W_K, Kb, D, 1, OUT_BLOCKED, 2);
+  ga.seg[2] = seg(W_V, Vb, D, 0, OUT_BLOCKED, 2 * plan->G);
+  mk.begin(0);
+  hipError_t e = launch_gemm(plan->et, ga, s);
+  mk.end(0);
+  if (e != hipSuccess) return hip_fail(e, "projection launch");
+  if ((st = check_sync(plan, "projection")) != CAT_OK) return st;
+
+  ScoreArgs sc{};
+  sc.Q = Qb;
+  sc.K = Kb;
+  sc.partial = part;
+  sc.BH = (int)(plan->p.B * plan->p.H);
+  sc.N = (int)plan->p.N;
+  sc.npair = plan->npair;
+  sc.ngrp = plan->ngrp;
+  sc.ppg = plan->ppg;
+  mk.begin(1);
+  e = launch_score_partial(plan->geom, sc, s);
+  mk.end(1);
+  if (e != hipSuccess) return hip_fail(e, "score launch");
+  if ((st = check_sync(plan, "scores")) != CAT_OK) return st;
+
+  SpecArgs sa = spec_base(plan, workspace);
+  sa.partial = part;
+  sa.ngrp = plan->ngrp;
+  sa.scale = 1.0f / std::sqrt((float)plan->d);
+  mk.begin(2);
+  e = launch_spectrum(plan->geom, 1, sa, s);
+  mk.end(2);
+  if (e != hipSuccess) return hip_fail(e, "spectrum launch");
+  if ((st = check_sync(plan, "spectrum")) != CAT_OK) return st;
+
+  ConvArgs ca = conv_base(plan, Vb, sa.spec, O);
+  mk.begin(3);
+  e = launch_conv(plan->geom, plan->et, ca, s);
+  mk.end(3);
+  if (e != hipSuccess) return hip_fail(e, "fft-conv launch");
+  return check_sync(plan, "fft-conv");
+}
+
+cat_status cat_step_project(cat_plan plan, const void* X, const void* W_A, const void* W_K,
+                            const void* W_V, void* V, void* z, void* K_out, void* stream) {
+  if (!plan) return fail(CAT_ERR_INVALID_ARG, "NULL plan");
+  if (plan->p.B == 0) return CAT_OK;
+  const bool two_d = plan->p.kind == CAT_BCCB_2D;
+  cat_status st = two_d ? check_ptrs({X, W_A, W_K, W_V, V, z, K_out}) : check_ptrs({X, W_A, W_V, V, z});
+  if (st != CAT_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int D = (int)plan->p.D;
+  GemmArgs ga = gemm_base(plan, X);
+  if (!two_d) {
+    ga.nseg = 2;
+    ga.seg[0] = seg(W_V, V, D, 0, OUT_ROWMAJOR, 1);
+    ga.seg[1] = seg(W_A, z, (int)plan->p.H, 1, OUT_HEADMAJOR, 1);
+  } else {
+    ga.nseg = 3;
+    ga.seg[0] = seg(W_A, z, D, 1, OUT_ROWMAJOR, 1);
+    ga.seg[1] = seg(W_K, K_out, D, 1, OUT_ROWMAJOR, 1);
+    ga.seg[2] = seg(W_V, V, D, 0, OUT_ROWMAJOR, 1);
+  }
+  hipError_t e = launch_gemm(plan->et, ga, s);
+  if (e != hipSuccess) return hip_fail(e, "projection launch");
+  return check_sync(plan, "projection");
+}
+
+cat_status cat_step_spectrum(cat_plan plan, const float* logits, float* probs, float* spec, void* stream) {
+  if (!plan) return fail(CAT_ERR_INVALID_ARG, "NULL plan");
+  if (plan->p.B == 0) return CAT_OK;
+  cat_status st = check_ptrs({logits, spec});
+  if (st != CAT_OK) return st;
+  if (probs && !aligned16(probs)) return fail(CAT_ERR_INVALID_ARG, "probs not 16-byte aligned");
+  SpecArgs a{};
+  a.logits = logits;
+  a.probs = probs;
+  a.spec = reinterpret_cast<float2*>(spec);
+  a.tw = plan->d_tw;
+  a.BH = (int)(plan->p.B * plan->p.H);
+  a.N = (int)plan->p.N;
+  a.scale = 1.0f;
+  a.G = plan->Gs;
+  hipError_t e = launch_spectrum(plan->geom, 0, a, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "spectrum launch");
+  return check_sync(plan, "spectrum");
+}
+
+cat_status cat_step_mix(cat_plan plan, const float* logits, const void* V, void* O, void* workspace,
+                        void* stream) {
+  if (!plan) return fail(CAT_ERR_INVALID_ARG, "NULL plan");
+  if (plan->p.B == 0) return CAT_OK;
+  cat_status st = check_ptrs({logits, V, O, workspace});
+  if (st != CAT_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  void* Vb = ws_at(workspace, plan->off_V);
+  RelayoutArgs ra{};
+  ra.src = V;
+  ra.dst = Vb;
+  ra.src_et = plan->et;
+  ra.dst_f32 = 0;
+  ra.B = (int)plan->p.B;
+  ra.N = (int)plan->p.N;
+  ra.D = (int)plan->p.D;
+  ra.H = (int)plan->p.H;
+  ra.d = plan->d;
+  ra.cg = 2 * plan->G;
+  hipError_t e = launch_relayout(ra, s);
+  if (e != hipSuccess) return hip_fail(e, "relayout launch");
+  SpecArgs sa = spec_base(plan, workspace);
+  sa.logits = logits;
+  e = launch_spectrum(plan->geom, 0, sa, s);
+  if (e != hipSuccess) return hip_fail(e, "spectrum launch");
+  if ((st = check_sync(plan, "spectrum")) != CAT_OK) return st;
+  ConvArgs ca = conv_base(plan, Vb, sa.spec, O);
+  e = launch_conv(plan->geom, plan->et, ca, s);
+  if (e != hipSuccess) return hip_fail(e, "fft-conv launch");
+  return check_sync(plan, "fft-conv");
+}
+
+cat_status cat_step_scores_2d(cat_plan plan, const float* Q, const float* K, float* probs, void* workspace,
+                              void* stream) {
+  if (!plan) return fail(CAT_ERR_INVALID_ARG, "NULL plan");
+  if (plan->p.kind != CAT_BCCB_2D) return fail(CAT_ERR_PLAN_MISMATCH, "plan is not 2D");
+  if (plan->p.B == 0) return CAT_OK;
+  cat_status st = check_ptrs({Q, K, probs, workspace});
+  if (st != CAT_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  float* Qb = reinterpret_cast<float*>(ws_at(workspace, plan->off_Q));
+  float* Kb = reinterpret_cast<float*>(ws_at(workspace, plan->off_K));
+  float2* part = reinterpret_cast<float2*>(ws_at(workspace, plan->off_part));
+  RelayoutArgs ra{};
+  ra.src_et = ET_F32;
+  ra.dst_f32 = 1;
+  ra.B = (int)plan->p.B;
+  ra.N = (int)plan->p.N;
+  ra.D = (int)plan->p.D;
+  ra.H = (int)plan->p.H;
+  ra.d = plan->d;
+  ra.cg = 2;
+  ra.src = Q;
+  ra.dst = Qb;
+  hipError_t e = launch_relayout(ra, s);
+  if (e != hipSuccess) return hip_fail(e, "relayout launch");
+  ra.src = K;
+  ra.dst = Kb;
+  e = launch_relayout(ra, s);
+  if (e != hipSuccess) return hip_fail(e, "relayout launch");
+  ScoreArgs sc{};
+  sc.Q = Qb;
+  sc.K = Kb;
+  sc.partial = part;
+  sc.BH = (int)(plan->p.B * plan->p.H);
+  sc.N = (int)plan->p.N;
+  sc.npair = plan->npair;
+  sc.ngrp = plan->ngrp;
+  sc.ppg = plan->ppg;
+  e = launch_score_partial(plan->geom, sc, s);
+  if (e != hipSuccess) return hip_fail(e, "score launch");
+  if ((st = check_sync(plan, "scores")) != CAT_OK) return st;
+  SpecArgs sa = spec_base(plan, workspace);
+  sa.partial = part;
+  sa.ngrp = plan->ngrp;
+  sa.scale = 1.0f / std::sqrt((float)plan->d);
+  sa.probs = probs;
+  e = launch_spectrum(plan->geom, 1, sa, s);
+  if (e != hipSuccess) return hip_fail(e, "spectrum launch");
+  return check_sync(plan, "spectrum");
+}
+
+}  // extern "C"

@@ -1,0 +1,116 @@
+// cat_fftconv.hip -- registry of transform geometries and the launchers of
+// the spectrum, FFT-convolution, score and relayout kernels.
+#include "cat_fftconv.hpp"
+
+namespace cat {
+
+const Entry* entries_1d_small(int* n);
+const Entry* entries_1d_mid(int* n);
+const Entry* entries_1d_large(int* n);
+const Entry* entries_2d_small(int* n);
+const Entry* entries_2d_96(int* n);
+
+namespace {
+
+using kern::ConvFn;
+using kern::ScoreFn;
+using kern::SpecFn;
+
+const Entry* find_entry(const LineGeom& g) {
+  using Getter = const Entry* (*)(int*);
+  static const Getter getters[] = {entries_1d_small, entries_1d_mid, entries_1d_large, entries_2d_small,
+                                   entries_2d_96};
+  for (Getter get : getters) {
+    int n = 0;
+    const Entry* e = get(&n);
+    for (int i = 0; i < n; ++i)
+      if (e[i].L1 == g.L1 && e[i].L2 == g.L2 && e[i].tw == g.twiddled) return &e[i];
+  }
+  return nullptr;
+}
+
+int ilog2(int v) {
+  int r = 0;
+  while ((1 << r) < v) ++r;
+  return r;
+}
+
+}  // namespace
+
+bool geom_supported(const LineGeom& g) { return find_entry(g) != nullptr; }
+
+size_t line_lds_bytes(const LineGeom& g) {
+  const int P2 = g.L2 + ((g.L2 % 2 == 0) ? 1 : 0);
+  const int base = g.L1 * P2;
+  const int LP = base + ((2 - base % 16) + 16) % 16;
+  return (size_t)LP * sizeof(float2);
+}
+
+int line_threads(const LineGeom& g) {
+  const Entry* e = find_entry(g);
+  return e ? e->T : 0;
+}
+
+hipError_t prepare_kernels(const LineGeom& g, size_t conv_lds, size_t spec_lds, size_t score_lds) {
+  const Entry* e = find_entry(g);
+  if (!e) return hipErrorInvalidValue;
+  hipError_t err = hipSuccess;
+  auto raise = [&](const void* fn, size_t bytes) {
+    if (fn && bytes > 0 && err == hipSuccess)
+      err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  };
+  raise((const void*)e->conv_f32, conv_lds);
+  raise((const void*)e->conv_bf16, conv_lds);
+  raise((const void*)e->spec0, spec_lds);
+  raise((const void*)e->spec1, spec_lds);
+  raise((const void*)e->score, score_lds);
+  return err;
+}
+
+hipError_t launch_spectrum(const LineGeom& g, int mode, const SpecArgs& a, hipStream_t s) {
+  const Entry* e = find_entry(g);
+  SpecFn fn = e ? (mode == 0 ? e->spec0 : e->spec1) : nullptr;
+  if (!fn) return hipErrorInvalidValue;
+  SpecArgs aa = a;
+  aa.log2G = ilog2(aa.G);
+  const size_t lds = (size_t)aa.G * line_lds_bytes(g) + (size_t)aa.G * e->T * sizeof(float);
+  const int blocks = (aa.BH + aa.G - 1) / aa.G;
+  hipLaunchKernelGGL(fn, dim3(blocks), dim3(aa.G * e->T), lds, s, aa);
+  return hipGetLastError();
+}
+
+hipError_t launch_conv(const LineGeom& g, int et, const ConvArgs& a, hipStream_t s) {
+  const Entry* e = find_entry(g);
+  ConvFn fn = e ? (et == ET_F32 ? e->conv_f32 : e->conv_bf16) : nullptr;
+  if (!fn) return hipErrorInvalidValue;
+  ConvArgs aa = a;
+  aa.log2G = ilog2(aa.G);
+  const size_t lds = (size_t)aa.G * line_lds_bytes(g);
+  const int blocks = aa.B * aa.H * aa.ng;
+  hipLaunchKernelGGL(fn, dim3(blocks), dim3(aa.G * e->T), lds, s, aa);
+  return hipGetLastError();
+}
+
+hipError_t launch_score_partial(const LineGeom& g, const ScoreArgs& a, hipStream_t s) {
+  const Entry* e = find_entry(g);
+  ScoreFn fn = e ? e->score : nullptr;
+  if (!fn) return hipErrorInvalidValue;
+  const size_t lds = 2 * line_lds_bytes(g);
+  hipLaunchKernelGGL(fn, dim3(a.BH * a.ngrp), dim3(2 * e->T), lds, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_relayout(const RelayoutArgs& a, hipStream_t s) {
+  const size_t total = (size_t)a.B * a.N * a.D;
+  const int blocks = (int)std::min<size_t>((total + 255) / 256, 65536);
+  if (a.src_et == ET_F32) {
+    hipLaunchKernelGGL((kern::relayout_kernel<ET_F32, 1>), dim3(blocks), dim3(256), 0, s, a);
+  } else if (a.dst_f32) {
+    hipLaunchKernelGGL((kern::relayout_kernel<ET_BF16, 1>), dim3(blocks), dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((kern::relayout_kernel<ET_BF16, 0>), dim3(blocks), dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace cat

@@ -1,0 +1,112 @@
+// cat_internal.hpp -- argument blocks and launchers shared by the C-ABI layer
+// and the kernel translation units (host-visible, no device code).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace cat {
+
+enum ElemType : int { ET_F32 = 0, ET_BF16 = 1 };
+
+// Output index maps of the projection GEMM.  Row m = b * Ntok + tok.
+//   ROWMAJOR: out[m * ncols + n]
+//   BLOCKED : channel n of head h = n / d lands in group g = (n % d) / cg:
+//             out[(((b * H + h) * (d / cg) + g) * Ntok + tok) * cg + n % cg]
+//             -- every group is one contiguous [Ntok][cg] block, the unit a
+//             transform workgroup reads.
+//   HEADMAJOR: out[(b * ncols + n) * Ntok + tok] (score logits, [B][H][N])
+enum OutLayout : int { OUT_ROWMAJOR = 0, OUT_BLOCKED = 1, OUT_HEADMAJOR = 2 };
+
+struct GemmSeg {
+  const void* W;  // [K][ncols] row-major, same element type as X
+  void* out;
+  int ncols;
+  int out_f32;  // 1: fp32 output; 0: the input element type
+  int layout;   // OutLayout
+  int cg;       // channels per group (BLOCKED)
+  int ntiles;   // filled by the launcher
+};
+
+struct GemmArgs {
+  const void* X;  // [M][K] row-major
+  int M, K;
+  int Ntok, H, d;
+  int nseg;
+  int ncoltiles;  // filled by the launcher
+  GemmSeg seg[3];
+};
+
+// Launch Y_s = X . W_s for every segment s; returns hipSuccess or the launch error.
+hipError_t launch_gemm(int et, GemmArgs args, hipStream_t stream);
+
+// Softmax + spectrum of one line per (batch, head).
+//   mode 0: input logits [BH][N] (fp32, spatial, not yet scaled)
+//   mode 1: input partial spectra [BH][ngrp][L] (complex fp32, 2D scores),
+//           summed and inverse-transformed to the logits first
+// The logits are multiplied by `scale`, softmaxed over the N valid positions
+// (optionally written to `probs` [BH][N]), laid on the length-L transform
+// line (periodically extended when L > N in 1D), multiplied by 1/L and
+// forward transformed:  spec[bh][k1 + L1 k2].
+struct SpecArgs {
+  const float* logits;
+  const float2* partial;
+  int ngrp;
+  float2* spec;
+  float* probs;
+  const float2* tw;  // 1D inter-pass twiddles (may be null for 2D)
+  int BH, N;
+  float scale;
+  int G, log2G;  // lines per workgroup
+};
+
+// Fused forward transform . Hadamard . inverse transform of one group of
+// 2G channels (G complex lines) of one (batch, head):
+//   O[b][p][h d + g 2G + c] = IFFT(spec[bh] . FFT(V line))[p]   for p < N
+struct ConvArgs {
+  const void* V;      // BLOCKED [B][H][ng][N][2G], element type et
+  const float2* spec; // [BH][L]
+  const float2* tw;   // 1D inter-pass twiddles (null for 2D)
+  void* O;            // [B][N][D], element type et
+  int B, H, D, N, d;
+  int G, log2G, ng;
+};
+
+// 2D scores: for each (bh, group of pairs) accumulate
+//   sum_pairs FFT2(q pair) . conj(FFT2(k pair))   into partial[bh][grp][L]
+struct ScoreArgs {
+  const float* Q;  // BLOCKED fp32, cg = 2: [BH][npair][N][2]
+  const float* K;
+  float2* partial;
+  int BH, N, npair, ngrp, ppg;
+};
+
+struct RelayoutArgs {
+  const void* src;  // [B][N][D] row-major
+  void* dst;        // BLOCKED
+  int src_et, dst_f32;
+  int B, N, D, H, d, cg;
+};
+
+// Transform geometry chosen for a problem.
+struct LineGeom {
+  int L1, L2;  // L = L1 * L2
+  int twiddled;  // 1D (inter-pass twiddles) vs 2D grid
+};
+
+// Supported geometries.  1D: powers of two 1..4096; 2D: a fixed list of grids.
+bool geom_supported(const LineGeom& g);
+// LDS bytes of one transform line and the threads per line.
+size_t line_lds_bytes(const LineGeom& g);
+int line_threads(const LineGeom& g);
+
+hipError_t launch_spectrum(const LineGeom& g, int mode, const SpecArgs& a, hipStream_t s);
+hipError_t launch_conv(const LineGeom& g, int et, const ConvArgs& a, hipStream_t s);
+hipError_t launch_score_partial(const LineGeom& g, const ScoreArgs& a, hipStream_t s);
+hipError_t launch_relayout(const RelayoutArgs& a, hipStream_t s);
+// Raise the dynamic-LDS limit of the kernels a geometry uses (once per plan).
+hipError_t prepare_kernels(const LineGeom& g, size_t conv_lds, size_t spec_lds, size_t score_lds);
+
+}  // namespace cat

@@ -1,0 +1,169 @@
+/*
+ * cat.h -- C ABI of the MI355X (gfx950) circulant softmax attention library
+ * (libcat.so).
+ *
+ * What it computes
+ * ----------------
+ * 1D, CAT (CAT: Circular-Convolutional Attention for Sub-Quadratic
+ * Transformers, "Method details / Overall framework" and "Key designs"):
+ *   for every image/sequence b and head h (channels [h d, (h+1) d), d = D/H):
+ *     z_h  = X_b W_A[:, h]                       (N logits, no scale, no bias)
+ *     z*_h = softmax over the N tokens of z_h
+ *     V    = X_b W_V
+ *     O_b[:, head h] = circ(z*_h) V[:, head h],  circ(w)[i][j] = w[(i - j) mod N]
+ *   evaluated as IFFT(FFT(z*_h) . FFT(V_h)) along the tokens ("Key designs:
+ *   FFT-accelerated computation").  There is no output projection.
+ *
+ * 2D, BCCB circulant attention (Vision Transformers are Circulant Attention
+ * Learners, "What does this finding overturn?" and "Circulant Attention:
+ * attention rebuilt with the FFT"), tokens in raster order n = r Wg + c on an
+ * Hg x Wg grid:
+ *     Q, K, V = X_b W_Q, X_b W_K, X_b W_V
+ *     a_h[s]  = (1/sqrt(d)) sum_{c in head h} sum_m Q[m][c] K[(m - s) mod grid][c]
+ *     a*_h    = softmax over all N = Hg Wg positions of a_h
+ *     O_b[:, head h] = BCCB(a*_h) V[:, head h]      (2D circular convolution)
+ *
+ * Data
+ * ----
+ * All buffers are device memory, dense, row-major, owned by the caller:
+ *   X [B][N][D], W_A [D][H], W_V / W_Q / W_K [D][D] (the product is X W, i.e.
+ *   the transpose of a torch nn.Linear weight), O [B][N][D].
+ * Storage dtype (CAT_F32 or CAT_BF16) is the same for X, the weights and O;
+ * all arithmetic is fp32 (bf16 inputs are widened exactly, O is rounded to
+ * nearest even).  X, the weights, O and the workspace must be 16-byte
+ * aligned; O must not overlap X, the weights or the workspace.
+ *
+ * Calls
+ * -----
+ * Forward calls only enqueue kernels on `stream` (a hipStream_t passed as
+ * void*; NULL is the default stream).  They never allocate, never
+ * synchronise, and return as soon as the work is queued.  A plan owns small
+ * device tables created at plan creation; the workspace (size from
+ * cat_plan_workspace_size) holds the intermediates and is owned by the
+ * caller.  Calls that share a plan and workspace must be ordered (same stream).
+ *
+ * Errors
+ * ------
+ * Every entry returns a cat_status and never aborts.  Bad shapes, NULL
+ * pointers, misalignment and a plan of the wrong kind are rejected before any
+ * HIP call.  cat_last_error() returns a message for the calling thread's last
+ * failure.  Setting the environment variable CAT_DEBUG_SYNC=1 makes every
+ * launch synchronise and check for asynchronous errors.
+ */
+#ifndef CAT_H_
+#define CAT_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct cat_plan_s* cat_plan;
+
+typedef enum {
+  CAT_OK = 0,
+  CAT_ERR_INVALID_ARG = -1,   /* bad shape, NULL pointer, misalignment */
+  CAT_ERR_UNSUPPORTED = -2,   /* valid problem outside what the kernels cover */
+  CAT_ERR_HIP = -3,           /* a HIP runtime call or launch failed */
+  CAT_ERR_ALLOC = -4,         /* host or device allocation in plan creation failed */
+  CAT_ERR_PLAN_MISMATCH = -5  /* plan built for the other kind */
+} cat_status;
+
+typedef enum { CAT_F32 = 0, CAT_BF16 = 1 } cat_dtype;
+typedef enum { CAT_1D = 0, CAT_BCCB_2D = 1 } cat_kind;
+
+/* Problem description.  1D: Hg = Wg = 0.  2D: N must equal Hg * Wg.
+ * Requirements: B >= 0 (B = 0 makes every forward call a no-op), N, D,
+ * H >= 1; D % H == 0; d = D / H even; D % 8 == 0; B * N * D < 2^31.
+ * Supported sizes (else CAT_ERR_UNSUPPORTED):
+ *   1D: N a power of two up to 4096, or any other N up to 2048 (the circular
+ *       convolution of length N is evaluated exactly on a power-of-two circle
+ *       of length L >= 2N - 1, the values zero-extended and the softmaxed
+ *       scores periodically extended);
+ *   2D: grids 1x1, 2x3, 3x4, 4x4, 6x8, 8x8, 12x12, 16x16, 32x32, 96x96. */
+typedef struct {
+  int32_t kind;  /* cat_kind */
+  int32_t dtype; /* cat_dtype */
+  int64_t B, N, D, H;
+  int64_t Hg, Wg;
+} cat_problem;
+
+/* Validate `p`, choose the transform geometry and build the device tables.
+ * On success *out owns host memory and device tables until cat_plan_destroy.
+ * On failure *out is NULL. */
+cat_status cat_plan_create(cat_plan* out, const cat_problem* p);
+
+/* Free a plan (NULL is accepted and ignored).  No work may be in flight. */
+cat_status cat_plan_destroy(cat_plan plan);
+
+/* Bytes of device workspace the forward calls of this plan need. */
+cat_status cat_plan_workspace_size(cat_plan plan, size_t* bytes);
+
+/* Length of the transform circle / grid the plan uses (L, and L1 x L2 of
+ * its two passes).  Diagnostic. */
+cat_status cat_plan_geometry(cat_plan plan, int64_t* L, int64_t* L1, int64_t* L2);
+
+/* CAT 1D forward (see top of file).  X [B][N][D], W_A [D][H], W_V [D][D],
+ * O [B][N][D] in the plan's storage dtype. */
+cat_status cat_forward_1d(cat_plan plan, const void* X, const void* W_A, const void* W_V,
+                          void* O, void* workspace, void* stream);
+
+/* 2D BCCB circulant attention forward (see top of file).  X [B][Hg Wg][D],
+ * W_Q, W_K, W_V [D][D], O [B][Hg Wg][D]. */
+cat_status cat_forward_bccb_2d(cat_plan plan, const void* X, const void* W_Q, const void* W_K,
+                               const void* W_V, void* O, void* workspace, void* stream);
+
+/* Per-kernel timing (diagnostic).  While enabled, each forward call records
+ * a HIP event before and after every kernel it launches, on the caller's
+ * stream, into plan-owned slots (events are created here, not in the
+ * forward calls; at most 512 calls are kept, older ones are overwritten).
+ * Enabling resets the slots.  cat_plan_kernel_times waits for the recorded
+ * events and returns, per kernel of the path in launch order (1D:
+ * projection, spectrum, fft-conv; 2D: projection, scores, spectrum,
+ * fft-conv), the summed milliseconds and the number of calls measured;
+ * *nkernels receives the number of kernels (arrays hold at least 8). */
+cat_status cat_plan_set_timing(cat_plan plan, int enable);
+cat_status cat_plan_kernel_times(cat_plan plan, double* total_ms, int64_t* calls, int* nkernels);
+
+const char* cat_status_string(cat_status s);
+/* Message of the calling thread's last failed call ("" if none). */
+const char* cat_last_error(void);
+
+/* ---- Step entry points: one step of the forward path each, with plain
+ * row-major inputs and outputs.  For testing and diagnosis of the
+ * individual steps; they share the kernels of the forward calls. */
+
+/* Projection step.  1D plan: V [B][N][D] (storage dtype) = X W_V and
+ * z [B][H][N] (fp32) = logits X W_A (W_K ignored).  2D plan: Q, K [B][N][D]
+ * fp32 = X W_Q, X W_K and V (storage dtype) = X W_V; pass W_A = W_Q,
+ * z = Q (fp32 [B][N][D]) and K_out for K.  No workspace is used. */
+cat_status cat_step_project(cat_plan plan, const void* X, const void* W_A, const void* W_K,
+                            const void* W_V, void* V, void* z, void* K_out, void* stream);
+
+/* Softmax + filter spectrum step from logits.  logits [B][H][N] fp32 (1D: z;
+ * 2D: the scaled scores a).  probs [B][H][N] fp32 receives the softmax
+ * (may be NULL); spec [B][H][L] complex fp32 (interleaved re, im) receives
+ * FFT_L of the (extended) softmax times 1/L in the kernels' spectral order
+ * k1 + L1 k2 with natural frequency k1 + L1 k2 in 1D and (k_r = k1,
+ * k_c = k2) on a 2D grid. */
+cat_status cat_step_spectrum(cat_plan plan, const float* logits, float* probs, float* spec,
+                             void* stream);
+
+/* Circulant mixing step: O = circ(softmax(logits)) V per head (1D) or
+ * BCCB(softmax(logits)) V (2D).  logits [B][H][N] fp32 (2D: already scaled),
+ * V and O [B][N][D] storage dtype. */
+cat_status cat_step_mix(cat_plan plan, const float* logits, const void* V, void* O,
+                        void* workspace, void* stream);
+
+/* 2D score step: probs [B][H][N] fp32 = softmax over the grid of the scaled
+ * circular cross-correlation of Q and K (both [B][N][D] fp32).  2D plans only. */
+cat_status cat_step_scores_2d(cat_plan plan, const float* Q, const float* K, float* probs,
+                              void* workspace, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CAT_H_ */

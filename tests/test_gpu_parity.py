@@ -1,0 +1,306 @@
+"""GPU parity: every step and the whole forward path, called through the C
+ABI, against the fp64 CPU oracle on the same seeded inputs.
+
+Bars (written here, from the workload specification): fp32 storage ->
+relative L2 <= 1e-5 and max-abs <= 1e-4; bf16 storage with fp32 compute ->
+relative L2 <= 2e-2.  Spectra (an internal quantity with no oracle function)
+are checked against numpy's FFT of the oracle's softmax, at the fp32 bar.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from circulant_softmax_attention_amd import workloads as W
+from helpers import assert_parity, ensure_lib, rel_l2, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[gpu-case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def cat():
+    ensure_lib()
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    from circulant_softmax_attention_amd import cat as c
+    return c
+
+
+def rng_inputs(seed, B, N, D, H, dtype, kind="1d", score_scale=1.0):
+    wl = W.Workload("adhoc", kind, B, N, D, H, dtype, seed)
+    if kind == "2d":
+        raise ValueError
+    return W.make_inputs(wl, score_scale=score_scale)
+
+
+def rng_inputs_2d(seed, B, Hg, Wg, D, H, dtype, score_scale=1.0):
+    wl = W.Workload("adhoc2d", "2d", B, Hg * Wg, D, H, dtype, seed, Hg=Hg, Wg=Wg)
+    return W.make_inputs(wl, score_scale=score_scale)
+
+
+def tdtype(dtype):
+    import torch
+    return torch.float32 if dtype == "f32" else torch.bfloat16
+
+
+# ------------------------------------------------------------------ 1D steps
+@pytest.mark.parametrize("B,N,D,H,dtype", [(1, 64, 64, 4, "f32"), (3, 37, 48, 3, "f32"), (2, 200, 136, 17, "bf16"),
+                                           (2, 256, 256, 4, "bf16")])
+def test_project_1d(cat, B, N, D, H, dtype):
+    say("project_1d", B, N, D, H, dtype)
+    inp = rng_inputs(11, B, N, D, H, dtype)
+    plan = cat.cat_plan_create("1d", dtype, B, N, D, H)
+    V, z = cat.cat_step_project(plan, to_dev(inp.X, dtype), to_dev(inp.W_A, dtype), to_dev(inp.W_V, dtype))
+    import torch
+    torch.cuda.synchronize()
+    assert_parity(to_np(V), oracle.matmul(inp.X, inp.W_V), dtype, "V")
+    assert_parity(to_np(z), oracle.scores_1d(inp.X, inp.W_A), "f32", "z")
+
+
+def _extended_line(zs, L):
+    """The length-L circle the spectrum lives on: softmax values periodically
+    extended (p < N: z*[p]; p > L - N: z*[p - L + N]; zero between)."""
+    B, H, N = zs.shape
+    out = np.zeros((B, H, L))
+    out[..., :N] = zs
+    if L > N:
+        out[..., L - N + 1:] = zs[..., 1:]
+    return out
+
+
+@pytest.mark.parametrize("N", [1, 2, 3, 5, 16, 64, 197, 256, 1000, 1024, 2047, 4096])
+def test_spectrum_1d(cat, N):
+    say("spectrum_1d", N)
+    import torch
+    B, H = 2, 3
+    D = 8 * H
+    plan = cat.cat_plan_create("1d", "f32", B, N, D, H)
+    L, L1, L2 = plan.geometry()
+    logits = np.random.default_rng(N).standard_normal((B, H, N)).astype(np.float32) * 2
+    probs, spec = cat.cat_step_spectrum(plan, torch.from_numpy(logits).cuda())
+    torch.cuda.synchronize()
+    zs = oracle.softmax(logits)
+    assert_parity(to_np(probs), zs, "f32", "softmax")
+    ref = np.fft.fft(_extended_line(zs, L), axis=-1) / L
+    got = spec.cpu().numpy()
+    assert rel_l2(got, ref) < 1e-5, rel_l2(got, ref)
+
+
+@pytest.mark.parametrize("B,N,D,H,dtype", [(1, 1, 16, 2, "f32"), (2, 2, 16, 2, "f32"), (2, 3, 16, 2, "f32"),
+                                           (1, 64, 64, 4, "f32"), (2, 197, 64, 2, "f32"), (2, 197, 64, 2, "bf16"),
+                                           (1, 1024, 128, 2, "bf16"), (1, 1000, 64, 4, "f32"),
+                                           (1, 2048, 32, 1, "f32"), (1, 4096, 32, 2, "f32"), (1, 2047, 16, 1, "f32"),
+                                           (3, 256, 96, 3, "f32"), (2, 512, 64, 32, "bf16")])
+def test_mix_1d(cat, B, N, D, H, dtype):
+    say("mix_1d", B, N, D, H, dtype)
+    import torch
+    rng = np.random.default_rng(N * 7 + D)
+    logits = (rng.standard_normal((B, H, N)) * 2).astype(np.float32)
+    V = rng.standard_normal((B, N, D)).astype(np.float32)
+    if dtype == "bf16":
+        V = W.bf16_bits_to_f32(W.round_bf16_bits(V)).reshape(V.shape)
+    plan = cat.cat_plan_create("1d", dtype, B, N, D, H)
+    O = cat.cat_step_mix(plan, torch.from_numpy(logits).cuda(), to_dev(V, dtype))
+    torch.cuda.synchronize()
+    ref = oracle.circulant_1d(oracle.softmax(logits), V)
+    assert_parity(to_np(O), ref, dtype, "O")
+
+
+# ------------------------------------------------------------------ 1D forward
+@pytest.mark.parametrize("B,N,D,H,dtype", [(1, 64, 64, 4, "f32"), (2, 37, 48, 3, "f32"), (3, 100, 64, 4, "bf16"),
+                                           (1, 1, 32, 2, "f32"), (2, 197, 96, 3, "f32"), (1, 1024, 64, 1, "bf16"),
+                                           (5, 128, 72, 9, "f32")])
+def test_forward_1d_small(cat, B, N, D, H, dtype):
+    say("forward_1d", B, N, D, H, dtype)
+    import torch
+    inp = rng_inputs(5, B, N, D, H, dtype)
+    plan = cat.cat_plan_create("1d", dtype, B, N, D, H)
+    O = cat.cat_forward_1d(plan, to_dev(inp.X, dtype), to_dev(inp.W_A, dtype), to_dev(inp.W_V, dtype))
+    torch.cuda.synchronize()
+    ref = oracle.cat_forward_1d(inp.X, inp.W_A, inp.W_V)["O"]
+    assert_parity(to_np(O), ref, dtype, "O")
+
+
+WL1D = [n for n, w in W.WORKLOADS.items() if w.kind == "1d"]
+
+
+@pytest.mark.parametrize("name", WL1D)
+def test_forward_1d_workload_full_size(cat, name):
+    """The workload at its full size, in the launch configuration bench.py
+    times; the oracle recomputes a sample of whole images."""
+    wl = W.WORKLOADS[name]
+    say("forward_1d_workload", name)
+    import torch
+    inp = W.make_inputs(wl)
+    plan = cat.cat_plan_create("1d", wl.dtype, wl.B, wl.N, wl.D, wl.H)
+    O = cat.cat_forward_1d(plan, to_dev(inp.X, wl.dtype), to_dev(inp.W_A, wl.dtype), to_dev(inp.W_V, wl.dtype))
+    torch.cuda.synchronize()
+    O = to_np(O)
+    assert np.all(np.isfinite(O))
+    for b in sorted({0, wl.B // 2, wl.B - 1}):
+        ref = oracle.cat_forward_1d(inp.X[b:b + 1], inp.W_A, inp.W_V)["O"][0]
+        assert_parity(O[b], ref, wl.dtype, f"{name} b={b}")
+
+
+def test_prime_length_is_exactly_circular(cat):
+    """N = 197 must wrap mod 197: the GPU result matches the oracle and is far
+    from what a length-256 zero-padded circular product would give."""
+    say("prime_length")
+    import torch
+    B, N, D, H = 2, 197, 64, 2
+    rng = np.random.default_rng(197)
+    logits = (rng.standard_normal((B, H, N)) * 3).astype(np.float32)
+    V = rng.standard_normal((B, N, D)).astype(np.float32)
+    plan = cat.cat_plan_create("1d", "f32", B, N, D, H)
+    O = to_np(cat.cat_step_mix(plan, torch.from_numpy(logits).cuda(), to_dev(V, "f32")))
+    zs = oracle.softmax(logits)
+    assert_parity(O, oracle.circulant_1d(zs, V), "f32", "O")
+    wrong = np.zeros_like(O)
+    for h in range(H):
+        w = np.zeros((B, 256))
+        w[:, :N] = zs[:, h]
+        v = np.zeros((B, 256, D // H))
+        v[:, :N] = V[:, :, h * (D // H):(h + 1) * (D // H)]
+        wrong[:, :, h * (D // H):(h + 1) * (D // H)] = np.fft.ifft(
+            np.fft.fft(w, axis=1)[:, :, None] * np.fft.fft(v, axis=1), axis=1).real[:, :N]
+    assert rel_l2(O, wrong) > 1e-2
+
+
+def test_determinism_1d(cat):
+    say("determinism_1d")
+    import torch
+    wl = W.WORKLOADS[W.HEADLINE].with_(B=2)
+    inp = W.make_inputs(wl, batch=2)
+    plan = cat.cat_plan_create("1d", wl.dtype, 2, wl.N, wl.D, wl.H)
+    args = [to_dev(a, wl.dtype) for a in (inp.X, inp.W_A, inp.W_V)]
+    O1 = cat.cat_forward_1d(plan, *args)
+    O2 = cat.cat_forward_1d(plan, *args)
+    torch.cuda.synchronize()
+    assert torch.equal(O1, O2)
+
+
+# ------------------------------------------------------------------ 2D
+GRIDS = [(1, 1), (2, 3), (3, 4), (4, 4), (6, 8), (8, 8), (12, 12), (16, 16)]
+
+
+@pytest.mark.parametrize("Hg,Wg", GRIDS + [(32, 32)])
+def test_scores_2d(cat, Hg, Wg):
+    say("scores_2d", Hg, Wg)
+    import torch
+    B, D, H = 2, 16, 2
+    rng = np.random.default_rng(Hg * 100 + Wg)
+    Q = (rng.standard_normal((B, Hg * Wg, D)) * 0.5).astype(np.float32)
+    K = (rng.standard_normal((B, Hg * Wg, D)) * 0.5).astype(np.float32)
+    plan = cat.cat_plan_create("2d", "f32", B, Hg * Wg, D, H, Hg, Wg)
+    probs = to_np(cat.cat_step_scores_2d(plan, torch.from_numpy(Q).cuda(), torch.from_numpy(K).cuda()))
+    a = oracle.scores_bccb_2d(Q, K, Hg, Wg, H)
+    ref = oracle.softmax(a.reshape(B, H, -1))
+    assert_parity(probs, ref, "f32", "a*")
+
+
+@pytest.mark.parametrize("Hg,Wg,dtype", [(g[0], g[1], "f32") for g in GRIDS] + [(12, 12, "bf16"), (32, 32, "f32")])
+def test_mix_2d(cat, Hg, Wg, dtype):
+    say("mix_2d", Hg, Wg, dtype)
+    import torch
+    B, D, H = 2, 16, 2
+    N = Hg * Wg
+    rng = np.random.default_rng(N + 3)
+    logits = (rng.standard_normal((B, H, N)) * 2).astype(np.float32)
+    V = rng.standard_normal((B, N, D)).astype(np.float32)
+    if dtype == "bf16":
+        V = W.bf16_bits_to_f32(W.round_bf16_bits(V)).reshape(V.shape)
+    plan = cat.cat_plan_create("2d", dtype, B, N, D, H, Hg, Wg)
+    O = to_np(cat.cat_step_mix(plan, torch.from_numpy(logits).cuda(), to_dev(V, dtype)))
+    ref = oracle.bccb_2d(oracle.softmax(logits).reshape(B, H, Hg, Wg), V)
+    assert_parity(O, ref, dtype, "O")
+
+
+@pytest.mark.parametrize("B,Hg,Wg,D,H,dtype,ss", [(1, 3, 4, 16, 2, "f32", 1.0), (2, 8, 8, 32, 2, "f32", 0.3),
+                                                  (2, 12, 12, 48, 3, "bf16", 0.3), (1, 6, 8, 64, 1, "f32", 1.0),
+                                                  (2, 16, 16, 64, 4, "bf16", 0.2)])
+def test_forward_2d_small(cat, B, Hg, Wg, D, H, dtype, ss):
+    say("forward_2d", B, Hg, Wg, D, H, dtype, ss)
+    import torch
+    inp = rng_inputs_2d(9, B, Hg, Wg, D, H, dtype, score_scale=ss)
+    plan = cat.cat_plan_create("2d", dtype, B, Hg * Wg, D, H, Hg, Wg)
+    O = cat.cat_forward_bccb_2d(plan, *[to_dev(a, dtype) for a in (inp.X, inp.W_Q, inp.W_K, inp.W_V)])
+    torch.cuda.synchronize()
+    ref = oracle.cat_forward_bccb_2d(inp.X, inp.W_Q, inp.W_K, inp.W_V, Hg, Wg, H)["O"]
+    assert_parity(to_np(O), ref, dtype, "O")
+
+
+def test_forward_2d_workload_full_size(cat):
+    """96x96 grid, B=8, D=384, H=6, bf16, at full size; the oracle recomputes
+    two (image, head) slices end to end."""
+    wl = W.WORKLOADS["bccb2d_1536px_96x96"]
+    say("forward_2d_workload", wl.name)
+    import torch
+    inp = W.make_inputs(wl)
+    plan = cat.cat_plan_create("2d", wl.dtype, wl.B, wl.N, wl.D, wl.H, wl.Hg, wl.Wg)
+    O = cat.cat_forward_bccb_2d(plan, *[to_dev(a, wl.dtype) for a in (inp.X, inp.W_Q, inp.W_K, inp.W_V)])
+    torch.cuda.synchronize()
+    O = to_np(O)
+    assert np.all(np.isfinite(O))
+    d = wl.d
+    for b, h in [(0, 0), (wl.B - 1, wl.H - 1)]:
+        hs = slice(h * d, (h + 1) * d)
+        ref = oracle.cat_forward_bccb_2d(inp.X[b:b + 1], inp.W_Q[:, hs], inp.W_K[:, hs], inp.W_V[:, hs],
+                                         wl.Hg, wl.Wg, 1)["O"][0]
+        assert_parity(O[b][:, hs], ref, wl.dtype, f"b={b} h={h}")
+
+
+def test_determinism_2d(cat):
+    say("determinism_2d")
+    import torch
+    inp = rng_inputs_2d(2, 2, 12, 12, 48, 3, "bf16", score_scale=0.3)
+    plan = cat.cat_plan_create("2d", "bf16", 2, 144, 48, 3, 12, 12)
+    args = [to_dev(a, "bf16") for a in (inp.X, inp.W_Q, inp.W_K, inp.W_V)]
+    O1 = cat.cat_forward_bccb_2d(plan, *args)
+    O2 = cat.cat_forward_bccb_2d(plan, *args)
+    torch.cuda.synchronize()
+    assert torch.equal(O1, O2)
+
+
+# ------------------------------------------------------------------ errors
+def test_plan_kind_mismatch_and_misalignment(cat):
+    say("errors")
+    import ctypes
+    import torch
+    plan = cat.cat_plan_create("1d", "f32", 1, 64, 64, 4)
+    X = torch.zeros(1, 64, 64, device="cuda")
+    Wv = torch.zeros(64, 64, device="cuda")
+    ws = cat.alloc_workspace(plan)
+    lib = cat.lib()
+    st = lib.cat_forward_bccb_2d(ctypes.c_void_p(plan.handle), ctypes.c_void_p(X.data_ptr()),
+                                 ctypes.c_void_p(Wv.data_ptr()), ctypes.c_void_p(Wv.data_ptr()),
+                                 ctypes.c_void_p(Wv.data_ptr()), ctypes.c_void_p(X.data_ptr()),
+                                 ctypes.c_void_p(ws.data_ptr()), None)
+    assert st == -5
+    flat = torch.zeros(64 * 64 + 4, device="cuda")
+    st = lib.cat_forward_1d(ctypes.c_void_p(plan.handle), ctypes.c_void_p(flat.data_ptr() + 4),
+                            ctypes.c_void_p(Wv.data_ptr()), ctypes.c_void_p(Wv.data_ptr()),
+                            ctypes.c_void_p(X.data_ptr()), ctypes.c_void_p(ws.data_ptr()), None)
+    assert st == -1
+    assert "aligned" in lib.cat_last_error().decode()
+
+
+def test_empty_batch_is_a_no_op(cat):
+    say("empty_batch")
+    import torch
+    for kind, extra in [("1d", {}), ("2d", {"Hg": 8, "Wg": 8})]:
+        plan = cat.cat_plan_create(kind, "f32", 0, 64, 32, 2, **extra)
+        X = torch.empty(0, 64, 32, device="cuda")
+        Wm = torch.zeros(32, 32, device="cuda")
+        if kind == "1d":
+            O = cat.cat_forward_1d(plan, X, torch.zeros(32, 2, device="cuda"), Wm)
+        else:
+            O = cat.cat_forward_bccb_2d(plan, X, Wm, Wm, Wm)
+        torch.cuda.synchronize()
+        assert O.shape == (0, 64, 32)

@@ -54,8 +54,10 @@ def kernel_model(wl, L: int, ngrp: int):
     spec_bytes = BH * L * 8
     m = {}
     if wl.kind == "1d":
-        m["project"] = dict(bytes=T * D * s + D * (D + H) * s + T * D * s + BH * N * 4,
-                            flops=2.0 * T * D * (D + H), unit="mfma_bf16" if s == 2 else "mfma_f32")
+        m["project"] = dict(bytes=T * D * s + D * D * s + T * D * s,
+                            flops=2.0 * T * D * D, unit="mfma_bf16" if s == 2 else "mfma_f32")
+        m["zproj"] = dict(bytes=T * D * s + D * H * s + BH * N * 4,
+                          flops=2.0 * T * D * H, unit="mfma_bf16" if s == 2 else "mfma_f32")
         m["spectrum"] = dict(bytes=BH * N * 4 + spec_bytes, flops=BH * (fft_flops(L) + 4.0 * N), unit="valu_f32")
     else:
         m["project"] = dict(bytes=T * D * s + 3 * D * D * s + 2 * T * D * 4 + T * D * s,
@@ -278,7 +280,19 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rotate-bytes", type=float, default=2.5 * MALL_BYTES,
                     help="total bytes of rotated buffer sets (defeats the Infinity Cache)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB, --steps times (for scaling HBM counters)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        n = args.copy_calibration << 20
+        src = [torch.ones(n, dtype=torch.uint8, device="cuda") for _ in range(2)]
+        dst = [torch.empty_like(src[0]) for _ in range(2)]
+        for i in range(args.steps):
+            dst[i % 2].copy_(src[i % 2])
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": args.steps}), flush=True)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path has no multi-GPU mode. "
               "Run with --gpus 1.", file=sys.stderr)

@@ -28,6 +28,9 @@ struct cat_plan_s {
   float2* d_tw;      // 1D inter-pass twiddles, L entries (null in 2D)
   size_t off_V, off_z, off_Q, off_K, off_part, off_spec, ws_bytes;
   bool debug_sync;
+  // side stream for the score chain (projection + spectrum), joined by events
+  hipStream_t side = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   // per-kernel timing slots: ev[slot][kernel][start/stop]
   static constexpr int kSlots = 512, kMaxK = 4;
   bool timing = false;
@@ -95,12 +98,14 @@ struct KernelMark {
       ++pl->calls;
     }
   }
-  void begin(int k) {
-    if (slot) (void)hipEventRecord(slot[2 * k], s);
+  void begin(int k, hipStream_t st) {
+    if (slot) (void)hipEventRecord(slot[2 * k], st);
   }
-  void end(int k) {
-    if (slot) (void)hipEventRecord(slot[2 * k + 1], s);
+  void end(int k, hipStream_t st) {
+    if (slot) (void)hipEventRecord(slot[2 * k + 1], st);
   }
+  void begin(int k) { begin(k, s); }
+  void end(int k) { end(k, s); }
 };
 
 }  // namespace
@@ -176,7 +181,7 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
   pl->G = G;
   pl->ng = d2 / G;
   int Gs = 1;
-  while ((2 * Gs) * T <= 128 && (2 * Gs) * (line_bytes + T * sizeof(float)) <= 96 * 1024) Gs *= 2;
+  while ((2 * Gs) * T <= 64 && spectrum_lds_bytes(g, 2 * Gs) <= 96 * 1024) Gs *= 2;
   pl->Gs = Gs;
   pl->npair = d2;
   pl->ppg = 4;
@@ -215,7 +220,7 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
       for (int k1 = 0; k1 < g.L1; ++k1) {
         const long e = ((long)n2 * k1) % pl->L;
         const double ang = two_pi * (double)e / (double)pl->L;
-        tw[(size_t)n2 * g.L1 + k1] = make_float2((float)std::cos(ang), (float)(-std::sin(ang)));
+        tw[(size_t)k1 * g.L2 + n2] = make_float2((float)std::cos(ang), (float)(-std::sin(ang)));
       }
     hipError_t e = hipMalloc(&pl->d_tw, tw.size() * sizeof(float2));
     if (e != hipSuccess) {
@@ -229,12 +234,20 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
       return hip_fail(e, "hipMemcpy(twiddles)");
     }
   }
-  hipError_t e = prepare_kernels(g, (size_t)G * line_bytes, (size_t)Gs * (line_bytes + T * sizeof(float)),
-                                 2 * line_bytes);
+  hipError_t e = prepare_kernels(g, (size_t)G * line_bytes, spectrum_lds_bytes(g, Gs), 2 * line_bytes);
+  if (e == hipSuccess && p->kind == CAT_1D) e = prepare_zproj(pl->et, (int)p->D);
   if (e != hipSuccess) {
     if (pl->d_tw) (void)hipFree(pl->d_tw);
     delete pl;
     return hip_fail(e, "hipFuncSetAttribute");
+  }
+  // default-priority side stream and fork/join events (no timing)
+  e = hipStreamCreateWithFlags(&pl->side, hipStreamNonBlocking);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&pl->ev_fork, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&pl->ev_join, hipEventDisableTiming);
+  if (e != hipSuccess) {
+    cat_plan_destroy(pl);
+    return hip_fail(e, "side stream / events");
   }
   *out = pl;
   g_err.clear();
@@ -245,6 +258,9 @@ cat_status cat_plan_destroy(cat_plan plan) {
   if (plan == nullptr) return CAT_OK;
   if (plan->d_tw) (void)hipFree(plan->d_tw);
   free_events(plan);
+  if (plan->ev_fork) (void)hipEventDestroy(plan->ev_fork);
+  if (plan->ev_join) (void)hipEventDestroy(plan->ev_join);
+  if (plan->side) (void)hipStreamDestroy(plan->side);
   delete plan;
   return CAT_OK;
 }
@@ -272,7 +288,7 @@ cat_status cat_plan_set_timing(cat_plan plan, int enable) {
 
 cat_status cat_plan_kernel_times(cat_plan plan, double* total_ms, int64_t* calls, int* nkernels) {
   if (!plan || !total_ms || !calls || !nkernels) return fail(CAT_ERR_INVALID_ARG, "NULL argument");
-  const int nk = plan->p.kind == CAT_1D ? 3 : 4;
+  const int nk = 4;
   *nkernels = nk;
   for (int k = 0; k < 8; ++k) {
     total_ms[k] = 0.0;
@@ -382,32 +398,56 @@ cat_status cat_forward_1d(cat_plan plan, const void* X, const void* W_A, const v
   cat_status st = check_ptrs({X, W_A, W_V, O, workspace});
   if (st != CAT_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipStream_t side = plan->side;
   void* Vb = ws_at(workspace, plan->off_V);
   float* z = reinterpret_cast<float*>(ws_at(workspace, plan->off_z));
   KernelMark mk(plan, s);
 
+  // fork: the score chain (X W_A -> softmax -> spectrum) runs on the side
+  // stream while the value projection runs on the caller's stream
+  hipError_t e = hipEventRecord(plan->ev_fork, s);
+  if (e == hipSuccess) e = hipStreamWaitEvent(side, plan->ev_fork, 0);
+  if (e != hipSuccess) return hip_fail(e, "fork");
+
+  ZprojArgs za{};
+  za.X = X;
+  za.W = W_A;
+  za.z = z;
+  za.M = (int)(plan->p.B * plan->p.N);
+  za.K = (int)plan->p.D;
+  za.H = (int)plan->p.H;
+  za.Ntok = (int)plan->p.N;
+  mk.begin(1, side);
+  e = launch_zproj(plan->et, za, side);
+  mk.end(1, side);
+  if (e != hipSuccess) return hip_fail(e, "score projection launch");
+  if ((st = check_sync(plan, "score projection")) != CAT_OK) return st;
+
+  SpecArgs sa = spec_base(plan, workspace);
+  sa.logits = z;
+  mk.begin(2, side);
+  e = launch_spectrum(plan->geom, 0, sa, side);
+  mk.end(2, side);
+  if (e != hipSuccess) return hip_fail(e, "spectrum launch");
+  if ((st = check_sync(plan, "spectrum")) != CAT_OK) return st;
+  e = hipEventRecord(plan->ev_join, side);
+  if (e != hipSuccess) return hip_fail(e, "join record");
+
   GemmArgs ga = gemm_base(plan, X);
-  ga.nseg = 2;
+  ga.nseg = 1;
   ga.seg[0] = seg(W_V, Vb, (int)plan->p.D, 0, OUT_BLOCKED, 2 * plan->G);
-  ga.seg[1] = seg(W_A, z, (int)plan->p.H, 1, OUT_HEADMAJOR, 1);
   mk.begin(0);
-  hipError_t e = launch_gemm(plan->et, ga, s);
+  e = launch_gemm(plan->et, ga, s);
   mk.end(0);
   if (e != hipSuccess) return hip_fail(e, "projection launch");
   if ((st = check_sync(plan, "projection")) != CAT_OK) return st;
 
-  SpecArgs sa = spec_base(plan, workspace);
-  sa.logits = z;
-  mk.begin(1);
-  e = launch_spectrum(plan->geom, 0, sa, s);
-  mk.end(1);
-  if (e != hipSuccess) return hip_fail(e, "spectrum launch");
-  if ((st = check_sync(plan, "spectrum")) != CAT_OK) return st;
-
+  e = hipStreamWaitEvent(s, plan->ev_join, 0);
+  if (e != hipSuccess) return hip_fail(e, "join wait");
   ConvArgs ca = conv_base(plan, Vb, sa.spec, O);
-  mk.begin(2);
+  mk.begin(3);
   e = launch_conv(plan->geom, plan->et, ca, s);
-  mk.end(2);
+  mk.end(3);
   if (e != hipSuccess) return hip_fail(e, "fft-conv launch");
   return check_sync(plan, "fft-conv");
 }
@@ -482,9 +522,19 @@ cat_status cat_step_project(cat_plan plan, const void* X, const void* W_A, const
   const int D = (int)plan->p.D;
   GemmArgs ga = gemm_base(plan, X);
   if (!two_d) {
-    ga.nseg = 2;
+    // the forward path's kernels: value GEMM + the narrow score projection
+    ga.nseg = 1;
     ga.seg[0] = seg(W_V, V, D, 0, OUT_ROWMAJOR, 1);
-    ga.seg[1] = seg(W_A, z, (int)plan->p.H, 1, OUT_HEADMAJOR, 1);
+    ZprojArgs za{};
+    za.X = X;
+    za.W = W_A;
+    za.z = reinterpret_cast<float*>(z);
+    za.M = (int)(plan->p.B * plan->p.N);
+    za.K = D;
+    za.H = (int)plan->p.H;
+    za.Ntok = (int)plan->p.N;
+    hipError_t ez = launch_zproj(plan->et, za, s);
+    if (ez != hipSuccess) return hip_fail(ez, "score projection launch");
   } else {
     ga.nseg = 3;
     ga.seg[0] = seg(W_A, z, D, 1, OUT_ROWMAJOR, 1);

@@ -46,6 +46,12 @@ size_t line_lds_bytes(const LineGeom& g) {
   return (size_t)LP * sizeof(float2);
 }
 
+size_t spectrum_lds_bytes(const LineGeom& g, int G) {
+  const Entry* e = find_entry(g);
+  const int T = e ? e->T : 1;
+  return (size_t)G * line_lds_bytes(g) + (size_t)((G * T + 1) / 2) * sizeof(float2);
+}
+
 int line_threads(const LineGeom& g) {
   const Entry* e = find_entry(g);
   return e ? e->T : 0;
@@ -73,7 +79,7 @@ hipError_t launch_spectrum(const LineGeom& g, int mode, const SpecArgs& a, hipSt
   if (!fn) return hipErrorInvalidValue;
   SpecArgs aa = a;
   aa.log2G = ilog2(aa.G);
-  const size_t lds = (size_t)aa.G * line_lds_bytes(g) + (size_t)aa.G * e->T * sizeof(float);
+  const size_t lds = spectrum_lds_bytes(g, aa.G);
   const int blocks = (aa.BH + aa.G - 1) / aa.G;
   hipLaunchKernelGGL(fn, dim3(blocks), dim3(aa.G * e->T), lds, s, aa);
   return hipGetLastError();

@@ -20,6 +20,29 @@ enum ElemType : int { ET_F32 = 0, ET_BF16 = 1 };
 //   HEADMAJOR: out[(b * ncols + n) * Ntok + tok] (score logits, [B][H][N])
 enum OutLayout : int { OUT_ROWMAJOR = 0, OUT_BLOCKED = 1, OUT_HEADMAJOR = 2 };
 
+// Division by a runtime-invariant divisor as a multiply-high and a shift
+// (round-up magic number; exact for 0 <= x < 2^31 and 1 <= div < 2^31).
+struct FastDiv {
+  uint32_t div, mul, shr;
+};
+inline FastDiv make_fastdiv(uint32_t d) {
+  FastDiv f;
+  f.div = d;
+  uint32_t s = 0;
+  while ((uint64_t(1) << s) < d) ++s;
+  f.shr = s;
+  f.mul = (uint32_t)(((uint64_t(1) << 32) * ((uint64_t(1) << s) - d)) / d + 1);
+  return f;
+}
+__host__ __device__ inline uint32_t fastdiv(uint32_t x, const FastDiv& f) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint32_t t = __umulhi(x, f.mul);
+#else
+  const uint32_t t = (uint32_t)(((uint64_t)x * f.mul) >> 32);
+#endif
+  return (t + x) >> f.shr;
+}
+
 struct GemmSeg {
   const void* W;  // [K][ncols] row-major, same element type as X
   void* out;
@@ -27,7 +50,10 @@ struct GemmSeg {
   int out_f32;  // 1: fp32 output; 0: the input element type
   int layout;   // OutLayout
   int cg;       // channels per group (BLOCKED)
-  int ntiles;   // filled by the launcher
+  // filled by the launcher
+  int ntiles;
+  int cr, cc;   // output chunk shape (rows x cols, one 16-byte store)
+  FastDiv fd_cg;
 };
 
 struct GemmArgs {
@@ -35,12 +61,26 @@ struct GemmArgs {
   int M, K;
   int Ntok, H, d;
   int nseg;
-  int ncoltiles;  // filled by the launcher
+  // filled by the launcher
+  int ncoltiles;
+  FastDiv fd_ntok, fd_d;
   GemmSeg seg[3];
 };
 
 // Launch Y_s = X . W_s for every segment s; returns hipSuccess or the launch error.
 hipError_t launch_gemm(int et, GemmArgs args, hipStream_t stream);
+
+// Score projection z [B][H][Ntok] (fp32) = X . W_A, W_A [K][H].
+struct ZprojArgs {
+  const void* X;
+  const void* W;
+  float* z;
+  int M, K, H, Ntok;
+  FastDiv fd_ntok;  // filled by the launcher
+};
+hipError_t launch_zproj(int et, ZprojArgs args, hipStream_t stream);
+size_t zproj_lds_bytes(int et, int K);
+hipError_t prepare_zproj(int et, int K);
 
 // Softmax + spectrum of one line per (batch, head).
 //   mode 0: input logits [BH][N] (fp32, spatial, not yet scaled)
@@ -101,6 +141,8 @@ bool geom_supported(const LineGeom& g);
 // LDS bytes of one transform line and the threads per line.
 size_t line_lds_bytes(const LineGeom& g);
 int line_threads(const LineGeom& g);
+// LDS bytes of a spectrum workgroup of G lines (lines, reduction scratch).
+size_t spectrum_lds_bytes(const LineGeom& g, int G);
 
 hipError_t launch_spectrum(const LineGeom& g, int mode, const SpecArgs& a, hipStream_t s);
 hipError_t launch_conv(const LineGeom& g, int et, const ConvArgs& a, hipStream_t s);

@@ -35,8 +35,11 @@
  *
  * Calls
  * -----
- * Forward calls only enqueue kernels on `stream` (a hipStream_t passed as
- * void*; NULL is the default stream).  They never allocate, never
+ * Forward calls only enqueue work ordered after everything already queued on
+ * `stream` (a hipStream_t passed as void*; NULL is the default stream), and
+ * everything queued on `stream` afterwards runs after it.  Inside a call the
+ * 1D path forks the score chain onto a plan-owned side stream with an event
+ * and joins it back before the fft-conv kernel.  Calls never allocate, never
  * synchronise, and return as soon as the work is queued.  A plan owns small
  * device tables created at plan creation; the workspace (size from
  * cat_plan_workspace_size) holds the intermediates and is owned by the
@@ -120,7 +123,7 @@ cat_status cat_forward_bccb_2d(cat_plan plan, const void* X, const void* W_Q, co
  * stream, into plan-owned slots (events are created here, not in the
  * forward calls; at most 512 calls are kept, older ones are overwritten).
  * Enabling resets the slots.  cat_plan_kernel_times waits for the recorded
- * events and returns, per kernel of the path in launch order (1D:
+ * events and returns, per kernel of the path (1D: value projection, score
  * projection, spectrum, fft-conv; 2D: projection, scores, spectrum,
  * fft-conv), the summed milliseconds and the number of calls measured;
  * *nkernels receives the number of kernels (arrays hold at least 8). */

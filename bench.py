@@ -156,10 +156,10 @@ def run(args):
 
     if wl.kind == "1d":
         plan = cat.cat_plan_create("1d", wl.dtype, wl.B, wl.N, wl.D, wl.H)
-        weights = [dev(inp.W_A), dev(inp.W_V)]
+        weights = [dev(inp.W_A.T), dev(inp.W_V.T)]  # output-major, as a linear layer stores them
     else:
         plan = cat.cat_plan_create("2d", wl.dtype, wl.B, wl.N, wl.D, wl.H, wl.Hg, wl.Wg)
-        weights = [dev(inp.W_Q), dev(inp.W_K), dev(inp.W_V)]
+        weights = [dev(inp.W_Q.T), dev(inp.W_K.T), dev(inp.W_V.T)]
     L, L1, L2 = plan.geometry()
     ws_bytes = plan.workspace_size()
     x0 = dev(inp.X)

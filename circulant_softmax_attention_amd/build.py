@@ -48,15 +48,21 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    """Compile every source and link libcat.so; always rebuilds."""
+def build(verbose: bool = True, only=None) -> str:
+    """Compile every source (or only the sources named in `only`, reusing the
+    other objects of an earlier build) and link libcat.so."""
     if shutil.which(HIPCC) is None and not os.path.exists(HIPCC):
         raise RuntimeError(f"hipcc not found at {HIPCC}")
     os.makedirs(BUILD, exist_ok=True)
+    todo = SOURCES if not only else [s for s in SOURCES if s in only]
     if verbose:
-        print(f"building {LIB} for {ARCH}", flush=True)
-    with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+        print(f"building {LIB} for {ARCH} ({len(todo)} of {len(SOURCES)} sources)", flush=True)
+    with cf.ThreadPoolExecutor(max_workers=len(todo)) as ex:
+        list(ex.map(lambda s: _compile(s, verbose), todo))
+    objs = [os.path.join(BUILD, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+    missing = [o for o in objs if not os.path.exists(o)]
+    if missing:
+        raise RuntimeError(f"objects missing (run a full build): {missing}")
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -67,5 +73,5 @@ def build(verbose: bool = True) -> str:
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, only=sys.argv[1:] or None)
     sys.exit(0)

@@ -235,7 +235,6 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
     }
   }
   hipError_t e = prepare_kernels(g, (size_t)G * line_bytes, spectrum_lds_bytes(g, Gs), 2 * line_bytes);
-  if (e == hipSuccess && p->kind == CAT_1D) e = prepare_zproj(pl->et, (int)p->D);
   if (e != hipSuccess) {
     if (pl->d_tw) (void)hipFree(pl->d_tw);
     delete pl;
@@ -390,12 +389,12 @@ ConvArgs conv_base(const cat_plan_s* pl, const void* Vblk, const float2* spec, v
 
 extern "C" {
 
-cat_status cat_forward_1d(cat_plan plan, const void* X, const void* W_A, const void* W_V, void* O,
+cat_status cat_forward_1d(cat_plan plan, const void* X, const void* W_A_t, const void* W_V_t, void* O,
                           void* workspace, void* stream) {
   if (!plan) return fail(CAT_ERR_INVALID_ARG, "NULL plan");
   if (plan->p.kind != CAT_1D) return fail(CAT_ERR_PLAN_MISMATCH, "plan is not 1D");
   if (plan->p.B == 0) return CAT_OK;  // empty batch: nothing to do
-  cat_status st = check_ptrs({X, W_A, W_V, O, workspace});
+  cat_status st = check_ptrs({X, W_A_t, W_V_t, O, workspace});
   if (st != CAT_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipStream_t side = plan->side;
@@ -411,7 +410,7 @@ cat_status cat_forward_1d(cat_plan plan, const void* X, const void* W_A, const v
 
   ZprojArgs za{};
   za.X = X;
-  za.W = W_A;
+  za.W = W_A_t;
   za.z = z;
   za.M = (int)(plan->p.B * plan->p.N);
   za.K = (int)plan->p.D;
@@ -435,7 +434,7 @@ cat_status cat_forward_1d(cat_plan plan, const void* X, const void* W_A, const v
 
   GemmArgs ga = gemm_base(plan, X);
   ga.nseg = 1;
-  ga.seg[0] = seg(W_V, Vb, (int)plan->p.D, 0, OUT_BLOCKED, 2 * plan->G);
+  ga.seg[0] = seg(W_V_t, Vb, (int)plan->p.D, 0, OUT_BLOCKED, 2 * plan->G);
   mk.begin(0);
   e = launch_gemm(plan->et, ga, s);
   mk.end(0);
@@ -452,12 +451,12 @@ cat_status cat_forward_1d(cat_plan plan, const void* X, const void* W_A, const v
   return check_sync(plan, "fft-conv");
 }
 
-cat_status cat_forward_bccb_2d(cat_plan plan, const void* X, const void* W_Q, const void* W_K,
-                               const void* W_V, void* O, void* workspace, void* stream) {
+cat_status cat_forward_bccb_2d(cat_plan plan, const void* X, const void* W_Q_t, const void* W_K_t,
+                               const void* W_V_t, void* O, void* workspace, void* stream) {
   if (!plan) return fail(CAT_ERR_INVALID_ARG, "NULL plan");
   if (plan->p.kind != CAT_BCCB_2D) return fail(CAT_ERR_PLAN_MISMATCH, "plan is not 2D");
   if (plan->p.B == 0) return CAT_OK;  // empty batch: nothing to do
-  cat_status st = check_ptrs({X, W_Q, W_K, W_V, O, workspace});
+  cat_status st = check_ptrs({X, W_Q_t, W_K_t, W_V_t, O, workspace});
   if (st != CAT_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   void* Vb = ws_at(workspace, plan->off_V);
@@ -469,9 +468,9 @@ cat_status cat_forward_bccb_2d(cat_plan plan, const void* X, const void* W_Q, co
 
   GemmArgs ga = gemm_base(plan, X);
   ga.nseg = 3;
-  ga.seg[0] = seg(W_Q, Qb, D, 1, OUT_BLOCKED, 2);
-  ga.seg[1] = seg(W_K, Kb, D, 1, OUT_BLOCKED, 2);
-  ga.seg[2] = seg(W_V, Vb, D, 0, OUT_BLOCKED, 2 * plan->G);
+  ga.seg[0] = seg(W_Q_t, Qb, D, 1, OUT_BLOCKED, 2);
+  ga.seg[1] = seg(W_K_t, Kb, D, 1, OUT_BLOCKED, 2);
+  ga.seg[2] = seg(W_V_t, Vb, D, 0, OUT_BLOCKED, 2 * plan->G);
   mk.begin(0);
   hipError_t e = launch_gemm(plan->et, ga, s);
   mk.end(0);
@@ -511,12 +510,12 @@ cat_status cat_forward_bccb_2d(cat_plan plan, const void* X, const void* W_Q, co
   return check_sync(plan, "fft-conv");
 }
 
-cat_status cat_step_project(cat_plan plan, const void* X, const void* W_A, const void* W_K,
-                            const void* W_V, void* V, void* z, void* K_out, void* stream) {
+cat_status cat_step_project(cat_plan plan, const void* X, const void* W_A_t, const void* W_K_t,
+                            const void* W_V_t, void* V, void* z, void* K_out, void* stream) {
   if (!plan) return fail(CAT_ERR_INVALID_ARG, "NULL plan");
   if (plan->p.B == 0) return CAT_OK;
   const bool two_d = plan->p.kind == CAT_BCCB_2D;
-  cat_status st = two_d ? check_ptrs({X, W_A, W_K, W_V, V, z, K_out}) : check_ptrs({X, W_A, W_V, V, z});
+  cat_status st = two_d ? check_ptrs({X, W_A_t, W_K_t, W_V_t, V, z, K_out}) : check_ptrs({X, W_A_t, W_V_t, V, z});
   if (st != CAT_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int D = (int)plan->p.D;
@@ -524,10 +523,10 @@ cat_status cat_step_project(cat_plan plan, const void* X, const void* W_A, const
   if (!two_d) {
     // the forward path's kernels: value GEMM + the narrow score projection
     ga.nseg = 1;
-    ga.seg[0] = seg(W_V, V, D, 0, OUT_ROWMAJOR, 1);
+    ga.seg[0] = seg(W_V_t, V, D, 0, OUT_ROWMAJOR, 1);
     ZprojArgs za{};
     za.X = X;
-    za.W = W_A;
+    za.W = W_A_t;
     za.z = reinterpret_cast<float*>(z);
     za.M = (int)(plan->p.B * plan->p.N);
     za.K = D;
@@ -537,9 +536,9 @@ cat_status cat_step_project(cat_plan plan, const void* X, const void* W_A, const
     if (ez != hipSuccess) return hip_fail(ez, "score projection launch");
   } else {
     ga.nseg = 3;
-    ga.seg[0] = seg(W_A, z, D, 1, OUT_ROWMAJOR, 1);
-    ga.seg[1] = seg(W_K, K_out, D, 1, OUT_ROWMAJOR, 1);
-    ga.seg[2] = seg(W_V, V, D, 0, OUT_ROWMAJOR, 1);
+    ga.seg[0] = seg(W_A_t, z, D, 1, OUT_ROWMAJOR, 1);
+    ga.seg[1] = seg(W_K_t, K_out, D, 1, OUT_ROWMAJOR, 1);
+    ga.seg[2] = seg(W_V_t, V, D, 0, OUT_ROWMAJOR, 1);
   }
   hipError_t e = launch_gemm(plan->et, ga, s);
   if (e != hipSuccess) return hip_fail(e, "projection launch");

@@ -5,22 +5,29 @@
 // "Method details / Overall framework"); the ViT circulant attention projects
 // them to Q, K and V (Vision Transformers are Circulant Attention Learners,
 // "Circulant Attention: attention rebuilt with the FFT").  Both are one dense
-// contraction Y = X W with X [M = B N][K = D] and W [D][ncols], run here as a
-// single launch over up to three column segments (e.g. W_V and W_A), each
-// written in the layout its consumer reads.
+// contraction Y = X W with X [M = B N][K = D] and W given output-major,
+// Wt [ncols][K] (each output channel's K weights contiguous, the layout a
+// linear layer stores), run here as a single launch over up to three column
+// segments, each written in the layout its consumer reads.
 //
 // Tiling: 128 x 128 output tile per 256-thread workgroup (4 waves, 2 x 2),
 // each wave a 64 x 64 block of 16 x 16 MFMA tiles.  K is walked in tiles of
-// two "K-chunks"; a K-chunk is what one lane feeds the MFMA from 16 bytes:
+// 128 bytes per row (64 bf16 or 32 fp32 values), i.e. eight 16-byte chunks;
+// a chunk is what one lane feeds the MFMA:
 //   bf16: 8 values -> v_mfma_f32_16x16x32_bf16 (fp32 accumulate)
 //   fp32: 4 values -> four v_mfma_f32_16x16x4_f32
 // Every lane reads the same K positions for its A row and its B column, so
 // the order in which the hardware walks K inside a chunk does not matter.
-// X tiles are staged row-major in LDS; W tiles are transposed on the way in
-// (K contiguous per output column) so both operands are 16-byte LDS reads.
-// LDS is double buffered: the next tile is fetched into registers while the
-// current one is multiplied.  The finished tile goes through LDS once more so
-// that every output store is a 16-byte vector in the consumer's layout.
+//
+// Staging: both operand tiles are row-major [row][K] (X rows, Wt rows), so
+// every chunk is one 16-byte load straight from global memory into LDS
+// (LDS-DMA, no register round trip).  Rows are unpadded and the 16-byte
+// position of chunk c in row r is c ^ (r % 8), which spreads the 16 rows of
+// one fragment read over distinct banks.  Two LDS stages: the DMA of tile
+// k + 1 is in flight while tile k is multiplied.  Rows beyond M or ncols are
+// clamped to the last valid row (their results are never stored); a K tail
+// that does not fill a tile goes through registers with the missing chunks
+// zeroed.
 #include "cat_common.hpp"
 #include "cat_internal.hpp"
 
@@ -32,18 +39,35 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4;
 namespace {
 
 constexpr int BM = 128, BN = 128, NTHR = 256;
-constexpr int CP = BN + 4;  // fp32 pitch of the staged output tile
+constexpr int ROWB = 128;                 // bytes of one row of a K tile
+constexpr int STAGE = (BM + BN) * ROWB;   // one LDS stage: A rows, then B rows
+constexpr int SMEM = 2 * STAGE;
 
 template <int ET>
 struct GemmCfg {
   static constexpr int ESZ = ET == ET_F32 ? 4 : 2;
-  static constexpr int VE = 16 / ESZ;   // elements per 16-byte chunk
-  static constexpr int KC = 4 * VE;     // K per chunk across the 4 lane groups
-  static constexpr int BK = 2 * KC;     // K per LDS tile
-  static constexpr int PITCH = BK + VE; // LDS row pitch (elements), +16 B pad
-  static constexpr int TILE_BYTES = 2 * 2 * 128 * PITCH * ESZ;  // A and B, two buffers
-  static constexpr int SMEM = TILE_BYTES > BM * CP * 4 ? TILE_BYTES : BM * CP * 4;
+  static constexpr int VE = 16 / ESZ;  // elements per 16-byte chunk
+  static constexpr int BK = 8 * VE;    // K per tile (8 chunks, 128 bytes per row)
 };
+
+// LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// One 16-byte LDS-DMA load per lane: lane l's 16 bytes at g land at LDS byte
+// address lds + 16 l (lds must be uniform across the wave).  Written as
+// inline asm so that the compiler adds no waits of its own before later LDS
+// reads; completion is awaited explicitly with wait_vmem_all.
+// M0 is reserved by the compiler, which only sets it right before the few
+// instructions that read it, so declaring it clobbered here is safe.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+__device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Element offset of output (row, col) of segment s.
 __device__ __forceinline__ size_t out_index(const GemmSeg& s, const GemmArgs& a, int row, int col) {
@@ -62,14 +86,12 @@ __device__ __forceinline__ size_t out_index(const GemmSeg& s, const GemmArgs& a,
 template <int ET>
 __global__ __launch_bounds__(NTHR, 2) void gemm_xw_kernel(GemmArgs a) {
   using C = GemmCfg<ET>;
-  constexpr int VE = C::VE, KC = C::KC, BK = C::BK, PITCH = C::PITCH;
+  constexpr int VE = C::VE, BK = C::BK;
   using elem_t = typename std::conditional<ET == ET_F32, float, uint16_t>::type;
-  __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
-  elem_t* As0 = reinterpret_cast<elem_t*>(smem);
-  elem_t* Bs0 = As0 + 2 * 128 * PITCH;
-  float* Cs = reinterpret_cast<float*>(smem);
+  __shared__ __attribute__((aligned(16))) char smem[SMEM];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
   const int q = xcd_remap(blockIdx.x, gridDim.x);
@@ -84,97 +106,51 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_xw_kernel(GemmArgs a) {
   const int m0 = rt * BM, n0 = ct * BN;
   const int M = a.M, K = a.K, ncols = sg.ncols;
 
-  // A: 4 chunks of 16 B per thread: row = tid/8 + 32 i, column chunk tid % 8.
-  constexpr int ACH = BK / VE;
-  static_assert(ACH == 8, "A staging assumes 8 chunks per row");
-  const int arow = tid / ACH, akc = tid % ACH;
-  const elem_t* aptr[4];
-  bool aok[4];
+  // Chunk slot s = tid + 256 i (i < 4) of an operand tile is row s / 8,
+  // 16-byte position s % 8, and holds K-chunk (s % 8) ^ (row % 8) -- the same
+  // chunk for all four i, since row % 8 = (tid / 8) % 8.
+  const int kch = ((tid & 7) ^ ((tid >> 3) & 7)) * VE;
+  const elem_t* asrc[4];
+  const elem_t* bsrc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int m = m0 + arow + 32 * i;
-    aok[i] = m < M;
-    aptr[i] = reinterpret_cast<const elem_t*>(a.X) + (size_t)(aok[i] ? m : 0) * K + akc * VE;
+    const int r = (tid >> 3) + 32 * i;
+    const int am = m0 + r < M ? m0 + r : M - 1;
+    const int bn = n0 + r < ncols ? n0 + r : ncols - 1;
+    asrc[i] = reinterpret_cast<const elem_t*>(a.X) + (size_t)am * K + kch;
+    bsrc[i] = reinterpret_cast<const elem_t*>(sg.W) + (size_t)bn * K + kch;
   }
-  // B: every thread reads 16 consecutive K rows of 4 bytes (2 bf16 columns or
-  // 1 fp32 column), so a wave covers 256 contiguous bytes of one W row per
-  // load; it then writes its columns K-contiguous into LDS.
-  constexpr int CPT = 4 / C::ESZ;
-  constexpr int NCT = BN / CPT;
-  constexpr int KR = BK / (NTHR / NCT);
-  static_assert(KR == 16, "B staging assumes 16 K rows per thread");
-  const int bc = tid % NCT, bk = tid / NCT;
-  const int bn = n0 + bc * CPT;
-  const elem_t* bptr = reinterpret_cast<const elem_t*>(sg.W) + (size_t)(KR * bk) * ncols + bn;
+  const uint32_t lds0 = lds_addr(smem) + (uint32_t)wave * 64 * 16;
 
-  uint4 ra[4];
-  uint32_t rb[KR];
-  // Interior tiles (the whole tile inside M x ncols, K a multiple of BK, W
-  // rows 4-byte aligned) take unconditional vector loads; edge tiles take the
-  // guarded path.  The choice is uniform across the workgroup, so the loads
-  // of a tile are issued back to back with no waits between them.
-  const bool full = (m0 + BM <= M) && (n0 + BN <= ncols) && (K % BK == 0) &&
-                    (ET == ET_F32 || (ncols % 2) == 0);
-  auto gload_full = [&](int k0) {
+  // Stage tile kt into LDS stage st.
+  auto issue = [&](int kt, int st) {
+    const int k0 = kt * BK;
+    if (k0 + BK <= K) {
+      const uint32_t base = lds0 + (uint32_t)(st * STAGE);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ra[i] = *reinterpret_cast<const uint4*>(aptr[i] + k0);
-    const elem_t* bp = bptr + (size_t)k0 * ncols;
+      for (int i = 0; i < 4; ++i) lds_dma16(asrc[i] + k0, base + i * NTHR * 16);
 #pragma unroll
-    for (int r = 0; r < KR; ++r) rb[r] = *reinterpret_cast<const uint32_t*>(bp + (size_t)r * ncols);
-  };
-  // Edge tiles: indices are clamped into range so every load is in bounds,
-  // and out-of-range elements are zeroed by a select (no branch per load).
-  auto gload_edge = [&](int k0) {
-    const int kk = k0 + akc * VE < K ? k0 : K - VE - akc * VE;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint4 v = *reinterpret_cast<const uint4*>(aptr[i] + kk);
-      ra[i] = (aok[i] & (k0 + akc * VE < K)) ? v : make_uint4(0, 0, 0, 0);
-    }
-    const elem_t* W = reinterpret_cast<const elem_t*>(sg.W);
-#pragma unroll
-    for (int r = 0; r < KR; ++r) {
-      const int k = k0 + KR * bk + r;
-      const int kc = k < K ? k : K - 1;
-      elem_t tmp[CPT];
-#pragma unroll
-      for (int j = 0; j < CPT; ++j) {
-        const int n = bn + j < ncols ? bn + j : ncols - 1;
-        const elem_t v = W[(size_t)kc * ncols + n];
-        tmp[j] = ((k < K) & (bn + j < ncols)) ? v : elem_t(0);
-      }
-      rb[r] = *reinterpret_cast<uint32_t*>(tmp);
-    }
-  };
-  auto gload = [&](int k0) {
-    if (full) gload_full(k0);
-    else gload_edge(k0);
-  };
-  auto lstore = [&](int buf) {
-    elem_t* As = As0 + buf * 128 * PITCH;
-    elem_t* Bs = Bs0 + buf * 128 * PITCH;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&As[(arow + 32 * i) * PITCH + akc * VE]) = ra[i];
-    if constexpr (ET == ET_F32) {
-      uint4* dst = reinterpret_cast<uint4*>(&Bs[bc * PITCH + KR * bk]);
-#pragma unroll
-      for (int q4 = 0; q4 < KR / 4; ++q4)
-        dst[q4] = make_uint4(rb[4 * q4], rb[4 * q4 + 1], rb[4 * q4 + 2], rb[4 * q4 + 3]);
+      for (int i = 0; i < 4; ++i) lds_dma16(bsrc[i] + k0, base + BM * ROWB + i * NTHR * 16);
     } else {
-      // rb[r] holds (column n, column n+1) of row r; split into two K-runs
-      uint32_t c0[KR / 2], c1[KR / 2];
+      // K tail: chunks at or beyond K are zero in both operands
+      const bool ok = k0 + kch < K;
+      const int kk = ok ? k0 : -kch;  // row start when the chunk is out of range
+      uint4 va[4], vb[4];
 #pragma unroll
-      for (int r = 0; r < KR / 2; ++r) {
-        const uint32_t a0 = rb[2 * r], a1 = rb[2 * r + 1];
-        c0[r] = (a0 & 0xffffu) | (a1 << 16);
-        c1[r] = (a0 >> 16) | (a1 & 0xffff0000u);
+      for (int i = 0; i < 4; ++i) {
+        const uint4 v = *reinterpret_cast<const uint4*>(asrc[i] + kk);
+        va[i] = ok ? v : make_uint4(0, 0, 0, 0);
       }
-      uint4* d0 = reinterpret_cast<uint4*>(&Bs[(2 * bc) * PITCH + KR * bk]);
-      uint4* d1 = reinterpret_cast<uint4*>(&Bs[(2 * bc + 1) * PITCH + KR * bk]);
-      d0[0] = make_uint4(c0[0], c0[1], c0[2], c0[3]);
-      d0[1] = make_uint4(c0[4], c0[5], c0[6], c0[7]);
-      d1[0] = make_uint4(c1[0], c1[1], c1[2], c1[3]);
-      d1[1] = make_uint4(c1[4], c1[5], c1[6], c1[7]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4 v = *reinterpret_cast<const uint4*>(bsrc[i] + kk);
+        vb[i] = ok ? v : make_uint4(0, 0, 0, 0);
+      }
+      uint4* dst = reinterpret_cast<uint4*>(smem + st * STAGE) + tid;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[i * NTHR] = va[i];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[BM * 8 + i * NTHR] = vb[i];
     }
   };
 
@@ -184,193 +160,170 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_xw_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = (K + BK - 1) / BK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
   const int lrow = lane & 15, lgrp = lane >> 4;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    const elem_t* As = As0 + buf * 128 * PITCH;
-    const elem_t* Bs = Bs0 + buf * 128 * PITCH;
-    if (kt + 1 < nk) gload((kt + 1) * BK);
+  const int sw = lrow & 7;  // row % 8 of every fragment row this lane reads
+  auto compute = [&](int st) {
+    const char* sa = smem + st * STAGE + (wm * 64 + lrow) * ROWB;
+    const char* sb = smem + st * STAGE + BM * ROWB + (wn * 64 + lrow) * ROWB;
 #pragma unroll
-    for (int kc = 0; kc < BK / KC; ++kc) {
+    for (int kc = 0; kc < 2; ++kc) {
+      const int pos = ((kc * 4 + lgrp) ^ sw) * 16;
       uint4 af[4], bfr[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        af[i] = *reinterpret_cast<const uint4*>(&As[(wm * 64 + 16 * i + lrow) * PITCH + kc * KC + lgrp * VE]);
+      for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const uint4*>(sa + 16 * i * ROWB + pos);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bfr[j] = *reinterpret_cast<const uint4*>(&Bs[(wn * 64 + 16 * j + lrow) * PITCH + kc * KC + lgrp * VE]);
+      for (int j = 0; j < 4; ++j) bfr[j] = *reinterpret_cast<const uint4*>(sb + 16 * j * ROWB + pos);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
+          // W fragment as the MFMA's A operand, X fragment as B: the 16 x 16
+          // result is Y^T, so each lane ends with 4 consecutive channels of
+          // one token (see the stores below)
           if constexpr (ET == ET_F32) {
             const float4 fa = *reinterpret_cast<const float4*>(&af[i]);
             const float4 fb = *reinterpret_cast<const float4*>(&bfr[j]);
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa.x, fb.x, acc[i][j], 0, 0, 0);
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa.y, fb.y, acc[i][j], 0, 0, 0);
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa.z, fb.z, acc[i][j], 0, 0, 0);
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa.w, fb.w, acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(fb.x, fa.x, acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(fb.y, fa.y, acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(fb.z, fa.z, acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(fb.w, fa.w, acc[i][j], 0, 0, 0);
           } else {
             const bf16x8 va = *reinterpret_cast<const bf16x8*>(&af[i]);
             const bf16x8 vb = *reinterpret_cast<const bf16x8*>(&bfr[j]);
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, vb, acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, va, acc[i][j], 0, 0, 0);
           }
         }
     }
-    if (kt + 1 < nk) lstore(buf ^ 1);
+  };
+
+  // Tile kt lives in stage kt % 2.  At the top of step kt every wave has its
+  // own DMA of tile kt complete and, after the barrier, all of them have
+  // finished multiplying tile kt - 1, whose stage then receives tile kt + 1.
+  const int nk = (K + BK - 1) / BK;
+  issue(0, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_vmem_all();
     __syncthreads();
+    if (kt + 1 < nk) issue(kt + 1, (kt + 1) & 1);
+    compute(kt & 1);
   }
-
-  // Stage the tile: 16x16 MFMA result layout is column (lane & 15),
-  // rows 4 (lane >> 4) + v.
+  // Result layout (16 x 16 MFMA, A = W rows, B = X rows): lane (lrow, lgrp)
+  // holds Y[token][channel] for token = tile row base + lrow and the four
+  // channels 4 lgrp + v, v = 0..3, of each 16-channel block.  Written
+  // straight from registers: 8 (bf16) or 16 (fp32) bytes per lane, and the 16
+  // lanes of a channel block cover 16 consecutive tokens.
+  const bool f32out = ET == ET_F32 || sg.out_f32;
+  const bool quad = (sg.layout == OUT_ROWMAJOR && (ncols & 3) == 0) ||
+                    (sg.layout == OUT_BLOCKED && (a.d & 3) == 0 && (sg.cg & 3) == 0);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i) {
+    const int token = m0 + wm * 64 + 16 * i + lrow;
+    if (token >= M) continue;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 4; ++j) {
+      const int ch0 = n0 + wn * 64 + 16 * j + 4 * lgrp;
+      if (ch0 >= ncols) continue;
+      const floatx4 v = acc[i][j];
+      if (quad && ch0 + 4 <= ncols) {
+        const size_t o = out_index(sg, a, token, ch0);
+        if (f32out) *reinterpret_cast<float4*>(reinterpret_cast<float*>(sg.out) + o) = make_float4(v[0], v[1], v[2], v[3]);
+        else *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(sg.out) + o) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+      } else if (sg.layout == OUT_BLOCKED && sg.cg == 2 && ch0 + 4 <= ncols) {
+        // channel pairs (d is even, so a pair never straddles two heads)
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
-        Cs[(wm * 64 + 16 * i + 4 * lgrp + v) * CP + wn * 64 + 16 * j + lrow] = acc[i][j][v];
-  __syncthreads();
-
-  // One 16-byte output chunk of cr x cc elements per step; the chunk shape
-  // keeps the chunk contiguous in the segment's layout.
-  const bool f32out = sg.out_f32 || ET == ET_F32;
-  const int VO = f32out ? 4 : 8;
-  const int cr = sg.cr, cc = sg.cc;
-  const int nrc = BM / cr, ncc = BN / cc;
-  const bool rows_fast = sg.layout != OUT_ROWMAJOR;
-  for (int qq = tid; qq < nrc * ncc; qq += NTHR) {
-    const int rci = rows_fast ? qq % nrc : qq / ncc;
-    const int cci = rows_fast ? qq / nrc : qq % ncc;
-    const int lr = rci * cr, lc = cci * cc;
-    const int row = m0 + lr, col = n0 + lc;
-    if (row >= M || col >= ncols) continue;
-    bool vec = row + cr <= M && col + cc <= ncols;
-    size_t idx = out_index(sg, a, row, col);
-    if (vec && cr > 1) {
-      const uint32_t b = fastdiv((uint32_t)row, a.fd_ntok);
-      vec = (uint32_t)(row + cr - 1) < (b + 1) * (uint32_t)a.Ntok;  // same sequence
-    }
-    vec = vec && (idx % VO) == 0;
-    if (vec) {
-      float v[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        if (e < VO) {
-          const int er = e / cc, ec = e - er * cc;
-          v[e] = Cs[(lr + er) * CP + lc + ec];
+        for (int p = 0; p < 2; ++p) {
+          const size_t o = out_index(sg, a, token, ch0 + 2 * p);
+          if (f32out) *reinterpret_cast<float2*>(reinterpret_cast<float*>(sg.out) + o) = make_float2(v[2 * p], v[2 * p + 1]);
+          else reinterpret_cast<uint32_t*>(sg.out)[o / 2] = pack_bf16x2(v[2 * p], v[2 * p + 1]);
         }
-      }
-      if (f32out) {
-        *reinterpret_cast<float4*>(reinterpret_cast<float*>(sg.out) + idx) = make_float4(v[0], v[1], v[2], v[3]);
       } else {
-        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(sg.out) + idx) =
-            make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
-                       pack_bf16x2(v[6], v[7]));
-      }
-    } else {
-      for (int er = 0; er < cr; ++er)
-        for (int ec = 0; ec < cc; ++ec) {
-          const int r = row + er, c = col + ec;
-          if (r >= M || c >= ncols) continue;
-          const size_t o = out_index(sg, a, r, c);
-          const float val = Cs[(lr + er) * CP + lc + ec];
-          if (f32out) reinterpret_cast<float*>(sg.out)[o] = val;
-          else reinterpret_cast<uint16_t*>(sg.out)[o] = to_bf16(val);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (ch0 + e >= ncols) break;
+          const size_t o = out_index(sg, a, token, ch0 + e);
+          if (f32out) reinterpret_cast<float*>(sg.out)[o] = v[e];
+          else reinterpret_cast<uint16_t*>(sg.out)[o] = to_bf16(v[e]);
         }
+      }
     }
   }
 }
 
 // Score projection z[b][h][tok] = sum_k X[b tok][k] W_A[k][h] for the H score
-// columns, on MFMA in 16-column blocks (CAT: Circular-Convolutional Attention
-// for Sub-Quadratic Transformers, "Key designs: circulant attention matrix
-// construction": Z = X W_A, one column per head).  A narrow product, so it is
-// a kernel of its own: each wave owns 16 tokens and reads its A fragments
-// straight from global memory; the 16 W_A columns of the block sit in LDS,
-// transposed to K-contiguous rows, zero beyond H and beyond K.
+// columns (CAT: Circular-Convolutional Attention for Sub-Quadratic
+// Transformers, "Key designs: circulant attention matrix construction":
+// Z = X W_A, one column per head).  A narrow product that only streams X, so
+// it is a kernel of its own with no LDS staging: a workgroup owns 16 tokens x
+// 16 heads, its four waves split K (wave w takes K-chunks w, w + 4, ...), each
+// lane loads its X row chunk and its W_A^T row chunk straight from global
+// memory (W_A^T [H][K] is small and stays in cache), and the four partial
+// 16 x 16 products are summed through LDS.
 constexpr int ZP_WAVES = 4;
+constexpr int ZP_MAXSTEP = 8;  // K-chunks per wave per batch of loads
 template <int ET>
 __global__ __launch_bounds__(ZP_WAVES * 64) void zproj_kernel(ZprojArgs a) {
   using C = GemmCfg<ET>;
-  constexpr int VE = C::VE, KC = C::KC;
+  constexpr int VE = C::VE, KC = 4 * VE;  // K per MFMA step
   using elem_t = typename std::conditional<ET == ET_F32, float, uint16_t>::type;
-  extern __shared__ __attribute__((aligned(16))) char zsm[];
-  elem_t* Bt = reinterpret_cast<elem_t*>(zsm);
+  __shared__ float red[ZP_WAVES - 1][4][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K = a.K, H = a.H, M = a.M;
-  const int nsteps = (K + KC - 1) / KC;
-  const int PB = nsteps * KC + VE;  // LDS pitch (elements) of one column
-  const int c0 = blockIdx.y * 16;
-  const elem_t* W = reinterpret_cast<const elem_t*>(a.W);
-  // W_A[:, c0 : c0+16] -> Bt[c][k], sixteen loads in flight per thread
-  const int total = 16 * PB;
-  for (int base = 0; base < total; base += 16 * ZP_WAVES * 64) {
-    elem_t v[16];
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int idx = base + u * ZP_WAVES * 64 + tid;
-      const int c = idx / PB, k = idx - c * PB;
-      const bool ok = (idx < total) & (k < K) & (c0 + c < H);
-      const int kk = k < K ? k : K - 1, cc = c0 + c < H ? c0 + c : H - 1;
-      const elem_t w = W[(size_t)kk * H + cc];
-      v[u] = ok ? w : elem_t(0);
-    }
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int idx = base + u * ZP_WAVES * 64 + tid;
-      if (idx < total) Bt[idx] = v[u];
-    }
-  }
-  __syncthreads();
-
   const int lrow = lane & 15, lgrp = lane >> 4;
-  const int row = blockIdx.x * (ZP_WAVES * 16) + wave * 16 + lrow;
-  const int rowc = row < M ? row : M - 1;
-  const elem_t* xr = reinterpret_cast<const elem_t*>(a.X) + (size_t)rowc * K;
+  const int r0 = blockIdx.x * 16, c0 = blockIdx.y * 16;
+  const int row = r0 + lrow < M ? r0 + lrow : M - 1;
+  const int head = c0 + lrow < H ? c0 + lrow : H - 1;  // clamped: extra columns are never stored
+  const elem_t* xr = reinterpret_cast<const elem_t*>(a.X) + (size_t)row * K;
+  const elem_t* wr = reinterpret_cast<const elem_t*>(a.W) + (size_t)head * K;
+  const int nsteps = (K + KC - 1) / KC;
   floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
-  constexpr int ZB = 16;  // A fragments in flight per wave
-  for (int s0 = 0; s0 < nsteps; s0 += ZB) {
-    uint4 af[ZB];
+  for (int s0 = wave; s0 < nsteps; s0 += ZP_WAVES * ZP_MAXSTEP) {
+    uint4 af[ZP_MAXSTEP], bf[ZP_MAXSTEP];
 #pragma unroll
-    for (int u = 0; u < ZB; ++u) {
-      const int k = (s0 + u) * KC + lgrp * VE;
-      const int kk = k < K ? k : K - VE;
-      const uint4 v = *reinterpret_cast<const uint4*>(xr + kk);
-      af[u] = ((k < K) & (row < M)) ? v : make_uint4(0, 0, 0, 0);
+    for (int u = 0; u < ZP_MAXSTEP; ++u) {
+      const int st = s0 + u * ZP_WAVES;
+      const int k = st * KC + lgrp * VE;
+      const bool ok = (st < nsteps) & (k < K);
+      const int kk = ok ? k : 0;  // K % VE == 0: an in-range chunk ends by K
+      const uint4 va = *reinterpret_cast<const uint4*>(xr + kk);
+      const uint4 vb = *reinterpret_cast<const uint4*>(wr + kk);
+      af[u] = ok ? va : make_uint4(0, 0, 0, 0);
+      bf[u] = ok ? vb : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int u = 0; u < ZB; ++u) {
-      if (s0 + u < nsteps) {
-        const uint4 bv = *reinterpret_cast<const uint4*>(&Bt[lrow * PB + (s0 + u) * KC + lgrp * VE]);
-        if constexpr (ET == ET_F32) {
-          const float4 fa = *reinterpret_cast<const float4*>(&af[u]);
-          const float4 fb = *reinterpret_cast<const float4*>(&bv);
-          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa.x, fb.x, acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa.y, fb.y, acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa.z, fb.z, acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa.w, fb.w, acc, 0, 0, 0);
-        } else {
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(&af[u]),
-                                                        *reinterpret_cast<const bf16x8*>(&bv), acc, 0, 0, 0);
-        }
+    for (int u = 0; u < ZP_MAXSTEP; ++u) {
+      if constexpr (ET == ET_F32) {
+        const float4 fa = *reinterpret_cast<const float4*>(&af[u]);
+        const float4 fb = *reinterpret_cast<const float4*>(&bf[u]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa.x, fb.x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa.y, fb.y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa.z, fb.z, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa.w, fb.w, acc, 0, 0, 0);
+      } else {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(&af[u]),
+                                                      *reinterpret_cast<const bf16x8*>(&bf[u]), acc, 0, 0, 0);
       }
     }
   }
-  // result: column (lane & 15) = head c0 + lrow, rows 4 lgrp + v of the wave
-  const int head = c0 + lrow;
-  if (head < H) {
+  if (wave > 0) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int r = blockIdx.x * (ZP_WAVES * 16) + wave * 16 + 4 * lgrp + v;
-      if (r < M) {
-        const uint32_t b = fastdiv((uint32_t)r, a.fd_ntok);
-        const uint32_t tok = (uint32_t)r - b * (uint32_t)a.Ntok;
-        a.z[((size_t)b * H + head) * a.Ntok + tok] = acc[v];
+    for (int v = 0; v < 4; ++v) red[wave - 1][v][lane] = acc[v];
+  }
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int w = 0; w < ZP_WAVES - 1; ++w)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[v] += red[w][v][lane];
+    // result: column (lane & 15) = head c0 + lrow, rows 4 lgrp + v
+    if (c0 + lrow < H) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = r0 + 4 * lgrp + v;
+        if (r < M) {
+          const uint32_t b = fastdiv((uint32_t)r, a.fd_ntok);
+          const uint32_t tok = (uint32_t)r - b * (uint32_t)a.Ntok;
+          a.z[((size_t)b * H + c0 + lrow) * a.Ntok + tok] = acc[v];
+        }
       }
     }
   }
@@ -386,20 +339,7 @@ hipError_t launch_gemm(int et, GemmArgs a, hipStream_t stream) {
     GemmSeg& g = a.seg[s];
     g.ntiles = (g.ncols + BN - 1) / BN;
     a.ncoltiles += g.ntiles;
-    const int vo = (g.out_f32 || et == ET_F32) ? 4 : 8;
-    if (g.layout == OUT_ROWMAJOR) {
-      g.cr = 1;
-      g.cc = vo;
-    } else if (g.layout == OUT_HEADMAJOR) {
-      g.cr = vo;
-      g.cc = 1;
-    } else if (g.cg >= vo) {
-      g.cr = 1;
-      g.cc = vo;
-    } else {
-      g.cr = vo / g.cg;
-      g.cc = g.cg;
-    }
+    if (g.layout == OUT_BLOCKED && (g.cg <= 0 || a.d % g.cg != 0)) return hipErrorInvalidValue;
     g.fd_cg = make_fastdiv((uint32_t)(g.cg > 0 ? g.cg : 1));
   }
   const int rowtiles = (a.M + BM - 1) / BM;
@@ -412,28 +352,13 @@ hipError_t launch_gemm(int et, GemmArgs a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-size_t zproj_lds_bytes(int et, int K) {
-  const int esz = et == ET_F32 ? 4 : 2;
-  const int kc = 4 * (16 / esz), ve = 16 / esz;
-  const int pb = ((K + kc - 1) / kc) * kc + ve;
-  return (size_t)16 * pb * esz;
-}
-
-hipError_t prepare_zproj(int et, int K) {
-  const size_t bytes = zproj_lds_bytes(et, K);
-  if (et == ET_F32)
-    return hipFuncSetAttribute((const void*)zproj_kernel<ET_F32>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-  return hipFuncSetAttribute((const void*)zproj_kernel<ET_BF16>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-}
-
 hipError_t launch_zproj(int et, ZprojArgs a, hipStream_t stream) {
   a.fd_ntok = make_fastdiv((uint32_t)a.Ntok);
-  const dim3 grid((unsigned)((a.M + ZP_WAVES * 16 - 1) / (ZP_WAVES * 16)), (unsigned)((a.H + 15) / 16));
-  const size_t lds = zproj_lds_bytes(et, a.K);
+  const dim3 grid((unsigned)((a.M + 15) / 16), (unsigned)((a.H + 15) / 16));
   if (et == ET_F32) {
-    hipLaunchKernelGGL(zproj_kernel<ET_F32>, grid, dim3(ZP_WAVES * 64), lds, stream, a);
+    hipLaunchKernelGGL(zproj_kernel<ET_F32>, grid, dim3(ZP_WAVES * 64), 0, stream, a);
   } else {
-    hipLaunchKernelGGL(zproj_kernel<ET_BF16>, grid, dim3(ZP_WAVES * 64), lds, stream, a);
+    hipLaunchKernelGGL(zproj_kernel<ET_BF16>, grid, dim3(ZP_WAVES * 64), 0, stream, a);
   }
   return hipGetLastError();
 }

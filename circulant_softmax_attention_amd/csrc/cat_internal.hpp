@@ -44,7 +44,7 @@ __host__ __device__ inline uint32_t fastdiv(uint32_t x, const FastDiv& f) {
 }
 
 struct GemmSeg {
-  const void* W;  // [K][ncols] row-major, same element type as X
+  const void* W;  // Wt [ncols][K] row-major (output-major), same element type as X
   void* out;
   int ncols;
   int out_f32;  // 1: fp32 output; 0: the input element type
@@ -52,7 +52,6 @@ struct GemmSeg {
   int cg;       // channels per group (BLOCKED)
   // filled by the launcher
   int ntiles;
-  int cr, cc;   // output chunk shape (rows x cols, one 16-byte store)
   FastDiv fd_cg;
 };
 
@@ -70,7 +69,7 @@ struct GemmArgs {
 // Launch Y_s = X . W_s for every segment s; returns hipSuccess or the launch error.
 hipError_t launch_gemm(int et, GemmArgs args, hipStream_t stream);
 
-// Score projection z [B][H][Ntok] (fp32) = X . W_A, W_A [K][H].
+// Score projection z [B][H][Ntok] (fp32) = X . W_A, given as W_A^T [H][K].
 struct ZprojArgs {
   const void* X;
   const void* W;
@@ -79,8 +78,6 @@ struct ZprojArgs {
   FastDiv fd_ntok;  // filled by the launcher
 };
 hipError_t launch_zproj(int et, ZprojArgs args, hipStream_t stream);
-size_t zproj_lds_bytes(int et, int K);
-hipError_t prepare_zproj(int et, int K);
 
 // Softmax + spectrum of one line per (batch, head).
 //   mode 0: input logits [BH][N] (fp32, spatial, not yet scaled)

@@ -54,10 +54,9 @@ def kernel_model(wl, L: int, ngrp: int):
     spec_bytes = BH * L * 8
     m = {}
     if wl.kind == "1d":
-        m["project"] = dict(bytes=T * D * s + D * D * s + T * D * s,
-                            flops=2.0 * T * D * D, unit="mfma_bf16" if s == 2 else "mfma_f32")
-        m["zproj"] = dict(bytes=T * D * s + D * H * s + BH * N * 4,
-                          flops=2.0 * T * D * H, unit="mfma_bf16" if s == 2 else "mfma_f32")
+        # X read once, W_V and W_A, V written (storage dtype) and z written (fp32)
+        m["project"] = dict(bytes=T * D * s + D * (D + H) * s + T * D * s + BH * N * 4,
+                            flops=2.0 * T * D * (D + H), unit="mfma_bf16" if s == 2 else "mfma_f32")
         m["spectrum"] = dict(bytes=BH * N * 4 + spec_bytes, flops=BH * (fft_flops(L) + 4.0 * N), unit="valu_f32")
     else:
         m["project"] = dict(bytes=T * D * s + 3 * D * D * s + 2 * T * D * 4 + T * D * s,
@@ -81,7 +80,7 @@ def source_hash(files):
 KERNEL_SOURCES = {
     "fftconv": ["circulant_softmax_attention_amd/csrc/cat_fftconv.hpp", "circulant_softmax_attention_amd/csrc/cat_fft.hpp",
                 "circulant_softmax_attention_amd/csrc/cat_common.hpp"],
-    "project": ["circulant_softmax_attention_amd/csrc/cat_gemm.hip"],
+    "project": ["circulant_softmax_attention_amd/csrc/cat_gemm.hip", "circulant_softmax_attention_amd/csrc/cat_common.hpp"],
 }
 KERNEL_SOURCES["spectrum"] = KERNEL_SOURCES["fftconv"]
 KERNEL_SOURCES["scores"] = KERNEL_SOURCES["fftconv"]

@@ -30,7 +30,7 @@ EXPORTS = ["cat_plan_create", "cat_plan_destroy", "cat_plan_workspace_size", "ca
            "cat_forward_1d", "cat_forward_bccb_2d", "cat_status_string", "cat_last_error",
            "cat_plan_set_timing", "cat_plan_kernel_times",
            "cat_step_project", "cat_step_spectrum", "cat_step_mix", "cat_step_scores_2d"]
-KERNELS_1D = ["project", "zproj", "spectrum", "fftconv"]
+KERNELS_1D = ["project", "spectrum", "fftconv"]
 KERNELS_2D = ["project", "scores", "spectrum", "fftconv"]
 
 

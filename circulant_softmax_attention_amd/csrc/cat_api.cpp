@@ -28,9 +28,7 @@ struct cat_plan_s {
   float2* d_tw;      // 1D inter-pass twiddles, L entries (null in 2D)
   size_t off_V, off_z, off_Q, off_K, off_part, off_spec, ws_bytes;
   bool debug_sync;
-  // side stream for the score chain (projection + spectrum), joined by events
-  hipStream_t side = nullptr;
-  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  int num_cu;        // compute units of the device current at plan creation
   // per-kernel timing slots: ev[slot][kernel][start/stop]
   static constexpr int kSlots = 512, kMaxK = 4;
   bool timing = false;
@@ -98,14 +96,12 @@ struct KernelMark {
       ++pl->calls;
     }
   }
-  void begin(int k, hipStream_t st) {
-    if (slot) (void)hipEventRecord(slot[2 * k], st);
+  void begin(int k) {
+    if (slot) (void)hipEventRecord(slot[2 * k], s);
   }
-  void end(int k, hipStream_t st) {
-    if (slot) (void)hipEventRecord(slot[2 * k + 1], st);
+  void end(int k) {
+    if (slot) (void)hipEventRecord(slot[2 * k + 1], s);
   }
-  void begin(int k) { begin(k, s); }
-  void end(int k) { end(k, s); }
 };
 
 }  // namespace
@@ -140,6 +136,9 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
   if (p->D % 8 != 0) return fail(CAT_ERR_INVALID_ARG, "D must be a multiple of 8");
   if (p->B * p->N * p->D >= (int64_t(1) << 31) || p->B * p->H > (int64_t(1) << 24))
     return fail(CAT_ERR_UNSUPPORTED, "problem too large (B*N*D must be < 2^31)");
+
+  if (p->kind == CAT_1D && p->H > 32)
+    return fail(CAT_ERR_UNSUPPORTED, "1D supports at most 32 heads (score projection fused into the GEMM)");
 
   LineGeom g{};
   if (p->kind == CAT_1D) {
@@ -213,6 +212,12 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
 
   // device tables and kernel attributes (first HIP calls)
   pl->d_tw = nullptr;
+  {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      n = 0;
+    pl->num_cu = n;
+  }
   if (g.twiddled) {
     std::vector<float2> tw((size_t)pl->L);
     const double two_pi = 6.283185307179586476925286766559;
@@ -240,14 +245,7 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
     delete pl;
     return hip_fail(e, "hipFuncSetAttribute");
   }
-  // default-priority side stream and fork/join events (no timing)
-  e = hipStreamCreateWithFlags(&pl->side, hipStreamNonBlocking);
-  if (e == hipSuccess) e = hipEventCreateWithFlags(&pl->ev_fork, hipEventDisableTiming);
-  if (e == hipSuccess) e = hipEventCreateWithFlags(&pl->ev_join, hipEventDisableTiming);
-  if (e != hipSuccess) {
-    cat_plan_destroy(pl);
-    return hip_fail(e, "side stream / events");
-  }
+
   *out = pl;
   g_err.clear();
   return CAT_OK;
@@ -257,9 +255,6 @@ cat_status cat_plan_destroy(cat_plan plan) {
   if (plan == nullptr) return CAT_OK;
   if (plan->d_tw) (void)hipFree(plan->d_tw);
   free_events(plan);
-  if (plan->ev_fork) (void)hipEventDestroy(plan->ev_fork);
-  if (plan->ev_join) (void)hipEventDestroy(plan->ev_join);
-  if (plan->side) (void)hipStreamDestroy(plan->side);
   delete plan;
   return CAT_OK;
 }
@@ -287,7 +282,7 @@ cat_status cat_plan_set_timing(cat_plan plan, int enable) {
 
 cat_status cat_plan_kernel_times(cat_plan plan, double* total_ms, int64_t* calls, int* nkernels) {
   if (!plan || !total_ms || !calls || !nkernels) return fail(CAT_ERR_INVALID_ARG, "NULL argument");
-  const int nk = 4;
+  const int nk = plan->p.kind == CAT_1D ? 3 : 4;
   *nkernels = nk;
   for (int k = 0; k < 8; ++k) {
     total_ms[k] = 0.0;
@@ -344,6 +339,7 @@ GemmArgs gemm_base(const cat_plan_s* pl, const void* X) {
   a.Ntok = (int)pl->p.N;
   a.H = (int)pl->p.H;
   a.d = pl->d;
+  a.num_cu = pl->num_cu;
   return a;
 }
 
@@ -397,56 +393,35 @@ cat_status cat_forward_1d(cat_plan plan, const void* X, const void* W_A_t, const
   cat_status st = check_ptrs({X, W_A_t, W_V_t, O, workspace});
   if (st != CAT_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  hipStream_t side = plan->side;
   void* Vb = ws_at(workspace, plan->off_V);
   float* z = reinterpret_cast<float*>(ws_at(workspace, plan->off_z));
   KernelMark mk(plan, s);
 
-  // fork: the score chain (X W_A -> softmax -> spectrum) runs on the side
-  // stream while the value projection runs on the caller's stream
-  hipError_t e = hipEventRecord(plan->ev_fork, s);
-  if (e == hipSuccess) e = hipStreamWaitEvent(side, plan->ev_fork, 0);
-  if (e != hipSuccess) return hip_fail(e, "fork");
-
-  ZprojArgs za{};
-  za.X = X;
-  za.W = W_A_t;
-  za.z = z;
-  za.M = (int)(plan->p.B * plan->p.N);
-  za.K = (int)plan->p.D;
-  za.H = (int)plan->p.H;
-  za.Ntok = (int)plan->p.N;
-  mk.begin(1, side);
-  e = launch_zproj(plan->et, za, side);
-  mk.end(1, side);
-  if (e != hipSuccess) return hip_fail(e, "score projection launch");
-  if ((st = check_sync(plan, "score projection")) != CAT_OK) return st;
-
-  SpecArgs sa = spec_base(plan, workspace);
-  sa.logits = z;
-  mk.begin(2, side);
-  e = launch_spectrum(plan->geom, 0, sa, side);
-  mk.end(2, side);
-  if (e != hipSuccess) return hip_fail(e, "spectrum launch");
-  if ((st = check_sync(plan, "spectrum")) != CAT_OK) return st;
-  e = hipEventRecord(plan->ev_join, side);
-  if (e != hipSuccess) return hip_fail(e, "join record");
-
+  // V = X W_V (blocked for the transform) and the logits z = X W_A in one pass
   GemmArgs ga = gemm_base(plan, X);
   ga.nseg = 1;
   ga.seg[0] = seg(W_V_t, Vb, (int)plan->p.D, 0, OUT_BLOCKED, 2 * plan->G);
+  ga.Wz = W_A_t;
+  ga.z = z;
+  ga.nz = (int)plan->p.H;
   mk.begin(0);
-  e = launch_gemm(plan->et, ga, s);
+  hipError_t e = launch_gemm(plan->et, ga, s);
   mk.end(0);
   if (e != hipSuccess) return hip_fail(e, "projection launch");
   if ((st = check_sync(plan, "projection")) != CAT_OK) return st;
 
-  e = hipStreamWaitEvent(s, plan->ev_join, 0);
-  if (e != hipSuccess) return hip_fail(e, "join wait");
+  SpecArgs sa = spec_base(plan, workspace);
+  sa.logits = z;
+  mk.begin(1);
+  e = launch_spectrum(plan->geom, 0, sa, s);
+  mk.end(1);
+  if (e != hipSuccess) return hip_fail(e, "spectrum launch");
+  if ((st = check_sync(plan, "spectrum")) != CAT_OK) return st;
+
   ConvArgs ca = conv_base(plan, Vb, sa.spec, O);
-  mk.begin(3);
+  mk.begin(2);
   e = launch_conv(plan->geom, plan->et, ca, s);
-  mk.end(3);
+  mk.end(2);
   if (e != hipSuccess) return hip_fail(e, "fft-conv launch");
   return check_sync(plan, "fft-conv");
 }
@@ -521,19 +496,12 @@ cat_status cat_step_project(cat_plan plan, const void* X, const void* W_A_t, con
   const int D = (int)plan->p.D;
   GemmArgs ga = gemm_base(plan, X);
   if (!two_d) {
-    // the forward path's kernels: value GEMM + the narrow score projection
+    // the forward path's kernel: value GEMM with the fused score projection
     ga.nseg = 1;
     ga.seg[0] = seg(W_V_t, V, D, 0, OUT_ROWMAJOR, 1);
-    ZprojArgs za{};
-    za.X = X;
-    za.W = W_A_t;
-    za.z = reinterpret_cast<float*>(z);
-    za.M = (int)(plan->p.B * plan->p.N);
-    za.K = D;
-    za.H = (int)plan->p.H;
-    za.Ntok = (int)plan->p.N;
-    hipError_t ez = launch_zproj(plan->et, za, s);
-    if (ez != hipSuccess) return hip_fail(ez, "score projection launch");
+    ga.Wz = W_A_t;
+    ga.z = reinterpret_cast<float*>(z);
+    ga.nz = (int)plan->p.H;
   } else {
     ga.nseg = 3;
     ga.seg[0] = seg(W_A_t, z, D, 1, OUT_ROWMAJOR, 1);

@@ -28,6 +28,11 @@
 // clamped to the last valid row (their results are never stored); a K tail
 // that does not fill a tile goes through registers with the missing chunks
 // zeroed.
+//
+// Score projection (1D): the workgroups of the first column tile also
+// multiply their staged X rows by W_A^T (up to 32 heads, staged like a third
+// operand of 32 rows), so z = X W_A costs no extra pass over X.  Each wave
+// takes 32 of its 64 rows for this.
 #include "cat_common.hpp"
 #include "cat_internal.hpp"
 
@@ -38,10 +43,9 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4;
 
 namespace {
 
-constexpr int BM = 128, BN = 128, NTHR = 256;
-constexpr int ROWB = 128;                 // bytes of one row of a K tile
-constexpr int STAGE = (BM + BN) * ROWB;   // one LDS stage: A rows, then B rows
-constexpr int SMEM = 2 * STAGE;
+constexpr int BM = 128, NTHR = 256;
+constexpr int ZR = 32;     // score-projection rows (heads) per stage
+constexpr int ROWB = 128;  // bytes of one row of a K tile
 
 template <int ET>
 struct GemmCfg {
@@ -69,6 +73,24 @@ __device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds) {
 #pragma clang diagnostic pop
 __device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// acc += A^T B over one 16-byte chunk (A, B: 16 rows x chunk each; the
+// result's column index follows B's rows).
+template <int ET>
+__device__ __forceinline__ floatx4 mfma_chunk(const uint4& ra, const uint4& rb, floatx4 acc) {
+  if constexpr (ET == ET_F32) {
+    const float4 fa = *reinterpret_cast<const float4*>(&ra);
+    const float4 fb = *reinterpret_cast<const float4*>(&rb);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa.x, fb.x, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa.y, fb.y, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa.z, fb.z, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa.w, fb.w, acc, 0, 0, 0);
+  } else {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(&ra),
+                                                  *reinterpret_cast<const bf16x8*>(&rb), acc, 0, 0, 0);
+  }
+  return acc;
+}
+
 // Element offset of output (row, col) of segment s.
 __device__ __forceinline__ size_t out_index(const GemmSeg& s, const GemmArgs& a, int row, int col) {
   if (s.layout == OUT_ROWMAJOR) return (size_t)row * s.ncols + col;
@@ -83,10 +105,15 @@ __device__ __forceinline__ size_t out_index(const GemmSeg& s, const GemmArgs& a,
   return (((size_t)(b * a.H + h) * ng + g) * a.Ntok + tok) * s.cg + j;
 }
 
-template <int ET>
+template <int ET, int BN>
 __global__ __launch_bounds__(NTHR, 2) void gemm_xw_kernel(GemmArgs a) {
   using C = GemmCfg<ET>;
   constexpr int VE = C::VE, BK = C::BK;
+  constexpr int STAGE = (BM + BN + ZR) * ROWB;  // one LDS stage: A rows, B rows, W_A^T rows
+  constexpr int SMEM = 2 * STAGE;
+  constexpr int BCH = BN * 8 / NTHR;            // B chunks per thread
+  constexpr int TN = BN / 32;                   // 16-column MFMA blocks per wave
+  static_assert(BCH * NTHR == BN * 8 && TN * 32 == BN, "tile width");
   using elem_t = typename std::conditional<ET == ET_F32, float, uint16_t>::type;
   __shared__ __attribute__((aligned(16))) char smem[SMEM];
 
@@ -106,19 +133,31 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_xw_kernel(GemmArgs a) {
   const int m0 = rt * BM, n0 = ct * BN;
   const int M = a.M, K = a.K, ncols = sg.ncols;
 
-  // Chunk slot s = tid + 256 i (i < 4) of an operand tile is row s / 8,
-  // 16-byte position s % 8, and holds K-chunk (s % 8) ^ (row % 8) -- the same
-  // chunk for all four i, since row % 8 = (tid / 8) % 8.
+  // Chunk slot s = tid + 256 i of an operand tile is row s / 8, 16-byte
+  // position s % 8, and holds K-chunk (s % 8) ^ (row % 8) -- the same chunk
+  // for every i, since row % 8 = (tid / 8) % 8.
   const int kch = ((tid & 7) ^ ((tid >> 3) & 7)) * VE;
   const elem_t* asrc[4];
-  const elem_t* bsrc[4];
+  const elem_t* bsrc[BCH];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = (tid >> 3) + 32 * i;
     const int am = m0 + r < M ? m0 + r : M - 1;
-    const int bn = n0 + r < ncols ? n0 + r : ncols - 1;
     asrc[i] = reinterpret_cast<const elem_t*>(a.X) + (size_t)am * K + kch;
+  }
+#pragma unroll
+  for (int i = 0; i < BCH; ++i) {
+    const int r = (tid >> 3) + 32 * i;
+    const int bn = n0 + r < ncols ? n0 + r : ncols - 1;
     bsrc[i] = reinterpret_cast<const elem_t*>(sg.W) + (size_t)bn * K + kch;
+  }
+  // score projection: W_A^T row tid / 8 (clamped; rows >= nz are never stored)
+  const bool zwg = a.nz > 0 && si == 0 && ct == 0;
+  const int nzb = (a.nz + 15) >> 4;
+  const elem_t* zsrc = reinterpret_cast<const elem_t*>(a.Wz);
+  if (zwg) {
+    const int zr = (tid >> 3) < a.nz ? (tid >> 3) : a.nz - 1;
+    zsrc += (size_t)zr * K + kch;
   }
   const uint32_t lds0 = lds_addr(smem) + (uint32_t)wave * 64 * 16;
 
@@ -130,19 +169,20 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_xw_kernel(GemmArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) lds_dma16(asrc[i] + k0, base + i * NTHR * 16);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) lds_dma16(bsrc[i] + k0, base + BM * ROWB + i * NTHR * 16);
+      for (int i = 0; i < BCH; ++i) lds_dma16(bsrc[i] + k0, base + BM * ROWB + i * NTHR * 16);
+      if (zwg) lds_dma16(zsrc + k0, base + (BM + BN) * ROWB);
     } else {
       // K tail: chunks at or beyond K are zero in both operands
       const bool ok = k0 + kch < K;
       const int kk = ok ? k0 : -kch;  // row start when the chunk is out of range
-      uint4 va[4], vb[4];
+      uint4 va[4], vb[BCH];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const uint4 v = *reinterpret_cast<const uint4*>(asrc[i] + kk);
         va[i] = ok ? v : make_uint4(0, 0, 0, 0);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < BCH; ++i) {
         const uint4 v = *reinterpret_cast<const uint4*>(bsrc[i] + kk);
         vb[i] = ok ? v : make_uint4(0, 0, 0, 0);
       }
@@ -150,49 +190,60 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_xw_kernel(GemmArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) dst[i * NTHR] = va[i];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dst[BM * 8 + i * NTHR] = vb[i];
+      for (int i = 0; i < BCH; ++i) dst[BM * 8 + i * NTHR] = vb[i];
+      if (zwg) {
+        const uint4 v = *reinterpret_cast<const uint4*>(zsrc + kk);
+        dst[(BM + BN) * 8] = ok ? v : make_uint4(0, 0, 0, 0);
+      }
     }
   };
 
-  floatx4 acc[4][4];
+  floatx4 acc[4][TN];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < TN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  // zacc[ii][zb]: tokens of row block 2 wn + ii, heads 16 zb ..
+  floatx4 zacc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) zacc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   const int lrow = lane & 15, lgrp = lane >> 4;
   const int sw = lrow & 7;  // row % 8 of every fragment row this lane reads
   auto compute = [&](int st) {
     const char* sa = smem + st * STAGE + (wm * 64 + lrow) * ROWB;
-    const char* sb = smem + st * STAGE + BM * ROWB + (wn * 64 + lrow) * ROWB;
+    const char* sb = smem + st * STAGE + BM * ROWB + (wn * (BN / 2) + lrow) * ROWB;
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
       const int pos = ((kc * 4 + lgrp) ^ sw) * 16;
-      uint4 af[4], bfr[4];
+      uint4 af[4], bfr[TN];
 #pragma unroll
       for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const uint4*>(sa + 16 * i * ROWB + pos);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) bfr[j] = *reinterpret_cast<const uint4*>(sb + 16 * j * ROWB + pos);
+      for (int j = 0; j < TN; ++j) bfr[j] = *reinterpret_cast<const uint4*>(sb + 16 * j * ROWB + pos);
+      // W fragment as the MFMA's A operand, X fragment as B: the 16 x 16
+      // result is Y^T, so each lane ends with 4 consecutive channels of one
+      // token (see the stores below)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          // W fragment as the MFMA's A operand, X fragment as B: the 16 x 16
-          // result is Y^T, so each lane ends with 4 consecutive channels of
-          // one token (see the stores below)
-          if constexpr (ET == ET_F32) {
-            const float4 fa = *reinterpret_cast<const float4*>(&af[i]);
-            const float4 fb = *reinterpret_cast<const float4*>(&bfr[j]);
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(fb.x, fa.x, acc[i][j], 0, 0, 0);
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(fb.y, fa.y, acc[i][j], 0, 0, 0);
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(fb.z, fa.z, acc[i][j], 0, 0, 0);
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(fb.w, fa.w, acc[i][j], 0, 0, 0);
-          } else {
-            const bf16x8 va = *reinterpret_cast<const bf16x8*>(&af[i]);
-            const bf16x8 vb = *reinterpret_cast<const bf16x8*>(&bfr[j]);
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, va, acc[i][j], 0, 0, 0);
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma_chunk<ET>(bfr[j], af[i], acc[i][j]);
+      if (zwg) {
+        const char* sz = smem + st * STAGE + (BM + BN + lrow) * ROWB + pos;
+#pragma unroll
+        for (int zb = 0; zb < 2; ++zb) {
+          if (zb < nzb) {
+            const uint4 zf = *reinterpret_cast<const uint4*>(sz + 16 * zb * ROWB);
+#pragma unroll
+            for (int ii = 0; ii < 2; ++ii) {
+              const uint4 xa = wn ? af[2 + ii] : af[ii];  // no dynamic register indexing
+              zacc[ii][zb] = mfma_chunk<ET>(zf, xa, zacc[ii][zb]);
+            }
           }
         }
+      }
     }
   };
 
@@ -212,6 +263,25 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_xw_kernel(GemmArgs a) {
   // channels 4 lgrp + v, v = 0..3, of each 16-channel block.  Written
   // straight from registers: 8 (bf16) or 16 (fp32) bytes per lane, and the 16
   // lanes of a channel block cover 16 consecutive tokens.
+  if (zwg) {
+    // z [B][nz][Ntok] fp32: lane holds token lrow of its row block and heads
+    // 16 zb + 4 lgrp + v; the 16 lanes of a head cover 16 consecutive tokens
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii) {
+      const int token = m0 + wm * 64 + 16 * (2 * wn + ii) + lrow;
+      if (token < M) {
+        const uint32_t b = fastdiv((uint32_t)token, a.fd_ntok);
+        const uint32_t tok = (uint32_t)token - b * (uint32_t)a.Ntok;
+#pragma unroll
+        for (int zb = 0; zb < 2; ++zb)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int head = 16 * zb + 4 * lgrp + v;
+            if (head < a.nz) a.z[((size_t)b * a.nz + head) * a.Ntok + tok] = zacc[ii][zb][v];
+          }
+      }
+    }
+  }
   const bool f32out = ET == ET_F32 || sg.out_f32;
   const bool quad = (sg.layout == OUT_ROWMAJOR && (ncols & 3) == 0) ||
                     (sg.layout == OUT_BLOCKED && (a.d & 3) == 0 && (sg.cg & 3) == 0);
@@ -220,8 +290,8 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_xw_kernel(GemmArgs a) {
     const int token = m0 + wm * 64 + 16 * i + lrow;
     if (token >= M) continue;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int ch0 = n0 + wn * 64 + 16 * j + 4 * lgrp;
+    for (int j = 0; j < TN; ++j) {
+      const int ch0 = n0 + wn * (BN / 2) + 16 * j + 4 * lgrp;
       if (ch0 >= ncols) continue;
       const floatx4 v = acc[i][j];
       if (quad && ch0 + 4 <= ncols) {
@@ -249,118 +319,59 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_xw_kernel(GemmArgs a) {
   }
 }
 
-// Score projection z[b][h][tok] = sum_k X[b tok][k] W_A[k][h] for the H score
-// columns (CAT: Circular-Convolutional Attention for Sub-Quadratic
-// Transformers, "Key designs: circulant attention matrix construction":
-// Z = X W_A, one column per head).  A narrow product that only streams X, so
-// it is a kernel of its own with no LDS staging: a workgroup owns 16 tokens x
-// 16 heads, its four waves split K (wave w takes K-chunks w, w + 4, ...), each
-// lane loads its X row chunk and its W_A^T row chunk straight from global
-// memory (W_A^T [H][K] is small and stays in cache), and the four partial
-// 16 x 16 products are summed through LDS.
-constexpr int ZP_WAVES = 4;
-constexpr int ZP_MAXSTEP = 8;  // K-chunks per wave per batch of loads
-template <int ET>
-__global__ __launch_bounds__(ZP_WAVES * 64) void zproj_kernel(ZprojArgs a) {
-  using C = GemmCfg<ET>;
-  constexpr int VE = C::VE, KC = 4 * VE;  // K per MFMA step
-  using elem_t = typename std::conditional<ET == ET_F32, float, uint16_t>::type;
-  __shared__ float red[ZP_WAVES - 1][4][64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int K = a.K, H = a.H, M = a.M;
-  const int lrow = lane & 15, lgrp = lane >> 4;
-  const int r0 = blockIdx.x * 16, c0 = blockIdx.y * 16;
-  const int row = r0 + lrow < M ? r0 + lrow : M - 1;
-  const int head = c0 + lrow < H ? c0 + lrow : H - 1;  // clamped: extra columns are never stored
-  const elem_t* xr = reinterpret_cast<const elem_t*>(a.X) + (size_t)row * K;
-  const elem_t* wr = reinterpret_cast<const elem_t*>(a.W) + (size_t)head * K;
-  const int nsteps = (K + KC - 1) / KC;
-  floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
-  for (int s0 = wave; s0 < nsteps; s0 += ZP_WAVES * ZP_MAXSTEP) {
-    uint4 af[ZP_MAXSTEP], bf[ZP_MAXSTEP];
-#pragma unroll
-    for (int u = 0; u < ZP_MAXSTEP; ++u) {
-      const int st = s0 + u * ZP_WAVES;
-      const int k = st * KC + lgrp * VE;
-      const bool ok = (st < nsteps) & (k < K);
-      const int kk = ok ? k : 0;  // K % VE == 0: an in-range chunk ends by K
-      const uint4 va = *reinterpret_cast<const uint4*>(xr + kk);
-      const uint4 vb = *reinterpret_cast<const uint4*>(wr + kk);
-      af[u] = ok ? va : make_uint4(0, 0, 0, 0);
-      bf[u] = ok ? vb : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int u = 0; u < ZP_MAXSTEP; ++u) {
-      if constexpr (ET == ET_F32) {
-        const float4 fa = *reinterpret_cast<const float4*>(&af[u]);
-        const float4 fb = *reinterpret_cast<const float4*>(&bf[u]);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa.x, fb.x, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa.y, fb.y, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa.z, fb.z, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa.w, fb.w, acc, 0, 0, 0);
-      } else {
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(&af[u]),
-                                                      *reinterpret_cast<const bf16x8*>(&bf[u]), acc, 0, 0, 0);
-      }
+// Output tile width: 128 or 96 columns.  Two workgroups fit a compute unit,
+// so the grid runs in rounds of 2 x CUs workgroups; the width whose grid fills
+// its last round best is taken (128 on a tie).
+int choose_tile_n(const GemmArgs& a) {
+  const int cus = a.num_cu > 0 ? a.num_cu : 256;
+  const int rowtiles = (a.M + BM - 1) / BM;
+  const long slots = 2L * cus;
+  int best = 128;
+  double best_fill = -1.0;
+  for (int bn : {128, 96}) {
+    long tiles = 0;
+    for (int s = 0; s < a.nseg; ++s) tiles += (long)rowtiles * ((a.seg[s].ncols + bn - 1) / bn);
+    const double fill = (double)tiles / (double)(((tiles + slots - 1) / slots) * slots);
+    if (fill > best_fill + 1e-9) {
+      best_fill = fill;
+      best = bn;
     }
   }
-  if (wave > 0) {
-#pragma unroll
-    for (int v = 0; v < 4; ++v) red[wave - 1][v][lane] = acc[v];
+  return best;
+}
+
+template <int BN>
+hipError_t launch_gemm_bn(int et, GemmArgs& a, hipStream_t stream) {
+  a.ncoltiles = 0;
+  for (int s = 0; s < a.nseg; ++s) {
+    a.seg[s].ntiles = (a.seg[s].ncols + BN - 1) / BN;
+    a.ncoltiles += a.seg[s].ntiles;
   }
-  __syncthreads();
-  if (wave == 0) {
-#pragma unroll
-    for (int w = 0; w < ZP_WAVES - 1; ++w)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) acc[v] += red[w][v][lane];
-    // result: column (lane & 15) = head c0 + lrow, rows 4 lgrp + v
-    if (c0 + lrow < H) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int r = r0 + 4 * lgrp + v;
-        if (r < M) {
-          const uint32_t b = fastdiv((uint32_t)r, a.fd_ntok);
-          const uint32_t tok = (uint32_t)r - b * (uint32_t)a.Ntok;
-          a.z[((size_t)b * H + c0 + lrow) * a.Ntok + tok] = acc[v];
-        }
-      }
-    }
+  const int rowtiles = (a.M + BM - 1) / BM;
+  const dim3 grid((unsigned)(rowtiles * a.ncoltiles)), block(NTHR);
+  if (et == ET_F32) {
+    hipLaunchKernelGGL((gemm_xw_kernel<ET_F32, BN>), grid, block, 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((gemm_xw_kernel<ET_BF16, BN>), grid, block, 0, stream, a);
   }
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_gemm(int et, GemmArgs a, hipStream_t stream) {
-  a.ncoltiles = 0;
   a.fd_ntok = make_fastdiv((uint32_t)a.Ntok);
   a.fd_d = make_fastdiv((uint32_t)a.d);
+  if (a.nz < 0 || a.nz > ZR || (a.nz > 0 && (a.Wz == nullptr || a.z == nullptr))) return hipErrorInvalidValue;
   for (int s = 0; s < a.nseg; ++s) {
     GemmSeg& g = a.seg[s];
-    g.ntiles = (g.ncols + BN - 1) / BN;
-    a.ncoltiles += g.ntiles;
     if (g.layout == OUT_BLOCKED && (g.cg <= 0 || a.d % g.cg != 0)) return hipErrorInvalidValue;
     g.fd_cg = make_fastdiv((uint32_t)(g.cg > 0 ? g.cg : 1));
   }
-  const int rowtiles = (a.M + BM - 1) / BM;
-  const dim3 grid((unsigned)(rowtiles * a.ncoltiles)), block(NTHR);
-  if (et == ET_F32) {
-    hipLaunchKernelGGL(gemm_xw_kernel<ET_F32>, grid, block, 0, stream, a);
-  } else {
-    hipLaunchKernelGGL(gemm_xw_kernel<ET_BF16>, grid, block, 0, stream, a);
-  }
-  return hipGetLastError();
-}
-
-hipError_t launch_zproj(int et, ZprojArgs a, hipStream_t stream) {
-  a.fd_ntok = make_fastdiv((uint32_t)a.Ntok);
-  const dim3 grid((unsigned)((a.M + 15) / 16), (unsigned)((a.H + 15) / 16));
-  if (et == ET_F32) {
-    hipLaunchKernelGGL(zproj_kernel<ET_F32>, grid, dim3(ZP_WAVES * 64), 0, stream, a);
-  } else {
-    hipLaunchKernelGGL(zproj_kernel<ET_BF16>, grid, dim3(ZP_WAVES * 64), 0, stream, a);
-  }
-  return hipGetLastError();
+  const int bn = a.tile_n ? a.tile_n : choose_tile_n(a);
+  if (bn == 96) return launch_gemm_bn<96>(et, a, stream);
+  if (bn == 128) return launch_gemm_bn<128>(et, a, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace cat

@@ -60,24 +60,22 @@ struct GemmArgs {
   int M, K;
   int Ntok, H, d;
   int nseg;
+  // optional score projection (1D): z [M / Ntok][nz][Ntok] fp32 = X . Wz^T,
+  // Wz = W_A^T [nz][K]; nz = 0 disables it, at most 32
+  const void* Wz;
+  float* z;
+  int nz;
+  int tile_n;  // output tile width (96 or 128); 0 lets the launcher choose
+  int num_cu;  // compute units of the device (0: assume 256)
   // filled by the launcher
   int ncoltiles;
   FastDiv fd_ntok, fd_d;
   GemmSeg seg[3];
 };
 
-// Launch Y_s = X . W_s for every segment s; returns hipSuccess or the launch error.
+// Launch Y_s = X . W_s for every segment s (and z when nz > 0); returns
+// hipSuccess or the launch error.
 hipError_t launch_gemm(int et, GemmArgs args, hipStream_t stream);
-
-// Score projection z [B][H][Ntok] (fp32) = X . W_A, given as W_A^T [H][K].
-struct ZprojArgs {
-  const void* X;
-  const void* W;
-  float* z;
-  int M, K, H, Ntok;
-  FastDiv fd_ntok;  // filled by the launcher
-};
-hipError_t launch_zproj(int et, ZprojArgs args, hipStream_t stream);
 
 // Softmax + spectrum of one line per (batch, head).
 //   mode 0: input logits [BH][N] (fp32, spatial, not yet scaled)

@@ -39,9 +39,9 @@
  * -----
  * Forward calls only enqueue work ordered after everything already queued on
  * `stream` (a hipStream_t passed as void*; NULL is the default stream), and
- * everything queued on `stream` afterwards runs after it.  Inside a call the
- * 1D path forks the score chain onto a plan-owned side stream with an event
- * and joins it back before the fft-conv kernel.  Calls never allocate, never
+ * everything queued on `stream` afterwards runs after it; every kernel of a
+ * call runs on `stream` (1D: projection with the fused score projection,
+ * softmax + spectrum, fft-conv).  Calls never allocate, never
  * synchronise, and return as soon as the work is queued.  A plan owns small
  * device tables created at plan creation; the workspace (size from
  * cat_plan_workspace_size) holds the intermediates and is owned by the
@@ -83,7 +83,7 @@ typedef enum { CAT_1D = 0, CAT_BCCB_2D = 1 } cat_kind;
  * Requirements: B >= 0 (B = 0 makes every forward call a no-op), N, D,
  * H >= 1; D % H == 0; d = D / H even; D % 8 == 0; B * N * D < 2^31.
  * Supported sizes (else CAT_ERR_UNSUPPORTED):
- *   1D: N a power of two up to 4096, or any other N up to 2048 (the circular
+ *   1D: H <= 32; N a power of two up to 4096, or any other N up to 2048 (the circular
  *       convolution of length N is evaluated exactly on a power-of-two circle
  *       of length L >= 2N - 1, the values zero-extended and the softmaxed
  *       scores periodically extended);
@@ -125,9 +125,9 @@ cat_status cat_forward_bccb_2d(cat_plan plan, const void* X, const void* W_Q_t, 
  * stream, into plan-owned slots (events are created here, not in the
  * forward calls; at most 512 calls are kept, older ones are overwritten).
  * Enabling resets the slots.  cat_plan_kernel_times waits for the recorded
- * events and returns, per kernel of the path (1D: value projection, score
- * projection, spectrum, fft-conv; 2D: projection, scores, spectrum,
- * fft-conv), the summed milliseconds and the number of calls measured;
+ * events and returns, per kernel of the path (1D: projection, spectrum,
+ * fft-conv; 2D: projection, scores, spectrum, fft-conv), the summed
+ * milliseconds and the number of calls measured;
  * *nkernels receives the number of kernels (arrays hold at least 8). */
 cat_status cat_plan_set_timing(cat_plan plan, int enable);
 cat_status cat_plan_kernel_times(cat_plan plan, double* total_ms, int64_t* calls, int* nkernels);

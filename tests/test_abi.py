@@ -62,6 +62,7 @@ def _create(**kw):
     (dict(kind=cat.CAT_BCCB_2D, N=35, Hg=5, Wg=7), -2),  # grid not instantiated
     (dict(N=3000), -2),           # non-power-of-two beyond 2048
     (dict(N=8192), -2),           # power of two beyond 4096
+    (dict(D=1024, H=64), -2),     # 1D with more than 32 heads
     (dict(B=1 << 20, N=4096, D=1024), -2),  # B*N*D >= 2^31
 ])
 def test_plan_create_rejects_before_any_hip_call(kw, status):

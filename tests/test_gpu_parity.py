@@ -52,7 +52,8 @@ def tdtype(dtype):
 
 # ------------------------------------------------------------------ 1D steps
 @pytest.mark.parametrize("B,N,D,H,dtype", [(1, 64, 64, 4, "f32"), (3, 37, 48, 3, "f32"), (2, 200, 136, 17, "bf16"),
-                                           (2, 256, 256, 4, "bf16")])
+                                           (2, 256, 256, 4, "bf16"), (1, 130, 200, 25, "bf16"),
+                                           (2, 96, 320, 32, "f32")])
 def test_project_1d(cat, B, N, D, H, dtype):
     say("project_1d", B, N, D, H, dtype)
     inp = rng_inputs(11, B, N, D, H, dtype)
@@ -116,7 +117,7 @@ def test_mix_1d(cat, B, N, D, H, dtype):
 # ------------------------------------------------------------------ 1D forward
 @pytest.mark.parametrize("B,N,D,H,dtype", [(1, 64, 64, 4, "f32"), (2, 37, 48, 3, "f32"), (3, 100, 64, 4, "bf16"),
                                            (1, 1, 32, 2, "f32"), (2, 197, 96, 3, "f32"), (1, 1024, 64, 1, "bf16"),
-                                           (5, 128, 72, 9, "f32")])
+                                           (5, 128, 72, 9, "f32"), (2, 64, 128, 32, "bf16")])
 def test_forward_1d_small(cat, B, N, D, H, dtype):
     say("forward_1d", B, N, D, H, dtype)
     import torch

@@ -30,8 +30,8 @@ EXPORTS = ["cat_plan_create", "cat_plan_destroy", "cat_plan_workspace_size", "ca
            "cat_forward_1d", "cat_forward_bccb_2d", "cat_status_string", "cat_last_error",
            "cat_plan_set_timing", "cat_plan_kernel_times",
            "cat_step_project", "cat_step_spectrum", "cat_step_mix", "cat_step_scores_2d"]
-KERNELS_1D = ["project", "spectrum", "fftconv"]
-KERNELS_2D = ["project", "scores", "spectrum", "fftconv"]
+KERNELS_1D = ["wtranspose", "project", "spectrum", "fftconv"]
+KERNELS_2D = ["wtranspose", "project", "scores", "spectrum", "fftconv"]
 
 
 class CatError(RuntimeError):
@@ -182,57 +182,57 @@ def _ptr(t: Optional[torch.Tensor], shape=None, dtype=None, name="tensor") -> ct
     return ctypes.c_void_p(t.data_ptr())
 
 
-def cat_forward_1d(plan: Plan, X, W_A_t, W_V_t, O=None, workspace=None, stream=None) -> torch.Tensor:
-    """O = CAT(X) per include/cat.h; the weights are given output-major
-    (W_A_t = W_A^T [H, D], W_V_t = W_V^T [D, D]); allocates O/workspace only
-    when not given."""
+def cat_forward_1d(plan: Plan, X, W_A, W_V, O=None, workspace=None, stream=None) -> torch.Tensor:
+    """O = CAT(X) per include/cat.h (W_A [D, H], W_V [D, D]); allocates
+    O/workspace only when not given."""
     B, N, D, H, dt = plan.B, plan.N, plan.D, plan.H, plan.dtype
     if O is None:
         O = torch.empty((B, N, D), dtype=dt, device=X.device)
     if workspace is None:
         workspace = alloc_workspace(plan, X.device)
     _check(_lib.cat_forward_1d(ctypes.c_void_p(plan.handle), _ptr(X, (B, N, D), dt, "X"),
-                               _ptr(W_A_t, (H, D), dt, "W_A_t"), _ptr(W_V_t, (D, D), dt, "W_V_t"),
+                               _ptr(W_A, (D, H), dt, "W_A"), _ptr(W_V, (D, D), dt, "W_V"),
                                _ptr(O, (B, N, D), dt, "O"), _ptr(workspace, None, None, "workspace"),
                                _stream_ptr(stream)), "cat_forward_1d")
     return O
 
 
-def cat_forward_bccb_2d(plan: Plan, X, W_Q_t, W_K_t, W_V_t, O=None, workspace=None, stream=None) -> torch.Tensor:
-    """O = 2D BCCB circulant attention(X); weights output-major ([D, D] transposes)."""
+def cat_forward_bccb_2d(plan: Plan, X, W_Q, W_K, W_V, O=None, workspace=None, stream=None) -> torch.Tensor:
+    """O = 2D BCCB circulant attention(X) per include/cat.h (weights [D, D])."""
     B, N, D, dt = plan.B, plan.N, plan.D, plan.dtype
     if O is None:
         O = torch.empty((B, N, D), dtype=dt, device=X.device)
     if workspace is None:
         workspace = alloc_workspace(plan, X.device)
     _check(_lib.cat_forward_bccb_2d(ctypes.c_void_p(plan.handle), _ptr(X, (B, N, D), dt, "X"),
-                                    _ptr(W_Q_t, (D, D), dt, "W_Q_t"), _ptr(W_K_t, (D, D), dt, "W_K_t"),
-                                    _ptr(W_V_t, (D, D), dt, "W_V_t"), _ptr(O, (B, N, D), dt, "O"),
+                                    _ptr(W_Q, (D, D), dt, "W_Q"), _ptr(W_K, (D, D), dt, "W_K"),
+                                    _ptr(W_V, (D, D), dt, "W_V"), _ptr(O, (B, N, D), dt, "O"),
                                     _ptr(workspace, None, None, "workspace"), _stream_ptr(stream)),
            "cat_forward_bccb_2d")
     return O
 
 
-def cat_step_project(plan: Plan, X, W_A_t, W_V_t, W_K_t=None, stream=None):
+def cat_step_project(plan: Plan, X, W_A, W_V, W_K=None, workspace=None, stream=None):
     """1D: returns (V [B,N,D] storage dtype, z [B,H,N] fp32).
-    2D (W_A_t is W_Q^T): returns (Q fp32, K fp32, V storage dtype), all [B,N,D].
-    Weights output-major, as in the forward calls."""
+    2D (W_A is W_Q): returns (Q fp32, K fp32, V storage dtype), all [B,N,D]."""
     B, N, D, H, dt = plan.B, plan.N, plan.D, plan.H, plan.dtype
     dev = X.device
     V = torch.empty((B, N, D), dtype=dt, device=dev)
+    if workspace is None:
+        workspace = alloc_workspace(plan, dev)
     if plan.kind == CAT_1D:
         z = torch.empty((B, H, N), dtype=torch.float32, device=dev)
         _check(_lib.cat_step_project(ctypes.c_void_p(plan.handle), _ptr(X, (B, N, D), dt, "X"),
-                                     _ptr(W_A_t, (H, D), dt, "W_A_t"), ctypes.c_void_p(None),
-                                     _ptr(W_V_t, (D, D), dt, "W_V_t"), _ptr(V), _ptr(z), ctypes.c_void_p(None),
-                                     _stream_ptr(stream)), "cat_step_project")
+                                     _ptr(W_A, (D, H), dt, "W_A"), ctypes.c_void_p(None),
+                                     _ptr(W_V, (D, D), dt, "W_V"), _ptr(V), _ptr(z), ctypes.c_void_p(None),
+                                     _ptr(workspace), _stream_ptr(stream)), "cat_step_project")
         return V, z
     Q = torch.empty((B, N, D), dtype=torch.float32, device=dev)
     K = torch.empty((B, N, D), dtype=torch.float32, device=dev)
     _check(_lib.cat_step_project(ctypes.c_void_p(plan.handle), _ptr(X, (B, N, D), dt, "X"),
-                                 _ptr(W_A_t, (D, D), dt, "W_Q_t"), _ptr(W_K_t, (D, D), dt, "W_K_t"),
-                                 _ptr(W_V_t, (D, D), dt, "W_V_t"), _ptr(V), _ptr(Q), _ptr(K),
-                                 _stream_ptr(stream)), "cat_step_project")
+                                 _ptr(W_A, (D, D), dt, "W_Q"), _ptr(W_K, (D, D), dt, "W_K"),
+                                 _ptr(W_V, (D, D), dt, "W_V"), _ptr(V), _ptr(Q), _ptr(K),
+                                 _ptr(workspace), _stream_ptr(stream)), "cat_step_project")
     return Q, K, V
 
 

@@ -73,7 +73,7 @@ hipError_t prepare_kernels(const LineGeom& g, size_t conv_lds, size_t spec_lds, 
   return err;
 }
 
-hipError_t launch_spectrum(const LineGeom& g, int mode, const SpecArgs& a, hipStream_t s) {
+hipError_t launch_spectrum(const LineGeom& g, int mode, const SpecArgs& a, hipStream_t s, const LaunchTiming* t) {
   const Entry* e = find_entry(g);
   SpecFn fn = e ? (mode == 0 ? e->spec0 : e->spec1) : nullptr;
   if (!fn) return hipErrorInvalidValue;
@@ -81,11 +81,10 @@ hipError_t launch_spectrum(const LineGeom& g, int mode, const SpecArgs& a, hipSt
   aa.log2G = ilog2(aa.G);
   const size_t lds = spectrum_lds_bytes(g, aa.G);
   const int blocks = (aa.BH + aa.G - 1) / aa.G;
-  hipLaunchKernelGGL(fn, dim3(blocks), dim3(aa.G * e->T), lds, s, aa);
-  return hipGetLastError();
+  return launch_k(fn, dim3(blocks), dim3(aa.G * e->T), lds, s, t, aa);
 }
 
-hipError_t launch_conv(const LineGeom& g, int et, const ConvArgs& a, hipStream_t s) {
+hipError_t launch_conv(const LineGeom& g, int et, const ConvArgs& a, hipStream_t s, const LaunchTiming* t) {
   const Entry* e = find_entry(g);
   ConvFn fn = e ? (et == ET_F32 ? e->conv_f32 : e->conv_bf16) : nullptr;
   if (!fn) return hipErrorInvalidValue;
@@ -93,17 +92,15 @@ hipError_t launch_conv(const LineGeom& g, int et, const ConvArgs& a, hipStream_t
   aa.log2G = ilog2(aa.G);
   const size_t lds = (size_t)aa.G * line_lds_bytes(g);
   const int blocks = aa.B * aa.H * aa.ng;
-  hipLaunchKernelGGL(fn, dim3(blocks), dim3(aa.G * e->T), lds, s, aa);
-  return hipGetLastError();
+  return launch_k(fn, dim3(blocks), dim3(aa.G * e->T), lds, s, t, aa);
 }
 
-hipError_t launch_score_partial(const LineGeom& g, const ScoreArgs& a, hipStream_t s) {
+hipError_t launch_score_partial(const LineGeom& g, const ScoreArgs& a, hipStream_t s, const LaunchTiming* t) {
   const Entry* e = find_entry(g);
   ScoreFn fn = e ? e->score : nullptr;
   if (!fn) return hipErrorInvalidValue;
   const size_t lds = 2 * line_lds_bytes(g);
-  hipLaunchKernelGGL(fn, dim3(a.BH * a.ngrp), dim3(2 * e->T), lds, s, a);
-  return hipGetLastError();
+  return launch_k(fn, dim3(a.BH * a.ngrp), dim3(2 * e->T), lds, s, t, a);
 }
 
 hipError_t launch_relayout(const RelayoutArgs& a, hipStream_t s) {

@@ -5,10 +5,11 @@
 // "Method details / Overall framework"); the ViT circulant attention projects
 // them to Q, K and V (Vision Transformers are Circulant Attention Learners,
 // "Circulant Attention: attention rebuilt with the FFT").  Both are one dense
-// contraction Y = X W with X [M = B N][K = D] and W given output-major,
-// Wt [ncols][K] (each output channel's K weights contiguous, the layout a
-// linear layer stores), run here as a single launch over up to three column
-// segments, each written in the layout its consumer reads.
+// contraction Y = X W with X [M = B N][K = D].  The GEMM reads W output-major,
+// Wt [ncols][K] (each output channel's K weights contiguous); a small
+// transpose kernel turns the input-major weights of the ABI into that layout
+// once per call.  One launch covers up to three column segments, each
+// written in the layout its consumer reads.
 //
 // Tiling: 128 x 128 output tile per 256-thread workgroup (4 waves, 2 x 2),
 // each wave a 64 x 64 block of 16 x 16 MFMA tiles.  K is walked in tiles of
@@ -319,6 +320,73 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_xw_kernel(GemmArgs a) {
   }
 }
 
+// Weight transpose W [rows][cols] -> W^T [cols][rows] through a 64 x 64 LDS
+// tile, so that the GEMM can stage every operand row with 16-byte LDS-DMA.
+// The weights are given input-major, X W as the pages write the projections;
+// this pass turns them output-major once per call.
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_kernel(TransposeArgs a) {
+  constexpr int VE = 16 / sizeof(T);  // elements per 16-byte chunk
+  constexpr int P = sizeof(T) == 2 ? 66 : 65;  // LDS pitch (elements): column reads spread over banks
+  __shared__ __attribute__((aligned(16))) T tile[64][P];
+  const int tid = threadIdx.x;
+  int b = blockIdx.x, m = 0;
+  while (m + 1 < a.n && b >= a.tile0[m + 1]) ++m;
+  b -= a.tile0[m];
+  const int R = a.rows[m], Cc = a.cols[m];
+  const int tcols = (Cc + 63) / 64;
+  const int tr = b / tcols, tc = b - tr * tcols;
+  const int r0 = tr * 64, c0 = tc * 64;
+  const T* src = reinterpret_cast<const T*>(a.src[m]);
+  T* dst = reinterpret_cast<T*>(a.dst[m]);
+  // interior tiles move 16-byte chunks; edge tiles move single elements
+  const bool full = (r0 + 64 <= R) & (c0 + 64 <= Cc) & (Cc % VE == 0) & (R % VE == 0);
+  if (full) {
+    constexpr int CPR = 64 / VE;        // chunks per 64-element row
+    constexpr int NCH = 64 * CPR / 256;  // chunks per thread
+    uint4 v[NCH];
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int q = tid + 256 * i, r = q / CPR, ch = q % CPR;
+      v[i] = *reinterpret_cast<const uint4*>(src + (size_t)(r0 + r) * Cc + c0 + ch * VE);
+    }
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int q = tid + 256 * i, r = q / CPR, ch = q % CPR;
+      const T* e = reinterpret_cast<const T*>(&v[i]);
+#pragma unroll
+      for (int k = 0; k < VE; ++k) tile[r][ch * VE + k] = e[k];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int q = tid + 256 * i, c = q / CPR, ch = q % CPR;
+      T e[VE];
+#pragma unroll
+      for (int k = 0; k < VE; ++k) e[k] = tile[ch * VE + k][c];
+      *reinterpret_cast<uint4*>(dst + (size_t)(c0 + c) * R + r0 + ch * VE) = *reinterpret_cast<const uint4*>(e);
+    }
+    return;
+  }
+  const int lo = tid & 63, hi = tid >> 6;
+  T v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = r0 + hi + 4 * i, c = c0 + lo;
+    const bool ok = (r < R) & (c < Cc);
+    const T x = src[(size_t)(r < R ? r : R - 1) * Cc + (c < Cc ? c : Cc - 1)];
+    v[i] = ok ? x : T(0);
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) tile[hi + 4 * i][lo] = v[i];
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int c = c0 + hi + 4 * i, r = r0 + lo;
+    if ((c < Cc) & (r < R)) dst[(size_t)c * R + r] = tile[lo][hi + 4 * i];
+  }
+}
+
 // Output tile width: 128 or 96 columns.  Two workgroups fit a compute unit,
 // so the grid runs in rounds of 2 x CUs workgroups; the width whose grid fills
 // its last round best is taken (128 on a tie).
@@ -341,7 +409,7 @@ int choose_tile_n(const GemmArgs& a) {
 }
 
 template <int BN>
-hipError_t launch_gemm_bn(int et, GemmArgs& a, hipStream_t stream) {
+hipError_t launch_gemm_bn(int et, GemmArgs& a, hipStream_t stream, const LaunchTiming* t) {
   a.ncoltiles = 0;
   for (int s = 0; s < a.nseg; ++s) {
     a.seg[s].ntiles = (a.seg[s].ncols + BN - 1) / BN;
@@ -349,17 +417,26 @@ hipError_t launch_gemm_bn(int et, GemmArgs& a, hipStream_t stream) {
   }
   const int rowtiles = (a.M + BM - 1) / BM;
   const dim3 grid((unsigned)(rowtiles * a.ncoltiles)), block(NTHR);
-  if (et == ET_F32) {
-    hipLaunchKernelGGL((gemm_xw_kernel<ET_F32, BN>), grid, block, 0, stream, a);
-  } else {
-    hipLaunchKernelGGL((gemm_xw_kernel<ET_BF16, BN>), grid, block, 0, stream, a);
-  }
-  return hipGetLastError();
+  if (et == ET_F32) return launch_k(gemm_xw_kernel<ET_F32, BN>, grid, block, 0, stream, t, a);
+  return launch_k(gemm_xw_kernel<ET_BF16, BN>, grid, block, 0, stream, t, a);
 }
 
 }  // namespace
 
-hipError_t launch_gemm(int et, GemmArgs a, hipStream_t stream) {
+hipError_t launch_transpose(int et, TransposeArgs a, hipStream_t stream, const LaunchTiming* t) {
+  if (a.n < 1 || a.n > 4) return hipErrorInvalidValue;
+  int nb = 0;
+  for (int m = 0; m < a.n; ++m) {
+    if (a.rows[m] < 1 || a.cols[m] < 1 || !a.src[m] || !a.dst[m]) return hipErrorInvalidValue;
+    a.tile0[m] = nb;
+    nb += ((a.rows[m] + 63) / 64) * ((a.cols[m] + 63) / 64);
+  }
+  a.tile0[a.n] = nb;
+  if (et == ET_F32) return launch_k(transpose_kernel<float>, dim3(nb), dim3(256), 0, stream, t, a);
+  return launch_k(transpose_kernel<uint16_t>, dim3(nb), dim3(256), 0, stream, t, a);
+}
+
+hipError_t launch_gemm(int et, GemmArgs a, hipStream_t stream, const LaunchTiming* t) {
   a.fd_ntok = make_fastdiv((uint32_t)a.Ntok);
   a.fd_d = make_fastdiv((uint32_t)a.d);
   if (a.nz < 0 || a.nz > ZR || (a.nz > 0 && (a.Wz == nullptr || a.z == nullptr))) return hipErrorInvalidValue;
@@ -369,8 +446,8 @@ hipError_t launch_gemm(int et, GemmArgs a, hipStream_t stream) {
     g.fd_cg = make_fastdiv((uint32_t)(g.cg > 0 ? g.cg : 1));
   }
   const int bn = a.tile_n ? a.tile_n : choose_tile_n(a);
-  if (bn == 96) return launch_gemm_bn<96>(et, a, stream);
-  if (bn == 128) return launch_gemm_bn<128>(et, a, stream);
+  if (bn == 96) return launch_gemm_bn<96>(et, a, stream, t);
+  if (bn == 128) return launch_gemm_bn<128>(et, a, stream, t);
   return hipErrorInvalidValue;
 }
 

@@ -2,6 +2,7 @@
 // and the kernel translation units (host-visible, no device code).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
@@ -10,6 +11,23 @@
 namespace cat {
 
 enum ElemType : int { ET_F32 = 0, ET_BF16 = 1 };
+
+// Optional per-launch timing: two events that the kernel's own dispatch
+// stamps at its start and its end (hipExtLaunchKernel), so no marker packet
+// sits between the kernels of a call.
+struct LaunchTiming {
+  hipEvent_t start, stop;
+};
+
+template <typename K, typename... Args>
+inline hipError_t launch_k(K kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s, const LaunchTiming* t,
+                           Args... args) {
+  if (t)
+    hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, s, t->start, t->stop, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
+  return hipGetLastError();
+}
 
 // Output index maps of the projection GEMM.  Row m = b * Ntok + tok.
 //   ROWMAJOR: out[m * ncols + n]
@@ -73,9 +91,20 @@ struct GemmArgs {
   GemmSeg seg[3];
 };
 
+// Weight re-layout for the GEMM: dst[m] [cols][rows] = src[m] [rows][cols]^T
+// for up to four matrices in one launch.
+struct TransposeArgs {
+  const void* src[4];
+  void* dst[4];
+  int rows[4], cols[4];
+  int n;
+  int tile0[5];  // filled by the launcher: first workgroup of each matrix
+};
+hipError_t launch_transpose(int et, TransposeArgs a, hipStream_t stream, const LaunchTiming* t = nullptr);
+
 // Launch Y_s = X . W_s for every segment s (and z when nz > 0); returns
 // hipSuccess or the launch error.
-hipError_t launch_gemm(int et, GemmArgs args, hipStream_t stream);
+hipError_t launch_gemm(int et, GemmArgs args, hipStream_t stream, const LaunchTiming* t = nullptr);
 
 // Softmax + spectrum of one line per (batch, head).
 //   mode 0: input logits [BH][N] (fp32, spatial, not yet scaled)
@@ -139,9 +168,11 @@ int line_threads(const LineGeom& g);
 // LDS bytes of a spectrum workgroup of G lines (lines, reduction scratch).
 size_t spectrum_lds_bytes(const LineGeom& g, int G);
 
-hipError_t launch_spectrum(const LineGeom& g, int mode, const SpecArgs& a, hipStream_t s);
-hipError_t launch_conv(const LineGeom& g, int et, const ConvArgs& a, hipStream_t s);
-hipError_t launch_score_partial(const LineGeom& g, const ScoreArgs& a, hipStream_t s);
+hipError_t launch_spectrum(const LineGeom& g, int mode, const SpecArgs& a, hipStream_t s,
+                           const LaunchTiming* t = nullptr);
+hipError_t launch_conv(const LineGeom& g, int et, const ConvArgs& a, hipStream_t s, const LaunchTiming* t = nullptr);
+hipError_t launch_score_partial(const LineGeom& g, const ScoreArgs& a, hipStream_t s,
+                                const LaunchTiming* t = nullptr);
 hipError_t launch_relayout(const RelayoutArgs& a, hipStream_t s);
 // Raise the dynamic-LDS limit of the kernels a geometry uses (once per plan).
 hipError_t prepare_kernels(const LineGeom& g, size_t conv_lds, size_t spec_lds, size_t score_lds);

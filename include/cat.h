@@ -26,10 +26,9 @@
  * Data
  * ----
  * All buffers are device memory, dense, row-major, owned by the caller:
- *   X [B][N][D], O [B][N][D], and the weights output-major (transposed):
- *   W_A_t = W_A^T [H][D], W_V_t / W_Q_t / W_K_t = W^T [D][D] -- each output
- *   channel's D input weights contiguous, the layout a linear layer (torch
- *   nn.Linear.weight) stores; the products are still X W_A, X W_V, ...
+ *   X [B][N][D], W_A [D][H], W_V / W_Q / W_K [D][D] (the products are X W as
+ *   the pages write them; a torch nn.Linear weight is the transpose),
+ *   O [B][N][D].
  * Storage dtype (CAT_F32 or CAT_BF16) is the same for X, the weights and O;
  * all arithmetic is fp32 (bf16 inputs are widened exactly, O is rounded to
  * nearest even).  X, the weights, O and the workspace must be 16-byte
@@ -40,8 +39,8 @@
  * Forward calls only enqueue work ordered after everything already queued on
  * `stream` (a hipStream_t passed as void*; NULL is the default stream), and
  * everything queued on `stream` afterwards runs after it; every kernel of a
- * call runs on `stream` (1D: projection with the fused score projection,
- * softmax + spectrum, fft-conv).  Calls never allocate, never
+ * call runs on `stream` (1D: weight re-layout, projection with the fused
+ * score projection, softmax + spectrum, fft-conv).  Calls never allocate, never
  * synchronise, and return as soon as the work is queued.  A plan owns small
  * device tables created at plan creation; the workspace (size from
  * cat_plan_workspace_size) holds the intermediates and is owned by the
@@ -110,25 +109,26 @@ cat_status cat_plan_workspace_size(cat_plan plan, size_t* bytes);
  * its two passes).  Diagnostic. */
 cat_status cat_plan_geometry(cat_plan plan, int64_t* L, int64_t* L1, int64_t* L2);
 
-/* CAT 1D forward (see top of file).  X [B][N][D], W_A_t [H][D],
- * W_V_t [D][D], O [B][N][D] in the plan's storage dtype. */
-cat_status cat_forward_1d(cat_plan plan, const void* X, const void* W_A_t, const void* W_V_t,
+/* CAT 1D forward (see top of file).  X [B][N][D], W_A [D][H], W_V [D][D],
+ * O [B][N][D] in the plan's storage dtype. */
+cat_status cat_forward_1d(cat_plan plan, const void* X, const void* W_A, const void* W_V,
                           void* O, void* workspace, void* stream);
 
 /* 2D BCCB circulant attention forward (see top of file).  X [B][Hg Wg][D],
- * W_Q_t, W_K_t, W_V_t [D][D] (output-major), O [B][Hg Wg][D]. */
-cat_status cat_forward_bccb_2d(cat_plan plan, const void* X, const void* W_Q_t, const void* W_K_t,
-                               const void* W_V_t, void* O, void* workspace, void* stream);
+ * W_Q, W_K, W_V [D][D], O [B][Hg Wg][D]. */
+cat_status cat_forward_bccb_2d(cat_plan plan, const void* X, const void* W_Q, const void* W_K,
+                               const void* W_V, void* O, void* workspace, void* stream);
 
-/* Per-kernel timing (diagnostic).  While enabled, each forward call records
- * a HIP event before and after every kernel it launches, on the caller's
- * stream, into plan-owned slots (events are created here, not in the
- * forward calls; at most 512 calls are kept, older ones are overwritten).
- * Enabling resets the slots.  cat_plan_kernel_times waits for the recorded
- * events and returns, per kernel of the path (1D: projection, spectrum,
- * fft-conv; 2D: projection, scores, spectrum, fft-conv), the summed
- * milliseconds and the number of calls measured;
- * *nkernels receives the number of kernels (arrays hold at least 8). */
+/* Per-kernel timing (diagnostic).  While enabled, each forward call launches
+ * every kernel with a start and a stop event that the kernel's own dispatch
+ * stamps (hipExtLaunchKernel), into plan-owned slots (events are created
+ * here, not in the forward calls; at most 512 calls are kept, older ones are
+ * overwritten).  Enabling resets the slots.  cat_plan_kernel_times waits for
+ * the recorded events and returns, per kernel of the path (1D: weight
+ * re-layout, projection, spectrum, fft-conv; 2D: weight re-layout,
+ * projection, scores, spectrum, fft-conv), the summed milliseconds and the
+ * number of calls measured; *nkernels receives the number of kernels (arrays
+ * hold at least 8). */
 cat_status cat_plan_set_timing(cat_plan plan, int enable);
 cat_status cat_plan_kernel_times(cat_plan plan, double* total_ms, int64_t* calls, int* nkernels);
 
@@ -140,13 +140,14 @@ const char* cat_last_error(void);
  * row-major inputs and outputs.  For testing and diagnosis of the
  * individual steps; they share the kernels of the forward calls. */
 
-/* Projection step (weights output-major as above).  1D plan: V [B][N][D]
- * (storage dtype) = X W_V and z [B][H][N] (fp32) = logits X W_A (W_K_t
- * ignored).  2D plan: Q, K [B][N][D] fp32 = X W_Q, X W_K and V (storage
- * dtype) = X W_V; pass W_A_t = W_Q_t, z = Q (fp32 [B][N][D]) and K_out for
- * K.  No workspace is used. */
-cat_status cat_step_project(cat_plan plan, const void* X, const void* W_A_t, const void* W_K_t,
-                            const void* W_V_t, void* V, void* z, void* K_out, void* stream);
+/* Projection step.  1D plan: V [B][N][D] (storage dtype) = X W_V and
+ * z [B][H][N] (fp32) = logits X W_A (W_K ignored).  2D plan: Q, K [B][N][D]
+ * fp32 = X W_Q, X W_K and V (storage dtype) = X W_V; pass W_A = W_Q,
+ * z = Q (fp32 [B][N][D]) and K_out for K.  The workspace (the plan's size)
+ * holds the re-laid-out weights. */
+cat_status cat_step_project(cat_plan plan, const void* X, const void* W_A, const void* W_K,
+                            const void* W_V, void* V, void* z, void* K_out, void* workspace,
+                            void* stream);
 
 /* Softmax + filter spectrum step from logits.  logits [B][H][N] fp32 (1D: z;
  * 2D: the scaled scores a).  probs [B][H][N] fp32 receives the softmax

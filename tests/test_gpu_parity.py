@@ -58,7 +58,7 @@ def test_project_1d(cat, B, N, D, H, dtype):
     say("project_1d", B, N, D, H, dtype)
     inp = rng_inputs(11, B, N, D, H, dtype)
     plan = cat.cat_plan_create("1d", dtype, B, N, D, H)
-    V, z = cat.cat_step_project(plan, to_dev(inp.X, dtype), to_dev(inp.W_A.T, dtype), to_dev(inp.W_V.T, dtype))
+    V, z = cat.cat_step_project(plan, to_dev(inp.X, dtype), to_dev(inp.W_A, dtype), to_dev(inp.W_V, dtype))
     import torch
     torch.cuda.synchronize()
     assert_parity(to_np(V), oracle.matmul(inp.X, inp.W_V), dtype, "V")
@@ -123,7 +123,7 @@ def test_forward_1d_small(cat, B, N, D, H, dtype):
     import torch
     inp = rng_inputs(5, B, N, D, H, dtype)
     plan = cat.cat_plan_create("1d", dtype, B, N, D, H)
-    O = cat.cat_forward_1d(plan, to_dev(inp.X, dtype), to_dev(inp.W_A.T, dtype), to_dev(inp.W_V.T, dtype))
+    O = cat.cat_forward_1d(plan, to_dev(inp.X, dtype), to_dev(inp.W_A, dtype), to_dev(inp.W_V, dtype))
     torch.cuda.synchronize()
     ref = oracle.cat_forward_1d(inp.X, inp.W_A, inp.W_V)["O"]
     assert_parity(to_np(O), ref, dtype, "O")
@@ -141,7 +141,7 @@ def test_forward_1d_workload_full_size(cat, name):
     import torch
     inp = W.make_inputs(wl)
     plan = cat.cat_plan_create("1d", wl.dtype, wl.B, wl.N, wl.D, wl.H)
-    O = cat.cat_forward_1d(plan, to_dev(inp.X, wl.dtype), to_dev(inp.W_A.T, wl.dtype), to_dev(inp.W_V.T, wl.dtype))
+    O = cat.cat_forward_1d(plan, to_dev(inp.X, wl.dtype), to_dev(inp.W_A, wl.dtype), to_dev(inp.W_V, wl.dtype))
     torch.cuda.synchronize()
     O = to_np(O)
     assert np.all(np.isfinite(O))
@@ -180,7 +180,7 @@ def test_determinism_1d(cat):
     wl = W.WORKLOADS[W.HEADLINE].with_(B=2)
     inp = W.make_inputs(wl, batch=2)
     plan = cat.cat_plan_create("1d", wl.dtype, 2, wl.N, wl.D, wl.H)
-    args = [to_dev(a, wl.dtype) for a in (inp.X, inp.W_A.T, inp.W_V.T)]
+    args = [to_dev(a, wl.dtype) for a in (inp.X, inp.W_A, inp.W_V)]
     O1 = cat.cat_forward_1d(plan, *args)
     O2 = cat.cat_forward_1d(plan, *args)
     torch.cuda.synchronize()
@@ -231,7 +231,7 @@ def test_forward_2d_small(cat, B, Hg, Wg, D, H, dtype, ss):
     import torch
     inp = rng_inputs_2d(9, B, Hg, Wg, D, H, dtype, score_scale=ss)
     plan = cat.cat_plan_create("2d", dtype, B, Hg * Wg, D, H, Hg, Wg)
-    O = cat.cat_forward_bccb_2d(plan, *[to_dev(a, dtype) for a in (inp.X, inp.W_Q.T, inp.W_K.T, inp.W_V.T)])
+    O = cat.cat_forward_bccb_2d(plan, *[to_dev(a, dtype) for a in (inp.X, inp.W_Q, inp.W_K, inp.W_V)])
     torch.cuda.synchronize()
     ref = oracle.cat_forward_bccb_2d(inp.X, inp.W_Q, inp.W_K, inp.W_V, Hg, Wg, H)["O"]
     assert_parity(to_np(O), ref, dtype, "O")
@@ -245,7 +245,7 @@ def test_forward_2d_workload_full_size(cat):
     import torch
     inp = W.make_inputs(wl)
     plan = cat.cat_plan_create("2d", wl.dtype, wl.B, wl.N, wl.D, wl.H, wl.Hg, wl.Wg)
-    O = cat.cat_forward_bccb_2d(plan, *[to_dev(a, wl.dtype) for a in (inp.X, inp.W_Q.T, inp.W_K.T, inp.W_V.T)])
+    O = cat.cat_forward_bccb_2d(plan, *[to_dev(a, wl.dtype) for a in (inp.X, inp.W_Q, inp.W_K, inp.W_V)])
     torch.cuda.synchronize()
     O = to_np(O)
     assert np.all(np.isfinite(O))
@@ -262,7 +262,7 @@ def test_determinism_2d(cat):
     import torch
     inp = rng_inputs_2d(2, 2, 12, 12, 48, 3, "bf16", score_scale=0.3)
     plan = cat.cat_plan_create("2d", "bf16", 2, 144, 48, 3, 12, 12)
-    args = [to_dev(a, "bf16") for a in (inp.X, inp.W_Q.T, inp.W_K.T, inp.W_V.T)]
+    args = [to_dev(a, "bf16") for a in (inp.X, inp.W_Q, inp.W_K, inp.W_V)]
     O1 = cat.cat_forward_bccb_2d(plan, *args)
     O2 = cat.cat_forward_bccb_2d(plan, *args)
     torch.cuda.synchronize()
@@ -300,7 +300,7 @@ def test_empty_batch_is_a_no_op(cat):
         X = torch.empty(0, 64, 32, device="cuda")
         Wm = torch.zeros(32, 32, device="cuda")
         if kind == "1d":
-            O = cat.cat_forward_1d(plan, X, torch.zeros(2, 32, device="cuda"), Wm)
+            O = cat.cat_forward_1d(plan, X, torch.zeros(32, 2, device="cuda"), Wm)
         else:
             O = cat.cat_forward_bccb_2d(plan, X, Wm, Wm, Wm)
         torch.cuda.synchronize()

@@ -89,9 +89,10 @@ KERNEL_SOURCES["wtranspose"] = KERNEL_SOURCES["project"]
 KERNEL_SOURCES["scores"] = KERNEL_SOURCES["fftconv"]
 
 
-def measured_traffic(kernel: str, workload: str):
+def measured_traffic(kernel: str, workload: str, launches_per_call: int):
     """HBM bytes per launch from a committed counter summary, if it was taken
-    on the current sources of that kernel; else None."""
+    on the current sources of that kernel with the same launches per call;
+    else None."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
@@ -99,6 +100,8 @@ def measured_traffic(kernel: str, workload: str):
         with open(path) as f:
             rec = json.load(f)
         if rec.get("source_hash") != source_hash(KERNEL_SOURCES[kernel]):
+            return None
+        if rec.get("launches_per_call", 1) != launches_per_call:
             return None
         return rec.get("hbm_bytes_per_launch")
     except Exception:
@@ -218,13 +221,15 @@ def run(args):
     kernels = {}
     for k, (ms, n) in ktimes.items():
         mm = model[k]
-        sec = ms / 1000.0
-        gbs = mm["bytes"] / sec / 1e9
-        tfl = mm["flops"] / sec / 1e12
-        kernels[k] = dict(us=round(ms * 1000, 3), bytes=int(mm["bytes"]), flops=float(mm["flops"]),
+        per_call = max(1, round(n / args.steps))  # launches of this kernel per forward call
+        sec = ms / 1000.0                          # average duration of one launch
+        nbytes, nflops = mm["bytes"] / per_call, mm["flops"] / per_call
+        gbs = nbytes / sec / 1e9
+        tfl = nflops / sec / 1e12
+        kernels[k] = dict(us=round(ms * 1000, 3), launches_per_call=per_call, bytes=int(nbytes), flops=float(nflops),
                           hbm_frac=round(gbs / HBM_PEAK_GBS, 4),
                           compute_frac=round(tfl / PEAK_TFLOPS[mm["unit"]], 4), compute_unit=mm["unit"])
-    dom = max(ktimes, key=lambda k: ktimes[k][0])
+    dom = max(ktimes, key=lambda k: ktimes[k][0] * kernels[k]["launches_per_call"])
     kd = kernels[dom]
     sec = ktimes[dom][0] / 1000.0
     if kd["compute_unit"].startswith("mfma"):
@@ -236,7 +241,7 @@ def run(args):
     else:
         achieved, peak, unit = kd["flops"] / sec / 1e12, PEAK_TFLOPS[kd["compute_unit"]], "TFLOP/s"
     roofline = dict(kernel=dom, bound=bound, achieved=round(achieved, 2), peak=peak, unit=unit,
-                    frac=round(achieved / peak, 4), traffic=measured_traffic(dom, wl.name),
+                    frac=round(achieved / peak, 4), traffic=measured_traffic(dom, wl.name, kd["launches_per_call"]),
                     hbm_frac=kd["hbm_frac"], compute_frac=kd["compute_frac"], us=kd["us"])
 
     cpu = None
@@ -302,8 +307,8 @@ def main():
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path has no multi-GPU mode. "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
-    if args.steps > 512:
-        print("--steps is limited to 512 (per-kernel timing slots)", file=sys.stderr)
+    if args.steps > 256:
+        print("--steps is limited to 256 (per-kernel timing slots)", file=sys.stderr)
         sys.exit(2)
     from circulant_softmax_attention_amd import workloads as W
     if args.workload is None:

@@ -148,7 +148,8 @@ def cat_plan_set_timing(plan: Plan, enable: bool = True):
 
 
 def cat_plan_kernel_times(plan: Plan):
-    """{kernel name: (average ms, calls)} over the calls recorded since timing was enabled."""
+    """{kernel name: (average ms per launch, launches)} over the calls recorded
+    since timing was enabled."""
     tot = (ctypes.c_double * 8)()
     cnt = (ctypes.c_int64 * 8)()
     nk = ctypes.c_int()

@@ -29,10 +29,12 @@ struct cat_plan_s {
   size_t off_W, off_V, off_z, off_Q, off_K, off_part, off_spec, ws_bytes;
   bool debug_sync;
   int num_cu;        // compute units of the device current at plan creation
-  // per-kernel timing slots: ev[slot][kernel][start/stop]
-  static constexpr int kSlots = 512, kMaxK = 5;
+  // per-launch timing slots: ev[slot][launch][start/stop], kind[slot][launch]
+  static constexpr int kSlots = 256, kMaxL = 32, kMaxK = 5;
   bool timing = false;
   hipEvent_t* ev = nullptr;
+  int8_t kind_of[kSlots][kMaxL];
+  int nlaunch[kSlots];
   int64_t calls = 0;
   int nk = 0;
 };
@@ -79,26 +81,34 @@ char* ws_at(void* ws, size_t off) { return reinterpret_cast<char*>(ws) + off; }
 
 void free_events(cat_plan_s* pl) {
   if (!pl->ev) return;
-  for (int i = 0; i < cat_plan_s::kSlots * cat_plan_s::kMaxK * 2; ++i)
+  for (int i = 0; i < cat_plan_s::kSlots * cat_plan_s::kMaxL * 2; ++i)
     if (pl->ev[i]) (void)hipEventDestroy(pl->ev[i]);
   delete[] pl->ev;
   pl->ev = nullptr;
 }
 
-// Timing events of kernel `k` of the current call (null when timing is off):
-// the kernel's dispatch stamps them at its start and end.
+// Timing events of one launch of the current call (null when timing is off):
+// the kernel's dispatch stamps them at its start and end.  Each launch takes
+// the next pair of the call's slot and records which kernel of the path it is.
 struct KernelMark {
   cat_plan_s* pl;
-  hipEvent_t* slot;
-  LaunchTiming lt[cat_plan_s::kMaxK];
-  explicit KernelMark(cat_plan_s* p) : pl(p), slot(nullptr) {
+  int slot = -1;
+  LaunchTiming lt[cat_plan_s::kMaxL];
+  explicit KernelMark(cat_plan_s* p) : pl(p) {
     if (pl->timing) {
-      slot = pl->ev + (size_t)(pl->calls % cat_plan_s::kSlots) * cat_plan_s::kMaxK * 2;
+      slot = (int)(pl->calls % cat_plan_s::kSlots);
       ++pl->calls;
-      for (int k = 0; k < cat_plan_s::kMaxK; ++k) lt[k] = LaunchTiming{slot[2 * k], slot[2 * k + 1]};
+      pl->nlaunch[slot] = 0;
     }
   }
-  const LaunchTiming* at(int k) const { return slot ? &lt[k] : nullptr; }
+  const LaunchTiming* at(int k) {
+    if (slot < 0 || pl->nlaunch[slot] >= cat_plan_s::kMaxL) return nullptr;
+    const int i = pl->nlaunch[slot]++;
+    hipEvent_t* e = pl->ev + ((size_t)slot * cat_plan_s::kMaxL + i) * 2;
+    pl->kind_of[slot][i] = (int8_t)k;
+    lt[i] = LaunchTiming{e[0], e[1]};
+    return &lt[i];
+  }
 };
 
 }  // namespace
@@ -245,6 +255,7 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
     return hip_fail(e, "hipFuncSetAttribute");
   }
 
+
   *out = pl;
   g_err.clear();
   return CAT_OK;
@@ -254,6 +265,7 @@ cat_status cat_plan_destroy(cat_plan plan) {
   if (plan == nullptr) return CAT_OK;
   if (plan->d_tw) (void)hipFree(plan->d_tw);
   free_events(plan);
+
   delete plan;
   return CAT_OK;
 }
@@ -264,7 +276,7 @@ cat_status cat_plan_set_timing(cat_plan plan, int enable) {
   plan->calls = 0;
   if (!enable) return CAT_OK;
   if (!plan->ev) {
-    const int n = cat_plan_s::kSlots * cat_plan_s::kMaxK * 2;
+    const int n = cat_plan_s::kSlots * cat_plan_s::kMaxL * 2;
     plan->ev = new (std::nothrow) hipEvent_t[n]();
     if (!plan->ev) return fail(CAT_ERR_ALLOC, "event table allocation failed");
     for (int i = 0; i < n; ++i) {
@@ -279,26 +291,27 @@ cat_status cat_plan_set_timing(cat_plan plan, int enable) {
   return CAT_OK;
 }
 
-cat_status cat_plan_kernel_times(cat_plan plan, double* total_ms, int64_t* calls, int* nkernels) {
-  if (!plan || !total_ms || !calls || !nkernels) return fail(CAT_ERR_INVALID_ARG, "NULL argument");
+cat_status cat_plan_kernel_times(cat_plan plan, double* total_ms, int64_t* launches, int* nkernels) {
+  if (!plan || !total_ms || !launches || !nkernels) return fail(CAT_ERR_INVALID_ARG, "NULL argument");
   const int nk = plan->p.kind == CAT_1D ? 4 : 5;
   *nkernels = nk;
   for (int k = 0; k < 8; ++k) {
     total_ms[k] = 0.0;
-    calls[k] = 0;
+    launches[k] = 0;
   }
   if (!plan->ev || plan->calls == 0) return CAT_OK;
   const int64_t n = plan->calls < cat_plan_s::kSlots ? plan->calls : cat_plan_s::kSlots;
   for (int64_t c = 0; c < n; ++c) {
-    hipEvent_t* slot = plan->ev + (size_t)c * cat_plan_s::kMaxK * 2;
-    for (int k = 0; k < nk; ++k) {
-      hipError_t e = hipEventSynchronize(slot[2 * k + 1]);
-      if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    for (int i = 0; i < plan->nlaunch[c]; ++i) {
+      hipEvent_t* e = plan->ev + ((size_t)c * cat_plan_s::kMaxL + i) * 2;
+      hipError_t err = hipEventSynchronize(e[1]);
+      if (err != hipSuccess) return hip_fail(err, "hipEventSynchronize");
       float ms = 0.f;
-      e = hipEventElapsedTime(&ms, slot[2 * k], slot[2 * k + 1]);
-      if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+      err = hipEventElapsedTime(&ms, e[0], e[1]);
+      if (err != hipSuccess) return hip_fail(err, "hipEventElapsedTime");
+      const int k = plan->kind_of[c][i];
       total_ms[k] += ms;
-      calls[k] += 1;
+      launches[k] += 1;
     }
   }
   return CAT_OK;

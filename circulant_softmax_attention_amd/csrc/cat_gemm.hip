@@ -213,25 +213,33 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_xw_kernel(GemmArgs a) {
 
   const int lrow = lane & 15, lgrp = lane >> 4;
   const int sw = lrow & 7;  // row % 8 of every fragment row this lane reads
+  // All fragments of both K-chunks are read first, so that the LDS latency of
+  // the second chunk hides under the MFMAs of the first.
   auto compute = [&](int st) {
     const char* sa = smem + st * STAGE + (wm * 64 + lrow) * ROWB;
     const char* sb = smem + st * STAGE + BM * ROWB + (wn * (BN / 2) + lrow) * ROWB;
+    uint4 af[2][4], bfr[2][TN];
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
       const int pos = ((kc * 4 + lgrp) ^ sw) * 16;
-      uint4 af[4], bfr[TN];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const uint4*>(sa + 16 * i * ROWB + pos);
+      for (int i = 0; i < 4; ++i) af[kc][i] = *reinterpret_cast<const uint4*>(sa + 16 * i * ROWB + pos);
 #pragma unroll
-      for (int j = 0; j < TN; ++j) bfr[j] = *reinterpret_cast<const uint4*>(sb + 16 * j * ROWB + pos);
-      // W fragment as the MFMA's A operand, X fragment as B: the 16 x 16
-      // result is Y^T, so each lane ends with 4 consecutive channels of one
-      // token (see the stores below)
+      for (int j = 0; j < TN; ++j) bfr[kc][j] = *reinterpret_cast<const uint4*>(sb + 16 * j * ROWB + pos);
+    }
+    // W fragment as the MFMA's A operand, X fragment as B: the 16 x 16 result
+    // is Y^T, so each lane ends with 4 consecutive channels of one token (see
+    // the stores below)
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = mfma_chunk<ET>(bfr[j], af[i], acc[i][j]);
-      if (zwg) {
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma_chunk<ET>(bfr[kc][j], af[kc][i], acc[i][j]);
+    if (zwg) {
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        const int pos = ((kc * 4 + lgrp) ^ sw) * 16;
         const char* sz = smem + st * STAGE + (BM + BN + lrow) * ROWB + pos;
 #pragma unroll
         for (int zb = 0; zb < 2; ++zb) {
@@ -239,7 +247,7 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_xw_kernel(GemmArgs a) {
             const uint4 zf = *reinterpret_cast<const uint4*>(sz + 16 * zb * ROWB);
 #pragma unroll
             for (int ii = 0; ii < 2; ++ii) {
-              const uint4 xa = wn ? af[2 + ii] : af[ii];  // no dynamic register indexing
+              const uint4 xa = wn ? af[kc][2 + ii] : af[kc][ii];  // no dynamic register indexing
               zacc[ii][zb] = mfma_chunk<ET>(zf, xa, zacc[ii][zb]);
             }
           }

@@ -122,15 +122,15 @@ cat_status cat_forward_bccb_2d(cat_plan plan, const void* X, const void* W_Q, co
 /* Per-kernel timing (diagnostic).  While enabled, each forward call launches
  * every kernel with a start and a stop event that the kernel's own dispatch
  * stamps (hipExtLaunchKernel), into plan-owned slots (events are created
- * here, not in the forward calls; at most 512 calls are kept, older ones are
- * overwritten).  Enabling resets the slots.  cat_plan_kernel_times waits for
- * the recorded events and returns, per kernel of the path (1D: weight
+ * here, not in the forward calls; the last 256 calls are kept, at most 32
+ * launches each).  Enabling resets the slots.  cat_plan_kernel_times waits
+ * for the recorded events and returns, per kernel of the path (1D: weight
  * re-layout, projection, spectrum, fft-conv; 2D: weight re-layout,
  * projection, scores, spectrum, fft-conv), the summed milliseconds and the
- * number of calls measured; *nkernels receives the number of kernels (arrays
- * hold at least 8). */
+ * number of launches measured (a call may launch a kernel once per batch
+ * chunk); *nkernels receives the number of kernels (arrays hold at least 8). */
 cat_status cat_plan_set_timing(cat_plan plan, int enable);
-cat_status cat_plan_kernel_times(cat_plan plan, double* total_ms, int64_t* calls, int* nkernels);
+cat_status cat_plan_kernel_times(cat_plan plan, double* total_ms, int64_t* launches, int* nkernels);
 
 const char* cat_status_string(cat_status s);
 /* Message of the calling thread's last failed call ("" if none). */

@@ -53,8 +53,6 @@ def kernel_model(wl, L: int, ngrp: int):
     lines = BH * (d // 2)
     spec_bytes = BH * L * 8
     m = {}
-    nw = D * (D + H) if wl.kind == "1d" else 3 * D * D
-    m["wtranspose"] = dict(bytes=2 * nw * s, flops=0.0, unit="valu_f32")  # weights read and written once
     if wl.kind == "1d":
         # X read once, W_V and W_A, V written (storage dtype) and z written (fp32)
         m["project"] = dict(bytes=T * D * s + D * (D + H) * s + T * D * s + BH * N * 4,
@@ -85,7 +83,6 @@ KERNEL_SOURCES = {
     "project": ["circulant_softmax_attention_amd/csrc/cat_gemm.hip", "circulant_softmax_attention_amd/csrc/cat_common.hpp"],
 }
 KERNEL_SOURCES["spectrum"] = KERNEL_SOURCES["fftconv"]
-KERNEL_SOURCES["wtranspose"] = KERNEL_SOURCES["project"]
 KERNEL_SOURCES["scores"] = KERNEL_SOURCES["fftconv"]
 
 
@@ -219,6 +216,7 @@ def run(args):
     ngrp = (wl.d // 2 + 3) // 4
     model = kernel_model(wl, L, ngrp)
     kernels = {}
+    ktimes = {k: v for k, v in ktimes.items() if v[1] > 0}  # kernels this path launched
     for k, (ms, n) in ktimes.items():
         mm = model[k]
         per_call = max(1, round(n / args.steps))  # launches of this kernel per forward call

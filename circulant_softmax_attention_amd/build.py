@@ -48,13 +48,26 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
+def _stale(src: str) -> bool:
+    """True when the object of `src` is missing or older than the source or
+    any header it may include (every header of csrc/ and include/)."""
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    if not os.path.exists(obj):
+        return True
+    deps = [os.path.join(CSRC, src)]
+    for d, ext in ((CSRC, ".hpp"), (os.path.join(ROOT, "include"), ".h")):
+        deps += [os.path.join(d, f) for f in os.listdir(d) if f.endswith(ext)]
+    return os.path.getmtime(obj) < max(os.path.getmtime(f) for f in deps)
+
+
 def build(verbose: bool = True, only=None) -> str:
-    """Compile every source (or only the sources named in `only`, reusing the
-    other objects of an earlier build) and link libcat.so."""
+    """Compile every source (or the sources named in `only` plus every source
+    whose object is out of date, reusing the other objects) and link
+    libcat.so."""
     if shutil.which(HIPCC) is None and not os.path.exists(HIPCC):
         raise RuntimeError(f"hipcc not found at {HIPCC}")
     os.makedirs(BUILD, exist_ok=True)
-    todo = SOURCES if not only else [s for s in SOURCES if s in only]
+    todo = SOURCES if not only else [s for s in SOURCES if s in only or _stale(s)]
     if verbose:
         print(f"building {LIB} for {ARCH} ({len(todo)} of {len(SOURCES)} sources)", flush=True)
     with cf.ThreadPoolExecutor(max_workers=len(todo)) as ex:

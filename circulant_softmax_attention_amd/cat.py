@@ -30,8 +30,8 @@ EXPORTS = ["cat_plan_create", "cat_plan_destroy", "cat_plan_workspace_size", "ca
            "cat_forward_1d", "cat_forward_bccb_2d", "cat_status_string", "cat_last_error",
            "cat_plan_set_timing", "cat_plan_kernel_times",
            "cat_step_project", "cat_step_spectrum", "cat_step_mix", "cat_step_scores_2d"]
-KERNELS_1D = ["wtranspose", "project", "spectrum", "fftconv"]
-KERNELS_2D = ["wtranspose", "project", "scores", "spectrum", "fftconv"]
+KERNELS_1D = ["project", "spectrum", "fftconv"]
+KERNELS_2D = ["project", "scores", "spectrum", "fftconv"]
 
 
 class CatError(RuntimeError):
@@ -213,27 +213,25 @@ def cat_forward_bccb_2d(plan: Plan, X, W_Q, W_K, W_V, O=None, workspace=None, st
     return O
 
 
-def cat_step_project(plan: Plan, X, W_A, W_V, W_K=None, workspace=None, stream=None):
+def cat_step_project(plan: Plan, X, W_A, W_V, W_K=None, stream=None):
     """1D: returns (V [B,N,D] storage dtype, z [B,H,N] fp32).
     2D (W_A is W_Q): returns (Q fp32, K fp32, V storage dtype), all [B,N,D]."""
     B, N, D, H, dt = plan.B, plan.N, plan.D, plan.H, plan.dtype
     dev = X.device
     V = torch.empty((B, N, D), dtype=dt, device=dev)
-    if workspace is None:
-        workspace = alloc_workspace(plan, dev)
     if plan.kind == CAT_1D:
         z = torch.empty((B, H, N), dtype=torch.float32, device=dev)
         _check(_lib.cat_step_project(ctypes.c_void_p(plan.handle), _ptr(X, (B, N, D), dt, "X"),
                                      _ptr(W_A, (D, H), dt, "W_A"), ctypes.c_void_p(None),
                                      _ptr(W_V, (D, D), dt, "W_V"), _ptr(V), _ptr(z), ctypes.c_void_p(None),
-                                     _ptr(workspace), _stream_ptr(stream)), "cat_step_project")
+                                     _stream_ptr(stream)), "cat_step_project")
         return V, z
     Q = torch.empty((B, N, D), dtype=torch.float32, device=dev)
     K = torch.empty((B, N, D), dtype=torch.float32, device=dev)
     _check(_lib.cat_step_project(ctypes.c_void_p(plan.handle), _ptr(X, (B, N, D), dt, "X"),
                                  _ptr(W_A, (D, D), dt, "W_Q"), _ptr(W_K, (D, D), dt, "W_K"),
                                  _ptr(W_V, (D, D), dt, "W_V"), _ptr(V), _ptr(Q), _ptr(K),
-                                 _ptr(workspace), _stream_ptr(stream)), "cat_step_project")
+                                 _stream_ptr(stream)), "cat_step_project")
     return Q, K, V
 
 

@@ -26,11 +26,11 @@ struct cat_plan_s {
   int Gs;            // lines per spectrum workgroup
   int npair, ngrp, ppg;  // 2D score partials
   float2* d_tw;      // 1D inter-pass twiddles, L entries (null in 2D)
-  size_t off_W, off_V, off_z, off_Q, off_K, off_part, off_spec, ws_bytes;
+  size_t off_V, off_z, off_Q, off_K, off_part, off_spec, ws_bytes;
   bool debug_sync;
   int num_cu;        // compute units of the device current at plan creation
   // per-launch timing slots: ev[slot][launch][start/stop], kind[slot][launch]
-  static constexpr int kSlots = 256, kMaxL = 32, kMaxK = 5;
+  static constexpr int kSlots = 256, kMaxL = 32, kMaxK = 4;
   bool timing = false;
   hipEvent_t* ev = nullptr;
   int8_t kind_of[kSlots][kMaxL];
@@ -198,8 +198,6 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
   const size_t BND = (size_t)p->B * p->N * p->D;
   const size_t BH = (size_t)p->B * p->H;
   size_t off = 0;
-  pl->off_W = off;  // output-major copies of the weights
-  off = up256(off + (size_t)p->D * (p->kind == CAT_1D ? p->D + p->H : 3 * p->D) * pl->esz);
   pl->off_V = off;
   off = up256(off + BND * pl->esz);
   pl->off_spec = off;
@@ -293,7 +291,7 @@ cat_status cat_plan_set_timing(cat_plan plan, int enable) {
 
 cat_status cat_plan_kernel_times(cat_plan plan, double* total_ms, int64_t* launches, int* nkernels) {
   if (!plan || !total_ms || !launches || !nkernels) return fail(CAT_ERR_INVALID_ARG, "NULL argument");
-  const int nk = plan->p.kind == CAT_1D ? 4 : 5;
+  const int nk = plan->p.kind == CAT_1D ? 3 : 4;
   *nkernels = nk;
   for (int k = 0; k < 8; ++k) {
     total_ms[k] = 0.0;
@@ -393,24 +391,6 @@ ConvArgs conv_base(const cat_plan_s* pl, const void* Vblk, const float2* spec, v
   return a;
 }
 
-// Output-major copies W^T of the n weights in the workspace (one launch);
-// wt[i] receives the address of W_i^T.
-hipError_t transpose_weights(const cat_plan_s* pl, void* ws, int n, const void* const* W, const int* cols,
-                             const void** wt, hipStream_t s, const LaunchTiming* t = nullptr) {
-  TransposeArgs ta{};
-  ta.n = n;
-  char* dst = ws_at(ws, pl->off_W);
-  for (int i = 0; i < n; ++i) {
-    ta.src[i] = W[i];
-    ta.dst[i] = dst;
-    ta.rows[i] = (int)pl->p.D;
-    ta.cols[i] = cols[i];
-    wt[i] = dst;
-    dst += (size_t)pl->p.D * cols[i] * pl->esz;
-  }
-  return launch_transpose(pl->et, ta, s, t);
-}
-
 }  // namespace
 
 extern "C" {
@@ -427,32 +407,25 @@ cat_status cat_forward_1d(cat_plan plan, const void* X, const void* W_A, const v
   float* z = reinterpret_cast<float*>(ws_at(workspace, plan->off_z));
   KernelMark mk(plan);
 
-  const void* W[2] = {W_V, W_A};
-  const int cols[2] = {(int)plan->p.D, (int)plan->p.H};
-  const void* Wt[2];
-  hipError_t e = transpose_weights(plan, workspace, 2, W, cols, Wt, s, mk.at(0));
-  if (e != hipSuccess) return hip_fail(e, "weight transpose launch");
-  if ((st = check_sync(plan, "weight transpose")) != CAT_OK) return st;
-
   // V = X W_V (blocked for the transform) and the logits z = X W_A in one pass
   GemmArgs ga = gemm_base(plan, X);
   ga.nseg = 1;
-  ga.seg[0] = seg(Wt[0], Vb, (int)plan->p.D, 0, OUT_BLOCKED, 2 * plan->G);
-  ga.Wz = Wt[1];
+  ga.seg[0] = seg(W_V, Vb, (int)plan->p.D, 0, OUT_BLOCKED, 2 * plan->G);
+  ga.Wz = W_A;
   ga.z = z;
   ga.nz = (int)plan->p.H;
-  e = launch_gemm(plan->et, ga, s, mk.at(1));
+  hipError_t e = launch_gemm(plan->et, ga, s, mk.at(0));
   if (e != hipSuccess) return hip_fail(e, "projection launch");
   if ((st = check_sync(plan, "projection")) != CAT_OK) return st;
 
   SpecArgs sa = spec_base(plan, workspace);
   sa.logits = z;
-  e = launch_spectrum(plan->geom, 0, sa, s, mk.at(2));
+  e = launch_spectrum(plan->geom, 0, sa, s, mk.at(1));
   if (e != hipSuccess) return hip_fail(e, "spectrum launch");
   if ((st = check_sync(plan, "spectrum")) != CAT_OK) return st;
 
   ConvArgs ca = conv_base(plan, Vb, sa.spec, O);
-  e = launch_conv(plan->geom, plan->et, ca, s, mk.at(3));
+  e = launch_conv(plan->geom, plan->et, ca, s, mk.at(2));
   if (e != hipSuccess) return hip_fail(e, "fft-conv launch");
   return check_sync(plan, "fft-conv");
 }
@@ -472,19 +445,12 @@ cat_status cat_forward_bccb_2d(cat_plan plan, const void* X, const void* W_Q, co
   const int D = (int)plan->p.D;
   KernelMark mk(plan);
 
-  const void* W[3] = {W_Q, W_K, W_V};
-  const int cols[3] = {D, D, D};
-  const void* Wt[3];
-  hipError_t e = transpose_weights(plan, workspace, 3, W, cols, Wt, s, mk.at(0));
-  if (e != hipSuccess) return hip_fail(e, "weight transpose launch");
-  if ((st = check_sync(plan, "weight transpose")) != CAT_OK) return st;
-
   GemmArgs ga = gemm_base(plan, X);
   ga.nseg = 3;
-  ga.seg[0] = seg(Wt[0], Qb, D, 1, OUT_BLOCKED, 2);
-  ga.seg[1] = seg(Wt[1], Kb, D, 1, OUT_BLOCKED, 2);
-  ga.seg[2] = seg(Wt[2], Vb, D, 0, OUT_BLOCKED, 2 * plan->G);
-  e = launch_gemm(plan->et, ga, s, mk.at(1));
+  ga.seg[0] = seg(W_Q, Qb, D, 1, OUT_BLOCKED, 2);
+  ga.seg[1] = seg(W_K, Kb, D, 1, OUT_BLOCKED, 2);
+  ga.seg[2] = seg(W_V, Vb, D, 0, OUT_BLOCKED, 2 * plan->G);
+  hipError_t e = launch_gemm(plan->et, ga, s, mk.at(0));
   if (e != hipSuccess) return hip_fail(e, "projection launch");
   if ((st = check_sync(plan, "projection")) != CAT_OK) return st;
 
@@ -497,7 +463,7 @@ cat_status cat_forward_bccb_2d(cat_plan plan, const void* X, const void* W_Q, co
   sc.npair = plan->npair;
   sc.ngrp = plan->ngrp;
   sc.ppg = plan->ppg;
-  e = launch_score_partial(plan->geom, sc, s, mk.at(2));
+  e = launch_score_partial(plan->geom, sc, s, mk.at(1));
   if (e != hipSuccess) return hip_fail(e, "score launch");
   if ((st = check_sync(plan, "scores")) != CAT_OK) return st;
 
@@ -505,50 +471,40 @@ cat_status cat_forward_bccb_2d(cat_plan plan, const void* X, const void* W_Q, co
   sa.partial = part;
   sa.ngrp = plan->ngrp;
   sa.scale = 1.0f / std::sqrt((float)plan->d);
-  e = launch_spectrum(plan->geom, 1, sa, s, mk.at(3));
+  e = launch_spectrum(plan->geom, 1, sa, s, mk.at(2));
   if (e != hipSuccess) return hip_fail(e, "spectrum launch");
   if ((st = check_sync(plan, "spectrum")) != CAT_OK) return st;
 
   ConvArgs ca = conv_base(plan, Vb, sa.spec, O);
-  e = launch_conv(plan->geom, plan->et, ca, s, mk.at(4));
+  e = launch_conv(plan->geom, plan->et, ca, s, mk.at(3));
   if (e != hipSuccess) return hip_fail(e, "fft-conv launch");
   return check_sync(plan, "fft-conv");
 }
 
 cat_status cat_step_project(cat_plan plan, const void* X, const void* W_A, const void* W_K,
-                            const void* W_V, void* V, void* z, void* K_out, void* workspace, void* stream) {
+                            const void* W_V, void* V, void* z, void* K_out, void* stream) {
   if (!plan) return fail(CAT_ERR_INVALID_ARG, "NULL plan");
   if (plan->p.B == 0) return CAT_OK;
   const bool two_d = plan->p.kind == CAT_BCCB_2D;
-  cat_status st = two_d ? check_ptrs({X, W_A, W_K, W_V, V, z, K_out, workspace})
-                        : check_ptrs({X, W_A, W_V, V, z, workspace});
+  cat_status st = two_d ? check_ptrs({X, W_A, W_K, W_V, V, z, K_out}) : check_ptrs({X, W_A, W_V, V, z});
   if (st != CAT_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int D = (int)plan->p.D;
-  // 1D: W_V^T then W_A^T (as in the forward call); 2D: W_Q^T, W_K^T, W_V^T
-  const void* W1[2] = {W_V, W_A};
-  const int c1[2] = {D, (int)plan->p.H};
-  const void* W2[3] = {W_A, W_K, W_V};
-  const int c2[3] = {D, D, D};
-  const void* Wt[3];
-  hipError_t e = two_d ? transpose_weights(plan, workspace, 3, W2, c2, Wt, s)
-                       : transpose_weights(plan, workspace, 2, W1, c1, Wt, s);
-  if (e != hipSuccess) return hip_fail(e, "weight transpose launch");
   GemmArgs ga = gemm_base(plan, X);
   if (!two_d) {
     // the forward path's kernel: value GEMM with the fused score projection
     ga.nseg = 1;
-    ga.seg[0] = seg(Wt[0], V, D, 0, OUT_ROWMAJOR, 1);
-    ga.Wz = Wt[1];
+    ga.seg[0] = seg(W_V, V, D, 0, OUT_ROWMAJOR, 1);
+    ga.Wz = W_A;
     ga.z = reinterpret_cast<float*>(z);
     ga.nz = (int)plan->p.H;
   } else {
     ga.nseg = 3;
-    ga.seg[0] = seg(Wt[0], z, D, 1, OUT_ROWMAJOR, 1);
-    ga.seg[1] = seg(Wt[1], K_out, D, 1, OUT_ROWMAJOR, 1);
-    ga.seg[2] = seg(Wt[2], V, D, 0, OUT_ROWMAJOR, 1);
+    ga.seg[0] = seg(W_A, z, D, 1, OUT_ROWMAJOR, 1);
+    ga.seg[1] = seg(W_K, K_out, D, 1, OUT_ROWMAJOR, 1);
+    ga.seg[2] = seg(W_V, V, D, 0, OUT_ROWMAJOR, 1);
   }
-  e = launch_gemm(plan->et, ga, s);
+  hipError_t e = launch_gemm(plan->et, ga, s);
   if (e != hipSuccess) return hip_fail(e, "projection launch");
   return check_sync(plan, "projection");
 }

@@ -62,7 +62,7 @@ __host__ __device__ inline uint32_t fastdiv(uint32_t x, const FastDiv& f) {
 }
 
 struct GemmSeg {
-  const void* W;  // Wt [ncols][K] row-major (output-major), same element type as X
+  const void* W;  // [K][ncols] row-major, same element type as X; ncols a multiple of 16 bytes
   void* out;
   int ncols;
   int out_f32;  // 1: fp32 output; 0: the input element type
@@ -78,29 +78,20 @@ struct GemmArgs {
   int M, K;
   int Ntok, H, d;
   int nseg;
-  // optional score projection (1D): z [M / Ntok][nz][Ntok] fp32 = X . Wz^T,
-  // Wz = W_A^T [nz][K]; nz = 0 disables it, at most 32
+  // optional score projection (1D): z [M / Ntok][nz][Ntok] fp32 = X . Wz,
+  // Wz = W_A [K][nz]; nz = 0 disables it, at most 32
   const void* Wz;
   float* z;
   int nz;
   int tile_n;  // output tile width (96 or 128); 0 lets the launcher choose
+  FastDiv fd_nz;  // filled by the launcher
   int num_cu;  // compute units of the device (0: assume 256)
   // filled by the launcher
+  int nzwg;  // score-projection workgroups ahead of the output tiles
   int ncoltiles;
   FastDiv fd_ntok, fd_d;
   GemmSeg seg[3];
 };
-
-// Weight re-layout for the GEMM: dst[m] [cols][rows] = src[m] [rows][cols]^T
-// for up to four matrices in one launch.
-struct TransposeArgs {
-  const void* src[4];
-  void* dst[4];
-  int rows[4], cols[4];
-  int n;
-  int tile0[5];  // filled by the launcher: first workgroup of each matrix
-};
-hipError_t launch_transpose(int et, TransposeArgs a, hipStream_t stream, const LaunchTiming* t = nullptr);
 
 // Launch Y_s = X . W_s for every segment s (and z when nz > 0); returns
 // hipSuccess or the launch error.

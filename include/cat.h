@@ -39,8 +39,8 @@
  * Forward calls only enqueue work ordered after everything already queued on
  * `stream` (a hipStream_t passed as void*; NULL is the default stream), and
  * everything queued on `stream` afterwards runs after it; every kernel of a
- * call runs on `stream` (1D: weight re-layout, projection with the fused
- * score projection, softmax + spectrum, fft-conv).  Calls never allocate, never
+ * call runs on `stream` (1D: projection with the fused score projection,
+ * softmax + spectrum, fft-conv).  Calls never allocate, never
  * synchronise, and return as soon as the work is queued.  A plan owns small
  * device tables created at plan creation; the workspace (size from
  * cat_plan_workspace_size) holds the intermediates and is owned by the
@@ -124,11 +124,10 @@ cat_status cat_forward_bccb_2d(cat_plan plan, const void* X, const void* W_Q, co
  * stamps (hipExtLaunchKernel), into plan-owned slots (events are created
  * here, not in the forward calls; the last 256 calls are kept, at most 32
  * launches each).  Enabling resets the slots.  cat_plan_kernel_times waits
- * for the recorded events and returns, per kernel of the path (1D: weight
- * re-layout, projection, spectrum, fft-conv; 2D: weight re-layout,
- * projection, scores, spectrum, fft-conv), the summed milliseconds and the
- * number of launches measured (a call may launch a kernel once per batch
- * chunk); *nkernels receives the number of kernels (arrays hold at least 8). */
+ * for the recorded events and returns, per kernel of the path (1D:
+ * projection, spectrum, fft-conv; 2D: projection, scores, spectrum,
+ * fft-conv), the summed milliseconds and the number of launches measured;
+ * *nkernels receives the number of kernels (arrays hold at least 8). */
 cat_status cat_plan_set_timing(cat_plan plan, int enable);
 cat_status cat_plan_kernel_times(cat_plan plan, double* total_ms, int64_t* launches, int* nkernels);
 
@@ -143,11 +142,9 @@ const char* cat_last_error(void);
 /* Projection step.  1D plan: V [B][N][D] (storage dtype) = X W_V and
  * z [B][H][N] (fp32) = logits X W_A (W_K ignored).  2D plan: Q, K [B][N][D]
  * fp32 = X W_Q, X W_K and V (storage dtype) = X W_V; pass W_A = W_Q,
- * z = Q (fp32 [B][N][D]) and K_out for K.  The workspace (the plan's size)
- * holds the re-laid-out weights. */
+ * z = Q (fp32 [B][N][D]) and K_out for K.  No workspace is used. */
 cat_status cat_step_project(cat_plan plan, const void* X, const void* W_A, const void* W_K,
-                            const void* W_V, void* V, void* z, void* K_out, void* workspace,
-                            void* stream);
+                            const void* W_V, void* V, void* z, void* K_out, void* stream);
 
 /* Softmax + filter spectrum step from logits.  logits [B][H][N] fp32 (1D: z;
  * 2D: the scaled scores a).  probs [B][H][N] fp32 receives the softmax

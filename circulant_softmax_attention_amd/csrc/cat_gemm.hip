@@ -372,35 +372,32 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_xw_kernel(GemmArgs a) {
     }
   };
 
-  // All fragments of both K-chunks are read first, so that the LDS latency of
-  // the second chunk hides under the MFMAs of the first.
-  auto compute = [&](int st) {
+  // Fragments of K-chunk kc (0 or 1) of the tile in stage st.
+  auto read_frags = [&](int st, int kc, uint4 (&af)[4], uint4 (&bf)[TN]) {
     const char* sa = smem + st * STAGE + (wm * 64 + lrow) * ROWB;
     const char* sb = smem + st * STAGE + BM * ROWB;
-    uint4 af[2][4], bfr[2][TN];
+    const int pos = ((kc * 4 + lgrp) ^ sw) * 16;
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-      const int pos = ((kc * 4 + lgrp) ^ sw) * 16;
+    for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const uint4*>(sa + 16 * i * ROWB + pos);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) af[kc][i] = *reinterpret_cast<const uint4*>(sa + 16 * i * ROWB + pos);
+    for (int j = 0; j < TN; ++j) bf[j] = kfrag(sb, PB, CPRB, wn * (BN / 2) + 16 * j, kc);
+  };
+  // W fragment as the MFMA's A operand, X fragment as B: the 16 x 16 result
+  // is Y^T, so each lane ends with 4 consecutive channels of one token (see
+  // the stores below)
+  auto mma = [&](const uint4 (&af)[4], const uint4 (&bf)[TN]) {
 #pragma unroll
-      for (int j = 0; j < TN; ++j) bfr[kc][j] = kfrag(sb, PB, CPRB, wn * (BN / 2) + 16 * j, kc);
-    }
-    // W fragment as the MFMA's A operand, X fragment as B: the 16 x 16 result
-    // is Y^T, so each lane ends with 4 consecutive channels of one token (see
-    // the stores below)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = mfma_chunk<ET>(bfr[kc][j], af[kc][i], acc[i][j]);
+      for (int j = 0; j < TN; ++j) acc[i][j] = mfma_chunk<ET>(bf[j], af[i], acc[i][j]);
   };
 
-  // Tile kt lives in stage kt % 2.  At the top of step kt every wave has its
-  // own DMA of tile kt complete and, after the barrier,
-  // all of them have finished multiplying tile kt - 1, whose stage then
-  // receives tile kt + 1.
+  // Tile kt lives in stage kt % 2.  Each step multiplies K-chunk 0 of tile
+  // kt while the fragments of its chunk 1 are read, then -- once every wave
+  // has its DMA of tile kt + 1 complete and has finished reading stage kt --
+  // sends tile kt + 2 into stage kt % 2 and multiplies chunk 1 while the
+  // fragments of chunk 0 of tile kt + 1 are read.  The MFMAs thus always have
+  // LDS reads to overlap with.
   const int nk = (K + BK - 1) / BK;
   issue(0, 0);
   // L2 warm-up: the column tiles of one row panel (consecutive workgroups on
@@ -423,21 +420,74 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_xw_kernel(GemmArgs a) {
       wv[u] = *reinterpret_cast<const uint32_t*>(xb + (size_t)r * K * ESZ + (size_t)c * 64);
     }
   }
+  wait_vmem_all();
+  __syncthreads();
+  if (nk > 1) issue(1, 1);
+  uint4 a0[4], b0[TN], a1[4], b1[TN];
+  read_frags(0, 0, a0, b0);
   for (int kt = 0; kt < nk; ++kt) {
-    wait_vmem_all();
-    __syncthreads();
-    if (kt + 1 < nk) issue(kt + 1, (kt + 1) & 1);
-    compute(kt & 1);
+    const int st = kt & 1;
+    read_frags(st, 1, a1, b1);
+    mma(a0, b0);
+    if (kt + 1 < nk) {
+      wait_vmem_all();  // this wave's DMA of tile kt + 1
+      __syncthreads();  // every wave's, and every wave done reading stage st
+      if (kt + 2 < nk) issue(kt + 2, st);
+      read_frags(st ^ 1, 0, a0, b0);
+    }
+    mma(a1, b1);
   }
   if (((wv[0] ^ wv[1]) + (wv[2] ^ wv[3])) == 0x9E3779B9u && M < 0)  // keeps the warm-up loads
     reinterpret_cast<float*>(sg.out)[0] = 0.f;
 
   // Result layout (16 x 16 MFMA, A = W rows, B = X rows): lane (lrow, lgrp)
   // holds Y[token][channel] for token = tile row base + lrow and the four
-  // channels 4 lgrp + v, v = 0..3, of each 16-channel block.  Written
-  // straight from registers: 8 (bf16) or 16 (fp32) bytes per lane, and the 16
-  // lanes of a channel block cover 16 consecutive tokens.
+  // channels 4 lgrp + v, v = 0..3, of each 16-channel block.
   const bool f32out = ET == ET_F32 || sg.out_f32;
+  // Staged epilogue: when every aligned group of 16 bytes of channels is
+  // contiguous in the output, the tile goes through LDS (free once every wave
+  // is done with the last K tile) and leaves in 16-byte stores whose lanes
+  // cover whole row segments -- far faster for the memory system than the
+  // 8-byte, 16-rows-apart stores the register layout gives.
+  const int vo = f32out ? 4 : 8;  // channels per 16 bytes of output
+  const bool staged = (sg.layout == OUT_ROWMAJOR && ncols % vo == 0) ||
+                      (sg.layout == OUT_BLOCKED && sg.cg % vo == 0 && a.d % vo == 0);
+  if (staged) {
+    auto stage_out = [&](auto osz_tag) {
+      constexpr int OSZ = decltype(osz_tag)::value;
+      constexpr int VO = 16 / OSZ;
+      constexpr int CPR = BN * OSZ / 16;  // 16-byte chunks per tile row
+      constexpr int PITCH = BM * (BN * OSZ + 16) <= SMEM ? BN * OSZ + 16 : BN * OSZ;
+      constexpr int PER = BM * CPR / NTHR;
+      static_assert(PER * NTHR == BM * CPR && BM * PITCH <= SMEM, "staged tile");
+      __syncthreads();  // every wave is done reading the last K tile
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const floatx4 v = acc[i][j];
+          char* dst = smem + (wm * 64 + 16 * i + lrow) * PITCH + (wn * (BN / 2) + 16 * j + 4 * lgrp) * OSZ;
+          if constexpr (OSZ == 4) *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+          else *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+        }
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int c = tid + NTHR * u;
+        const int row = c / CPR, cc = c - row * CPR;
+        const int token = m0 + row, ch = n0 + cc * VO;
+        if (token < M && ch < ncols) {
+          const uint4 v = *reinterpret_cast<const uint4*>(smem + row * PITCH + cc * 16);
+          *reinterpret_cast<uint4*>(reinterpret_cast<char*>(sg.out) + out_index(sg, a, token, ch) * OSZ) = v;
+        }
+      }
+    };
+    if (f32out) stage_out(std::integral_constant<int, 4>{});
+    else stage_out(std::integral_constant<int, 2>{});
+    return;
+  }
+  // Otherwise straight from registers: 8 (bf16) or 16 (fp32) bytes per lane,
+  // the 16 lanes of a channel block covering 16 consecutive tokens.
   const bool quad = (sg.layout == OUT_ROWMAJOR && (ncols & 3) == 0) ||
                     (sg.layout == OUT_BLOCKED && (a.d & 3) == 0 && (sg.cg & 3) == 0);
 #pragma unroll

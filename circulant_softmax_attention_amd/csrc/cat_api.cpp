@@ -28,6 +28,7 @@ struct cat_plan_s {
   float2* d_tw;      // 1D inter-pass twiddles, L entries (null in 2D)
   size_t off_V, off_z, off_Q, off_K, off_part, off_spec, ws_bytes;
   bool debug_sync;
+  int tile_n;        // forced GEMM tile width (0: the GEMM chooses)
   int num_cu;        // compute units of the device current at plan creation
   // per-launch timing slots: ev[slot][launch][start/stop], kind[slot][launch]
   static constexpr int kSlots = 256, kMaxL = 32, kMaxK = 4;
@@ -194,6 +195,9 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
   pl->ngrp = (d2 + pl->ppg - 1) / pl->ppg;
   const char* ds = std::getenv("CAT_DEBUG_SYNC");
   pl->debug_sync = ds && ds[0] == '1';
+  const char* tn = std::getenv("CAT_GEMM_TILE_N");
+  pl->tile_n = tn ? std::atoi(tn) : 0;
+  if (pl->tile_n != 96 && pl->tile_n != 128 && pl->tile_n != 192) pl->tile_n = 0;
 
   const size_t BND = (size_t)p->B * p->N * p->D;
   const size_t BH = (size_t)p->B * p->H;
@@ -350,6 +354,7 @@ GemmArgs gemm_base(const cat_plan_s* pl, const void* X) {
   a.H = (int)pl->p.H;
   a.d = pl->d;
   a.num_cu = pl->num_cu;
+  a.tile_n = pl->tile_n;
   return a;
 }
 

@@ -52,7 +52,6 @@ namespace {
 
 constexpr int BM = 128, NTHR = 256;
 constexpr int ZMAX = 32;   // score-projection columns (heads) one launch covers
-constexpr int ZROWS = 64;  // X rows per score-projection workgroup (16 per wave)
 constexpr int ROWB = 128;  // bytes of one X row of a K tile
 
 template <int ET>
@@ -113,125 +112,8 @@ __device__ __forceinline__ size_t out_index(const GemmSeg& s, const GemmArgs& a,
   return (((size_t)(b * a.H + h) * ng + g) * a.Ntok + tok) * s.cg + j;
 }
 
-// Score projection of rows zt * 64 .. + 63: z [M / Ntok][nz][Ntok] fp32.
-// Wave w takes the 16 rows 16 w ..; lane (lrow, lgrp) loads, for every K step
-// of 4 chunks, the 16-byte chunk lgrp of row lrow -- the MFMA's A operand --
-// and reads the same K positions of head lrow of W_A^T from LDS as B.  The
-// result lane then holds head lrow for the 4 consecutive tokens 4 lgrp + v.
-// K goes in passes of KC values (768 bf16 / 384 fp32, so D = 768 bf16 takes
-// one).  A pass first issues its W_A loads (the contiguous [kn][nz] block, in
-// 16-byte chunks), then all its X loads, then scatters W_A into the
-// head-major LDS rows while the X loads are still in flight.
-template <int ET>
-__device__ __forceinline__ void zproj_tile(const GemmArgs& a, int zt, char* smem) {
-  using C = GemmCfg<ET>;
-  constexpr int VE = C::VE, ESZ = C::ESZ;
-  constexpr int KSTEP = 4 * VE;                       // K per MFMA chunk step (4 lane groups)
-  constexpr int KC = 1536 / ESZ;                      // K per pass
-  constexpr int NL = KC / KSTEP;                      // X chunk loads per lane per pass
-  constexpr int PITCH = KC * ESZ + 16;                // LDS row pitch: the 16 rows of one read hit distinct banks
-  constexpr int WCH = (KC * 16 * ESZ / 16 + NTHR - 1) / NTHR;  // W_A chunks per thread and batch
-  using elem_t = typename std::conditional<ET == ET_F32, float, uint16_t>::type;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lrow = lane & 15, lgrp = lane >> 4;
-  const int M = a.M, K = a.K, nz = a.nz;
-  const int nzb = (nz + 15) >> 4;
-  const int row = zt * ZROWS + wave * 16 + lrow;
-  const elem_t* xrow = reinterpret_cast<const elem_t*>(a.X) + (size_t)(row < M ? row : M - 1) * K + VE * lgrp;
-  floatx4 zacc[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
-  for (int kp = 0; kp < K; kp += KC) {
-    const int kn = K - kp < KC ? K - kp : KC;
-    // [kn][nz] block of W_A: kn nz ESZ bytes, a whole number of chunks
-    // since K % 8 == 0 and the pass starts at a multiple of 1536 nz bytes.
-    // Loaded in batches of WCH chunks per thread (one batch covers up to 16
-    // heads; the first batch goes out ahead of the X loads).
-    const int nch = kn * nz * ESZ / 16;
-    const uint4* wsrc = reinterpret_cast<const uint4*>(reinterpret_cast<const elem_t*>(a.Wz) + (size_t)kp * nz);
-    uint4 wr[WCH];
-    auto wload = [&](int c0) {
-#pragma unroll
-      for (int i = 0; i < WCH; ++i) {
-        const int c = c0 + tid + NTHR * i;
-        wr[i] = c < nch ? wsrc[c] : make_uint4(0, 0, 0, 0);
-      }
-    };
-    // W_A^T[h][k - kp]; heads beyond nz are never written and only reach
-    // results that are never stored
-    auto wscatter = [&](int c0) {
-#pragma unroll
-      for (int i = 0; i < WCH; ++i) {
-        const int c = c0 + tid + NTHR * i;
-        if (c < nch) {
-          const elem_t* e = reinterpret_cast<const elem_t*>(&wr[i]);
-          uint32_t k = fastdiv((uint32_t)(c * VE), a.fd_nz);
-          uint32_t h = (uint32_t)(c * VE) - k * (uint32_t)nz;
-#pragma unroll
-          for (int u = 0; u < VE; ++u) {
-            *reinterpret_cast<elem_t*>(smem + h * PITCH + k * ESZ) = e[u];
-            if (++h == (uint32_t)nz) {
-              h = 0;
-              ++k;
-            }
-          }
-        }
-      }
-    };
-    wload(0);
-    uint4 xr[NL];
-#pragma unroll
-    for (int s = 0; s < NL; ++s) {
-      const int k = kp + s * KSTEP + VE * lgrp;  // K % VE == 0: a chunk is all in or all out
-      xr[s] = k < K ? *reinterpret_cast<const uint4*>(xrow + kp + s * KSTEP) : make_uint4(0, 0, 0, 0);
-    }
-    if (kp > 0) __syncthreads();  // every wave is done reading the previous pass
-    wscatter(0);
-    for (int c0 = WCH * NTHR; c0 < nch; c0 += WCH * NTHR) {
-      wload(c0);
-      wscatter(c0);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int s = 0; s < NL; ++s) {
-      if (kp + s * KSTEP >= K) break;  // uniform
-      // in the last step of a K that is not a multiple of KSTEP, lane groups
-      // past K take zeros for both operands (the LDS there was not written)
-      const bool kin = kp + s * KSTEP + VE * lgrp < K;
-#pragma unroll
-      for (int zb = 0; zb < 2; ++zb) {
-        if (zb < nzb) {
-          uint4 w = *reinterpret_cast<const uint4*>(smem + (16 * zb + lrow) * PITCH + (s * KSTEP + VE * lgrp) * ESZ);
-          w = kin ? w : make_uint4(0, 0, 0, 0);
-          zacc[zb] = mfma_chunk<ET>(xr[s], w, zacc[zb]);
-        }
-      }
-    }
-  }
-  // lane: head 16 zb + lrow, tokens 4 lgrp + v of the wave's 16 rows
-  const int m = zt * ZROWS + wave * 16 + 4 * lgrp;
-  const uint32_t b = fastdiv((uint32_t)(m < M ? m : M - 1), a.fd_ntok);
-  const int tok = m - (int)b * a.Ntok;
-  const bool vec = m + 3 < M && tok + 3 < a.Ntok && (a.Ntok & 3) == 0;
-#pragma unroll
-  for (int zb = 0; zb < 2; ++zb) {
-    const int head = 16 * zb + lrow;
-    if (zb >= nzb || head >= nz) continue;
-    if (vec) {
-      float* dst = a.z + ((size_t)b * nz + head) * a.Ntok + tok;
-      *reinterpret_cast<float4*>(dst) = make_float4(zacc[zb][0], zacc[zb][1], zacc[zb][2], zacc[zb][3]);
-    } else {
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int mv = m + v;
-        if (mv >= M) break;
-        const uint32_t bv = fastdiv((uint32_t)mv, a.fd_ntok);
-        const int tv = mv - (int)bv * a.Ntok;
-        a.z[((size_t)bv * nz + head) * a.Ntok + tv] = zacc[zb][v];
-      }
-    }
-  }
-}
-
-template <int ET, int BN>
+// ZB: 16-head blocks of the score projection (0: none, at most 2).
+template <int ET, int BN, int ZB>
 __global__ __launch_bounds__(NTHR, 2) void gemm_xw_kernel(GemmArgs a) {
   using C = GemmCfg<ET>;
   constexpr int VE = C::VE, BK = C::BK, ESZ = C::ESZ;
@@ -242,7 +124,6 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_xw_kernel(GemmArgs a) {
   constexpr int BCH = BK * CPRB / NTHR;         // W chunks per thread
   constexpr int TN = BN / 32;                   // 16-column MFMA blocks per wave
   static_assert(BCH * NTHR == BK * CPRB && TN * 32 == BN, "tile width");
-  static_assert(ZMAX * (1536 + 16) <= SMEM, "score-projection pass fits the LDS");
   using elem_t = typename std::conditional<ET == ET_F32, float, uint16_t>::type;
   __shared__ __attribute__((aligned(16))) char smem[SMEM];
 
@@ -250,11 +131,7 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_xw_kernel(GemmArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
-  if ((int)blockIdx.x < a.nzwg) {  // score-projection workgroups come first
-    zproj_tile<ET>(a, blockIdx.x, smem);
-    return;
-  }
-  const int q = xcd_remap((int)blockIdx.x - a.nzwg, (int)gridDim.x - a.nzwg);
+  const int q = xcd_remap(blockIdx.x, gridDim.x);
   const int rt = q / a.ncoltiles;
   const int ctg = q - rt * a.ncoltiles;  // column tile over all segments
   int ct = ctg;
@@ -266,6 +143,20 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_xw_kernel(GemmArgs a) {
   const GemmSeg sg = a.seg[si];
   const int m0 = rt * BM, n0 = ct * BN;
   const int M = a.M, K = a.K, ncols = sg.ncols;
+
+  // Score projection (first segment only): the first nct <= 8 column tiles
+  // of a row panel share its eight 16-row blocks, block rb going to column
+  // tile rb % nct and, inside it, to wave (rb / 4, rb % 2).  A wave thus
+  // handles blocks 4 wm + wn + 2 ii, ii = 0, 1, of its own X rows.  The
+  // W_A^T fragments come straight from global memory (W_A is a few KB and
+  // stays cached), a K tile ahead of their use.
+  const int nz = a.nz;
+  const int nct = a.seg[0].ntiles < 8 ? a.seg[0].ntiles : 8;
+  const bool zon = ZB > 0 && si == 0 && ct < nct;
+  bool zrb[2];
+#pragma unroll
+  for (int ii = 0; ii < 2; ++ii) zrb[ii] = zon && (4 * wm + wn + 2 * ii) % nct == ct;
+  const bool zwave = zrb[0] || zrb[1];
 
   // X tile: chunk slot s = tid + 256 i is row s / 8, 16-byte position s % 8,
   // and holds K-chunk (s % 8) ^ (row % 8) -- the same chunk for every i,
@@ -392,14 +283,57 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_xw_kernel(GemmArgs a) {
       for (int j = 0; j < TN; ++j) acc[i][j] = mfma_chunk<ET>(bf[j], af[i], acc[i][j]);
   };
 
-  // Tile kt lives in stage kt % 2.  Each step multiplies K-chunk 0 of tile
-  // kt while the fragments of its chunk 1 are read, then -- once every wave
-  // has its DMA of tile kt + 1 complete and has finished reading stage kt --
-  // sends tile kt + 2 into stage kt % 2 and multiplies chunk 1 while the
-  // fragments of chunk 0 of tile kt + 1 are read.  The MFMAs thus always have
-  // LDS reads to overlap with.
+  // W_A^T fragments of K tile kt, [zb][kc]: lane (lrow, lgrp) holds head
+  // 16 zb + lrow (clamped to nz - 1; such heads are never stored) at the K
+  // positions of its X fragments; K positions at or beyond K read zero.
+  constexpr int ZA = ZB > 0 ? ZB : 1;  // register arrays need a size
+  uint4 zw[ZA][2];
+  auto zload = [&](int kt) {
+    const elem_t* wa = reinterpret_cast<const elem_t*>(a.Wz);
+#pragma unroll
+    for (int zb = 0; zb < ZB; ++zb) {
+      const int h0 = 16 * zb + lrow;
+      const int h = h0 < nz ? h0 : nz - 1;
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        const int kb = kt * BK + (kc * 4 + lgrp) * VE;
+        elem_t e[VE];
+#pragma unroll
+        for (int u = 0; u < VE; ++u) {
+          const int k = kb + u < K ? kb + u : K - 1;
+          const elem_t v = wa[(size_t)k * nz + h];
+          e[u] = kb + u < K ? v : elem_t(0);
+        }
+        zw[zb][kc] = *reinterpret_cast<const uint4*>(e);
+      }
+    }
+  };
+  floatx4 zacc[2][ZA];  // [ii][zb]
+#pragma unroll
+  for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+    for (int zb = 0; zb < ZA; ++zb) zacc[ii][zb] = floatx4{0.f, 0.f, 0.f, 0.f};
+  auto zmma = [&](int kc, const uint4 (&af)[4]) {
+    if (ZB == 0 || !zwave) return;
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii) {
+      if (zrb[ii]) {
+        const uint4 xa = wn ? af[1 + 2 * ii] : af[2 * ii];  // no dynamic register indexing
+#pragma unroll
+        for (int zb = 0; zb < ZB; ++zb) zacc[ii][zb] = mfma_chunk<ET>(zw[zb][kc], xa, zacc[ii][zb]);
+      }
+    }
+  };
+
+  // Tile kt lives in stage kt % 2.  At the top of step kt every wave has its
+  // own DMA of tile kt complete and, after the barrier, all of them have
+  // finished multiplying tile kt - 1, whose stage then receives tile kt + 1.
+  // Two workgroups share a compute unit, so one's LDS reads overlap the
+  // other's MFMAs.  The W_A^T fragments of tile kt + 1 are requested once
+  // tile kt's are used, and awaited with the DMA at the next step's top.
   const int nk = (K + BK - 1) / BK;
   issue(0, 0);
+  if (ZB > 0 && zwave) zload(0);
   // L2 warm-up: the column tiles of one row panel (consecutive workgroups on
   // one XCD) together touch every 64-byte sector of the panel's X rows once,
   // so that the staging loads of the later K tiles hit L2 rather than HBM.
@@ -420,22 +354,19 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_xw_kernel(GemmArgs a) {
       wv[u] = *reinterpret_cast<const uint32_t*>(xb + (size_t)r * K * ESZ + (size_t)c * 64);
     }
   }
-  wait_vmem_all();
-  __syncthreads();
-  if (nk > 1) issue(1, 1);
-  uint4 a0[4], b0[TN], a1[4], b1[TN];
-  read_frags(0, 0, a0, b0);
+  uint4 af[4], bf[TN];
   for (int kt = 0; kt < nk; ++kt) {
     const int st = kt & 1;
-    read_frags(st, 1, a1, b1);
-    mma(a0, b0);
-    if (kt + 1 < nk) {
-      wait_vmem_all();  // this wave's DMA of tile kt + 1
-      __syncthreads();  // every wave's, and every wave done reading stage st
-      if (kt + 2 < nk) issue(kt + 2, st);
-      read_frags(st ^ 1, 0, a0, b0);
+    wait_vmem_all();
+    __syncthreads();
+    if (kt + 1 < nk) issue(kt + 1, st ^ 1);
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      read_frags(st, kc, af, bf);
+      mma(af, bf);
+      zmma(kc, af);
     }
-    mma(a1, b1);
+    if (ZB > 0 && zwave && kt + 1 < nk) zload(kt + 1);
   }
   if (((wv[0] ^ wv[1]) + (wv[2] ^ wv[3])) == 0x9E3779B9u && M < 0)  // keeps the warm-up loads
     reinterpret_cast<float*>(sg.out)[0] = 0.f;
@@ -443,6 +374,25 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_xw_kernel(GemmArgs a) {
   // Result layout (16 x 16 MFMA, A = W rows, B = X rows): lane (lrow, lgrp)
   // holds Y[token][channel] for token = tile row base + lrow and the four
   // channels 4 lgrp + v, v = 0..3, of each 16-channel block.
+  // z [B][nz][Ntok] fp32: lane holds token lrow of its row block and heads
+  // 16 zb + 4 lgrp + v; the 16 lanes of a head cover 16 consecutive tokens
+  if (ZB > 0 && zwave) {
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii) {
+      const int token = m0 + wm * 64 + 16 * (wn + 2 * ii) + lrow;
+      if (zrb[ii] && token < M) {
+        const uint32_t b = fastdiv((uint32_t)token, a.fd_ntok);
+        const uint32_t tok = (uint32_t)token - b * (uint32_t)a.Ntok;
+#pragma unroll
+        for (int zb = 0; zb < ZB; ++zb)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int head = 16 * zb + 4 * lgrp + v;
+            if (head < nz) a.z[((size_t)b * nz + head) * a.Ntok + tok] = zacc[ii][zb][v];
+          }
+      }
+    }
+  }
   const bool f32out = ET == ET_F32 || sg.out_f32;
   // Staged epilogue: when every aligned group of 16 bytes of channels is
   // contiguous in the output, the tile goes through LDS (free once every wave
@@ -450,8 +400,9 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_xw_kernel(GemmArgs a) {
   // cover whole row segments -- far faster for the memory system than the
   // 8-byte, 16-rows-apart stores the register layout gives.
   const int vo = f32out ? 4 : 8;  // channels per 16 bytes of output
-  const bool staged = (sg.layout == OUT_ROWMAJOR && ncols % vo == 0) ||
-                      (sg.layout == OUT_BLOCKED && sg.cg % vo == 0 && a.d % vo == 0);
+  constexpr bool FIT4 = BM * BN * 4 <= SMEM;  // an fp32 tile fits the LDS
+  const bool staged = (!f32out || FIT4) && ((sg.layout == OUT_ROWMAJOR && ncols % vo == 0) ||
+                                            (sg.layout == OUT_BLOCKED && sg.cg % vo == 0 && a.d % vo == 0));
   if (staged) {
     auto stage_out = [&](auto osz_tag) {
       constexpr int OSZ = decltype(osz_tag)::value;
@@ -482,10 +433,16 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_xw_kernel(GemmArgs a) {
         }
       }
     };
-    if (f32out) stage_out(std::integral_constant<int, 4>{});
-    else stage_out(std::integral_constant<int, 2>{});
+    if constexpr (FIT4) {
+      if (f32out) stage_out(std::integral_constant<int, 4>{});
+      else stage_out(std::integral_constant<int, 2>{});
+    } else {
+      stage_out(std::integral_constant<int, 2>{});
+    }
     return;
   }
+  // (192-wide tiles are launched only where the staged path applies)
+  if constexpr (BN != 192) {
   // Otherwise straight from registers: 8 (bf16) or 16 (fp32) bytes per lane,
   // the 16 lanes of a channel block covering 16 consecutive tokens.
   const bool quad = (sg.layout == OUT_ROWMAJOR && (ncols & 3) == 0) ||
@@ -522,25 +479,42 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_xw_kernel(GemmArgs a) {
       }
     }
   }
+  }
 }
 
-// Output tile width: 128 or 96 columns.  Two workgroups fit a compute unit,
-// so the grid runs in rounds of 2 x CUs workgroups; the width whose grid fills
-// its last round best is taken (128 on a tie).  A score-projection workgroup
-// counts as a quarter of a tile.
-int choose_tile_n(const GemmArgs& a) {
-  const int cus = a.num_cu > 0 ? a.num_cu : 256;
-  const int rowtiles = (a.M + BM - 1) / BM;
-  const double slots = 2.0 * cus;
-  const double zw = a.nz > 0 ? 0.25 * ((a.M + ZROWS - 1) / ZROWS) : 0.0;
+// Output tile width: 192, 128 or 96 columns.  Two workgroups fit a compute
+// unit, so the grid runs in rounds of 2 x CUs workgroups; the estimated time
+// is rounds x (BN + 48) (a tile costs its columns plus a fixed part), and the
+// cheapest width is taken.  192-column tiles are for 2-byte operands and
+// 2-byte outputs that take the staged epilogue only (the LDS holds two stages
+// of an fp32 W tile of that width, or an fp32 output tile, only barely or not).
+// 192-wide tiles: 2-byte operands, at most 16 score-projection heads (more
+// would not fit the registers), and every segment takes the staged epilogue
+// with 2-byte output.
+bool wide_ok(int et, const GemmArgs& a) {
+  bool ok = et != ET_F32 && a.nz <= 16;
+  for (int s = 0; s < a.nseg; ++s) {
+    const GemmSeg& g = a.seg[s];
+    ok = ok && !g.out_f32 &&
+         ((g.layout == OUT_ROWMAJOR && g.ncols % 8 == 0) || (g.layout == OUT_BLOCKED && g.cg % 8 == 0 && a.d % 8 == 0));
+  }
+  return ok;
+}
+
+int choose_tile_n(int et, const GemmArgs& a) {
+  const long cus = a.num_cu > 0 ? a.num_cu : 256;
+  const long rowtiles = (a.M + BM - 1) / BM;
+  const long slots = 2 * cus;
   int best = 128;
-  double best_fill = -1.0;
-  for (int bn : {128, 96}) {
-    double work = zw;
-    for (int s = 0; s < a.nseg; ++s) work += (double)rowtiles * ((a.seg[s].ncols + bn - 1) / bn);
-    const double fill = work / (std::ceil(work / slots) * slots);
-    if (fill > best_fill + 1e-9) {
-      best_fill = fill;
+  long best_cost = -1;
+  const bool stage2 = wide_ok(et, a);
+  for (int bn : {192, 128, 96}) {
+    if (bn == 192 && !stage2) continue;
+    long tiles = 0;
+    for (int s = 0; s < a.nseg; ++s) tiles += rowtiles * ((a.seg[s].ncols + bn - 1) / bn);
+    const long cost = ((tiles + slots - 1) / slots) * (bn + 48);
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
       best = bn;
     }
   }
@@ -555,10 +529,21 @@ hipError_t launch_gemm_bn(int et, GemmArgs& a, hipStream_t stream, const LaunchT
     a.ncoltiles += a.seg[s].ntiles;
   }
   const int rowtiles = (a.M + BM - 1) / BM;
-  a.nzwg = a.nz > 0 ? (a.M + ZROWS - 1) / ZROWS : 0;
-  const dim3 grid((unsigned)(a.nzwg + rowtiles * a.ncoltiles)), block(NTHR);
-  if (et == ET_F32) return launch_k(gemm_xw_kernel<ET_F32, BN>, grid, block, 0, stream, t, a);
-  return launch_k(gemm_xw_kernel<ET_BF16, BN>, grid, block, 0, stream, t, a);
+  const dim3 grid((unsigned)(rowtiles * a.ncoltiles)), block(NTHR);
+  const int zb = (a.nz + 15) / 16;
+  if constexpr (BN == 192) {  // (never with more than 16 heads)
+    if (zb == 0) return launch_k(gemm_xw_kernel<ET_BF16, BN, 0>, grid, block, 0, stream, t, a);
+    return launch_k(gemm_xw_kernel<ET_BF16, BN, 1>, grid, block, 0, stream, t, a);
+  } else {
+    if (et == ET_F32) {
+      if (zb == 0) return launch_k(gemm_xw_kernel<ET_F32, BN, 0>, grid, block, 0, stream, t, a);
+      if (zb == 1) return launch_k(gemm_xw_kernel<ET_F32, BN, 1>, grid, block, 0, stream, t, a);
+      return launch_k(gemm_xw_kernel<ET_F32, BN, 2>, grid, block, 0, stream, t, a);
+    }
+    if (zb == 0) return launch_k(gemm_xw_kernel<ET_BF16, BN, 0>, grid, block, 0, stream, t, a);
+    if (zb == 1) return launch_k(gemm_xw_kernel<ET_BF16, BN, 1>, grid, block, 0, stream, t, a);
+    return launch_k(gemm_xw_kernel<ET_BF16, BN, 2>, grid, block, 0, stream, t, a);
+  }
 }
 
 }  // namespace
@@ -575,9 +560,11 @@ hipError_t launch_gemm(int et, GemmArgs a, hipStream_t stream, const LaunchTimin
     if (g.layout == OUT_BLOCKED && (g.cg <= 0 || a.d % g.cg != 0)) return hipErrorInvalidValue;
     g.fd_cg = make_fastdiv((uint32_t)(g.cg > 0 ? g.cg : 1));
   }
-  const int bn = a.tile_n ? a.tile_n : choose_tile_n(a);
+  int bn = a.tile_n ? a.tile_n : choose_tile_n(et, a);
+  if (bn == 192 && !wide_ok(et, a)) bn = choose_tile_n(et, a);
   if (bn == 96) return launch_gemm_bn<96>(et, a, stream, t);
   if (bn == 128) return launch_gemm_bn<128>(et, a, stream, t);
+  if (bn == 192) return launch_gemm_bn<192>(et, a, stream, t);
   return hipErrorInvalidValue;
 }
 

@@ -83,11 +83,10 @@ struct GemmArgs {
   const void* Wz;
   float* z;
   int nz;
-  int tile_n;  // output tile width (96 or 128); 0 lets the launcher choose
+  int tile_n;  // output tile width (96, 128 or 192); 0 lets the launcher choose
   FastDiv fd_nz;  // filled by the launcher
   int num_cu;  // compute units of the device (0: assume 256)
   // filled by the launcher
-  int nzwg;  // score-projection workgroups ahead of the output tiles
   int ncoltiles;
   FastDiv fd_ntok, fd_d;
   GemmSeg seg[3];

@@ -53,6 +53,12 @@
  * HIP call.  cat_last_error() returns a message for the calling thread's last
  * failure.  Setting the environment variable CAT_DEBUG_SYNC=1 makes every
  * launch synchronise and check for asynchronous errors.
+ *
+ * Tuning: the projection GEMM picks its output tile width (96, 128 or 192
+ * columns) from the problem; CAT_GEMM_TILE_N=96|128|192, read when a plan is
+ * created, forces one for that plan's calls (192 only where the GEMM's staged
+ * 2-byte epilogue applies; elsewhere the choice falls back to the default).
+ * It changes speed, never results beyond rounding order.
  */
 #ifndef CAT_H_
 #define CAT_H_

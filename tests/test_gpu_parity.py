@@ -65,6 +65,39 @@ def test_project_1d(cat, B, N, D, H, dtype):
     assert_parity(to_np(z), oracle.scores_1d(inp.X, inp.W_A), "f32", "z")
 
 
+@pytest.mark.parametrize("tile_n", [96, 128, 192])
+@pytest.mark.parametrize("B,N,D,H,dtype", [(2, 300, 264, 12, "bf16"), (1, 200, 200, 25, "bf16"),
+                                           (3, 130, 136, 17, "f32")])
+def test_project_tile_widths(cat, monkeypatch, tile_n, B, N, D, H, dtype):
+    """Every output tile width of the projection GEMM (forced through the
+    tuning variable), with ragged rows, a K tail, several column tiles and
+    one or two 16-head blocks of the score projection.  192-wide tiles do not
+    apply to fp32 operands; the launcher then falls back to its own choice."""
+    say("project_tile", tile_n, B, N, D, H, dtype)
+    monkeypatch.setenv("CAT_GEMM_TILE_N", str(tile_n))
+    inp = rng_inputs(17, B, N, D, H, dtype)
+    plan = cat.cat_plan_create("1d", dtype, B, N, D, H)
+    V, z = cat.cat_step_project(plan, to_dev(inp.X, dtype), to_dev(inp.W_A, dtype), to_dev(inp.W_V, dtype))
+    import torch
+    torch.cuda.synchronize()
+    assert_parity(to_np(V), oracle.matmul(inp.X, inp.W_V), dtype, "V")
+    assert_parity(to_np(z), oracle.scores_1d(inp.X, inp.W_A), "f32", "z")
+
+
+@pytest.mark.parametrize("tile_n", [96, 128, 192])
+def test_forward_1d_tile_widths(cat, monkeypatch, tile_n):
+    """The whole 1D path (blocked value layout) at every GEMM tile width."""
+    B, N, D, H, dtype = 2, 160, 384, 6, "bf16"
+    say("forward_tile", tile_n, B, N, D, H, dtype)
+    monkeypatch.setenv("CAT_GEMM_TILE_N", str(tile_n))
+    inp = rng_inputs(19, B, N, D, H, dtype)
+    plan = cat.cat_plan_create("1d", dtype, B, N, D, H)
+    O = cat.cat_forward_1d(plan, to_dev(inp.X, dtype), to_dev(inp.W_A, dtype), to_dev(inp.W_V, dtype))
+    import torch
+    torch.cuda.synchronize()
+    assert_parity(to_np(O), oracle.cat_forward_1d(inp.X, inp.W_A, inp.W_V)["O"], dtype, "O")
+
+
 def _extended_line(zs, L):
     """The length-L circle the spectrum lives on: softmax values periodically
     extended (p < N: z*[p]; p > L - N: z*[p - L + N]; zero between)."""

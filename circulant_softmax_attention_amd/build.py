@@ -26,8 +26,12 @@ ARCH = "gfx950"
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", os.path.join(ROOT, "include"),
           "-I", CSRC, "-Wall", "-Wno-unused-function"]
+# The matrix-core conv reads every MFMA result with vector ALU instructions;
+# asking the backend for MFMAs that write VGPRs directly saves a copy of each
+# result out of the accumulation registers.
+FILE_FLAGS = {"cat_mconv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 SOURCES = ["cat_inst_2d_96.hip", "cat_inst_1d_large.hip", "cat_inst_1d_mid.hip", "cat_inst_2d_small.hip",
-           "cat_inst_1d_small.hip", "cat_gemm.hip", "cat_fftconv.hip", "cat_api.cpp"]
+           "cat_inst_1d_small.hip", "cat_gemm.hip", "cat_mconv.hip", "cat_fftconv.hip", "cat_api.cpp"]
 
 
 def _compile(src: str, verbose: bool) -> str:
@@ -35,6 +39,7 @@ def _compile(src: str, verbose: bool) -> str:
     cmd = [HIPCC] + COMMON
     if src.endswith(".hip"):
         cmd += DEVICE_FLAGS
+    cmd += FILE_FLAGS.get(src, [])
     cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
     t0 = time.time()
     r = subprocess.run(cmd, capture_output=True, text=True)

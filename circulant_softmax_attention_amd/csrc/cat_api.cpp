@@ -23,6 +23,8 @@ struct cat_plan_s {
   int L;
   int G;             // complex lines per transform workgroup
   int ng;            // line groups per head (d / 2 / G)
+  bool mconv;        // 1D conv on the matrix cores (L = 1024, bf16, d % 32 == 0)
+  int cg;            // channels per group of the blocked V (2 G, or 32 for mconv)
   int Gs;            // lines per spectrum workgroup
   int npair, ngrp, ppg;  // 2D score partials
   float2* d_tw;      // 1D inter-pass twiddles, L entries (null in 2D)
@@ -187,6 +189,13 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
   while (G < 8 && d2 % (2 * G) == 0 && (2 * G) * T <= 256 && (2 * G) * line_bytes <= lds_cap) G *= 2;
   pl->G = G;
   pl->ng = d2 / G;
+  {
+    const char* cv = std::getenv("CAT_CONV");
+    const bool force_valu = cv && std::strcmp(cv, "valu") == 0;
+    pl->mconv = !force_valu && p->kind == CAT_1D && p->dtype == CAT_BF16 && g.L1 * g.L2 == 1024 && d % 32 == 0;
+    pl->cg = pl->mconv ? 32 : 2 * G;
+    if (pl->mconv) pl->ng = (int)d / 32;
+  }
   int Gs = 1;
   while ((2 * Gs) * T <= 64 && spectrum_lds_bytes(g, 2 * Gs) <= 96 * 1024) Gs *= 2;
   pl->Gs = Gs;
@@ -238,6 +247,14 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
         const double ang = two_pi * (double)e / (double)pl->L;
         tw[(size_t)k1 * g.L2 + n2] = make_float2((float)std::cos(ang), (float)(-std::sin(ang)));
       }
+    if (pl->mconv) {  // two more copies for the matrix-core conv: W x 32 and conj(W) / 32
+      const size_t L = (size_t)pl->L;
+      tw.resize(3 * L);
+      for (size_t i = 0; i < L; ++i) {
+        tw[L + i] = make_float2(32.f * tw[i].x, 32.f * tw[i].y);
+        tw[2 * L + i] = make_float2(tw[i].x / 32.f, -tw[i].y / 32.f);
+      }
+    }
     hipError_t e = hipMalloc(&pl->d_tw, tw.size() * sizeof(float2));
     if (e != hipSuccess) {
       delete pl;
@@ -396,6 +413,11 @@ ConvArgs conv_base(const cat_plan_s* pl, const void* Vblk, const float2* spec, v
   return a;
 }
 
+// The 1D conv: on the matrix cores where the plan chose that path.
+hipError_t run_conv_1d(const cat_plan_s* pl, const ConvArgs& ca, hipStream_t s, const LaunchTiming* t = nullptr) {
+  return pl->mconv ? launch_mconv(ca, s, t) : launch_conv(pl->geom, pl->et, ca, s, t);
+}
+
 }  // namespace
 
 extern "C" {
@@ -415,7 +437,7 @@ cat_status cat_forward_1d(cat_plan plan, const void* X, const void* W_A, const v
   // V = X W_V (blocked for the transform) and the logits z = X W_A in one pass
   GemmArgs ga = gemm_base(plan, X);
   ga.nseg = 1;
-  ga.seg[0] = seg(W_V, Vb, (int)plan->p.D, 0, OUT_BLOCKED, 2 * plan->G);
+  ga.seg[0] = seg(W_V, Vb, (int)plan->p.D, 0, OUT_BLOCKED, plan->cg);
   ga.Wz = W_A;
   ga.z = z;
   ga.nz = (int)plan->p.H;
@@ -430,7 +452,7 @@ cat_status cat_forward_1d(cat_plan plan, const void* X, const void* W_A, const v
   if ((st = check_sync(plan, "spectrum")) != CAT_OK) return st;
 
   ConvArgs ca = conv_base(plan, Vb, sa.spec, O);
-  e = launch_conv(plan->geom, plan->et, ca, s, mk.at(2));
+  e = run_conv_1d(plan, ca, s, mk.at(2));
   if (e != hipSuccess) return hip_fail(e, "fft-conv launch");
   return check_sync(plan, "fft-conv");
 }
@@ -552,7 +574,7 @@ cat_status cat_step_mix(cat_plan plan, const float* logits, const void* V, void*
   ra.D = (int)plan->p.D;
   ra.H = (int)plan->p.H;
   ra.d = plan->d;
-  ra.cg = 2 * plan->G;
+  ra.cg = plan->cg;
   hipError_t e = launch_relayout(ra, s);
   if (e != hipSuccess) return hip_fail(e, "relayout launch");
   SpecArgs sa = spec_base(plan, workspace);
@@ -561,7 +583,7 @@ cat_status cat_step_mix(cat_plan plan, const float* logits, const void* V, void*
   if (e != hipSuccess) return hip_fail(e, "spectrum launch");
   if ((st = check_sync(plan, "spectrum")) != CAT_OK) return st;
   ConvArgs ca = conv_base(plan, Vb, sa.spec, O);
-  e = launch_conv(plan->geom, plan->et, ca, s);
+  e = run_conv_1d(plan, ca, s);
   if (e != hipSuccess) return hip_fail(e, "fft-conv launch");
   return check_sync(plan, "fft-conv");
 }

@@ -122,7 +122,8 @@ struct SpecArgs {
 struct ConvArgs {
   const void* V;      // BLOCKED [B][H][ng][N][2G], element type et
   const float2* spec; // [BH][L]
-  const float2* tw;   // 1D inter-pass twiddles (null for 2D)
+  const float2* tw;   // 1D inter-pass twiddles (null for 2D); matrix-core conv plans
+                      // append W x 32 and conj(W) / 32 (3 L entries)
   void* O;            // [B][N][D], element type et
   int B, H, D, N, d;
   int G, log2G, ng;
@@ -161,6 +162,10 @@ size_t spectrum_lds_bytes(const LineGeom& g, int G);
 hipError_t launch_spectrum(const LineGeom& g, int mode, const SpecArgs& a, hipStream_t s,
                            const LaunchTiming* t = nullptr);
 hipError_t launch_conv(const LineGeom& g, int et, const ConvArgs& a, hipStream_t s, const LaunchTiming* t = nullptr);
+// 1D FFT-convolution for L = 1024 with the radix-32 passes on the matrix
+// cores (bf16 storage): V BLOCKED with 32-channel groups (a.ng = d / 32),
+// N <= 1024, d % 32 == 0.
+hipError_t launch_mconv(const ConvArgs& a, hipStream_t s, const LaunchTiming* t = nullptr);
 hipError_t launch_score_partial(const LineGeom& g, const ScoreArgs& a, hipStream_t s,
                                 const LaunchTiming* t = nullptr);
 hipError_t launch_relayout(const RelayoutArgs& a, hipStream_t s);

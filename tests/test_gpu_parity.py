@@ -147,6 +147,32 @@ def test_mix_1d(cat, B, N, D, H, dtype):
     assert_parity(to_np(O), ref, dtype, "O")
 
 
+@pytest.mark.parametrize("conv", ["auto", "valu"])
+@pytest.mark.parametrize("B,N,D,H,vscale,lscale", [(2, 1024, 128, 2, 1.0, 2.0), (1, 1024, 96, 3, 1.0, 0.0),
+                                                   (2, 300, 64, 1, 1.0, 2.0), (1, 511, 96, 1, 1.0, 3.0),
+                                                   (3, 257, 64, 2, 1.0, 2.0), (1, 1024, 64, 1, 1e-4, 2.0),
+                                                   (1, 1024, 64, 1, 3e4, 2.0), (1, 1024, 64, 1, 1.0, 40.0)])
+def test_mix_1d_l1024(cat, monkeypatch, conv, B, N, D, H, vscale, lscale):
+    """The 1D conv at transform length 1024 (N = 1024, or N in 257..511 on
+    the exact 2N-1 circle): bf16 storage takes the matrix-core path by
+    default; CAT_CONV=valu forces the vector path on the same inputs.  Cases
+    span value scales far from 1 (the fp16 stages scale each line), uniform
+    scores (lscale 0) and a near one-hot softmax (lscale 40)."""
+    say("mix_1d_l1024", conv, B, N, D, H, vscale, lscale)
+    import torch
+    if conv == "valu":
+        monkeypatch.setenv("CAT_CONV", "valu")
+    rng = np.random.default_rng(N * 11 + D)
+    logits = (rng.standard_normal((B, H, N)) * lscale).astype(np.float32)
+    V = (rng.standard_normal((B, N, D)) * vscale).astype(np.float32)
+    V = W.bf16_bits_to_f32(W.round_bf16_bits(V)).reshape(V.shape)
+    plan = cat.cat_plan_create("1d", "bf16", B, N, D, H)
+    O = cat.cat_step_mix(plan, torch.from_numpy(logits).cuda(), to_dev(V, "bf16"))
+    torch.cuda.synchronize()
+    ref = oracle.circulant_1d(oracle.softmax(logits), V)
+    assert_parity(to_np(O), ref, "bf16", "O")
+
+
 # ------------------------------------------------------------------ 1D forward
 @pytest.mark.parametrize("B,N,D,H,dtype", [(1, 64, 64, 4, "f32"), (2, 37, 48, 3, "f32"), (3, 100, 64, 4, "bf16"),
                                            (1, 1, 32, 2, "f32"), (2, 197, 96, 3, "f32"), (1, 1024, 64, 1, "bf16"),

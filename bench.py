@@ -31,7 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-PEAK_TFLOPS = {"mfma_bf16": 2500.0, "mfma_f32": 157.3, "valu_f32": 78.6}
+PEAK_TFLOPS = {"mfma_bf16": 2500.0, "mfma_f16": 2500.0, "mfma_f32": 157.3, "valu_f32": 78.6}
 MALL_BYTES = 256 << 20
 
 
@@ -44,8 +44,14 @@ def fft_flops(L: int) -> float:
     return 5.0 * L * math.log2(L) if L > 1 else 0.0
 
 
-def kernel_model(wl, L: int, ngrp: int):
-    """Algorithmic bytes and flops of each kernel of one forward call."""
+def kernel_model(wl, L: int, ngrp: int, fused_spectrum: bool = False):
+    """Algorithmic bytes and flops of each kernel of one forward call.
+
+    fused_spectrum: the 1D conv ran on the matrix cores and computed the
+    softmax spectrum itself (no spectrum launch): it reads the logits instead
+    of a spectrum, and its flops are the matrix products it executes (four
+    32x32x32 complex products per line, each 4 x 2 x 32^3 real flops, plus two
+    per workgroup for the spectrum line)."""
     s = 4 if wl.dtype == "f32" else 2
     B, N, D, H, d = wl.B, wl.N, wl.D, wl.H, wl.d
     T = B * N
@@ -66,6 +72,10 @@ def kernel_model(wl, L: int, ngrp: int):
         m["spectrum"] = dict(bytes=BH * ngrp * L * 8 + spec_bytes,
                              flops=BH * (2 * fft_flops(L) + 4.0 * N), unit="valu_f32")
     m["fftconv"] = dict(bytes=2 * T * D * s + spec_bytes, flops=lines * (2 * fft_flops(L) + 6.0 * L), unit="valu_f32")
+    if fused_spectrum:
+        cplx = 4 * 2.0 * 32 ** 3  # one 32x32x32 complex product in real flops
+        m["fftconv"] = dict(bytes=2 * T * D * s + BH * N * 4, flops=lines * 4 * cplx + B * H * (d // 32) * 2 * cplx,
+                            unit="mfma_f16")
     return m
 
 
@@ -78,7 +88,8 @@ def source_hash(files):
 
 
 KERNEL_SOURCES = {
-    "fftconv": ["circulant_softmax_attention_amd/csrc/cat_fftconv.hpp", "circulant_softmax_attention_amd/csrc/cat_fft.hpp",
+    "fftconv": ["circulant_softmax_attention_amd/csrc/cat_mconv.hip",
+                "circulant_softmax_attention_amd/csrc/cat_fftconv.hpp", "circulant_softmax_attention_amd/csrc/cat_fft.hpp",
                 "circulant_softmax_attention_amd/csrc/cat_common.hpp"],
     "project": ["circulant_softmax_attention_amd/csrc/cat_gemm.hip", "circulant_softmax_attention_amd/csrc/cat_common.hpp"],
 }
@@ -214,7 +225,8 @@ def run(args):
         log(f"  kernel {k:10s} {ms * 1000:9.2f} us avg over {n} launches")
 
     ngrp = (wl.d // 2 + 3) // 4
-    model = kernel_model(wl, L, ngrp)
+    fused = wl.kind == "1d" and ktimes.get("spectrum", (0.0, 0))[1] == 0
+    model = kernel_model(wl, L, ngrp, fused_spectrum=fused)
     kernels = {}
     ktimes = {k: v for k, v in ktimes.items() if v[1] > 0}  # kernels this path launched
     for k, (ms, n) in ktimes.items():
@@ -230,7 +242,7 @@ def run(args):
     dom = max(ktimes, key=lambda k: ktimes[k][0] * kernels[k]["launches_per_call"])
     kd = kernels[dom]
     sec = ktimes[dom][0] / 1000.0
-    if kd["compute_unit"].startswith("mfma"):
+    if kd["compute_unit"].startswith("mfma") and kd["compute_frac"] >= kd["hbm_frac"]:
         bound = "mfma"
     else:
         bound = "hbm" if kd["hbm_frac"] >= kd["compute_frac"] else "alu"

@@ -447,11 +447,14 @@ cat_status cat_forward_1d(cat_plan plan, const void* X, const void* W_A, const v
 
   SpecArgs sa = spec_base(plan, workspace);
   sa.logits = z;
-  e = launch_spectrum(plan->geom, 0, sa, s, mk.at(1));
-  if (e != hipSuccess) return hip_fail(e, "spectrum launch");
-  if ((st = check_sync(plan, "spectrum")) != CAT_OK) return st;
+  if (!plan->mconv) {  // (the matrix-core conv takes the softmax spectrum itself)
+    e = launch_spectrum(plan->geom, 0, sa, s, mk.at(1));
+    if (e != hipSuccess) return hip_fail(e, "spectrum launch");
+    if ((st = check_sync(plan, "spectrum")) != CAT_OK) return st;
+  }
 
   ConvArgs ca = conv_base(plan, Vb, sa.spec, O);
+  if (plan->mconv) ca.logits = z;
   e = run_conv_1d(plan, ca, s, mk.at(2));
   if (e != hipSuccess) return hip_fail(e, "fft-conv launch");
   return check_sync(plan, "fft-conv");
@@ -579,10 +582,13 @@ cat_status cat_step_mix(cat_plan plan, const float* logits, const void* V, void*
   if (e != hipSuccess) return hip_fail(e, "relayout launch");
   SpecArgs sa = spec_base(plan, workspace);
   sa.logits = logits;
-  e = launch_spectrum(plan->geom, 0, sa, s);
-  if (e != hipSuccess) return hip_fail(e, "spectrum launch");
-  if ((st = check_sync(plan, "spectrum")) != CAT_OK) return st;
+  if (!plan->mconv) {
+    e = launch_spectrum(plan->geom, 0, sa, s);
+    if (e != hipSuccess) return hip_fail(e, "spectrum launch");
+    if ((st = check_sync(plan, "spectrum")) != CAT_OK) return st;
+  }
   ConvArgs ca = conv_base(plan, Vb, sa.spec, O);
+  if (plan->mconv) ca.logits = logits;
   e = run_conv_1d(plan, ca, s);
   if (e != hipSuccess) return hip_fail(e, "fft-conv launch");
   return check_sync(plan, "fft-conv");

@@ -122,6 +122,8 @@ struct SpecArgs {
 struct ConvArgs {
   const void* V;      // BLOCKED [B][H][ng][N][2G], element type et
   const float2* spec; // [BH][L]
+  const float* logits;  // matrix-core conv only: when set, [BH][N] fp32 logits whose
+                        // softmax spectrum the conv computes itself (spec unused)
   const float2* tw;   // 1D inter-pass twiddles (null for 2D); matrix-core conv plans
                       // append W x 32 and conj(W) / 32 (3 L entries)
   void* O;            // [B][N][D], element type et

@@ -129,6 +129,30 @@ __device__ __forceinline__ C8 stack(const CT& t0, const CT& t1) {
 __device__ __forceinline__ float2 cmulf(float2 a, float2 b) {
   return make_float2(a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x);
 }
+// Float max and sum over the wave, the same DPP pattern (a mirror swap adds
+// the partner's partial, which after the quad steps holds its group's total).
+template <bool SUM>
+__device__ __forceinline__ float wave_reduce_f(float x) {
+  auto op = [](float p, float q) { return SUM ? p + q : fmaxf(p, q); };
+  auto dpp = [](float v, int ctrl) {
+    const int i = __float_as_int(v);
+    switch (ctrl) {
+      case 0: return __int_as_float(__builtin_amdgcn_update_dpp(i, i, 0xB1, 0xF, 0xF, false));
+      case 1: return __int_as_float(__builtin_amdgcn_update_dpp(i, i, 0x4E, 0xF, 0xF, false));
+      case 2: return __int_as_float(__builtin_amdgcn_update_dpp(i, i, 0x141, 0xF, 0xF, false));
+      default: return __int_as_float(__builtin_amdgcn_update_dpp(i, i, 0x140, 0xF, 0xF, false));
+    }
+  };
+  x = op(x, dpp(x, 0));
+  x = op(x, dpp(x, 1));
+  x = op(x, dpp(x, 2));
+  x = op(x, dpp(x, 3));
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+  return op(op(r0, r1), op(r2, r3));
+}
 // Largest value over the wave (non-negative ints): DPP max within each row
 // of 16 lanes (quad swaps, then the half-row and row mirrors), then the four
 // row results.
@@ -181,6 +205,25 @@ __global__ __launch_bounds__(MNTHR) void mconv_kernel(ConvArgs a) {
   const int b = bh / a.H, h = bh - b * a.H;
   const int N = a.N;
 
+  // With logits given, wave 0 computes the filter spectrum itself.  Its 16
+  // logits (the positions its lanes hold in the first pass's operand) are
+  // requested before the block's DMA, so they have arrived by the time the
+  // block has.  Position t of the length-1024 circle takes logit t (t < N),
+  // t - 1024 + N (t > 1024 - N; the periodic extension), or none.
+  const bool fused = a.logits != nullptr;
+  float zl[2][8];
+  if (fused && wave == 0) {
+    const float* zr = a.logits + (size_t)bh * N;
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int t = 32 * (4 * grp + (s & 3) + 16 * (s >> 2)) + lo + 16 * bb;
+        const int src = t < N ? t : (t > ML - N ? t - ML + N : -1);
+        zl[bb][s] = src >= 0 ? zr[src] : -INFINITY;
+      }
+  }
+
   // Stage the [N][32] block: wave w takes rows 256 w .. + 255, 16 rows per
   // DMA; lane l fills LDS chunk l % 4 of row n0 + l / 4 with the global chunk
   // (l % 4) ^ ((n >> 2) & 3).  Rows at or beyond N repeat row N - 1 (never
@@ -196,12 +239,13 @@ __global__ __launch_bounds__(MNTHR) void mconv_kernel(ConvArgs a) {
       const int ns = n < N ? n : N - 1;
       lds_dma16(vblk + (size_t)ns * MROWB + c * 16, base + (uint32_t)n0 * MROWB);
     }
-    // the spectrum: 8 KB, two 1 KB pieces per wave
-    const char* sg = reinterpret_cast<const char*>(a.spec + (size_t)bh * ML);
+    if (!fused) {  // the spectrum: 8 KB, two 1 KB pieces per wave
+      const char* sg = reinterpret_cast<const char*>(a.spec + (size_t)bh * ML);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int piece = wave * 2 + i;
-      lds_dma16(sg + piece * 1024 + lane * 16, lds_addr(sp) + piece * 1024);
+      for (int i = 0; i < 2; ++i) {
+        const int piece = wave * 2 + i;
+        lds_dma16(sg + piece * 1024 + lane * 16, lds_addr(sp) + piece * 1024);
+      }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -239,6 +283,65 @@ __global__ __launch_bounds__(MNTHR) void mconv_kernel(ConvArgs a) {
           t2[x][y][v] = u2;
         }
   }
+  // The filter spectrum S[k1 + 32 k2] = FFT(softmax line)[k] / L: softmax in
+  // fp32 (each logit counted once in the sum: the positions t < N), then the
+  // two forward passes as for the data lines.
+  if (fused && wave == 0) {
+    float mz = -INFINITY;
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+      for (int s = 0; s < 8; ++s) mz = fmaxf(mz, zl[bb][s]);
+    mz = wave_reduce_f<false>(mz);
+    float se = 0.f;
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int t = 32 * (4 * grp + (s & 3) + 16 * (s >> 2)) + lo + 16 * bb;
+        zl[bb][s] = __expf(zl[bb][s] - mz);
+        if (t < N) se += zl[bb][s];
+      }
+    se = wave_reduce_f<true>(se);
+    const int ez = scale_exp(1.f / se, 3);  // largest probability 1 / se -> [8, 16)
+    const float sz = pow2f(ez) / se;
+    C8 x1[2];
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        x1[bb].re[s] = (_Float16)(zl[bb][s] * sz);
+        x1[bb].im[s] = (_Float16)0.f;
+      }
+    CT d1[2][2];
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        d1[bb][kb] = mul_dA<false>(x1[bb], kf[kb]);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float2 r = cmulf(make_float2(d1[bb][kb].re[v], d1[bb][kb].im[v]), t1[bb][kb][v]);
+          d1[bb][kb].re[v] = r.x;
+          d1[bb][kb].im[v] = r.y;
+        }
+      }
+    const float unscale = pow2f(-ez - 15);  // / (2^ez x 32 x L)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const C8 y2 = stack(d1[0][kb], d1[1][kb]);
+#pragma unroll
+      for (int k2b = 0; k2b < 2; ++k2b) {
+        const CT d2 = mul_dB<false>(kf[k2b], y2);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int k2 = 16 * k2b + 4 * grp + v, k1 = lo + 16 * kb;
+          sp[k1 + 32 * k2] = make_float2(d2.re[v] * unscale, d2.im[v] * unscale);
+        }
+      }
+    }
+  }
+
   // Every token this lane reads or writes is lo + 128 grp + (a multiple of
   // 16), so bits 2..3 of the token, which set the chunk swizzle, are those of
   // lo: one per-lane base, and compile-time offsets for the rest.
@@ -296,6 +399,7 @@ __global__ __launch_bounds__(MNTHR) void mconv_kernel(ConvArgs a) {
     for (int k2b = 0; k2b < 2; ++k2b)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) d2[k2b][kb] = mul_dB<false>(kf[k2b], y2[kb]);
+    if (fused && li == 0) __syncthreads();  // wave 0's spectrum is in LDS
     // ---- spectrum product
 #pragma unroll
     for (int k2b = 0; k2b < 2; ++k2b)

@@ -51,7 +51,7 @@ def kernel_model(wl, L: int, ngrp: int, fused_spectrum: bool = False):
     softmax spectrum itself (no spectrum launch): it reads the logits instead
     of a spectrum, and its flops are the matrix products it executes (four
     32x32x32 complex products per line, each 4 x 2 x 32^3 real flops, plus two
-    per workgroup for the spectrum line)."""
+    per workgroup of 16 channels for the spectrum line)."""
     s = 4 if wl.dtype == "f32" else 2
     B, N, D, H, d = wl.B, wl.N, wl.D, wl.H, wl.d
     T = B * N
@@ -74,7 +74,7 @@ def kernel_model(wl, L: int, ngrp: int, fused_spectrum: bool = False):
     m["fftconv"] = dict(bytes=2 * T * D * s + spec_bytes, flops=lines * (2 * fft_flops(L) + 6.0 * L), unit="valu_f32")
     if fused_spectrum:
         cplx = 4 * 2.0 * 32 ** 3  # one 32x32x32 complex product in real flops
-        m["fftconv"] = dict(bytes=2 * T * D * s + BH * N * 4, flops=lines * 4 * cplx + B * H * (d // 32) * 2 * cplx,
+        m["fftconv"] = dict(bytes=2 * T * D * s + BH * N * 4, flops=lines * 4 * cplx + B * H * (d // 16) * 2 * cplx,
                             unit="mfma_f16")
     return m
 

@@ -23,8 +23,8 @@ struct cat_plan_s {
   int L;
   int G;             // complex lines per transform workgroup
   int ng;            // line groups per head (d / 2 / G)
-  bool mconv;        // 1D conv on the matrix cores (L = 1024, bf16, d % 32 == 0)
-  int cg;            // channels per group of the blocked V (2 G, or 32 for mconv)
+  bool mconv;        // 1D conv on the matrix cores (L = 1024, bf16, d % 16 == 0)
+  int cg;            // channels per group of the blocked V (2 G, or 16 for mconv)
   int Gs;            // lines per spectrum workgroup
   int npair, ngrp, ppg;  // 2D score partials
   float2* d_tw;      // 1D inter-pass twiddles, L entries (null in 2D)
@@ -192,9 +192,9 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
   {
     const char* cv = std::getenv("CAT_CONV");
     const bool force_valu = cv && std::strcmp(cv, "valu") == 0;
-    pl->mconv = !force_valu && p->kind == CAT_1D && p->dtype == CAT_BF16 && g.L1 * g.L2 == 1024 && d % 32 == 0;
-    pl->cg = pl->mconv ? 32 : 2 * G;
-    if (pl->mconv) pl->ng = (int)d / 32;
+    pl->mconv = !force_valu && p->kind == CAT_1D && p->dtype == CAT_BF16 && g.L1 * g.L2 == 1024 && d % 16 == 0;
+    pl->cg = pl->mconv ? 16 : 2 * G;
+    if (pl->mconv) pl->ng = (int)d / 16;
   }
   int Gs = 1;
   while ((2 * Gs) * T <= 64 && spectrum_lds_bytes(g, 2 * Gs) <= 96 * 1024) Gs *= 2;

@@ -165,8 +165,8 @@ hipError_t launch_spectrum(const LineGeom& g, int mode, const SpecArgs& a, hipSt
                            const LaunchTiming* t = nullptr);
 hipError_t launch_conv(const LineGeom& g, int et, const ConvArgs& a, hipStream_t s, const LaunchTiming* t = nullptr);
 // 1D FFT-convolution for L = 1024 with the radix-32 passes on the matrix
-// cores (bf16 storage): V BLOCKED with 32-channel groups (a.ng = d / 32),
-// N <= 1024, d % 32 == 0.
+// cores (bf16 storage): V BLOCKED with 16-channel groups (a.ng = d / 16),
+// N <= 1024, d % 16 == 0.
 hipError_t launch_mconv(const ConvArgs& a, hipStream_t s, const LaunchTiming* t = nullptr);
 hipError_t launch_score_partial(const LineGeom& g, const ScoreArgs& a, hipStream_t s,
                                 const LaunchTiming* t = nullptr);

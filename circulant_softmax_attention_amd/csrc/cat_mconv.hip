@@ -38,13 +38,15 @@
 // below 2^10 x sqrt2; the last products accumulate in fp32.  The line scale,
 // a power of two, is divided out exactly at the end.
 //
-// Workgroup: one (batch, head, group of 32 channels) = 16 complex lines,
-// 4 waves of 4 lines each.  The group's [N][32] block of V (blocked layout,
-// 64 bytes per token) is staged into LDS by 16-byte LDS-DMA with the chunk
-// position XOR-swizzled by bits 2..3 of the token; each wave reads its
-// line's column from there, and writes the line's outputs back into the same
-// column (no other wave reads it).  The block then leaves as 16-byte stores
-// covering the 64-byte row segments of O.
+// Workgroup: one (batch, head, group of 16 channels) = 8 complex lines,
+// 4 waves of 2 lines each; three workgroups share a compute unit, so every
+// unit gets the same number of lines at the headline shape.  The group's
+// [N][16] block of V (blocked layout, 32 bytes per token) is staged into LDS
+// by 16-byte LDS-DMA (the two chunks of a row swapped by bit 3 of the token).
+// Each wave reads its line's column and writes the line's outputs back into
+// the same column (no other wave reads it).  The block then leaves as
+// 16-byte stores of the 32-byte row segments of O; the groups of one head run
+// on one XCD, so their segments meet in its L2.
 #include "cat_common.hpp"
 #include "cat_internal.hpp"
 
@@ -56,8 +58,9 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4;
 namespace {
 
 constexpr int ML = 1024;      // transform length
-constexpr int MCG = 32;       // channels per workgroup
-constexpr int MROWB = MCG * 2;  // bytes per token row of the staged block
+constexpr int MCG = 16;         // channels per workgroup (8 complex lines)
+constexpr int MROWB = MCG * 2;  // bytes per token row of the V block and of the LDS tile
+constexpr int TILE = ML * MROWB;
 constexpr int MNTHR = 256;
 
 struct W32Table {
@@ -113,21 +116,32 @@ __device__ __forceinline__ CT mul_dB(const K8& k, const C8& d) {
   r.im = mm(ki, d.re, mm(k.re, d.im, z));
   return r;
 }
+// Two fp32 values to one fp16 pair (round to nearest even, one instruction).
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f2v;
+typedef __attribute__((__vector_size__(2 * sizeof(_Float16)))) _Float16 h2v;
+__device__ __forceinline__ uint32_t cvt2(float x, float y) {
+  const h2v h = __builtin_convertvector((f2v{x, y}), h2v);
+  return __builtin_bit_cast(uint32_t, h);
+}
 // Operand whose slot s = v + 4 y takes value v of tile y (the two tiles
 // stacked along the contracted index).
 __device__ __forceinline__ C8 stack(const CT& t0, const CT& t1) {
-  C8 c;
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    c.re[v] = (_Float16)t0.re[v];
-    c.im[v] = (_Float16)t0.im[v];
-    c.re[4 + v] = (_Float16)t1.re[v];
-    c.im[4 + v] = (_Float16)t1.im[v];
-  }
-  return c;
+  union {
+    uint32_t u[4];
+    half8 h;
+  } re, im;
+  re.u[0] = cvt2(t0.re[0], t0.re[1]);
+  re.u[1] = cvt2(t0.re[2], t0.re[3]);
+  re.u[2] = cvt2(t1.re[0], t1.re[1]);
+  re.u[3] = cvt2(t1.re[2], t1.re[3]);
+  im.u[0] = cvt2(t0.im[0], t0.im[1]);
+  im.u[1] = cvt2(t0.im[2], t0.im[3]);
+  im.u[2] = cvt2(t1.im[0], t1.im[1]);
+  im.u[3] = cvt2(t1.im[2], t1.im[3]);
+  return C8{re.h, im.h};
 }
 __device__ __forceinline__ float2 cmulf(float2 a, float2 b) {
-  return make_float2(a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x);
+  return make_float2(fmaf(a.x, b.x, -a.y * b.y), fmaf(a.x, b.y, a.y * b.x));
 }
 // Float max and sum over the wave, the same DPP pattern (a mirror swap adds
 // the partner's partial, which after the quad steps holds its group's total).
@@ -177,9 +191,13 @@ __device__ __forceinline__ int scale_exp(float m, int target) {
   return s;
 }
 
-// LDS byte offset of channel pair p of token n in the staged block.
-__device__ __forceinline__ uint32_t slot_of(int n, int p) {
-  return (uint32_t)n * MROWB + ((((uint32_t)p >> 2) ^ (((uint32_t)n >> 2) & 3)) << 4) + (((uint32_t)p & 3) << 2);
+// The block lives in one LDS tile [1024][32 bytes]; the 16-byte chunk j of
+// token n's row sits at position j ^ bit 3 of n.
+__device__ __forceinline__ uint32_t tsw(int n) { return ((uint32_t)n >> 3) & 1; }
+// Pins a loaded value: the compiler waits for its load here.
+template <class T>
+__device__ __forceinline__ void pin(const T& x) {
+  asm volatile("" ::"v"(x));
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -195,7 +213,7 @@ __device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds) {
 // FULL: N == 1024, no token beyond N.
 template <bool FULL>
 __global__ __launch_bounds__(MNTHR) void mconv_kernel(ConvArgs a) {
-  __shared__ __attribute__((aligned(16))) char blk[ML * MROWB];
+  __shared__ __attribute__((aligned(16))) char blk[TILE];
   __shared__ __attribute__((aligned(16))) float2 sp[ML];  // the (b, h) filter spectrum
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -205,11 +223,42 @@ __global__ __launch_bounds__(MNTHR) void mconv_kernel(ConvArgs a) {
   const int b = bh / a.H, h = bh - b * a.H;
   const int N = a.N;
 
-  // With logits given, wave 0 computes the filter spectrum itself.  Its 16
-  // logits (the positions its lanes hold in the first pass's operand) are
-  // requested before the block's DMA, so they have arrived by the time the
-  // block has.  Position t of the length-1024 circle takes logit t (t < N),
-  // t - 1024 + N (t > 1024 - N; the periodic extension), or none.
+  // Loads the compiler tracks come first (constants, twiddles, wave 0's
+  // logits), then the DMA of the block (and the spectrum, if given).
+
+  // Constant operands: F[lo + 16 x][4 grp + v + 16 y] in slot v + 4 y (read
+  // here, turned into fp16 operands once the first DMA is under way).
+  float kre[2][8], kim[2][8];
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int j = lo + 16 * x, k = 4 * grp + (s & 3) + 16 * (s >> 2);
+      const int m = (j * k) & 31;
+      kre[x][s] = kW32.re[m];
+      kim[x][s] = kW32.im[m];
+    }
+  // The lane's twiddles are the same for all its lines: loaded once.
+  //   t1[bb][kb][v] = W^(b k1) x 32,      b = 16 bb + 4 grp + v, k1 = lo + 16 kb
+  //   t2[kb][ab][v] = conj W^(a k1) / 32, k1 = 16 kb + 4 grp + v, a = lo + 16 ab
+  float2 t1[2][2][4], t2[2][2][4];
+  {
+    const float2* tw1 = a.tw + ML;
+    const float2* tw2 = a.tw + 2 * ML;
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int y = 0; y < 2; ++y)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          t1[x][y][v] = tw1[(lo + 16 * y) * 32 + 16 * x + 4 * grp + v];
+          t2[x][y][v] = tw2[(16 * x + 4 * grp + v) * 32 + lo + 16 * y];
+        }
+  }
+  // With logits given, wave 0 computes the filter spectrum itself, from the
+  // 16 logits its lanes hold in the first pass's operand: position t of the
+  // length-1024 circle takes logit t (t < N), t - 1024 + N (t > 1024 - N;
+  // the periodic extension), or none.
   const bool fused = a.logits != nullptr;
   float zl[2][8];
   if (fused && wave == 0) {
@@ -224,65 +273,61 @@ __global__ __launch_bounds__(MNTHR) void mconv_kernel(ConvArgs a) {
       }
   }
 
-  // Stage the [N][32] block: wave w takes rows 256 w .. + 255, 16 rows per
-  // DMA; lane l fills LDS chunk l % 4 of row n0 + l / 4 with the global chunk
-  // (l % 4) ^ ((n >> 2) & 3).  Rows at or beyond N repeat row N - 1 (never
-  // used).
-  {
-    const char* vblk = reinterpret_cast<const char*>(a.V) + ((size_t)bh * a.ng + g) * (size_t)N * MROWB;
+  // The [N][16] block: 32 DMAs of 32 rows, 8 per wave; lane l fills
+  // position l % 2 of row n0 + l / 2 with the global chunk (l % 2) ^ bit 3
+  // of n.  Rows at or beyond N repeat row N - 1 (never used).
+  const char* vblk = reinterpret_cast<const char*>(a.V) + ((size_t)bh * a.ng + g) * (size_t)N * MROWB;
+  auto dma_tile = [&]() {
     const uint32_t base = lds_addr(blk);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int n0 = wave * 256 + 16 * i;
-      const int n = n0 + (lane >> 2);
-      const int c = (lane & 3) ^ ((n >> 2) & 3);
+    for (int i = 0; i < 8; ++i) {
+      const int n0 = (wave * 8 + i) * 32;
+      const int n = n0 + (lane >> 1);
+      const int c = (lane & 1) ^ (int)tsw(n);
       const int ns = n < N ? n : N - 1;
       lds_dma16(vblk + (size_t)ns * MROWB + c * 16, base + (uint32_t)n0 * MROWB);
     }
-    if (!fused) {  // the spectrum: 8 KB, two 1 KB pieces per wave
-      const char* sg = reinterpret_cast<const char*>(a.spec + (size_t)bh * ML);
+  };
+  if (!fused) {  // the spectrum: 8 KB, two 1 KB pieces per wave
+    const char* sg = reinterpret_cast<const char*>(a.spec + (size_t)bh * ML);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int piece = wave * 2 + i;
-        lds_dma16(sg + piece * 1024 + lane * 16, lds_addr(sp) + piece * 1024);
-      }
+    for (int i = 0; i < 2; ++i) {
+      const int piece = wave * 2 + i;
+      lds_dma16(sg + piece * 1024 + lane * 16, lds_addr(sp) + piece * 1024);
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
   }
-
-  // Constant operands: F[lo + 16 x][4 grp + v + 16 y] in slot v + 4 y.
+  dma_tile();
   K8 kf[2];
 #pragma unroll
   for (int x = 0; x < 2; ++x)
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const int j = lo + 16 * x, k = 4 * grp + (s & 3) + 16 * (s >> 2);
-      const int m = (j * k) & 31;
-      kf[x].re[s] = (_Float16)kW32.re[m];
-      kf[x].im[s] = (_Float16)kW32.im[m];
-      kf[x].nim[s] = (_Float16)(-kW32.im[m]);
+      kf[x].re[s] = (_Float16)kre[x][s];
+      kf[x].im[s] = (_Float16)kim[x][s];
+      kf[x].nim[s] = (_Float16)(-kim[x][s]);
     }
-
-  // The lane's twiddles are the same for all its lines: loaded once.
-  //   t1[bb][kb][v] = W^(b k1) x 32,      b = 16 bb + 4 grp + v, k1 = lo + 16 kb
-  //   t2[kb][ab][v] = conj W^(a k1) / 32, k1 = 16 kb + 4 grp + v, a = lo + 16 ab
-  float2 t1[2][2][4], t2[2][2][4];
-  {
-    const float2* tw1 = a.tw + ML;
-    const float2* tw2 = a.tw + 2 * ML;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
-    for (int x = 0; x < 2; ++x)
+  for (int x = 0; x < 2; ++x) {
+    pin(kf[x].re);
+    pin(kf[x].im);
+    pin(kf[x].nim);
 #pragma unroll
-      for (int y = 0; y < 2; ++y)
+    for (int y = 0; y < 2; ++y)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float2 u1 = tw1[(lo + 16 * y) * 32 + 16 * x + 4 * grp + v];
-          const float2 u2 = tw2[(16 * x + 4 * grp + v) * 32 + lo + 16 * y];
-          t1[x][y][v] = u1;
-          t2[x][y][v] = u2;
-        }
+      for (int v = 0; v < 4; ++v) {
+        pin(t1[x][y][v]);
+        pin(t2[x][y][v]);
+      }
   }
+  if (fused && wave == 0) {
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+      for (int s = 0; s < 8; ++s) pin(zl[bb][s]);
+  }
+  __syncthreads();  // the block (and the spectrum, if given) is in LDS
+
   // The filter spectrum S[k1 + 32 k2] = FFT(softmax line)[k] / L: softmax in
   // fp32 (each logit counted once in the sum: the positions t < N), then the
   // two forward passes as for the data lines.
@@ -343,13 +388,13 @@ __global__ __launch_bounds__(MNTHR) void mconv_kernel(ConvArgs a) {
   }
 
   // Every token this lane reads or writes is lo + 128 grp + (a multiple of
-  // 16), so bits 2..3 of the token, which set the chunk swizzle, are those of
+  // 16), so bit 3 of the token, which sets the chunk position, is that of
   // lo: one per-lane base, and compile-time offsets for the rest.
   const uint32_t lane_row = (uint32_t)(lo + 128 * grp) * MROWB;
 #pragma unroll 1
-  for (int li = 0; li < 4; ++li) {
-    const int p = wave * 4 + li;  // channel pair (complex line) of the group
-    const char* lb = blk + lane_row + ((((uint32_t)p >> 2) ^ (((uint32_t)lo >> 2) & 3)) << 4) + (((uint32_t)p & 3) << 2);
+  for (int li = 0; li < 2; ++li) {
+    const int pp = 2 * wave + li;  // channel pair (complex line) of the group
+    const char* lb = blk + lane_row + ((((uint32_t)pp >> 2) ^ tsw(lo)) << 4) + (((uint32_t)pp & 3) << 2);
     // ---- input: x[32 a + b], b = lo + 16 bb, a in the slots; bf16 pairs
     uint32_t xw[2][8];
     int mb = 0;  // largest |part| as bf16 bits (monotonic in the magnitude)
@@ -456,12 +501,11 @@ __global__ __launch_bounds__(MNTHR) void mconv_kernel(ConvArgs a) {
   {
     char* ob = reinterpret_cast<char*>(a.O) + ((size_t)b * N * a.D + (size_t)h * a.d + (size_t)g * MCG) * 2;
 #pragma unroll 4
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < 8; ++i) {
       const int qq = tid + MNTHR * i;
-      const int n = qq >> 2, j = qq & 3;
+      const int n = qq >> 1, c = qq & 1;  // global chunk c of row n
       if (n < N) {
-        const int c = j ^ ((n >> 2) & 3);
-        const uint4 v = *reinterpret_cast<const uint4*>(blk + n * MROWB + j * 16);
+        const uint4 v = *reinterpret_cast<const uint4*>(blk + n * MROWB + ((c ^ tsw(n)) << 4));
         *reinterpret_cast<uint4*>(ob + (size_t)n * a.D * 2 + c * 16) = v;
       }
     }
@@ -471,7 +515,7 @@ __global__ __launch_bounds__(MNTHR) void mconv_kernel(ConvArgs a) {
 }  // namespace
 
 hipError_t launch_mconv(const ConvArgs& a, hipStream_t s, const LaunchTiming* t) {
-  if (a.N > ML || a.N < 1 || a.d % MCG != 0) return hipErrorInvalidValue;
+  if (a.N > ML || a.N < 1 || a.d % MCG != 0 || a.ng != a.d / MCG) return hipErrorInvalidValue;
   const int blocks = a.B * a.H * a.ng;
   if (a.N == ML) return launch_k(mconv_kernel<true>, dim3(blocks), dim3(MNTHR), 0, s, t, a);
   return launch_k(mconv_kernel<false>, dim3(blocks), dim3(MNTHR), 0, s, t, a);

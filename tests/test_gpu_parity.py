@@ -151,7 +151,8 @@ def test_mix_1d(cat, B, N, D, H, dtype):
 @pytest.mark.parametrize("B,N,D,H,vscale,lscale", [(2, 1024, 128, 2, 1.0, 2.0), (1, 1024, 96, 3, 1.0, 0.0),
                                                    (2, 300, 64, 1, 1.0, 2.0), (1, 511, 96, 1, 1.0, 3.0),
                                                    (3, 257, 64, 2, 1.0, 2.0), (1, 1024, 64, 1, 1e-4, 2.0),
-                                                   (1, 1024, 64, 1, 3e4, 2.0), (1, 1024, 64, 1, 1.0, 40.0)])
+                                                   (1, 1024, 64, 1, 3e4, 2.0), (1, 1024, 64, 1, 1.0, 40.0),
+                                                   (2, 1024, 48, 3, 1.0, 2.0)])
 def test_mix_1d_l1024(cat, monkeypatch, conv, B, N, D, H, vscale, lscale):
     """The 1D conv at transform length 1024 (N = 1024, or N in 257..511 on
     the exact 2N-1 circle): bf16 storage takes the matrix-core path by

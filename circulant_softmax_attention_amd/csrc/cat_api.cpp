@@ -247,14 +247,6 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
         const double ang = two_pi * (double)e / (double)pl->L;
         tw[(size_t)k1 * g.L2 + n2] = make_float2((float)std::cos(ang), (float)(-std::sin(ang)));
       }
-    if (pl->mconv) {  // two more copies for the matrix-core conv: W x 32 and conj(W) / 32
-      const size_t L = (size_t)pl->L;
-      tw.resize(3 * L);
-      for (size_t i = 0; i < L; ++i) {
-        tw[L + i] = make_float2(32.f * tw[i].x, 32.f * tw[i].y);
-        tw[2 * L + i] = make_float2(tw[i].x / 32.f, -tw[i].y / 32.f);
-      }
-    }
     hipError_t e = hipMalloc(&pl->d_tw, tw.size() * sizeof(float2));
     if (e != hipSuccess) {
       delete pl;

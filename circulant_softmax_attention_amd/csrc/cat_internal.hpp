@@ -124,8 +124,7 @@ struct ConvArgs {
   const float2* spec; // [BH][L]
   const float* logits;  // matrix-core conv only: when set, [BH][N] fp32 logits whose
                         // softmax spectrum the conv computes itself (spec unused)
-  const float2* tw;   // 1D inter-pass twiddles (null for 2D); matrix-core conv plans
-                      // append W x 32 and conj(W) / 32 (3 L entries)
+  const float2* tw;   // 1D inter-pass twiddles (null for 2D; unused by the matrix-core conv)
   void* O;            // [B][N][D], element type et
   int B, H, D, N, d;
   int G, log2G, ng;

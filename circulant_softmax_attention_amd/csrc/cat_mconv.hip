@@ -63,20 +63,6 @@ constexpr int MROWB = MCG * 2;  // bytes per token row of the V block and of the
 constexpr int TILE = ML * MROWB;
 constexpr int MNTHR = 256;
 
-struct W32Table {
-  float re[32], im[32];
-};
-constexpr W32Table make_w32() {
-  W32Table t{};
-  for (int m = 0; m < 32; ++m) {
-    const ct::cs w = ct::cossin_2pi(m, 32);
-    t.re[m] = (float)w.c;
-    t.im[m] = (float)(-w.s);  // forward: e^(-2 pi i m / 32)
-  }
-  return t;
-}
-__constant__ W32Table kW32 = make_w32();
-
 // 8 complex values in the K slots of one MFMA operand.
 struct C8 {
   half8 re, im;
@@ -194,11 +180,6 @@ __device__ __forceinline__ int scale_exp(float m, int target) {
 // The block lives in one LDS tile [1024][32 bytes]; the 16-byte chunk j of
 // token n's row sits at position j ^ bit 3 of n.
 __device__ __forceinline__ uint32_t tsw(int n) { return ((uint32_t)n >> 3) & 1; }
-// Pins a loaded value: the compiler waits for its load here.
-template <class T>
-__device__ __forceinline__ void pin(const T& x) {
-  asm volatile("" ::"v"(x));
-}
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
@@ -223,38 +204,36 @@ __global__ __launch_bounds__(MNTHR) void mconv_kernel(ConvArgs a) {
   const int b = bh / a.H, h = bh - b * a.H;
   const int N = a.N;
 
-  // Loads the compiler tracks come first (constants, twiddles, wave 0's
-  // logits), then the DMA of the block (and the spectrum, if given).
-
-  // Constant operands: F[lo + 16 x][4 grp + v + 16 y] in slot v + 4 y (read
-  // here, turned into fp16 operands once the first DMA is under way).
-  float kre[2][8], kim[2][8];
+  // Constant operands F[lo + 16 x][4 grp + v + 16 y] (slot v + 4 y) and the
+  // lane's twiddles, which are the same for all its lines, come from the
+  // hardware sine and cosine (their argument is in revolutions, and every
+  // angle here is an exact multiple of 1/1024 revolution):
+  //   t1[bb][kb][v] = W^(b k1) x 32,      b = 16 bb + 4 grp + v, k1 = lo + 16 kb
+  //   t2[kb][ab][v] = conj W^(a k1) / 32, k1 = 16 kb + 4 grp + v, a = lo + 16 ab
+  K8 kf[2];
 #pragma unroll
   for (int x = 0; x < 2; ++x)
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const int j = lo + 16 * x, k = 4 * grp + (s & 3) + 16 * (s >> 2);
-      const int m = (j * k) & 31;
-      kre[x][s] = kW32.re[m];
-      kim[x][s] = kW32.im[m];
+      const float rev = (float)((j * k) & 31) * (1.f / 32.f);
+      const float c = __builtin_amdgcn_cosf(rev), sn = __builtin_amdgcn_sinf(rev);
+      kf[x].re[s] = (_Float16)c;
+      kf[x].im[s] = (_Float16)(-sn);
+      kf[x].nim[s] = (_Float16)sn;
     }
-  // The lane's twiddles are the same for all its lines: loaded once.
-  //   t1[bb][kb][v] = W^(b k1) x 32,      b = 16 bb + 4 grp + v, k1 = lo + 16 kb
-  //   t2[kb][ab][v] = conj W^(a k1) / 32, k1 = 16 kb + 4 grp + v, a = lo + 16 ab
   float2 t1[2][2][4], t2[2][2][4];
-  {
-    const float2* tw1 = a.tw + ML;
-    const float2* tw2 = a.tw + 2 * ML;
 #pragma unroll
-    for (int x = 0; x < 2; ++x)
+  for (int x = 0; x < 2; ++x)
 #pragma unroll
-      for (int y = 0; y < 2; ++y)
+    for (int y = 0; y < 2; ++y)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          t1[x][y][v] = tw1[(lo + 16 * y) * 32 + 16 * x + 4 * grp + v];
-          t2[x][y][v] = tw2[(16 * x + 4 * grp + v) * 32 + lo + 16 * y];
-        }
-  }
+      for (int v = 0; v < 4; ++v) {
+        const int e1 = ((16 * x + 4 * grp + v) * (lo + 16 * y)) & (ML - 1);
+        const float r1 = (float)e1 * (1.f / ML);
+        t1[x][y][v] = make_float2(32.f * __builtin_amdgcn_cosf(r1), -32.f * __builtin_amdgcn_sinf(r1));
+        t2[x][y][v] = make_float2(__builtin_amdgcn_cosf(r1) * (1.f / 32.f), __builtin_amdgcn_sinf(r1) * (1.f / 32.f));
+      }
   // With logits given, wave 0 computes the filter spectrum itself, from the
   // 16 logits its lanes hold in the first pass's operand: position t of the
   // length-1024 circle takes logit t (t < N), t - 1024 + N (t > 1024 - N;
@@ -297,35 +276,7 @@ __global__ __launch_bounds__(MNTHR) void mconv_kernel(ConvArgs a) {
     }
   }
   dma_tile();
-  K8 kf[2];
-#pragma unroll
-  for (int x = 0; x < 2; ++x)
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      kf[x].re[s] = (_Float16)kre[x][s];
-      kf[x].im[s] = (_Float16)kim[x][s];
-      kf[x].nim[s] = (_Float16)(-kim[x][s]);
-    }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-#pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    pin(kf[x].re);
-    pin(kf[x].im);
-    pin(kf[x].nim);
-#pragma unroll
-    for (int y = 0; y < 2; ++y)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        pin(t1[x][y][v]);
-        pin(t2[x][y][v]);
-      }
-  }
-  if (fused && wave == 0) {
-#pragma unroll
-    for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-      for (int s = 0; s < 8; ++s) pin(zl[bb][s]);
-  }
   __syncthreads();  // the block (and the spectrum, if given) is in LDS
 
   // The filter spectrum S[k1 + 32 k2] = FFT(softmax line)[k] / L: softmax in

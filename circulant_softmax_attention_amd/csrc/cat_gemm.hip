@@ -21,12 +21,14 @@
 // Staging: both operand tiles are loaded straight from global memory into
 // LDS with 16-byte LDS-DMA (no register round trip), each in the layout it
 // has in memory: X tiles [row][K], W tiles [K][column].  X rows are unpadded
-// with the 16-byte position of chunk c in row r at c ^ (r % 8), which spreads
-// the 16 rows of one fragment read over distinct banks.  A W fragment needs
-// the K values of one column: bf16 uses the transposing LDS read of gfx950
-// (ds_read_b64_tr_b16, 4 K values of one column per lane and read), fp32 one
-// 4-byte read per value; W rows are rotated by 2 (k % 4) chunks so that the
-// rows one such read touches fall in different banks.  Two LDS stages: the
+// with the 16-byte position of chunk c in row r at c ^ ((r / 2) % 8): the 16
+// rows of one fragment read (two to a 256-byte bank line) then cover all 64
+// banks.  A W fragment needs the K values of one column: bf16 uses the
+// transposing LDS read of gfx950 (ds_read_b64_tr_b16, 4 K values of one
+// column per lane and read), fp32 one 4-byte read per value; W row k is
+// rotated by rot(k) = 2 (k % 4) + 8 ((k / 8) % 2) chunks, so that the four
+// rows of a lane group and the next group's four (8 rows on) fall in
+// different banks.  Two LDS stages: the
 // DMA of tile k + 1 is in flight while tile k is multiplied.  Rows beyond M
 // and columns beyond ncols are clamped to the last valid ones (their results
 // are never stored); a K tail that does not fill a tile goes through
@@ -98,6 +100,9 @@ __device__ __forceinline__ floatx4 mfma_chunk(const uint4& ra, const uint4& rb, 
   return acc;
 }
 
+// Rotation (in 16-byte chunks) of row k of a staged W tile.
+__device__ __forceinline__ int wrot(int k) { return 2 * (k & 3) + 8 * ((k >> 3) & 1); }
+
 // Element offset of output (row, col) of segment s.
 __device__ __forceinline__ size_t out_index(const GemmSeg& s, const GemmArgs& a, int row, int col) {
   if (s.layout == OUT_ROWMAJOR) return (size_t)row * s.ncols + col;
@@ -159,9 +164,9 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_xw_kernel(GemmArgs a) {
   const bool zwave = zrb[0] || zrb[1];
 
   // X tile: chunk slot s = tid + 256 i is row s / 8, 16-byte position s % 8,
-  // and holds K-chunk (s % 8) ^ (row % 8) -- the same chunk for every i,
-  // since row % 8 = (tid / 8) % 8.
-  const int kch = ((tid & 7) ^ ((tid >> 3) & 7)) * VE;
+  // and holds K-chunk (s % 8) ^ ((row / 2) % 8) -- the same chunk for every
+  // i, since (row / 2) % 8 = (tid / 16) % 8.
+  const int kch = ((tid & 7) ^ ((tid >> 4) & 7)) * VE;
   const elem_t* asrc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -170,16 +175,15 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_xw_kernel(GemmArgs a) {
     asrc[i] = reinterpret_cast<const elem_t*>(a.X) + (size_t)am * K + kch;
   }
   // W tile, K-major as W is stored: slot s = tid + 256 i is K row s / CPRB,
-  // position s % CPRB, and holds column chunk (position - rot(row)) mod CPRB
-  // with rot(k) = 2 (k % 4): the four rows one transposing read touches sit
-  // 32 bytes apart in the banks.  Columns beyond ncols are clamped to the
-  // last chunk (their results are never stored).
+  // position s % CPRB, and holds column chunk (position - rot(row)) mod CPRB.
+  // Columns beyond ncols are clamped to the last chunk (their results are
+  // never stored).
   const elem_t* bsrc[BCH];
   int brow[BCH];
 #pragma unroll
   for (int i = 0; i < BCH; ++i) {
     const int s_ = tid + NTHR * i, k = s_ / CPRB, pos = s_ - k * CPRB;
-    const int c = (pos + CPRB - (2 * (k & 3)) % CPRB) % CPRB;
+    const int c = (pos + CPRB - wrot(k) % CPRB) % CPRB;
     int col = n0 + c * VE;
     col = col + VE <= ncols ? col : ncols - VE;
     brow[i] = k;
@@ -221,7 +225,7 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_xw_kernel(GemmArgs a) {
   };
 
   const int lrow = lane & 15, lgrp = lane >> 4;
-  const int sw = lrow & 7;  // row % 8 of every X fragment row this lane reads
+  const int sw = (lrow >> 1) & 7;  // (row / 2) % 8 of every X fragment row this lane reads
   floatx4 acc[4][TN];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -229,7 +233,7 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_xw_kernel(GemmArgs a) {
     for (int j = 0; j < TN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   // Fragment of 16 columns (col0 ..) x one K step of a K-major tile (row
-  // pitch `pitch` bytes, `cpr` chunks, rows rotated by 2 (k % 4) chunks) for
+  // pitch `pitch` bytes, `cpr` chunks, rows rotated by rot(k) chunks) for
   // this lane: column col0 + lrow, the K values of group lgrp.  bf16: two
   // transposing LDS reads, each giving 4 consecutive K values of the lane's
   // column (the 16 lanes of a group address 4 rows x 4 column quads); fp32:
@@ -243,7 +247,7 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_xw_kernel(GemmArgs a) {
 #pragma unroll
       for (int hlf = 0; hlf < 2; ++hlf) {
         const int k = kc * 32 + 8 * lgrp + 4 * hlf + (lrow >> 2);
-        const int pos = (c + 2 * (k & 3)) % cpr;
+        const int pos = (c + wrot(k)) % cpr;
         const char* ptr = tile + k * pitch + pos * 16 + 8 * (lrow & 1);
         const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (lds_v4s*)(const __attribute__((address_space(3))) char*)ptr);
@@ -256,7 +260,7 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_xw_kernel(GemmArgs a) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int k = kc * 16 + 4 * lgrp + u;
-        const int pos = (col / 4 + 2 * (k & 3)) % cpr;
+        const int pos = (col / 4 + wrot(k)) % cpr;
         f[u] = *reinterpret_cast<const float*>(tile + k * pitch + pos * 16 + 4 * (col & 3));
       }
       return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3]));

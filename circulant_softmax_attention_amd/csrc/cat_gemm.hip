@@ -100,8 +100,18 @@ __device__ __forceinline__ floatx4 mfma_chunk(const uint4& ra, const uint4& rb, 
   return acc;
 }
 
-// Rotation (in 16-byte chunks) of row k of a staged W tile.
-__device__ __forceinline__ int wrot(int k) { return 2 * (k & 3) + 8 * ((k >> 3) & 1); }
+// Rotation (in 16-byte chunks) of row k of a staged W tile, chosen per
+// element type and tile width so that the 64 lanes of every fragment read
+// (two transposing 8-byte reads per lane for bf16, one 4-byte read per K value
+// for fp32) fall on distinct LDS banks, or on at most two where no rotation of
+// this form avoids it (fp32, 96 columns).
+template <int ET, int BN>
+__device__ __forceinline__ int wrot(int k) {
+  if constexpr (ET != ET_BF16) return 4 * ((k >> 2) & 1) + 8 * ((k >> 3) & 1);
+  else if constexpr (BN == 96) return 2 * ((k >> 3) & 1);
+  else if constexpr (BN == 128) return 2 * (k & 3) + 8 * ((k >> 3) & 1);
+  else return 6 * (k & 3) + 6 * ((k >> 3) & 1);
+}
 
 // Element offset of output (row, col) of segment s.
 __device__ __forceinline__ size_t out_index(const GemmSeg& s, const GemmArgs& a, int row, int col) {
@@ -183,7 +193,7 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_xw_kernel(GemmArgs a) {
 #pragma unroll
   for (int i = 0; i < BCH; ++i) {
     const int s_ = tid + NTHR * i, k = s_ / CPRB, pos = s_ - k * CPRB;
-    const int c = (pos + CPRB - wrot(k) % CPRB) % CPRB;
+    const int c = (pos + CPRB - wrot<ET, BN>(k) % CPRB) % CPRB;
     int col = n0 + c * VE;
     col = col + VE <= ncols ? col : ncols - VE;
     brow[i] = k;
@@ -247,7 +257,7 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_xw_kernel(GemmArgs a) {
 #pragma unroll
       for (int hlf = 0; hlf < 2; ++hlf) {
         const int k = kc * 32 + 8 * lgrp + 4 * hlf + (lrow >> 2);
-        const int pos = (c + wrot(k)) % cpr;
+        const int pos = (c + wrot<ET, BN>(k)) % cpr;
         const char* ptr = tile + k * pitch + pos * 16 + 8 * (lrow & 1);
         const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (lds_v4s*)(const __attribute__((address_space(3))) char*)ptr);
@@ -260,7 +270,7 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_xw_kernel(GemmArgs a) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int k = kc * 16 + 4 * lgrp + u;
-        const int pos = (col / 4 + wrot(k)) % cpr;
+        const int pos = (col / 4 + wrot<ET, BN>(k)) % cpr;
         f[u] = *reinterpret_cast<const float*>(tile + k * pitch + pos * 16 + 4 * (col & 3));
       }
       return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3]));

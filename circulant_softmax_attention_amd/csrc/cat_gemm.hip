@@ -297,12 +297,13 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_xw_kernel(GemmArgs a) {
       for (int j = 0; j < TN; ++j) acc[i][j] = mfma_chunk<ET>(bf[j], af[i], acc[i][j]);
   };
 
-  // W_A^T fragments of K tile kt, [zb][kc]: lane (lrow, lgrp) holds head
-  // 16 zb + lrow (clamped to nz - 1; such heads are never stored) at the K
-  // positions of its X fragments; K positions at or beyond K read zero.
+  // W_A^T fragments of K tile kt, [buf][zb][kc] (buf = kt % 2): lane (lrow,
+  // lgrp) holds head 16 zb + lrow (clamped to nz - 1; such heads are never
+  // stored) at the K positions of its X fragments; K positions at or beyond K
+  // read zero.
   constexpr int ZA = ZB > 0 ? ZB : 1;  // register arrays need a size
-  uint4 zw[ZA][2];
-  auto zload = [&](int kt) {
+  uint4 zw[2][ZA][2];
+  auto zload = [&](int kt, int buf) {
     const elem_t* wa = reinterpret_cast<const elem_t*>(a.Wz);
 #pragma unroll
     for (int zb = 0; zb < ZB; ++zb) {
@@ -318,7 +319,7 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_xw_kernel(GemmArgs a) {
           const elem_t v = wa[(size_t)k * nz + h];
           e[u] = kb + u < K ? v : elem_t(0);
         }
-        zw[zb][kc] = *reinterpret_cast<const uint4*>(e);
+        zw[buf][zb][kc] = *reinterpret_cast<const uint4*>(e);
       }
     }
   };
@@ -327,14 +328,14 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_xw_kernel(GemmArgs a) {
   for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
     for (int zb = 0; zb < ZA; ++zb) zacc[ii][zb] = floatx4{0.f, 0.f, 0.f, 0.f};
-  auto zmma = [&](int kc, const uint4 (&af)[4]) {
+  auto zmma = [&](int kc, const uint4 (&af)[4], int buf) {
     if (ZB == 0 || !zwave) return;
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii) {
       if (zrb[ii]) {
         const uint4 xa = wn ? af[1 + 2 * ii] : af[2 * ii];  // no dynamic register indexing
 #pragma unroll
-        for (int zb = 0; zb < ZB; ++zb) zacc[ii][zb] = mfma_chunk<ET>(zw[zb][kc], xa, zacc[ii][zb]);
+        for (int zb = 0; zb < ZB; ++zb) zacc[ii][zb] = mfma_chunk<ET>(zw[buf][zb][kc], xa, zacc[ii][zb]);
       }
     }
   };
@@ -343,11 +344,14 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_xw_kernel(GemmArgs a) {
   // own DMA of tile kt complete and, after the barrier, all of them have
   // finished multiplying tile kt - 1, whose stage then receives tile kt + 1.
   // Two workgroups share a compute unit, so one's LDS reads overlap the
-  // other's MFMAs.  The W_A^T fragments of tile kt + 1 are requested once
-  // tile kt's are used, and awaited with the DMA at the next step's top.
+  // other's MFMAs.  The W_A^T fragments are double-buffered in registers:
+  // those of tile kt + 1 are requested right after the barrier of step kt,
+  // before its MFMAs, so their global-load latency hides behind a whole step.
+  // The loop is unrolled by two so that stage and buffer indices are
+  // compile-time constants.
   const int nk = (K + BK - 1) / BK;
   issue(0, 0);
-  if (ZB > 0 && zwave) zload(0);
+  if (ZB > 0 && zwave) zload(0, 0);
   // L2 warm-up: the column tiles of one row panel (consecutive workgroups on
   // one XCD) together touch every 64-byte sector of the panel's X rows once,
   // so that the staging loads of the later K tiles hit L2 rather than HBM.
@@ -369,18 +373,34 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_xw_kernel(GemmArgs a) {
     }
   }
   uint4 af[4], bf[TN];
-  for (int kt = 0; kt < nk; ++kt) {
-    const int st = kt & 1;
+  auto step = [&](int kt, auto parity) {
+    constexpr int st = decltype(parity)::value;
     wait_vmem_all();
     __syncthreads();
+    if (ZB > 0 && zwave) {
+      // The fragments of tile kt are complete (the wait above); tying them to
+      // this point makes the compiler's own wait for them land here, before
+      // the loads of the next tile are issued, instead of at their first use.
+#pragma unroll
+      for (int zb = 0; zb < ZA; ++zb)
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+          const uint4 v = zw[st][zb][kc];
+          asm volatile("" ::"v"(v.x), "v"(v.y), "v"(v.z), "v"(v.w));
+        }
+      if (kt + 1 < nk) zload(kt + 1, st ^ 1);
+    }
     if (kt + 1 < nk) issue(kt + 1, st ^ 1);
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
       read_frags(st, kc, af, bf);
       mma(af, bf);
-      zmma(kc, af);
+      zmma(kc, af, st);
     }
-    if (ZB > 0 && zwave && kt + 1 < nk) zload(kt + 1);
+  };
+  for (int kt = 0; kt < nk; kt += 2) {
+    step(kt, std::integral_constant<int, 0>{});
+    if (kt + 1 < nk) step(kt + 1, std::integral_constant<int, 1>{});
   }
   if (((wv[0] ^ wv[1]) + (wv[2] ^ wv[3])) == 0x9E3779B9u && M < 0)  // keeps the warm-up loads
     reinterpret_cast<float*>(sg.out)[0] = 0.f;

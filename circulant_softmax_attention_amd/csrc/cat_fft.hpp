@@ -223,15 +223,25 @@ constexpr int cgcd(int a, int b) { return b == 0 ? a : cgcd(b, a % b); }
 // 1D an inter-pass twiddle W_L^{n2 k1} joins the passes; on a 2D Hg x Wg grid
 // (L1 = Hg, L2 = Wg, p = r Wg + c) there is none and the pair of passes is
 // the 2D DFT.
-//   pass 1: thread t holds J1 = E/L1 columns n2 = t + T j, registers j*L1 + n1
-//   pass 2: thread t holds J2 = E/L2 rows    k1 = t + T j, registers j*L2 + n2
-template <int L1_, int L2_>
+//
+// Each length-L1 (pass 1) or length-L2 (pass 2) DFT is held by S threads
+// (S = 1 or 2): thread h of the S holds the indices congruent to h mod S, in
+// and out (an even/odd split joined by one exchange between the two threads).
+// With TC = T / S thread groups and t = S c + h:
+//   pass 1: group c holds J1 = E S / L1 columns n2 = c + TC j; register
+//           j (L1/S) + m holds n1 (in) or k1 (out) = S m + h
+//   pass 2: group c holds J2 = E S / L2 rows    k1 = c + TC j; register
+//           j (L2/S) + m holds n2 (in) or k2 (out) = S m + h
+template <int L1_, int L2_, int S_ = 1>
 struct Grid2 {
-  static constexpr int L1 = L1_, L2 = L2_, L = L1_ * L2_;
-  static constexpr int T = cgcd(L1_, L2_);
+  static constexpr int L1 = L1_, L2 = L2_, L = L1_ * L2_, S = S_;
+  static constexpr int T = S_ * cgcd(L1_, L2_);
   static constexpr int E = L / T;
-  static constexpr int J1 = E / L1_;
-  static constexpr int J2 = E / L2_;
+  static constexpr int Q1 = L1_ / S_, Q2 = L2_ / S_;  // values of one DFT per thread
+  static constexpr int J1 = E / Q1;
+  static constexpr int J2 = E / Q2;
+  static constexpr int TC = T / S_;
+  static_assert(S_ == 1 || (S_ == 2 && Q1 % 2 == 0 && Q2 % 2 == 0), "split DFTs need even halves");
   // LDS row pitch (complex) of the [L1][L2] exchange tile, padded so that a
   // wave's 64-bit accesses spread over the banks.
   static constexpr int P2 = L2_ + ((L2_ % 2 == 0) ? 1 : 0);

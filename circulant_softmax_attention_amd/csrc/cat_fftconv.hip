@@ -78,6 +78,7 @@ hipError_t launch_spectrum(const LineGeom& g, int mode, const SpecArgs& a, hipSt
   SpecFn fn = e ? (mode == 0 ? e->spec0 : e->spec1) : nullptr;
   if (!fn) return hipErrorInvalidValue;
   SpecArgs aa = a;
+  if (e->S > 1 && aa.G != 1) return hipErrorInvalidValue;  // split DFTs pair adjacent lanes
   aa.log2G = ilog2(aa.G);
   const size_t lds = spectrum_lds_bytes(g, aa.G);
   const int blocks = (aa.BH + aa.G - 1) / aa.G;
@@ -89,6 +90,7 @@ hipError_t launch_conv(const LineGeom& g, int et, const ConvArgs& a, hipStream_t
   ConvFn fn = e ? (et == ET_F32 ? e->conv_f32 : e->conv_bf16) : nullptr;
   if (!fn) return hipErrorInvalidValue;
   ConvArgs aa = a;
+  if (e->S > 1 && aa.G != 1) return hipErrorInvalidValue;  // split DFTs pair adjacent lanes
   aa.log2G = ilog2(aa.G);
   const size_t lds = (size_t)aa.G * line_lds_bytes(g);
   const int blocks = aa.B * aa.H * aa.ng;

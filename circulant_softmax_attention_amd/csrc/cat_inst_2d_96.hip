@@ -4,7 +4,7 @@
 namespace cat {
 const Entry* entries_2d_96(int* n) {
   static const Entry e[] = {
-      kern::make_entry<96, 96, false>(),
+      kern::make_entry<96, 96, false, 2>(),
   };
   *n = (int)(sizeof(e) / sizeof(e[0]));
   return e;

@@ -251,11 +251,11 @@ def test_determinism_1d(cat):
 GRIDS = [(1, 1), (2, 3), (3, 4), (4, 4), (6, 8), (8, 8), (12, 12), (16, 16)]
 
 
-@pytest.mark.parametrize("Hg,Wg", GRIDS + [(32, 32)])
+@pytest.mark.parametrize("Hg,Wg", GRIDS + [(32, 32), (96, 96)])
 def test_scores_2d(cat, Hg, Wg):
     say("scores_2d", Hg, Wg)
     import torch
-    B, D, H = 2, 16, 2
+    B, D, H = (1 if Hg * Wg > 4096 else 2), 16, 2
     rng = np.random.default_rng(Hg * 100 + Wg)
     Q = (rng.standard_normal((B, Hg * Wg, D)) * 0.5).astype(np.float32)
     K = (rng.standard_normal((B, Hg * Wg, D)) * 0.5).astype(np.float32)
@@ -266,11 +266,12 @@ def test_scores_2d(cat, Hg, Wg):
     assert_parity(probs, ref, "f32", "a*")
 
 
-@pytest.mark.parametrize("Hg,Wg,dtype", [(g[0], g[1], "f32") for g in GRIDS] + [(12, 12, "bf16"), (32, 32, "f32")])
+@pytest.mark.parametrize("Hg,Wg,dtype", [(g[0], g[1], "f32") for g in GRIDS] +
+                         [(12, 12, "bf16"), (32, 32, "f32"), (96, 96, "f32"), (96, 96, "bf16")])
 def test_mix_2d(cat, Hg, Wg, dtype):
     say("mix_2d", Hg, Wg, dtype)
     import torch
-    B, D, H = 2, 16, 2
+    B, D, H = (1 if Hg * Wg > 4096 else 2), 16, 2
     N = Hg * Wg
     rng = np.random.default_rng(N + 3)
     logits = (rng.standard_normal((B, H, N)) * 2).astype(np.float32)

@@ -44,14 +44,18 @@ def fft_flops(L: int) -> float:
     return 5.0 * L * math.log2(L) if L > 1 else 0.0
 
 
-def kernel_model(wl, L: int, ngrp: int, fused_spectrum: bool = False):
+def kernel_model(wl, L: int, ngrp: int, fused_spectrum: bool = False, direct: bool = False):
     """Algorithmic bytes and flops of each kernel of one forward call.
 
     fused_spectrum: the 1D conv ran on the matrix cores and computed the
     softmax spectrum itself (no spectrum launch): it reads the logits instead
     of a spectrum, and its flops are the matrix products it executes (four
     32x32x32 complex products per line, each 4 x 2 x 32^3 real flops, plus two
-    per workgroup of 16 channels for the spectrum line)."""
+    per workgroup of 16 channels for the spectrum line).
+
+    direct: the 1D mixing ran as the direct product circ(z*) V on the matrix
+    cores ("directconv", softmax included): it reads V and the logits and
+    writes O; its flops are the product's 2 N^2 d per (batch, head)."""
     s = 4 if wl.dtype == "f32" else 2
     B, N, D, H, d = wl.B, wl.N, wl.D, wl.H, wl.d
     T = B * N
@@ -76,6 +80,9 @@ def kernel_model(wl, L: int, ngrp: int, fused_spectrum: bool = False):
         cplx = 4 * 2.0 * 32 ** 3  # one 32x32x32 complex product in real flops
         m["fftconv"] = dict(bytes=2 * T * D * s + BH * N * 4, flops=lines * 4 * cplx + B * H * (d // 16) * 2 * cplx,
                             unit="mfma_f16")
+    if direct:
+        m["directconv"] = dict(bytes=2 * T * D * s + BH * N * 4, flops=2.0 * BH * N * N * d,
+                               unit="mfma_bf16" if s == 2 else "mfma_f32")
     return m
 
 
@@ -93,6 +100,8 @@ KERNEL_SOURCES = {
                 "circulant_softmax_attention_amd/csrc/cat_common.hpp"],
     "project": ["circulant_softmax_attention_amd/csrc/cat_gemm.hip", "circulant_softmax_attention_amd/csrc/cat_common.hpp"],
 }
+KERNEL_SOURCES["directconv"] = ["circulant_softmax_attention_amd/csrc/cat_dconv.hip",
+                                 "circulant_softmax_attention_amd/csrc/cat_common.hpp"]
 KERNEL_SOURCES["spectrum"] = KERNEL_SOURCES["fftconv"]
 KERNEL_SOURCES["scores"] = KERNEL_SOURCES["fftconv"]
 
@@ -221,12 +230,15 @@ def run(args):
     inst_ms = (time.perf_counter() - t0) * 1000.0 / args.steps
     ktimes = cat.cat_plan_kernel_times(plan)
     cat.cat_plan_set_timing(plan, False)
+    conv_path = plan.conv_path()
+    if conv_path == "direct":  # the mixing launch is the direct product, not a transform
+        ktimes["directconv"] = ktimes.pop("fftconv")
     for k, (ms, n) in ktimes.items():
         log(f"  kernel {k:10s} {ms * 1000:9.2f} us avg over {n} launches")
 
     ngrp = (wl.d // 2 + 3) // 4
     fused = wl.kind == "1d" and ktimes.get("spectrum", (0.0, 0))[1] == 0
-    model = kernel_model(wl, L, ngrp, fused_spectrum=fused)
+    model = kernel_model(wl, L, ngrp, fused_spectrum=fused, direct=conv_path == "direct")
     kernels = {}
     ktimes = {k: v for k, v in ktimes.items() if v[1] > 0}  # kernels this path launched
     for k, (ms, n) in ktimes.items():
@@ -278,7 +290,7 @@ def run(args):
         "data": "synthetic (seeded PCG64: X~N(0,1), W~N(0,1/D))",
         "config": {"workload": wl.name, "kind": wl.kind, "B": wl.B, "N": wl.N, "D": wl.D, "H": wl.H,
                    "grid": [wl.Hg, wl.Wg] if wl.kind == "2d" else None, "storage": wl.dtype,
-                   "transform": [L, L1, L2], "global_batch": wl.B, "seq_len": wl.N, "parallelism": "none"},
+                   "transform": [L, L1, L2], "mixing": conv_path, "global_batch": wl.B, "seq_len": wl.N, "parallelism": "none"},
         "e2e_hbm_frac": round(((2 * tokens * wl.D * esz) + sum(w.numel() * esz for w in weights))
                               / (ms_per_step / 1000.0) / 1e9 / HBM_PEAK_GBS, 4),
         "gpu_event_ms_per_step": round(gpu_ms_per_step, 5),

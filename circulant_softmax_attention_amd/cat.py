@@ -28,7 +28,7 @@ CAT_1D, CAT_BCCB_2D = 0, 1
 # Every symbol include/cat.h declares.
 EXPORTS = ["cat_plan_create", "cat_plan_destroy", "cat_plan_workspace_size", "cat_plan_geometry",
            "cat_forward_1d", "cat_forward_bccb_2d", "cat_status_string", "cat_last_error",
-           "cat_plan_set_timing", "cat_plan_kernel_times",
+           "cat_plan_set_timing", "cat_plan_kernel_times", "cat_plan_conv_path",
            "cat_step_project", "cat_step_spectrum", "cat_step_mix", "cat_step_scores_2d"]
 KERNELS_1D = ["project", "spectrum", "fftconv"]
 KERNELS_2D = ["project", "scores", "spectrum", "fftconv"]
@@ -58,6 +58,7 @@ def _load() -> ctypes.CDLL:
     lib.cat_forward_1d.argtypes = [vp] * 7
     lib.cat_forward_bccb_2d.argtypes = [vp] * 8
     lib.cat_plan_set_timing.argtypes = [vp, ctypes.c_int]
+    lib.cat_plan_conv_path.argtypes = [vp, ctypes.POINTER(ctypes.c_int)]
     lib.cat_plan_kernel_times.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64),
                                           ctypes.POINTER(ctypes.c_int)]
     lib.cat_step_project.argtypes = [vp] * 9
@@ -115,6 +116,9 @@ class Plan:
     def geometry(self):
         return cat_plan_geometry(self)
 
+    def conv_path(self) -> str:
+        return cat_plan_conv_path(self)
+
     def __del__(self):
         if getattr(self, "handle", None):
             _lib.cat_plan_destroy(ctypes.c_void_p(self.handle))
@@ -141,6 +145,17 @@ def cat_plan_geometry(plan: Plan):
     _check(_lib.cat_plan_geometry(ctypes.c_void_p(plan.handle), ctypes.byref(L), ctypes.byref(L1),
                                   ctypes.byref(L2)), "cat_plan_geometry")
     return int(L.value), int(L1.value), int(L2.value)
+
+
+CONV_PATHS = {0: "fft_valu", 1: "fft_matrix", 2: "direct"}
+
+
+def cat_plan_conv_path(plan: Plan) -> str:
+    """How the plan evaluates the circulant mixing: "fft_valu", "fft_matrix"
+    or "direct" (include/cat.h, cat_plan_conv_path)."""
+    p = ctypes.c_int()
+    _check(_lib.cat_plan_conv_path(ctypes.c_void_p(plan.handle), ctypes.byref(p)), "cat_plan_conv_path")
+    return CONV_PATHS[int(p.value)]
 
 
 def cat_plan_set_timing(plan: Plan, enable: bool = True):

@@ -24,7 +24,8 @@ struct cat_plan_s {
   int G;             // complex lines per transform workgroup
   int ng;            // line groups per head (d / 2 / G)
   bool mconv;        // 1D conv on the matrix cores (L = 1024, bf16, d % 16 == 0)
-  int cg;            // channels per group of the blocked V (2 G, or 16 for mconv)
+  bool direct;       // 1D direct circulant product on the matrix cores (bf16, N <= 256, d % 32 == 0)
+  int cg;            // channels per group of the blocked V (2 G; 16 for mconv, 32 for direct)
   int Gs;            // lines per spectrum workgroup
   int npair, ngrp, ppg;  // 2D score partials
   float2* d_tw;      // 1D inter-pass twiddles, L entries (null in 2D)
@@ -192,9 +193,13 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
   {
     const char* cv = std::getenv("CAT_CONV");
     const bool force_valu = cv && std::strcmp(cv, "valu") == 0;
-    pl->mconv = !force_valu && p->kind == CAT_1D && p->dtype == CAT_BF16 && g.L1 * g.L2 == 1024 && d % 16 == 0;
-    pl->cg = pl->mconv ? 16 : 2 * G;
+    const bool force_fft = force_valu || (cv && std::strcmp(cv, "fft") == 0);
+    pl->direct = !force_fft && p->kind == CAT_1D && p->dtype == CAT_BF16 && p->N <= 256 && d % 32 == 0;
+    pl->mconv = !pl->direct && !force_valu && p->kind == CAT_1D && p->dtype == CAT_BF16 &&
+                g.L1 * g.L2 == 1024 && d % 16 == 0;
+    pl->cg = pl->direct ? 32 : pl->mconv ? 16 : 2 * G;
     if (pl->mconv) pl->ng = (int)d / 16;
+    if (pl->direct) pl->ng = (int)d / 32;
   }
   int Gs = 1;
   while ((2 * Gs) * T <= 64 && spectrum_lds_bytes(g, 2 * Gs) <= 96 * 1024) Gs *= 2;
@@ -334,6 +339,12 @@ cat_status cat_plan_workspace_size(cat_plan plan, size_t* bytes) {
   return CAT_OK;
 }
 
+cat_status cat_plan_conv_path(cat_plan plan, int* path) {
+  if (!plan || !path) return fail(CAT_ERR_INVALID_ARG, "NULL argument");
+  *path = plan->direct ? CAT_PATH_DIRECT : plan->mconv ? CAT_PATH_FFT_MATRIX : CAT_PATH_FFT_VALU;
+  return CAT_OK;
+}
+
 cat_status cat_plan_geometry(cat_plan plan, int64_t* L, int64_t* L1, int64_t* L2) {
   if (!plan) return fail(CAT_ERR_INVALID_ARG, "NULL plan");
   if (L) *L = plan->L;
@@ -407,6 +418,7 @@ ConvArgs conv_base(const cat_plan_s* pl, const void* Vblk, const float2* spec, v
 
 // The 1D conv: on the matrix cores where the plan chose that path.
 hipError_t run_conv_1d(const cat_plan_s* pl, const ConvArgs& ca, hipStream_t s, const LaunchTiming* t = nullptr) {
+  if (pl->direct) return launch_dconv(pl->et, ca, s, t);
   return pl->mconv ? launch_mconv(ca, s, t) : launch_conv(pl->geom, pl->et, ca, s, t);
 }
 
@@ -439,14 +451,15 @@ cat_status cat_forward_1d(cat_plan plan, const void* X, const void* W_A, const v
 
   SpecArgs sa = spec_base(plan, workspace);
   sa.logits = z;
-  if (!plan->mconv) {  // (the matrix-core conv takes the softmax spectrum itself)
+  const bool own_softmax = plan->mconv || plan->direct;  // (these take the logits themselves)
+  if (!own_softmax) {
     e = launch_spectrum(plan->geom, 0, sa, s, mk.at(1));
     if (e != hipSuccess) return hip_fail(e, "spectrum launch");
     if ((st = check_sync(plan, "spectrum")) != CAT_OK) return st;
   }
 
   ConvArgs ca = conv_base(plan, Vb, sa.spec, O);
-  if (plan->mconv) ca.logits = z;
+  if (own_softmax) ca.logits = z;
   e = run_conv_1d(plan, ca, s, mk.at(2));
   if (e != hipSuccess) return hip_fail(e, "fft-conv launch");
   return check_sync(plan, "fft-conv");
@@ -574,13 +587,14 @@ cat_status cat_step_mix(cat_plan plan, const float* logits, const void* V, void*
   if (e != hipSuccess) return hip_fail(e, "relayout launch");
   SpecArgs sa = spec_base(plan, workspace);
   sa.logits = logits;
-  if (!plan->mconv) {
+  const bool own_softmax = plan->mconv || plan->direct;
+  if (!own_softmax) {
     e = launch_spectrum(plan->geom, 0, sa, s);
     if (e != hipSuccess) return hip_fail(e, "spectrum launch");
     if ((st = check_sync(plan, "spectrum")) != CAT_OK) return st;
   }
   ConvArgs ca = conv_base(plan, Vb, sa.spec, O);
-  if (plan->mconv) ca.logits = logits;
+  if (own_softmax) ca.logits = logits;
   e = run_conv_1d(plan, ca, s);
   if (e != hipSuccess) return hip_fail(e, "fft-conv launch");
   return check_sync(plan, "fft-conv");

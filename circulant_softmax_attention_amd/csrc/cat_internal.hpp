@@ -167,6 +167,11 @@ hipError_t launch_conv(const LineGeom& g, int et, const ConvArgs& a, hipStream_t
 // cores (bf16 storage): V BLOCKED with 16-channel groups (a.ng = d / 16),
 // N <= 1024, d % 16 == 0.
 hipError_t launch_mconv(const ConvArgs& a, hipStream_t s, const LaunchTiming* t = nullptr);
+// 1D circulant mixing for N <= 256 as the direct product circ(z*) V on the
+// matrix cores, softmax of a.logits [BH][N] included: bf16 storage only
+// (et == ET_BF16), V BLOCKED with 32-channel groups (a.ng = d / 32),
+// d % 32 == 0; a.spec and a.tw unused.
+hipError_t launch_dconv(int et, const ConvArgs& a, hipStream_t s, const LaunchTiming* t = nullptr);
 hipError_t launch_score_partial(const LineGeom& g, const ScoreArgs& a, hipStream_t s,
                                 const LaunchTiming* t = nullptr);
 hipError_t launch_relayout(const RelayoutArgs& a, hipStream_t s);

@@ -12,7 +12,10 @@
  *     V    = X_b W_V
  *     O_b[:, head h] = circ(z*_h) V[:, head h],  circ(w)[i][j] = w[(i - j) mod N]
  *   evaluated as IFFT(FFT(z*_h) . FFT(V_h)) along the tokens ("Key designs:
- *   FFT-accelerated computation").  There is no output projection.
+ *   FFT-accelerated computation"), or, in bf16 for N <= 256, as the product with
+ *   circ(z*_h) itself on the matrix cores (the same page notes that at
+ *   N = 256 the FFT's overhead cancels its advantage; see
+ *   cat_plan_conv_path).  There is no output projection.
  *
  * 2D, BCCB circulant attention (Vision Transformers are Circulant Attention
  * Learners, "What does this finding overturn?" and "Circulant Attention:
@@ -114,6 +117,26 @@ cat_status cat_plan_workspace_size(cat_plan plan, size_t* bytes);
 /* Length of the transform circle / grid the plan uses (L, and L1 x L2 of
  * its two passes).  Diagnostic. */
 cat_status cat_plan_geometry(cat_plan plan, int64_t* L, int64_t* L1, int64_t* L2);
+
+/* How the plan evaluates the circulant mixing (diagnostic).  *path:
+ *   CAT_PATH_FFT_VALU   (0) transforms on the vector ALU, with a separate
+ *                           softmax-spectrum launch (every 2D plan; 1D when
+ *                           no other path applies);
+ *   CAT_PATH_FFT_MATRIX (1) 1D, L = 1024, bf16: radix-32 DFT passes on the
+ *                           matrix cores, softmax spectrum computed in the
+ *                           same launch;
+ *   CAT_PATH_DIRECT     (2) 1D, bf16, N <= 256, d a multiple of 32: the product
+ *                           circ(z*_h) V_h formed directly on the matrix
+ *                           cores, softmax in the same launch (CAT, "Key
+ *                           designs: circulant attention matrix
+ *                           construction").
+ * The environment variable CAT_CONV=fft (at plan creation) excludes path 2,
+ * CAT_CONV=valu paths 1 and 2.  Errors: CAT_ERR_INVALID_ARG for a NULL plan
+ * or NULL path. */
+#define CAT_PATH_FFT_VALU 0
+#define CAT_PATH_FFT_MATRIX 1
+#define CAT_PATH_DIRECT 2
+cat_status cat_plan_conv_path(cat_plan plan, int* path);
 
 /* CAT 1D forward (see top of file).  X [B][N][D], W_A [D][H], W_V [D][D],
  * O [B][N][D] in the plan's storage dtype. */

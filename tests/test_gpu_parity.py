@@ -174,6 +174,50 @@ def test_mix_1d_l1024(cat, monkeypatch, conv, B, N, D, H, vscale, lscale):
     assert_parity(to_np(O), ref, "bf16", "O")
 
 
+@pytest.mark.parametrize("conv", ["auto", "fft"])
+@pytest.mark.parametrize("B,N,D,H,dtype,vscale,lscale", [
+    (2, 1, 64, 2, "f32", 1.0, 2.0), (2, 2, 64, 2, "bf16", 1.0, 2.0), (1, 17, 96, 1, "f32", 1.0, 2.0),
+    (2, 31, 64, 1, "bf16", 1.0, 2.0), (1, 32, 64, 2, "f32", 1.0, 2.0), (2, 33, 128, 2, "bf16", 1.0, 2.0),
+    (3, 100, 192, 2, "f32", 1.0, 2.0), (2, 197, 128, 2, "bf16", 1.0, 3.0), (1, 255, 64, 1, "f32", 1.0, 2.0),
+    (2, 256, 256, 4, "bf16", 1.0, 2.0), (1, 256, 64, 2, "f32", 1e-4, 2.0), (1, 256, 64, 2, "bf16", 3e4, 2.0),
+    (1, 200, 64, 1, "f32", 1.0, 0.0), (1, 200, 64, 1, "bf16", 1.0, 40.0), (2, 256, 96, 1, "f32", 1.0, 40.0)])
+def test_mix_1d_direct(cat, monkeypatch, conv, B, N, D, H, dtype, vscale, lscale):
+    """bf16 storage with N <= 256 and d a multiple of 32 takes the direct
+    circulant product on the matrix cores (fp32 storage keeps the FFT path);
+    CAT_CONV=fft forces the FFT path on the same inputs.
+    Cases cover N = 1, lengths around the 16/32 padding steps, N = 256,
+    value scales far from 1, uniform scores (lscale 0) and a near one-hot
+    softmax (lscale 40)."""
+    say("mix_1d_direct", conv, B, N, D, H, dtype, vscale, lscale)
+    import torch
+    if conv == "fft":
+        monkeypatch.setenv("CAT_CONV", "fft")
+    rng = np.random.default_rng(N * 13 + D)
+    logits = (rng.standard_normal((B, H, N)) * lscale).astype(np.float32)
+    V = (rng.standard_normal((B, N, D)) * vscale).astype(np.float32)
+    if dtype == "bf16":
+        V = W.bf16_bits_to_f32(W.round_bf16_bits(V)).reshape(V.shape)
+    plan = cat.cat_plan_create("1d", dtype, B, N, D, H)
+    assert plan.conv_path() == ("direct" if conv == "auto" and dtype == "bf16" else "fft_valu")
+    O = cat.cat_step_mix(plan, torch.from_numpy(logits).cuda(), to_dev(V, dtype))
+    torch.cuda.synchronize()
+    ref = oracle.circulant_1d(oracle.softmax(logits), V)
+    assert_parity(to_np(O), ref, dtype, "O")
+
+
+@pytest.mark.parametrize("N,D,H,dtype,path", [
+    (256, 1024, 16, "bf16", "direct"), (197, 384, 6, "f32", "fft_valu"), (197, 384, 6, "bf16", "direct"),
+    (64, 64, 4, "f32", "fft_valu"), (256, 64, 2, "f32", "fft_valu"),
+    (257, 64, 1, "bf16", "fft_matrix"), (1024, 768, 12, "bf16", "fft_matrix"), (1024, 768, 12, "f32", "fft_valu"),
+    (256, 96, 2, "f32", "fft_valu"), (128, 64, 1, "bf16", "direct")])
+def test_conv_path_choice(cat, N, D, H, dtype, path):
+    """Which circulant-mixing path a 1D plan takes (direct: bf16, N <= 256 and
+    d a multiple of 32; matrix-core FFT: transform length 1024 in bf16)."""
+    say("conv_path", N, D, H, dtype, path)
+    plan = cat.cat_plan_create("1d", dtype, 1, N, D, H)
+    assert plan.conv_path() == path
+
+
 # ------------------------------------------------------------------ 1D forward
 @pytest.mark.parametrize("B,N,D,H,dtype", [(1, 64, 64, 4, "f32"), (2, 37, 48, 3, "f32"), (3, 100, 64, 4, "bf16"),
                                            (1, 1, 32, 2, "f32"), (2, 197, 96, 3, "f32"), (1, 1024, 64, 1, "bf16"),

@@ -73,7 +73,8 @@ def kernel_model(wl, L: int, ngrp: int, fused_spectrum: bool = False, direct: bo
                             flops=2.0 * T * D * 3 * D, unit="mfma_bf16" if s == 2 else "mfma_f32")
         m["scores"] = dict(bytes=2 * T * D * 4 + BH * ngrp * L * 8,
                            flops=lines * (2 * fft_flops(L) + 8.0 * L), unit="valu_f32")
-        m["spectrum"] = dict(bytes=BH * ngrp * L * 8 + spec_bytes,
+        m["psum"] = dict(bytes=BH * ngrp * L * 8 + BH * L * 8, flops=2.0 * BH * (ngrp - 1) * L, unit="valu_f32")
+        m["spectrum"] = dict(bytes=BH * L * 8 + spec_bytes,
                              flops=BH * (2 * fft_flops(L) + 4.0 * N), unit="valu_f32")
     m["fftconv"] = dict(bytes=2 * T * D * s + spec_bytes, flops=lines * (2 * fft_flops(L) + 6.0 * L), unit="valu_f32")
     if fused_spectrum:
@@ -236,7 +237,7 @@ def run(args):
     for k, (ms, n) in ktimes.items():
         log(f"  kernel {k:10s} {ms * 1000:9.2f} us avg over {n} launches")
 
-    ngrp = (wl.d // 2 + 3) // 4
+    ngrp = (wl.d // 2 + 1) // 2  # score partials per (batch, head): pairs in groups of 2
     fused = wl.kind == "1d" and ktimes.get("spectrum", (0.0, 0))[1] == 0
     model = kernel_model(wl, L, ngrp, fused_spectrum=fused, direct=conv_path == "direct")
     kernels = {}

@@ -29,7 +29,7 @@ struct cat_plan_s {
   int Gs;            // lines per spectrum workgroup
   int npair, ngrp, ppg;  // 2D score partials
   float2* d_tw;      // 1D inter-pass twiddles, L entries (null in 2D)
-  size_t off_V, off_z, off_Q, off_K, off_part, off_spec, ws_bytes;
+  size_t off_V, off_z, off_Q, off_K, off_part, off_psum, off_spec, ws_bytes;
   bool debug_sync;
   int tile_n;        // forced GEMM tile width (0: the GEMM chooses)
   int num_cu;        // compute units of the device current at plan creation
@@ -205,7 +205,10 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
   while ((2 * Gs) * T <= 64 && spectrum_lds_bytes(g, 2 * Gs) <= 96 * 1024) Gs *= 2;
   pl->Gs = Gs;
   pl->npair = d2;
-  pl->ppg = 4;
+  // pairs per score workgroup: 2 -- at the 96x96 workload (48 heads x 32
+  // pairs) that is 768 workgroups of one per CU, three even rounds on 256
+  // CUs; with 4 it was 384, and half the CUs ran two
+  pl->ppg = 2;
   pl->ngrp = (d2 + pl->ppg - 1) / pl->ppg;
   const char* ds = std::getenv("CAT_DEBUG_SYNC");
   pl->debug_sync = ds && ds[0] == '1';
@@ -223,7 +226,7 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
   if (p->kind == CAT_1D) {
     pl->off_z = off;
     off = up256(off + BH * p->N * sizeof(float));
-    pl->off_Q = pl->off_K = pl->off_part = 0;
+    pl->off_Q = pl->off_K = pl->off_part = pl->off_psum = 0;
   } else {
     pl->off_z = 0;
     pl->off_Q = off;
@@ -232,6 +235,8 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
     off = up256(off + BND * sizeof(float));
     pl->off_part = off;
     off = up256(off + BH * pl->ngrp * pl->L * sizeof(float2));
+    pl->off_psum = off;
+    off = up256(off + BH * pl->L * sizeof(float2));
   }
   pl->ws_bytes = off;
 
@@ -309,7 +314,7 @@ cat_status cat_plan_set_timing(cat_plan plan, int enable) {
 
 cat_status cat_plan_kernel_times(cat_plan plan, double* total_ms, int64_t* launches, int* nkernels) {
   if (!plan || !total_ms || !launches || !nkernels) return fail(CAT_ERR_INVALID_ARG, "NULL argument");
-  const int nk = plan->p.kind == CAT_1D ? 3 : 4;
+  const int nk = plan->p.kind == CAT_1D ? 3 : 5;
   *nkernels = nk;
   for (int k = 0; k < 8; ++k) {
     total_ms[k] = 0.0;
@@ -501,10 +506,14 @@ cat_status cat_forward_bccb_2d(cat_plan plan, const void* X, const void* W_Q, co
   e = launch_score_partial(plan->geom, sc, s, mk.at(1));
   if (e != hipSuccess) return hip_fail(e, "score launch");
   if ((st = check_sync(plan, "scores")) != CAT_OK) return st;
+  float2* psum = reinterpret_cast<float2*>(ws_at(workspace, plan->off_psum));
+  e = launch_psum(part, psum, sc.BH, plan->ngrp, plan->L, s, mk.at(4));
+  if (e != hipSuccess) return hip_fail(e, "partial-sum launch");
+  if ((st = check_sync(plan, "partial sum")) != CAT_OK) return st;
 
   SpecArgs sa = spec_base(plan, workspace);
-  sa.partial = part;
-  sa.ngrp = plan->ngrp;
+  sa.partial = psum;
+  sa.ngrp = 1;
   sa.scale = 1.0f / std::sqrt((float)plan->d);
   e = launch_spectrum(plan->geom, 1, sa, s, mk.at(2));
   if (e != hipSuccess) return hip_fail(e, "spectrum launch");
@@ -640,9 +649,13 @@ cat_status cat_step_scores_2d(cat_plan plan, const float* Q, const float* K, flo
   e = launch_score_partial(plan->geom, sc, s);
   if (e != hipSuccess) return hip_fail(e, "score launch");
   if ((st = check_sync(plan, "scores")) != CAT_OK) return st;
+  float2* psum = reinterpret_cast<float2*>(ws_at(workspace, plan->off_psum));
+  e = launch_psum(part, psum, sc.BH, plan->ngrp, plan->L, s);
+  if (e != hipSuccess) return hip_fail(e, "partial-sum launch");
+  if ((st = check_sync(plan, "partial sum")) != CAT_OK) return st;
   SpecArgs sa = spec_base(plan, workspace);
-  sa.partial = part;
-  sa.ngrp = plan->ngrp;
+  sa.partial = psum;
+  sa.ngrp = 1;
   sa.scale = 1.0f / std::sqrt((float)plan->d);
   sa.probs = probs;
   e = launch_spectrum(plan->geom, 1, sa, s);

@@ -105,6 +105,39 @@ hipError_t launch_score_partial(const LineGeom& g, const ScoreArgs& a, hipStream
   return launch_k(fn, dim3(a.BH * a.ngrp), dim3(2 * e->T), lds, s, t, a);
 }
 
+namespace {
+
+// Sum of the 2D score partials of each (batch, head): out[bh][k] =
+// sum over g of part[bh][g][k], g in order (the sum the spectrum kernel
+// would otherwise form itself, with far fewer workgroups).  One complex
+// value per thread.
+__global__ __launch_bounds__(256) void psum_kernel(const float2* __restrict__ part, float2* __restrict__ out,
+                                                   int BH, int ngrp, int L) {
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (size_t)BH * L) return;
+  const size_t line = idx / (size_t)L, k = idx - line * (size_t)L;
+  const float2* src = part + line * (size_t)ngrp * L + k;
+  float2 acc = src[0];
+#pragma unroll 4
+  for (int g = 1; g < ngrp; ++g) {
+    const float2 v = src[(size_t)g * L];
+    acc.x += v.x;
+    acc.y += v.y;
+  }
+  out[idx] = acc;
+}
+
+}  // namespace
+
+hipError_t launch_psum(const float2* part, float2* out, int BH, int ngrp, int L, hipStream_t s,
+                       const LaunchTiming* t) {
+  if (BH < 1 || ngrp < 1 || L < 1) return hipErrorInvalidValue;
+  const size_t total = (size_t)BH * L;
+  const size_t blocks = (total + 255) / 256;
+  if (blocks > 0x7fffffffu) return hipErrorInvalidValue;
+  return launch_k(psum_kernel, dim3((unsigned)blocks), dim3(256), 0, s, t, part, out, BH, ngrp, L);
+}
+
 hipError_t launch_relayout(const RelayoutArgs& a, hipStream_t s) {
   const size_t total = (size_t)a.B * a.N * a.D;
   const int blocks = (int)std::min<size_t>((total + 255) / 256, 65536);

@@ -174,6 +174,10 @@ hipError_t launch_mconv(const ConvArgs& a, hipStream_t s, const LaunchTiming* t 
 hipError_t launch_dconv(int et, const ConvArgs& a, hipStream_t s, const LaunchTiming* t = nullptr);
 hipError_t launch_score_partial(const LineGeom& g, const ScoreArgs& a, hipStream_t s,
                                 const LaunchTiming* t = nullptr);
+// 2D: out[bh][k] = sum over g of part[bh][g][k] (partials [BH][ngrp][L],
+// out [BH][L], complex fp32; summed in order g = 0, 1, ..).
+hipError_t launch_psum(const float2* part, float2* out, int BH, int ngrp, int L, hipStream_t s,
+                       const LaunchTiming* t = nullptr);
 hipError_t launch_relayout(const RelayoutArgs& a, hipStream_t s);
 // Raise the dynamic-LDS limit of the kernels a geometry uses (once per plan).
 hipError_t prepare_kernels(const LineGeom& g, size_t conv_lds, size_t spec_lds, size_t score_lds);

@@ -147,12 +147,12 @@ def cat_plan_geometry(plan: Plan):
     return int(L.value), int(L1.value), int(L2.value)
 
 
-CONV_PATHS = {0: "fft_valu", 1: "fft_matrix", 2: "direct"}
+CONV_PATHS = {0: "fft_valu", 1: "fft_matrix", 2: "direct", 3: "fft_multipass"}
 
 
 def cat_plan_conv_path(plan: Plan) -> str:
-    """How the plan evaluates the circulant mixing: "fft_valu", "fft_matrix"
-    or "direct" (include/cat.h, cat_plan_conv_path)."""
+    """How the plan evaluates the circulant mixing: "fft_valu", "fft_matrix",
+    "direct" or "fft_multipass" (include/cat.h, cat_plan_conv_path)."""
     p = ctypes.c_int()
     _check(_lib.cat_plan_conv_path(ctypes.c_void_p(plan.handle), ctypes.byref(p)), "cat_plan_conv_path")
     return CONV_PATHS[int(p.value)]

@@ -25,11 +25,14 @@ struct cat_plan_s {
   int ng;            // line groups per head (d / 2 / G)
   bool mconv;        // 1D conv on the matrix cores (L = 1024, bf16, d % 16 == 0)
   bool direct;       // 1D direct circulant product on the matrix cores (bf16, N <= 256, d % 32 == 0)
+  bool longn;        // 1D power-of-two N beyond one workgroup's line: three passes over HBM
+  int logL1, logL2;  // long path: L = 2^logL1 x 2^logL2
   int cg;            // channels per group of the blocked V (2 G; 16 for mconv, 32 for direct)
   int Gs;            // lines per spectrum workgroup
   int npair, ngrp, ppg;  // 2D score partials
   float2* d_tw;      // 1D inter-pass twiddles, L entries (null in 2D)
   size_t off_V, off_z, off_Q, off_K, off_part, off_psum, off_spec, ws_bytes;
+  size_t off_A, off_zc, off_Az;  // long path scratch
   bool debug_sync;
   int tile_n;        // forced GEMM tile width (0: the GEMM chooses)
   int num_cu;        // compute units of the device current at plan creation
@@ -152,7 +155,15 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
     return fail(CAT_ERR_UNSUPPORTED, "1D supports at most 32 heads (score projection fused into the GEMM)");
 
   LineGeom g{};
-  if (p->kind == CAT_1D) {
+  const bool longn = p->kind == CAT_1D && is_pow2(p->N) && p->N > 4096 && p->N <= 65536;
+  if (longn) {
+    // three passes over HBM, L = N = L1 x L2 (L1 >= L2)
+    int e = 0;
+    while ((int64_t(1) << e) < p->N) ++e;
+    g.L1 = 1 << ((e + 1) / 2);
+    g.L2 = 1 << (e / 2);
+    g.twiddled = 1;
+  } else if (p->kind == CAT_1D) {
     int L = 0;
     if (is_pow2(p->N) && p->N <= 4096) {
       L = (int)p->N;
@@ -160,7 +171,8 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
       L = 1;
       while (L < 2 * p->N - 1) L <<= 1;
     } else {
-      return fail(CAT_ERR_UNSUPPORTED, "1D N beyond the single-workgroup transform (pow2 <= 4096, other <= 2048)");
+      return fail(CAT_ERR_UNSUPPORTED,
+                  "1D N beyond the supported lengths (powers of two up to 65536, other N up to 2048)");
     }
     split_pow2(L, &g.L1, &g.L2);
     g.twiddled = 1;
@@ -171,7 +183,7 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
     g.L2 = (int)p->Wg;
     g.twiddled = 0;
   }
-  if (!geom_supported(g)) return fail(CAT_ERR_UNSUPPORTED, "transform length / grid not instantiated");
+  if (!longn && !geom_supported(g)) return fail(CAT_ERR_UNSUPPORTED, "transform length / grid not instantiated");
 
   cat_plan_s* pl = new (std::nothrow) cat_plan_s();
   if (!pl) return fail(CAT_ERR_ALLOC, "host allocation failed");
@@ -181,8 +193,12 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
   pl->esz = p->dtype == CAT_F32 ? 4 : 2;
   pl->geom = g;
   pl->L = g.L1 * g.L2;
-  const int T = line_threads(g);
-  const size_t line_bytes = line_lds_bytes(g);
+  pl->longn = longn;
+  pl->logL1 = pl->logL2 = 0;
+  while ((1 << pl->logL1) < g.L1) ++pl->logL1;
+  while ((1 << pl->logL2) < g.L2) ++pl->logL2;
+  const int T = longn ? 1 : line_threads(g);
+  const size_t line_bytes = longn ? 0 : line_lds_bytes(g);
   const int d2 = (int)d / 2;
   // lines per transform workgroup: power of two dividing d/2, <= 256 threads
   int G = 1;
@@ -195,8 +211,11 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
     const bool force_valu = cv && std::strcmp(cv, "valu") == 0;
     const bool force_fft = force_valu || (cv && std::strcmp(cv, "fft") == 0);
     pl->direct = !force_fft && p->kind == CAT_1D && p->dtype == CAT_BF16 && p->N <= 256 && d % 32 == 0;
-    pl->mconv = !pl->direct && !force_valu && p->kind == CAT_1D && p->dtype == CAT_BF16 &&
+    pl->mconv = !longn && !pl->direct && !force_valu && p->kind == CAT_1D && p->dtype == CAT_BF16 &&
                 g.L1 * g.L2 == 1024 && d % 16 == 0;
+    if (longn) G = 1;
+    pl->G = G;
+    pl->ng = d2 / G;
     pl->cg = pl->direct ? 32 : pl->mconv ? 16 : 2 * G;
     if (pl->mconv) pl->ng = (int)d / 16;
     if (pl->direct) pl->ng = (int)d / 32;
@@ -223,10 +242,19 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
   off = up256(off + BND * pl->esz);
   pl->off_spec = off;
   off = up256(off + BH * pl->L * sizeof(float2));
+  pl->off_A = pl->off_zc = pl->off_Az = 0;
   if (p->kind == CAT_1D) {
     pl->off_z = off;
     off = up256(off + BH * p->N * sizeof(float));
     pl->off_Q = pl->off_K = pl->off_part = pl->off_psum = 0;
+    if (longn) {
+      pl->off_A = off;
+      off = up256(off + BH * (size_t)d2 * pl->L * sizeof(float2));
+      pl->off_zc = off;
+      off = up256(off + BH * pl->L * sizeof(float2));
+      pl->off_Az = off;
+      off = up256(off + BH * pl->L * sizeof(float2));
+    }
   } else {
     pl->off_z = 0;
     pl->off_Q = off;
@@ -251,12 +279,20 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
   if (g.twiddled) {
     std::vector<float2> tw((size_t)pl->L);
     const double two_pi = 6.283185307179586476925286766559;
-    for (int n2 = 0; n2 < g.L2; ++n2)
-      for (int k1 = 0; k1 < g.L1; ++k1) {
-        const long e = ((long)n2 * k1) % pl->L;
-        const double ang = two_pi * (double)e / (double)pl->L;
-        tw[(size_t)k1 * g.L2 + n2] = make_float2((float)std::cos(ang), (float)(-std::sin(ang)));
+    if (longn) {
+      // long path: W_L^m for every m < L
+      for (int m = 0; m < pl->L; ++m) {
+        const double ang = two_pi * (double)m / (double)pl->L;
+        tw[(size_t)m] = make_float2((float)std::cos(ang), (float)(-std::sin(ang)));
       }
+    } else {
+      for (int n2 = 0; n2 < g.L2; ++n2)
+        for (int k1 = 0; k1 < g.L1; ++k1) {
+          const long e = ((long)n2 * k1) % pl->L;
+          const double ang = two_pi * (double)e / (double)pl->L;
+          tw[(size_t)k1 * g.L2 + n2] = make_float2((float)std::cos(ang), (float)(-std::sin(ang)));
+        }
+    }
     hipError_t e = hipMalloc(&pl->d_tw, tw.size() * sizeof(float2));
     if (e != hipSuccess) {
       delete pl;
@@ -269,7 +305,7 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
       return hip_fail(e, "hipMemcpy(twiddles)");
     }
   }
-  hipError_t e = prepare_kernels(g, (size_t)G * line_bytes, spectrum_lds_bytes(g, Gs), 2 * line_bytes);
+  hipError_t e = longn ? hipSuccess : prepare_kernels(g, (size_t)G * line_bytes, spectrum_lds_bytes(g, Gs), 2 * line_bytes);
   if (e != hipSuccess) {
     if (pl->d_tw) (void)hipFree(pl->d_tw);
     delete pl;
@@ -346,7 +382,10 @@ cat_status cat_plan_workspace_size(cat_plan plan, size_t* bytes) {
 
 cat_status cat_plan_conv_path(cat_plan plan, int* path) {
   if (!plan || !path) return fail(CAT_ERR_INVALID_ARG, "NULL argument");
-  *path = plan->direct ? CAT_PATH_DIRECT : plan->mconv ? CAT_PATH_FFT_MATRIX : CAT_PATH_FFT_VALU;
+  *path = plan->longn ? CAT_PATH_FFT_MULTIPASS
+         : plan->direct ? CAT_PATH_DIRECT
+         : plan->mconv  ? CAT_PATH_FFT_MATRIX
+                        : CAT_PATH_FFT_VALU;
   return CAT_OK;
 }
 
@@ -421,6 +460,34 @@ ConvArgs conv_base(const cat_plan_s* pl, const void* Vblk, const float2* spec, v
   return a;
 }
 
+LongArgs long_base(const cat_plan_s* pl) {
+  LongArgs a{};
+  a.tw = pl->d_tw;
+  a.logL1 = pl->logL1;
+  a.logL2 = pl->logL2;
+  a.BH = (int)(pl->p.B * pl->p.H);
+  a.pairs = pl->d / 2;
+  a.H = (int)pl->p.H;
+  a.D = (int)pl->p.D;
+  a.d = pl->d;
+  return a;
+}
+
+// The long-sequence mixing (three passes): softmax line and filter spectrum
+// (timing slot 1), then the values (slot 2).
+hipError_t run_long_1d(const cat_plan_s* pl, const float* logits, const void* Vb, void* O, void* ws, hipStream_t s,
+                       KernelMark* mk) {
+  const LaunchTiming* ts[6] = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+  if (mk) {
+    for (int i = 0; i < 3; ++i) ts[i] = mk->at(1);
+    for (int i = 3; i < 6; ++i) ts[i] = mk->at(2);
+  }
+  return launch_longconv(pl->et, long_base(pl), logits, Vb, reinterpret_cast<float2*>(ws_at(ws, pl->off_zc)),
+                         reinterpret_cast<float2*>(ws_at(ws, pl->off_Az)),
+                         reinterpret_cast<float2*>(ws_at(ws, pl->off_spec)),
+                         reinterpret_cast<float2*>(ws_at(ws, pl->off_A)), O, s, ts);
+}
+
 // The 1D conv: on the matrix cores where the plan chose that path.
 hipError_t run_conv_1d(const cat_plan_s* pl, const ConvArgs& ca, hipStream_t s, const LaunchTiming* t = nullptr) {
   if (pl->direct) return launch_dconv(pl->et, ca, s, t);
@@ -453,6 +520,12 @@ cat_status cat_forward_1d(cat_plan plan, const void* X, const void* W_A, const v
   hipError_t e = launch_gemm(plan->et, ga, s, mk.at(0));
   if (e != hipSuccess) return hip_fail(e, "projection launch");
   if ((st = check_sync(plan, "projection")) != CAT_OK) return st;
+
+  if (plan->longn) {
+    e = run_long_1d(plan, z, Vb, O, workspace, s, &mk);
+    if (e != hipSuccess) return hip_fail(e, "long-sequence fft-conv launch");
+    return check_sync(plan, "long-sequence fft-conv");
+  }
 
   SpecArgs sa = spec_base(plan, workspace);
   sa.logits = z;
@@ -559,6 +632,7 @@ cat_status cat_step_spectrum(cat_plan plan, const float* logits, float* probs, f
   cat_status st = check_ptrs({logits, spec});
   if (st != CAT_OK) return st;
   if (probs && !aligned16(probs)) return fail(CAT_ERR_INVALID_ARG, "probs not 16-byte aligned");
+  if (plan->longn) return fail(CAT_ERR_UNSUPPORTED, "the spectrum step covers single-workgroup lines (N <= 4096)");
   SpecArgs a{};
   a.logits = logits;
   a.probs = probs;
@@ -594,6 +668,11 @@ cat_status cat_step_mix(cat_plan plan, const float* logits, const void* V, void*
   ra.cg = plan->cg;
   hipError_t e = launch_relayout(ra, s);
   if (e != hipSuccess) return hip_fail(e, "relayout launch");
+  if (plan->longn) {
+    e = run_long_1d(plan, logits, Vb, O, workspace, s, nullptr);
+    if (e != hipSuccess) return hip_fail(e, "long-sequence fft-conv launch");
+    return check_sync(plan, "long-sequence fft-conv");
+  }
   SpecArgs sa = spec_base(plan, workspace);
   sa.logits = logits;
   const bool own_softmax = plan->mconv || plan->direct;

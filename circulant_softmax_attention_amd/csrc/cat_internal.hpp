@@ -174,6 +174,22 @@ hipError_t launch_mconv(const ConvArgs& a, hipStream_t s, const LaunchTiming* t 
 hipError_t launch_dconv(int et, const ConvArgs& a, hipStream_t s, const LaunchTiming* t = nullptr);
 hipError_t launch_score_partial(const LineGeom& g, const ScoreArgs& a, hipStream_t s,
                                 const LaunchTiming* t = nullptr);
+// 1D mixing for power-of-two N = L1 L2 beyond one workgroup's line
+// (three passes over HBM; see cat_longconv.hip).
+struct LongArgs {
+  const float2* tw;  // W_L^m, m < L (L = N)
+  int logL1, logL2;  // L1 = 2^logL1 (column DFTs), L2 = 2^logL2 (row DFTs)
+  int BH, pairs;     // (batch, head) lines and channel pairs per head (d / 2)
+  int H, D, d;
+  int cb, rb;        // filled by the launcher: columns / rows per workgroup
+};
+// Launches, in order: softmax line, column pass and row pass of the filter
+// spectrum (zc, Az: [BH][L] complex fp32 scratch; S: [BH][L] spectrum), then
+// column pass, row pass with the spectrum product, inverse column pass of
+// the values (V BLOCKED with 2-channel groups, A: [BH d/2][L] complex fp32
+// scratch, O [B][N][D]).  t: six timing slots or null.
+hipError_t launch_longconv(int et, const LongArgs& a, const float* logits, const void* V, float2* zc, float2* Az,
+                           float2* S, float2* A, void* O, hipStream_t s, const LaunchTiming* const* t = nullptr);
 // 2D: out[bh][k] = sum over g of part[bh][g][k] (partials [BH][ngrp][L],
 // out [BH][L], complex fp32; summed in order g = 0, 1, ..).
 hipError_t launch_psum(const float2* part, float2* out, int BH, int ngrp, int L, hipStream_t s,

@@ -1,0 +1,238 @@
+// cat_longconv.hip -- the 1D circulant mixing for sequences longer than one
+// workgroup's transform line (power-of-two N, 4096 < N <= 65536).
+//
+// CAT evaluates O_h = circ(z*_h) V_h as IFFT(FFT(z*_h) . FFT(V_h)) along the
+// tokens (CAT: Circular-Convolutional Attention for Sub-Quadratic
+// Transformers, "Key designs: FFT-accelerated computation"); the page names
+// sequences beyond 10^4 tokens as where that O(N log N) route should pay.
+// A length L = L1 L2 transform does not fit one workgroup here, so it runs
+// as three passes over HBM (four-step FFT), with L = N:
+//
+//   column pass   for each n2: A[k1][n2] = W_L^(k1 n2) sum_n1 x[n1 L2 + n2] W_L1^(n1 k1)
+//   row pass      for each k1: X[k1 + L1 k2] = sum_n2 A[k1][n2] W_L2^(n2 k2);
+//                 times S[k1 + L1 k2] (the filter spectrum over L), then the
+//                 inverse over k2 back to B[k1][n2]
+//   inverse column pass  for each n2: o[n1 L2 + n2] = sum_k1 B[k1][n2] conj W_L^(k1 n2) conj W_L1^(n1 k1)
+//
+// The filter spectrum is the column pass and the forward half of the row
+// pass applied to the softmax line, scaled by 1/L.  Each short DFT runs as a
+// radix-2 Stockham transform in LDS (natural order in and out), several
+// lines per workgroup; all twiddles come from one table W_L^m, m < L,
+// computed in double precision on the host.  Two real channels ride in one
+// complex line, as in the single-workgroup convolution.
+//
+// Layouts: V is BLOCKED with 2-channel groups ([BH][d/2][N][2], one complex
+// line per channel pair); the intermediate A is [lines][L1][L2] complex
+// fp32; the spectrum S is [BH][L1][L2] complex fp32 (entry k1 L2 + k2 holds
+// frequency k1 + L1 k2).
+#include "cat_common.hpp"
+#include "cat_internal.hpp"
+
+namespace cat {
+
+namespace {
+
+constexpr int LTHR = 256;
+constexpr int LBUF = 2048;  // complex values of the lines one workgroup transforms
+constexpr int LPAD = LBUF + 64;  // LDS buffer size: lines at pitch M + 1 (at most 64 lines)
+
+__device__ __forceinline__ float2 cmul2(float2 a, float2 b) {
+  return make_float2(fmaf(a.x, b.x, -a.y * b.y), fmaf(a.x, b.y, a.y * b.x));
+}
+__device__ __forceinline__ float2 conj2(float2 a) { return make_float2(a.x, -a.y); }
+
+// R independent lines of M points (M a power of two) at a[r (M + 1) + i]
+// (the odd pitch keeps column-wise accesses off a single bank), natural
+// order in and out, unscaled; b is the ping-pong buffer.  Returns the buffer
+// holding the result.  Ends with a barrier.
+template <bool INV>
+__device__ float2* lds_fft(float2* a, float2* b, int M, int logM, int R, const float2* __restrict__ tw, int logL) {
+  const int P = M + 1;
+  const int half = M >> 1;
+  for (int s = 0; s < logM; ++s) {
+    const int Ns = 1 << s;
+    __syncthreads();
+    for (int q = threadIdx.x; q < R * half; q += LTHR) {
+      const int r = q >> (logM - 1), j = q & (half - 1);
+      const int k = j & (Ns - 1);
+      const float2 v0 = a[r * P + j];
+      float2 w = tw[k << (logL - 1 - s)];  // W_(2 Ns)^k = W_L^(k L / (2 Ns))
+      if (INV) w = conj2(w);
+      const float2 v1 = cmul2(a[r * P + j + half], w);
+      const int d = ((j >> s) << (s + 1)) + k;
+      b[r * P + d] = make_float2(v0.x + v1.x, v0.y + v1.y);
+      b[r * P + d + Ns] = make_float2(v0.x - v1.x, v0.y - v1.y);
+    }
+    float2* t = a;
+    a = b;
+    b = t;
+  }
+  __syncthreads();
+  return a;
+}
+
+template <int ET>
+__device__ __forceinline__ float2 load_c(const void* base, size_t i) {
+  if constexpr (ET == ET_F32) {
+    return reinterpret_cast<const float2*>(base)[i];
+  } else {
+    const uint32_t u = reinterpret_cast<const uint32_t*>(base)[i];
+    return make_float2(bf16lo(u), bf16hi(u));
+  }
+}
+
+// ---- softmax of one (b, h) logit line, as a complex line (imaginary 0)
+__global__ __launch_bounds__(LTHR) void softmax_line_kernel(const float* __restrict__ z, float2* __restrict__ zc,
+                                                            int N) {
+  __shared__ float red[LTHR / 64];
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  const float* zr = z + (size_t)bh * N;
+  auto reduce = [&](float v, bool is_max) {
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float p = __shfl_xor(v, o, 64);
+      v = is_max ? fmaxf(v, p) : v + p;
+    }
+    __syncthreads();
+    if ((tid & 63) == 0) red[tid >> 6] = v;
+    __syncthreads();
+    float r = red[0];
+    for (int w = 1; w < LTHR / 64; ++w) r = is_max ? fmaxf(r, red[w]) : r + red[w];
+    return r;
+  };
+  float m = -INFINITY;
+  for (int n = tid; n < N; n += LTHR) m = fmaxf(m, zr[n]);
+  m = reduce(m, true);
+  float s = 0.f;
+  for (int n = tid; n < N; n += LTHR) s += __expf(zr[n] - m);
+  s = reduce(s, false);
+  const float inv = 1.f / s;
+  float2* out = zc + (size_t)bh * N;
+  for (int n = tid; n < N; n += LTHR) out[n] = make_float2(__expf(zr[n] - m) * inv, 0.f);
+}
+
+// ---- column pass: line `line` of src (complex values, element type SET:
+// ET_F32 float2 or ET_BF16 bf16 pairs), CB adjacent columns n2 per
+// workgroup: A[line][k1 L2 + n2] = W_L^(k1 n2) DFT_L1 over n1.
+template <int SET>
+__global__ __launch_bounds__(LTHR) void col_fwd_kernel(LongArgs a, const void* __restrict__ src, float2* __restrict__ A) {
+  __shared__ float2 buf[2][LPAD];
+  const int L1 = 1 << a.logL1, L2 = 1 << a.logL2, L = L1 * L2, CB = a.cb;
+  const int nblk = L2 / CB;
+  const int line = blockIdx.x / nblk, n20 = (blockIdx.x - line * nblk) * CB;
+  const size_t lbase = (size_t)line * L;
+  // buf[0][c L1 + n1] = x[n1 L2 + n20 + c]; consecutive threads take consecutive c
+  for (int q = threadIdx.x; q < CB * L1; q += LTHR) {
+    const int n1 = q / CB, c = q - n1 * CB;
+    buf[0][c * (L1 + 1) + n1] = load_c<SET>(src, lbase + (size_t)n1 * L2 + n20 + c);
+  }
+  const float2* U = lds_fft<false>(buf[0], buf[1], L1, a.logL1, CB, a.tw, a.logL1 + a.logL2);
+  for (int q = threadIdx.x; q < CB * L1; q += LTHR) {
+    const int k1 = q / CB, c = q - k1 * CB;
+    const int n2 = n20 + c;
+    const float2 w = a.tw[(k1 * n2) & (L - 1)];
+    A[lbase + (size_t)k1 * L2 + n2] = cmul2(U[c * (L1 + 1) + k1], w);
+  }
+}
+
+// ---- row pass, RB rows k1 per workgroup.  MODE 0 (spectrum): S = DFT_L2 / L
+// of the rows of Az.  MODE 1 (mixing): A = IDFT_L2(DFT_L2(A) . S[bh]) in
+// place, bh = line / pairs.
+template <int MODE>
+__global__ __launch_bounds__(LTHR) void row_kernel(LongArgs a, float2* __restrict__ A, float2* __restrict__ S) {
+  __shared__ float2 buf[2][LPAD];
+  const int L1 = 1 << a.logL1, L2 = 1 << a.logL2, L = L1 * L2, RB = a.rb;
+  const int nblk = L1 / RB;
+  const int line = blockIdx.x / nblk, k10 = (blockIdx.x - line * nblk) * RB;
+  const size_t base = (size_t)line * L + (size_t)k10 * L2;  // RB contiguous rows
+  const int P2 = L2 + 1;
+  for (int q = threadIdx.x; q < RB * L2; q += LTHR) buf[0][(q >> a.logL2) * P2 + (q & (L2 - 1))] = A[base + q];
+  const int logL = a.logL1 + a.logL2;
+  float2* X = lds_fft<false>(buf[0], buf[1], L2, a.logL2, RB, a.tw, logL);
+  float2* Y = X == buf[0] ? buf[1] : buf[0];
+  if constexpr (MODE == 0) {
+    const float sc = 1.f / (float)L;
+    for (int q = threadIdx.x; q < RB * L2; q += LTHR) {
+      const float2 v = X[(q >> a.logL2) * P2 + (q & (L2 - 1))];
+      S[base + q] = make_float2(v.x * sc, v.y * sc);
+    }
+  } else {
+    const size_t sbase = (size_t)(line / a.pairs) * L + (size_t)k10 * L2;
+    for (int q = threadIdx.x; q < RB * L2; q += LTHR) {
+      const int i = (q >> a.logL2) * P2 + (q & (L2 - 1));
+      X[i] = cmul2(X[i], S[sbase + q]);
+    }
+    const float2* Bv = lds_fft<true>(X, Y, L2, a.logL2, RB, a.tw, logL);
+    for (int q = threadIdx.x; q < RB * L2; q += LTHR) A[base + q] = Bv[(q >> a.logL2) * P2 + (q & (L2 - 1))];
+  }
+}
+
+// ---- inverse column pass: o[n1 L2 + n2] = IDFT_L1 over k1 of
+// B[k1][n2] conj W_L^(k1 n2), written to O[b][n][h d + 2 p ..] (storage
+// element type DET), line = bh * pairs + p.
+template <int DET>
+__global__ __launch_bounds__(LTHR) void col_inv_kernel(LongArgs a, const float2* __restrict__ A, void* __restrict__ O) {
+  __shared__ float2 buf[2][LPAD];
+  const int L1 = 1 << a.logL1, L2 = 1 << a.logL2, L = L1 * L2, CB = a.cb;
+  const int nblk = L2 / CB;
+  const int line = blockIdx.x / nblk, n20 = (blockIdx.x - line * nblk) * CB;
+  const size_t lbase = (size_t)line * L;
+  for (int q = threadIdx.x; q < CB * L1; q += LTHR) {
+    const int k1 = q / CB, c = q - k1 * CB;
+    const int n2 = n20 + c;
+    buf[0][c * (L1 + 1) + k1] = cmul2(A[lbase + (size_t)k1 * L2 + n2], conj2(a.tw[(k1 * n2) & (L - 1)]));
+  }
+  const float2* U = lds_fft<true>(buf[0], buf[1], L1, a.logL1, CB, a.tw, a.logL1 + a.logL2);
+  const int bh = line / a.pairs, p = line - bh * a.pairs;
+  const int b = bh / a.H, h = bh - b * a.H;
+  const size_t obase = (size_t)b * L * a.D + (size_t)h * a.d + 2 * (size_t)p;
+  for (int q = threadIdx.x; q < CB * L1; q += LTHR) {
+    const int n1 = q / CB, c = q - n1 * CB;
+    const size_t n = (size_t)n1 * L2 + n20 + c;
+    const float2 v = U[c * (L1 + 1) + n1];
+    if constexpr (DET == ET_F32) {
+      *reinterpret_cast<float2*>(reinterpret_cast<float*>(O) + obase + n * a.D) = v;
+    } else {
+      *reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(O) + obase + n * a.D) = pack_bf16x2(v.x, v.y);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_longconv(int et, const LongArgs& a0, const float* logits, const void* V, float2* zc, float2* Az,
+                           float2* S, float2* A, void* O, hipStream_t s, const LaunchTiming* const* t) {
+  const LaunchTiming* none[6] = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+  if (!t) t = none;
+  LongArgs a = a0;
+  const int L1 = 1 << a.logL1, L2 = 1 << a.logL2;
+  if (a.logL1 < 1 || a.logL2 < 1 || L1 > LBUF || L2 > LBUF || a.pairs < 1 || a.BH < 1) return hipErrorInvalidValue;
+  a.cb = LBUF / L1 < L2 ? LBUF / L1 : L2;  // adjacent columns per workgroup
+  a.rb = LBUF / L2 < L1 ? LBUF / L2 : L1;  // rows per workgroup
+  if (a.cb > 64) a.cb = 64;
+  if (a.rb > 64) a.rb = 64;
+  const int N = L1 * L2;
+  const long lines = (long)a.BH * a.pairs;
+  const long colb_z = (long)a.BH * (L2 / a.cb), rowb_z = (long)a.BH * (L1 / a.rb);
+  const long colb = lines * (L2 / a.cb), rowb = lines * (L1 / a.rb);
+  if (colb > 0x7fffffffL || rowb > 0x7fffffffL) return hipErrorInvalidValue;
+  // the filter spectrum
+  hipError_t e = launch_k(softmax_line_kernel, dim3(a.BH), dim3(LTHR), 0, s, t[0], logits, zc, N);
+  if (e != hipSuccess) return e;
+  e = launch_k(col_fwd_kernel<ET_F32>, dim3((unsigned)colb_z), dim3(LTHR), 0, s, t[1], a, (const void*)zc, Az);
+  if (e != hipSuccess) return e;
+  e = launch_k(row_kernel<0>, dim3((unsigned)rowb_z), dim3(LTHR), 0, s, t[2], a, Az, S);
+  if (e != hipSuccess) return e;
+  // the mixing
+  if (et == ET_F32)
+    e = launch_k(col_fwd_kernel<ET_F32>, dim3((unsigned)colb), dim3(LTHR), 0, s, t[3], a, V, A);
+  else
+    e = launch_k(col_fwd_kernel<ET_BF16>, dim3((unsigned)colb), dim3(LTHR), 0, s, t[3], a, V, A);
+  if (e != hipSuccess) return e;
+  e = launch_k(row_kernel<1>, dim3((unsigned)rowb), dim3(LTHR), 0, s, t[4], a, A, S);
+  if (e != hipSuccess) return e;
+  if (et == ET_F32)
+    return launch_k(col_inv_kernel<ET_F32>, dim3((unsigned)colb), dim3(LTHR), 0, s, t[5], a, (const float2*)A, O);
+  return launch_k(col_inv_kernel<ET_BF16>, dim3((unsigned)colb), dim3(LTHR), 0, s, t[5], a, (const float2*)A, O);
+}
+
+}  // namespace cat

@@ -91,10 +91,11 @@ typedef enum { CAT_1D = 0, CAT_BCCB_2D = 1 } cat_kind;
  * Requirements: B >= 0 (B = 0 makes every forward call a no-op), N, D,
  * H >= 1; D % H == 0; d = D / H even; D % 8 == 0; B * N * D < 2^31.
  * Supported sizes (else CAT_ERR_UNSUPPORTED):
- *   1D: H <= 32; N a power of two up to 4096, or any other N up to 2048 (the circular
- *       convolution of length N is evaluated exactly on a power-of-two circle
- *       of length L >= 2N - 1, the values zero-extended and the softmaxed
- *       scores periodically extended);
+ *   1D: H <= 32; N a power of two up to 65536 (beyond 4096 by three passes
+ *       over HBM, see cat_plan_conv_path), or any other N up to 2048 (the
+ *       circular convolution of length N is evaluated exactly on a
+ *       power-of-two circle of length L >= 2N - 1, the values zero-extended
+ *       and the softmaxed scores periodically extended);
  *   2D: grids 1x1, 2x3, 3x4, 4x4, 6x8, 8x8, 12x12, 16x16, 32x32, 96x96. */
 typedef struct {
   int32_t kind;  /* cat_kind */
@@ -130,12 +131,18 @@ cat_status cat_plan_geometry(cat_plan plan, int64_t* L, int64_t* L1, int64_t* L2
  *                           cores, softmax in the same launch (CAT, "Key
  *                           designs: circulant attention matrix
  *                           construction").
+ *   CAT_PATH_FFT_MULTIPASS (3) 1D, power-of-two N in (4096, 65536]: the
+ *                           transform does not fit one workgroup; column,
+ *                           row and inverse column passes over HBM (CAT,
+ *                           "Key designs: FFT-accelerated computation";
+ *                           the page names N > 10^4 as where it should pay).
  * The environment variable CAT_CONV=fft (at plan creation) excludes path 2,
  * CAT_CONV=valu paths 1 and 2.  Errors: CAT_ERR_INVALID_ARG for a NULL plan
  * or NULL path. */
 #define CAT_PATH_FFT_VALU 0
 #define CAT_PATH_FFT_MATRIX 1
 #define CAT_PATH_DIRECT 2
+#define CAT_PATH_FFT_MULTIPASS 3
 cat_status cat_plan_conv_path(cat_plan plan, int* path);
 
 /* CAT 1D forward (see top of file).  X [B][N][D], W_A [D][H], W_V [D][D],

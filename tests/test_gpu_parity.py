@@ -209,13 +209,60 @@ def test_mix_1d_direct(cat, monkeypatch, conv, B, N, D, H, dtype, vscale, lscale
     (256, 1024, 16, "bf16", "direct"), (197, 384, 6, "f32", "fft_valu"), (197, 384, 6, "bf16", "direct"),
     (64, 64, 4, "f32", "fft_valu"), (256, 64, 2, "f32", "fft_valu"),
     (257, 64, 1, "bf16", "fft_matrix"), (1024, 768, 12, "bf16", "fft_matrix"), (1024, 768, 12, "f32", "fft_valu"),
-    (256, 96, 2, "f32", "fft_valu"), (128, 64, 1, "bf16", "direct")])
+    (256, 96, 2, "f32", "fft_valu"), (128, 64, 1, "bf16", "direct"), (8192, 64, 2, "bf16", "fft_multipass"),
+    (65536, 16, 1, "f32", "fft_multipass")])
 def test_conv_path_choice(cat, N, D, H, dtype, path):
     """Which circulant-mixing path a 1D plan takes (direct: bf16, N <= 256 and
     d a multiple of 32; matrix-core FFT: transform length 1024 in bf16)."""
     say("conv_path", N, D, H, dtype, path)
     plan = cat.cat_plan_create("1d", dtype, 1, N, D, H)
     assert plan.conv_path() == path
+
+
+@pytest.mark.parametrize("B,N,D,H,dtype,lscale", [
+    (1, 8192, 8, 2, "f32", 2.0), (1, 8192, 8, 2, "bf16", 2.0), (2, 16384, 24, 3, "f32", 3.0),
+    (1, 16384, 8, 1, "f32", 0.0), (1, 16384, 8, 1, "bf16", 40.0), (1, 32768, 8, 1, "f32", 2.0),
+    (1, 65536, 8, 2, "f32", 2.0), (1, 65536, 8, 1, "bf16", 2.0)])
+def test_mix_1d_long(cat, B, N, D, H, dtype, lscale):
+    """Power-of-two N beyond one workgroup's line: column, row and inverse
+    column passes over HBM.  Cases span N = 2^13 .. 2^16 (square and 2:1
+    splits), uniform scores (lscale 0) and a near one-hot softmax (lscale
+    40); beyond 16384 x 16384 x 24 multiply-adds the oracle checks 1024
+    sampled rows."""
+    say("mix_1d_long", B, N, D, H, dtype, lscale)
+    import torch
+    rng = np.random.default_rng(N + 5 * D)
+    logits = (rng.standard_normal((B, H, N)) * lscale).astype(np.float32)
+    V = rng.standard_normal((B, N, D)).astype(np.float32)
+    if dtype == "bf16":
+        V = W.bf16_bits_to_f32(W.round_bf16_bits(V)).reshape(V.shape)
+    plan = cat.cat_plan_create("1d", dtype, B, N, D, H)
+    assert plan.conv_path() == "fft_multipass"
+    O = to_np(cat.cat_step_mix(plan, torch.from_numpy(logits).cuda(), to_dev(V, dtype)))
+    zs = oracle.softmax(logits)
+    if N * N * D * B <= 16384 * 16384 * 24:
+        assert_parity(O, oracle.circulant_1d(zs, V), dtype, "O")
+    else:
+        rows = np.unique(np.random.default_rng(1).integers(0, B * N, 1024))
+        ref = oracle.circulant_1d(zs, V, rows=rows)
+        assert_parity(O.reshape(B * N, D)[rows], ref, dtype, "O rows")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_forward_1d_long(cat, dtype):
+    """The whole 1D path at N = 16384 (projection, then the three-pass
+    mixing), on 512 sampled rows."""
+    B, N, D, H = 1, 16384, 64, 2
+    say("forward_1d_long", B, N, D, H, dtype)
+    import torch
+    inp = rng_inputs(23, B, N, D, H, dtype)
+    plan = cat.cat_plan_create("1d", dtype, B, N, D, H)
+    assert plan.conv_path() == "fft_multipass"
+    O = cat.cat_forward_1d(plan, to_dev(inp.X, dtype), to_dev(inp.W_A, dtype), to_dev(inp.W_V, dtype))
+    torch.cuda.synchronize()
+    rows = np.unique(np.random.default_rng(2).integers(0, B * N, 512))
+    ref = oracle.cat_forward_1d(inp.X, inp.W_A, inp.W_V, rows=rows)["O"]
+    assert_parity(to_np(O).reshape(B * N, D)[rows], ref, dtype, "O rows")
 
 
 # ------------------------------------------------------------------ 1D forward

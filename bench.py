@@ -44,7 +44,8 @@ def fft_flops(L: int) -> float:
     return 5.0 * L * math.log2(L) if L > 1 else 0.0
 
 
-def kernel_model(wl, L: int, ngrp: int, fused_spectrum: bool = False, direct: bool = False):
+def kernel_model(wl, L: int, ngrp: int, fused_spectrum: bool = False, direct: bool = False,
+                 multipass: bool = False):
     """Algorithmic bytes and flops of each kernel of one forward call.
 
     fused_spectrum: the 1D conv ran on the matrix cores and computed the
@@ -55,7 +56,12 @@ def kernel_model(wl, L: int, ngrp: int, fused_spectrum: bool = False, direct: bo
 
     direct: the 1D mixing ran as the direct product circ(z*) V on the matrix
     cores ("directconv", softmax included): it reads V and the logits and
-    writes O; its flops are the product's 2 N^2 d per (batch, head)."""
+    writes O; its flops are the product's 2 N^2 d per (batch, head).
+
+    multipass: the 1D mixing ran as three passes over HBM (three launches
+    each for the spectrum and for the values).  The bytes are the algorithmic
+    ones (V read, O written, spectrum read; logits read, spectrum written),
+    not the passes' intermediates, so hbm_frac shows what the passes cost."""
     s = 4 if wl.dtype == "f32" else 2
     B, N, D, H, d = wl.B, wl.N, wl.D, wl.H, wl.d
     T = B * N
@@ -81,6 +87,10 @@ def kernel_model(wl, L: int, ngrp: int, fused_spectrum: bool = False, direct: bo
         cplx = 4 * 2.0 * 32 ** 3  # one 32x32x32 complex product in real flops
         m["fftconv"] = dict(bytes=2 * T * D * s + BH * N * 4, flops=lines * 4 * cplx + B * H * (d // 16) * 2 * cplx,
                             unit="mfma_f16")
+    if multipass:
+        m["spectrum"] = dict(bytes=BH * N * 4 + spec_bytes, flops=BH * fft_flops(L), unit="valu_f32")
+        m["fftconv"] = dict(bytes=2 * T * D * s + spec_bytes, flops=lines * (2 * fft_flops(L) + 6.0 * L),
+                            unit="valu_f32")
     if direct:
         m["directconv"] = dict(bytes=2 * T * D * s + BH * N * 4, flops=2.0 * BH * N * N * d,
                                unit="mfma_bf16" if s == 2 else "mfma_f32")
@@ -132,6 +142,29 @@ def cpu_baseline(wl, inp, target_s: float):
 
     import oracle
     threads = oracle.num_threads()
+    if wl.kind == "1d" and wl.N > 4096:
+        # one sequence's projections in full, and the circulant sum for a
+        # sample of its rows; the time per token adds both shares
+        t0 = time.perf_counter()
+        oracle.scores_1d(inp.X[:1], inp.W_A)
+        oracle.matmul(inp.X[:1], inp.W_V)
+        t_proj = time.perf_counter() - t0
+        zs = oracle.softmax(oracle.scores_1d(inp.X[:1], inp.W_A))
+        V = oracle.matmul(inp.X[:1], inp.W_V)
+        r = 64
+        t0 = time.perf_counter()
+        oracle.circulant_1d(zs, V, rows=list(range(r)))
+        t_row = (time.perf_counter() - t0) / r
+        per_token = t_proj / wl.N + t_row
+        r = int(max(r, min(wl.N, (target_s - t_proj) / max(t_row, 1e-9))))
+        t0 = time.perf_counter()
+        oracle.circulant_1d(zs, V, rows=list(range(r)))
+        t_row = (time.perf_counter() - t0) / r
+        per_token = t_proj / wl.N + t_row
+        return dict(value=1.0 / per_token, unit="tokens/s", cores=threads, kind="oracle",
+                    sample=f"projections of 1 sequence ({wl.N} tokens, {t_proj:.1f} s) and the fp64 direct "
+                           f"circulant sum for {r} of its rows ({t_row * r:.1f} s); tokens/s = 1 / "
+                           f"(projection time per token + sum time per row)")
     if wl.kind == "1d":
         t0 = time.perf_counter()
         oracle.cat_forward_1d(inp.X[:1], inp.W_A, inp.W_V)
@@ -239,7 +272,8 @@ def run(args):
 
     ngrp = (wl.d // 2 + 1) // 2  # score partials per (batch, head): pairs in groups of 2
     fused = wl.kind == "1d" and ktimes.get("spectrum", (0.0, 0))[1] == 0
-    model = kernel_model(wl, L, ngrp, fused_spectrum=fused, direct=conv_path == "direct")
+    model = kernel_model(wl, L, ngrp, fused_spectrum=fused and conv_path == "fft_matrix",
+                         direct=conv_path == "direct", multipass=conv_path == "fft_multipass")
     kernels = {}
     ktimes = {k: v for k, v in ktimes.items() if v[1] > 0}  # kernels this path launched
     for k, (ms, n) in ktimes.items():

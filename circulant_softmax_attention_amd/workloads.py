@@ -62,7 +62,9 @@ class Workload:
 
 
 # The five workloads, seeds 0..4 in this order.  The N=256 shape is run in two
-# storage dtypes from the same draws.
+# storage dtypes from the same draws.  Seed 5 is a long-sequence layer (the
+# GPT-2-small shape at 65536 tokens), where the CAT page expects the
+# O(N log N) route to pay; it measures the multi-pass path.
 WORKLOADS: Dict[str, Workload] = {
     w.name: w
     for w in [
@@ -78,6 +80,8 @@ WORKLOADS: Dict[str, Workload] = {
                  note="CAT 1D at prime length 197 (14x14 patches + CLS), DeiT-S shape, fp32"),
         Workload("bccb2d_1536px_96x96", "2d", 8, 96 * 96, 384, 6, BF16, 4, Hg=96, Wg=96,
                  note="2D BCCB circulant attention, 1536x1536 image at patch 16 (96x96 grid), bf16"),
+        Workload("cat1d_long_n65536", "1d", 1, 65536, 768, 12, BF16, 5,
+                 note="CAT 1D, GPT-2-small layer shape at N=65536 (multi-pass FFT), bf16 storage / fp32 compute"),
     ]
 }
 

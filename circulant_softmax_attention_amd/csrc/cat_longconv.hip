@@ -35,18 +35,31 @@ namespace {
 constexpr int LTHR = 256;
 constexpr int LBUF = 2048;  // complex values of the lines one workgroup transforms
 constexpr int LPAD = LBUF + 64;  // LDS buffer size: lines at pitch M + 1 (at most 64 lines)
+constexpr int LMAXM = 256;       // longest short DFT (L1, L2 <= 256: N <= 65536)
 
 __device__ __forceinline__ float2 cmul2(float2 a, float2 b) {
   return make_float2(fmaf(a.x, b.x, -a.y * b.y), fmaf(a.x, b.y, a.y * b.x));
 }
 __device__ __forceinline__ float2 conj2(float2 a) { return make_float2(a.x, -a.y); }
 
+// Twiddles of every stage of an M-point transform, in LDS: entry
+// 2^s - 1 + k holds W_(2^(s+1))^k = W_L^(k L / 2^(s+1)) for k < 2^s (M - 1
+// entries).  Read by lds_fft after its first barrier.
+__device__ __forceinline__ void stage_twiddles(float2* tws, int logM, const float2* __restrict__ tw, int logL) {
+  const int M = 1 << logM;
+  for (int i = threadIdx.x; i < M - 1; i += LTHR) {
+    const int s = 31 - __clz(i + 1), k = i + 1 - (1 << s);
+    tws[i] = tw[k << (logL - 1 - s)];
+  }
+}
+
 // R independent lines of M points (M a power of two) at a[r (M + 1) + i]
 // (the odd pitch keeps column-wise accesses off a single bank), natural
-// order in and out, unscaled; b is the ping-pong buffer.  Returns the buffer
-// holding the result.  Ends with a barrier.
+// order in and out, unscaled; b is the ping-pong buffer; tws the stage
+// twiddles (stage_twiddles).  Returns the buffer holding the result.  Ends
+// with a barrier.
 template <bool INV>
-__device__ float2* lds_fft(float2* a, float2* b, int M, int logM, int R, const float2* __restrict__ tw, int logL) {
+__device__ float2* lds_fft(float2* a, float2* b, int M, int logM, int R, const float2* tws) {
   const int P = M + 1;
   const int half = M >> 1;
   for (int s = 0; s < logM; ++s) {
@@ -56,7 +69,7 @@ __device__ float2* lds_fft(float2* a, float2* b, int M, int logM, int R, const f
       const int r = q >> (logM - 1), j = q & (half - 1);
       const int k = j & (Ns - 1);
       const float2 v0 = a[r * P + j];
-      float2 w = tw[k << (logL - 1 - s)];  // W_(2 Ns)^k = W_L^(k L / (2 Ns))
+      float2 w = tws[Ns - 1 + k];  // W_(2 Ns)^k
       if (INV) w = conj2(w);
       const float2 v1 = cmul2(a[r * P + j + half], w);
       const int d = ((j >> s) << (s + 1)) + k;
@@ -116,6 +129,7 @@ __global__ __launch_bounds__(LTHR) void softmax_line_kernel(const float* __restr
 template <int SET>
 __global__ __launch_bounds__(LTHR) void col_fwd_kernel(LongArgs a, const void* __restrict__ src, float2* __restrict__ A) {
   __shared__ float2 buf[2][LPAD];
+  __shared__ float2 tws[LMAXM];
   const int L1 = 1 << a.logL1, L2 = 1 << a.logL2, L = L1 * L2, CB = a.cb;
   const int nblk = L2 / CB;
   const int line = blockIdx.x / nblk, n20 = (blockIdx.x - line * nblk) * CB;
@@ -125,7 +139,8 @@ __global__ __launch_bounds__(LTHR) void col_fwd_kernel(LongArgs a, const void* _
     const int n1 = q / CB, c = q - n1 * CB;
     buf[0][c * (L1 + 1) + n1] = load_c<SET>(src, lbase + (size_t)n1 * L2 + n20 + c);
   }
-  const float2* U = lds_fft<false>(buf[0], buf[1], L1, a.logL1, CB, a.tw, a.logL1 + a.logL2);
+  stage_twiddles(tws, a.logL1, a.tw, a.logL1 + a.logL2);
+  const float2* U = lds_fft<false>(buf[0], buf[1], L1, a.logL1, CB, tws);
   for (int q = threadIdx.x; q < CB * L1; q += LTHR) {
     const int k1 = q / CB, c = q - k1 * CB;
     const int n2 = n20 + c;
@@ -140,14 +155,15 @@ __global__ __launch_bounds__(LTHR) void col_fwd_kernel(LongArgs a, const void* _
 template <int MODE>
 __global__ __launch_bounds__(LTHR) void row_kernel(LongArgs a, float2* __restrict__ A, float2* __restrict__ S) {
   __shared__ float2 buf[2][LPAD];
+  __shared__ float2 tws[LMAXM];
   const int L1 = 1 << a.logL1, L2 = 1 << a.logL2, L = L1 * L2, RB = a.rb;
   const int nblk = L1 / RB;
   const int line = blockIdx.x / nblk, k10 = (blockIdx.x - line * nblk) * RB;
   const size_t base = (size_t)line * L + (size_t)k10 * L2;  // RB contiguous rows
   const int P2 = L2 + 1;
   for (int q = threadIdx.x; q < RB * L2; q += LTHR) buf[0][(q >> a.logL2) * P2 + (q & (L2 - 1))] = A[base + q];
-  const int logL = a.logL1 + a.logL2;
-  float2* X = lds_fft<false>(buf[0], buf[1], L2, a.logL2, RB, a.tw, logL);
+  stage_twiddles(tws, a.logL2, a.tw, a.logL1 + a.logL2);
+  float2* X = lds_fft<false>(buf[0], buf[1], L2, a.logL2, RB, tws);
   float2* Y = X == buf[0] ? buf[1] : buf[0];
   if constexpr (MODE == 0) {
     const float sc = 1.f / (float)L;
@@ -161,7 +177,7 @@ __global__ __launch_bounds__(LTHR) void row_kernel(LongArgs a, float2* __restric
       const int i = (q >> a.logL2) * P2 + (q & (L2 - 1));
       X[i] = cmul2(X[i], S[sbase + q]);
     }
-    const float2* Bv = lds_fft<true>(X, Y, L2, a.logL2, RB, a.tw, logL);
+    const float2* Bv = lds_fft<true>(X, Y, L2, a.logL2, RB, tws);
     for (int q = threadIdx.x; q < RB * L2; q += LTHR) A[base + q] = Bv[(q >> a.logL2) * P2 + (q & (L2 - 1))];
   }
 }
@@ -172,6 +188,7 @@ __global__ __launch_bounds__(LTHR) void row_kernel(LongArgs a, float2* __restric
 template <int DET>
 __global__ __launch_bounds__(LTHR) void col_inv_kernel(LongArgs a, const float2* __restrict__ A, void* __restrict__ O) {
   __shared__ float2 buf[2][LPAD];
+  __shared__ float2 tws[LMAXM];
   const int L1 = 1 << a.logL1, L2 = 1 << a.logL2, L = L1 * L2, CB = a.cb;
   const int nblk = L2 / CB;
   const int line = blockIdx.x / nblk, n20 = (blockIdx.x - line * nblk) * CB;
@@ -181,7 +198,8 @@ __global__ __launch_bounds__(LTHR) void col_inv_kernel(LongArgs a, const float2*
     const int n2 = n20 + c;
     buf[0][c * (L1 + 1) + k1] = cmul2(A[lbase + (size_t)k1 * L2 + n2], conj2(a.tw[(k1 * n2) & (L - 1)]));
   }
-  const float2* U = lds_fft<true>(buf[0], buf[1], L1, a.logL1, CB, a.tw, a.logL1 + a.logL2);
+  stage_twiddles(tws, a.logL1, a.tw, a.logL1 + a.logL2);
+  const float2* U = lds_fft<true>(buf[0], buf[1], L1, a.logL1, CB, tws);
   const int bh = line / a.pairs, p = line - bh * a.pairs;
   const int b = bh / a.H, h = bh - b * a.H;
   const size_t obase = (size_t)b * L * a.D + (size_t)h * a.d + 2 * (size_t)p;
@@ -205,7 +223,7 @@ hipError_t launch_longconv(int et, const LongArgs& a0, const float* logits, cons
   if (!t) t = none;
   LongArgs a = a0;
   const int L1 = 1 << a.logL1, L2 = 1 << a.logL2;
-  if (a.logL1 < 1 || a.logL2 < 1 || L1 > LBUF || L2 > LBUF || a.pairs < 1 || a.BH < 1) return hipErrorInvalidValue;
+  if (a.logL1 < 1 || a.logL2 < 1 || L1 > LMAXM || L2 > LMAXM || a.pairs < 1 || a.BH < 1) return hipErrorInvalidValue;
   a.cb = LBUF / L1 < L2 ? LBUF / L1 : L2;  // adjacent columns per workgroup
   a.rb = LBUF / L2 < L1 ? LBUF / L2 : L1;  // rows per workgroup
   if (a.cb > 64) a.cb = 64;

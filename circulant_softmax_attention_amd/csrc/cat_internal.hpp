@@ -183,8 +183,9 @@ struct LongArgs {
   int H, D, d;
   int cb, rb;        // filled by the launcher: columns / rows per workgroup
 };
-// Launches, in order: softmax line, column pass and row pass of the filter
-// spectrum (zc, Az: [BH][L] complex fp32 scratch; S: [BH][L] spectrum), then
+// Launches, in order: softmax chunk partials, column pass and row pass of
+// the filter spectrum (zc: partials scratch, at least [BH][N / 1024] complex;
+// Az: [BH][L] complex fp32 scratch; S: [BH][L] spectrum), then
 // column pass, row pass with the spectrum product, inverse column pass of
 // the values (V BLOCKED with 2-channel groups, A: [BH d/2][L] complex fp32
 // scratch, O [B][N][D]).  t: six timing slots or null.

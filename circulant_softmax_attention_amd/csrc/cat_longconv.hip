@@ -15,7 +15,9 @@
 //   inverse column pass  for each n2: o[n1 L2 + n2] = sum_k1 B[k1][n2] conj W_L^(k1 n2) conj W_L1^(n1 k1)
 //
 // The filter spectrum is the column pass and the forward half of the row
-// pass applied to the softmax line, scaled by 1/L.  Each short DFT runs as a
+// pass applied to the softmax line, scaled by 1/L; the softmax is reduced
+// in chunks first, and the column pass normalises the logits as it loads
+// them.  Each short DFT runs as a
 // radix-2 Stockham transform in LDS (natural order in and out), several
 // lines per workgroup; all twiddles come from one table W_L^m, m < L,
 // computed in double precision on the host.  Two real channels ride in one
@@ -94,50 +96,77 @@ __device__ __forceinline__ float2 load_c(const void* base, size_t i) {
   }
 }
 
-// ---- softmax of one (b, h) logit line, as a complex line (imaginary 0)
-__global__ __launch_bounds__(LTHR) void softmax_line_kernel(const float* __restrict__ z, float2* __restrict__ zc,
+// ---- softmax partials: chunk c (SMC logits) of line bh -> (max m_c,
+// sum exp(z - m_c)); the column pass of the spectrum combines the chunks of
+// its line and normalises on the fly.
+constexpr int SMC = 1024;
+__global__ __launch_bounds__(LTHR) void softmax_part_kernel(const float* __restrict__ z, float2* __restrict__ part,
                                                             int N) {
   __shared__ float red[LTHR / 64];
-  const int bh = blockIdx.x, tid = threadIdx.x;
-  const float* zr = z + (size_t)bh * N;
-  auto reduce = [&](float v, bool is_max) {
+  const int nc = N / SMC;
+  const int bh = blockIdx.x / nc, c = blockIdx.x - bh * nc, tid = threadIdx.x;
+  const float* zr = z + (size_t)bh * N + (size_t)c * SMC;
+  float v[SMC / LTHR];
+#pragma unroll
+  for (int i = 0; i < SMC / LTHR; ++i) v[i] = zr[tid + LTHR * i];
+  auto reduce = [&](float x, bool is_max) {
     for (int o = 32; o >= 1; o >>= 1) {
-      const float p = __shfl_xor(v, o, 64);
-      v = is_max ? fmaxf(v, p) : v + p;
+      const float p = __shfl_xor(x, o, 64);
+      x = is_max ? fmaxf(x, p) : x + p;
     }
     __syncthreads();
-    if ((tid & 63) == 0) red[tid >> 6] = v;
+    if ((tid & 63) == 0) red[tid >> 6] = x;
     __syncthreads();
     float r = red[0];
     for (int w = 1; w < LTHR / 64; ++w) r = is_max ? fmaxf(r, red[w]) : r + red[w];
     return r;
   };
-  float m = -INFINITY;
-  for (int n = tid; n < N; n += LTHR) m = fmaxf(m, zr[n]);
+  float m = v[0];
+#pragma unroll
+  for (int i = 1; i < SMC / LTHR; ++i) m = fmaxf(m, v[i]);
   m = reduce(m, true);
-  float s = 0.f;
-  for (int n = tid; n < N; n += LTHR) s += __expf(zr[n] - m);
-  s = reduce(s, false);
-  const float inv = 1.f / s;
-  float2* out = zc + (size_t)bh * N;
-  for (int n = tid; n < N; n += LTHR) out[n] = make_float2(__expf(zr[n] - m) * inv, 0.f);
+  float se = 0.f;
+#pragma unroll
+  for (int i = 0; i < SMC / LTHR; ++i) se += __expf(v[i] - m);
+  se = reduce(se, false);
+  if (tid == 0) part[blockIdx.x] = make_float2(m, se);
 }
 
 // ---- column pass: line `line` of src (complex values, element type SET:
 // ET_F32 float2 or ET_BF16 bf16 pairs), CB adjacent columns n2 per
 // workgroup: A[line][k1 L2 + n2] = W_L^(k1 n2) DFT_L1 over n1.
 template <int SET>
-__global__ __launch_bounds__(LTHR) void col_fwd_kernel(LongArgs a, const void* __restrict__ src, float2* __restrict__ A) {
+__global__ __launch_bounds__(LTHR) void col_fwd_kernel(LongArgs a, const void* __restrict__ src, float2* __restrict__ A,
+                                                       const float2* __restrict__ smpart) {
   __shared__ float2 buf[2][LPAD];
   __shared__ float2 tws[LMAXM];
+  __shared__ float2 msum;
   const int L1 = 1 << a.logL1, L2 = 1 << a.logL2, L = L1 * L2, CB = a.cb;
   const int nblk = L2 / CB;
   const int line = blockIdx.x / nblk, n20 = (blockIdx.x - line * nblk) * CB;
   const size_t lbase = (size_t)line * L;
+  if constexpr (SET == 2) {
+    // softmax of the line from its chunk partials: m = max m_c,
+    // s = sum s_c exp(m_c - m); one wave combines them
+    const int nc = L / SMC;
+    if (threadIdx.x < 64) {
+      float2 p = threadIdx.x < nc ? smpart[(size_t)line * nc + threadIdx.x] : make_float2(-INFINITY, 0.f);
+      float m = p.x;
+      for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+      float sv = threadIdx.x < nc ? p.y * __expf(p.x - m) : 0.f;
+      for (int o = 32; o >= 1; o >>= 1) sv += __shfl_xor(sv, o, 64);
+      if (threadIdx.x == 0) msum = make_float2(m, 1.f / sv);
+    }
+    __syncthreads();
+  }
   // buf[0][c L1 + n1] = x[n1 L2 + n20 + c]; consecutive threads take consecutive c
   for (int q = threadIdx.x; q < CB * L1; q += LTHR) {
     const int n1 = q / CB, c = q - n1 * CB;
-    buf[0][c * (L1 + 1) + n1] = load_c<SET>(src, lbase + (size_t)n1 * L2 + n20 + c);
+    const size_t i = lbase + (size_t)n1 * L2 + n20 + c;
+    if constexpr (SET == 2)
+      buf[0][c * (L1 + 1) + n1] = make_float2(__expf(reinterpret_cast<const float*>(src)[i] - msum.x) * msum.y, 0.f);
+    else
+      buf[0][c * (L1 + 1) + n1] = load_c<SET>(src, i);
   }
   stage_twiddles(tws, a.logL1, a.tw, a.logL1 + a.logL2);
   const float2* U = lds_fft<false>(buf[0], buf[1], L1, a.logL1, CB, tws);
@@ -233,18 +262,23 @@ hipError_t launch_longconv(int et, const LongArgs& a0, const float* logits, cons
   const long colb_z = (long)a.BH * (L2 / a.cb), rowb_z = (long)a.BH * (L1 / a.rb);
   const long colb = lines * (L2 / a.cb), rowb = lines * (L1 / a.rb);
   if (colb > 0x7fffffffL || rowb > 0x7fffffffL) return hipErrorInvalidValue;
-  // the filter spectrum
-  hipError_t e = launch_k(softmax_line_kernel, dim3(a.BH), dim3(LTHR), 0, s, t[0], logits, zc, N);
+  // the filter spectrum: softmax partials (in zc), then the column pass of
+  // the normalised line, straight from the logits
+  if (N % SMC != 0 || N / SMC > 64) return hipErrorInvalidValue;
+  hipError_t e = launch_k(softmax_part_kernel, dim3((unsigned)(a.BH * (N / SMC))), dim3(LTHR), 0, s, t[0], logits, zc, N);
   if (e != hipSuccess) return e;
-  e = launch_k(col_fwd_kernel<ET_F32>, dim3((unsigned)colb_z), dim3(LTHR), 0, s, t[1], a, (const void*)zc, Az);
+  e = launch_k(col_fwd_kernel<2>, dim3((unsigned)colb_z), dim3(LTHR), 0, s, t[1], a, (const void*)logits, Az,
+               (const float2*)zc);
   if (e != hipSuccess) return e;
   e = launch_k(row_kernel<0>, dim3((unsigned)rowb_z), dim3(LTHR), 0, s, t[2], a, Az, S);
   if (e != hipSuccess) return e;
   // the mixing
   if (et == ET_F32)
-    e = launch_k(col_fwd_kernel<ET_F32>, dim3((unsigned)colb), dim3(LTHR), 0, s, t[3], a, V, A);
+    e = launch_k(col_fwd_kernel<ET_F32>, dim3((unsigned)colb), dim3(LTHR), 0, s, t[3], a, V, A,
+                 (const float2*)nullptr);
   else
-    e = launch_k(col_fwd_kernel<ET_BF16>, dim3((unsigned)colb), dim3(LTHR), 0, s, t[3], a, V, A);
+    e = launch_k(col_fwd_kernel<ET_BF16>, dim3((unsigned)colb), dim3(LTHR), 0, s, t[3], a, V, A,
+                 (const float2*)nullptr);
   if (e != hipSuccess) return e;
   e = launch_k(row_kernel<1>, dim3((unsigned)rowb), dim3(LTHR), 0, s, t[4], a, A, S);
   if (e != hipSuccess) return e;

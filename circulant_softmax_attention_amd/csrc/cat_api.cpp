@@ -213,7 +213,10 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
     pl->direct = !force_fft && p->kind == CAT_1D && p->dtype == CAT_BF16 && p->N <= 256 && d % 32 == 0;
     pl->mconv = !longn && !pl->direct && !force_valu && p->kind == CAT_1D && p->dtype == CAT_BF16 &&
                 g.L1 * g.L2 == 1024 && d % 16 == 0;
-    if (longn) G = 1;
+    if (longn) {  // pair blocks of the long path: the largest power of two <= 8 dividing d/2
+      G = 1;
+      while (G < 8 && d2 % (2 * G) == 0) G *= 2;
+    }
     pl->G = G;
     pl->ng = d2 / G;
     pl->cg = pl->direct ? 32 : pl->mconv ? 16 : 2 * G;
@@ -470,6 +473,7 @@ LongArgs long_base(const cat_plan_s* pl) {
   a.H = (int)pl->p.H;
   a.D = (int)pl->p.D;
   a.d = pl->d;
+  a.pb = pl->cg / 2;
   return a;
 }
 

@@ -181,14 +181,14 @@ struct LongArgs {
   int logL1, logL2;  // L1 = 2^logL1 (column DFTs), L2 = 2^logL2 (row DFTs)
   int BH, pairs;     // (batch, head) lines and channel pairs per head (d / 2)
   int H, D, d;
-  int cb, rb;        // filled by the launcher: columns / rows per workgroup
+  int pb;            // channel pairs per block of V and of the intermediates (1, 2, 4 or 8; divides pairs)
 };
 // Launches, in order: softmax chunk partials, column pass and row pass of
 // the filter spectrum (zc: partials scratch, at least [BH][N / 1024] complex;
 // Az: [BH][L] complex fp32 scratch; S: [BH][L] spectrum), then
 // column pass, row pass with the spectrum product, inverse column pass of
-// the values (V BLOCKED with 2-channel groups, A: [BH d/2][L] complex fp32
-// scratch, O [B][N][D]).  t: six timing slots or null.
+// the values (V BLOCKED with 2 pb-channel groups, A: [BH d/2][L] complex
+// fp32 scratch, O [B][N][D]).  t: six timing slots or null.
 hipError_t launch_longconv(int et, const LongArgs& a, const float* logits, const void* V, float2* zc, float2* Az,
                            float2* S, float2* A, void* O, hipStream_t s, const LaunchTiming* const* t = nullptr);
 // 2D: out[bh][k] = sum over g of part[bh][g][k] (partials [BH][ngrp][L],

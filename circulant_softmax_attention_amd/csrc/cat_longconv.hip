@@ -23,10 +23,10 @@
 // computed in double precision on the host.  Two real channels ride in one
 // complex line, as in the single-workgroup convolution.
 //
-// Layouts: V is BLOCKED with 2-channel groups ([BH][d/2][N][2], one complex
-// line per channel pair); the intermediate A is [lines][L1][L2] complex
-// fp32; the spectrum S is [BH][L1][L2] complex fp32 (entry k1 L2 + k2 holds
-// frequency k1 + L1 k2).
+// Layouts: V is BLOCKED with 2 PB-channel groups ([BH][d/2/PB][N][PB]
+// complex, PB channel pairs per block); the intermediate A is
+// [BH][d/2/PB][L1][L2][PB] complex fp32; the spectrum S is [BH][L1][L2]
+// complex fp32 (entry k1 L2 + k2 holds frequency k1 + L1 k2).
 #include "cat_common.hpp"
 #include "cat_internal.hpp"
 
@@ -132,25 +132,34 @@ __global__ __launch_bounds__(LTHR) void softmax_part_kernel(const float* __restr
   if (tid == 0) part[blockIdx.x] = make_float2(m, se);
 }
 
-// ---- column pass: line `line` of src (complex values, element type SET:
-// ET_F32 float2 or ET_BF16 bf16 pairs), CB adjacent columns n2 per
-// workgroup: A[line][k1 L2 + n2] = W_L^(k1 n2) DFT_L1 over n1.
+// Pair blocks.  The values' lines come in blocks of PB channel pairs with
+// the pair index innermost: V [BH][P / PB][N][PB] (the blocked layout with
+// 2 PB-channel groups) and A [BH][P / PB][L1][L2][PB], so that one token (or
+// one (k1, n2) point) of a block is PB contiguous complex values.  A
+// workgroup transforms every pair of its block; the spectrum's line is a
+// block of one.
+
+// ---- column pass: CB adjacent columns n2 of block `gl`, every pair:
+// A[gl][k1][n2][j] = W_L^(k1 n2) DFT_L1 over n1 of x[n1 L2 + n2][j].
+// SET: ET_F32 (float2 values), ET_BF16 (bf16 pairs), or 2 (fp32 logits,
+// softmax from the chunk partials; PB = 1).
 template <int SET>
-__global__ __launch_bounds__(LTHR) void col_fwd_kernel(LongArgs a, const void* __restrict__ src, float2* __restrict__ A,
-                                                       const float2* __restrict__ smpart) {
+__global__ __launch_bounds__(LTHR) void col_fwd_kernel(LongArgs a, int PB, const void* __restrict__ src,
+                                                       float2* __restrict__ A, const float2* __restrict__ smpart) {
   __shared__ float2 buf[2][LPAD];
   __shared__ float2 tws[LMAXM];
   __shared__ float2 msum;
-  const int L1 = 1 << a.logL1, L2 = 1 << a.logL2, L = L1 * L2, CB = a.cb;
+  const int L1 = 1 << a.logL1, L2 = 1 << a.logL2, L = L1 * L2;
+  const int CB = LBUF / (PB * L1) < L2 ? LBUF / (PB * L1) : L2, R = CB * PB;
   const int nblk = L2 / CB;
-  const int line = blockIdx.x / nblk, n20 = (blockIdx.x - line * nblk) * CB;
-  const size_t lbase = (size_t)line * L;
+  const int gl = blockIdx.x / nblk, n20 = (blockIdx.x - gl * nblk) * CB;
+  const size_t gbase = (size_t)gl * L * PB;
   if constexpr (SET == 2) {
     // softmax of the line from its chunk partials: m = max m_c,
     // s = sum s_c exp(m_c - m); one wave combines them
     const int nc = L / SMC;
     if (threadIdx.x < 64) {
-      float2 p = threadIdx.x < nc ? smpart[(size_t)line * nc + threadIdx.x] : make_float2(-INFINITY, 0.f);
+      float2 p = threadIdx.x < nc ? smpart[(size_t)gl * nc + threadIdx.x] : make_float2(-INFINITY, 0.f);
       float m = p.x;
       for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
       float sv = threadIdx.x < nc ? p.y * __expf(p.x - m) : 0.f;
@@ -159,132 +168,148 @@ __global__ __launch_bounds__(LTHR) void col_fwd_kernel(LongArgs a, const void* _
     }
     __syncthreads();
   }
-  // buf[0][c L1 + n1] = x[n1 L2 + n20 + c]; consecutive threads take consecutive c
-  for (int q = threadIdx.x; q < CB * L1; q += LTHR) {
-    const int n1 = q / CB, c = q - n1 * CB;
-    const size_t i = lbase + (size_t)n1 * L2 + n20 + c;
+  // line r = c PB + j of the workgroup holds column n20 + c of pair j:
+  // buf[0][r (L1 + 1) + n1]; consecutive threads read consecutive memory
+  for (int q = threadIdx.x; q < R * L1; q += LTHR) {
+    const int n1 = q / R, r = q - n1 * R;
+    const size_t i = gbase + ((size_t)n1 * L2 + n20) * PB + r;
     if constexpr (SET == 2)
-      buf[0][c * (L1 + 1) + n1] = make_float2(__expf(reinterpret_cast<const float*>(src)[i] - msum.x) * msum.y, 0.f);
+      buf[0][r * (L1 + 1) + n1] = make_float2(__expf(reinterpret_cast<const float*>(src)[i] - msum.x) * msum.y, 0.f);
     else
-      buf[0][c * (L1 + 1) + n1] = load_c<SET>(src, i);
+      buf[0][r * (L1 + 1) + n1] = load_c<SET>(src, i);
   }
   stage_twiddles(tws, a.logL1, a.tw, a.logL1 + a.logL2);
-  const float2* U = lds_fft<false>(buf[0], buf[1], L1, a.logL1, CB, tws);
-  for (int q = threadIdx.x; q < CB * L1; q += LTHR) {
-    const int k1 = q / CB, c = q - k1 * CB;
-    const int n2 = n20 + c;
+  const float2* U = lds_fft<false>(buf[0], buf[1], L1, a.logL1, R, tws);
+  for (int q = threadIdx.x; q < R * L1; q += LTHR) {
+    const int k1 = q / R, r = q - k1 * R;
+    const int n2 = n20 + r / PB;
     const float2 w = a.tw[(k1 * n2) & (L - 1)];
-    A[lbase + (size_t)k1 * L2 + n2] = cmul2(U[c * (L1 + 1) + k1], w);
+    A[gbase + ((size_t)k1 * L2 + n20) * PB + r] = cmul2(U[r * (L1 + 1) + k1], w);
   }
 }
 
-// ---- row pass, RB rows k1 per workgroup.  MODE 0 (spectrum): S = DFT_L2 / L
-// of the rows of Az.  MODE 1 (mixing): A = IDFT_L2(DFT_L2(A) . S[bh]) in
-// place, bh = line / pairs.
+// ---- row pass, RB rows k1 of block `gl` per workgroup, every pair.
+// MODE 0 (spectrum, PB = 1): S = DFT_L2 / L of the rows of Az.  MODE 1
+// (mixing): A = IDFT_L2(DFT_L2(A) . S[bh]) in place, bh = gl / (P / PB).
 template <int MODE>
-__global__ __launch_bounds__(LTHR) void row_kernel(LongArgs a, float2* __restrict__ A, float2* __restrict__ S) {
+__global__ __launch_bounds__(LTHR) void row_kernel(LongArgs a, int PB, float2* __restrict__ A, float2* __restrict__ S) {
   __shared__ float2 buf[2][LPAD];
   __shared__ float2 tws[LMAXM];
-  const int L1 = 1 << a.logL1, L2 = 1 << a.logL2, L = L1 * L2, RB = a.rb;
+  const int L1 = 1 << a.logL1, L2 = 1 << a.logL2, L = L1 * L2;
+  const int RB = LBUF / (PB * L2) < L1 ? LBUF / (PB * L2) : L1, R = RB * PB;
   const int nblk = L1 / RB;
-  const int line = blockIdx.x / nblk, k10 = (blockIdx.x - line * nblk) * RB;
-  const size_t base = (size_t)line * L + (size_t)k10 * L2;  // RB contiguous rows
+  const int gl = blockIdx.x / nblk, k10 = (blockIdx.x - gl * nblk) * RB;
+  const size_t base = ((size_t)gl * L + (size_t)k10 * L2) * PB;  // RB contiguous rows of the block
   const int P2 = L2 + 1;
-  for (int q = threadIdx.x; q < RB * L2; q += LTHR) buf[0][(q >> a.logL2) * P2 + (q & (L2 - 1))] = A[base + q];
+  // LDS line r = (k1 - k10) PB + j: row k1 of pair j, buf[r P2 + n2]
+  const int RL = L2 * PB;  // values per row of the block
+  for (int q = threadIdx.x; q < RB * RL; q += LTHR) {
+    const int rr = q / RL, rem = q - rr * RL, n2 = rem / PB, j = rem - n2 * PB;
+    buf[0][(rr * PB + j) * P2 + n2] = A[base + q];
+  }
   stage_twiddles(tws, a.logL2, a.tw, a.logL1 + a.logL2);
-  float2* X = lds_fft<false>(buf[0], buf[1], L2, a.logL2, RB, tws);
+  float2* X = lds_fft<false>(buf[0], buf[1], L2, a.logL2, R, tws);
   float2* Y = X == buf[0] ? buf[1] : buf[0];
   if constexpr (MODE == 0) {
     const float sc = 1.f / (float)L;
     for (int q = threadIdx.x; q < RB * L2; q += LTHR) {
-      const float2 v = X[(q >> a.logL2) * P2 + (q & (L2 - 1))];
+      const int rr = q >> a.logL2, k2 = q & (L2 - 1);
+      const float2 v = X[rr * P2 + k2];
       S[base + q] = make_float2(v.x * sc, v.y * sc);
     }
   } else {
-    const size_t sbase = (size_t)(line / a.pairs) * L + (size_t)k10 * L2;
-    for (int q = threadIdx.x; q < RB * L2; q += LTHR) {
-      const int i = (q >> a.logL2) * P2 + (q & (L2 - 1));
-      X[i] = cmul2(X[i], S[sbase + q]);
+    const size_t sbase = (size_t)(gl / (a.pairs / PB)) * L + (size_t)k10 * L2;
+    for (int q = threadIdx.x; q < R * L2; q += LTHR) {
+      const int r = q >> a.logL2, k2 = q & (L2 - 1);
+      const int i = r * P2 + k2;
+      X[i] = cmul2(X[i], S[sbase + (size_t)(r / PB) * L2 + k2]);
     }
-    const float2* Bv = lds_fft<true>(X, Y, L2, a.logL2, RB, tws);
-    for (int q = threadIdx.x; q < RB * L2; q += LTHR) A[base + q] = Bv[(q >> a.logL2) * P2 + (q & (L2 - 1))];
+    const float2* Bv = lds_fft<true>(X, Y, L2, a.logL2, R, tws);
+    for (int q = threadIdx.x; q < RB * RL; q += LTHR) {
+      const int rr = q / RL, rem = q - rr * RL, n2 = rem / PB, j = rem - n2 * PB;
+      A[base + q] = Bv[(rr * PB + j) * P2 + n2];
+    }
   }
 }
 
-// ---- inverse column pass: o[n1 L2 + n2] = IDFT_L1 over k1 of
-// B[k1][n2] conj W_L^(k1 n2), written to O[b][n][h d + 2 p ..] (storage
-// element type DET), line = bh * pairs + p.
+// ---- inverse column pass: o[n1 L2 + n2][j] = IDFT_L1 over k1 of
+// A[gl][k1][n2][j] conj W_L^(k1 n2), written to O[b][n][h d + 2 (g PB + j) ..]
+// (storage element type DET), gl = bh (P / PB) + g.
 template <int DET>
-__global__ __launch_bounds__(LTHR) void col_inv_kernel(LongArgs a, const float2* __restrict__ A, void* __restrict__ O) {
+__global__ __launch_bounds__(LTHR) void col_inv_kernel(LongArgs a, int PB, const float2* __restrict__ A,
+                                                       void* __restrict__ O) {
   __shared__ float2 buf[2][LPAD];
   __shared__ float2 tws[LMAXM];
-  const int L1 = 1 << a.logL1, L2 = 1 << a.logL2, L = L1 * L2, CB = a.cb;
+  const int L1 = 1 << a.logL1, L2 = 1 << a.logL2, L = L1 * L2;
+  const int CB = LBUF / (PB * L1) < L2 ? LBUF / (PB * L1) : L2, R = CB * PB;
   const int nblk = L2 / CB;
-  const int line = blockIdx.x / nblk, n20 = (blockIdx.x - line * nblk) * CB;
-  const size_t lbase = (size_t)line * L;
-  for (int q = threadIdx.x; q < CB * L1; q += LTHR) {
-    const int k1 = q / CB, c = q - k1 * CB;
-    const int n2 = n20 + c;
-    buf[0][c * (L1 + 1) + k1] = cmul2(A[lbase + (size_t)k1 * L2 + n2], conj2(a.tw[(k1 * n2) & (L - 1)]));
+  const int gl = blockIdx.x / nblk, n20 = (blockIdx.x - gl * nblk) * CB;
+  const size_t gbase = (size_t)gl * L * PB;
+  for (int q = threadIdx.x; q < R * L1; q += LTHR) {
+    const int k1 = q / R, r = q - k1 * R;
+    const int n2 = n20 + r / PB;
+    buf[0][r * (L1 + 1) + k1] =
+        cmul2(A[gbase + ((size_t)k1 * L2 + n20) * PB + r], conj2(a.tw[(k1 * n2) & (L - 1)]));
   }
   stage_twiddles(tws, a.logL1, a.tw, a.logL1 + a.logL2);
-  const float2* U = lds_fft<true>(buf[0], buf[1], L1, a.logL1, CB, tws);
-  const int bh = line / a.pairs, p = line - bh * a.pairs;
+  const float2* U = lds_fft<true>(buf[0], buf[1], L1, a.logL1, R, tws);
+  const int groups = a.pairs / PB;
+  const int bh = gl / groups, g = gl - bh * groups;
   const int b = bh / a.H, h = bh - b * a.H;
-  const size_t obase = (size_t)b * L * a.D + (size_t)h * a.d + 2 * (size_t)p;
-  for (int q = threadIdx.x; q < CB * L1; q += LTHR) {
-    const int n1 = q / CB, c = q - n1 * CB;
+  const size_t obase = (size_t)b * L * a.D + (size_t)h * a.d + 2 * (size_t)g * PB;
+  for (int q = threadIdx.x; q < R * L1; q += LTHR) {
+    const int n1 = q / R, r = q - n1 * R;
+    const int c = r / PB, j = r - c * PB;
     const size_t n = (size_t)n1 * L2 + n20 + c;
-    const float2 v = U[c * (L1 + 1) + n1];
+    const float2 v = U[r * (L1 + 1) + n1];
     if constexpr (DET == ET_F32) {
-      *reinterpret_cast<float2*>(reinterpret_cast<float*>(O) + obase + n * a.D) = v;
+      *reinterpret_cast<float2*>(reinterpret_cast<float*>(O) + obase + n * a.D + 2 * j) = v;
     } else {
-      *reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(O) + obase + n * a.D) = pack_bf16x2(v.x, v.y);
+      *reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(O) + obase + n * a.D + 2 * j) = pack_bf16x2(v.x, v.y);
     }
   }
 }
 
 }  // namespace
 
-hipError_t launch_longconv(int et, const LongArgs& a0, const float* logits, const void* V, float2* zc, float2* Az,
+hipError_t launch_longconv(int et, const LongArgs& a, const float* logits, const void* V, float2* zc, float2* Az,
                            float2* S, float2* A, void* O, hipStream_t s, const LaunchTiming* const* t) {
   const LaunchTiming* none[6] = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
   if (!t) t = none;
-  LongArgs a = a0;
-  const int L1 = 1 << a.logL1, L2 = 1 << a.logL2;
+  const int L1 = 1 << a.logL1, L2 = 1 << a.logL2, N = L1 * L2, PB = a.pb;
   if (a.logL1 < 1 || a.logL2 < 1 || L1 > LMAXM || L2 > LMAXM || a.pairs < 1 || a.BH < 1) return hipErrorInvalidValue;
-  a.cb = LBUF / L1 < L2 ? LBUF / L1 : L2;  // adjacent columns per workgroup
-  a.rb = LBUF / L2 < L1 ? LBUF / L2 : L1;  // rows per workgroup
-  if (a.cb > 64) a.cb = 64;
-  if (a.rb > 64) a.rb = 64;
-  const int N = L1 * L2;
-  const long lines = (long)a.BH * a.pairs;
-  const long colb_z = (long)a.BH * (L2 / a.cb), rowb_z = (long)a.BH * (L1 / a.rb);
-  const long colb = lines * (L2 / a.cb), rowb = lines * (L1 / a.rb);
+  if (PB < 1 || PB > 8 || (PB & (PB - 1)) != 0 || a.pairs % PB != 0) return hipErrorInvalidValue;
+  // lines per workgroup (CB PB columns, RB PB rows) stay within the LDS pad
+  const int cb1 = LBUF / L1 < L2 ? LBUF / L1 : L2, rb1 = LBUF / L2 < L1 ? LBUF / L2 : L1;
+  const int cb = LBUF / (PB * L1) < L2 ? LBUF / (PB * L1) : L2, rb = LBUF / (PB * L2) < L1 ? LBUF / (PB * L2) : L1;
+  if (cb < 1 || rb < 1 || cb1 > 64 || rb1 > 64 || cb * PB > 64 || rb * PB > 64) return hipErrorInvalidValue;
+  if (N % SMC != 0 || N / SMC > 64) return hipErrorInvalidValue;
+  const long blocks = (long)a.BH * (a.pairs / PB);
+  const long colb_z = (long)a.BH * (L2 / cb1), rowb_z = (long)a.BH * (L1 / rb1);
+  const long colb = blocks * (L2 / cb), rowb = blocks * (L1 / rb);
   if (colb > 0x7fffffffL || rowb > 0x7fffffffL) return hipErrorInvalidValue;
   // the filter spectrum: softmax partials (in zc), then the column pass of
-  // the normalised line, straight from the logits
-  if (N % SMC != 0 || N / SMC > 64) return hipErrorInvalidValue;
+  // the normalised line, straight from the logits, then the rows
   hipError_t e = launch_k(softmax_part_kernel, dim3((unsigned)(a.BH * (N / SMC))), dim3(LTHR), 0, s, t[0], logits, zc, N);
   if (e != hipSuccess) return e;
-  e = launch_k(col_fwd_kernel<2>, dim3((unsigned)colb_z), dim3(LTHR), 0, s, t[1], a, (const void*)logits, Az,
+  e = launch_k(col_fwd_kernel<2>, dim3((unsigned)colb_z), dim3(LTHR), 0, s, t[1], a, 1, (const void*)logits, Az,
                (const float2*)zc);
   if (e != hipSuccess) return e;
-  e = launch_k(row_kernel<0>, dim3((unsigned)rowb_z), dim3(LTHR), 0, s, t[2], a, Az, S);
+  e = launch_k(row_kernel<0>, dim3((unsigned)rowb_z), dim3(LTHR), 0, s, t[2], a, 1, Az, S);
   if (e != hipSuccess) return e;
-  // the mixing
+  // the mixing, PB pairs per block
   if (et == ET_F32)
-    e = launch_k(col_fwd_kernel<ET_F32>, dim3((unsigned)colb), dim3(LTHR), 0, s, t[3], a, V, A,
+    e = launch_k(col_fwd_kernel<ET_F32>, dim3((unsigned)colb), dim3(LTHR), 0, s, t[3], a, PB, V, A,
                  (const float2*)nullptr);
   else
-    e = launch_k(col_fwd_kernel<ET_BF16>, dim3((unsigned)colb), dim3(LTHR), 0, s, t[3], a, V, A,
+    e = launch_k(col_fwd_kernel<ET_BF16>, dim3((unsigned)colb), dim3(LTHR), 0, s, t[3], a, PB, V, A,
                  (const float2*)nullptr);
   if (e != hipSuccess) return e;
-  e = launch_k(row_kernel<1>, dim3((unsigned)rowb), dim3(LTHR), 0, s, t[4], a, A, S);
+  e = launch_k(row_kernel<1>, dim3((unsigned)rowb), dim3(LTHR), 0, s, t[4], a, PB, A, S);
   if (e != hipSuccess) return e;
   if (et == ET_F32)
-    return launch_k(col_inv_kernel<ET_F32>, dim3((unsigned)colb), dim3(LTHR), 0, s, t[5], a, (const float2*)A, O);
-  return launch_k(col_inv_kernel<ET_BF16>, dim3((unsigned)colb), dim3(LTHR), 0, s, t[5], a, (const float2*)A, O);
+    return launch_k(col_inv_kernel<ET_F32>, dim3((unsigned)colb), dim3(LTHR), 0, s, t[5], a, PB, (const float2*)A, O);
+  return launch_k(col_inv_kernel<ET_BF16>, dim3((unsigned)colb), dim3(LTHR), 0, s, t[5], a, PB, (const float2*)A, O);
 }
 
 }  // namespace cat

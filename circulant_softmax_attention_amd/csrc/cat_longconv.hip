@@ -44,14 +44,21 @@ __device__ __forceinline__ float2 cmul2(float2 a, float2 b) {
 }
 __device__ __forceinline__ float2 conj2(float2 a) { return make_float2(a.x, -a.y); }
 
-// Twiddles of every stage of an M-point transform, in LDS: entry
-// 2^s - 1 + k holds W_(2^(s+1))^k = W_L^(k L / 2^(s+1)) for k < 2^s (M - 1
-// entries).  Read by lds_fft after its first barrier.
+// Stockham stages of an M-point transform: one radix-2 stage first when
+// log2 M is odd, then radix-4 stages with Ns = 1 or 2, then x4 up to M.
+// The radix-4 stage twiddles live in LDS: the stage with span Ns holds, at
+// offset toff(Ns) + 3 k + r - 1, W_(4 Ns)^(r k) = W_L^(r k L / (4 Ns)) for
+// k < Ns, r = 1..3 (at most 255 entries for M <= 256).  Read by lds_fft
+// after its first barrier.
 __device__ __forceinline__ void stage_twiddles(float2* tws, int logM, const float2* __restrict__ tw, int logL) {
-  const int M = 1 << logM;
-  for (int i = threadIdx.x; i < M - 1; i += LTHR) {
-    const int s = 31 - __clz(i + 1), k = i + 1 - (1 << s);
-    tws[i] = tw[k << (logL - 1 - s)];
+  const int M = 1 << logM, L = 1 << logL;
+  int Ns = (logM & 1) ? 2 : 1, toff = 0;
+  for (; Ns < M; toff += 3 * Ns, Ns *= 4) {
+    const int step = L / (4 * Ns);
+    for (int i = threadIdx.x; i < 3 * Ns; i += LTHR) {
+      const int k = i / 3, r = i - 3 * k + 1;
+      tws[toff + i] = tw[(r * k * step) & (L - 1)];
+    }
   }
 }
 
@@ -63,20 +70,48 @@ __device__ __forceinline__ void stage_twiddles(float2* tws, int logM, const floa
 template <bool INV>
 __device__ float2* lds_fft(float2* a, float2* b, int M, int logM, int R, const float2* tws) {
   const int P = M + 1;
-  const int half = M >> 1;
-  for (int s = 0; s < logM; ++s) {
-    const int Ns = 1 << s;
+  int Ns = 1, toff = 0;
+  if (logM & 1) {  // radix 2, span 1: no twiddle
+    const int half = M >> 1;
     __syncthreads();
     for (int q = threadIdx.x; q < R * half; q += LTHR) {
       const int r = q >> (logM - 1), j = q & (half - 1);
+      const float2 v0 = a[r * P + j], v1 = a[r * P + j + half];
+      b[r * P + 2 * j] = make_float2(v0.x + v1.x, v0.y + v1.y);
+      b[r * P + 2 * j + 1] = make_float2(v0.x - v1.x, v0.y - v1.y);
+    }
+    float2* t = a;
+    a = b;
+    b = t;
+    Ns = 2;
+  }
+  const int quarter = M >> 2;
+  const int lq = logM - 2;
+  for (; Ns < M; toff += 3 * Ns, Ns *= 4) {
+    __syncthreads();
+    for (int q = threadIdx.x; q < R * quarter; q += LTHR) {
+      const int r = q >> lq, j = q & (quarter - 1);
       const int k = j & (Ns - 1);
-      const float2 v0 = a[r * P + j];
-      float2 w = tws[Ns - 1 + k];  // W_(2 Ns)^k
-      if (INV) w = conj2(w);
-      const float2 v1 = cmul2(a[r * P + j + half], w);
-      const int d = ((j >> s) << (s + 1)) + k;
-      b[r * P + d] = make_float2(v0.x + v1.x, v0.y + v1.y);
-      b[r * P + d + Ns] = make_float2(v0.x - v1.x, v0.y - v1.y);
+      const float2* src = a + r * P + j;
+      float2 v0 = src[0], v1 = src[quarter], v2 = src[2 * quarter], v3 = src[3 * quarter];
+      float2 w1 = tws[toff + 3 * k], w2 = tws[toff + 3 * k + 1], w3 = tws[toff + 3 * k + 2];
+      if (INV) {
+        w1 = conj2(w1);
+        w2 = conj2(w2);
+        w3 = conj2(w3);
+      }
+      v1 = cmul2(v1, w1);
+      v2 = cmul2(v2, w2);
+      v3 = cmul2(v3, w3);
+      const float2 t0 = make_float2(v0.x + v2.x, v0.y + v2.y), t1 = make_float2(v0.x - v2.x, v0.y - v2.y);
+      const float2 t2 = make_float2(v1.x + v3.x, v1.y + v3.y), t3 = make_float2(v1.x - v3.x, v1.y - v3.y);
+      // forward W_4 = -i: X1 = t1 - i t3, X3 = t1 + i t3 (inverse: swapped)
+      const float2 mt3 = INV ? make_float2(-t3.y, t3.x) : make_float2(t3.y, -t3.x);  // -/+ i t3
+      float2* dst = b + r * P + ((j & ~(Ns - 1)) << 2) + k;
+      dst[0] = make_float2(t0.x + t2.x, t0.y + t2.y);
+      dst[Ns] = make_float2(t1.x + mt3.x, t1.y + mt3.y);
+      dst[2 * Ns] = make_float2(t0.x - t2.x, t0.y - t2.y);
+      dst[3 * Ns] = make_float2(t1.x - mt3.x, t1.y - mt3.y);
     }
     float2* t = a;
     a = b;

@@ -222,13 +222,14 @@ def test_conv_path_choice(cat, N, D, H, dtype, path):
 @pytest.mark.parametrize("B,N,D,H,dtype,lscale", [
     (1, 8192, 8, 2, "f32", 2.0), (1, 8192, 8, 2, "bf16", 2.0), (2, 16384, 24, 3, "f32", 3.0),
     (1, 16384, 8, 1, "f32", 0.0), (1, 16384, 8, 1, "bf16", 40.0), (1, 32768, 8, 1, "f32", 2.0),
-    (1, 65536, 8, 2, "f32", 2.0), (1, 65536, 8, 1, "bf16", 2.0)])
+    (1, 65536, 8, 2, "f32", 2.0), (1, 65536, 8, 1, "bf16", 2.0),
+    (1, 8192, 24, 4, "f32", 2.0), (2, 8192, 24, 2, "bf16", 2.0)])
 def test_mix_1d_long(cat, B, N, D, H, dtype, lscale):
     """Power-of-two N beyond one workgroup's line: column, row and inverse
     column passes over HBM.  Cases span N = 2^13 .. 2^16 (square and 2:1
-    splits), uniform scores (lscale 0) and a near one-hot softmax (lscale
-    40); beyond 16384 x 16384 x 24 multiply-adds the oracle checks 1024
-    sampled rows."""
+    splits), uniform scores (lscale 0), a near one-hot softmax (lscale 40),
+    and pair blocks of 1, 2 and 4 channel pairs (d = 6, 12, 8); beyond
+    16384 x 16384 x 24 multiply-adds the oracle checks 1024 sampled rows."""
     say("mix_1d_long", B, N, D, H, dtype, lscale)
     import torch
     rng = np.random.default_rng(N + 5 * D)
@@ -382,7 +383,8 @@ def test_mix_2d(cat, Hg, Wg, dtype):
 
 @pytest.mark.parametrize("B,Hg,Wg,D,H,dtype,ss", [(1, 3, 4, 16, 2, "f32", 1.0), (2, 8, 8, 32, 2, "f32", 0.3),
                                                   (2, 12, 12, 48, 3, "bf16", 0.3), (1, 6, 8, 64, 1, "f32", 1.0),
-                                                  (2, 16, 16, 64, 4, "bf16", 0.2)])
+                                                  (2, 16, 16, 64, 4, "bf16", 0.2), (2, 8, 8, 24, 4, "f32", 0.5),
+                                                  (1, 12, 12, 24, 2, "bf16", 0.3)])
 def test_forward_2d_small(cat, B, Hg, Wg, D, H, dtype, ss):
     say("forward_2d", B, Hg, Wg, D, H, dtype, ss)
     import torch

@@ -17,11 +17,12 @@
 // The filter spectrum is the column pass and the forward half of the row
 // pass applied to the softmax line, scaled by 1/L; the softmax is reduced
 // in chunks first, and the column pass normalises the logits as it loads
-// them.  Each short DFT runs as a
-// radix-2 Stockham transform in LDS (natural order in and out), several
-// lines per workgroup; all twiddles come from one table W_L^m, m < L,
-// computed in double precision on the host.  Two real channels ride in one
-// complex line, as in the single-workgroup convolution.
+// them.  Each short DFT runs as a Stockham transform in LDS (radix-4
+// stages, one radix-2 stage when log2 of its length is odd; natural order
+// in and out), several lines per workgroup; all twiddles come from one
+// table W_L^m, m < L, computed in double precision on the host.  Two real
+// channels ride in one complex line, as in the single-workgroup
+// convolution.
 //
 // Layouts: V is BLOCKED with 2 PB-channel groups ([BH][d/2/PB][N][PB]
 // complex, PB channel pairs per block); the intermediate A is

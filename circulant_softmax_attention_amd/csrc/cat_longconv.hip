@@ -268,6 +268,77 @@ __global__ __launch_bounds__(LTHR) void row_kernel(LongArgs a, int PB, float2* _
   }
 }
 
+// ---- register four-step transform of one line of M = MS^2 points, held
+// by MS lanes: lane t holds element ma MS + t in register ma (ma < MS).
+// DFT over ma in registers, twiddle W_M^(ka t), exchange through the
+// line's [MS][MS + 1] LDS tile, DFT over the other digit: lane t then holds
+// X[t + MS kb] in register kb.  That output layout is the input layout of
+// the next transform (high digit in the register), so a forward and an
+// inverse transform chain with no reordering.  xl: the line's LDS tile;
+// twm: W_M^e, e < M.  Ends with a barrier.
+template <int MS, bool INV>
+__device__ __forceinline__ void reg_fft(cf* x, int t, float2* xl, const float2* twm) {
+  constexpr int M = MS * MS;
+  Dft<MS, INV>::run(x);
+#pragma unroll
+  for (int ka = 1; ka < MS; ++ka) {
+    const float2 w = twm[(ka * t) & (M - 1)];
+    x[ka] = INV ? cmulc(x[ka], cfm(w.x, w.y)) : cmul(x[ka], cfm(w.x, w.y));
+  }
+#pragma unroll
+  for (int ka = 0; ka < MS; ++ka) xl[ka * (MS + 1) + t] = make_float2(x[ka].x, x[ka].y);
+  __syncthreads();
+#pragma unroll
+  for (int mb = 0; mb < MS; ++mb) {
+    const float2 v = xl[t * (MS + 1) + mb];
+    x[mb] = cfm(v.x, v.y);
+  }
+  __syncthreads();  // the tile may be reused
+  Dft<MS, INV>::run(x);
+}
+
+// ---- row pass on registers (L2 = MS^2), 128 threads: R = 128 / MS lines
+// (rows x pairs) per workgroup, lane r = tid % R of each line fastest so a
+// wave's loads and stores are contiguous.  MODE as row_kernel.
+template <int MODE, int MS>
+__global__ __launch_bounds__(128) void row_reg_kernel(LongArgs a, int PB, float2* __restrict__ A,
+                                                      float2* __restrict__ S) {
+  constexpr int M = MS * MS, R = 128 / MS, TP = MS * (MS + 1);
+  __shared__ float2 xb[R * TP];
+  __shared__ float2 twm[M];
+  const int L1 = 1 << a.logL1, L = L1 * M;
+  const int RB = R / PB;  // rows per workgroup
+  const int nblk = L1 / RB;
+  const int gl = blockIdx.x / nblk, k10 = (blockIdx.x - gl * nblk) * RB;
+  const size_t base = ((size_t)gl * L + (size_t)k10 * M) * PB;
+  const int r = threadIdx.x % R, t = threadIdx.x / R;
+  const int rr = r / PB, j = r - rr * PB;
+  for (int e = threadIdx.x; e < M; e += 128) twm[e] = a.tw[e * (L / M)];
+  cf x[MS];
+#pragma unroll
+  for (int ma = 0; ma < MS; ++ma) {
+    const float2 v = A[base + ((size_t)rr * M + ma * MS + t) * PB + j];
+    x[ma] = cfm(v.x, v.y);
+  }
+  __syncthreads();  // twiddles in LDS
+  float2* xl = xb + r * TP;
+  reg_fft<MS, false>(x, t, xl, twm);
+  if constexpr (MODE == 0) {
+    const float sc = 1.f / (float)L;
+#pragma unroll
+    for (int kb = 0; kb < MS; ++kb)
+      S[base + (size_t)rr * M + t + MS * kb] = make_float2(x[kb].x * sc, x[kb].y * sc);
+  } else {
+    const size_t sbase = (size_t)(gl / (a.pairs / PB)) * L + (size_t)(k10 + rr) * M;
+#pragma unroll
+    for (int kb = 0; kb < MS; ++kb) x[kb] = cmul(x[kb], *reinterpret_cast<const cf*>(&S[sbase + t + MS * kb]));
+    reg_fft<MS, true>(x, t, xl, twm);
+#pragma unroll
+    for (int nb = 0; nb < MS; ++nb)
+      A[base + ((size_t)rr * M + t + MS * nb) * PB + j] = make_float2(x[nb].x, x[nb].y);
+  }
+}
+
 // ---- inverse column pass: o[n1 L2 + n2][j] = IDFT_L1 over k1 of
 // A[gl][k1][n2][j] conj W_L^(k1 n2), written to O[b][n][h d + 2 (g PB + j) ..]
 // (storage element type DET), gl = bh (P / PB) + g.
@@ -331,7 +402,18 @@ hipError_t launch_longconv(int et, const LongArgs& a, const float* logits, const
   e = launch_k(col_fwd_kernel<2>, dim3((unsigned)colb_z), dim3(LTHR), 0, s, t[1], a, 1, (const void*)logits, Az,
                (const float2*)zc);
   if (e != hipSuccess) return e;
-  e = launch_k(row_kernel<0>, dim3((unsigned)rowb_z), dim3(LTHR), 0, s, t[2], a, 1, Az, S);
+  // row passes on registers when L2 is a square of 8 or 16 (R = 128 / sqrt(L2) lines per workgroup)
+  const int ms = L2 == 256 ? 16 : L2 == 64 ? 8 : 0;
+  const int rl = ms ? 128 / ms : 0;
+  if (ms) {
+    const long rz = (long)a.BH * (L1 / rl);
+    if (ms == 16)
+      e = launch_k(row_reg_kernel<0, 16>, dim3((unsigned)rz), dim3(128), 0, s, t[2], a, 1, Az, S);
+    else
+      e = launch_k(row_reg_kernel<0, 8>, dim3((unsigned)rz), dim3(128), 0, s, t[2], a, 1, Az, S);
+  } else {
+    e = launch_k(row_kernel<0>, dim3((unsigned)rowb_z), dim3(LTHR), 0, s, t[2], a, 1, Az, S);
+  }
   if (e != hipSuccess) return e;
   // the mixing, PB pairs per block
   if (et == ET_F32)
@@ -341,7 +423,15 @@ hipError_t launch_longconv(int et, const LongArgs& a, const float* logits, const
     e = launch_k(col_fwd_kernel<ET_BF16>, dim3((unsigned)colb), dim3(LTHR), 0, s, t[3], a, PB, V, A,
                  (const float2*)nullptr);
   if (e != hipSuccess) return e;
-  e = launch_k(row_kernel<1>, dim3((unsigned)rowb), dim3(LTHR), 0, s, t[4], a, PB, A, S);
+  if (ms) {
+    const long rv = blocks * (L1 / (rl / PB));
+    if (ms == 16)
+      e = launch_k(row_reg_kernel<1, 16>, dim3((unsigned)rv), dim3(128), 0, s, t[4], a, PB, A, S);
+    else
+      e = launch_k(row_reg_kernel<1, 8>, dim3((unsigned)rv), dim3(128), 0, s, t[4], a, PB, A, S);
+  } else {
+    e = launch_k(row_kernel<1>, dim3((unsigned)rowb), dim3(LTHR), 0, s, t[4], a, PB, A, S);
+  }
   if (e != hipSuccess) return e;
   if (et == ET_F32)
     return launch_k(col_inv_kernel<ET_F32>, dim3((unsigned)colb), dim3(LTHR), 0, s, t[5], a, PB, (const float2*)A, O);

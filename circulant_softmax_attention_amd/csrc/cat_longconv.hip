@@ -339,6 +339,103 @@ __global__ __launch_bounds__(128) void row_reg_kernel(LongArgs a, int PB, float2
   }
 }
 
+// ---- column passes on registers (L1 = MS^2), 128 threads: R = 128 / MS
+// lines (CB = R / PB columns x PB pairs) per workgroup, lane r fastest.
+// Forward: SET as col_fwd_kernel.  Lane t of line r = c PB + j holds
+// x[(ma MS + t) L2 + n20 + c][j] in register ma; after the transform it
+// holds k1 = t + MS kb in register kb.
+template <int SET, int MS>
+__global__ __launch_bounds__(128) void col_reg_kernel(LongArgs a, int PB, const void* __restrict__ src,
+                                                      float2* __restrict__ A, const float2* __restrict__ smpart) {
+  constexpr int M = MS * MS, R = 128 / MS, TP = MS * (MS + 1);
+  __shared__ float2 xb[R * TP];
+  __shared__ float2 twm[M];
+  __shared__ float2 msum;
+  const int L2 = 1 << a.logL2, L = M * L2;
+  const int CB = R / PB;
+  const int nblk = L2 / CB;
+  const int gl = blockIdx.x / nblk, n20 = (blockIdx.x - gl * nblk) * CB;
+  const size_t gbase = (size_t)gl * L * PB;
+  const int r = threadIdx.x % R, t = threadIdx.x / R;
+  const int c = r / PB;
+  for (int e = threadIdx.x; e < M; e += 128) twm[e] = a.tw[e * (L / M)];
+  if constexpr (SET == 2) {
+    const int nc = L / SMC;
+    if (threadIdx.x < 64) {
+      float2 p = threadIdx.x < nc ? smpart[(size_t)gl * nc + threadIdx.x] : make_float2(-INFINITY, 0.f);
+      float m = p.x;
+      for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+      float sv = threadIdx.x < nc ? p.y * __expf(p.x - m) : 0.f;
+      for (int o = 32; o >= 1; o >>= 1) sv += __shfl_xor(sv, o, 64);
+      if (threadIdx.x == 0) msum = make_float2(m, 1.f / sv);
+    }
+  }
+  __syncthreads();  // twiddles (and the softmax constants) in LDS
+  cf x[MS];
+#pragma unroll
+  for (int ma = 0; ma < MS; ++ma) {
+    const size_t i = gbase + ((size_t)(ma * MS + t) * L2 + n20) * PB + r;
+    float2 v;
+    if constexpr (SET == 2)
+      v = make_float2(__expf(reinterpret_cast<const float*>(src)[i] - msum.x) * msum.y, 0.f);
+    else
+      v = load_c<SET>(src, i);
+    x[ma] = cfm(v.x, v.y);
+  }
+  reg_fft<MS, false>(x, t, xb + r * TP, twm);
+  const int n2 = n20 + c;
+#pragma unroll
+  for (int kb = 0; kb < MS; ++kb) {
+    const int k1 = t + MS * kb;
+    const float2 w = a.tw[(k1 * n2) & (L - 1)];
+    const cf y = cmul(x[kb], cfm(w.x, w.y));
+    A[gbase + ((size_t)k1 * L2 + n20) * PB + r] = make_float2(y.x, y.y);
+  }
+}
+
+// Inverse column pass on registers: lane t of line r holds
+// A[k1][n2][j] conj W_L^(k1 n2) for k1 = ma MS + t in register ma; after the
+// inverse transform it holds n1 = t + MS nb in register nb, written to O.
+template <int DET, int MS>
+__global__ __launch_bounds__(128) void col_inv_reg_kernel(LongArgs a, int PB, const float2* __restrict__ A,
+                                                          void* __restrict__ O) {
+  constexpr int M = MS * MS, R = 128 / MS, TP = MS * (MS + 1);
+  __shared__ float2 xb[R * TP];
+  __shared__ float2 twm[M];
+  const int L2 = 1 << a.logL2, L = M * L2;
+  const int CB = R / PB;
+  const int nblk = L2 / CB;
+  const int gl = blockIdx.x / nblk, n20 = (blockIdx.x - gl * nblk) * CB;
+  const size_t gbase = (size_t)gl * L * PB;
+  const int r = threadIdx.x % R, t = threadIdx.x / R;
+  const int c = r / PB, j = r - c * PB;
+  const int n2 = n20 + c;
+  for (int e = threadIdx.x; e < M; e += 128) twm[e] = a.tw[e * (L / M)];
+  cf x[MS];
+#pragma unroll
+  for (int ma = 0; ma < MS; ++ma) {
+    const int k1 = ma * MS + t;
+    const float2 v = A[gbase + ((size_t)k1 * L2 + n20) * PB + r];
+    const float2 w = a.tw[(k1 * n2) & (L - 1)];
+    x[ma] = cmulc(cfm(v.x, v.y), cfm(w.x, w.y));
+  }
+  __syncthreads();  // twiddles in LDS
+  reg_fft<MS, true>(x, t, xb + r * TP, twm);
+  const int groups = a.pairs / PB;
+  const int bh = gl / groups, g = gl - bh * groups;
+  const int b = bh / a.H, h = bh - b * a.H;
+  const size_t obase = (size_t)b * L * a.D + (size_t)h * a.d + 2 * ((size_t)g * PB + j);
+#pragma unroll
+  for (int nb = 0; nb < MS; ++nb) {
+    const size_t n = (size_t)(t + MS * nb) * L2 + n2;
+    if constexpr (DET == ET_F32) {
+      *reinterpret_cast<float2*>(reinterpret_cast<float*>(O) + obase + n * a.D) = make_float2(x[nb].x, x[nb].y);
+    } else {
+      *reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(O) + obase + n * a.D) = pack_bf16x2(x[nb].x, x[nb].y);
+    }
+  }
+}
+
 // ---- inverse column pass: o[n1 L2 + n2][j] = IDFT_L1 over k1 of
 // A[gl][k1][n2][j] conj W_L^(k1 n2), written to O[b][n][h d + 2 (g PB + j) ..]
 // (storage element type DET), gl = bh (P / PB) + g.
@@ -399,8 +496,21 @@ hipError_t launch_longconv(int et, const LongArgs& a, const float* logits, const
   // the normalised line, straight from the logits, then the rows
   hipError_t e = launch_k(softmax_part_kernel, dim3((unsigned)(a.BH * (N / SMC))), dim3(LTHR), 0, s, t[0], logits, zc, N);
   if (e != hipSuccess) return e;
-  e = launch_k(col_fwd_kernel<2>, dim3((unsigned)colb_z), dim3(LTHR), 0, s, t[1], a, 1, (const void*)logits, Az,
-               (const float2*)zc);
+  // column passes on registers when L1 is a square of 8 or 16 (C = 128 / sqrt(L1) lines per workgroup)
+  const int mc = L1 == 256 ? 16 : L1 == 64 ? 8 : 0;
+  const int cl = mc ? 128 / mc : 0;
+  if (mc) {
+    const long cz = (long)a.BH * (L2 / cl);
+    if (mc == 16)
+      e = launch_k(col_reg_kernel<2, 16>, dim3((unsigned)cz), dim3(128), 0, s, t[1], a, 1, (const void*)logits, Az,
+                   (const float2*)zc);
+    else
+      e = launch_k(col_reg_kernel<2, 8>, dim3((unsigned)cz), dim3(128), 0, s, t[1], a, 1, (const void*)logits, Az,
+                   (const float2*)zc);
+  } else {
+    e = launch_k(col_fwd_kernel<2>, dim3((unsigned)colb_z), dim3(LTHR), 0, s, t[1], a, 1, (const void*)logits, Az,
+                 (const float2*)zc);
+  }
   if (e != hipSuccess) return e;
   // row passes on registers when L2 is a square of 8 or 16 (R = 128 / sqrt(L2) lines per workgroup)
   const int ms = L2 == 256 ? 16 : L2 == 64 ? 8 : 0;
@@ -416,7 +526,18 @@ hipError_t launch_longconv(int et, const LongArgs& a, const float* logits, const
   }
   if (e != hipSuccess) return e;
   // the mixing, PB pairs per block
-  if (et == ET_F32)
+  const long cv = mc ? blocks * (L2 / (cl / PB)) : 0;
+  if (mc == 16)
+    e = et == ET_F32 ? launch_k(col_reg_kernel<ET_F32, 16>, dim3((unsigned)cv), dim3(128), 0, s, t[3], a, PB, V, A,
+                                (const float2*)nullptr)
+                     : launch_k(col_reg_kernel<ET_BF16, 16>, dim3((unsigned)cv), dim3(128), 0, s, t[3], a, PB, V, A,
+                                (const float2*)nullptr);
+  else if (mc == 8)
+    e = et == ET_F32 ? launch_k(col_reg_kernel<ET_F32, 8>, dim3((unsigned)cv), dim3(128), 0, s, t[3], a, PB, V, A,
+                                (const float2*)nullptr)
+                     : launch_k(col_reg_kernel<ET_BF16, 8>, dim3((unsigned)cv), dim3(128), 0, s, t[3], a, PB, V, A,
+                                (const float2*)nullptr);
+  else if (et == ET_F32)
     e = launch_k(col_fwd_kernel<ET_F32>, dim3((unsigned)colb), dim3(LTHR), 0, s, t[3], a, PB, V, A,
                  (const float2*)nullptr);
   else
@@ -433,6 +554,16 @@ hipError_t launch_longconv(int et, const LongArgs& a, const float* logits, const
     e = launch_k(row_kernel<1>, dim3((unsigned)rowb), dim3(LTHR), 0, s, t[4], a, PB, A, S);
   }
   if (e != hipSuccess) return e;
+  if (mc == 16)
+    return et == ET_F32 ? launch_k(col_inv_reg_kernel<ET_F32, 16>, dim3((unsigned)cv), dim3(128), 0, s, t[5], a, PB,
+                                   (const float2*)A, O)
+                        : launch_k(col_inv_reg_kernel<ET_BF16, 16>, dim3((unsigned)cv), dim3(128), 0, s, t[5], a, PB,
+                                   (const float2*)A, O);
+  if (mc == 8)
+    return et == ET_F32 ? launch_k(col_inv_reg_kernel<ET_F32, 8>, dim3((unsigned)cv), dim3(128), 0, s, t[5], a, PB,
+                                   (const float2*)A, O)
+                        : launch_k(col_inv_reg_kernel<ET_BF16, 8>, dim3((unsigned)cv), dim3(128), 0, s, t[5], a, PB,
+                                   (const float2*)A, O);
   if (et == ET_F32)
     return launch_k(col_inv_kernel<ET_F32>, dim3((unsigned)colb), dim3(LTHR), 0, s, t[5], a, PB, (const float2*)A, O);
   return launch_k(col_inv_kernel<ET_BF16>, dim3((unsigned)colb), dim3(LTHR), 0, s, t[5], a, PB, (const float2*)A, O);

@@ -201,11 +201,13 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
   const size_t line_bytes = longn ? 0 : line_lds_bytes(g);
   const int d2 = (int)d / 2;
   // lines per transform workgroup: power of two dividing d/2, <= 256 threads
+  // (the long path instead takes pair blocks: the largest power of two <= 8 dividing d/2)
   int G = 1;
   const size_t lds_cap = p->kind == CAT_1D ? 96 * 1024 : 152 * 1024;
-  while (G < 8 && d2 % (2 * G) == 0 && (2 * G) * T <= 256 && (2 * G) * line_bytes <= lds_cap) G *= 2;
-  pl->G = G;
-  pl->ng = d2 / G;
+  if (longn)
+    while (G < 8 && d2 % (2 * G) == 0) G *= 2;
+  else
+    while (G < 8 && d2 % (2 * G) == 0 && (2 * G) * T <= 256 && (2 * G) * line_bytes <= lds_cap) G *= 2;
   {
     const char* cv = std::getenv("CAT_CONV");
     const bool force_valu = cv && std::strcmp(cv, "valu") == 0;
@@ -213,10 +215,6 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
     pl->direct = !force_fft && p->kind == CAT_1D && p->dtype == CAT_BF16 && p->N <= 256 && d % 32 == 0;
     pl->mconv = !longn && !pl->direct && !force_valu && p->kind == CAT_1D && p->dtype == CAT_BF16 &&
                 g.L1 * g.L2 == 1024 && d % 16 == 0;
-    if (longn) {  // pair blocks of the long path: the largest power of two <= 8 dividing d/2
-      G = 1;
-      while (G < 8 && d2 % (2 * G) == 0) G *= 2;
-    }
     pl->G = G;
     pl->ng = d2 / G;
     pl->cg = pl->direct ? 32 : pl->mconv ? 16 : 2 * G;

@@ -25,7 +25,7 @@ struct cat_plan_s {
   int ng;            // line groups per head (d / 2 / G)
   bool mconv;        // 1D conv on the matrix cores (L = 1024, bf16, d % 16 == 0)
   bool direct;       // 1D direct circulant product on the matrix cores (bf16, N <= 256, d % 32 == 0)
-  bool longn;        // 1D power-of-two N beyond one workgroup's line: three passes over HBM
+  bool longn;        // 1D N beyond one workgroup's line: three passes over HBM
   int logL1, logL2;  // long path: L = 2^logL1 x 2^logL2
   int cg;            // channels per group of the blocked V (2 G; 16 for mconv, 32 for direct)
   int Gs;            // lines per spectrum workgroup
@@ -155,11 +155,15 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
     return fail(CAT_ERR_UNSUPPORTED, "1D supports at most 32 heads (score projection fused into the GEMM)");
 
   LineGeom g{};
-  const bool longn = p->kind == CAT_1D && is_pow2(p->N) && p->N > 4096 && p->N <= 65536;
+  // beyond one workgroup's line: a power-of-two N up to 65536 (L = N), or
+  // any other N up to 32768 on the power-of-two circle L >= 2N - 1
+  const bool longn = p->kind == CAT_1D && ((is_pow2(p->N) && p->N > 4096 && p->N <= 65536) ||
+                                           (!is_pow2(p->N) && p->N > 2048 && p->N <= 32768));
   if (longn) {
-    // three passes over HBM, L = N = L1 x L2 (L1 >= L2)
+    // three passes over HBM, L = L1 x L2 (L1 >= L2)
+    const int64_t Lmin = is_pow2(p->N) ? p->N : 2 * p->N - 1;
     int e = 0;
-    while ((int64_t(1) << e) < p->N) ++e;
+    while ((int64_t(1) << e) < Lmin) ++e;
     g.L1 = 1 << ((e + 1) / 2);
     g.L2 = 1 << (e / 2);
     g.twiddled = 1;
@@ -172,7 +176,7 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
       while (L < 2 * p->N - 1) L <<= 1;
     } else {
       return fail(CAT_ERR_UNSUPPORTED,
-                  "1D N beyond the supported lengths (powers of two up to 65536, other N up to 2048)");
+                  "1D N beyond the supported lengths (powers of two up to 65536, other N up to 32768)");
     }
     split_pow2(L, &g.L1, &g.L2);
     g.twiddled = 1;
@@ -468,6 +472,7 @@ LongArgs long_base(const cat_plan_s* pl) {
   a.logL2 = pl->logL2;
   a.BH = (int)(pl->p.B * pl->p.H);
   a.pairs = pl->d / 2;
+  a.N = (int)pl->p.N;
   a.H = (int)pl->p.H;
   a.D = (int)pl->p.D;
   a.d = pl->d;
@@ -634,7 +639,7 @@ cat_status cat_step_spectrum(cat_plan plan, const float* logits, float* probs, f
   cat_status st = check_ptrs({logits, spec});
   if (st != CAT_OK) return st;
   if (probs && !aligned16(probs)) return fail(CAT_ERR_INVALID_ARG, "probs not 16-byte aligned");
-  if (plan->longn) return fail(CAT_ERR_UNSUPPORTED, "the spectrum step covers single-workgroup lines (N <= 4096)");
+  if (plan->longn) return fail(CAT_ERR_UNSUPPORTED, "the spectrum step covers single-workgroup lines (the multi-pass path keeps its spectrum internal)");
   SpecArgs a{};
   a.logits = logits;
   a.probs = probs;

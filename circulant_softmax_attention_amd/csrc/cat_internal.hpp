@@ -174,17 +174,19 @@ hipError_t launch_mconv(const ConvArgs& a, hipStream_t s, const LaunchTiming* t 
 hipError_t launch_dconv(int et, const ConvArgs& a, hipStream_t s, const LaunchTiming* t = nullptr);
 hipError_t launch_score_partial(const LineGeom& g, const ScoreArgs& a, hipStream_t s,
                                 const LaunchTiming* t = nullptr);
-// 1D mixing for power-of-two N = L1 L2 beyond one workgroup's line
-// (three passes over HBM; see cat_longconv.hip).
+// 1D mixing for N beyond one workgroup's line, on a transform of length
+// L = L1 L2 (three passes over HBM; see cat_longconv.hip): L = N for a
+// power-of-two N, else a power of two >= 2N - 1.
 struct LongArgs {
-  const float2* tw;  // W_L^m, m < L (L = N)
+  const float2* tw;  // W_L^m, m < L
   int logL1, logL2;  // L1 = 2^logL1 (column DFTs), L2 = 2^logL2 (row DFTs)
   int BH, pairs;     // (batch, head) lines and channel pairs per head (d / 2)
+  int N;             // tokens per line (N == L, or 2N - 1 <= L)
   int H, D, d;
   int pb;            // channel pairs per block of V and of the intermediates (1, 2, 4 or 8; divides pairs)
 };
 // Launches, in order: softmax chunk partials, column pass and row pass of
-// the filter spectrum (zc: partials scratch, at least [BH][N / 1024] complex;
+// the filter spectrum (zc: partials scratch, at least [BH][ceil(N / 1024)] complex;
 // Az: [BH][L] complex fp32 scratch; S: [BH][L] spectrum), then
 // column pass, row pass with the spectrum product, inverse column pass of
 // the values (V BLOCKED with 2 pb-channel groups, A: [BH d/2][L] complex

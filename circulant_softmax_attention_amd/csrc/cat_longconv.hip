@@ -1,12 +1,17 @@
 // cat_longconv.hip -- the 1D circulant mixing for sequences longer than one
-// workgroup's transform line (power-of-two N, 4096 < N <= 65536).
+// workgroup's transform line (power-of-two N with 4096 < N <= 65536, other
+// N with 2048 < N <= 32768).
 //
 // CAT evaluates O_h = circ(z*_h) V_h as IFFT(FFT(z*_h) . FFT(V_h)) along the
 // tokens (CAT: Circular-Convolutional Attention for Sub-Quadratic
 // Transformers, "Key designs: FFT-accelerated computation"); the page names
 // sequences beyond 10^4 tokens as where that O(N log N) route should pay.
 // A length L = L1 L2 transform does not fit one workgroup here, so it runs
-// as three passes over HBM (four-step FFT), with L = N:
+// as three passes over HBM (four-step FFT), with L = N for a power-of-two
+// N.  Any other N runs exactly on a power-of-two circle L >= 2N - 1: the
+// values are zero-padded to L, the softmax line is wrapped (entry j < N at
+// j, entry N - m at L - m for 0 < m < N, zeros between), and the first N
+// outputs of the length-L circular product are the length-N ones:
 //
 //   column pass   for each n2: A[k1][n2] = W_L^(k1 n2) sum_n1 x[n1 L2 + n2] W_L1^(n1 k1)
 //   row pass      for each k1: X[k1 + L1 k2] = sum_n2 A[k1][n2] W_L2^(n2 k2);
@@ -25,7 +30,7 @@
 // convolution.
 //
 // Layouts: V is BLOCKED with 2 PB-channel groups ([BH][d/2/PB][N][PB]
-// complex, PB channel pairs per block); the intermediate A is
+// complex, PB channel pairs per block); O is [B][N][D]; the intermediate A is
 // [BH][d/2/PB][L1][L2][PB] complex fp32; the spectrum S is [BH][L1][L2]
 // complex fp32 (entry k1 L2 + k2 holds frequency k1 + L1 k2).
 #include "cat_common.hpp"
@@ -132,19 +137,30 @@ __device__ __forceinline__ float2 load_c(const void* base, size_t i) {
   }
 }
 
-// ---- softmax partials: chunk c (SMC logits) of line bh -> (max m_c,
-// sum exp(z - m_c)); the column pass of the spectrum combines the chunks of
-// its line and normalises on the fly.
+// Entry j of the softmax line on the transform circle: the line itself when
+// L = N; otherwise its wrapped extension (z*[j] for j < N, z*[j - (L - N)]
+// for j > L - N, zero between; L >= 2N - 1 keeps the two ranges apart).
+// zl: the line's logits; ms: (max, 1 / sum of exp).
+__device__ __forceinline__ float circle_score(const float* __restrict__ zl, int j, int N, int L, float2 ms) {
+  const int n = j < N ? j : j > L - N ? j - (L - N) : -1;
+  return n < 0 ? 0.f : __expf(zl[n] - ms.x) * ms.y;
+}
+
+// ---- softmax partials: chunk c (SMC logits, the last one ragged) of line
+// bh -> (max m_c, sum exp(z - m_c)); the column pass of the spectrum
+// combines the chunks of its line and normalises on the fly.
 constexpr int SMC = 1024;
+__host__ __device__ constexpr int smc_chunks(int N) { return (N + SMC - 1) / SMC; }
 __global__ __launch_bounds__(LTHR) void softmax_part_kernel(const float* __restrict__ z, float2* __restrict__ part,
                                                             int N) {
   __shared__ float red[LTHR / 64];
-  const int nc = N / SMC;
+  const int nc = smc_chunks(N);
   const int bh = blockIdx.x / nc, c = blockIdx.x - bh * nc, tid = threadIdx.x;
   const float* zr = z + (size_t)bh * N + (size_t)c * SMC;
+  const int len = N - c * SMC;  // >= 1; entries past it are -inf and add nothing
   float v[SMC / LTHR];
 #pragma unroll
-  for (int i = 0; i < SMC / LTHR; ++i) v[i] = zr[tid + LTHR * i];
+  for (int i = 0; i < SMC / LTHR; ++i) v[i] = tid + LTHR * i < len ? zr[tid + LTHR * i] : -INFINITY;
   auto reduce = [&](float x, bool is_max) {
     for (int o = 32; o >= 1; o >>= 1) {
       const float p = __shfl_xor(x, o, 64);
@@ -193,7 +209,7 @@ __global__ __launch_bounds__(LTHR) void col_fwd_kernel(LongArgs a, int PB, const
   if constexpr (SET == 2) {
     // softmax of the line from its chunk partials: m = max m_c,
     // s = sum s_c exp(m_c - m); one wave combines them
-    const int nc = L / SMC;
+    const int nc = smc_chunks(a.N);
     if (threadIdx.x < 64) {
       float2 p = threadIdx.x < nc ? smpart[(size_t)gl * nc + threadIdx.x] : make_float2(-INFINITY, 0.f);
       float m = p.x;
@@ -208,11 +224,13 @@ __global__ __launch_bounds__(LTHR) void col_fwd_kernel(LongArgs a, int PB, const
   // buf[0][r (L1 + 1) + n1]; consecutive threads read consecutive memory
   for (int q = threadIdx.x; q < R * L1; q += LTHR) {
     const int n1 = q / R, r = q - n1 * R;
-    const size_t i = gbase + ((size_t)n1 * L2 + n20) * PB + r;
+    const int j = n1 * L2 + n20 + r / PB;  // position on the circle
     if constexpr (SET == 2)
-      buf[0][r * (L1 + 1) + n1] = make_float2(__expf(reinterpret_cast<const float*>(src)[i] - msum.x) * msum.y, 0.f);
+      buf[0][r * (L1 + 1) + n1] =
+          make_float2(circle_score(reinterpret_cast<const float*>(src) + (size_t)gl * a.N, j, a.N, L, msum), 0.f);
     else
-      buf[0][r * (L1 + 1) + n1] = load_c<SET>(src, i);
+      buf[0][r * (L1 + 1) + n1] = j < a.N ? load_c<SET>(src, (size_t)gl * a.N * PB + ((size_t)n1 * L2 + n20) * PB + r)
+                                          : make_float2(0.f, 0.f);
   }
   stage_twiddles(tws, a.logL1, a.tw, a.logL1 + a.logL2);
   const float2* U = lds_fft<false>(buf[0], buf[1], L1, a.logL1, R, tws);
@@ -360,7 +378,7 @@ __global__ __launch_bounds__(128) void col_reg_kernel(LongArgs a, int PB, const 
   const int c = r / PB;
   for (int e = threadIdx.x; e < M; e += 128) twm[e] = a.tw[e * (L / M)];
   if constexpr (SET == 2) {
-    const int nc = L / SMC;
+    const int nc = smc_chunks(a.N);
     if (threadIdx.x < 64) {
       float2 p = threadIdx.x < nc ? smpart[(size_t)gl * nc + threadIdx.x] : make_float2(-INFINITY, 0.f);
       float m = p.x;
@@ -374,12 +392,12 @@ __global__ __launch_bounds__(128) void col_reg_kernel(LongArgs a, int PB, const 
   cf x[MS];
 #pragma unroll
   for (int ma = 0; ma < MS; ++ma) {
-    const size_t i = gbase + ((size_t)(ma * MS + t) * L2 + n20) * PB + r;
+    const int n = (ma * MS + t) * L2 + n20;
     float2 v;
     if constexpr (SET == 2)
-      v = make_float2(__expf(reinterpret_cast<const float*>(src)[i] - msum.x) * msum.y, 0.f);
+      v = make_float2(circle_score(reinterpret_cast<const float*>(src) + (size_t)gl * a.N, n + c, a.N, L, msum), 0.f);
     else
-      v = load_c<SET>(src, i);
+      v = n + c < a.N ? load_c<SET>(src, (size_t)gl * a.N * PB + (size_t)n * PB + r) : make_float2(0.f, 0.f);
     x[ma] = cfm(v.x, v.y);
   }
   reg_fft<MS, false>(x, t, xb + r * TP, twm);
@@ -424,10 +442,11 @@ __global__ __launch_bounds__(128) void col_inv_reg_kernel(LongArgs a, int PB, co
   const int groups = a.pairs / PB;
   const int bh = gl / groups, g = gl - bh * groups;
   const int b = bh / a.H, h = bh - b * a.H;
-  const size_t obase = (size_t)b * L * a.D + (size_t)h * a.d + 2 * ((size_t)g * PB + j);
+  const size_t obase = (size_t)b * a.N * a.D + (size_t)h * a.d + 2 * ((size_t)g * PB + j);
 #pragma unroll
   for (int nb = 0; nb < MS; ++nb) {
-    const size_t n = (size_t)(t + MS * nb) * L2 + n2;
+    const int n = (t + MS * nb) * L2 + n2;
+    if (n >= a.N) continue;  // past the line: the padded circle's tail
     if constexpr (DET == ET_F32) {
       *reinterpret_cast<float2*>(reinterpret_cast<float*>(O) + obase + n * a.D) = make_float2(x[nb].x, x[nb].y);
     } else {
@@ -460,11 +479,12 @@ __global__ __launch_bounds__(LTHR) void col_inv_kernel(LongArgs a, int PB, const
   const int groups = a.pairs / PB;
   const int bh = gl / groups, g = gl - bh * groups;
   const int b = bh / a.H, h = bh - b * a.H;
-  const size_t obase = (size_t)b * L * a.D + (size_t)h * a.d + 2 * (size_t)g * PB;
+  const size_t obase = (size_t)b * a.N * a.D + (size_t)h * a.d + 2 * (size_t)g * PB;
   for (int q = threadIdx.x; q < R * L1; q += LTHR) {
     const int n1 = q / R, r = q - n1 * R;
     const int c = r / PB, j = r - c * PB;
-    const size_t n = (size_t)n1 * L2 + n20 + c;
+    const int n = n1 * L2 + n20 + c;
+    if (n >= a.N) continue;  // past the line: the padded circle's tail
     const float2 v = U[r * (L1 + 1) + n1];
     if constexpr (DET == ET_F32) {
       *reinterpret_cast<float2*>(reinterpret_cast<float*>(O) + obase + n * a.D + 2 * j) = v;
@@ -480,21 +500,22 @@ hipError_t launch_longconv(int et, const LongArgs& a, const float* logits, const
                            float2* S, float2* A, void* O, hipStream_t s, const LaunchTiming* const* t) {
   const LaunchTiming* none[6] = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
   if (!t) t = none;
-  const int L1 = 1 << a.logL1, L2 = 1 << a.logL2, N = L1 * L2, PB = a.pb;
+  const int L1 = 1 << a.logL1, L2 = 1 << a.logL2, L = L1 * L2, N = a.N, PB = a.pb;
   if (a.logL1 < 1 || a.logL2 < 1 || L1 > LMAXM || L2 > LMAXM || a.pairs < 1 || a.BH < 1) return hipErrorInvalidValue;
   if (PB < 1 || PB > 8 || (PB & (PB - 1)) != 0 || a.pairs % PB != 0) return hipErrorInvalidValue;
   // lines per workgroup (CB PB columns, RB PB rows) stay within the LDS pad
   const int cb1 = LBUF / L1 < L2 ? LBUF / L1 : L2, rb1 = LBUF / L2 < L1 ? LBUF / L2 : L1;
   const int cb = LBUF / (PB * L1) < L2 ? LBUF / (PB * L1) : L2, rb = LBUF / (PB * L2) < L1 ? LBUF / (PB * L2) : L1;
   if (cb < 1 || rb < 1 || cb1 > 64 || rb1 > 64 || cb * PB > 64 || rb * PB > 64) return hipErrorInvalidValue;
-  if (N % SMC != 0 || N / SMC > 64) return hipErrorInvalidValue;
+  // the line fills the circle, or fits on it twice less one (the wrapped product)
+  if (N < 1 || (N != L && 2 * N - 1 > L) || smc_chunks(N) > 64) return hipErrorInvalidValue;
   const long blocks = (long)a.BH * (a.pairs / PB);
   const long colb_z = (long)a.BH * (L2 / cb1), rowb_z = (long)a.BH * (L1 / rb1);
   const long colb = blocks * (L2 / cb), rowb = blocks * (L1 / rb);
   if (colb > 0x7fffffffL || rowb > 0x7fffffffL) return hipErrorInvalidValue;
   // the filter spectrum: softmax partials (in zc), then the column pass of
   // the normalised line, straight from the logits, then the rows
-  hipError_t e = launch_k(softmax_part_kernel, dim3((unsigned)(a.BH * (N / SMC))), dim3(LTHR), 0, s, t[0], logits, zc, N);
+  hipError_t e = launch_k(softmax_part_kernel, dim3((unsigned)(a.BH * smc_chunks(N))), dim3(LTHR), 0, s, t[0], logits, zc, N);
   if (e != hipSuccess) return e;
   // column passes on registers when L1 is a square of 8 or 16 (C = 128 / sqrt(L1) lines per workgroup)
   const int mc = L1 == 256 ? 16 : L1 == 64 ? 8 : 0;

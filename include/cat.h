@@ -91,11 +91,12 @@ typedef enum { CAT_1D = 0, CAT_BCCB_2D = 1 } cat_kind;
  * Requirements: B >= 0 (B = 0 makes every forward call a no-op), N, D,
  * H >= 1; D % H == 0; d = D / H even; D % 8 == 0; B * N * D < 2^31.
  * Supported sizes (else CAT_ERR_UNSUPPORTED):
- *   1D: H <= 32; N a power of two up to 65536 (beyond 4096 by three passes
- *       over HBM, see cat_plan_conv_path), or any other N up to 2048 (the
- *       circular convolution of length N is evaluated exactly on a
+ *   1D: H <= 32; N a power of two up to 65536, or any other N up to 32768
+ *       (the circular convolution of length N is evaluated exactly on a
  *       power-of-two circle of length L >= 2N - 1, the values zero-extended
- *       and the softmaxed scores periodically extended);
+ *       and the softmaxed scores periodically extended); a power-of-two N
+ *       beyond 4096, and any other N beyond 2048, by three passes over HBM
+ *       (see cat_plan_conv_path);
  *   2D: grids 1x1, 2x3, 3x4, 4x4, 6x8, 8x8, 12x12, 16x16, 32x32, 96x96. */
 typedef struct {
   int32_t kind;  /* cat_kind */
@@ -131,7 +132,8 @@ cat_status cat_plan_geometry(cat_plan plan, int64_t* L, int64_t* L1, int64_t* L2
  *                           cores, softmax in the same launch (CAT, "Key
  *                           designs: circulant attention matrix
  *                           construction").
- *   CAT_PATH_FFT_MULTIPASS (3) 1D, power-of-two N in (4096, 65536]: the
+ *   CAT_PATH_FFT_MULTIPASS (3) 1D, power-of-two N in (4096, 65536] or
+ *                           other N in (2048, 32768]: the
  *                           transform does not fit one workgroup; column,
  *                           row and inverse column passes over HBM (CAT,
  *                           "Key designs: FFT-accelerated computation";
@@ -188,7 +190,8 @@ cat_status cat_step_project(cat_plan plan, const void* X, const void* W_A, const
  * (may be NULL); spec [B][H][L] complex fp32 (interleaved re, im) receives
  * FFT_L of the (extended) softmax times 1/L in the kernels' spectral order
  * k1 + L1 k2 with natural frequency k1 + L1 k2 in 1D and (k_r = k1,
- * k_c = k2) on a 2D grid. */
+ * k_c = k2) on a 2D grid.  Plans on CAT_PATH_FFT_MULTIPASS return
+ * CAT_ERR_UNSUPPORTED (their spectrum lives only inside cat_step_mix). */
 cat_status cat_step_spectrum(cat_plan plan, const float* logits, float* probs, float* spec,
                              void* stream);
 

@@ -60,9 +60,9 @@ def _create(**kw):
     (dict(D=36, H=2), -1),        # D % 8 != 0
     (dict(kind=cat.CAT_BCCB_2D, N=64, Hg=8, Wg=7), -1),  # Hg*Wg != N
     (dict(kind=cat.CAT_BCCB_2D, N=35, Hg=5, Wg=7), -2),  # grid not instantiated
-    (dict(N=3000), -2),           # non-power-of-two beyond 2048
+    (dict(N=32769), -2),          # non-power-of-two beyond 32768
     (dict(N=131072), -2),         # power of two beyond 65536
-    (dict(N=6000), -2),           # non-power-of-two beyond 2048
+    (dict(N=40000), -2),          # non-power-of-two beyond 32768
     (dict(D=1024, H=64), -2),     # 1D with more than 32 heads
     (dict(B=1 << 20, N=4096, D=1024), -2),  # B*N*D >= 2^31
 ])

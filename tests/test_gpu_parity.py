@@ -210,7 +210,8 @@ def test_mix_1d_direct(cat, monkeypatch, conv, B, N, D, H, dtype, vscale, lscale
     (64, 64, 4, "f32", "fft_valu"), (256, 64, 2, "f32", "fft_valu"),
     (257, 64, 1, "bf16", "fft_matrix"), (1024, 768, 12, "bf16", "fft_matrix"), (1024, 768, 12, "f32", "fft_valu"),
     (256, 96, 2, "f32", "fft_valu"), (128, 64, 1, "bf16", "direct"), (8192, 64, 2, "bf16", "fft_multipass"),
-    (65536, 16, 1, "f32", "fft_multipass")])
+    (65536, 16, 1, "f32", "fft_multipass"), (2047, 64, 1, "f32", "fft_valu"), (4096, 64, 1, "bf16", "fft_valu"),
+    (2049, 64, 1, "f32", "fft_multipass"), (32767, 16, 1, "bf16", "fft_multipass")])
 def test_conv_path_choice(cat, N, D, H, dtype, path):
     """Which circulant-mixing path a 1D plan takes (direct: bf16, N <= 256 and
     d a multiple of 32; matrix-core FFT: transform length 1024 in bf16)."""
@@ -249,11 +250,44 @@ def test_mix_1d_long(cat, B, N, D, H, dtype, lscale):
         assert_parity(O.reshape(B * N, D)[rows], ref, dtype, "O rows")
 
 
+@pytest.mark.parametrize("B,N,D,H,dtype,lscale,L", [
+    (1, 2049, 24, 4, "f32", 2.0, 8192), (1, 3000, 8, 2, "bf16", 2.0, 8192), (2, 4099, 8, 1, "f32", 3.0, 16384),
+    (2, 5000, 24, 3, "f32", 3.0, 16384), (1, 12289, 8, 1, "bf16", 40.0, 32768), (1, 10000, 16, 2, "f32", 0.0, 32768),
+    (1, 20000, 16, 2, "bf16", 2.0, 65536), (1, 32767, 8, 1, "f32", 2.0, 65536)])
+def test_mix_1d_long_wrapped(cat, B, N, D, H, dtype, lscale, L):
+    """Non-power-of-two N beyond 2048: the three passes on the power-of-two
+    circle L >= 2N - 1 (values zero-padded, softmax line wrapped, outputs
+    past N dropped).  Cases: the smallest such N (2049), a prime (4099),
+    splits 128 x 64 .. 256 x 256 of L, a ragged last softmax chunk
+    everywhere, uniform and near one-hot scores, pair blocks of 1, 2, 4;
+    beyond 16384 x 16384 x 24 multiply-adds, 1024 sampled rows."""
+    say("mix_1d_long_wrapped", B, N, D, H, dtype, lscale)
+    import torch
+    rng = np.random.default_rng(N + 7 * D)
+    logits = (rng.standard_normal((B, H, N)) * lscale).astype(np.float32)
+    V = rng.standard_normal((B, N, D)).astype(np.float32)
+    if dtype == "bf16":
+        V = W.bf16_bits_to_f32(W.round_bf16_bits(V)).reshape(V.shape)
+    plan = cat.cat_plan_create("1d", dtype, B, N, D, H)
+    assert plan.conv_path() == "fft_multipass"
+    assert plan.geometry()[0] == L
+    O = to_np(cat.cat_step_mix(plan, torch.from_numpy(logits).cuda(), to_dev(V, dtype)))
+    assert O.shape == (B, N, D)
+    zs = oracle.softmax(logits)
+    if N * N * D * B <= 16384 * 16384 * 24:
+        assert_parity(O, oracle.circulant_1d(zs, V), dtype, "O")
+    else:
+        rows = np.unique(np.concatenate([np.random.default_rng(3).integers(0, B * N, 1024), [0, N - 1]]))
+        ref = oracle.circulant_1d(zs, V, rows=rows)
+        assert_parity(O.reshape(B * N, D)[rows], ref, dtype, "O rows")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_forward_1d_long(cat, dtype):
-    """The whole 1D path at N = 16384 (projection, then the three-pass
-    mixing), on 512 sampled rows."""
-    B, N, D, H = 1, 16384, 64, 2
+@pytest.mark.parametrize("N", [16384, 6000])
+def test_forward_1d_long(cat, dtype, N):
+    """The whole 1D path at N = 16384 and at N = 6000 (on a circle of
+    16384): projection, then the three-pass mixing, on 512 sampled rows."""
+    B, D, H = 1, 64, 2
     say("forward_1d_long", B, N, D, H, dtype)
     import torch
     inp = rng_inputs(23, B, N, D, H, dtype)

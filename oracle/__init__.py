@@ -15,6 +15,11 @@ the steps in the order the pages give:
       Z = X W_A  ->  Z* = softmax over the N tokens, per head
       V = X W_V  ->  O_h = circ(Z*_h) V_h,  C[i][j] = Z*[(i - j) mod N]
 
+  Backward of the 1D mixing (CAT is trained end to end; the chain rule of
+  the forward sums, written out as direct sums):
+      dV_h = circ(Z*_h)^T G_h,   dZ*_h[k] = sum_c sum_i G[i][c] V[(i - k) mod N][c],
+      dZ_h = Z*_h . (dZ*_h - <Z*_h, dZ*_h>)
+
   2D circulant attention (Vision Transformers are Circulant Attention
   Learners, "Circulant Attention: attention rebuilt with the FFT"):
       Q, K, V = X W_Q, X W_K, X W_V
@@ -57,8 +62,11 @@ def _load():
         lib.oracle_scores_bccb_2d.argtypes = [_P, _P, _P, _i64, _i64, _i64, _i64, _i64,
                                               ctypes.c_double]
         lib.oracle_bccb_2d.argtypes = [_P, _P, _P, _i64, _i64, _i64, _i64, _i64, _I64P, _i64]
+        lib.oracle_circulant_1d_transpose.argtypes = [_P, _P, _P, _i64, _i64, _i64, _i64]
+        lib.oracle_circulant_1d_grad_w.argtypes = [_P, _P, _P, _i64, _i64, _i64, _i64]
         for f in ("oracle_matmul", "oracle_scores_1d", "oracle_softmax_rows",
-                  "oracle_circulant_1d", "oracle_scores_bccb_2d", "oracle_bccb_2d"):
+                  "oracle_circulant_1d", "oracle_scores_bccb_2d", "oracle_bccb_2d",
+                  "oracle_circulant_1d_transpose", "oracle_circulant_1d_grad_w"):
             getattr(lib, f).restype = None
         _lib = lib
     return _lib
@@ -165,7 +173,54 @@ def bccb_2d(w, V, rows: Optional[Sequence[int]] = None) -> np.ndarray:
     return O
 
 
+def circulant_1d_transpose(w, G) -> np.ndarray:
+    """dV[b, j, c] = sum_i w[b, h(c), (i - j) mod N] G[b, i, c]: circ(w_h)^T G_h,
+    the gradient of circulant_1d with respect to V for output gradient G."""
+    w = _f64(w)
+    G = _f64(G)
+    B, H, N = w.shape
+    assert G.shape[:2] == (B, N) and G.shape[2] % H == 0
+    dV = np.empty_like(G)
+    _load().oracle_circulant_1d_transpose(_ptr(w), _ptr(G), _ptr(dV), B, N, G.shape[2], H)
+    return dV
+
+
+def circulant_1d_grad_w(G, V, H: int) -> np.ndarray:
+    """dw[b, h, k] = sum over the head's channels c and tokens i of
+    G[b, i, c] V[b, (i - k) mod N, c]: the gradient of circulant_1d with
+    respect to its filter w for output gradient G."""
+    G = _f64(G)
+    V = _f64(V)
+    B, N, D = G.shape
+    assert V.shape == G.shape and D % H == 0
+    dw = np.empty((B, H, N), dtype=np.float64)
+    _load().oracle_circulant_1d_grad_w(_ptr(G), _ptr(V), _ptr(dw), B, N, D, H)
+    return dw
+
+
+def softmax_backward(zstar, g) -> np.ndarray:
+    """dL/dz from g = dL/dz* through z* = softmax(z) over the last axis:
+    z*_k (g_k - sum_m z*_m g_m)."""
+    zstar = _f64(zstar)
+    g = _f64(g)
+    return zstar * (g - np.sum(zstar * g, axis=-1, keepdims=True))
+
+
 # ---------------------------------------------------------------- composites
+def mix_backward_1d(z, V, G) -> Dict[str, np.ndarray]:
+    """Backward of the CAT mixing O_h = circ(softmax(z_h)) V_h for output
+    gradient G: returns dz (logits gradient [B,H,N]) and dV ([B,N,D]).  The
+    chain rule of the forward (CAT: Circular-Convolutional Attention for
+    Sub-Quadratic Transformers, "Method details / Overall framework"):
+    dV = circ(z*)^T G, dz* = circulant_1d_grad_w(G, V), dz = softmax'(dz*)."""
+    z = _f64(z)
+    zstar = softmax(z)
+    dV = circulant_1d_transpose(zstar, G)
+    dzs = circulant_1d_grad_w(G, V, z.shape[1])
+    return {"dz": softmax_backward(zstar, dzs), "dV": dV, "dzstar": dzs}
+
+
+# ---------------------------------------------------------------- composites (forward)
 def cat_forward_1d(X, W_A, W_V, rows: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
     """CAT forward: returns z (logits [B,H,N]), zstar (softmax), V (= X W_V) and O."""
     z = scores_1d(X, W_A)

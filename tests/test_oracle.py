@@ -448,5 +448,89 @@ def test_planted_conjugate_on_wrong_side_is_caught():
     assert not np.array_equal(bad[0, 0], np.array(case["a"]))
 
 
+# ---------------------------------------------------------------- 1D mixing backward
+def _mix_loss(z, V, G):
+    """The scalar <circ(softmax(z)) V, G> whose gradients the backward gives."""
+    return float(np.sum(oracle.circulant_1d(oracle.softmax(z), V) * G))
+
+
+@pytest.mark.parametrize("B,N,H,d", [(1, 1, 1, 2), (2, 5, 2, 2), (1, 7, 3, 2), (1, 4, 1, 4)])
+def test_mix_backward_matches_finite_differences(B, N, H, d):
+    """Central differences of the (separately pinned) forward: every logit and
+    every value entry, step 1e-5, agreement to ~1e-8 relative."""
+    rng = np.random.default_rng(7 + N)
+    z = rng.standard_normal((B, H, N)) * 1.5
+    V = rng.standard_normal((B, N, H * d))
+    G = rng.standard_normal((B, N, H * d))
+    got = oracle.mix_backward_1d(z, V, G)
+    eps = 1e-5
+    num_dz = np.zeros_like(z)
+    for idx in np.ndindex(z.shape):
+        zp, zm = z.copy(), z.copy()
+        zp[idx] += eps
+        zm[idx] -= eps
+        num_dz[idx] = (_mix_loss(zp, V, G) - _mix_loss(zm, V, G)) / (2 * eps)
+    num_dV = np.zeros_like(V)
+    for idx in np.ndindex(V.shape):
+        Vp, Vm = V.copy(), V.copy()
+        Vp[idx] += eps
+        Vm[idx] -= eps
+        num_dV[idx] = (_mix_loss(z, Vp, G) - _mix_loss(z, Vm, G)) / (2 * eps)
+    assert np.allclose(got["dz"], num_dz, rtol=1e-7, atol=1e-9), np.max(np.abs(got["dz"] - num_dz))
+    assert np.allclose(got["dV"], num_dV, rtol=1e-7, atol=1e-9), np.max(np.abs(got["dV"] - num_dV))
+
+
+@pytest.mark.parametrize("N,H,d", [(6, 2, 3), (16, 1, 4), (9, 3, 2)])
+def test_mix_backward_matches_library_routes(N, H, d):
+    """dV against the materialised scipy circulant's transpose; dz* against the
+    FFT cross-correlation summed over the head's channels."""
+    rng = np.random.default_rng(100 + N)
+    w = rng.random((1, H, N))
+    V = rng.standard_normal((1, N, H * d))
+    G = rng.standard_normal((1, N, H * d))
+    dV = oracle.circulant_1d_transpose(w, G)
+    dw = oracle.circulant_1d_grad_w(G, V, H)
+    for h in range(H):
+        C = scipy.linalg.circulant(w[0, h])  # C[i][j] = w[(i - j) mod N]
+        sl = slice(h * d, (h + 1) * d)
+        assert np.allclose(dV[0][:, sl], C.T @ G[0][:, sl], rtol=1e-12, atol=1e-12)
+        xc = np.fft.ifft(np.sum(np.fft.fft(G[0][:, sl], axis=0) * np.conj(np.fft.fft(V[0][:, sl], axis=0)), axis=1))
+        assert np.allclose(dw[0, h], xc.real, rtol=1e-10, atol=1e-10)
+
+
+def test_mix_backward_logit_gradient_sums_to_zero():
+    """Softmax is invariant to adding a constant to a line's logits, so each
+    line of dz sums to zero; uniform values (token-constant V) give dz = 0."""
+    rng = np.random.default_rng(3)
+    B, N, H, d = 2, 11, 2, 2
+    z = rng.standard_normal((B, H, N))
+    G = rng.standard_normal((B, N, H * d))
+    V = rng.standard_normal((B, N, H * d))
+    dz = oracle.mix_backward_1d(z, V, G)["dz"]
+    assert np.allclose(dz.sum(axis=-1), 0.0, atol=1e-12)
+    Vc = np.broadcast_to(rng.standard_normal((B, 1, H * d)), (B, N, H * d))
+    assert np.allclose(oracle.mix_backward_1d(z, Vc, G)["dz"], 0.0, atol=1e-12)
+
+
+def test_planted_backward_lag_sign_is_caught():
+    """A score gradient correlating the wrong way (V[(i + k) mod N]) fails the
+    finite-difference pin."""
+    rng = np.random.default_rng(11)
+    B, N, H, d = 1, 5, 1, 2
+    z = rng.standard_normal((B, H, N))
+    V = rng.standard_normal((B, N, d))
+    G = rng.standard_normal((B, N, d))
+    zs = oracle.softmax(z)
+    bad = oracle.softmax_backward(zs, oracle.circulant_1d_grad_w(G[:, (-np.arange(N)) % N], V[:, (-np.arange(N)) % N], H))
+    eps = 1e-5
+    num = np.zeros_like(z)
+    for idx in np.ndindex(z.shape):
+        zp, zm = z.copy(), z.copy()
+        zp[idx] += eps
+        zm[idx] -= eps
+        num[idx] = (_mix_loss(zp, V, G) - _mix_loss(zm, V, G)) / (2 * eps)
+    assert not np.allclose(bad, num, rtol=1e-4, atol=1e-6)
+
+
 def test_oracle_reports_threads():
     assert oracle.num_threads() >= 1

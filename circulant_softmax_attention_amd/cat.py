@@ -29,7 +29,8 @@ CAT_1D, CAT_BCCB_2D = 0, 1
 EXPORTS = ["cat_plan_create", "cat_plan_destroy", "cat_plan_workspace_size", "cat_plan_geometry",
            "cat_forward_1d", "cat_forward_bccb_2d", "cat_status_string", "cat_last_error",
            "cat_plan_set_timing", "cat_plan_kernel_times", "cat_plan_conv_path",
-           "cat_step_project", "cat_step_spectrum", "cat_step_mix", "cat_step_scores_2d"]
+           "cat_step_project", "cat_step_spectrum", "cat_step_mix", "cat_step_mix_backward_1d",
+           "cat_step_scores_2d"]
 KERNELS_1D = ["project", "spectrum", "fftconv"]
 KERNELS_2D = ["project", "scores", "spectrum", "fftconv", "psum"]
 
@@ -64,6 +65,7 @@ def _load() -> ctypes.CDLL:
     lib.cat_step_project.argtypes = [vp] * 9
     lib.cat_step_spectrum.argtypes = [vp] * 5
     lib.cat_step_mix.argtypes = [vp] * 6
+    lib.cat_step_mix_backward_1d.argtypes = [vp] * 8
     lib.cat_step_scores_2d.argtypes = [vp] * 6
     for f in EXPORTS:
         fn = getattr(lib, f)
@@ -271,6 +273,21 @@ def cat_step_mix(plan: Plan, logits, V, O=None, workspace=None, stream=None) -> 
                              _ptr(V, (B, N, D), dt, "V"), _ptr(O, (B, N, D), dt, "O"), _ptr(workspace),
                              _stream_ptr(stream)), "cat_step_mix")
     return O
+
+
+def cat_step_mix_backward_1d(plan: Plan, logits, V, dO, workspace=None, stream=None):
+    """(dlogits [B,H,N] fp32, dV [B,N,D] storage dtype) for output gradient dO."""
+    B, N, D, H, dt = plan.B, plan.N, plan.D, plan.H, plan.dtype
+    if workspace is None:
+        workspace = alloc_workspace(plan, V.device)
+    dlogits = torch.empty((B, H, N), dtype=torch.float32, device=V.device)
+    dV = torch.empty((B, N, D), dtype=dt, device=V.device)
+    _check(_lib.cat_step_mix_backward_1d(ctypes.c_void_p(plan.handle),
+                                         _ptr(logits, (B, H, N), torch.float32, "logits"),
+                                         _ptr(V, (B, N, D), dt, "V"), _ptr(dO, (B, N, D), dt, "dO"),
+                                         _ptr(dlogits), _ptr(dV), _ptr(workspace), _stream_ptr(stream)),
+           "cat_step_mix_backward_1d")
+    return dlogits, dV
 
 
 def cat_step_scores_2d(plan: Plan, Q, K, workspace=None, stream=None) -> torch.Tensor:

@@ -252,6 +252,18 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
     pl->off_z = off;
     off = up256(off + BH * p->N * sizeof(float));
     pl->off_Q = pl->off_K = pl->off_part = pl->off_psum = 0;
+    if (!longn) {
+      // the mixing backward: fp32 copies of dO and V (channel pairs), the
+      // score-gradient partials and their sum
+      pl->off_Q = off;
+      off = up256(off + BND * sizeof(float));
+      pl->off_K = off;
+      off = up256(off + BND * sizeof(float));
+      pl->off_part = off;
+      off = up256(off + BH * pl->ngrp * pl->L * sizeof(float2));
+      pl->off_psum = off;
+      off = up256(off + BH * pl->L * sizeof(float2));
+    }
     if (longn) {
       pl->off_A = off;
       off = up256(off + BH * (size_t)d2 * pl->L * sizeof(float2));
@@ -501,6 +513,45 @@ hipError_t run_conv_1d(const cat_plan_s* pl, const ConvArgs& ca, hipStream_t s, 
   return pl->mconv ? launch_mconv(ca, s, t) : launch_conv(pl->geom, pl->et, ca, s, t);
 }
 
+// The mixing O = circ(softmax(logits)) V (1D) or BCCB(..) V (2D) from
+// [B][N][D] values: relayout to the blocked layout, then the plan's path.
+cat_status mix_impl(cat_plan plan, const float* logits, const void* V, void* O, void* workspace, hipStream_t s) {
+  cat_status st = CAT_OK;
+  void* Vb = ws_at(workspace, plan->off_V);
+  RelayoutArgs ra{};
+  ra.src = V;
+  ra.dst = Vb;
+  ra.src_et = plan->et;
+  ra.dst_f32 = 0;
+  ra.B = (int)plan->p.B;
+  ra.N = (int)plan->p.N;
+  ra.D = (int)plan->p.D;
+  ra.H = (int)plan->p.H;
+  ra.d = plan->d;
+  ra.cg = plan->cg;
+  hipError_t e = launch_relayout(ra, s);
+  if (e != hipSuccess) return hip_fail(e, "relayout launch");
+  if (plan->longn) {
+    e = run_long_1d(plan, logits, Vb, O, workspace, s, nullptr);
+    if (e != hipSuccess) return hip_fail(e, "long-sequence fft-conv launch");
+    return check_sync(plan, "long-sequence fft-conv");
+  }
+  SpecArgs sa = spec_base(plan, workspace);
+  sa.logits = logits;
+  const bool own_softmax = plan->mconv || plan->direct;
+  if (!own_softmax) {
+    e = launch_spectrum(plan->geom, 0, sa, s);
+    if (e != hipSuccess) return hip_fail(e, "spectrum launch");
+    if ((st = check_sync(plan, "spectrum")) != CAT_OK) return st;
+  }
+  ConvArgs ca = conv_base(plan, Vb, sa.spec, O);
+  if (own_softmax) ca.logits = logits;
+  e = run_conv_1d(plan, ca, s);
+  if (e != hipSuccess) return hip_fail(e, "fft-conv launch");
+  return check_sync(plan, "fft-conv");
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -654,45 +705,73 @@ cat_status cat_step_spectrum(cat_plan plan, const float* logits, float* probs, f
   return check_sync(plan, "spectrum");
 }
 
+
 cat_status cat_step_mix(cat_plan plan, const float* logits, const void* V, void* O, void* workspace,
                         void* stream) {
   if (!plan) return fail(CAT_ERR_INVALID_ARG, "NULL plan");
   if (plan->p.B == 0) return CAT_OK;
   cat_status st = check_ptrs({logits, V, O, workspace});
   if (st != CAT_OK) return st;
+  return mix_impl(plan, logits, V, O, workspace, reinterpret_cast<hipStream_t>(stream));
+}
+
+cat_status cat_step_mix_backward_1d(cat_plan plan, const float* logits, const void* V, const void* dO,
+                                    float* dlogits, void* dV, void* workspace, void* stream) {
+  if (!plan) return fail(CAT_ERR_INVALID_ARG, "NULL plan");
+  if (plan->p.kind != CAT_1D) return fail(CAT_ERR_PLAN_MISMATCH, "plan is not 1D");
+  if (plan->p.B == 0) return CAT_OK;
+  cat_status st = check_ptrs({logits, V, dO, dlogits, dV, workspace});
+  if (st != CAT_OK) return st;
+  if (plan->longn)
+    return fail(CAT_ERR_UNSUPPORTED, "the mixing backward covers single-workgroup lines (not the multi-pass path)");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  void* Vb = ws_at(workspace, plan->off_V);
+  const int BH = (int)(plan->p.B * plan->p.H), N = (int)plan->p.N;
+  // dV = circ(z*)^T dO = circ(softmax(zr)) dO with zr the reversed logits
+  float* zr = reinterpret_cast<float*>(ws_at(workspace, plan->off_z));
+  hipError_t e = launch_reverse_lines(logits, zr, BH, N, s);
+  if (e != hipSuccess) return hip_fail(e, "reverse launch");
+  if ((st = mix_impl(plan, zr, dO, dV, workspace, s)) != CAT_OK) return st;
+  // dz*: channel-pair copies (fp32) of dO and V, cross-correlation spectra
+  // per pair group, summed per (batch, head)
+  float* Qb = reinterpret_cast<float*>(ws_at(workspace, plan->off_Q));
+  float* Kb = reinterpret_cast<float*>(ws_at(workspace, plan->off_K));
+  float2* part = reinterpret_cast<float2*>(ws_at(workspace, plan->off_part));
+  float2* psum = reinterpret_cast<float2*>(ws_at(workspace, plan->off_psum));
   RelayoutArgs ra{};
-  ra.src = V;
-  ra.dst = Vb;
   ra.src_et = plan->et;
-  ra.dst_f32 = 0;
+  ra.dst_f32 = 1;
   ra.B = (int)plan->p.B;
-  ra.N = (int)plan->p.N;
+  ra.N = N;
   ra.D = (int)plan->p.D;
   ra.H = (int)plan->p.H;
   ra.d = plan->d;
-  ra.cg = plan->cg;
-  hipError_t e = launch_relayout(ra, s);
-  if (e != hipSuccess) return hip_fail(e, "relayout launch");
-  if (plan->longn) {
-    e = run_long_1d(plan, logits, Vb, O, workspace, s, nullptr);
-    if (e != hipSuccess) return hip_fail(e, "long-sequence fft-conv launch");
-    return check_sync(plan, "long-sequence fft-conv");
-  }
+  ra.cg = 2;
+  ra.src = dO;
+  ra.dst = Qb;
+  if ((e = launch_relayout(ra, s)) != hipSuccess) return hip_fail(e, "relayout launch");
+  ra.src = V;
+  ra.dst = Kb;
+  if ((e = launch_relayout(ra, s)) != hipSuccess) return hip_fail(e, "relayout launch");
+  ScoreArgs sc{};
+  sc.Q = Qb;
+  sc.K = Kb;
+  sc.partial = part;
+  sc.BH = BH;
+  sc.N = N;
+  sc.npair = plan->npair;
+  sc.ngrp = plan->ngrp;
+  sc.ppg = plan->ppg;
+  sc.tw = plan->d_tw;
+  if ((e = launch_score_partial(plan->geom, sc, s)) != hipSuccess) return hip_fail(e, "score-gradient launch");
+  if ((e = launch_psum(part, psum, BH, plan->ngrp, plan->L, s)) != hipSuccess) return hip_fail(e, "psum launch");
+  // dlogits = z* (dz* - <z*, dz*>)
   SpecArgs sa = spec_base(plan, workspace);
   sa.logits = logits;
-  const bool own_softmax = plan->mconv || plan->direct;
-  if (!own_softmax) {
-    e = launch_spectrum(plan->geom, 0, sa, s);
-    if (e != hipSuccess) return hip_fail(e, "spectrum launch");
-    if ((st = check_sync(plan, "spectrum")) != CAT_OK) return st;
-  }
-  ConvArgs ca = conv_base(plan, Vb, sa.spec, O);
-  if (own_softmax) ca.logits = logits;
-  e = run_conv_1d(plan, ca, s);
-  if (e != hipSuccess) return hip_fail(e, "fft-conv launch");
-  return check_sync(plan, "fft-conv");
+  sa.partial = psum;
+  sa.ngrp = 1;
+  sa.probs = dlogits;
+  if ((e = launch_spectrum(plan->geom, 2, sa, s)) != hipSuccess) return hip_fail(e, "logits-gradient launch");
+  return check_sync(plan, "mixing backward");
 }
 
 cat_status cat_step_scores_2d(cat_plan plan, const float* Q, const float* K, float* probs, void* workspace,

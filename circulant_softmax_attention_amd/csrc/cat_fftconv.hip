@@ -69,13 +69,14 @@ hipError_t prepare_kernels(const LineGeom& g, size_t conv_lds, size_t spec_lds, 
   raise((const void*)e->conv_bf16, conv_lds);
   raise((const void*)e->spec0, spec_lds);
   raise((const void*)e->spec1, spec_lds);
+  raise((const void*)e->spec2, spec_lds);
   raise((const void*)e->score, score_lds);
   return err;
 }
 
 hipError_t launch_spectrum(const LineGeom& g, int mode, const SpecArgs& a, hipStream_t s, const LaunchTiming* t) {
   const Entry* e = find_entry(g);
-  SpecFn fn = e ? (mode == 0 ? e->spec0 : e->spec1) : nullptr;
+  SpecFn fn = e ? (mode == 0 ? e->spec0 : mode == 1 ? e->spec1 : e->spec2) : nullptr;
   if (!fn) return hipErrorInvalidValue;
   SpecArgs aa = a;
   if (e->S > 1 && aa.G != 1) return hipErrorInvalidValue;  // split DFTs pair adjacent lanes
@@ -127,7 +128,25 @@ __global__ __launch_bounds__(256) void psum_kernel(const float2* __restrict__ pa
   out[idx] = acc;
 }
 
+// zr[bh][k] = z[bh][(N - k) mod N]: the line reversed about token 0, so
+// that circ(softmax(zr)) = circ(softmax(z))^T.
+__global__ __launch_bounds__(256) void reverse_lines_kernel(const float* __restrict__ z, float* __restrict__ zr,
+                                                            int BH, int N) {
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (size_t)BH * N) return;
+  const size_t line = idx / (size_t)N;
+  const int k = (int)(idx - line * (size_t)N);
+  zr[idx] = z[line * (size_t)N + (k == 0 ? 0 : N - k)];
+}
+
 }  // namespace
+
+hipError_t launch_reverse_lines(const float* z, float* zr, int BH, int N, hipStream_t s, const LaunchTiming* t) {
+  if (BH < 1 || N < 1) return hipErrorInvalidValue;
+  const size_t blocks = ((size_t)BH * N + 255) / 256;
+  if (blocks > 0x7fffffffu) return hipErrorInvalidValue;
+  return launch_k(reverse_lines_kernel, dim3((unsigned)blocks), dim3(256), 0, s, t, z, zr, BH, N);
+}
 
 hipError_t launch_psum(const float2* part, float2* out, int BH, int ngrp, int L, hipStream_t s,
                        const LaunchTiming* t) {

@@ -135,8 +135,9 @@ struct ConvArgs {
 struct ScoreArgs {
   const float* Q;  // BLOCKED fp32, cg = 2: [BH][npair][N][2]
   const float* K;
-  float2* partial;
+  float2* partial;  // [BH][ngrp][L] complex
   int BH, N, npair, ngrp, ppg;
+  const float2* tw;  // 1D inter-pass twiddles (null for 2D)
 };
 
 struct RelayoutArgs {
@@ -160,6 +161,8 @@ int line_threads(const LineGeom& g);
 // LDS bytes of a spectrum workgroup of G lines (lines, reduction scratch).
 size_t spectrum_lds_bytes(const LineGeom& g, int G);
 
+// mode 0: softmax spectrum from logits; 1 (2D): from summed score partials;
+// 2 (1D): the logits gradient of the mixing backward into a.probs.
 hipError_t launch_spectrum(const LineGeom& g, int mode, const SpecArgs& a, hipStream_t s,
                            const LaunchTiming* t = nullptr);
 hipError_t launch_conv(const LineGeom& g, int et, const ConvArgs& a, hipStream_t s, const LaunchTiming* t = nullptr);
@@ -173,6 +176,9 @@ hipError_t launch_mconv(const ConvArgs& a, hipStream_t s, const LaunchTiming* t 
 // d % 32 == 0; a.spec and a.tw unused.
 hipError_t launch_dconv(int et, const ConvArgs& a, hipStream_t s, const LaunchTiming* t = nullptr);
 hipError_t launch_score_partial(const LineGeom& g, const ScoreArgs& a, hipStream_t s,
+                                const LaunchTiming* t = nullptr);
+// zr[bh][k] = z[bh][(N - k) mod N] for BH lines of N fp32 values.
+hipError_t launch_reverse_lines(const float* z, float* zr, int BH, int N, hipStream_t s,
                                 const LaunchTiming* t = nullptr);
 // 1D mixing for N beyond one workgroup's line, on a transform of length
 // L = L1 L2 (three passes over HBM; see cat_longconv.hip): L = N for a

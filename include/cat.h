@@ -201,6 +201,28 @@ cat_status cat_step_spectrum(cat_plan plan, const float* logits, float* probs, f
 cat_status cat_step_mix(cat_plan plan, const float* logits, const void* V, void* O,
                         void* workspace, void* stream);
 
+/* Backward of the 1D mixing step (CAT is trained end to end: CAT:
+ * Circular-Convolutional Attention for Sub-Quadratic Transformers, "Method
+ * details / Overall framework"; the gradients are the chain rule of
+ * O_h = circ(z*_h) V_h, z*_h = softmax(logits_h)).  Given the output
+ * gradient dO:
+ *   dV[b][j][c]      = sum_i z*[b][h][(i - j) mod N] dO[b][i][c]
+ *                      (circ(z*_h)^T dO_h, evaluated as the forward mixing
+ *                      of the reversed logits, on the plan's mixing path);
+ *   dz*[b][h][k]     = sum over the head's channels c and tokens i of
+ *                      dO[b][i][c] V[b][(i - k) mod N][c]
+ *                      (a cross-correlation, by FFT on the plan's circle);
+ *   dlogits[b][h][k] = z*[k] (dz*[k] - sum_m z*[m] dz*[m]).
+ * logits [B][H][N] fp32 (the forward's z), V and dO [B][N][D] storage
+ * dtype (all caller-owned device memory, read only); dlogits [B][H][N] fp32
+ * and dV [B][N][D] storage dtype are written.  dV in bf16 is rounded from
+ * fp32; dlogits is computed in fp32 from the stored V and dO.  workspace:
+ * cat_plan_workspace_size bytes.  Errors: CAT_ERR_PLAN_MISMATCH for a 2D
+ * plan; CAT_ERR_UNSUPPORTED for plans on CAT_PATH_FFT_MULTIPASS;
+ * CAT_ERR_INVALID_ARG for NULL or misaligned pointers. */
+cat_status cat_step_mix_backward_1d(cat_plan plan, const float* logits, const void* V, const void* dO,
+                                    float* dlogits, void* dV, void* workspace, void* stream);
+
 /* 2D score step: probs [B][H][N] fp32 = softmax over the grid of the scaled
  * circular cross-correlation of Q and K (both [B][N][D] fp32).  2D plans only. */
 cat_status cat_step_scores_2d(cat_plan plan, const float* Q, const float* K, float* probs,

@@ -300,6 +300,57 @@ def test_forward_1d_long(cat, dtype, N):
     assert_parity(to_np(O).reshape(B * N, D)[rows], ref, dtype, "O rows")
 
 
+# ------------------------------------------------------------------ 1D mixing backward
+@pytest.mark.parametrize("B,N,D,H,dtype,path", [
+    (2, 64, 64, 4, "f32", "fft_valu"), (1, 1, 16, 2, "f32", "fft_valu"), (2, 2, 16, 2, "f32", "fft_valu"),
+    (1, 197, 96, 3, "f32", "fft_valu"), (3, 2047, 16, 1, "f32", "fft_valu"), (1, 1000, 64, 4, "f32", "fft_valu"),
+    (1, 4096, 32, 2, "f32", "fft_valu"), (2, 1024, 128, 2, "bf16", "fft_matrix"), (2, 128, 64, 1, "bf16", "direct"),
+    (1, 197, 384, 6, "bf16", "direct"), (2, 512, 64, 32, "bf16", "fft_valu")])
+def test_mix_backward_1d(cat, B, N, D, H, dtype, path):
+    """Gradients of the mixing for an output gradient dO: dV on the plan's
+    own mixing path (reversed logits), dlogits from the FFT cross-correlation
+    and the softmax Jacobian, against the oracle's direct sums.  Covers
+    N = 1 and 2, primes and other N on the 2N - 1 circle, L up to 4096 and
+    every 1D mixing path for dV.  dlogits is computed in fp32 from the stored
+    values, so it meets the fp32 bar in both storage dtypes."""
+    say("mix_backward_1d", B, N, D, H, dtype, path)
+    import torch
+    rng = np.random.default_rng(N * 3 + D)
+    logits = (rng.standard_normal((B, H, N)) * 2).astype(np.float32)
+    V = rng.standard_normal((B, N, D)).astype(np.float32)
+    dO = rng.standard_normal((B, N, D)).astype(np.float32)
+    if dtype == "bf16":
+        V = W.bf16_bits_to_f32(W.round_bf16_bits(V)).reshape(V.shape)
+        dO = W.bf16_bits_to_f32(W.round_bf16_bits(dO)).reshape(dO.shape)
+    plan = cat.cat_plan_create("1d", dtype, B, N, D, H)
+    assert plan.conv_path() == path
+    dlogits, dV = cat.cat_step_mix_backward_1d(plan, torch.from_numpy(logits).cuda(), to_dev(V, dtype),
+                                               to_dev(dO, dtype))
+    torch.cuda.synchronize()
+    ref = oracle.mix_backward_1d(logits, V, dO)
+    assert_parity(to_np(dV), ref["dV"], dtype, "dV")
+    got = to_np(dlogits)
+    assert_parity(got, ref["dz"], "f32", "dlogits")
+    # each line sums to zero, up to fp32 rounding of its entries
+    assert np.all(np.abs(got.sum(axis=-1)) <= 1e-5 * np.abs(got).sum(axis=-1) + 1e-7)
+
+
+def test_mix_backward_1d_rejections(cat):
+    """The multi-pass path has no backward yet; 2D plans are the wrong kind."""
+    import torch
+    plan = cat.cat_plan_create("1d", "f32", 1, 8192, 8, 2)
+    z = torch.zeros((1, 2, 8192), device="cuda")
+    V = torch.zeros((1, 8192, 8), device="cuda")
+    with pytest.raises(cat.CatError) as e:
+        cat.cat_step_mix_backward_1d(plan, z, V, V)
+    assert e.value.status == -2
+    p2 = cat.cat_plan_create("2d", "f32", 1, 64, 16, 2, Hg=8, Wg=8)
+    with pytest.raises(cat.CatError) as e:
+        cat.cat_step_mix_backward_1d(p2, torch.zeros((1, 2, 64), device="cuda"), torch.zeros((1, 64, 16), device="cuda"),
+                                     torch.zeros((1, 64, 16), device="cuda"))
+    assert e.value.status == -5
+
+
 # ------------------------------------------------------------------ 1D forward
 @pytest.mark.parametrize("B,N,D,H,dtype", [(1, 64, 64, 4, "f32"), (2, 37, 48, 3, "f32"), (3, 100, 64, 4, "bf16"),
                                            (1, 1, 32, 2, "f32"), (2, 197, 96, 3, "f32"), (1, 1024, 64, 1, "bf16"),

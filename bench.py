@@ -337,6 +337,157 @@ def run(args):
     return line
 
 
+def backward_model(wl, L: int, ngrp: int, fwd_model):
+    """Algorithmic bytes and flops of each kernel of one mixing-backward call
+    (all launches of a kind together).  dV runs as the forward mixing of the
+    reversed logits, so its spectrum / conv entries are the forward's."""
+    s = 4 if wl.dtype == "f32" else 2
+    B, N, D, H, d = wl.B, wl.N, wl.D, wl.H, wl.d
+    T, BH = B * N, B * H
+    lines = BH * (d // 2)
+    m = {k: v for k, v in fwd_model.items() if k in ("spectrum", "fftconv", "directconv")}
+    m["reverse"] = dict(bytes=2 * BH * N * 4, flops=0.0, unit="valu_f32")
+    # dO to the blocked storage layout (read + write), dO and V to fp32 pairs (read, write fp32)
+    m["relayout"] = dict(bytes=2 * T * D * s + 2 * (T * D * s + T * D * 4), flops=0.0, unit="valu_f32")
+    m["score_grad"] = dict(bytes=2 * T * D * 4 + BH * ngrp * L * 8,
+                           flops=lines * (2 * fft_flops(L) + 8.0 * L), unit="valu_f32")
+    m["psum"] = dict(bytes=BH * ngrp * L * 8 + BH * L * 8, flops=2.0 * BH * (ngrp - 1) * L, unit="valu_f32")
+    m["logits_grad"] = dict(bytes=BH * L * 8 + 2 * BH * N * 4, flops=BH * (fft_flops(L) + 8.0 * N), unit="valu_f32")
+    return m
+
+
+def run_backward(args):
+    """The 1D mixing backward (dlogits, dV from logits, V and dO) on the
+    workload's shapes: V and the logits from the projection of the workload's
+    X, dO ~ N(0, 1) seeded."""
+    import numpy as np
+    import torch
+
+    from circulant_softmax_attention_amd import workloads as W
+    from circulant_softmax_attention_amd import cat
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a ROCm GPU")
+    wl = W.WORKLOADS[args.workload]
+    if wl.kind != "1d":
+        raise SystemExit("--backward covers 1D workloads")
+    log("workload", wl.name, "(mixing backward)")
+    inp = W.make_inputs(wl)
+    dt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dt).cuda()
+
+    plan = cat.cat_plan_create("1d", wl.dtype, wl.B, wl.N, wl.D, wl.H)
+    L, L1, L2 = plan.geometry()
+    conv_path = plan.conv_path()
+    V0, z0 = cat.cat_step_project(plan, dev(inp.X), dev(inp.W_A), dev(inp.W_V))
+    g = np.random.default_rng(99).standard_normal((wl.B, wl.N, wl.D)).astype(np.float32)
+    dO0 = dev(g)
+    esz = 4 if wl.dtype == "f32" else 2
+    ws_bytes = plan.workspace_size()
+    set_bytes = 4 * V0.numel() * esz + 2 * z0.numel() * 4 + ws_bytes
+    nsets = max(1, math.ceil(args.rotate_bytes / set_bytes))
+    sets = []
+    for i in range(nsets):
+        sets.append((z0 if i == 0 else z0.clone(), V0 if i == 0 else V0.clone(), dO0 if i == 0 else dO0.clone(),
+                     cat.alloc_workspace(plan)))
+    log(f"transform {L} = {L1} x {L2}; mixing path {conv_path}; {nsets} buffer sets of {set_bytes / 2**20:.1f} MiB")
+
+    def step(i):
+        z, V, dO, ws = sets[i % nsets]
+        cat.cat_step_mix_backward_1d(plan, z, V, dO, workspace=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for i in range(args.steps):
+        step(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1000.0 / args.steps
+    gpu_ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    log(f"{args.steps} steps: {ms_per_step * 1000:.1f} us/step wall, {gpu_ms_per_step * 1000:.1f} us/step events")
+
+    cat.cat_plan_set_timing(plan, True)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    ktimes = {k: v for k, v in cat.cat_plan_kernel_times(plan).items() if v[1] > 0}
+    cat.cat_plan_set_timing(plan, False)
+    if conv_path == "direct":
+        ktimes["directconv"] = ktimes.pop("fftconv")
+    ngrp = (wl.d // 2 + 1) // 2
+    fwd = kernel_model(wl, L, ngrp, fused_spectrum=conv_path == "fft_matrix", direct=conv_path == "direct")
+    model = backward_model(wl, L, ngrp, fwd)
+    kernels = {}
+    for k, (ms, n) in ktimes.items():
+        mm = model[k]
+        per_call = max(1, round(n / args.steps))
+        sec = ms / 1000.0
+        nbytes, nflops = mm["bytes"] / per_call, mm["flops"] / per_call
+        kernels[k] = dict(us=round(ms * 1000, 3), launches_per_call=per_call, bytes=int(nbytes), flops=float(nflops),
+                          hbm_frac=round(nbytes / sec / 1e9 / HBM_PEAK_GBS, 4),
+                          compute_frac=round(nflops / sec / 1e12 / PEAK_TFLOPS[mm["unit"]], 4),
+                          compute_unit=mm["unit"])
+        log(f"  kernel {k:12s} {ms * 1000:9.2f} us avg over {n} launches ({per_call}/call)")
+    dom = max(kernels, key=lambda k: kernels[k]["us"] * kernels[k]["launches_per_call"])
+    kd = kernels[dom]
+    sec = kd["us"] / 1e6
+    if kd["compute_unit"].startswith("mfma") and kd["compute_frac"] >= kd["hbm_frac"]:
+        bound, achieved, peak, unit = "mfma", kd["flops"] / sec / 1e12, PEAK_TFLOPS[kd["compute_unit"]], "TFLOP/s"
+    elif kd["hbm_frac"] >= kd["compute_frac"]:
+        bound, achieved, peak, unit = "hbm", kd["bytes"] / sec / 1e9, HBM_PEAK_GBS, "GB/s"
+    else:
+        bound, achieved, peak, unit = "alu", kd["flops"] / sec / 1e12, PEAK_TFLOPS[kd["compute_unit"]], "TFLOP/s"
+    roofline = dict(kernel=dom, bound=bound, achieved=round(achieved, 2), peak=peak, unit=unit,
+                    frac=round(achieved / peak, 4), traffic=None, hbm_frac=kd["hbm_frac"],
+                    compute_frac=kd["compute_frac"], us=kd["us"])
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        zc = z0[:1].cpu().numpy()
+        Vc = V0[:1].float().cpu().numpy()
+        gc = dO0[:1].float().cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.mix_backward_1d(zc, Vc, gc)
+        secs = time.perf_counter() - t0
+        cpu = dict(value=wl.N / secs, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
+                   sample=f"1 of {wl.B} sequences ({wl.N} tokens), fp64 direct O(N^2 d) sums for dV and dz*, "
+                          f"{secs:.1f} s")
+        log("cpu baseline:", cpu)
+
+    tokens = wl.B * wl.N
+    io_bytes = 3 * tokens * wl.D * esz + 2 * wl.B * wl.H * wl.N * 4  # V, dO read, dV written; logits, dlogits
+    return {
+        "metric": f"circulant mixing backward tokens/s ({wl.name})",
+        "value": round(tokens / (ms_per_step / 1000.0), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if wl.dtype == "f32" else "bf16-storage/f32-compute",
+        "data": "synthetic (seeded PCG64: V, logits = projections of X~N(0,1); dO~N(0,1))",
+        "config": {"workload": wl.name, "kind": "1d-mix-backward", "B": wl.B, "N": wl.N, "D": wl.D, "H": wl.H,
+                   "storage": wl.dtype, "transform": [L, L1, L2], "mixing": conv_path, "global_batch": wl.B,
+                   "seq_len": wl.N, "parallelism": "none"},
+        "e2e_hbm_frac": round(io_bytes / (ms_per_step / 1000.0) / 1e9 / HBM_PEAK_GBS, 4),
+        "gpu_event_ms_per_step": round(gpu_ms_per_step, 5),
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -345,6 +496,8 @@ def main():
     ap.add_argument("--workload", default=None, help="workload name (default: the N=1024, D=768 one)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the 1D mixing backward (cat_step_mix_backward_1d) instead of the forward")
     ap.add_argument("--rotate-bytes", type=float, default=2.5 * MALL_BYTES,
                     help="total bytes of rotated buffer sets (defeats the Infinity Cache)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -370,7 +523,7 @@ def main():
     from circulant_softmax_attention_amd import workloads as W
     if args.workload is None:
         args.workload = W.HEADLINE
-    line = run(args)
+    line = run_backward(args) if args.backward else run(args)
     print(json.dumps(line), flush=True)
 
 

@@ -31,7 +31,7 @@ EXPORTS = ["cat_plan_create", "cat_plan_destroy", "cat_plan_workspace_size", "ca
            "cat_plan_set_timing", "cat_plan_kernel_times", "cat_plan_conv_path",
            "cat_step_project", "cat_step_spectrum", "cat_step_mix", "cat_step_mix_backward_1d",
            "cat_step_scores_2d"]
-KERNELS_1D = ["project", "spectrum", "fftconv"]
+KERNELS_1D = ["project", "spectrum", "fftconv", "reverse", "relayout", "score_grad", "psum", "logits_grad"]
 KERNELS_2D = ["project", "scores", "spectrum", "fftconv", "psum"]
 
 

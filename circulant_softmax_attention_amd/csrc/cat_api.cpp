@@ -367,7 +367,7 @@ cat_status cat_plan_set_timing(cat_plan plan, int enable) {
 
 cat_status cat_plan_kernel_times(cat_plan plan, double* total_ms, int64_t* launches, int* nkernels) {
   if (!plan || !total_ms || !launches || !nkernels) return fail(CAT_ERR_INVALID_ARG, "NULL argument");
-  const int nk = plan->p.kind == CAT_1D ? 3 : 5;
+  const int nk = plan->p.kind == CAT_1D ? 8 : 5;
   *nkernels = nk;
   for (int k = 0; k < 8; ++k) {
     total_ms[k] = 0.0;
@@ -515,7 +515,8 @@ hipError_t run_conv_1d(const cat_plan_s* pl, const ConvArgs& ca, hipStream_t s, 
 
 // The mixing O = circ(softmax(logits)) V (1D) or BCCB(..) V (2D) from
 // [B][N][D] values: relayout to the blocked layout, then the plan's path.
-cat_status mix_impl(cat_plan plan, const float* logits, const void* V, void* O, void* workspace, hipStream_t s) {
+cat_status mix_impl(cat_plan plan, const float* logits, const void* V, void* O, void* workspace, hipStream_t s,
+                    KernelMark* mk = nullptr) {
   cat_status st = CAT_OK;
   void* Vb = ws_at(workspace, plan->off_V);
   RelayoutArgs ra{};
@@ -529,10 +530,10 @@ cat_status mix_impl(cat_plan plan, const float* logits, const void* V, void* O, 
   ra.H = (int)plan->p.H;
   ra.d = plan->d;
   ra.cg = plan->cg;
-  hipError_t e = launch_relayout(ra, s);
+  hipError_t e = launch_relayout(ra, s, mk ? mk->at(4) : nullptr);
   if (e != hipSuccess) return hip_fail(e, "relayout launch");
   if (plan->longn) {
-    e = run_long_1d(plan, logits, Vb, O, workspace, s, nullptr);
+    e = run_long_1d(plan, logits, Vb, O, workspace, s, mk);
     if (e != hipSuccess) return hip_fail(e, "long-sequence fft-conv launch");
     return check_sync(plan, "long-sequence fft-conv");
   }
@@ -540,13 +541,13 @@ cat_status mix_impl(cat_plan plan, const float* logits, const void* V, void* O, 
   sa.logits = logits;
   const bool own_softmax = plan->mconv || plan->direct;
   if (!own_softmax) {
-    e = launch_spectrum(plan->geom, 0, sa, s);
+    e = launch_spectrum(plan->geom, 0, sa, s, mk ? mk->at(1) : nullptr);
     if (e != hipSuccess) return hip_fail(e, "spectrum launch");
     if ((st = check_sync(plan, "spectrum")) != CAT_OK) return st;
   }
   ConvArgs ca = conv_base(plan, Vb, sa.spec, O);
   if (own_softmax) ca.logits = logits;
-  e = run_conv_1d(plan, ca, s);
+  e = run_conv_1d(plan, ca, s, mk ? mk->at(2) : nullptr);
   if (e != hipSuccess) return hip_fail(e, "fft-conv launch");
   return check_sync(plan, "fft-conv");
 }
@@ -726,11 +727,12 @@ cat_status cat_step_mix_backward_1d(cat_plan plan, const float* logits, const vo
     return fail(CAT_ERR_UNSUPPORTED, "the mixing backward covers single-workgroup lines (not the multi-pass path)");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int BH = (int)(plan->p.B * plan->p.H), N = (int)plan->p.N;
+  KernelMark mk(plan);
   // dV = circ(z*)^T dO = circ(softmax(zr)) dO with zr the reversed logits
   float* zr = reinterpret_cast<float*>(ws_at(workspace, plan->off_z));
-  hipError_t e = launch_reverse_lines(logits, zr, BH, N, s);
+  hipError_t e = launch_reverse_lines(logits, zr, BH, N, s, mk.at(3));
   if (e != hipSuccess) return hip_fail(e, "reverse launch");
-  if ((st = mix_impl(plan, zr, dO, dV, workspace, s)) != CAT_OK) return st;
+  if ((st = mix_impl(plan, zr, dO, dV, workspace, s, &mk)) != CAT_OK) return st;
   // dz*: channel-pair copies (fp32) of dO and V, cross-correlation spectra
   // per pair group, summed per (batch, head)
   float* Qb = reinterpret_cast<float*>(ws_at(workspace, plan->off_Q));
@@ -748,10 +750,10 @@ cat_status cat_step_mix_backward_1d(cat_plan plan, const float* logits, const vo
   ra.cg = 2;
   ra.src = dO;
   ra.dst = Qb;
-  if ((e = launch_relayout(ra, s)) != hipSuccess) return hip_fail(e, "relayout launch");
+  if ((e = launch_relayout(ra, s, mk.at(4))) != hipSuccess) return hip_fail(e, "relayout launch");
   ra.src = V;
   ra.dst = Kb;
-  if ((e = launch_relayout(ra, s)) != hipSuccess) return hip_fail(e, "relayout launch");
+  if ((e = launch_relayout(ra, s, mk.at(4))) != hipSuccess) return hip_fail(e, "relayout launch");
   ScoreArgs sc{};
   sc.Q = Qb;
   sc.K = Kb;
@@ -762,15 +764,18 @@ cat_status cat_step_mix_backward_1d(cat_plan plan, const float* logits, const vo
   sc.ngrp = plan->ngrp;
   sc.ppg = plan->ppg;
   sc.tw = plan->d_tw;
-  if ((e = launch_score_partial(plan->geom, sc, s)) != hipSuccess) return hip_fail(e, "score-gradient launch");
-  if ((e = launch_psum(part, psum, BH, plan->ngrp, plan->L, s)) != hipSuccess) return hip_fail(e, "psum launch");
+  if ((e = launch_score_partial(plan->geom, sc, s, mk.at(5))) != hipSuccess)
+    return hip_fail(e, "score-gradient launch");
+  if ((e = launch_psum(part, psum, BH, plan->ngrp, plan->L, s, mk.at(6))) != hipSuccess)
+    return hip_fail(e, "psum launch");
   // dlogits = z* (dz* - <z*, dz*>)
   SpecArgs sa = spec_base(plan, workspace);
   sa.logits = logits;
   sa.partial = psum;
   sa.ngrp = 1;
   sa.probs = dlogits;
-  if ((e = launch_spectrum(plan->geom, 2, sa, s)) != hipSuccess) return hip_fail(e, "logits-gradient launch");
+  if ((e = launch_spectrum(plan->geom, 2, sa, s, mk.at(7))) != hipSuccess)
+    return hip_fail(e, "logits-gradient launch");
   return check_sync(plan, "mixing backward");
 }
 

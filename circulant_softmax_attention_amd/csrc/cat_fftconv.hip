@@ -157,17 +157,28 @@ hipError_t launch_psum(const float2* part, float2* out, int BH, int ngrp, int L,
   return launch_k(psum_kernel, dim3((unsigned)blocks), dim3(256), 0, s, t, part, out, BH, ngrp, L);
 }
 
-hipError_t launch_relayout(const RelayoutArgs& a, hipStream_t s) {
-  const size_t total = (size_t)a.B * a.N * a.D;
-  const int blocks = (int)std::min<size_t>((total + 255) / 256, 65536);
-  if (a.src_et == ET_F32) {
-    hipLaunchKernelGGL((kern::relayout_kernel<ET_F32, 1>), dim3(blocks), dim3(256), 0, s, a);
-  } else if (a.dst_f32) {
-    hipLaunchKernelGGL((kern::relayout_kernel<ET_BF16, 1>), dim3(blocks), dim3(256), 0, s, a);
-  } else {
-    hipLaunchKernelGGL((kern::relayout_kernel<ET_BF16, 0>), dim3(blocks), dim3(256), 0, s, a);
+hipError_t launch_relayout(const RelayoutArgs& a, hipStream_t s, const LaunchTiming* t) {
+  if (a.D % 8 != 0 || a.d % 2 != 0 || a.cg % 2 != 0 || a.d % a.cg != 0) return hipErrorInvalidValue;
+  if (a.D % 64 == 0 && 64 % a.cg == 0) {
+    // 64 x 64 tiles through LDS
+    const size_t nb = (size_t)a.B * ((a.N + 63) / 64) * (a.D / 64);
+    if (nb == 0) return hipSuccess;
+    if (nb > 0x7fffffffu) return hipErrorInvalidValue;
+    if (a.src_et == ET_F32)
+      return launch_k(kern::relayout_tile_kernel<ET_F32, 1>, dim3((unsigned)nb), dim3(256), 0, s, t, a);
+    if (a.dst_f32) return launch_k(kern::relayout_tile_kernel<ET_BF16, 1>, dim3((unsigned)nb), dim3(256), 0, s, t, a);
+    return launch_k(kern::relayout_tile_kernel<ET_BF16, 0>, dim3((unsigned)nb), dim3(256), 0, s, t, a);
   }
-  return hipGetLastError();
+  // otherwise one thread per 16-byte chunk of a row, 4 rows each (D % 8 == 0)
+  const int VE = a.src_et == ET_F32 ? 4 : 8;
+  const size_t threads = (((size_t)a.B * a.N + 3) / 4) * (size_t)(a.D / VE);
+  if (threads == 0) return hipSuccess;
+  const size_t nb = (threads + 255) / 256;
+  if (nb > 0x7fffffffu) return hipErrorInvalidValue;
+  const int blocks = (int)nb;
+  if (a.src_et == ET_F32) return launch_k(kern::relayout_kernel<ET_F32, 1>, dim3(blocks), dim3(256), 0, s, t, a);
+  if (a.dst_f32) return launch_k(kern::relayout_kernel<ET_BF16, 1>, dim3(blocks), dim3(256), 0, s, t, a);
+  return launch_k(kern::relayout_kernel<ET_BF16, 0>, dim3(blocks), dim3(256), 0, s, t, a);
 }
 
 }  // namespace cat

@@ -203,7 +203,7 @@ hipError_t launch_longconv(int et, const LongArgs& a, const float* logits, const
 // out [BH][L], complex fp32; summed in order g = 0, 1, ..).
 hipError_t launch_psum(const float2* part, float2* out, int BH, int ngrp, int L, hipStream_t s,
                        const LaunchTiming* t = nullptr);
-hipError_t launch_relayout(const RelayoutArgs& a, hipStream_t s);
+hipError_t launch_relayout(const RelayoutArgs& a, hipStream_t s, const LaunchTiming* t = nullptr);
 // Raise the dynamic-LDS limit of the kernels a geometry uses (once per plan).
 hipError_t prepare_kernels(const LineGeom& g, size_t conv_lds, size_t spec_lds, size_t score_lds);
 

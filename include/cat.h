@@ -164,9 +164,12 @@ cat_status cat_forward_bccb_2d(cat_plan plan, const void* X, const void* W_Q, co
  * launches each).  Enabling resets the slots.  cat_plan_kernel_times waits
  * for the recorded events and returns, per kernel of the path (1D:
  * projection, spectrum, fft-conv -- the mixing launch of whichever path the
- * plan takes; 2D: projection, scores, spectrum, fft-conv, partial-score
- * sum), the summed milliseconds and the number of launches measured;
- * *nkernels receives the number of kernels (arrays hold at least 8). */
+ * plan takes -- then the mixing backward's own: logits reversal, relayout,
+ * score-gradient partials, partial sum, logits gradient; 2D: projection,
+ * scores, spectrum, fft-conv, partial-score sum), the summed milliseconds
+ * and the number of launches measured; *nkernels receives the number of
+ * kernels (arrays hold at least 8).  cat_forward_* and
+ * cat_step_mix_backward_1d record; the other step calls do not. */
 cat_status cat_plan_set_timing(cat_plan plan, int enable);
 cat_status cat_plan_kernel_times(cat_plan plan, double* total_ms, int64_t* launches, int* nkernels);
 

@@ -253,12 +253,10 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
     off = up256(off + BH * p->N * sizeof(float));
     pl->off_Q = pl->off_K = pl->off_part = pl->off_psum = 0;
     if (!longn) {
-      // the mixing backward: fp32 copies of dO and V (channel pairs), the
-      // score-gradient partials and their sum
+      // the mixing backward: V in the blocked layout, the score-gradient
+      // partials and their sum
       pl->off_Q = off;
-      off = up256(off + BND * sizeof(float));
-      pl->off_K = off;
-      off = up256(off + BND * sizeof(float));
+      off = up256(off + BND * pl->esz);
       pl->off_part = off;
       off = up256(off + BH * pl->ngrp * pl->L * sizeof(float2));
       pl->off_psum = off;
@@ -635,6 +633,8 @@ cat_status cat_forward_bccb_2d(cat_plan plan, const void* X, const void* W_Q, co
   sc.npair = plan->npair;
   sc.ngrp = plan->ngrp;
   sc.ppg = plan->ppg;
+  sc.et = ET_F32;
+  sc.cg = 2;
   e = launch_score_partial(plan->geom, sc, s, mk.at(1));
   if (e != hipSuccess) return hip_fail(e, "score launch");
   if ((st = check_sync(plan, "scores")) != CAT_OK) return st;
@@ -733,30 +733,30 @@ cat_status cat_step_mix_backward_1d(cat_plan plan, const float* logits, const vo
   hipError_t e = launch_reverse_lines(logits, zr, BH, N, s, mk.at(3));
   if (e != hipSuccess) return hip_fail(e, "reverse launch");
   if ((st = mix_impl(plan, zr, dO, dV, workspace, s, &mk)) != CAT_OK) return st;
-  // dz*: channel-pair copies (fp32) of dO and V, cross-correlation spectra
-  // per pair group, summed per (batch, head)
-  float* Qb = reinterpret_cast<float*>(ws_at(workspace, plan->off_Q));
-  float* Kb = reinterpret_cast<float*>(ws_at(workspace, plan->off_K));
+  // dz*: cross-correlation spectra of dO and V per pair group, summed per
+  // (batch, head).  dO is still in the workspace in the blocked layout the
+  // dV mixing made of it; V gets the same layout.
+  const void* dOb = ws_at(workspace, plan->off_V);
+  void* Vb = ws_at(workspace, plan->off_Q);
   float2* part = reinterpret_cast<float2*>(ws_at(workspace, plan->off_part));
   float2* psum = reinterpret_cast<float2*>(ws_at(workspace, plan->off_psum));
   RelayoutArgs ra{};
+  ra.src = V;
+  ra.dst = Vb;
   ra.src_et = plan->et;
-  ra.dst_f32 = 1;
+  ra.dst_f32 = 0;
   ra.B = (int)plan->p.B;
   ra.N = N;
   ra.D = (int)plan->p.D;
   ra.H = (int)plan->p.H;
   ra.d = plan->d;
-  ra.cg = 2;
-  ra.src = dO;
-  ra.dst = Qb;
-  if ((e = launch_relayout(ra, s, mk.at(4))) != hipSuccess) return hip_fail(e, "relayout launch");
-  ra.src = V;
-  ra.dst = Kb;
+  ra.cg = plan->cg;
   if ((e = launch_relayout(ra, s, mk.at(4))) != hipSuccess) return hip_fail(e, "relayout launch");
   ScoreArgs sc{};
-  sc.Q = Qb;
-  sc.K = Kb;
+  sc.Q = dOb;
+  sc.K = Vb;
+  sc.et = plan->et;
+  sc.cg = plan->cg;
   sc.partial = part;
   sc.BH = BH;
   sc.N = N;
@@ -816,6 +816,8 @@ cat_status cat_step_scores_2d(cat_plan plan, const float* Q, const float* K, flo
   sc.npair = plan->npair;
   sc.ngrp = plan->ngrp;
   sc.ppg = plan->ppg;
+  sc.et = ET_F32;
+  sc.cg = 2;
   e = launch_score_partial(plan->geom, sc, s);
   if (e != hipSuccess) return hip_fail(e, "score launch");
   if ((st = check_sync(plan, "scores")) != CAT_OK) return st;

@@ -71,6 +71,7 @@ hipError_t prepare_kernels(const LineGeom& g, size_t conv_lds, size_t spec_lds, 
   raise((const void*)e->spec1, spec_lds);
   raise((const void*)e->spec2, spec_lds);
   raise((const void*)e->score, score_lds);
+  raise((const void*)e->score_bf16, score_lds);
   return err;
 }
 
@@ -100,8 +101,8 @@ hipError_t launch_conv(const LineGeom& g, int et, const ConvArgs& a, hipStream_t
 
 hipError_t launch_score_partial(const LineGeom& g, const ScoreArgs& a, hipStream_t s, const LaunchTiming* t) {
   const Entry* e = find_entry(g);
-  ScoreFn fn = e ? e->score : nullptr;
-  if (!fn) return hipErrorInvalidValue;
+  ScoreFn fn = e ? (a.et == ET_F32 ? e->score : e->score_bf16) : nullptr;
+  if (!fn || a.cg < 2 || a.cg % 2 != 0 || a.npair % (a.cg / 2) != 0) return hipErrorInvalidValue;
   const size_t lds = 2 * line_lds_bytes(g);
   return launch_k(fn, dim3(a.BH * a.ngrp), dim3(2 * e->T), lds, s, t, a);
 }

@@ -133,11 +133,12 @@ struct ConvArgs {
 // 2D scores: for each (bh, group of pairs) accumulate
 //   sum_pairs FFT2(q pair) . conj(FFT2(k pair))   into partial[bh][grp][L]
 struct ScoreArgs {
-  const float* Q;  // BLOCKED fp32, cg = 2: [BH][npair][N][2]
-  const float* K;
+  const void* Q;  // BLOCKED [BH][npair / (cg / 2)][N][cg], element type et
+  const void* K;
   float2* partial;  // [BH][ngrp][L] complex
   int BH, N, npair, ngrp, ppg;
   const float2* tw;  // 1D inter-pass twiddles (null for 2D)
+  int et, cg;        // ET_F32 (2D: fp32, cg = 2) or ET_BF16 (1D only); cg even, (cg / 2) | npair
 };
 
 struct RelayoutArgs {

@@ -347,9 +347,11 @@ def backward_model(wl, L: int, ngrp: int, fwd_model):
     lines = BH * (d // 2)
     m = {k: v for k, v in fwd_model.items() if k in ("spectrum", "fftconv", "directconv")}
     m["reverse"] = dict(bytes=2 * BH * N * 4, flops=0.0, unit="valu_f32")
-    # dO to the blocked storage layout (read + write), dO and V to fp32 pairs (read, write fp32)
-    m["relayout"] = dict(bytes=2 * T * D * s + 2 * (T * D * s + T * D * 4), flops=0.0, unit="valu_f32")
-    m["score_grad"] = dict(bytes=2 * T * D * 4 + BH * ngrp * L * 8,
+    # dO (for the dV mixing) and V (for the score gradient) to the blocked
+    # layout in the storage dtype: read + write each
+    m["relayout"] = dict(bytes=2 * (2 * T * D * s), flops=0.0, unit="valu_f32")
+    # the blocked dO and V read once, the per-group partial spectra written
+    m["score_grad"] = dict(bytes=2 * T * D * s + BH * ngrp * L * 8,
                            flops=lines * (2 * fft_flops(L) + 8.0 * L), unit="valu_f32")
     m["psum"] = dict(bytes=BH * ngrp * L * 8 + BH * L * 8, flops=2.0 * BH * (ngrp - 1) * L, unit="valu_f32")
     m["logits_grad"] = dict(bytes=BH * L * 8 + 2 * BH * N * 4, flops=BH * (fft_flops(L) + 8.0 * N), unit="valu_f32")
@@ -451,15 +453,17 @@ def run_backward(args):
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
-        zc = z0[:1].cpu().numpy()
-        Vc = V0[:1].float().cpu().numpy()
-        gc = dO0[:1].float().cpu().numpy()
-        t0 = time.perf_counter()
-        oracle.mix_backward_1d(zc, Vc, gc)
-        secs = time.perf_counter() - t0
-        cpu = dict(value=wl.N / secs, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
-                   sample=f"1 of {wl.B} sequences ({wl.N} tokens), fp64 direct O(N^2 d) sums for dV and dz*, "
-                          f"{secs:.1f} s")
+        # whole sequences, one at a time, until about --cpu-seconds of work
+        zc, Vc, gc = z0.cpu().numpy(), V0.float().cpu().numpy(), dO0.float().cpu().numpy()
+        secs, nseq = 0.0, 0
+        while nseq < wl.B and (nseq == 0 or secs < args.cpu_seconds):
+            t0 = time.perf_counter()
+            oracle.mix_backward_1d(zc[nseq:nseq + 1], Vc[nseq:nseq + 1], gc[nseq:nseq + 1])
+            secs += time.perf_counter() - t0
+            nseq += 1
+        cpu = dict(value=nseq * wl.N / secs, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
+                   sample=f"{nseq} of {wl.B} sequences ({nseq * wl.N} tokens), fp64 direct O(N^2 d) sums for dV "
+                          f"and dz*, {secs:.1f} s")
         log("cpu baseline:", cpu)
 
     tokens = wl.B * wl.N

@@ -115,6 +115,9 @@ KERNEL_SOURCES["directconv"] = ["circulant_softmax_attention_amd/csrc/cat_dconv.
                                  "circulant_softmax_attention_amd/csrc/cat_common.hpp"]
 KERNEL_SOURCES["spectrum"] = KERNEL_SOURCES["fftconv"]
 KERNEL_SOURCES["scores"] = KERNEL_SOURCES["fftconv"]
+KERNEL_SOURCES["score_grad"] = ["circulant_softmax_attention_amd/csrc/cat_fftconv.hpp",
+                                "circulant_softmax_attention_amd/csrc/cat_fft.hpp",
+                                "circulant_softmax_attention_amd/csrc/cat_common.hpp"]
 
 
 def measured_traffic(kernel: str, workload: str, launches_per_call: int):
@@ -446,8 +449,9 @@ def run_backward(args):
         bound, achieved, peak, unit = "hbm", kd["bytes"] / sec / 1e9, HBM_PEAK_GBS, "GB/s"
     else:
         bound, achieved, peak, unit = "alu", kd["flops"] / sec / 1e12, PEAK_TFLOPS[kd["compute_unit"]], "TFLOP/s"
+    traffic = measured_traffic(dom, wl.name, kd["launches_per_call"]) if dom in KERNEL_SOURCES else None
     roofline = dict(kernel=dom, bound=bound, achieved=round(achieved, 2), peak=peak, unit=unit,
-                    frac=round(achieved / peak, 4), traffic=None, hbm_frac=kd["hbm_frac"],
+                    frac=round(achieved / peak, 4), traffic=traffic, hbm_frac=kd["hbm_frac"],
                     compute_frac=kd["compute_frac"], us=kd["us"])
 
     cpu = None

@@ -141,9 +141,12 @@ __device__ __forceinline__ float2 load_c(const void* base, size_t i) {
 // L = N; otherwise its wrapped extension (z*[j] for j < N, z*[j - (L - N)]
 // for j > L - N, zero between; L >= 2N - 1 keeps the two ranges apart).
 // zl: the line's logits; ms: (max, 1 / sum of exp).
+// The load is clamped to a valid token and the zero selected afterwards, so
+// no load sits behind a branch and all of a thread's loads issue together.
 __device__ __forceinline__ float circle_score(const float* __restrict__ zl, int j, int N, int L, float2 ms) {
   const int n = j < N ? j : j > L - N ? j - (L - N) : -1;
-  return n < 0 ? 0.f : __expf(zl[n] - ms.x) * ms.y;
+  const float v = __expf(zl[n < 0 ? 0 : n] - ms.x) * ms.y;
+  return n < 0 ? 0.f : v;
 }
 
 // ---- softmax partials: chunk c (SMC logits, the last one ragged) of line
@@ -194,8 +197,10 @@ __global__ __launch_bounds__(LTHR) void softmax_part_kernel(const float* __restr
 // ---- column pass: CB adjacent columns n2 of block `gl`, every pair:
 // A[gl][k1][n2][j] = W_L^(k1 n2) DFT_L1 over n1 of x[n1 L2 + n2][j].
 // SET: ET_F32 (float2 values), ET_BF16 (bf16 pairs), or 2 (fp32 logits,
-// softmax from the chunk partials; PB = 1).
-template <int SET>
+// softmax from the chunk partials; PB = 1).  WRAP: the line is shorter than
+// the circle (values zero past N, the softmax line wrapped); without it
+// L = N and every load is a plain one.
+template <int SET, bool WRAP>
 __global__ __launch_bounds__(LTHR) void col_fwd_kernel(LongArgs a, int PB, const void* __restrict__ src,
                                                        float2* __restrict__ A, const float2* __restrict__ smpart) {
   __shared__ float2 buf[2][LPAD];
@@ -225,12 +230,21 @@ __global__ __launch_bounds__(LTHR) void col_fwd_kernel(LongArgs a, int PB, const
   for (int q = threadIdx.x; q < R * L1; q += LTHR) {
     const int n1 = q / R, r = q - n1 * R;
     const int j = n1 * L2 + n20 + r / PB;  // position on the circle
-    if constexpr (SET == 2)
+    if constexpr (!WRAP) {  // L = N
+      const size_t i = gbase + ((size_t)n1 * L2 + n20) * PB + r;
+      if constexpr (SET == 2)
+        buf[0][r * (L1 + 1) + n1] = make_float2(__expf(reinterpret_cast<const float*>(src)[i] - msum.x) * msum.y, 0.f);
+      else
+        buf[0][r * (L1 + 1) + n1] = load_c<SET>(src, i);
+    } else if constexpr (SET == 2) {
       buf[0][r * (L1 + 1) + n1] =
           make_float2(circle_score(reinterpret_cast<const float*>(src) + (size_t)gl * a.N, j, a.N, L, msum), 0.f);
-    else
-      buf[0][r * (L1 + 1) + n1] = j < a.N ? load_c<SET>(src, (size_t)gl * a.N * PB + ((size_t)n1 * L2 + n20) * PB + r)
-                                          : make_float2(0.f, 0.f);
+    } else {
+      // clamped load, then select (past N: zero padding)
+      const bool ok = j < a.N;
+      const float2 v = load_c<SET>(src, (size_t)gl * a.N * PB + (ok ? ((size_t)n1 * L2 + n20) * PB : 0) + r);
+      buf[0][r * (L1 + 1) + n1] = ok ? v : make_float2(0.f, 0.f);
+    }
   }
   stage_twiddles(tws, a.logL1, a.tw, a.logL1 + a.logL2);
   const float2* U = lds_fft<false>(buf[0], buf[1], L1, a.logL1, R, tws);
@@ -362,7 +376,7 @@ __global__ __launch_bounds__(128) void row_reg_kernel(LongArgs a, int PB, float2
 // Forward: SET as col_fwd_kernel.  Lane t of line r = c PB + j holds
 // x[(ma MS + t) L2 + n20 + c][j] in register ma; after the transform it
 // holds k1 = t + MS kb in register kb.
-template <int SET, int MS>
+template <int SET, int MS, bool WRAP>
 __global__ __launch_bounds__(128) void col_reg_kernel(LongArgs a, int PB, const void* __restrict__ src,
                                                       float2* __restrict__ A, const float2* __restrict__ smpart) {
   constexpr int M = MS * MS, R = 128 / MS, TP = MS * (MS + 1);
@@ -394,10 +408,20 @@ __global__ __launch_bounds__(128) void col_reg_kernel(LongArgs a, int PB, const 
   for (int ma = 0; ma < MS; ++ma) {
     const int n = (ma * MS + t) * L2 + n20;
     float2 v;
-    if constexpr (SET == 2)
+    if constexpr (!WRAP) {  // L = N
+      const size_t i = gbase + (size_t)n * PB + r;
+      if constexpr (SET == 2)
+        v = make_float2(__expf(reinterpret_cast<const float*>(src)[i] - msum.x) * msum.y, 0.f);
+      else
+        v = load_c<SET>(src, i);
+    } else if constexpr (SET == 2) {
       v = make_float2(circle_score(reinterpret_cast<const float*>(src) + (size_t)gl * a.N, n + c, a.N, L, msum), 0.f);
-    else
-      v = n + c < a.N ? load_c<SET>(src, (size_t)gl * a.N * PB + (size_t)n * PB + r) : make_float2(0.f, 0.f);
+    } else {
+      // clamped load, then select (past N: zero padding)
+      const bool ok = n + c < a.N;
+      v = load_c<SET>(src, (size_t)gl * a.N * PB + (ok ? (size_t)n * PB : 0) + r);
+      v = ok ? v : make_float2(0.f, 0.f);
+    }
     x[ma] = cfm(v.x, v.y);
   }
   reg_fft<MS, false>(x, t, xb + r * TP, twm);
@@ -518,19 +542,25 @@ hipError_t launch_longconv(int et, const LongArgs& a, const float* logits, const
   hipError_t e = launch_k(softmax_part_kernel, dim3((unsigned)(a.BH * smc_chunks(N))), dim3(LTHR), 0, s, t[0], logits, zc, N);
   if (e != hipSuccess) return e;
   // column passes on registers when L1 is a square of 8 or 16 (C = 128 / sqrt(L1) lines per workgroup)
+  const bool wrap = N != L;
+  auto col = [&](auto plain, auto wrapped, unsigned grid, unsigned threads, const LaunchTiming* tt, int pb,
+                 const void* src, float2* dst, const float2* sm) {
+    return wrap ? launch_k(wrapped, dim3(grid), dim3(threads), 0, s, tt, a, pb, src, dst, sm)
+                : launch_k(plain, dim3(grid), dim3(threads), 0, s, tt, a, pb, src, dst, sm);
+  };
   const int mc = L1 == 256 ? 16 : L1 == 64 ? 8 : 0;
   const int cl = mc ? 128 / mc : 0;
   if (mc) {
-    const long cz = (long)a.BH * (L2 / cl);
+    const unsigned cz = (unsigned)((long)a.BH * (L2 / cl));
     if (mc == 16)
-      e = launch_k(col_reg_kernel<2, 16>, dim3((unsigned)cz), dim3(128), 0, s, t[1], a, 1, (const void*)logits, Az,
-                   (const float2*)zc);
+      e = col(col_reg_kernel<2, 16, false>, col_reg_kernel<2, 16, true>, cz, 128, t[1], 1, (const void*)logits, Az,
+              (const float2*)zc);
     else
-      e = launch_k(col_reg_kernel<2, 8>, dim3((unsigned)cz), dim3(128), 0, s, t[1], a, 1, (const void*)logits, Az,
-                   (const float2*)zc);
+      e = col(col_reg_kernel<2, 8, false>, col_reg_kernel<2, 8, true>, cz, 128, t[1], 1, (const void*)logits, Az,
+              (const float2*)zc);
   } else {
-    e = launch_k(col_fwd_kernel<2>, dim3((unsigned)colb_z), dim3(LTHR), 0, s, t[1], a, 1, (const void*)logits, Az,
-                 (const float2*)zc);
+    e = col(col_fwd_kernel<2, false>, col_fwd_kernel<2, true>, (unsigned)colb_z, LTHR, t[1], 1, (const void*)logits, Az,
+            (const float2*)zc);
   }
   if (e != hipSuccess) return e;
   // row passes on registers when L2 is a square of 8 or 16 (R = 128 / sqrt(L2) lines per workgroup)
@@ -547,23 +577,20 @@ hipError_t launch_longconv(int et, const LongArgs& a, const float* logits, const
   }
   if (e != hipSuccess) return e;
   // the mixing, PB pairs per block
-  const long cv = mc ? blocks * (L2 / (cl / PB)) : 0;
+  const unsigned cv = mc ? (unsigned)(blocks * (L2 / (cl / PB))) : 0;
+  const float2* nosm = nullptr;
   if (mc == 16)
-    e = et == ET_F32 ? launch_k(col_reg_kernel<ET_F32, 16>, dim3((unsigned)cv), dim3(128), 0, s, t[3], a, PB, V, A,
-                                (const float2*)nullptr)
-                     : launch_k(col_reg_kernel<ET_BF16, 16>, dim3((unsigned)cv), dim3(128), 0, s, t[3], a, PB, V, A,
-                                (const float2*)nullptr);
+    e = et == ET_F32 ? col(col_reg_kernel<ET_F32, 16, false>, col_reg_kernel<ET_F32, 16, true>, cv, 128, t[3], PB, V, A, nosm)
+                     : col(col_reg_kernel<ET_BF16, 16, false>, col_reg_kernel<ET_BF16, 16, true>, cv, 128, t[3], PB, V, A,
+                           nosm);
   else if (mc == 8)
-    e = et == ET_F32 ? launch_k(col_reg_kernel<ET_F32, 8>, dim3((unsigned)cv), dim3(128), 0, s, t[3], a, PB, V, A,
-                                (const float2*)nullptr)
-                     : launch_k(col_reg_kernel<ET_BF16, 8>, dim3((unsigned)cv), dim3(128), 0, s, t[3], a, PB, V, A,
-                                (const float2*)nullptr);
+    e = et == ET_F32 ? col(col_reg_kernel<ET_F32, 8, false>, col_reg_kernel<ET_F32, 8, true>, cv, 128, t[3], PB, V, A, nosm)
+                     : col(col_reg_kernel<ET_BF16, 8, false>, col_reg_kernel<ET_BF16, 8, true>, cv, 128, t[3], PB, V, A,
+                           nosm);
   else if (et == ET_F32)
-    e = launch_k(col_fwd_kernel<ET_F32>, dim3((unsigned)colb), dim3(LTHR), 0, s, t[3], a, PB, V, A,
-                 (const float2*)nullptr);
+    e = col(col_fwd_kernel<ET_F32, false>, col_fwd_kernel<ET_F32, true>, (unsigned)colb, LTHR, t[3], PB, V, A, nosm);
   else
-    e = launch_k(col_fwd_kernel<ET_BF16>, dim3((unsigned)colb), dim3(LTHR), 0, s, t[3], a, PB, V, A,
-                 (const float2*)nullptr);
+    e = col(col_fwd_kernel<ET_BF16, false>, col_fwd_kernel<ET_BF16, true>, (unsigned)colb, LTHR, t[3], PB, V, A, nosm);
   if (e != hipSuccess) return e;
   if (ms) {
     const long rv = blocks * (L1 / (rl / PB));

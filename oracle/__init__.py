@@ -20,6 +20,9 @@ the steps in the order the pages give:
       dV_h = circ(Z*_h)^T G_h,   dZ*_h[k] = sum_c sum_i G[i][c] V[(i - k) mod N][c],
       dZ_h = Z*_h . (dZ*_h - <Z*_h, dZ*_h>)
 
+  CAT-scored 2D variant: the CAT scores z = X W_A, softmaxed over the grid,
+  as the filter of the 2D circular convolution below.
+
   2D circulant attention (Vision Transformers are Circulant Attention
   Learners, "Circulant Attention: attention rebuilt with the FFT"):
       Q, K, V = X W_Q, X W_K, X W_V
@@ -227,6 +230,23 @@ def cat_forward_1d(X, W_A, W_V, rows: Optional[Sequence[int]] = None) -> Dict[st
     zstar = softmax(z)
     V = matmul(X, W_V)
     O = circulant_1d(zstar, V, rows=rows)
+    return {"z": z, "zstar": zstar, "V": V, "O": O}
+
+
+def cat_scored_forward_2d(X, W_A, W_V, Hg: int, Wg: int, rows: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
+    """CAT's scoring on a token grid: z = X W_A (one column per head),
+    z* = softmax over all Hg*Wg tokens, O_h = BCCB(z*_h) V_h (2D circular
+    convolution).  The circulant-attention page models the attention map as
+    a BCCB matrix ("Circulant Attention: attention rebuilt with the FFT");
+    here its filter comes from CAT's per-head score projection (CAT,
+    "Method details / Overall framework") instead of the Q/K correlation.
+    Returns z ([B,H,N]), zstar, V and O."""
+    z = scores_1d(X, W_A)
+    zstar = softmax(z)
+    V = matmul(X, W_V)
+    B, H, N = zstar.shape
+    assert N == Hg * Wg
+    O = bccb_2d(zstar.reshape(B, H, Hg, Wg), V, rows=rows)
     return {"z": z, "zstar": zstar, "V": V, "O": O}
 
 

@@ -448,6 +448,55 @@ def test_planted_conjugate_on_wrong_side_is_caught():
     assert not np.array_equal(bad[0, 0], np.array(case["a"]))
 
 
+# ---------------------------------------------------------------- CAT-scored 2D variant
+@pytest.mark.parametrize("Hg,Wg", [(1, 7), (5, 1), (1, 12)])
+def test_cat_scored_2d_on_a_line_is_cat_1d(Hg, Wg):
+    """A 1 x N (or N x 1) grid's BCCB matrix is the circulant of the line, so
+    the CAT-scored 2D forward equals the 1D CAT forward there."""
+    rng = np.random.default_rng(40 + Hg * Wg)
+    B, D, H = 2, 6, 3
+    N = Hg * Wg
+    X = rng.standard_normal((B, N, D))
+    WA, WV = rng.standard_normal((D, H)), rng.standard_normal((D, D))
+    got = oracle.cat_scored_forward_2d(X, WA, WV, Hg, Wg)["O"]
+    assert np.allclose(got, oracle.cat_forward_1d(X, WA, WV)["O"], rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("s1,s2", [(1, 0), (0, 2), (2, 3)])
+def test_cat_scored_2d_grid_roll_rolls_output_twice(s1, s2):
+    """Scores move with their tokens and so do the values: rolling X on the
+    grid by (s1, s2) rolls the output by (2 s1, 2 s2)."""
+    rng = np.random.default_rng(7)
+    B, Hg, Wg, D, H = 1, 4, 5, 4, 2
+    X = rng.standard_normal((B, Hg * Wg, D))
+    WA, WV = rng.standard_normal((D, H)), rng.standard_normal((D, D))
+
+    def fwd(x):
+        return oracle.cat_scored_forward_2d(x, WA, WV, Hg, Wg)["O"].reshape(B, Hg, Wg, D)
+
+    Xr = np.roll(X.reshape(B, Hg, Wg, D), (s1, s2), axis=(1, 2)).reshape(B, Hg * Wg, D)
+    assert np.allclose(fwd(Xr), np.roll(fwd(X), (2 * s1, 2 * s2), axis=(1, 2)), atol=1e-12)
+
+
+def test_cat_scored_2d_matches_materialised_bccb():
+    """Against the BCCB matrix built entry by entry from the softmaxed scores."""
+    rng = np.random.default_rng(5)
+    B, Hg, Wg, D, H = 1, 3, 4, 4, 2
+    N, d = Hg * Wg, D // H
+    X = rng.standard_normal((B, N, D))
+    WA, WV = rng.standard_normal((D, H)), rng.standard_normal((D, D))
+    got = oracle.cat_scored_forward_2d(X, WA, WV, Hg, Wg)["O"]
+    z = X[0] @ WA
+    zs = np.exp(z - z.max(axis=0)) / np.exp(z - z.max(axis=0)).sum(axis=0)
+    V = X[0] @ WV
+    for h in range(H):
+        C = np.zeros((N, N))
+        for i in range(N):
+            for j in range(N):
+                C[i, j] = zs[((i // Wg - j // Wg) % Hg) * Wg + (i % Wg - j % Wg) % Wg, h]
+        assert np.allclose(got[0][:, h * d:(h + 1) * d], C @ V[:, h * d:(h + 1) * d], atol=1e-12)
+
+
 # ---------------------------------------------------------------- 1D mixing backward
 def _mix_loss(z, V, G):
     """The scalar <circ(softmax(z)) V, G> whose gradients the backward gives."""

@@ -27,7 +27,7 @@ CAT_1D, CAT_BCCB_2D = 0, 1
 
 # Every symbol include/cat.h declares.
 EXPORTS = ["cat_plan_create", "cat_plan_destroy", "cat_plan_workspace_size", "cat_plan_geometry",
-           "cat_forward_1d", "cat_forward_bccb_2d", "cat_status_string", "cat_last_error",
+           "cat_forward_1d", "cat_forward_bccb_2d", "cat_forward_cat_2d", "cat_status_string", "cat_last_error",
            "cat_plan_set_timing", "cat_plan_kernel_times", "cat_plan_conv_path",
            "cat_step_project", "cat_step_spectrum", "cat_step_mix", "cat_step_mix_backward_1d",
            "cat_step_scores_2d"]
@@ -58,6 +58,7 @@ def _load() -> ctypes.CDLL:
     lib.cat_plan_geometry.argtypes = [vp] + [ctypes.POINTER(ctypes.c_int64)] * 3
     lib.cat_forward_1d.argtypes = [vp] * 7
     lib.cat_forward_bccb_2d.argtypes = [vp] * 8
+    lib.cat_forward_cat_2d.argtypes = [vp] * 7
     lib.cat_plan_set_timing.argtypes = [vp, ctypes.c_int]
     lib.cat_plan_conv_path.argtypes = [vp, ctypes.POINTER(ctypes.c_int)]
     lib.cat_plan_kernel_times.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64),
@@ -227,6 +228,20 @@ def cat_forward_bccb_2d(plan: Plan, X, W_Q, W_K, W_V, O=None, workspace=None, st
                                     _ptr(W_V, (D, D), dt, "W_V"), _ptr(O, (B, N, D), dt, "O"),
                                     _ptr(workspace, None, None, "workspace"), _stream_ptr(stream)),
            "cat_forward_bccb_2d")
+    return O
+
+
+def cat_forward_cat_2d(plan: Plan, X, W_A, W_V, O=None, workspace=None, stream=None) -> torch.Tensor:
+    """O = the CAT-scored 2D variant per include/cat.h (W_A [D, H], W_V [D, D])."""
+    B, N, D, H, dt = plan.B, plan.N, plan.D, plan.H, plan.dtype
+    if O is None:
+        O = torch.empty((B, N, D), dtype=dt, device=X.device)
+    if workspace is None:
+        workspace = alloc_workspace(plan, X.device)
+    _check(_lib.cat_forward_cat_2d(ctypes.c_void_p(plan.handle), _ptr(X, (B, N, D), dt, "X"),
+                                   _ptr(W_A, (D, H), dt, "W_A"), _ptr(W_V, (D, D), dt, "W_V"),
+                                   _ptr(O, (B, N, D), dt, "O"), _ptr(workspace, None, None, "workspace"),
+                                   _stream_ptr(stream)), "cat_forward_cat_2d")
     return O
 
 

@@ -271,7 +271,8 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
       off = up256(off + BH * pl->L * sizeof(float2));
     }
   } else {
-    pl->off_z = 0;
+    pl->off_z = off;  // the CAT-scored variant's logits
+    off = up256(off + BH * p->N * sizeof(float));
     pl->off_Q = off;
     off = up256(off + BND * sizeof(float));
     pl->off_K = off;
@@ -596,6 +597,43 @@ cat_status cat_forward_1d(cat_plan plan, const void* X, const void* W_A, const v
   ConvArgs ca = conv_base(plan, Vb, sa.spec, O);
   if (own_softmax) ca.logits = z;
   e = run_conv_1d(plan, ca, s, mk.at(2));
+  if (e != hipSuccess) return hip_fail(e, "fft-conv launch");
+  return check_sync(plan, "fft-conv");
+}
+
+cat_status cat_forward_cat_2d(cat_plan plan, const void* X, const void* W_A, const void* W_V, void* O,
+                              void* workspace, void* stream) {
+  if (!plan) return fail(CAT_ERR_INVALID_ARG, "NULL plan");
+  if (plan->p.kind != CAT_BCCB_2D) return fail(CAT_ERR_PLAN_MISMATCH, "plan is not 2D");
+  if (plan->p.B == 0) return CAT_OK;
+  cat_status st = check_ptrs({X, W_A, W_V, O, workspace});
+  if (st != CAT_OK) return st;
+  if (plan->p.H > 32)
+    return fail(CAT_ERR_UNSUPPORTED, "the CAT-scored variant supports at most 32 heads (scores fused into the GEMM)");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  void* Vb = ws_at(workspace, plan->off_V);
+  float* z = reinterpret_cast<float*>(ws_at(workspace, plan->off_z));
+  KernelMark mk(plan);
+
+  // V = X W_V (blocked for the transform) and z = X W_A in one pass
+  GemmArgs ga = gemm_base(plan, X);
+  ga.nseg = 1;
+  ga.seg[0] = seg(W_V, Vb, (int)plan->p.D, 0, OUT_BLOCKED, plan->cg);
+  ga.Wz = W_A;
+  ga.z = z;
+  ga.nz = (int)plan->p.H;
+  hipError_t e = launch_gemm(plan->et, ga, s, mk.at(0));
+  if (e != hipSuccess) return hip_fail(e, "projection launch");
+  if ((st = check_sync(plan, "projection")) != CAT_OK) return st;
+
+  // softmax over the grid and its 2D spectrum, then the 2D convolution
+  SpecArgs sa = spec_base(plan, workspace);
+  sa.logits = z;
+  e = launch_spectrum(plan->geom, 0, sa, s, mk.at(2));
+  if (e != hipSuccess) return hip_fail(e, "spectrum launch");
+  if ((st = check_sync(plan, "spectrum")) != CAT_OK) return st;
+  ConvArgs ca = conv_base(plan, Vb, sa.spec, O);
+  e = launch_conv(plan->geom, plan->et, ca, s, mk.at(3));
   if (e != hipSuccess) return hip_fail(e, "fft-conv launch");
   return check_sync(plan, "fft-conv");
 }

@@ -157,6 +157,22 @@ cat_status cat_forward_1d(cat_plan plan, const void* X, const void* W_A, const v
 cat_status cat_forward_bccb_2d(cat_plan plan, const void* X, const void* W_Q, const void* W_K,
                                const void* W_V, void* O, void* workspace, void* stream);
 
+/* CAT-scored 2D variant on a 2D plan: CAT's per-head scores on the token
+ * grid as the filter of the BCCB mixing.  z_h = X W_A[:, h] (CAT:
+ * Circular-Convolutional Attention for Sub-Quadratic Transformers, "Method
+ * details / Overall framework"), z*_h = softmax over all Hg Wg tokens, and
+ * O_h = BCCB(z*_h) V_h with V = X W_V, i.e. the 2D circular convolution
+ * O[(i1, i2)] = sum_j z*[((i1 - j1) mod Hg, (i2 - j2) mod Wg)] V[j]
+ * (Vision Transformers are Circulant Attention Learners, "Circulant
+ * Attention: attention rebuilt with the FFT", with its filter from the
+ * CAT score projection instead of the Q/K correlation).  X [B][Hg Wg][D],
+ * W_A [D][H], W_V [D][D], O [B][Hg Wg][D], storage dtype, caller-owned
+ * device memory.  Errors: CAT_ERR_PLAN_MISMATCH for a 1D plan;
+ * CAT_ERR_UNSUPPORTED for H > 32; CAT_ERR_INVALID_ARG for NULL or
+ * misaligned pointers. */
+cat_status cat_forward_cat_2d(cat_plan plan, const void* X, const void* W_A, const void* W_V, void* O,
+                              void* workspace, void* stream);
+
 /* Per-kernel timing (diagnostic).  While enabled, each forward call launches
  * every kernel with a start and a stop event that the kernel's own dispatch
  * stamps (hipExtLaunchKernel), into plan-owned slots (events are created

@@ -481,6 +481,39 @@ def test_forward_2d_small(cat, B, Hg, Wg, D, H, dtype, ss):
     assert_parity(to_np(O), ref, dtype, "O")
 
 
+@pytest.mark.parametrize("B,Hg,Wg,D,H,dtype", [
+    (2, 8, 8, 64, 4, "f32"), (1, 12, 12, 48, 3, "bf16"), (2, 2, 3, 16, 2, "f32"), (1, 16, 16, 32, 2, "bf16"),
+    (1, 6, 8, 24, 2, "f32"), (1, 1, 1, 16, 2, "f32"), (1, 32, 32, 64, 2, "f32"), (1, 96, 96, 64, 2, "bf16")])
+def test_forward_cat_2d(cat, B, Hg, Wg, D, H, dtype):
+    """The CAT-scored 2D variant (X W_A scores, softmax over the grid, BCCB
+    mixing) against the oracle, on grids from 1 x 1 to 96 x 96."""
+    say("forward_cat_2d", B, Hg, Wg, D, H, dtype)
+    import torch
+    inp = rng_inputs_2d(17, B, Hg, Wg, D, H, dtype)
+    W_A = (np.random.default_rng(Hg * Wg + D).standard_normal((D, H)) * 1.5 / np.sqrt(D)).astype(np.float32)
+    if dtype == "bf16":
+        W_A = W.bf16_bits_to_f32(W.round_bf16_bits(W_A)).reshape(W_A.shape)
+    plan = cat.cat_plan_create("2d", dtype, B, Hg * Wg, D, H, Hg, Wg)
+    O = cat.cat_forward_cat_2d(plan, to_dev(inp.X, dtype), to_dev(W_A, dtype), to_dev(inp.W_V, dtype))
+    torch.cuda.synchronize()
+    ref = oracle.cat_scored_forward_2d(inp.X, W_A, inp.W_V, Hg, Wg)["O"]
+    assert_parity(to_np(O), ref, dtype, "O")
+
+
+def test_forward_cat_2d_rejections(cat):
+    import torch
+    p1 = cat.cat_plan_create("1d", "f32", 1, 64, 64, 4)
+    X = torch.zeros((1, 64, 64), device="cuda")
+    with pytest.raises(cat.CatError) as e:
+        cat.cat_forward_cat_2d(p1, X, torch.zeros((64, 4), device="cuda"), torch.zeros((64, 64), device="cuda"))
+    assert e.value.status == -5
+    p2 = cat.cat_plan_create("2d", "f32", 1, 64, 128, 64, 8, 8)  # 64 heads of 2 channels
+    X2 = torch.zeros((1, 64, 128), device="cuda")
+    with pytest.raises(cat.CatError) as e:
+        cat.cat_forward_cat_2d(p2, X2, torch.zeros((128, 64), device="cuda"), torch.zeros((128, 128), device="cuda"))
+    assert e.value.status == -2
+
+
 def test_forward_2d_workload_full_size(cat):
     """96x96 grid, B=8, D=384, H=6, bf16, at full size; the oracle recomputes
     two (image, head) slices end to end."""

@@ -20,6 +20,7 @@ bounded sample of the same workload on this host.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -139,12 +140,22 @@ def measured_traffic(kernel: str, workload: str, launches_per_call: int):
         return None
 
 
-def cpu_baseline(wl, inp, target_s: float):
-    """The fp64 oracle, as it stands, on a bounded sample of the workload."""
+def cpu_baseline(wl, inp, target_s: float, W_A=None):
+    """The fp64 oracle, as it stands, on a bounded sample of the workload
+    (W_A given: the CAT-scored 2D variant)."""
     import numpy as np
 
     import oracle
     threads = oracle.num_threads()
+    if W_A is not None:
+        # one head of one image end to end; a whole image is H such slices
+        d = wl.d
+        t0 = time.perf_counter()
+        oracle.cat_scored_forward_2d(inp.X[:1], W_A[:, :1], inp.W_V[:, :d], wl.Hg, wl.Wg)
+        secs = time.perf_counter() - t0
+        return dict(value=wl.N / (secs * wl.H), unit="tokens/s", cores=threads, kind="oracle",
+                    sample=f"one head of one image (1/{wl.H} of an image, {wl.N} tokens) in {secs:.1f} s, "
+                           f"scaled by {wl.H} heads per image; fp64 direct O(N^2 d) sums")
     if wl.kind == "1d" and wl.N > 4096:
         # one sequence's projections in full, and the circulant sum for a
         # sample of its rows; the time per token adds both shares
@@ -213,12 +224,19 @@ def run(args):
     def dev(a):
         return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dt).cuda()
 
+    cat2d = args.variant == "cat2d"
+    if cat2d and wl.kind != "2d":
+        raise SystemExit("--variant cat2d runs on 2D workloads")
     if wl.kind == "1d":
         plan = cat.cat_plan_create("1d", wl.dtype, wl.B, wl.N, wl.D, wl.H)
         weights = [dev(inp.W_A), dev(inp.W_V)]
     else:
         plan = cat.cat_plan_create("2d", wl.dtype, wl.B, wl.N, wl.D, wl.H, wl.Hg, wl.Wg)
         weights = [dev(inp.W_Q), dev(inp.W_K), dev(inp.W_V)]
+        if cat2d:
+            # the CAT score projection by the workload's weight recipe (N(0, 1/D), seeded)
+            W_A = np.random.default_rng(wl.seed + 1000).standard_normal((wl.D, wl.H)) / math.sqrt(wl.D)
+            weights = [dev(W_A), dev(inp.W_V)]
     L, L1, L2 = plan.geometry()
     ws_bytes = plan.workspace_size()
     x0 = dev(inp.X)
@@ -230,7 +248,7 @@ def run(args):
     WS = [cat.alloc_workspace(plan) for _ in range(nsets)]
     log(f"transform {L} = {L1} x {L2}; {nsets} buffer sets of {set_bytes / 2**20:.1f} MiB")
 
-    fwd = cat.cat_forward_1d if wl.kind == "1d" else cat.cat_forward_bccb_2d
+    fwd = cat.cat_forward_1d if wl.kind == "1d" else cat.cat_forward_cat_2d if cat2d else cat.cat_forward_bccb_2d
 
     def step(i):
         k = i % nsets
@@ -275,7 +293,10 @@ def run(args):
 
     ngrp = (wl.d // 2 + 1) // 2  # score partials per (batch, head): pairs in groups of 2
     fused = wl.kind == "1d" and ktimes.get("spectrum", (0.0, 0))[1] == 0
-    model = kernel_model(wl, L, ngrp, fused_spectrum=fused and conv_path == "fft_matrix",
+    # the CAT-scored 2D variant has the 1D launch structure (fused scores,
+    # spectrum from logits, conv) on the 2D grid's transforms
+    model = kernel_model(dataclasses.replace(wl, kind="1d") if cat2d else wl, L, ngrp,
+                         fused_spectrum=fused and conv_path == "fft_matrix",
                          direct=conv_path == "direct", multipass=conv_path == "fft_multipass")
     kernels = {}
     ktimes = {k: v for k, v in ktimes.items() if v[1] > 0}  # kernels this path launched
@@ -307,14 +328,15 @@ def run(args):
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
-        cpu = cpu_baseline(wl, inp, args.cpu_seconds)
+        cpu = cpu_baseline(wl, inp, args.cpu_seconds, W_A=W_A if cat2d else None)
         log("cpu baseline:", cpu)
 
     tokens = wl.B * wl.N
     value = tokens / (ms_per_step / 1000.0)
     line = {
         "metric": "circulant-attention tokens/s at N=1024,D=768; % of HBM roofline (1 GPU)"
-        if wl.name == W.HEADLINE else f"circulant-attention tokens/s ({wl.name})",
+        if wl.name == W.HEADLINE else f"CAT-scored 2D tokens/s ({wl.name})" if cat2d
+        else f"circulant-attention tokens/s ({wl.name})",
         "value": round(value, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -326,7 +348,7 @@ def run(args):
         "vs_baseline": None,
         "dtype": "f32" if wl.dtype == "f32" else "bf16-storage/f32-compute",
         "data": "synthetic (seeded PCG64: X~N(0,1), W~N(0,1/D))",
-        "config": {"workload": wl.name, "kind": wl.kind, "B": wl.B, "N": wl.N, "D": wl.D, "H": wl.H,
+        "config": {"workload": wl.name, "kind": "2d-cat-scored" if cat2d else wl.kind, "B": wl.B, "N": wl.N, "D": wl.D, "H": wl.H,
                    "grid": [wl.Hg, wl.Wg] if wl.kind == "2d" else None, "storage": wl.dtype,
                    "transform": [L, L1, L2], "mixing": conv_path, "global_batch": wl.B, "seq_len": wl.N, "parallelism": "none"},
         "e2e_hbm_frac": round(((2 * tokens * wl.D * esz) + sum(w.numel() * esz for w in weights))
@@ -504,6 +526,8 @@ def main():
     ap.add_argument("--workload", default=None, help="workload name (default: the N=1024, D=768 one)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--variant", choices=["cat2d"], default=None,
+                    help="cat2d: the CAT-scored 2D variant (cat_forward_cat_2d) on a 2D workload")
     ap.add_argument("--backward", action="store_true",
                     help="time the 1D mixing backward (cat_step_mix_backward_1d) instead of the forward")
     ap.add_argument("--rotate-bytes", type=float, default=2.5 * MALL_BYTES,

@@ -335,6 +335,28 @@ def test_mix_backward_1d(cat, B, N, D, H, dtype, path):
     assert np.all(np.abs(got.sum(axis=-1)) <= 1e-5 * np.abs(got).sum(axis=-1) + 1e-7)
 
 
+def test_mix_backward_1d_workload_full_size(cat):
+    """The mixing backward at the benchmarked shape (B = 16, N = 1024, D = 768,
+    H = 12, bf16; V and the logits from the workload's projection, dO seeded),
+    on the launch configuration bench.py --backward times; the oracle checks
+    the first and the last sequence in full."""
+    import torch
+    wl = W.WORKLOADS["cat1d_gpt2_n1024"]
+    say("mix_backward_full", wl.name)
+    inp = W.make_inputs(wl)
+    plan = cat.cat_plan_create("1d", wl.dtype, wl.B, wl.N, wl.D, wl.H)
+    V, z = cat.cat_step_project(plan, to_dev(inp.X, wl.dtype), to_dev(inp.W_A, wl.dtype), to_dev(inp.W_V, wl.dtype))
+    g = np.random.default_rng(99).standard_normal((wl.B, wl.N, wl.D)).astype(np.float32)
+    g = W.bf16_bits_to_f32(W.round_bf16_bits(g)).reshape(g.shape)
+    dlogits, dV = cat.cat_step_mix_backward_1d(plan, z, V, to_dev(g, wl.dtype))
+    torch.cuda.synchronize()
+    zc, Vc, dz, dVc = to_np(z), to_np(V), to_np(dlogits), to_np(dV)
+    for b in (0, wl.B - 1):
+        ref = oracle.mix_backward_1d(zc[b:b + 1], Vc[b:b + 1], g[b:b + 1])
+        assert_parity(dVc[b:b + 1], ref["dV"], wl.dtype, f"dV b={b}")
+        assert_parity(dz[b:b + 1], ref["dz"], "f32", f"dlogits b={b}")
+
+
 def test_mix_backward_1d_rejections(cat):
     """The multi-pass path has no backward yet; 2D plans are the wrong kind."""
     import torch
@@ -498,6 +520,27 @@ def test_forward_cat_2d(cat, B, Hg, Wg, D, H, dtype):
     torch.cuda.synchronize()
     ref = oracle.cat_scored_forward_2d(inp.X, W_A, inp.W_V, Hg, Wg)["O"]
     assert_parity(to_np(O), ref, dtype, "O")
+
+
+def test_forward_cat_2d_workload_full_size(cat):
+    """The CAT-scored variant at the 96 x 96 workload (B = 8, D = 384, H = 6,
+    bf16) as bench.py --variant cat2d runs it; the oracle recomputes two
+    (image, head) slices end to end."""
+    import torch
+    wl = W.WORKLOADS["bccb2d_1536px_96x96"]
+    say("forward_cat_2d_full", wl.name)
+    inp = W.make_inputs(wl)
+    W_A = (np.random.default_rng(wl.seed + 1000).standard_normal((wl.D, wl.H)) / np.sqrt(wl.D)).astype(np.float32)
+    W_A = W.bf16_bits_to_f32(W.round_bf16_bits(W_A)).reshape(W_A.shape)
+    plan = cat.cat_plan_create("2d", wl.dtype, wl.B, wl.N, wl.D, wl.H, wl.Hg, wl.Wg)
+    O = to_np(cat.cat_forward_cat_2d(plan, to_dev(inp.X, wl.dtype), to_dev(W_A, wl.dtype), to_dev(inp.W_V, wl.dtype)))
+    torch.cuda.synchronize()
+    assert np.all(np.isfinite(O))
+    d = wl.d
+    for b, h in [(0, 0), (wl.B - 1, wl.H - 1)]:
+        hs = slice(h * d, (h + 1) * d)
+        ref = oracle.cat_scored_forward_2d(inp.X[b:b + 1], W_A[:, h:h + 1], inp.W_V[:, hs], wl.Hg, wl.Wg)["O"][0]
+        assert_parity(O[b][:, hs], ref, wl.dtype, f"b={b} h={h}")
 
 
 def test_forward_cat_2d_rejections(cat):

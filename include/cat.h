@@ -113,7 +113,9 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p);
 /* Free a plan (NULL is accepted and ignored).  No work may be in flight. */
 cat_status cat_plan_destroy(cat_plan plan);
 
-/* Bytes of device workspace the forward calls of this plan need. */
+/* Bytes of device workspace every call of this plan needs (the forward
+ * calls, the step calls, cat_step_mix_backward_1d and cat_forward_cat_2d
+ * all fit in it). */
 cat_status cat_plan_workspace_size(cat_plan plan, size_t* bytes);
 
 /* Length of the transform circle / grid the plan uses (L, and L1 x L2 of

@@ -223,6 +223,28 @@ def mix_backward_1d(z, V, G) -> Dict[str, np.ndarray]:
     return {"dz": softmax_backward(zstar, dzs), "dV": dV, "dzstar": dzs}
 
 
+def cat_backward_1d(X, W_A, W_V, G) -> Dict[str, np.ndarray]:
+    """Gradients of the CAT forward (cat_forward_1d) for output gradient G:
+    dX, dW_A, dW_V (and the mixing's dz, dV).  The chain rule through
+    V = X W_V and z_h = X W_A[:, h]: dW_V = sum_b X_b^T dV_b,
+    dW_A[k][h] = sum_{b,n} X[b][n][k] dz[b][h][n],
+    dX = dV W_V^T + dz^T W_A^T."""
+    X = _f64(X)
+    W_A = _f64(W_A)
+    W_V = _f64(W_V)
+    z = scores_1d(X, W_A)
+    V = matmul(X, W_V)
+    mb = mix_backward_1d(z, V, G)
+    dV, dz = mb["dV"], mb["dz"]
+    B, N, D = X.shape
+    Xf = X.reshape(B * N, D)
+    dzt = np.transpose(dz, (0, 2, 1)).reshape(B * N, -1)  # [B*N, H]
+    dW_V = matmul(Xf.T, dV.reshape(B * N, D))
+    dW_A = matmul(Xf.T, dzt)
+    dX = (matmul(dV.reshape(B * N, D), W_V.T) + matmul(dzt, W_A.T)).reshape(B, N, D)
+    return {"dX": dX, "dW_A": dW_A, "dW_V": dW_V, "dz": dz, "dV": dV}
+
+
 # ---------------------------------------------------------------- composites (forward)
 def cat_forward_1d(X, W_A, W_V, rows: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
     """CAT forward: returns z (logits [B,H,N]), zstar (softmax), V (= X W_V) and O."""

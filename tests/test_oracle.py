@@ -561,6 +561,32 @@ def test_mix_backward_logit_gradient_sums_to_zero():
     assert np.allclose(oracle.mix_backward_1d(z, Vc, G)["dz"], 0.0, atol=1e-12)
 
 
+def test_cat_backward_matches_finite_differences():
+    """Central differences of the whole (pinned) CAT forward, for every entry
+    of X, W_A and W_V."""
+    rng = np.random.default_rng(21)
+    B, N, D, H = 2, 4, 4, 2
+    X = rng.standard_normal((B, N, D))
+    WA = rng.standard_normal((D, H))
+    WV = rng.standard_normal((D, D))
+    G = rng.standard_normal((B, N, D))
+    got = oracle.cat_backward_1d(X, WA, WV, G)
+
+    def loss(x, wa, wv):
+        return float(np.sum(oracle.cat_forward_1d(x, wa, wv)["O"] * G))
+
+    eps = 1e-5
+    for name, arr, idx_of in (("dX", X, 0), ("dW_A", WA, 1), ("dW_V", WV, 2)):
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            args_p = [X.copy(), WA.copy(), WV.copy()]
+            args_m = [X.copy(), WA.copy(), WV.copy()]
+            args_p[idx_of][idx] += eps
+            args_m[idx_of][idx] -= eps
+            num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+        assert np.allclose(got[name], num, rtol=1e-7, atol=1e-8), (name, np.max(np.abs(got[name] - num)))
+
+
 def test_planted_backward_lag_sign_is_caught():
     """A score gradient correlating the wrong way (V[(i + k) mod N]) fails the
     finite-difference pin."""

@@ -30,7 +30,7 @@ EXPORTS = ["cat_plan_create", "cat_plan_destroy", "cat_plan_workspace_size", "ca
            "cat_forward_1d", "cat_forward_bccb_2d", "cat_forward_cat_2d", "cat_status_string", "cat_last_error",
            "cat_plan_set_timing", "cat_plan_kernel_times", "cat_plan_conv_path",
            "cat_step_project", "cat_step_spectrum", "cat_step_mix", "cat_step_mix_backward_1d",
-           "cat_step_scores_2d"]
+           "cat_backward_1d", "cat_step_scores_2d"]
 KERNELS_1D = ["project", "spectrum", "fftconv", "reverse", "relayout", "score_grad", "psum", "logits_grad"]
 KERNELS_2D = ["project", "scores", "spectrum", "fftconv", "psum"]
 
@@ -67,6 +67,7 @@ def _load() -> ctypes.CDLL:
     lib.cat_step_spectrum.argtypes = [vp] * 5
     lib.cat_step_mix.argtypes = [vp] * 6
     lib.cat_step_mix_backward_1d.argtypes = [vp] * 8
+    lib.cat_backward_1d.argtypes = [vp] * 10
     lib.cat_step_scores_2d.argtypes = [vp] * 6
     for f in EXPORTS:
         fn = getattr(lib, f)
@@ -303,6 +304,20 @@ def cat_step_mix_backward_1d(plan: Plan, logits, V, dO, workspace=None, stream=N
                                          _ptr(dlogits), _ptr(dV), _ptr(workspace), _stream_ptr(stream)),
            "cat_step_mix_backward_1d")
     return dlogits, dV
+
+
+def cat_backward_1d(plan: Plan, X, W_A, W_V, dO, workspace=None, stream=None):
+    """(dX [B,N,D], dW_A [D,H], dW_V [D,D]), storage dtype, for output gradient dO."""
+    B, N, D, H, dt = plan.B, plan.N, plan.D, plan.H, plan.dtype
+    if workspace is None:
+        workspace = alloc_workspace(plan, X.device)
+    dX = torch.empty((B, N, D), dtype=dt, device=X.device)
+    dW_A = torch.empty((D, H), dtype=dt, device=X.device)
+    dW_V = torch.empty((D, D), dtype=dt, device=X.device)
+    _check(_lib.cat_backward_1d(ctypes.c_void_p(plan.handle), _ptr(X, (B, N, D), dt, "X"), _ptr(W_A, (D, H), dt, "W_A"),
+                                _ptr(W_V, (D, D), dt, "W_V"), _ptr(dO, (B, N, D), dt, "dO"), _ptr(dX), _ptr(dW_A),
+                                _ptr(dW_V), _ptr(workspace), _stream_ptr(stream)), "cat_backward_1d")
+    return dX, dW_A, dW_V
 
 
 def cat_step_scores_2d(plan: Plan, Q, K, workspace=None, stream=None) -> torch.Tensor:

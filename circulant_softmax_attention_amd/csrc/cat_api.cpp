@@ -32,6 +32,9 @@ struct cat_plan_s {
   int npair, ngrp, ppg;  // 2D score partials
   float2* d_tw;      // 1D inter-pass twiddles, L entries (null in 2D)
   size_t off_V, off_z, off_Q, off_K, off_part, off_psum, off_spec, ws_bytes;
+  // the CAT backward's projection gradients (1D single-workgroup lines)
+  size_t off_bz, off_bV, off_bdV, off_bdz, off_bWt, off_bdXf, off_bXt, off_bdzt, off_bdWA;
+  int Hp;  // heads padded to a whole 16-byte column chunk
   size_t off_A, off_zc, off_Az;  // long path scratch
   bool debug_sync;
   int tile_n;        // forced GEMM tile width (0: the GEMM chooses)
@@ -261,6 +264,19 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
       off = up256(off + BH * pl->ngrp * pl->L * sizeof(float2));
       pl->off_psum = off;
       off = up256(off + BH * pl->L * sizeof(float2));
+      // the whole backward: V and z recomputed, dV and dz, W_V^T, dX in
+      // fp32, X^T, dz token-major, dW_A padded
+      const size_t Dz = (size_t)p->D, BN = (size_t)p->B * p->N;
+      pl->Hp = (int)((p->H + 7) / 8 * 8);
+      const size_t sizes[9] = {BH * p->N * sizeof(float), BND * pl->esz, BND * pl->esz, BH * p->N * sizeof(float),
+                               Dz * Dz * pl->esz, BND * sizeof(float), BND * pl->esz, BN * pl->Hp * pl->esz,
+                               Dz * pl->Hp * pl->esz};
+      size_t* offs[9] = {&pl->off_bz, &pl->off_bV, &pl->off_bdV, &pl->off_bdz, &pl->off_bWt,
+                         &pl->off_bdXf, &pl->off_bXt, &pl->off_bdzt, &pl->off_bdWA};
+      for (int i = 0; i < 9; ++i) {
+        *offs[i] = off;
+        off = up256(off + sizes[i]);
+      }
     }
     if (longn) {
       pl->off_A = off;
@@ -552,6 +568,64 @@ cat_status mix_impl(cat_plan plan, const float* logits, const void* V, void* O, 
 }
 
 
+const LaunchTiming* mk_at(KernelMark* mk, int k) { return mk ? mk->at(k) : nullptr; }
+
+// The mixing backward (see cat_step_mix_backward_1d), plan and pointers checked.
+cat_status mix_backward_core(cat_plan plan, const float* logits, const void* V, const void* dO, float* dlogits,
+                             void* dV, void* workspace, hipStream_t s, KernelMark* mk) {
+  cat_status st = CAT_OK;
+  const int BH = (int)(plan->p.B * plan->p.H), N = (int)plan->p.N;
+  // dV = circ(z*)^T dO = circ(softmax(zr)) dO with zr the reversed logits
+  float* zr = reinterpret_cast<float*>(ws_at(workspace, plan->off_z));
+  hipError_t e = launch_reverse_lines(logits, zr, BH, N, s, mk_at(mk, 3));
+  if (e != hipSuccess) return hip_fail(e, "reverse launch");
+  if ((st = mix_impl(plan, zr, dO, dV, workspace, s, mk)) != CAT_OK) return st;
+  // dz*: cross-correlation spectra of dO and V per pair group, summed per
+  // (batch, head).  dO is still in the workspace in the blocked layout the
+  // dV mixing made of it; V gets the same layout.
+  const void* dOb = ws_at(workspace, plan->off_V);
+  void* Vb = ws_at(workspace, plan->off_Q);
+  float2* part = reinterpret_cast<float2*>(ws_at(workspace, plan->off_part));
+  float2* psum = reinterpret_cast<float2*>(ws_at(workspace, plan->off_psum));
+  RelayoutArgs ra{};
+  ra.src = V;
+  ra.dst = Vb;
+  ra.src_et = plan->et;
+  ra.dst_f32 = 0;
+  ra.B = (int)plan->p.B;
+  ra.N = N;
+  ra.D = (int)plan->p.D;
+  ra.H = (int)plan->p.H;
+  ra.d = plan->d;
+  ra.cg = plan->cg;
+  if ((e = launch_relayout(ra, s, mk_at(mk, 4))) != hipSuccess) return hip_fail(e, "relayout launch");
+  ScoreArgs sc{};
+  sc.Q = dOb;
+  sc.K = Vb;
+  sc.et = plan->et;
+  sc.cg = plan->cg;
+  sc.partial = part;
+  sc.BH = BH;
+  sc.N = N;
+  sc.npair = plan->npair;
+  sc.ngrp = plan->ngrp;
+  sc.ppg = plan->ppg;
+  sc.tw = plan->d_tw;
+  if ((e = launch_score_partial(plan->geom, sc, s, mk_at(mk, 5))) != hipSuccess)
+    return hip_fail(e, "score-gradient launch");
+  if ((e = launch_psum(part, psum, BH, plan->ngrp, plan->L, s, mk_at(mk, 6))) != hipSuccess)
+    return hip_fail(e, "psum launch");
+  // dlogits = z* (dz* - <z*, dz*>)
+  SpecArgs sa = spec_base(plan, workspace);
+  sa.logits = logits;
+  sa.partial = psum;
+  sa.ngrp = 1;
+  sa.probs = dlogits;
+  if ((e = launch_spectrum(plan->geom, 2, sa, s, mk_at(mk, 7))) != hipSuccess)
+    return hip_fail(e, "logits-gradient launch");
+  return check_sync(plan, "mixing backward");
+}
+
 }  // namespace
 
 extern "C" {
@@ -764,57 +838,66 @@ cat_status cat_step_mix_backward_1d(cat_plan plan, const float* logits, const vo
   if (plan->longn)
     return fail(CAT_ERR_UNSUPPORTED, "the mixing backward covers single-workgroup lines (not the multi-pass path)");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const int BH = (int)(plan->p.B * plan->p.H), N = (int)plan->p.N;
   KernelMark mk(plan);
-  // dV = circ(z*)^T dO = circ(softmax(zr)) dO with zr the reversed logits
-  float* zr = reinterpret_cast<float*>(ws_at(workspace, plan->off_z));
-  hipError_t e = launch_reverse_lines(logits, zr, BH, N, s, mk.at(3));
-  if (e != hipSuccess) return hip_fail(e, "reverse launch");
-  if ((st = mix_impl(plan, zr, dO, dV, workspace, s, &mk)) != CAT_OK) return st;
-  // dz*: cross-correlation spectra of dO and V per pair group, summed per
-  // (batch, head).  dO is still in the workspace in the blocked layout the
-  // dV mixing made of it; V gets the same layout.
-  const void* dOb = ws_at(workspace, plan->off_V);
-  void* Vb = ws_at(workspace, plan->off_Q);
-  float2* part = reinterpret_cast<float2*>(ws_at(workspace, plan->off_part));
-  float2* psum = reinterpret_cast<float2*>(ws_at(workspace, plan->off_psum));
-  RelayoutArgs ra{};
-  ra.src = V;
-  ra.dst = Vb;
-  ra.src_et = plan->et;
-  ra.dst_f32 = 0;
-  ra.B = (int)plan->p.B;
-  ra.N = N;
-  ra.D = (int)plan->p.D;
-  ra.H = (int)plan->p.H;
-  ra.d = plan->d;
-  ra.cg = plan->cg;
-  if ((e = launch_relayout(ra, s, mk.at(4))) != hipSuccess) return hip_fail(e, "relayout launch");
-  ScoreArgs sc{};
-  sc.Q = dOb;
-  sc.K = Vb;
-  sc.et = plan->et;
-  sc.cg = plan->cg;
-  sc.partial = part;
-  sc.BH = BH;
-  sc.N = N;
-  sc.npair = plan->npair;
-  sc.ngrp = plan->ngrp;
-  sc.ppg = plan->ppg;
-  sc.tw = plan->d_tw;
-  if ((e = launch_score_partial(plan->geom, sc, s, mk.at(5))) != hipSuccess)
-    return hip_fail(e, "score-gradient launch");
-  if ((e = launch_psum(part, psum, BH, plan->ngrp, plan->L, s, mk.at(6))) != hipSuccess)
-    return hip_fail(e, "psum launch");
-  // dlogits = z* (dz* - <z*, dz*>)
-  SpecArgs sa = spec_base(plan, workspace);
-  sa.logits = logits;
-  sa.partial = psum;
-  sa.ngrp = 1;
-  sa.probs = dlogits;
-  if ((e = launch_spectrum(plan->geom, 2, sa, s, mk.at(7))) != hipSuccess)
-    return hip_fail(e, "logits-gradient launch");
-  return check_sync(plan, "mixing backward");
+  return mix_backward_core(plan, logits, V, dO, dlogits, dV, workspace, s, &mk);
+}
+
+cat_status cat_backward_1d(cat_plan plan, const void* X, const void* W_A, const void* W_V, const void* dO, void* dX,
+                           void* dW_A, void* dW_V, void* workspace, void* stream) {
+  if (!plan) return fail(CAT_ERR_INVALID_ARG, "NULL plan");
+  if (plan->p.kind != CAT_1D) return fail(CAT_ERR_PLAN_MISMATCH, "plan is not 1D");
+  cat_status st = check_ptrs({X, W_A, W_V, dO, dX, dW_A, dW_V, workspace});
+  if (st != CAT_OK) return st;
+  if (plan->longn)
+    return fail(CAT_ERR_UNSUPPORTED, "the backward covers single-workgroup lines (not the multi-pass path)");
+  const int B = (int)plan->p.B, N = (int)plan->p.N, D = (int)plan->p.D, H = (int)plan->p.H;
+  if (B == 0 || (B * N) % 8 != 0)
+    return fail(CAT_ERR_UNSUPPORTED, "the weight gradients need B*N >= 8 and a multiple of 8 (X^T rows in 16-byte chunks)");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int et = plan->et;
+  void* bV = ws_at(workspace, plan->off_bV);
+  float* bz = reinterpret_cast<float*>(ws_at(workspace, plan->off_bz));
+  void* bdV = ws_at(workspace, plan->off_bdV);
+  float* bdz = reinterpret_cast<float*>(ws_at(workspace, plan->off_bdz));
+  KernelMark mk(plan);
+
+  // the forward's V (row-major) and logits
+  GemmArgs ga = gemm_base(plan, X);
+  ga.nseg = 1;
+  ga.seg[0] = seg(W_V, bV, D, 0, OUT_ROWMAJOR, 1);
+  ga.Wz = W_A;
+  ga.z = bz;
+  ga.nz = H;
+  hipError_t e = launch_gemm(et, ga, s, mk.at(0));
+  if (e != hipSuccess) return hip_fail(e, "projection launch");
+  // dlogits (fp32) and dV
+  if ((st = mix_backward_core(plan, bz, bV, dO, bdz, bdV, workspace, s, &mk)) != CAT_OK) return st;
+  // dX = dV W_V^T (fp32), then + dz^T W_A^T in the storage dtype
+  void* bWt = ws_at(workspace, plan->off_bWt);
+  float* bdXf = reinterpret_cast<float*>(ws_at(workspace, plan->off_bdXf));
+  if ((e = launch_transpose(et, W_V, bWt, D, D, s)) != hipSuccess) return hip_fail(e, "transpose launch");
+  GemmArgs gx = gemm_base(plan, bdV);
+  gx.nseg = 1;
+  gx.seg[0] = seg(bWt, bdXf, D, 1, OUT_ROWMAJOR, 1);
+  if ((e = launch_gemm(et, gx, s)) != hipSuccess) return hip_fail(e, "dX launch");
+  if ((e = launch_rank_heads_add(et, bdXf, bdz, W_A, dX, B, N, D, H, s)) != hipSuccess)
+    return hip_fail(e, "dX heads launch");
+  // dW_V = X^T dV and dW_A = X^T dz^T: X^T as the row operand, K = B N
+  void* bXt = ws_at(workspace, plan->off_bXt);
+  void* bdzt = ws_at(workspace, plan->off_bdzt);
+  void* bdWA = ws_at(workspace, plan->off_bdWA);
+  if ((e = launch_transpose(et, X, bXt, B * N, D, s)) != hipSuccess) return hip_fail(e, "transpose launch");
+  GemmArgs gw = gemm_base(plan, bXt);
+  gw.M = D;
+  gw.K = B * N;
+  gw.nseg = 1;
+  gw.seg[0] = seg(bdV, dW_V, D, 0, OUT_ROWMAJOR, 1);
+  if ((e = launch_gemm(et, gw, s)) != hipSuccess) return hip_fail(e, "dW_V launch");
+  if ((e = launch_pack_heads(et, bdz, bdzt, B, H, N, plan->Hp, s)) != hipSuccess) return hip_fail(e, "pack launch");
+  gw.seg[0] = seg(bdzt, bdWA, plan->Hp, 0, OUT_ROWMAJOR, 1);
+  if ((e = launch_gemm(et, gw, s)) != hipSuccess) return hip_fail(e, "dW_A launch");
+  if ((e = launch_take_cols(et, bdWA, dW_A, D, plan->Hp, H, s)) != hipSuccess) return hip_fail(e, "dW_A copy launch");
+  return check_sync(plan, "backward");
 }
 
 cat_status cat_step_scores_2d(cat_plan plan, const float* Q, const float* K, float* probs, void* workspace,

@@ -1,0 +1,128 @@
+// cat_backward.hip -- layout and elementwise kernels of the CAT backward's
+// projection gradients.  With V = X W_V and z_h = X W_A[:, h] (CAT:
+// Circular-Convolutional Attention for Sub-Quadratic Transformers, "Method
+// details / Overall framework"), the chain rule gives
+//   dX = dV W_V^T + dz^T W_A^T,  dW_V = X^T dV,  dW_A = X^T dz^T;
+// the products run on the projection GEMM, and these kernels supply its
+// transposed operands and the rank-H term.
+#include "cat_common.hpp"
+#include "cat_internal.hpp"
+
+namespace cat {
+
+namespace {
+
+template <int ET>
+__device__ __forceinline__ float ld_elem(const void* p, size_t i) {
+  if constexpr (ET == ET_F32)
+    return reinterpret_cast<const float*>(p)[i];
+  else
+    return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(p)[i] << 16);
+}
+
+template <int ET>
+__device__ __forceinline__ void st_elem(void* p, size_t i, float v) {
+  if constexpr (ET == ET_F32)
+    reinterpret_cast<float*>(p)[i] = v;
+  else
+    reinterpret_cast<uint16_t*>(p)[i] = to_bf16(v);
+}
+
+// dst [C][R] = src [R][C]^T, storage dtype, 32 x 32 tiles through LDS (one
+// workgroup per tile, 1D grid of tiles).
+template <int ET>
+__global__ __launch_bounds__(256) void transpose_kernel(const void* __restrict__ src, void* __restrict__ dst, int R,
+                                                        int C) {
+  __shared__ float tile[32][33];
+  const int tcs = (C + 31) / 32;
+  const int tr = blockIdx.x / tcs, tc = blockIdx.x - tr * tcs;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
+  for (int k = ty; k < 32; k += 8) {
+    const int r = tr * 32 + k, c = tc * 32 + tx;
+    if (r < R && c < C) tile[k][tx] = ld_elem<ET>(src, (size_t)r * C + c);
+  }
+  __syncthreads();
+  for (int k = ty; k < 32; k += 8) {
+    const int c = tc * 32 + k, r = tr * 32 + tx;
+    if (r < R && c < C) st_elem<ET>(dst, (size_t)c * R + r, tile[tx][k]);
+  }
+}
+
+// dzt [B N][Hp] (storage dtype) = dz [B][H][N] token-major, zero for h >= H.
+template <int ET>
+__global__ __launch_bounds__(256) void pack_heads_kernel(const float* __restrict__ dz, void* __restrict__ dzt, int B,
+                                                         int H, int N, int Hp) {
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (size_t)B * N * Hp) return;
+  const size_t m = idx / Hp;
+  const int h = (int)(idx - m * Hp);
+  const int b = (int)(m / N), n = (int)(m - (size_t)b * N);
+  st_elem<ET>(dzt, idx, h < H ? dz[((size_t)b * H + h) * N + n] : 0.f);
+}
+
+// dX[m][c] = dXf[m][c] + sum_h dz[b][h][n] W_A[c][h]  (m = b N + n), in the
+// storage dtype.
+template <int ET>
+__global__ __launch_bounds__(256) void rank_heads_add_kernel(const float* __restrict__ dXf, const float* __restrict__ dz,
+                                                             const void* __restrict__ W_A, void* __restrict__ dX,
+                                                             int B, int N, int D, int H) {
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (size_t)B * N * D) return;
+  const size_t m = idx / D;
+  const int c = (int)(idx - m * D);
+  const int b = (int)(m / N), n = (int)(m - (size_t)b * N);
+  float acc = dXf[idx];
+  for (int h = 0; h < H; ++h) acc = fmaf(dz[((size_t)b * H + h) * N + n], ld_elem<ET>(W_A, (size_t)c * H + h), acc);
+  st_elem<ET>(dX, idx, acc);
+}
+
+// dst [R][Cd] = the first Cd columns of src [R][Cs], storage dtype.
+template <int ET>
+__global__ __launch_bounds__(256) void take_cols_kernel(const void* __restrict__ src, void* __restrict__ dst, int R,
+                                                        int Cs, int Cd) {
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (size_t)R * Cd) return;
+  const size_t r = idx / Cd;
+  const int c = (int)(idx - r * Cd);
+  st_elem<ET>(dst, idx, ld_elem<ET>(src, r * Cs + c));
+}
+
+unsigned blocks_for(size_t n) { return (unsigned)((n + 255) / 256); }
+
+}  // namespace
+
+hipError_t launch_transpose(int et, const void* src, void* dst, int R, int C, hipStream_t s, const LaunchTiming* t) {
+  if (R < 1 || C < 1) return hipErrorInvalidValue;
+  const size_t tiles = (size_t)((R + 31) / 32) * ((C + 31) / 32);
+  if (tiles > 0x7fffffffu) return hipErrorInvalidValue;
+  return et == ET_F32 ? launch_k(transpose_kernel<ET_F32>, dim3((unsigned)tiles), dim3(256), 0, s, t, src, dst, R, C)
+                      : launch_k(transpose_kernel<ET_BF16>, dim3((unsigned)tiles), dim3(256), 0, s, t, src, dst, R, C);
+}
+
+hipError_t launch_pack_heads(int et, const float* dz, void* dzt, int B, int H, int N, int Hp, hipStream_t s,
+                             const LaunchTiming* t) {
+  const size_t n = (size_t)B * N * Hp;
+  if (n == 0 || Hp < H || blocks_for(n) > 0x7fffffffu) return hipErrorInvalidValue;
+  return et == ET_F32 ? launch_k(pack_heads_kernel<ET_F32>, dim3(blocks_for(n)), dim3(256), 0, s, t, dz, dzt, B, H, N, Hp)
+                      : launch_k(pack_heads_kernel<ET_BF16>, dim3(blocks_for(n)), dim3(256), 0, s, t, dz, dzt, B, H, N, Hp);
+}
+
+hipError_t launch_rank_heads_add(int et, const float* dXf, const float* dz, const void* W_A, void* dX, int B, int N,
+                                 int D, int H, hipStream_t s, const LaunchTiming* t) {
+  const size_t n = (size_t)B * N * D;
+  if (n == 0 || blocks_for(n) > 0x7fffffffu) return hipErrorInvalidValue;
+  return et == ET_F32
+             ? launch_k(rank_heads_add_kernel<ET_F32>, dim3(blocks_for(n)), dim3(256), 0, s, t, dXf, dz, W_A, dX, B, N, D, H)
+             : launch_k(rank_heads_add_kernel<ET_BF16>, dim3(blocks_for(n)), dim3(256), 0, s, t, dXf, dz, W_A, dX, B, N, D,
+                        H);
+}
+
+hipError_t launch_take_cols(int et, const void* src, void* dst, int R, int Cs, int Cd, hipStream_t s,
+                            const LaunchTiming* t) {
+  const size_t n = (size_t)R * Cd;
+  if (n == 0 || Cd > Cs || blocks_for(n) > 0x7fffffffu) return hipErrorInvalidValue;
+  return et == ET_F32 ? launch_k(take_cols_kernel<ET_F32>, dim3(blocks_for(n)), dim3(256), 0, s, t, src, dst, R, Cs, Cd)
+                      : launch_k(take_cols_kernel<ET_BF16>, dim3(blocks_for(n)), dim3(256), 0, s, t, src, dst, R, Cs, Cd);
+}
+
+}  // namespace cat

@@ -244,6 +244,22 @@ cat_status cat_step_mix(cat_plan plan, const float* logits, const void* V, void*
 cat_status cat_step_mix_backward_1d(cat_plan plan, const float* logits, const void* V, const void* dO,
                                     float* dlogits, void* dV, void* workspace, void* stream);
 
+/* Gradients of the 1D CAT forward (cat_forward_1d) for an output gradient
+ * dO [B][N][D]: dX [B][N][D], dW_A [D][H], dW_V [D][D], all in the storage
+ * dtype, caller-owned device memory.  The chain rule through V = X W_V,
+ * z_h = X W_A[:, h] (CAT: Circular-Convolutional Attention for
+ * Sub-Quadratic Transformers, "Method details / Overall framework") and the
+ * mixing (cat_step_mix_backward_1d):
+ *   dW_V = X^T dV,  dW_A = X^T dz^T,  dX = dV W_V^T + dz^T W_A^T,
+ * with V and z recomputed from X.  The products run on the projection
+ * GEMM (fp32 accumulation; dX is accumulated in fp32 and rounded once; dV
+ * and dz enter the weight products rounded to the storage dtype).
+ * Errors: CAT_ERR_PLAN_MISMATCH for a 2D plan; CAT_ERR_UNSUPPORTED on the
+ * multi-pass path and unless B N is a positive multiple of 8;
+ * CAT_ERR_INVALID_ARG for NULL or misaligned pointers. */
+cat_status cat_backward_1d(cat_plan plan, const void* X, const void* W_A, const void* W_V, const void* dO, void* dX,
+                           void* dW_A, void* dW_V, void* workspace, void* stream);
+
 /* 2D score step: probs [B][H][N] fp32 = softmax over the grid of the scaled
  * circular cross-correlation of Q and K (both [B][N][D] fp32).  2D plans only. */
 cat_status cat_step_scores_2d(cat_plan plan, const float* Q, const float* K, float* probs,

@@ -357,6 +357,43 @@ def test_mix_backward_1d_workload_full_size(cat):
         assert_parity(dz[b:b + 1], ref["dz"], "f32", f"dlogits b={b}")
 
 
+@pytest.mark.parametrize("B,N,D,H,dtype,path", [
+    (2, 64, 64, 4, "f32", "fft_valu"), (1, 128, 128, 2, "bf16", "direct"), (2, 1024, 128, 2, "bf16", "fft_matrix"),
+    (1, 200, 96, 3, "f32", "fft_valu"), (4, 6, 16, 2, "f32", "fft_valu"), (1, 8, 64, 32, "bf16", "fft_valu"),
+    (2, 512, 96, 12, "bf16", "fft_valu")])
+def test_backward_1d(cat, B, N, D, H, dtype, path):
+    """Gradients of the whole 1D forward (dX, dW_A, dW_V) against the oracle's
+    chain rule; the mixing runs on the plan's path, the products on the
+    projection GEMM."""
+    say("backward_1d", B, N, D, H, dtype, path)
+    import torch
+    inp = rng_inputs(31, B, N, D, H, dtype)
+    g = np.random.default_rng(N + D).standard_normal((B, N, D)).astype(np.float32)
+    if dtype == "bf16":
+        g = W.bf16_bits_to_f32(W.round_bf16_bits(g)).reshape(g.shape)
+    plan = cat.cat_plan_create("1d", dtype, B, N, D, H)
+    assert plan.conv_path() == path
+    dX, dWA, dWV = cat.cat_backward_1d(plan, to_dev(inp.X, dtype), to_dev(inp.W_A, dtype), to_dev(inp.W_V, dtype),
+                                       to_dev(g, dtype))
+    torch.cuda.synchronize()
+    ref = oracle.cat_backward_1d(inp.X, inp.W_A, inp.W_V, g)
+    assert_parity(to_np(dX), ref["dX"], dtype, "dX")
+    assert_parity(to_np(dWA), ref["dW_A"], dtype, "dW_A")
+    assert_parity(to_np(dWV), ref["dW_V"], dtype, "dW_V")
+
+
+def test_backward_1d_rejections(cat):
+    """B N not a multiple of 8 (X^T rows would not be whole 16-byte chunks)
+    and the multi-pass path are rejected before any launch."""
+    import torch
+    for (B, N, D, H) in [(1, 197, 64, 2), (1, 8192, 16, 2)]:
+        plan = cat.cat_plan_create("1d", "f32", B, N, D, H)
+        z = torch.zeros((B, N, D), device="cuda")
+        with pytest.raises(cat.CatError) as e:
+            cat.cat_backward_1d(plan, z, torch.zeros((D, H), device="cuda"), torch.zeros((D, D), device="cuda"), z)
+        assert e.value.status == -2
+
+
 def test_mix_backward_1d_rejections(cat):
     """The multi-pass path has no backward yet; 2D plans are the wrong kind."""
     import torch

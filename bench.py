@@ -421,9 +421,15 @@ def run_backward(args):
                      cat.alloc_workspace(plan)))
     log(f"transform {L} = {L1} x {L2}; mixing path {conv_path}; {nsets} buffer sets of {set_bytes / 2**20:.1f} MiB")
 
+    full = args.backward == "full"
+    Xd, WAd, WVd = dev(inp.X), dev(inp.W_A), dev(inp.W_V)
+
     def step(i):
         z, V, dO, ws = sets[i % nsets]
-        cat.cat_step_mix_backward_1d(plan, z, V, dO, workspace=ws)
+        if full:
+            cat.cat_backward_1d(plan, Xd, WAd, WVd, dO, workspace=ws)
+        else:
+            cat.cat_step_mix_backward_1d(plan, z, V, dO, workspace=ws)
 
     for i in range(args.warmup):
         step(i)
@@ -446,6 +452,8 @@ def run_backward(args):
     torch.cuda.synchronize()
     ktimes = {k: v for k, v in cat.cat_plan_kernel_times(plan).items() if v[1] > 0}
     cat.cat_plan_set_timing(plan, False)
+    if full:
+        ktimes.pop("project", None)  # the recompute GEMM; the gradient GEMMs are not in the timing slots
     if conv_path == "direct":
         ktimes["directconv"] = ktimes.pop("fftconv")
     ngrp = (wl.d // 2 + 1) // 2
@@ -477,7 +485,7 @@ def run_backward(args):
                     compute_frac=kd["compute_frac"], us=kd["us"])
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not full:
         import oracle
         # whole sequences, one at a time, until about --cpu-seconds of work
         zc, Vc, gc = z0.cpu().numpy(), V0.float().cpu().numpy(), dO0.float().cpu().numpy()
@@ -495,7 +503,8 @@ def run_backward(args):
     tokens = wl.B * wl.N
     io_bytes = 3 * tokens * wl.D * esz + 2 * wl.B * wl.H * wl.N * 4  # V, dO read, dV written; logits, dlogits
     return {
-        "metric": f"circulant mixing backward tokens/s ({wl.name})",
+        "metric": f"CAT backward (dX, dW_A, dW_V) tokens/s ({wl.name})" if full
+        else f"circulant mixing backward tokens/s ({wl.name})",
         "value": round(tokens / (ms_per_step / 1000.0), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -507,7 +516,9 @@ def run_backward(args):
         "vs_baseline": None,
         "dtype": "f32" if wl.dtype == "f32" else "bf16-storage/f32-compute",
         "data": "synthetic (seeded PCG64: V, logits = projections of X~N(0,1); dO~N(0,1))",
-        "config": {"workload": wl.name, "kind": "1d-mix-backward", "B": wl.B, "N": wl.N, "D": wl.D, "H": wl.H,
+        "gemm_flops_per_step": (2.0 * tokens * wl.D * (2 * wl.D + wl.H) + 2.0 * wl.D * tokens * (wl.D + (wl.H + 7) // 8 * 8))
+        if full else None,
+        "config": {"workload": wl.name, "kind": "1d-backward" if full else "1d-mix-backward", "B": wl.B, "N": wl.N, "D": wl.D, "H": wl.H,
                    "storage": wl.dtype, "transform": [L, L1, L2], "mixing": conv_path, "global_batch": wl.B,
                    "seq_len": wl.N, "parallelism": "none"},
         "e2e_hbm_frac": round(io_bytes / (ms_per_step / 1000.0) / 1e9 / HBM_PEAK_GBS, 4),
@@ -528,8 +539,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--variant", choices=["cat2d"], default=None,
                     help="cat2d: the CAT-scored 2D variant (cat_forward_cat_2d) on a 2D workload")
-    ap.add_argument("--backward", action="store_true",
-                    help="time the 1D mixing backward (cat_step_mix_backward_1d) instead of the forward")
+    ap.add_argument("--backward", nargs="?", const="mix", choices=["mix", "full"], default=None,
+                    help="time a 1D backward instead of the forward: mix = cat_step_mix_backward_1d, "
+                         "full = cat_backward_1d (dX, dW_A, dW_V)")
     ap.add_argument("--rotate-bytes", type=float, default=2.5 * MALL_BYTES,
                     help="total bytes of rotated buffer sets (defeats the Infinity Cache)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",

@@ -3,8 +3,9 @@
 // Circular-Convolutional Attention for Sub-Quadratic Transformers, "Method
 // details / Overall framework"), the chain rule gives
 //   dX = dV W_V^T + dz^T W_A^T,  dW_V = X^T dV,  dW_A = X^T dz^T;
-// the products run on the projection GEMM, and these kernels supply its
-// transposed operands and the rank-H term.
+// the products run on the projection GEMM (dW_V and dW_A as one product
+// X^T [dV | dz^T]), and these kernels supply its operands and the rank-H
+// term.
 #include "cat_common.hpp"
 #include "cat_internal.hpp"
 
@@ -48,32 +49,61 @@ __global__ __launch_bounds__(256) void transpose_kernel(const void* __restrict__
   }
 }
 
-// dzt [B N][Hp] (storage dtype) = dz [B][H][N] token-major, zero for h >= H.
+// P [B N][D + Hp] (storage dtype) = [dV | dz token-major | 0]: the column
+// operand of the product X^T P = [dW_V | dW_A | 0].
 template <int ET>
-__global__ __launch_bounds__(256) void pack_heads_kernel(const float* __restrict__ dz, void* __restrict__ dzt, int B,
-                                                         int H, int N, int Hp) {
+__global__ __launch_bounds__(256) void pack_grads_kernel(const void* __restrict__ dV, const float* __restrict__ dz,
+                                                         void* __restrict__ P, int B, int N, int D, int H, int Hp) {
+  const int W = D + Hp;
   const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (size_t)B * N * Hp) return;
-  const size_t m = idx / Hp;
-  const int h = (int)(idx - m * Hp);
-  const int b = (int)(m / N), n = (int)(m - (size_t)b * N);
-  st_elem<ET>(dzt, idx, h < H ? dz[((size_t)b * H + h) * N + n] : 0.f);
+  if (idx >= (size_t)B * N * W) return;
+  const size_t m = idx / W;
+  const int col = (int)(idx - m * W);
+  float v;
+  if (col < D) {
+    v = ld_elem<ET>(dV, m * D + col);
+  } else {
+    const int h = col - D;
+    const int b = (int)(m / N), n = (int)(m - (size_t)b * N);
+    v = h < H ? dz[((size_t)b * H + h) * N + n] : 0.f;
+  }
+  st_elem<ET>(P, idx, v);
 }
 
-// dX[m][c] = dXf[m][c] + sum_h dz[b][h][n] W_A[c][h]  (m = b N + n), in the
-// storage dtype.
+// dX[m][c] = dXf[m][c] + sum_h dz[b][h][n] W_A[c][h]  (m = b N + n, H <= 32),
+// in the storage dtype.  A workgroup takes RB token rows: their dz values
+// go to LDS (zero past H), each thread keeps its column's W_A row in
+// registers and walks the rows, so dXf and dX move in coalesced rows.
+constexpr int RB = 16;
 template <int ET>
 __global__ __launch_bounds__(256) void rank_heads_add_kernel(const float* __restrict__ dXf, const float* __restrict__ dz,
                                                              const void* __restrict__ W_A, void* __restrict__ dX,
                                                              int B, int N, int D, int H) {
-  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (size_t)B * N * D) return;
-  const size_t m = idx / D;
-  const int c = (int)(idx - m * D);
-  const int b = (int)(m / N), n = (int)(m - (size_t)b * N);
-  float acc = dXf[idx];
-  for (int h = 0; h < H; ++h) acc = fmaf(dz[((size_t)b * H + h) * N + n], ld_elem<ET>(W_A, (size_t)c * H + h), acc);
-  st_elem<ET>(dX, idx, acc);
+  __shared__ float dzs[RB][33];
+  const int M = B * N, m0 = blockIdx.x * RB;
+  const int rows = M - m0 < RB ? M - m0 : RB;
+  for (int i = threadIdx.x; i < RB * 32; i += 256) {
+    const int r = i >> 5, h = i & 31;
+    float v = 0.f;
+    if (r < rows && h < H) {
+      const int m = m0 + r, b = m / N, n = m - b * N;
+      v = dz[((size_t)b * H + h) * N + n];
+    }
+    dzs[r][h] = v;
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < D; c += 256) {
+    float w[32];
+#pragma unroll
+    for (int h = 0; h < 32; ++h) w[h] = h < H ? ld_elem<ET>(W_A, (size_t)c * H + h) : 0.f;
+    for (int r = 0; r < rows; ++r) {
+      const size_t i = (size_t)(m0 + r) * D + c;
+      float acc = dXf[i];
+#pragma unroll
+      for (int h = 0; h < 32; ++h) acc = fmaf(dzs[r][h], w[h], acc);
+      st_elem<ET>(dX, i, acc);
+    }
+  }
 }
 
 // dst [R][Cd] = the first Cd columns of src [R][Cs], storage dtype.
@@ -99,21 +129,22 @@ hipError_t launch_transpose(int et, const void* src, void* dst, int R, int C, hi
                       : launch_k(transpose_kernel<ET_BF16>, dim3((unsigned)tiles), dim3(256), 0, s, t, src, dst, R, C);
 }
 
-hipError_t launch_pack_heads(int et, const float* dz, void* dzt, int B, int H, int N, int Hp, hipStream_t s,
-                             const LaunchTiming* t) {
-  const size_t n = (size_t)B * N * Hp;
+hipError_t launch_pack_grads(int et, const void* dV, const float* dz, void* P, int B, int N, int D, int H, int Hp,
+                             hipStream_t s, const LaunchTiming* t) {
+  const size_t n = (size_t)B * N * (D + Hp);
   if (n == 0 || Hp < H || blocks_for(n) > 0x7fffffffu) return hipErrorInvalidValue;
-  return et == ET_F32 ? launch_k(pack_heads_kernel<ET_F32>, dim3(blocks_for(n)), dim3(256), 0, s, t, dz, dzt, B, H, N, Hp)
-                      : launch_k(pack_heads_kernel<ET_BF16>, dim3(blocks_for(n)), dim3(256), 0, s, t, dz, dzt, B, H, N, Hp);
+  return et == ET_F32
+             ? launch_k(pack_grads_kernel<ET_F32>, dim3(blocks_for(n)), dim3(256), 0, s, t, dV, dz, P, B, N, D, H, Hp)
+             : launch_k(pack_grads_kernel<ET_BF16>, dim3(blocks_for(n)), dim3(256), 0, s, t, dV, dz, P, B, N, D, H, Hp);
 }
 
 hipError_t launch_rank_heads_add(int et, const float* dXf, const float* dz, const void* W_A, void* dX, int B, int N,
                                  int D, int H, hipStream_t s, const LaunchTiming* t) {
-  const size_t n = (size_t)B * N * D;
-  if (n == 0 || blocks_for(n) > 0x7fffffffu) return hipErrorInvalidValue;
+  const size_t nb = ((size_t)B * N + RB - 1) / RB;
+  if (nb == 0 || H > 32 || nb > 0x7fffffffu) return hipErrorInvalidValue;
   return et == ET_F32
-             ? launch_k(rank_heads_add_kernel<ET_F32>, dim3(blocks_for(n)), dim3(256), 0, s, t, dXf, dz, W_A, dX, B, N, D, H)
-             : launch_k(rank_heads_add_kernel<ET_BF16>, dim3(blocks_for(n)), dim3(256), 0, s, t, dXf, dz, W_A, dX, B, N, D,
+             ? launch_k(rank_heads_add_kernel<ET_F32>, dim3((unsigned)nb), dim3(256), 0, s, t, dXf, dz, W_A, dX, B, N, D, H)
+             : launch_k(rank_heads_add_kernel<ET_BF16>, dim3((unsigned)nb), dim3(256), 0, s, t, dXf, dz, W_A, dX, B, N, D,
                         H);
 }
 

@@ -179,13 +179,13 @@ hipError_t launch_dconv(int et, const ConvArgs& a, hipStream_t s, const LaunchTi
 hipError_t launch_score_partial(const LineGeom& g, const ScoreArgs& a, hipStream_t s,
                                 const LaunchTiming* t = nullptr);
 // Projection-gradient helpers of the CAT backward (cat_backward.hip), storage
-// dtype et: dst [C][R] = src [R][C]^T; dzt [B N][Hp] = dz [B][H][N]
-// token-major, zero-padded to Hp >= H; dX = dXf + dz^T W_A^T (W_A [D][H]);
+// dtype et: dst [C][R] = src [R][C]^T; P [B N][D + Hp] = [dV | dz token-major
+// | 0] (Hp >= H); dX = dXf + dz^T W_A^T (W_A [D][H], H <= 32);
 // dst [R][Cd] = the first Cd columns of src [R][Cs].
 hipError_t launch_transpose(int et, const void* src, void* dst, int R, int C, hipStream_t s,
                             const LaunchTiming* t = nullptr);
-hipError_t launch_pack_heads(int et, const float* dz, void* dzt, int B, int H, int N, int Hp, hipStream_t s,
-                             const LaunchTiming* t = nullptr);
+hipError_t launch_pack_grads(int et, const void* dV, const float* dz, void* P, int B, int N, int D, int H, int Hp,
+                             hipStream_t s, const LaunchTiming* t = nullptr);
 hipError_t launch_rank_heads_add(int et, const float* dXf, const float* dz, const void* W_A, void* dX, int B, int N,
                                  int D, int H, hipStream_t s, const LaunchTiming* t = nullptr);
 hipError_t launch_take_cols(int et, const void* src, void* dst, int R, int Cs, int Cd, hipStream_t s,

@@ -265,12 +265,12 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
       pl->off_psum = off;
       off = up256(off + BH * pl->L * sizeof(float2));
       // the whole backward: V and z recomputed, dV and dz, W_V^T, dX in
-      // fp32, X^T, [dV | dz^T | 0] and [dW_V | dW_A | 0]
+      // fp32, X^T, dz token-major (padded to Hp heads) and dW_A padded
       const size_t Dz = (size_t)p->D, BN = (size_t)p->B * p->N;
       pl->Hp = (int)((p->H + 7) / 8 * 8);
       const size_t sizes[9] = {BH * p->N * sizeof(float), BND * pl->esz, BND * pl->esz, BH * p->N * sizeof(float),
                                Dz * Dz * pl->esz, BND * sizeof(float), BND * pl->esz,
-                               BN * (Dz + pl->Hp) * pl->esz, Dz * (Dz + pl->Hp) * pl->esz};
+                               BN * pl->Hp * pl->esz, Dz * pl->Hp * pl->esz};
       size_t* offs[9] = {&pl->off_bz, &pl->off_bV, &pl->off_bdV, &pl->off_bdz, &pl->off_bWt,
                          &pl->off_bdXf, &pl->off_bXt, &pl->off_bP, &pl->off_bdW};
       for (int i = 0; i < 9; ++i) {
@@ -882,24 +882,23 @@ cat_status cat_backward_1d(cat_plan plan, const void* X, const void* W_A, const 
   if ((e = launch_gemm(et, gx, s)) != hipSuccess) return hip_fail(e, "dX launch");
   if ((e = launch_rank_heads_add(et, bdXf, bdz, W_A, dX, B, N, D, H, s)) != hipSuccess)
     return hip_fail(e, "dX heads launch");
-  // [dW_V | dW_A | 0] = X^T [dV | dz^T | 0]: one product, X^T as the row
-  // operand, K = B N, then the two column blocks copied out
+  // dW_V = X^T dV and dW_A = X^T dz^T as two output segments of one
+  // product (X^T the shared row operand, K = B N); dW_A's padded columns
+  // are dropped afterwards
   void* bXt = ws_at(workspace, plan->off_bXt);
-  void* bP = ws_at(workspace, plan->off_bP);
-  void* bdW = ws_at(workspace, plan->off_bdW);
-  const int Wc = D + plan->Hp;
+  void* bdzt = ws_at(workspace, plan->off_bP);
+  void* bdWA = ws_at(workspace, plan->off_bdW);
   if ((e = launch_transpose(et, X, bXt, B * N, D, s)) != hipSuccess) return hip_fail(e, "transpose launch");
-  if ((e = launch_pack_grads(et, bdV, bdz, bP, B, N, D, H, plan->Hp, s)) != hipSuccess)
+  if ((e = launch_pack_grads(et, nullptr, bdz, bdzt, B, N, 0, H, plan->Hp, s)) != hipSuccess)
     return hip_fail(e, "pack launch");
   GemmArgs gw = gemm_base(plan, bXt);
   gw.M = D;
   gw.K = B * N;
-  gw.nseg = 1;
-  gw.seg[0] = seg(bP, bdW, Wc, 0, OUT_ROWMAJOR, 1);
+  gw.nseg = 2;
+  gw.seg[0] = seg(bdV, dW_V, D, 0, OUT_ROWMAJOR, 1);
+  gw.seg[1] = seg(bdzt, bdWA, plan->Hp, 0, OUT_ROWMAJOR, 1);
   if ((e = launch_gemm(et, gw, s)) != hipSuccess) return hip_fail(e, "dW launch");
-  if ((e = launch_take_cols(et, bdW, dW_V, D, Wc, D, s)) != hipSuccess) return hip_fail(e, "dW_V copy launch");
-  const void* bdWA = static_cast<const char*>(bdW) + (size_t)D * plan->esz;  // column D onwards
-  if ((e = launch_take_cols(et, bdWA, dW_A, D, Wc, H, s)) != hipSuccess) return hip_fail(e, "dW_A copy launch");
+  if ((e = launch_take_cols(et, bdWA, dW_A, D, plan->Hp, H, s)) != hipSuccess) return hip_fail(e, "dW_A copy launch");
   return check_sync(plan, "backward");
 }
 

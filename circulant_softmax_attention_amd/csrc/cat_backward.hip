@@ -3,9 +3,9 @@
 // Circular-Convolutional Attention for Sub-Quadratic Transformers, "Method
 // details / Overall framework"), the chain rule gives
 //   dX = dV W_V^T + dz^T W_A^T,  dW_V = X^T dV,  dW_A = X^T dz^T;
-// the products run on the projection GEMM (dW_V and dW_A as one product
-// X^T [dV | dz^T]), and these kernels supply its operands and the rank-H
-// term.
+// the products run on the projection GEMM (dW_V and dW_A as two output
+// segments of one launch sharing the row operand X^T), and these kernels
+// supply its operands and the rank-H term.
 #include "cat_common.hpp"
 #include "cat_internal.hpp"
 

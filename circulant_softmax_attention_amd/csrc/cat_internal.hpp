@@ -180,7 +180,8 @@ hipError_t launch_score_partial(const LineGeom& g, const ScoreArgs& a, hipStream
                                 const LaunchTiming* t = nullptr);
 // Projection-gradient helpers of the CAT backward (cat_backward.hip), storage
 // dtype et: dst [C][R] = src [R][C]^T; P [B N][D + Hp] = [dV | dz token-major
-// | 0] (Hp >= H); dX = dXf + dz^T W_A^T (W_A [D][H], H <= 32);
+// | 0] (Hp >= H; D = 0: the dz block alone, dV unused); dX = dXf + dz^T W_A^T
+// (W_A [D][H], H <= 32);
 // dst [R][Cd] = the first Cd columns of src [R][Cs].
 hipError_t launch_transpose(int et, const void* src, void* dst, int R, int C, hipStream_t s,
                             const LaunchTiming* t = nullptr);

@@ -35,6 +35,10 @@ struct cat_plan_s {
   // the CAT backward's projection gradients (1D single-workgroup lines)
   size_t off_bz, off_bV, off_bdV, off_bdz, off_bWt, off_bdXf, off_bXt, off_bP, off_bdW;
   int Hp;  // heads padded to a whole 16-byte column chunk
+  // the backward's weight-gradient branch runs on a plan-owned stream
+  // (default priority), forked from and joined back to the caller's stream
+  hipStream_t side = nullptr;
+  hipEvent_t fork_ev = nullptr, join_ev = nullptr;
   size_t off_A, off_zc, off_Az;  // long path scratch
   bool debug_sync;
   int tile_n;        // forced GEMM tile width (0: the GEMM chooses)
@@ -345,6 +349,19 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
   }
 
 
+  if (p->kind == CAT_1D && !longn) {
+    hipError_t se = hipStreamCreateWithFlags(&pl->side, hipStreamNonBlocking);
+    if (se == hipSuccess) se = hipEventCreateWithFlags(&pl->fork_ev, hipEventDisableTiming);
+    if (se == hipSuccess) se = hipEventCreateWithFlags(&pl->join_ev, hipEventDisableTiming);
+    if (se != hipSuccess) {
+      if (pl->fork_ev) (void)hipEventDestroy(pl->fork_ev);
+      if (pl->side) (void)hipStreamDestroy(pl->side);
+      if (pl->d_tw) (void)hipFree(pl->d_tw);
+      delete pl;
+      return hip_fail(se, "stream / event creation");
+    }
+  }
+
   *out = pl;
   g_err.clear();
   return CAT_OK;
@@ -354,6 +371,9 @@ cat_status cat_plan_destroy(cat_plan plan) {
   if (plan == nullptr) return CAT_OK;
   if (plan->d_tw) (void)hipFree(plan->d_tw);
   free_events(plan);
+  if (plan->join_ev) (void)hipEventDestroy(plan->join_ev);
+  if (plan->fork_ev) (void)hipEventDestroy(plan->fork_ev);
+  if (plan->side) (void)hipStreamDestroy(plan->side);
 
   delete plan;
   return CAT_OK;
@@ -872,6 +892,28 @@ cat_status cat_backward_1d(cat_plan plan, const void* X, const void* W_A, const 
   if (e != hipSuccess) return hip_fail(e, "projection launch");
   // dlogits (fp32) and dV
   if ((st = mix_backward_core(plan, bz, bV, dO, bdz, bdV, workspace, s, &mk)) != CAT_OK) return st;
+  // the weight gradients (the longer branch, enqueued first) run on the
+  // plan's side stream beside dX
+  if ((e = hipEventRecord(plan->fork_ev, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  if ((e = hipStreamWaitEvent(plan->side, plan->fork_ev, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+  // dW_V = X^T dV and dW_A = X^T dz^T as two output segments of one
+  // product (X^T the shared row operand, K = B N); dW_A's padded columns
+  // are dropped afterwards
+  hipStream_t sw = plan->side;
+  void* bXt = ws_at(workspace, plan->off_bXt);
+  void* bdzt = ws_at(workspace, plan->off_bP);
+  void* bdWA = ws_at(workspace, plan->off_bdW);
+  if ((e = launch_transpose(et, X, bXt, B * N, D, sw)) != hipSuccess) return hip_fail(e, "transpose launch");
+  if ((e = launch_pack_grads(et, nullptr, bdz, bdzt, B, N, 0, H, plan->Hp, sw)) != hipSuccess)
+    return hip_fail(e, "pack launch");
+  GemmArgs gw = gemm_base(plan, bXt);
+  gw.M = D;
+  gw.K = B * N;
+  gw.nseg = 2;
+  gw.seg[0] = seg(bdV, dW_V, D, 0, OUT_ROWMAJOR, 1);
+  gw.seg[1] = seg(bdzt, bdWA, plan->Hp, 0, OUT_ROWMAJOR, 1);
+  if ((e = launch_gemm(et, gw, sw)) != hipSuccess) return hip_fail(e, "dW launch");
+  if ((e = launch_take_cols(et, bdWA, dW_A, D, plan->Hp, H, sw)) != hipSuccess) return hip_fail(e, "dW_A copy launch");
   // dX = dV W_V^T (fp32), then + dz^T W_A^T in the storage dtype
   void* bWt = ws_at(workspace, plan->off_bWt);
   float* bdXf = reinterpret_cast<float*>(ws_at(workspace, plan->off_bdXf));
@@ -882,23 +924,9 @@ cat_status cat_backward_1d(cat_plan plan, const void* X, const void* W_A, const 
   if ((e = launch_gemm(et, gx, s)) != hipSuccess) return hip_fail(e, "dX launch");
   if ((e = launch_rank_heads_add(et, bdXf, bdz, W_A, dX, B, N, D, H, s)) != hipSuccess)
     return hip_fail(e, "dX heads launch");
-  // dW_V = X^T dV and dW_A = X^T dz^T as two output segments of one
-  // product (X^T the shared row operand, K = B N); dW_A's padded columns
-  // are dropped afterwards
-  void* bXt = ws_at(workspace, plan->off_bXt);
-  void* bdzt = ws_at(workspace, plan->off_bP);
-  void* bdWA = ws_at(workspace, plan->off_bdW);
-  if ((e = launch_transpose(et, X, bXt, B * N, D, s)) != hipSuccess) return hip_fail(e, "transpose launch");
-  if ((e = launch_pack_grads(et, nullptr, bdz, bdzt, B, N, 0, H, plan->Hp, s)) != hipSuccess)
-    return hip_fail(e, "pack launch");
-  GemmArgs gw = gemm_base(plan, bXt);
-  gw.M = D;
-  gw.K = B * N;
-  gw.nseg = 2;
-  gw.seg[0] = seg(bdV, dW_V, D, 0, OUT_ROWMAJOR, 1);
-  gw.seg[1] = seg(bdzt, bdWA, plan->Hp, 0, OUT_ROWMAJOR, 1);
-  if ((e = launch_gemm(et, gw, s)) != hipSuccess) return hip_fail(e, "dW launch");
-  if ((e = launch_take_cols(et, bdWA, dW_A, D, plan->Hp, H, s)) != hipSuccess) return hip_fail(e, "dW_A copy launch");
+  // join: the caller's stream waits for the weight gradients
+  if ((e = hipEventRecord(plan->join_ev, sw)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  if ((e = hipStreamWaitEvent(s, plan->join_ev, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
   return check_sync(plan, "backward");
 }
 

@@ -44,8 +44,11 @@
  * everything queued on `stream` afterwards runs after it; every kernel of a
  * call runs on `stream` (1D: projection with the fused score projection,
  * softmax + spectrum, fft-conv).  Calls never allocate, never
- * synchronise, and return as soon as the work is queued.  A plan owns small
- * device tables created at plan creation; the workspace (size from
+ * synchronise, and return as soon as the work is queued (cat_backward_1d
+ * also uses one plan-owned stream, joined back to `stream` before it
+ * returns).  A plan owns small device tables (and, for 1D plans on
+ * single-workgroup lines, that stream and two events) created at plan
+ * creation; the workspace (size from
  * cat_plan_workspace_size) holds the intermediates and is owned by the
  * caller.  Calls that share a plan and workspace must be ordered (same stream).
  *
@@ -256,7 +259,11 @@ cat_status cat_step_mix_backward_1d(cat_plan plan, const float* logits, const vo
  * and dz enter the weight products rounded to the storage dtype).
  * Errors: CAT_ERR_PLAN_MISMATCH for a 2D plan; CAT_ERR_UNSUPPORTED on the
  * multi-pass path and unless B N is a positive multiple of 8;
- * CAT_ERR_INVALID_ARG for NULL or misaligned pointers. */
+ * CAT_ERR_INVALID_ARG for NULL or misaligned pointers.  Streams: the
+ * weight-gradient branch runs on a stream the plan owns (default priority),
+ * forked from `stream` by an event after the mixing backward and joined
+ * back before the call returns, so every output is ordered on `stream` like
+ * any other call's; calls sharing a plan must still be ordered. */
 cat_status cat_backward_1d(cat_plan plan, const void* X, const void* W_A, const void* W_V, const void* dO, void* dX,
                            void* dW_A, void* dW_V, void* workspace, void* stream);
 

@@ -360,7 +360,7 @@ def test_mix_backward_1d_workload_full_size(cat):
 @pytest.mark.parametrize("B,N,D,H,dtype,path", [
     (2, 64, 64, 4, "f32", "fft_valu"), (1, 128, 128, 2, "bf16", "direct"), (2, 1024, 128, 2, "bf16", "fft_matrix"),
     (1, 200, 96, 3, "f32", "fft_valu"), (4, 6, 16, 2, "f32", "fft_valu"), (1, 8, 64, 32, "bf16", "fft_valu"),
-    (2, 512, 96, 12, "bf16", "fft_valu")])
+    (2, 512, 96, 12, "bf16", "fft_valu"), (8, 1000, 64, 4, "f32", "fft_valu"), (2, 4096, 32, 2, "f32", "fft_valu")])
 def test_backward_1d(cat, B, N, D, H, dtype, path):
     """Gradients of the whole 1D forward (dX, dW_A, dW_V) against the oracle's
     chain rule; the mixing runs on the plan's path, the products on the
@@ -378,8 +378,12 @@ def test_backward_1d(cat, B, N, D, H, dtype, path):
     torch.cuda.synchronize()
     ref = oracle.cat_backward_1d(inp.X, inp.W_A, inp.W_V, g)
     assert_parity(to_np(dX), ref["dX"], dtype, "dX")
-    assert_parity(to_np(dWA), ref["dW_A"], dtype, "dW_A")
-    assert_parity(to_np(dWV), ref["dW_V"], dtype, "dW_V")
+    # the weight gradients sum over all B N tokens, so their entries grow
+    # with B N; the fp32 max-abs bar (stated for unit-scale outputs) is
+    # applied relative to the largest entry
+    for name, got in (("dW_A", dWA), ("dW_V", dWV)):
+        sc = max(1.0, float(np.max(np.abs(ref[name]))))
+        assert_parity(to_np(got) / sc, ref[name] / sc, dtype, name)
 
 
 def test_backward_1d_rejections(cat):

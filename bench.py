@@ -153,7 +153,7 @@ def cpu_baseline(wl, inp, target_s: float, W_A=None):
         t0 = time.perf_counter()
         oracle.cat_scored_forward_2d(inp.X[:1], W_A[:, :1], inp.W_V[:, :d], wl.Hg, wl.Wg)
         secs = time.perf_counter() - t0
-        return dict(value=wl.N / (secs * wl.H), unit="tokens/s", cores=threads, kind="oracle",
+        return dict(cpu_model=cpu_model(), value=wl.N / (secs * wl.H), unit="tokens/s", cores=threads, kind="oracle",
                     sample=f"one head of one image (1/{wl.H} of an image, {wl.N} tokens) in {secs:.1f} s, "
                            f"scaled by {wl.H} heads per image; fp64 direct O(N^2 d) sums")
     if wl.kind == "1d" and wl.N > 4096:
@@ -175,7 +175,7 @@ def cpu_baseline(wl, inp, target_s: float, W_A=None):
         oracle.circulant_1d(zs, V, rows=list(range(r)))
         t_row = (time.perf_counter() - t0) / r
         per_token = t_proj / wl.N + t_row
-        return dict(value=1.0 / per_token, unit="tokens/s", cores=threads, kind="oracle",
+        return dict(cpu_model=cpu_model(), value=1.0 / per_token, unit="tokens/s", cores=threads, kind="oracle",
                     sample=f"projections of 1 sequence ({wl.N} tokens, {t_proj:.1f} s) and the fp64 direct "
                            f"circulant sum for {r} of its rows ({t_row * r:.1f} s); tokens/s = 1 / "
                            f"(projection time per token + sum time per row)")
@@ -188,7 +188,7 @@ def cpu_baseline(wl, inp, target_s: float, W_A=None):
         oracle.cat_forward_1d(inp.X[1:1 + n], inp.W_A, inp.W_V)
         tn = time.perf_counter() - t0
         imgs, secs = 1 + n, t1 + tn
-        return dict(value=imgs * wl.N / secs, unit="tokens/s", cores=threads, kind="oracle",
+        return dict(cpu_model=cpu_model(), value=imgs * wl.N / secs, unit="tokens/s", cores=threads, kind="oracle",
                     sample=f"{imgs} of {wl.B} sequences ({imgs * wl.N} tokens), fp64 direct O(N^2 d) sums, "
                            f"{secs:.1f} s")
     # 2D: one (image, head) slice end to end; a whole image is H such slices
@@ -198,9 +198,83 @@ def cpu_baseline(wl, inp, target_s: float, W_A=None):
     oracle.cat_forward_bccb_2d(inp.X[:1], inp.W_Q[:, hs], inp.W_K[:, hs], inp.W_V[:, hs], wl.Hg, wl.Wg, 1)
     secs = time.perf_counter() - t0
     per_image = secs * wl.H
-    return dict(value=wl.N / per_image, unit="tokens/s", cores=threads, kind="oracle",
+    return dict(cpu_model=cpu_model(), value=wl.N / per_image, unit="tokens/s", cores=threads, kind="oracle",
                 sample=f"one head of one image (1/{wl.H} of an image, {wl.N} tokens) in {secs:.1f} s, "
                        f"scaled by {wl.H} heads per image; fp64 direct O(N^2 d) sums")
+
+
+def timed_steps(step, K: int):
+    """The timed region: K steps between synchronisations, with an event on
+    the launch stream at every step boundary.  Returns the wall-clock mean
+    (the headline's step time), the events' mean, and the per-step event
+    durations (their median is reported beside the mean)."""
+    import torch
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    evs[0].record()
+    for i in range(K):
+        step(i)
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(K)]
+    ms = wall * 1000.0 / K
+    ev_ms = evs[0].elapsed_time(evs[K]) / K
+    log(f"{K} steps: {ms * 1000:.1f} us/step wall, {ev_ms * 1000:.1f} us/step events, "
+        f"median {sorted(per)[K // 2] * 1000:.1f} us")
+    return ms, ev_ms, per
+
+
+def step_stats(per):
+    """Median and 10th / 90th percentiles of per-step event times (ms)."""
+    q = sorted(per)
+    n = len(q)
+    return {"median": round(q[n // 2], 5), "p10": round(q[n // 10], 5), "p90": round(q[min(n - 1, (9 * n) // 10)], 5)}
+
+
+def copy_bandwidth(nbytes: int = 1 << 30, reps: int = 10):
+    """Measured device-to-device copy rate (GB/s, bytes read + written per
+    second) of torch's copy kernel over two buffers far larger than the
+    Infinity Cache: the attainable HBM rate on this machine, next to the 8 TB/s
+    peak."""
+    import torch
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    secs = e0.elapsed_time(e1) / 1000.0 / reps
+    del src, dst
+    return round(2.0 * nbytes / secs / 1e9, 1)
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def dtype_label(storage: str, conv_path: str) -> str:
+    """What the path computes in: storage dtype, then the arithmetic of the
+    projection and of the mixing; accumulation is fp32 everywhere."""
+    if storage == "f32":
+        return "f32 (fp32 MFMA GEMM, fp32 transforms)"
+    mix = {"fft_matrix": "fp16-operand MFMA DFT products with per-line power-of-two scaling",
+           "direct": "bf16 MFMA direct product (softmax weights rounded to bf16)",
+           "fft_valu": "fp32 vector-ALU transforms",
+           "fft_multipass": "fp32 vector-ALU transforms"}.get(conv_path, conv_path)
+    return f"bf16 storage; bf16 MFMA GEMM; {mix}; fp32 accumulate"
 
 
 def run(args):
@@ -258,19 +332,7 @@ def run(args):
         step(i)
     torch.cuda.synchronize()
 
-    # timed region: K steps between synchronisations
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record()
-    for i in range(args.steps):
-        step(i)
-    ev1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1000.0 / args.steps
-    gpu_ms_per_step = ev0.elapsed_time(ev1) / args.steps
-    log(f"{args.steps} steps: {ms_per_step * 1000:.1f} us/step wall, {gpu_ms_per_step * 1000:.1f} us/step events")
+    ms_per_step, gpu_ms_per_step, step_ms = timed_steps(step, args.steps)
 
     # instrumented pass, K more steps: the library launches every kernel with
     # start/stop events that its dispatch stamps (same stream as the kernel);
@@ -325,6 +387,49 @@ def run(args):
                     frac=round(achieved / peak, 4), traffic=measured_traffic(dom, wl.name, kd["launches_per_call"]),
                     hbm_frac=kd["hbm_frac"], compute_frac=kd["compute_frac"], us=kd["us"])
 
+    if wl.kind == "1d" and conv_path in ("fft_matrix", "direct") and not cat2d:
+        # the same mixing on the fp32 vector-ALU transforms (CAT_CONV=valu),
+        # its kernels timed over K forward calls of a plan that takes them
+        # (one buffer set; reported beside the step, not part of it)
+        prev = os.environ.get("CAT_CONV")
+        os.environ["CAT_CONV"] = "valu"
+        try:
+            vplan = cat.cat_plan_create("1d", wl.dtype, wl.B, wl.N, wl.D, wl.H)
+        finally:
+            if prev is None:
+                os.environ.pop("CAT_CONV")
+            else:
+                os.environ["CAT_CONV"] = prev
+        vws = cat.alloc_workspace(vplan)
+        Ov = torch.empty_like(x0)
+        for _ in range(3):
+            cat.cat_forward_1d(vplan, X[0], *weights, O=Ov, workspace=vws)
+        cat.cat_plan_set_timing(vplan, True)
+        for _ in range(args.steps):
+            cat.cat_forward_1d(vplan, X[0], *weights, O=Ov, workspace=vws)
+        torch.cuda.synchronize()
+        vt = cat.cat_plan_kernel_times(vplan)
+        cat.cat_plan_set_timing(vplan, False)
+        vmodel = kernel_model(wl, vplan.geometry()[0], ngrp)
+        for k in ("spectrum", "fftconv"):
+            ms, n = vt[k]
+            if n:
+                mm = vmodel[k]
+                kernels[k + "_valu_f32"] = dict(us=round(ms * 1000, 3), launches_per_call=1, bytes=int(mm["bytes"]),
+                                                flops=float(mm["flops"]),
+                                                hbm_frac=round(mm["bytes"] / (ms / 1000) / 1e9 / HBM_PEAK_GBS, 4),
+                                                compute_frac=round(mm["flops"] / (ms / 1000) / 1e12 / PEAK_TFLOPS["valu_f32"], 4),
+                                                compute_unit="valu_f32", note="fp32 vector-ALU mixing (CAT_CONV=valu), "
+                                                "not in the timed step")
+                log(f"  kernel {k + '_valu_f32':18s} {ms * 1000:9.2f} us (fp32 vector path, not in the step)")
+        del vplan
+
+    copy_gbs = copy_bandwidth()
+    log(f"device copy: {copy_gbs:.0f} GB/s")
+    roofline["measured_copy_GBps"] = copy_gbs
+    if roofline["unit"] == "GB/s":
+        roofline["frac_of_copy"] = round(roofline["achieved"] / copy_gbs, 4)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
@@ -343,10 +448,11 @@ def run(args):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
+        "step_ms_events": step_stats(step_ms),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32" if wl.dtype == "f32" else "bf16-storage/f32-compute",
+        "dtype": dtype_label(wl.dtype, conv_path),
         "data": "synthetic (seeded PCG64: X~N(0,1), W~N(0,1/D))",
         "config": {"workload": wl.name, "kind": "2d-cat-scored" if cat2d else wl.kind, "B": wl.B, "N": wl.N, "D": wl.D, "H": wl.H,
                    "grid": [wl.Hg, wl.Wg] if wl.kind == "2d" else None, "storage": wl.dtype,
@@ -434,16 +540,7 @@ def run_backward(args):
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    ev0.record()
-    for i in range(args.steps):
-        step(i)
-    ev1.record()
-    torch.cuda.synchronize()
-    ms_per_step = (time.perf_counter() - t0) * 1000.0 / args.steps
-    gpu_ms_per_step = ev0.elapsed_time(ev1) / args.steps
-    log(f"{args.steps} steps: {ms_per_step * 1000:.1f} us/step wall, {gpu_ms_per_step * 1000:.1f} us/step events")
+    ms_per_step, gpu_ms_per_step, step_ms = timed_steps(step, args.steps)
 
     cat.cat_plan_set_timing(plan, True)
     torch.cuda.synchronize()
@@ -495,7 +592,7 @@ def run_backward(args):
             oracle.mix_backward_1d(zc[nseq:nseq + 1], Vc[nseq:nseq + 1], gc[nseq:nseq + 1])
             secs += time.perf_counter() - t0
             nseq += 1
-        cpu = dict(value=nseq * wl.N / secs, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
+        cpu = dict(cpu_model=cpu_model(), value=nseq * wl.N / secs, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
                    sample=f"{nseq} of {wl.B} sequences ({nseq * wl.N} tokens), fp64 direct O(N^2 d) sums for dV "
                           f"and dz*, {secs:.1f} s")
         log("cpu baseline:", cpu)
@@ -511,10 +608,11 @@ def run_backward(args):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
+        "step_ms_events": step_stats(step_ms),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32" if wl.dtype == "f32" else "bf16-storage/f32-compute",
+        "dtype": dtype_label(wl.dtype, conv_path),
         "data": "synthetic (seeded PCG64: V, logits = projections of X~N(0,1); dO~N(0,1))",
         "gemm_flops_per_step": (2.0 * tokens * wl.D * (2 * wl.D + wl.H) + 2.0 * wl.D * tokens * (wl.D + (wl.H + 7) // 8 * 8))
         if full else None,

@@ -646,6 +646,60 @@ cat_status mix_backward_core(cat_plan plan, const float* logits, const void* V, 
   return check_sync(plan, "mixing backward");
 }
 
+// The two branches of the whole backward after the mixing backward: dW_V
+// and dW_A on the plan's side stream (already forked from `s`), dX on `s`.
+// Returns the first failure; the caller joins the side stream either way.
+cat_status backward_branches(cat_plan plan, const void* X, const void* W_A, const void* W_V, void* dX, void* dW_A,
+                             void* dW_V, void* workspace, hipStream_t s, void* bdV, float* bdz) {
+  const int B = (int)plan->p.B, N = (int)plan->p.N, D = (int)plan->p.D, H = (int)plan->p.H;
+  const int et = plan->et;
+  hipError_t e;
+  // dW_V = X^T dV and dW_A = X^T dz^T as two output segments of one
+  // product (X^T the shared row operand, K = B N); dW_A's padded columns
+  // are dropped afterwards
+  hipStream_t sw = plan->side;
+  void* bXt = ws_at(workspace, plan->off_bXt);
+  void* bdzt = ws_at(workspace, plan->off_bP);
+  void* bdWA = ws_at(workspace, plan->off_bdW);
+  if ((e = launch_transpose(et, X, bXt, B * N, D, sw)) != hipSuccess) return hip_fail(e, "transpose launch");
+  if ((e = launch_pack_grads(et, nullptr, bdz, bdzt, B, N, 0, H, plan->Hp, sw)) != hipSuccess)
+    return hip_fail(e, "pack launch");
+  GemmArgs gw = gemm_base(plan, bXt);
+  gw.M = D;
+  gw.K = B * N;
+  gw.nseg = 2;
+  gw.seg[0] = seg(bdV, dW_V, D, 0, OUT_ROWMAJOR, 1);
+  gw.seg[1] = seg(bdzt, bdWA, plan->Hp, 0, OUT_ROWMAJOR, 1);
+  if ((e = launch_gemm(et, gw, sw)) != hipSuccess) return hip_fail(e, "dW launch");
+  if ((e = launch_take_cols(et, bdWA, dW_A, D, plan->Hp, H, sw)) != hipSuccess) return hip_fail(e, "dW_A copy launch");
+  // dX = dV W_V^T (fp32), then + dz^T W_A^T in the storage dtype
+  void* bWt = ws_at(workspace, plan->off_bWt);
+  float* bdXf = reinterpret_cast<float*>(ws_at(workspace, plan->off_bdXf));
+  if ((e = launch_transpose(et, W_V, bWt, D, D, s)) != hipSuccess) return hip_fail(e, "transpose launch");
+  GemmArgs gx = gemm_base(plan, bdV);
+  gx.nseg = 1;
+  gx.seg[0] = seg(bWt, bdXf, D, 1, OUT_ROWMAJOR, 1);
+  if ((e = launch_gemm(et, gx, s)) != hipSuccess) return hip_fail(e, "dX launch");
+  if ((e = launch_rank_heads_add(et, bdXf, bdz, W_A, dX, B, N, D, H, s)) != hipSuccess)
+    return hip_fail(e, "dX heads launch");
+  return CAT_OK;
+}
+
+// Join: `s` waits for everything queued on the plan's side stream.
+cat_status join_side(cat_plan plan, hipStream_t s) {
+  hipError_t e = hipEventRecord(plan->join_ev, plan->side);
+  if (e != hipSuccess) {
+    // without the event, wait for the side stream from the host instead
+    (void)hipStreamSynchronize(plan->side);
+    return hip_fail(e, "hipEventRecord");
+  }
+  if ((e = hipStreamWaitEvent(s, plan->join_ev, 0)) != hipSuccess) {
+    (void)hipStreamSynchronize(plan->side);
+    return hip_fail(e, "hipStreamWaitEvent");
+  }
+  return CAT_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -896,37 +950,13 @@ cat_status cat_backward_1d(cat_plan plan, const void* X, const void* W_A, const 
   // plan's side stream beside dX
   if ((e = hipEventRecord(plan->fork_ev, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   if ((e = hipStreamWaitEvent(plan->side, plan->fork_ev, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
-  // dW_V = X^T dV and dW_A = X^T dz^T as two output segments of one
-  // product (X^T the shared row operand, K = B N); dW_A's padded columns
-  // are dropped afterwards
-  hipStream_t sw = plan->side;
-  void* bXt = ws_at(workspace, plan->off_bXt);
-  void* bdzt = ws_at(workspace, plan->off_bP);
-  void* bdWA = ws_at(workspace, plan->off_bdW);
-  if ((e = launch_transpose(et, X, bXt, B * N, D, sw)) != hipSuccess) return hip_fail(e, "transpose launch");
-  if ((e = launch_pack_grads(et, nullptr, bdz, bdzt, B, N, 0, H, plan->Hp, sw)) != hipSuccess)
-    return hip_fail(e, "pack launch");
-  GemmArgs gw = gemm_base(plan, bXt);
-  gw.M = D;
-  gw.K = B * N;
-  gw.nseg = 2;
-  gw.seg[0] = seg(bdV, dW_V, D, 0, OUT_ROWMAJOR, 1);
-  gw.seg[1] = seg(bdzt, bdWA, plan->Hp, 0, OUT_ROWMAJOR, 1);
-  if ((e = launch_gemm(et, gw, sw)) != hipSuccess) return hip_fail(e, "dW launch");
-  if ((e = launch_take_cols(et, bdWA, dW_A, D, plan->Hp, H, sw)) != hipSuccess) return hip_fail(e, "dW_A copy launch");
-  // dX = dV W_V^T (fp32), then + dz^T W_A^T in the storage dtype
-  void* bWt = ws_at(workspace, plan->off_bWt);
-  float* bdXf = reinterpret_cast<float*>(ws_at(workspace, plan->off_bdXf));
-  if ((e = launch_transpose(et, W_V, bWt, D, D, s)) != hipSuccess) return hip_fail(e, "transpose launch");
-  GemmArgs gx = gemm_base(plan, bdV);
-  gx.nseg = 1;
-  gx.seg[0] = seg(bWt, bdXf, D, 1, OUT_ROWMAJOR, 1);
-  if ((e = launch_gemm(et, gx, s)) != hipSuccess) return hip_fail(e, "dX launch");
-  if ((e = launch_rank_heads_add(et, bdXf, bdz, W_A, dX, B, N, D, H, s)) != hipSuccess)
-    return hip_fail(e, "dX heads launch");
-  // join: the caller's stream waits for the weight gradients
-  if ((e = hipEventRecord(plan->join_ev, sw)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-  if ((e = hipStreamWaitEvent(s, plan->join_ev, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+  // From here on every exit joins the side stream back into `s`, so no
+  // work of this call can still be queued on it once the caller reuses
+  // the outputs or the workspace.
+  st = backward_branches(plan, X, W_A, W_V, dX, dW_A, dW_V, workspace, s, bdV, bdz);
+  const cat_status jst = join_side(plan, s);
+  if (st != CAT_OK) return st;
+  if (jst != CAT_OK) return jst;
   return check_sync(plan, "backward");
 }
 

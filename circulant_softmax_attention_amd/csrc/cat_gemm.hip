@@ -9,7 +9,7 @@
 // write it.  One launch covers up to three column segments, each written in
 // the layout its consumer reads.
 //
-// Tiling: 128 x BN output tile (BN = 96 or 128) per 256-thread workgroup (4
+// Tiling: 128 x BN output tile (BN = 96, 128 or 192) per 256-thread workgroup (4
 // waves, 2 x 2), each wave a 64 x BN/2 block of 16 x 16 MFMA tiles.  K is
 // walked in tiles of 128 bytes of an X row (64 bf16 or 32 fp32 values), i.e.
 // eight 16-byte chunks; a chunk is what one lane feeds the MFMA:
@@ -35,13 +35,13 @@
 // registers with the missing values zeroed.
 //
 // Score projection (1D): z = X W_A has only one column per head (at most
-// 32), far too narrow for a tile of its own.  It is computed by extra
-// workgroups placed ahead of the output tiles in the same grid, so they run
-// in the first round beside the tiles and need no launch of their own.  Each
-// takes 64 rows of X, reads them with plain 16-byte loads straight into MFMA
-// operand registers (many loads in flight per lane), and multiplies them by
-// W_A^T, which it stages head-major in LDS in K passes that fit the kernel's
-// LDS.
+// 32), far too narrow for a tile of its own.  It is folded into the output
+// tiles of the first segment: the first min(8, column tiles) tiles of a row
+// panel share its eight 16-row blocks, and the wave that owns a block
+// multiplies the X fragments it already holds for the main product by W_A^T
+// fragments (16 heads per MFMA block, one or two blocks) loaded from global
+// memory a K tile ahead.  X is therefore read once for both products; z
+// leaves head-major ([B][H][N] fp32) from registers.
 #include "cat_common.hpp"
 #include "cat_internal.hpp"
 

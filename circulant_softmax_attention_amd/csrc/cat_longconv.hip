@@ -22,10 +22,13 @@
 // The filter spectrum is the column pass and the forward half of the row
 // pass applied to the softmax line, scaled by 1/L; the softmax is reduced
 // in chunks first, and the column pass normalises the logits as it loads
-// them.  Each short DFT runs as a Stockham transform in LDS (radix-4
-// stages, one radix-2 stage when log2 of its length is odd; natural order
-// in and out), several lines per workgroup; all twiddles come from one
-// table W_L^m, m < L, computed in double precision on the host.  Two real
+// them.  A short DFT of square length (64 or 256) runs as a register
+// four-step: sqrt(M) lanes per line, a register DFT over each lane's
+// values, the twiddle, one exchange through LDS and a second register DFT;
+// other lengths (128) run as a Stockham transform in LDS (radix-4 stages,
+// one radix-2 stage when log2 of the length is odd; natural order in and
+// out), several lines per workgroup.  All twiddles come from one table
+// W_L^m, m < L, computed in double precision on the host.  Two real
 // channels ride in one complex line, as in the single-workgroup
 // convolution.
 //

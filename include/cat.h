@@ -33,8 +33,12 @@
  *   the pages write them; a torch nn.Linear weight is the transpose),
  *   O [B][N][D].
  * Storage dtype (CAT_F32 or CAT_BF16) is the same for X, the weights and O;
- * all arithmetic is fp32 (bf16 inputs are widened exactly, O is rounded to
- * nearest even).  X, the weights, O and the workspace must be 16-byte
+ * accumulation is fp32 throughout (bf16 inputs are widened exactly, O is
+ * rounded to nearest even).  Two bf16 paths multiply in lower precision:
+ * CAT_PATH_FFT_MATRIX runs its DFT products on fp16 operands (each line
+ * scaled by a power of two) and CAT_PATH_DIRECT rounds the softmax weights
+ * to bf16 for its products; CAT_CONV=valu (see cat_plan_conv_path) keeps
+ * every product in fp32.  X, the weights, O and the workspace must be 16-byte
  * aligned; O must not overlap X, the weights or the workspace.
  *
  * Calls
@@ -262,8 +266,11 @@ cat_status cat_step_mix_backward_1d(cat_plan plan, const float* logits, const vo
  * CAT_ERR_INVALID_ARG for NULL or misaligned pointers.  Streams: the
  * weight-gradient branch runs on a stream the plan owns (default priority),
  * forked from `stream` by an event after the mixing backward and joined
- * back before the call returns, so every output is ordered on `stream` like
- * any other call's; calls sharing a plan must still be ordered. */
+ * back before the call returns (on every return after the fork, errors
+ * included), so every output is ordered on `stream` like any other call's.
+ * Calls sharing a plan must be ordered, and two host threads must not run
+ * this entry on one plan at the same time: the fork and join events belong
+ * to the plan. */
 cat_status cat_backward_1d(cat_plan plan, const void* X, const void* W_A, const void* W_V, const void* dO, void* dX,
                            void* dW_A, void* dW_V, void* workspace, void* stream);
 

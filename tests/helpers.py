@@ -21,14 +21,49 @@ def ensure_lib():
     return LIB
 
 
+def _real(a, what: str) -> np.ndarray:
+    a = np.asarray(a)
+    if np.iscomplexobj(a):
+        raise TypeError(f"{what} is complex: compare complex values through as_real_pairs()")
+    return a.astype(np.float64)
+
+
+def as_real_pairs(a) -> np.ndarray:
+    """Complex array -> float64 array with a trailing (real, imag) axis, so
+    that both parts enter the parity metrics."""
+    a = np.asarray(a)
+    return np.stack([a.real, a.imag], axis=-1).astype(np.float64)
+
+
 def rel_l2(got, ref) -> float:
-    got = np.asarray(got, dtype=np.float64)
-    ref = np.asarray(ref, dtype=np.float64)
+    got = _real(got, "got")
+    ref = _real(ref, "ref")
     return float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
 
 
 def max_abs(got, ref) -> float:
-    return float(np.max(np.abs(np.asarray(got, dtype=np.float64) - np.asarray(ref, dtype=np.float64))))
+    return float(np.max(np.abs(_real(got, "got") - _real(ref, "ref"))))
+
+
+U32 = 2.0 ** -24  # unit roundoff of fp32
+
+
+def sum_bar(K: int, rms_a: float, rms_b: float, eps_in: float = 1e-5, tail: float = 5.0) -> float:
+    """Max-abs bar for entries of an fp32 product summed over K terms a_t b_t
+    (the weight gradients, K = B N tokens).
+
+    Accumulation: the running sum of K terms of random sign has size about
+    sqrt(t) rms(a b) after t terms, and each of the (at most K) additions
+    rounds it with a relative error up to u = 2^-24; independent roundings
+    add in quadrature, sqrt(sum_t t) u rms(ab) = u K rms(ab) / sqrt(2).
+    Inputs: b is itself a computed fp32 result held to relative L2 eps_in
+    (the fp32 bar of the step that makes it), so its errors add
+    sqrt(K) eps_in rms(a) rms(b).  rms(ab) <= rms(a) rms(b) for independent
+    factors.  `tail` covers the largest of many entries (about 5 standard
+    deviations).  Never tighter than the stated 1e-4 for unit-scale outputs.
+    """
+    per = (U32 * K / np.sqrt(2.0) + eps_in * np.sqrt(K)) * rms_a * rms_b
+    return float(max(1e-4, tail * per))
 
 
 def assert_parity(got, ref, dtype: str, what: str = ""):
@@ -40,6 +75,12 @@ def assert_parity(got, ref, dtype: str, what: str = ""):
     if tol["abs"] is not None:
         assert m <= tol["abs"], msg
     return r, m
+
+
+def assert_spectrum_parity(got, ref, what: str = ""):
+    """Complex spectra at the fp32 bar, real and imaginary parts both."""
+    assert np.iscomplexobj(got) and np.iscomplexobj(ref), what
+    return assert_parity(as_real_pairs(got), as_real_pairs(ref), "f32", what)
 
 
 def to_dev(arr, dtype: str, device="cuda"):

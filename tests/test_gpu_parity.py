@@ -14,7 +14,8 @@ import pytest
 
 import oracle
 from circulant_softmax_attention_amd import workloads as W
-from helpers import assert_parity, ensure_lib, rel_l2, to_dev, to_np
+from helpers import (as_real_pairs, assert_parity, assert_spectrum_parity, ensure_lib, rel_l2, sum_bar, to_dev,
+                     to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -124,7 +125,8 @@ def test_spectrum_1d(cat, N):
     assert_parity(to_np(probs), zs, "f32", "softmax")
     ref = np.fft.fft(_extended_line(zs, L), axis=-1) / L
     got = spec.cpu().numpy()
-    assert rel_l2(got, ref) < 1e-5, rel_l2(got, ref)
+    assert np.iscomplexobj(got) and got.shape == ref.shape
+    assert_spectrum_parity(got, ref, "spectrum")
 
 
 @pytest.mark.parametrize("B,N,D,H,dtype", [(1, 1, 16, 2, "f32"), (2, 2, 16, 2, "f32"), (2, 3, 16, 2, "f32"),
@@ -378,12 +380,26 @@ def test_backward_1d(cat, B, N, D, H, dtype, path):
     torch.cuda.synchronize()
     ref = oracle.cat_backward_1d(inp.X, inp.W_A, inp.W_V, g)
     assert_parity(to_np(dX), ref["dX"], dtype, "dX")
-    # the weight gradients sum over all B N tokens, so their entries grow
-    # with B N; the fp32 max-abs bar (stated for unit-scale outputs) is
-    # applied relative to the largest entry
-    for name, got in (("dW_A", dWA), ("dW_V", dWV)):
-        sc = max(1.0, float(np.max(np.abs(ref[name]))))
-        assert_parity(to_np(got) / sc, ref[name] / sc, dtype, name)
+    check_weight_grads(ref, inp.X, {"dW_A": dWA, "dW_V": dWV}, dtype)
+
+
+def check_weight_grads(ref, X, got, dtype):
+    """dW_V = X^T dV and dW_A = X^T dz^T sum over K = B N tokens.  The
+    relative L2 bar is the stated one; the fp32 max-abs bar is derived from
+    fp32 accumulation over K terms and the fp32 bar of the mixing step that
+    makes dV and dz (helpers.sum_bar), since the stated 1e-4 is for
+    unit-scale outputs of short sums."""
+    B, N, _ = X.shape
+    K = B * N
+    rms_x = float(np.sqrt(np.mean(np.asarray(X, np.float64) ** 2)))
+    for name, fac in (("dW_A", "dz"), ("dW_V", "dV")):
+        g, r = to_np(got[name]), ref[name]
+        rl = rel_l2(g, r)
+        assert rl <= (1e-5 if dtype == "f32" else 2e-2), f"{name}: rel_l2={rl:.3e}"
+        if dtype == "f32":
+            bar = sum_bar(K, rms_x, float(np.sqrt(np.mean(ref[fac] ** 2))))
+            m = float(np.max(np.abs(g - r)))
+            assert m <= bar, f"{name}: max_abs={m:.3e} > bar {bar:.3e} (K={K})"
 
 
 def test_backward_1d_rejections(cat):

@@ -23,6 +23,14 @@ the steps in the order the pages give:
   CAT-scored 2D variant: the CAT scores z = X W_A, softmaxed over the grid,
   as the filter of the 2D circular convolution below.
 
+  Averaged-key variant (the ablation table's "qkv (Averaged-Key)" row):
+      Q, K, V = X W_Q, X W_K, X W_V;  kbar_h = token mean of K_h
+      z_h[n] = Q_h[n] . kbar_h / sqrt(d)  ->  softmax over n  ->  circ(.) V_h
+
+  Causal CAT (the training-strategy note on causal language models): row i
+  of circ(z_h) keeps the tokens j <= i and is softmaxed over them,
+      O[i] = sum_{j<=i} exp(z[i - j]) V[j] / sum_{j<=i} exp(z[i - j])
+
   2D circulant attention (Vision Transformers are Circulant Attention
   Learners, "Circulant Attention: attention rebuilt with the FFT"):
       Q, K, V = X W_Q, X W_K, X W_V
@@ -67,9 +75,10 @@ def _load():
         lib.oracle_bccb_2d.argtypes = [_P, _P, _P, _i64, _i64, _i64, _i64, _i64, _I64P, _i64]
         lib.oracle_circulant_1d_transpose.argtypes = [_P, _P, _P, _i64, _i64, _i64, _i64]
         lib.oracle_circulant_1d_grad_w.argtypes = [_P, _P, _P, _i64, _i64, _i64, _i64]
+        lib.oracle_causal_1d.argtypes = [_P, _P, _P, _i64, _i64, _i64, _i64, _I64P, _i64]
         for f in ("oracle_matmul", "oracle_scores_1d", "oracle_softmax_rows",
                   "oracle_circulant_1d", "oracle_scores_bccb_2d", "oracle_bccb_2d",
-                  "oracle_circulant_1d_transpose", "oracle_circulant_1d_grad_w"):
+                  "oracle_circulant_1d_transpose", "oracle_circulant_1d_grad_w", "oracle_causal_1d"):
             getattr(lib, f).restype = None
         _lib = lib
     return _lib
@@ -201,6 +210,37 @@ def circulant_1d_grad_w(G, V, H: int) -> np.ndarray:
     return dw
 
 
+def causal_1d(z, V, rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """Causal CAT mixing from the logits z [B, H, N]:
+    O[b, i, c] = sum_{j<=i} softmax_{j<=i}(z[b, h(c), i - j]) V[b, j, c],
+    the row softmax of circ(z_h) with the tokens beyond i masked out.
+    Returns [B, N, D], or [len(rows), D] for flattened rows b * N + i."""
+    z = _f64(z)
+    V = _f64(V)
+    B, H, N = z.shape
+    assert V.shape[:2] == (B, N) and V.shape[2] % H == 0
+    D = V.shape[2]
+    r, rp, nr = _rows(rows)
+    O = np.empty(((nr,) if r is not None else (B, N)) + (D,), dtype=np.float64)
+    _load().oracle_causal_1d(_ptr(z), _ptr(V), _ptr(O), B, N, D, H, rp, nr)
+    return O
+
+
+def avgkey_scores_1d(X, W_Q, W_K, H: int) -> np.ndarray:
+    """Averaged-key logits [B, H, N]: with Q = X W_Q and K = X W_K, the key
+    of head h is averaged over the N tokens, kbar_h = (1/N) sum_n K_h[n], and
+    each token's query meets it as in scaled dot-product attention:
+    z_h[n] = Q_h[n] . kbar_h / sqrt(d)  (d = D / H channels per head)."""
+    X = _f64(X)
+    B, N, D = X.shape
+    d = D // H
+    Q = matmul(X, W_Q).reshape(B, N, H, d)
+    K = matmul(X, W_K).reshape(B, N, H, d)
+    kbar = K.mean(axis=1)                                  # [B, H, d]
+    z = (Q * kbar[:, None, :, :]).sum(axis=-1) / math.sqrt(d)  # [B, N, H]
+    return np.ascontiguousarray(np.transpose(z, (0, 2, 1)))
+
+
 def softmax_backward(zstar, g) -> np.ndarray:
     """dL/dz from g = dL/dz* through z* = softmax(z) over the last axis:
     z*_k (g_k - sum_m z*_m g_m)."""
@@ -253,6 +293,28 @@ def cat_forward_1d(X, W_A, W_V, rows: Optional[Sequence[int]] = None) -> Dict[st
     V = matmul(X, W_V)
     O = circulant_1d(zstar, V, rows=rows)
     return {"z": z, "zstar": zstar, "V": V, "O": O}
+
+
+def cat_avgkey_forward_1d(X, W_Q, W_K, W_V, H: int, rows: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
+    """Averaged-key variant of CAT (CAT: Circular-Convolutional Attention for
+    Sub-Quadratic Transformers, ablation table, row "qkv (Averaged-Key)":
+    3 D^2 parameters, O(N log N)): the logits of avgkey_scores_1d, softmaxed
+    over the N tokens, generate the circulant that mixes V = X W_V per head.
+    Returns z, zstar, V and O."""
+    z = avgkey_scores_1d(X, W_Q, W_K, H)
+    zstar = softmax(z)
+    V = matmul(X, W_V)
+    O = circulant_1d(zstar, V, rows=rows)
+    return {"z": z, "zstar": zstar, "V": V, "O": O}
+
+
+def cat_causal_forward_1d(X, W_A, W_V, rows: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
+    """Causal CAT: the CAT logits z = X W_A, then causal_1d (each row of
+    circ(z_h) masked to the tokens j <= i and softmaxed over them) applied
+    to V = X W_V.  Returns z, V and O."""
+    z = scores_1d(X, W_A)
+    V = matmul(X, W_V)
+    return {"z": z, "V": V, "O": causal_1d(z, V, rows=rows)}
 
 
 def cat_scored_forward_2d(X, W_A, W_V, Hg: int, Wg: int, rows: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:

@@ -609,3 +609,174 @@ def test_planted_backward_lag_sign_is_caught():
 
 def test_oracle_reports_threads():
     assert oracle.num_threads() >= 1
+
+
+# ---------------------------------------------------------------- averaged-key variant
+def test_avgkey_scores_golden_digits():
+    g = gold("avgkey_scores_n3_digits.json")
+    z = oracle.avgkey_scores_1d(np.array(g["X"])[None], np.array(g["W_Q"]), np.array(g["W_K"]), g["H"])
+    np.testing.assert_array_equal(z[0, 0], np.array(g["z"]))
+
+
+@pytest.mark.parametrize("H,alpha", [(1, 0.7), (3, -1.3), (4, 2.0)])
+def test_avgkey_reduces_to_cat_for_a_one_hot_mean_key(H, alpha):
+    """With a token-constant input channel (X[:, :, 0] = 1) and W_K whose only
+    nonzero entries are W_K[0][c_h] = alpha for one channel c_h of each head,
+    the averaged key of head h is alpha e_{c_h}, so z_h = alpha Q[:, c_h] /
+    sqrt(d) = X (alpha W_Q[:, c_h] / sqrt(d)): the CAT logits of the pinned
+    scores_1d with that W_A column, and the whole forward equals CAT's."""
+    rng = np.random.default_rng(60 + H)
+    B, N, d = 2, 9, 4
+    D = H * d
+    X = rng.standard_normal((B, N, D))
+    X[:, :, 0] = 1.0
+    WQ, WV = rng.standard_normal((D, D)), rng.standard_normal((D, D))
+    WK = np.zeros((D, D))
+    cs = [h * d + (h + 1) % d for h in range(H)]
+    for c in cs:
+        WK[0, c] = alpha
+    WA = np.stack([alpha * WQ[:, c] / np.sqrt(d) for c in cs], axis=1)
+    got = oracle.cat_avgkey_forward_1d(X, WQ, WK, WV, H)
+    ref = oracle.cat_forward_1d(X, WA, WV)
+    assert np.allclose(got["z"], ref["z"], rtol=1e-12, atol=1e-12)
+    assert np.allclose(got["O"], ref["O"], rtol=1e-12, atol=1e-12)
+
+
+def test_avgkey_matches_reassociated_library_route():
+    """z = X (W_Q,h kbar_h) / sqrt(d) with kbar = mean(X) W_K by BLAS (the
+    same sums in another association), then scipy's circulant matrix."""
+    rng = np.random.default_rng(77)
+    B, N, D, H = 2, 11, 12, 3
+    d = D // H
+    X = rng.standard_normal((B, N, D))
+    WQ, WK, WV = (rng.standard_normal((D, D)) for _ in range(3))
+    got = oracle.cat_avgkey_forward_1d(X, WQ, WK, WV, H)
+    for b in range(B):
+        kbar = X[b].mean(axis=0) @ WK
+        V = X[b] @ WV
+        for h in range(H):
+            sl = slice(h * d, (h + 1) * d)
+            z = X[b] @ (WQ[:, sl] @ kbar[sl]) / np.sqrt(d)
+            assert np.allclose(got["z"][b, h], z, rtol=1e-12, atol=1e-12)
+            C = scipy.linalg.circulant(scipy.special.softmax(z))
+            assert np.allclose(got["O"][b][:, sl], C @ V[:, sl], rtol=1e-11, atol=1e-12)
+
+
+def test_avgkey_invariants():
+    """Token-constant X gives equal logits, a uniform circulant and O = V;
+    rolling X along the tokens leaves the mean key unchanged, so the output
+    rolls twice as far, as in CAT."""
+    rng = np.random.default_rng(8)
+    B, N, D, H = 1, 10, 8, 2
+    WQ, WK, WV = (rng.standard_normal((D, D)) for _ in range(3))
+    Xc = np.broadcast_to(rng.standard_normal((B, 1, D)), (B, N, D)).copy()
+    r = oracle.cat_avgkey_forward_1d(Xc, WQ, WK, WV, H)
+    assert np.allclose(r["zstar"], 1.0 / N, atol=1e-15)
+    assert np.allclose(r["O"], r["V"], rtol=1e-12, atol=1e-12)
+    X = rng.standard_normal((B, N, D))
+    O = oracle.cat_avgkey_forward_1d(X, WQ, WK, WV, H)["O"]
+    Or = oracle.cat_avgkey_forward_1d(np.roll(X, 3, axis=1), WQ, WK, WV, H)["O"]
+    assert np.allclose(Or, np.roll(O, 6, axis=1), atol=1e-12)
+
+
+def test_planted_avgkey_mistakes_are_caught():
+    """A sum instead of a mean, a missing 1/sqrt(d), Q and K swapped, or the
+    mean taken over channels instead of tokens each miss the golden digits."""
+    g = gold("avgkey_scores_n3_digits.json")
+    X, WQ, WK = np.array(g["X"])[None], np.array(g["W_Q"]), np.array(g["W_K"])
+    want = np.array(g["z"])
+    d = X.shape[2]
+    Q, K = X[0] @ WQ, X[0] @ WK
+    mutants = {
+        "sum": Q @ K.sum(axis=0) / np.sqrt(d),
+        "no scale": Q @ K.mean(axis=0),
+        "swapped": K @ Q.mean(axis=0) / np.sqrt(d),
+        "channel mean": (Q * K.mean(axis=1, keepdims=True)).sum(axis=1) / np.sqrt(d),
+    }
+    for name, z in mutants.items():
+        assert not np.allclose(z, want), name
+
+
+# ---------------------------------------------------------------- causal CAT
+def test_causal_golden_digits():
+    g = gold("causal_1d_n3_digits.json")
+    O = oracle.causal_1d(np.array(g["z"])[None, None, :], np.array(g["V"])[None])[0]
+    np.testing.assert_allclose(O, np.array(g["O"]), rtol=1e-15)
+    np.testing.assert_allclose(np.array(g["numerators"]) / np.array(g["denominators"]), np.array(g["O"])[:, 0])
+
+
+@pytest.mark.parametrize("N,H,d", [(1, 1, 2), (2, 2, 1), (7, 1, 3), (16, 3, 2), (31, 2, 4)])
+def test_causal_matches_masked_dense_attention(N, H, d):
+    """Against the materialised score matrix S[i][j] = z[(i - j) mod N] (via
+    scipy's circulant), the entries j > i set to -inf, scipy's row softmax,
+    and a BLAS product."""
+    rng = np.random.default_rng(200 + N)
+    B, D = 2, H * d
+    z = rng.standard_normal((B, H, N)) * 2
+    V = rng.standard_normal((B, N, D))
+    O = oracle.causal_1d(z, V)
+    for b in range(B):
+        for h in range(H):
+            S = scipy.linalg.circulant(z[b, h]).copy()
+            S[np.triu_indices(N, 1)] = -np.inf
+            P = scipy.special.softmax(S, axis=1)
+            sl = slice(h * d, (h + 1) * d)
+            assert np.allclose(O[b][:, sl], P @ V[b][:, sl], rtol=1e-12, atol=1e-12)
+
+
+def test_causal_special_rows_and_invariants():
+    """Row 0 is V[0]; the last row keeps every token and every lag, so it is
+    the last row of the (pinned) non-causal circulant; weights sum to one
+    (token-constant V is returned); row i depends only on tokens <= i (the
+    causal output of a prefix is the prefix of the causal output); a huge
+    common shift of the logits changes nothing (max subtraction)."""
+    rng = np.random.default_rng(9)
+    B, N, H, d = 2, 13, 2, 3
+    D = H * d
+    z = rng.standard_normal((B, H, N)) * 3
+    V = rng.standard_normal((B, N, D))
+    O = oracle.causal_1d(z, V)
+    assert np.allclose(O[:, 0], V[:, 0], rtol=1e-14, atol=1e-15)
+    full = oracle.circulant_1d(oracle.softmax(z), V)
+    assert np.allclose(O[:, N - 1], full[:, N - 1], rtol=1e-12, atol=1e-13)
+    Vc = np.broadcast_to(rng.standard_normal((B, 1, D)), (B, N, D)).copy()
+    assert np.allclose(oracle.causal_1d(z, Vc), Vc, rtol=1e-13, atol=1e-14)
+    M = 6
+    assert np.allclose(oracle.causal_1d(z[..., :M], V[:, :M]), O[:, :M], rtol=1e-13, atol=1e-14)
+    # (adding 4000 rounds each logit by up to 2^-41, about 5e-13)
+    assert np.allclose(oracle.causal_1d(z + 4000.0, V), O, rtol=1e-10, atol=1e-11)
+    rows = [0, 5, N + 3, 2 * N - 1]
+    assert np.allclose(oracle.causal_1d(z, V, rows=rows), O.reshape(B * N, D)[rows], rtol=1e-15, atol=0)
+
+
+def test_planted_causal_mistakes_are_caught():
+    """An anti-causal mask (j >= i), a strict mask (j < i, row 0 undefined,
+    so the diagonal is dropped on the others), and masking after a global
+    softmax without renormalising each miss the golden digits."""
+    g = gold("causal_1d_n3_digits.json")
+    z, V, want = np.array(g["z"]), np.array(g["V"])[:, 0], np.array(g["O"])[:, 0]
+    N = len(z)
+    S = scipy.linalg.circulant(z)
+
+    def masked(keep, renorm=True):
+        P = np.where(keep, np.exp(S), 0.0)
+        if renorm:
+            P = P / np.maximum(P.sum(axis=1, keepdims=True), 1e-300)
+        else:
+            P = P / np.exp(z).sum()
+        return P @ V
+
+    i, j = np.indices((N, N))
+    assert not np.allclose(masked(j >= i), want)
+    assert not np.allclose(masked((j < i) | (i == 0)), want)
+    assert not np.allclose(masked(j <= i, renorm=False), want)
+    assert np.allclose(masked(j <= i), want)
+
+
+@pytest.mark.parametrize("B,N,D,H", [(1, 5, 4, 2), (2, 12, 6, 3)])
+def test_cat_causal_forward_composes_pinned_steps(B, N, D, H):
+    rng = np.random.default_rng(N)
+    X = rng.standard_normal((B, N, D))
+    WA, WV = rng.standard_normal((D, H)), rng.standard_normal((D, D))
+    r = oracle.cat_causal_forward_1d(X, WA, WV)
+    assert np.allclose(r["O"], oracle.causal_1d(np.transpose(X @ WA, (0, 2, 1)), X @ WV), rtol=1e-12, atol=1e-12)

@@ -30,8 +30,10 @@ EXPORTS = ["cat_plan_create", "cat_plan_destroy", "cat_plan_workspace_size", "ca
            "cat_forward_1d", "cat_forward_bccb_2d", "cat_forward_cat_2d", "cat_status_string", "cat_last_error",
            "cat_plan_set_timing", "cat_plan_kernel_times", "cat_plan_conv_path",
            "cat_step_project", "cat_step_spectrum", "cat_step_mix", "cat_step_mix_backward_1d",
-           "cat_backward_1d", "cat_step_scores_2d"]
-KERNELS_1D = ["project", "spectrum", "fftconv", "reverse", "relayout", "score_grad", "psum", "logits_grad"]
+           "cat_backward_1d", "cat_step_scores_2d", "cat_forward_avgkey_1d", "cat_step_avgkey_logits",
+           "cat_forward_causal_1d", "cat_step_mix_causal_1d"]
+KERNELS_1D = ["project", "spectrum", "fftconv", "reverse", "relayout", "score_grad", "psum", "logits_grad",
+              "avgkey_logits"]
 KERNELS_2D = ["project", "scores", "spectrum", "fftconv", "psum"]
 
 
@@ -69,6 +71,10 @@ def _load() -> ctypes.CDLL:
     lib.cat_step_mix_backward_1d.argtypes = [vp] * 8
     lib.cat_backward_1d.argtypes = [vp] * 10
     lib.cat_step_scores_2d.argtypes = [vp] * 6
+    lib.cat_forward_avgkey_1d.argtypes = [vp] * 8
+    lib.cat_step_avgkey_logits.argtypes = [vp] * 7
+    lib.cat_forward_causal_1d.argtypes = [vp] * 7
+    lib.cat_step_mix_causal_1d.argtypes = [vp] * 6
     for f in EXPORTS:
         fn = getattr(lib, f)
         if f in ("cat_status_string", "cat_last_error"):
@@ -169,8 +175,8 @@ def cat_plan_set_timing(plan: Plan, enable: bool = True):
 def cat_plan_kernel_times(plan: Plan):
     """{kernel name: (average ms per launch, launches)} over the calls recorded
     since timing was enabled."""
-    tot = (ctypes.c_double * 8)()
-    cnt = (ctypes.c_int64 * 8)()
+    tot = (ctypes.c_double * 16)()
+    cnt = (ctypes.c_int64 * 16)()
     nk = ctypes.c_int()
     _check(_lib.cat_plan_kernel_times(ctypes.c_void_p(plan.handle), tot, cnt, ctypes.byref(nk)),
            "cat_plan_kernel_times")
@@ -318,6 +324,61 @@ def cat_backward_1d(plan: Plan, X, W_A, W_V, dO, workspace=None, stream=None):
                                 _ptr(W_V, (D, D), dt, "W_V"), _ptr(dO, (B, N, D), dt, "dO"), _ptr(dX), _ptr(dW_A),
                                 _ptr(dW_V), _ptr(workspace), _stream_ptr(stream)), "cat_backward_1d")
     return dX, dW_A, dW_V
+
+
+def cat_forward_avgkey_1d(plan: Plan, X, W_Q, W_K, W_V, O=None, workspace=None, stream=None) -> torch.Tensor:
+    """O = the averaged-key variant of CAT per include/cat.h (weights [D, D])."""
+    B, N, D, dt = plan.B, plan.N, plan.D, plan.dtype
+    if O is None:
+        O = torch.empty((B, N, D), dtype=dt, device=X.device)
+    if workspace is None:
+        workspace = alloc_workspace(plan, X.device)
+    _check(_lib.cat_forward_avgkey_1d(ctypes.c_void_p(plan.handle), _ptr(X, (B, N, D), dt, "X"),
+                                      _ptr(W_Q, (D, D), dt, "W_Q"), _ptr(W_K, (D, D), dt, "W_K"),
+                                      _ptr(W_V, (D, D), dt, "W_V"), _ptr(O, (B, N, D), dt, "O"),
+                                      _ptr(workspace, None, None, "workspace"), _stream_ptr(stream)),
+           "cat_forward_avgkey_1d")
+    return O
+
+
+def cat_step_avgkey_logits(plan: Plan, X, W_Q, W_K, workspace=None, stream=None) -> torch.Tensor:
+    """z [B, H, N] fp32: the averaged-key logits."""
+    B, N, D, H, dt = plan.B, plan.N, plan.D, plan.H, plan.dtype
+    if workspace is None:
+        workspace = alloc_workspace(plan, X.device)
+    z = torch.empty((B, H, N), dtype=torch.float32, device=X.device)
+    _check(_lib.cat_step_avgkey_logits(ctypes.c_void_p(plan.handle), _ptr(X, (B, N, D), dt, "X"),
+                                       _ptr(W_Q, (D, D), dt, "W_Q"), _ptr(W_K, (D, D), dt, "W_K"), _ptr(z),
+                                       _ptr(workspace, None, None, "workspace"), _stream_ptr(stream)),
+           "cat_step_avgkey_logits")
+    return z
+
+
+def cat_forward_causal_1d(plan: Plan, X, W_A, W_V, O=None, workspace=None, stream=None) -> torch.Tensor:
+    """O = causal CAT per include/cat.h (W_A [D, H], W_V [D, D])."""
+    B, N, D, H, dt = plan.B, plan.N, plan.D, plan.H, plan.dtype
+    if O is None:
+        O = torch.empty((B, N, D), dtype=dt, device=X.device)
+    if workspace is None:
+        workspace = alloc_workspace(plan, X.device)
+    _check(_lib.cat_forward_causal_1d(ctypes.c_void_p(plan.handle), _ptr(X, (B, N, D), dt, "X"),
+                                      _ptr(W_A, (D, H), dt, "W_A"), _ptr(W_V, (D, D), dt, "W_V"),
+                                      _ptr(O, (B, N, D), dt, "O"), _ptr(workspace, None, None, "workspace"),
+                                      _stream_ptr(stream)), "cat_forward_causal_1d")
+    return O
+
+
+def cat_step_mix_causal_1d(plan: Plan, logits, V, O=None, workspace=None, stream=None) -> torch.Tensor:
+    B, N, D, H, dt = plan.B, plan.N, plan.D, plan.H, plan.dtype
+    if O is None:
+        O = torch.empty((B, N, D), dtype=dt, device=V.device)
+    if workspace is None:
+        workspace = alloc_workspace(plan, V.device)
+    _check(_lib.cat_step_mix_causal_1d(ctypes.c_void_p(plan.handle),
+                                       _ptr(logits, (B, H, N), torch.float32, "logits"), _ptr(V, (B, N, D), dt, "V"),
+                                       _ptr(O, (B, N, D), dt, "O"), _ptr(workspace), _stream_ptr(stream)),
+           "cat_step_mix_causal_1d")
+    return O
 
 
 def cat_step_scores_2d(plan: Plan, Q, K, workspace=None, stream=None) -> torch.Tensor:

@@ -40,6 +40,7 @@ struct cat_plan_s {
   hipStream_t side = nullptr;
   hipEvent_t fork_ev = nullptr, join_ev = nullptr;
   size_t off_A, off_zc, off_Az;  // long path scratch
+  size_t off_xpart, off_kbar, off_weff;  // averaged-key logits scratch (1D)
   bool debug_sync;
   int tile_n;        // forced GEMM tile width (0: the GEMM chooses)
   int num_cu;        // compute units of the device current at plan creation
@@ -290,6 +291,13 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
       pl->off_Az = off;
       off = up256(off + BH * pl->L * sizeof(float2));
     }
+    // the averaged-key logits: column-sum partials, mean key, score weights
+    pl->off_xpart = off;
+    off = up256(off + avgkey_part_floats((int)p->B, (int)p->N, (int)p->D) * sizeof(float));
+    pl->off_kbar = off;
+    off = up256(off + (size_t)p->B * p->D * sizeof(float));
+    pl->off_weff = off;
+    off = up256(off + (size_t)p->B * p->D * p->H * sizeof(float));
   } else {
     pl->off_z = off;  // the CAT-scored variant's logits
     off = up256(off + BH * p->N * sizeof(float));
@@ -402,9 +410,9 @@ cat_status cat_plan_set_timing(cat_plan plan, int enable) {
 
 cat_status cat_plan_kernel_times(cat_plan plan, double* total_ms, int64_t* launches, int* nkernels) {
   if (!plan || !total_ms || !launches || !nkernels) return fail(CAT_ERR_INVALID_ARG, "NULL argument");
-  const int nk = plan->p.kind == CAT_1D ? 8 : 5;
+  const int nk = plan->p.kind == CAT_1D ? 9 : 5;
   *nkernels = nk;
-  for (int k = 0; k < 8; ++k) {
+  for (int k = 0; k < 16; ++k) {
     total_ms[k] = 0.0;
     launches[k] = 0;
   }
@@ -700,6 +708,79 @@ cat_status join_side(cat_plan plan, hipStream_t s) {
   return CAT_OK;
 }
 
+// The 1D mixing from logits z [B][H][N] and V already in the blocked
+// layout of the plan's path (plan->cg channels per group): the plan's path
+// (matrix-core FFT, direct product, vector FFT or the three passes).
+cat_status mix_from_blocked(cat_plan plan, const float* z, const void* Vb, void* O, void* workspace, hipStream_t s,
+                            KernelMark* mk) {
+  hipError_t e;
+  cat_status st;
+  if (plan->longn) {
+    e = run_long_1d(plan, z, Vb, O, workspace, s, mk);
+    if (e != hipSuccess) return hip_fail(e, "long-sequence fft-conv launch");
+    return check_sync(plan, "long-sequence fft-conv");
+  }
+  SpecArgs sa = spec_base(plan, workspace);
+  sa.logits = z;
+  const bool own_softmax = plan->mconv || plan->direct;  // (these take the logits themselves)
+  if (!own_softmax) {
+    e = launch_spectrum(plan->geom, 0, sa, s, mk_at(mk, 1));
+    if (e != hipSuccess) return hip_fail(e, "spectrum launch");
+    if ((st = check_sync(plan, "spectrum")) != CAT_OK) return st;
+  }
+  ConvArgs ca = conv_base(plan, Vb, sa.spec, O);
+  if (own_softmax) ca.logits = z;
+  e = run_conv_1d(plan, ca, s, mk_at(mk, 2));
+  if (e != hipSuccess) return hip_fail(e, "fft-conv launch");
+  return check_sync(plan, "fft-conv");
+}
+
+cat_status avgkey_supported(const cat_plan_s* pl) {
+  if (pl->p.D > 3072)
+    return fail(CAT_ERR_UNSUPPORTED, "the averaged-key logits support D <= 3072");
+  if (pl->p.B > 65535) return fail(CAT_ERR_UNSUPPORTED, "the averaged-key logits support B <= 65535");
+  return CAT_OK;
+}
+
+// Averaged-key logits into z (timing slots: kind 8).
+cat_status avgkey_logits(cat_plan plan, const void* X, const void* W_Q, const void* W_K, float* z, void* workspace,
+                         hipStream_t s, KernelMark* mk) {
+  AvgKeyArgs a{};
+  a.X = X;
+  a.W_Q = W_Q;
+  a.W_K = W_K;
+  a.part = reinterpret_cast<float*>(ws_at(workspace, plan->off_xpart));
+  a.kbar = reinterpret_cast<float*>(ws_at(workspace, plan->off_kbar));
+  a.weff = reinterpret_cast<float*>(ws_at(workspace, plan->off_weff));
+  a.z = z;
+  a.B = (int)plan->p.B;
+  a.N = (int)plan->p.N;
+  a.D = (int)plan->p.D;
+  a.H = (int)plan->p.H;
+  a.scale = 1.0f / std::sqrt((float)plan->d);
+  const LaunchTiming* ts[4] = {mk_at(mk, 8), mk_at(mk, 8), mk_at(mk, 8), mk_at(mk, 8)};
+  hipError_t e = launch_avgkey(plan->et, a, s, ts);
+  if (e != hipSuccess) return hip_fail(e, "averaged-key logits launch");
+  return check_sync(plan, "averaged-key logits");
+}
+
+// Causal CAT runs on the direct product: bf16, N <= 256, 32-channel groups.
+constexpr int kCausalCg = 32;
+cat_status causal_supported(const cat_plan_s* pl) {
+  if (pl->et != ET_BF16 || pl->p.N > 256 || pl->d % kCausalCg != 0)
+    return fail(CAT_ERR_UNSUPPORTED, "causal CAT supports bf16 storage, N <= 256 and d a multiple of 32");
+  return CAT_OK;
+}
+
+cat_status causal_mix(cat_plan plan, const float* z, const void* Vb, void* O, hipStream_t s, const LaunchTiming* t) {
+  ConvArgs ca = conv_base(plan, Vb, nullptr, O);
+  ca.logits = z;
+  ca.ng = plan->d / kCausalCg;
+  hipError_t e = launch_dconv(plan->et, ca, s, t, true);
+  if (e != hipSuccess) return hip_fail(e, "causal mixing launch");
+  return check_sync(plan, "causal mixing");
+}
+
 }  // namespace
 
 extern "C" {
@@ -727,26 +808,92 @@ cat_status cat_forward_1d(cat_plan plan, const void* X, const void* W_A, const v
   if (e != hipSuccess) return hip_fail(e, "projection launch");
   if ((st = check_sync(plan, "projection")) != CAT_OK) return st;
 
-  if (plan->longn) {
-    e = run_long_1d(plan, z, Vb, O, workspace, s, &mk);
-    if (e != hipSuccess) return hip_fail(e, "long-sequence fft-conv launch");
-    return check_sync(plan, "long-sequence fft-conv");
-  }
+  return mix_from_blocked(plan, z, Vb, O, workspace, s, &mk);
+}
 
-  SpecArgs sa = spec_base(plan, workspace);
-  sa.logits = z;
-  const bool own_softmax = plan->mconv || plan->direct;  // (these take the logits themselves)
-  if (!own_softmax) {
-    e = launch_spectrum(plan->geom, 0, sa, s, mk.at(1));
-    if (e != hipSuccess) return hip_fail(e, "spectrum launch");
-    if ((st = check_sync(plan, "spectrum")) != CAT_OK) return st;
-  }
+cat_status cat_forward_avgkey_1d(cat_plan plan, const void* X, const void* W_Q, const void* W_K, const void* W_V,
+                                 void* O, void* workspace, void* stream) {
+  if (!plan) return fail(CAT_ERR_INVALID_ARG, "NULL plan");
+  if (plan->p.kind != CAT_1D) return fail(CAT_ERR_PLAN_MISMATCH, "plan is not 1D");
+  if (plan->p.B == 0) return CAT_OK;
+  cat_status st = check_ptrs({X, W_Q, W_K, W_V, O, workspace});
+  if (st != CAT_OK) return st;
+  if ((st = avgkey_supported(plan)) != CAT_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  void* Vb = ws_at(workspace, plan->off_V);
+  float* z = reinterpret_cast<float*>(ws_at(workspace, plan->off_z));
+  KernelMark mk(plan);
 
-  ConvArgs ca = conv_base(plan, Vb, sa.spec, O);
-  if (own_softmax) ca.logits = z;
-  e = run_conv_1d(plan, ca, s, mk.at(2));
-  if (e != hipSuccess) return hip_fail(e, "fft-conv launch");
-  return check_sync(plan, "fft-conv");
+  // V = X W_V (blocked for the mixing), then the averaged-key logits
+  GemmArgs ga = gemm_base(plan, X);
+  ga.nseg = 1;
+  ga.seg[0] = seg(W_V, Vb, (int)plan->p.D, 0, OUT_BLOCKED, plan->cg);
+  hipError_t e = launch_gemm(plan->et, ga, s, mk.at(0));
+  if (e != hipSuccess) return hip_fail(e, "projection launch");
+  if ((st = check_sync(plan, "projection")) != CAT_OK) return st;
+  if ((st = avgkey_logits(plan, X, W_Q, W_K, z, workspace, s, &mk)) != CAT_OK) return st;
+  return mix_from_blocked(plan, z, Vb, O, workspace, s, &mk);
+}
+
+cat_status cat_step_avgkey_logits(cat_plan plan, const void* X, const void* W_Q, const void* W_K, float* z,
+                                  void* workspace, void* stream) {
+  if (!plan) return fail(CAT_ERR_INVALID_ARG, "NULL plan");
+  if (plan->p.kind != CAT_1D) return fail(CAT_ERR_PLAN_MISMATCH, "plan is not 1D");
+  if (plan->p.B == 0) return CAT_OK;
+  cat_status st = check_ptrs({X, W_Q, W_K, z, workspace});
+  if (st != CAT_OK) return st;
+  if ((st = avgkey_supported(plan)) != CAT_OK) return st;
+  return avgkey_logits(plan, X, W_Q, W_K, z, workspace, reinterpret_cast<hipStream_t>(stream), nullptr);
+}
+
+cat_status cat_forward_causal_1d(cat_plan plan, const void* X, const void* W_A, const void* W_V, void* O,
+                                 void* workspace, void* stream) {
+  if (!plan) return fail(CAT_ERR_INVALID_ARG, "NULL plan");
+  if (plan->p.kind != CAT_1D) return fail(CAT_ERR_PLAN_MISMATCH, "plan is not 1D");
+  if (plan->p.B == 0) return CAT_OK;
+  cat_status st = check_ptrs({X, W_A, W_V, O, workspace});
+  if (st != CAT_OK) return st;
+  if ((st = causal_supported(plan)) != CAT_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  void* Vb = ws_at(workspace, plan->off_V);
+  float* z = reinterpret_cast<float*>(ws_at(workspace, plan->off_z));
+  KernelMark mk(plan);
+  GemmArgs ga = gemm_base(plan, X);
+  ga.nseg = 1;
+  ga.seg[0] = seg(W_V, Vb, (int)plan->p.D, 0, OUT_BLOCKED, kCausalCg);
+  ga.Wz = W_A;
+  ga.z = z;
+  ga.nz = (int)plan->p.H;
+  hipError_t e = launch_gemm(plan->et, ga, s, mk.at(0));
+  if (e != hipSuccess) return hip_fail(e, "projection launch");
+  if ((st = check_sync(plan, "projection")) != CAT_OK) return st;
+  return causal_mix(plan, z, Vb, O, s, mk.at(2));
+}
+
+cat_status cat_step_mix_causal_1d(cat_plan plan, const float* logits, const void* V, void* O, void* workspace,
+                                  void* stream) {
+  if (!plan) return fail(CAT_ERR_INVALID_ARG, "NULL plan");
+  if (plan->p.kind != CAT_1D) return fail(CAT_ERR_PLAN_MISMATCH, "plan is not 1D");
+  if (plan->p.B == 0) return CAT_OK;
+  cat_status st = check_ptrs({logits, V, O, workspace});
+  if (st != CAT_OK) return st;
+  if ((st = causal_supported(plan)) != CAT_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  void* Vb = ws_at(workspace, plan->off_V);
+  RelayoutArgs ra{};
+  ra.src = V;
+  ra.dst = Vb;
+  ra.src_et = plan->et;
+  ra.dst_f32 = 0;
+  ra.B = (int)plan->p.B;
+  ra.N = (int)plan->p.N;
+  ra.D = (int)plan->p.D;
+  ra.H = (int)plan->p.H;
+  ra.d = plan->d;
+  ra.cg = kCausalCg;
+  hipError_t e = launch_relayout(ra, s);
+  if (e != hipSuccess) return hip_fail(e, "relayout launch");
+  return causal_mix(plan, logits, Vb, O, s, nullptr);
 }
 
 cat_status cat_forward_cat_2d(cat_plan plan, const void* X, const void* W_A, const void* W_V, void* O,

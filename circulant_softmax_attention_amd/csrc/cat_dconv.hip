@@ -22,9 +22,10 @@
 //    over the workgroup).
 //  - C is never materialised.  Its entries are the reversed, periodically
 //    extended softmax line R[t] = z*[(N - t) mod N] (C[i][j] = R[j - i + N]),
-//    here without the division by the sum (exp(z - max), in (0, 1]; the
-//    fp32 products are divided by the sum at the end),
-//    held in LDS as bf16 (RNE) in 8 copies shifted by 0 .. 7 entries, so
+//    here without the division by the sum (exp(z - max), in (0, 1], rounded
+//    to bf16 (RNE); the fp32 products are divided at the end by the sum of
+//    these rounded weights, so each row's weights add up to one),
+//    held in LDS in 8 copies shifted by 0 .. 7 entries, so
 //    that the run of 8 consecutive j values one lane feeds an MFMA is one
 //    aligned 16-byte read from the copy that matches its offset.
 //  - V's block [N][32] (the blocked layout with 32-channel groups) is staged
@@ -37,6 +38,21 @@
 //    blocks tb = w, w + 4, .. and both 16-channel blocks.
 //  - The tile goes through LDS (over the V tile) and leaves as 16-byte
 //    stores of the rows' 32-channel segments.
+//
+// Causal CAT (CAUSAL = true).  The same page notes that a causal language
+// model has to shift Z to stay causal, which costs O(N^2) ("Loss function /
+// training strategy", "Limitations and outlook"): row i of circ(z) keeps
+// only the tokens j <= i and is softmaxed over them,
+//
+//   O[i][c] = sum_{j <= i} exp(z[i - j]) V[j][c] / sum_{k <= i} exp(z[k]),
+//
+// exactly the O(N^2) direct product this kernel already forms.  R loses its
+// periodic extension (R[t] = e[N - t] for 1 <= t <= N, zero beyond, so the
+// entries j > i of each row vanish) and each row is divided by its own
+// prefix sum P[i] = sum_{k <= i} e[k] (an inclusive scan in LDS) instead of
+// the line's total.  e = exp(z - max over the whole line), as above; a row
+// whose kept logits all lie more than about 87 below that maximum would
+// underflow to 0 / 0.
 #include "cat_common.hpp"
 #include "cat_internal.hpp"
 
@@ -79,12 +95,31 @@ __device__ __forceinline__ float block_reduce(float x, float* red) {
   return r;
 }
 
+// Inclusive prefix sum of one value per thread over the workgroup.
+__device__ __forceinline__ float block_scan(float x, float* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float y = __shfl_up(x, o, 64);
+    x += lane >= o ? y : 0.f;
+  }
+  __syncthreads();  // earlier readers of red are done
+  if (lane == 63) red[wave] = x;
+  __syncthreads();
+  float off = 0.f;
+#pragma unroll
+  for (int w = 0; w < DTHR / 64 - 1; ++w) off += w < wave ? red[w] : 0.f;
+  return x + off;
+}
+
+template <bool CAUSAL>
 __global__ __launch_bounds__(DTHR) void dconv_kernel(ConvArgs a) {
   using elem_t = uint16_t;  // bf16 bits
   __shared__ __attribute__((aligned(16))) char tile[TILE_BYTES];  // Vt, then the O tile
   __shared__ __attribute__((aligned(16))) elem_t rc[VE][RPP];       // shifted copies of R
   __shared__ float zs[DNMAX];
   __shared__ float red[DTHR / 64];
+  __shared__ float psum[CAUSAL ? DNMAX : 1];  // causal: row normalisers P[i]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -132,29 +167,45 @@ __global__ __launch_bounds__(DTHR) void dconv_kernel(ConvArgs a) {
   float ev;
   {
     const float mz = block_reduce<false>(zv, red);
-    ev = tid < N ? __expf(zv - mz) : 0.f;
+    // rounded to bf16 here, as the products will see it, so that the
+    // normalisers below sum exactly the weights the products use (each row's
+    // weights then add up to one up to fp32 rounding)
+    ev = tid < N ? __uint_as_float((uint32_t)to_bf16(__expf(zv - mz)) << 16) : 0.f;
     if (tid < N) zs[tid] = ev;
   }
   __syncthreads();
+  if (CAUSAL) {
+    const float p = block_scan(ev, red);
+    if (tid < N) psum[tid] = p;
+  }
   // ---- shifted copies of R: rc[s][p] = R[p + s - RB] = z*[(N - (p + s - RB)) mod N],
   // VE entries (one 16-byte run) per item: one modulo, then the index steps
-  // down by one per entry, wrapping at 0.
+  // down by one per entry, wrapping at 0.  Causal: R[t] = e[N - t] for
+  // 1 <= t <= N and zero elsewhere (no wrap).
   for (int e = tid; e < VE * (RP / VE); e += DTHR) {
     const int s = e / (RP / VE), p0 = (e - s * (RP / VE)) * VE;
-    int idx = (N - (p0 + s - RB)) % N;
-    idx += idx < 0 ? N : 0;
     float v[VE];
+    if (CAUSAL) {
 #pragma unroll
-    for (int u = 0; u < VE; ++u) {
-      v[u] = zs[idx];
-      idx = idx == 0 ? N - 1 : idx - 1;
+      for (int u = 0; u < VE; ++u) {
+        const int t = p0 + u + s - RB;
+        v[u] = t >= 1 && t <= N ? zs[N - t] : 0.f;
+      }
+    } else {
+      int idx = (N - (p0 + s - RB)) % N;
+      idx += idx < 0 ? N : 0;
+#pragma unroll
+      for (int u = 0; u < VE; ++u) {
+        v[u] = zs[idx];
+        idx = idx == 0 ? N - 1 : idx - 1;
+      }
     }
     *reinterpret_cast<uint4*>(&rc[s][p0]) = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
                                                        pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
   }
   __syncthreads();
 
-  const float inv_sum = 1.f / block_reduce<true>(ev, red);
+  const float inv_sum = CAUSAL ? 1.f : 1.f / block_reduce<true>(ev, red);
 
   // ---- O^T = V^T C^T on MFMA
   constexpr int TBW = DNMAX / 16 / (DTHR / 64);  // token blocks per wave at most
@@ -204,10 +255,11 @@ __global__ __launch_bounds__(DTHR) void dconv_kernel(ConvArgs a) {
     const int tb = wave + 4 * t;
     if (tb < ntb) {
       const int i = 16 * tb + lrow;
+      const float inv = CAUSAL ? (i < N ? 1.f / psum[i] : 0.f) : inv_sum;
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
         char* dst = tile + i * OP + (16 * cb + 4 * lgrp) * ESZ;
-        const floatx4 r = acc[t][cb] * inv_sum;
+        const floatx4 r = acc[t][cb] * inv;
         *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]));
       }
     }
@@ -227,13 +279,14 @@ __global__ __launch_bounds__(DTHR) void dconv_kernel(ConvArgs a) {
 
 }  // namespace
 
-hipError_t launch_dconv(int et, const ConvArgs& a, hipStream_t s, const LaunchTiming* t) {
+hipError_t launch_dconv(int et, const ConvArgs& a, hipStream_t s, const LaunchTiming* t, bool causal) {
   if (a.N > DNMAX || a.N < 1 || a.d % DCG != 0 || a.ng != a.d / DCG || a.logits == nullptr)
     return hipErrorInvalidValue;
   const long blocks = (long)a.B * a.H * a.ng;
   if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
   if (et != ET_BF16) return hipErrorInvalidValue;  // fp32 storage keeps the FFT path
-  return launch_k(dconv_kernel, dim3((unsigned)blocks), dim3(DTHR), 0, s, t, a);
+  if (causal) return launch_k(dconv_kernel<true>, dim3((unsigned)blocks), dim3(DTHR), 0, s, t, a);
+  return launch_k(dconv_kernel<false>, dim3((unsigned)blocks), dim3(DTHR), 0, s, t, a);
 }
 
 }  // namespace cat

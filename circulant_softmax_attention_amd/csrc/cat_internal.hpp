@@ -174,8 +174,10 @@ hipError_t launch_mconv(const ConvArgs& a, hipStream_t s, const LaunchTiming* t 
 // 1D circulant mixing for N <= 256 as the direct product circ(z*) V on the
 // matrix cores, softmax of a.logits [BH][N] included: bf16 storage only
 // (et == ET_BF16), V BLOCKED with 32-channel groups (a.ng = d / 32),
-// d % 32 == 0; a.spec and a.tw unused.
-hipError_t launch_dconv(int et, const ConvArgs& a, hipStream_t s, const LaunchTiming* t = nullptr);
+// d % 32 == 0; a.spec and a.tw unused.  causal: each row i keeps only the
+// tokens j <= i and is normalised over them (causal CAT).
+hipError_t launch_dconv(int et, const ConvArgs& a, hipStream_t s, const LaunchTiming* t = nullptr,
+                        bool causal = false);
 hipError_t launch_score_partial(const LineGeom& g, const ScoreArgs& a, hipStream_t s,
                                 const LaunchTiming* t = nullptr);
 // Projection-gradient helpers of the CAT backward (cat_backward.hip), storage
@@ -218,6 +220,27 @@ hipError_t launch_longconv(int et, const LongArgs& a, const float* logits, const
 hipError_t launch_psum(const float2* part, float2* out, int BH, int ngrp, int L, hipStream_t s,
                        const LaunchTiming* t = nullptr);
 hipError_t launch_relayout(const RelayoutArgs& a, hipStream_t s, const LaunchTiming* t = nullptr);
+// Logits of the averaged-key variant (cat_variants.hip):
+//   z[b][h][n] = X[b][n] . (W_Q[:, head h] kbar[b]_h) * scale,
+//   kbar[b] = (token mean of X[b]) W_K.
+// X [B][N][D], W_Q, W_K [D][D] in the storage dtype; part: at least
+// avgkey_part_floats(B, N, D) floats of scratch; kbar [B][D], weff [B][D][H]
+// and z [B][H][N] fp32.  D % 8 == 0, D <= 3072, H <= 32, B <= 65535.  t:
+// four timing slots or null.
+struct AvgKeyArgs {
+  const void* X;
+  const void* W_Q;
+  const void* W_K;
+  float* part;
+  float* kbar;
+  float* weff;
+  float* z;
+  int B, N, D, H;
+  float scale;
+};
+size_t avgkey_part_floats(int B, int N, int D);
+hipError_t launch_avgkey(int et, const AvgKeyArgs& a, hipStream_t s, const LaunchTiming* const* t = nullptr);
+
 // Raise the dynamic-LDS limit of the kernels a geometry uses (once per plan).
 hipError_t prepare_kernels(const LineGeom& g, size_t conv_lds, size_t spec_lds, size_t score_lds);
 

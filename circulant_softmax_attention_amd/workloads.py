@@ -162,3 +162,14 @@ def make_inputs(wl: Workload, seed: Optional[int] = None, batch: Optional[int] =
         if b is not None:
             bits[name] = b
     return Inputs(wl=wl if batch is None else wl.with_(B=B), bits=bits or None, **out)
+
+
+def extra_square_weights(wl: Workload, count: int, seed_offset: int = 1000):
+    """`count` further [D, D] weights ~ N(0, 1/D) for the variants that need
+    more projections than a workload's own (the averaged-key variant's W_Q
+    and W_K on a 1D workload), from their own stream: PCG64 seeded with
+    wl.seed + seed_offset, drawn in fp64 in order and stored like the
+    workload's inputs."""
+    rng = np.random.Generator(np.random.PCG64(wl.seed + seed_offset))
+    std = 1.0 / np.sqrt(wl.D)
+    return [_store(rng.standard_normal((wl.D, wl.D)) * std, wl.dtype)[0] for _ in range(count)]

@@ -190,11 +190,13 @@ cat_status cat_forward_cat_2d(cat_plan plan, const void* X, const void* W_A, con
  * for the recorded events and returns, per kernel of the path (1D:
  * projection, spectrum, fft-conv -- the mixing launch of whichever path the
  * plan takes -- then the mixing backward's own: logits reversal, relayout,
- * score-gradient partials, partial sum, logits gradient; 2D: projection,
+ * score-gradient partials, partial sum, logits gradient, then the
+ * averaged-key logits (four launches per call); 2D: projection,
  * scores, spectrum, fft-conv, partial-score sum), the summed milliseconds
  * and the number of launches measured; *nkernels receives the number of
- * kernels (arrays hold at least 8).  cat_forward_* and
- * cat_step_mix_backward_1d record; the other step calls do not. */
+ * kernels (arrays hold at least 16).  cat_forward_* and
+ * cat_step_mix_backward_1d record; the other step calls do not.  The
+ * causal forward records its mixing launch as the fft-conv kind. */
 cat_status cat_plan_set_timing(cat_plan plan, int enable);
 cat_status cat_plan_kernel_times(cat_plan plan, double* total_ms, int64_t* launches, int* nkernels);
 
@@ -273,6 +275,53 @@ cat_status cat_step_mix_backward_1d(cat_plan plan, const float* logits, const vo
  * to the plan. */
 cat_status cat_backward_1d(cat_plan plan, const void* X, const void* W_A, const void* W_V, const void* dO, void* dX,
                            void* dW_A, void* dW_V, void* workspace, void* stream);
+
+/* Averaged-key variant of CAT on a 1D plan (CAT: Circular-Convolutional
+ * Attention for Sub-Quadratic Transformers, ablation table, row "qkv
+ * (Averaged-Key)": 3 D^2 parameters at O(N log N)).  Read as the key
+ * averaged over the tokens and met by each query as in scaled dot-product
+ * attention:
+ *   Q = X_b W_Q,  K = X_b W_K,  kbar_h = (1/N) sum_n K_h[n],
+ *   z_h[n] = Q_h[n] . kbar_h / sqrt(d),  z*_h = softmax over n,
+ *   O_b[:, head h] = circ(z*_h) V[:, head h],  V = X_b W_V,
+ * with the circulant mixing of cat_forward_1d on the plan's path.  The
+ * logits are evaluated as X_b (W_Q,h kbar_h) / sqrt(d) with kbar =
+ * (token mean of X_b) W_K -- the same sums in another association, in fp32
+ * -- so Q and K are never formed.  X [B][N][D], W_Q, W_K, W_V [D][D], O
+ * [B][N][D], storage dtype, caller-owned device memory.  Errors:
+ * CAT_ERR_PLAN_MISMATCH for a 2D plan; CAT_ERR_UNSUPPORTED for D > 3072 or
+ * B > 65535; CAT_ERR_INVALID_ARG for NULL or misaligned pointers. */
+cat_status cat_forward_avgkey_1d(cat_plan plan, const void* X, const void* W_Q, const void* W_K, const void* W_V,
+                                 void* O, void* workspace, void* stream);
+
+/* The averaged-key logits alone: z [B][H][N] fp32 (caller-owned device
+ * memory), as in cat_forward_avgkey_1d.  Same errors. */
+cat_status cat_step_avgkey_logits(cat_plan plan, const void* X, const void* W_Q, const void* W_K, float* z,
+                                  void* workspace, void* stream);
+
+/* Causal CAT on a 1D plan (CAT: Circular-Convolutional Attention for
+ * Sub-Quadratic Transformers, "Loss function / training strategy": a causal
+ * language model must shift Z to stay causal, at O(N^2) cost; "Limitations
+ * and outlook").  Read as standard causal masking of the circulant score
+ * matrix before its row softmax: row i of circ(z_h) keeps the tokens
+ * j <= i,
+ *   O_b[i][c] = sum_{j <= i} exp(z_h[i - j]) V[j][c] / sum_{k <= i} exp(z_h[k]),
+ * with z_h = X_b W_A[:, h] and V = X_b W_V as in cat_forward_1d, evaluated
+ * as the O(N^2) direct product on the matrix cores.  The exponentials are
+ * taken against the maximum of the whole line, so a row whose kept logits
+ * all lie more than about 87 below it would underflow.  X [B][N][D], W_A
+ * [D][H], W_V [D][D], O [B][N][D], caller-owned device memory.  Errors:
+ * CAT_ERR_PLAN_MISMATCH for a 2D plan; CAT_ERR_UNSUPPORTED unless the
+ * storage is bf16, N <= 256 and d is a multiple of 32; CAT_ERR_INVALID_ARG
+ * for NULL or misaligned pointers. */
+cat_status cat_forward_causal_1d(cat_plan plan, const void* X, const void* W_A, const void* W_V, void* O,
+                                 void* workspace, void* stream);
+
+/* The causal mixing alone: O = causal CAT mixing of V [B][N][D] (storage
+ * dtype) with the logits [B][H][N] fp32, as in cat_forward_causal_1d.  Same
+ * errors. */
+cat_status cat_step_mix_causal_1d(cat_plan plan, const float* logits, const void* V, void* O, void* workspace,
+                                  void* stream);
 
 /* 2D score step: probs [B][H][N] fp32 = softmax over the grid of the scaled
  * circular cross-correlation of Q and K (both [B][N][D] fp32).  2D plans only. */

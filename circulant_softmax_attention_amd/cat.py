@@ -31,7 +31,7 @@ EXPORTS = ["cat_plan_create", "cat_plan_destroy", "cat_plan_workspace_size", "ca
            "cat_plan_set_timing", "cat_plan_kernel_times", "cat_plan_conv_path",
            "cat_step_project", "cat_step_spectrum", "cat_step_mix", "cat_step_mix_backward_1d",
            "cat_backward_1d", "cat_step_scores_2d", "cat_forward_avgkey_1d", "cat_step_avgkey_logits",
-           "cat_forward_causal_1d", "cat_step_mix_causal_1d"]
+           "cat_forward_causal_1d", "cat_step_mix_causal_1d", "cat_forward_1d_noalloc"]
 KERNELS_1D = ["project", "spectrum", "fftconv", "reverse", "relayout", "score_grad", "psum", "logits_grad",
               "avgkey_logits"]
 KERNELS_2D = ["project", "scores", "spectrum", "fftconv", "psum"]
@@ -75,6 +75,7 @@ def _load() -> ctypes.CDLL:
     lib.cat_step_avgkey_logits.argtypes = [vp] * 7
     lib.cat_forward_causal_1d.argtypes = [vp] * 7
     lib.cat_step_mix_causal_1d.argtypes = [vp] * 6
+    lib.cat_forward_1d_noalloc.argtypes = [vp] * 6
     for f in EXPORTS:
         fn = getattr(lib, f)
         if f in ("cat_status_string", "cat_last_error"):
@@ -220,6 +221,18 @@ def cat_forward_1d(plan: Plan, X, W_A, W_V, O=None, workspace=None, stream=None)
                                _ptr(W_A, (D, H), dt, "W_A"), _ptr(W_V, (D, D), dt, "W_V"),
                                _ptr(O, (B, N, D), dt, "O"), _ptr(workspace, None, None, "workspace"),
                                _stream_ptr(stream)), "cat_forward_1d")
+    return O
+
+
+def cat_forward_1d_noalloc(plan: Plan, X, W_A, W_V, O=None, stream=None) -> torch.Tensor:
+    """cat_forward_1d on the library's fixed device scratch (no workspace);
+    allocates O only when not given."""
+    B, N, D, H, dt = plan.B, plan.N, plan.D, plan.H, plan.dtype
+    if O is None:
+        O = torch.empty((B, N, D), dtype=dt, device=X.device)
+    _check(_lib.cat_forward_1d_noalloc(ctypes.c_void_p(plan.handle), _ptr(X, (B, N, D), dt, "X"),
+                                       _ptr(W_A, (D, H), dt, "W_A"), _ptr(W_V, (D, D), dt, "W_V"),
+                                       _ptr(O, (B, N, D), dt, "O"), _stream_ptr(stream)), "cat_forward_1d_noalloc")
     return O
 
 

@@ -41,6 +41,7 @@ struct cat_plan_s {
   hipEvent_t fork_ev = nullptr, join_ev = nullptr;
   size_t off_A, off_zc, off_Az;  // long path scratch
   size_t off_xpart, off_kbar, off_weff;  // averaged-key logits scratch (1D)
+  size_t fwd_ws_bytes;  // workspace bytes the 1D forward itself touches (a prefix of the layout)
   bool debug_sync;
   int tile_n;        // forced GEMM tile width (0: the GEMM chooses)
   int num_cu;        // compute units of the device current at plan creation
@@ -260,6 +261,7 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
     pl->off_z = off;
     off = up256(off + BH * p->N * sizeof(float));
     pl->off_Q = pl->off_K = pl->off_part = pl->off_psum = 0;
+    pl->fwd_ws_bytes = off;  // V, spectrum, logits (the long path adds its scratch below)
     if (!longn) {
       // the mixing backward: V in the blocked layout, the score-gradient
       // partials and their sum
@@ -290,6 +292,7 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
       off = up256(off + BH * pl->L * sizeof(float2));
       pl->off_Az = off;
       off = up256(off + BH * pl->L * sizeof(float2));
+      pl->fwd_ws_bytes = off;
     }
     // the averaged-key logits: column-sum partials, mean key, score weights
     pl->off_xpart = off;
@@ -299,6 +302,7 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
     pl->off_weff = off;
     off = up256(off + (size_t)p->B * p->D * p->H * sizeof(float));
   } else {
+    pl->fwd_ws_bytes = 0;  // (1D only)
     pl->off_z = off;  // the CAT-scored variant's logits
     off = up256(off + BH * p->N * sizeof(float));
     pl->off_Q = off;
@@ -792,6 +796,32 @@ cat_status cat_forward_1d(cat_plan plan, const void* X, const void* W_A, const v
   if (plan->p.B == 0) return CAT_OK;  // empty batch: nothing to do
   cat_status st = check_ptrs({X, W_A, W_V, O, workspace});
   if (st != CAT_OK) return st;
+  return cat::forward_1d_checked(plan, X, W_A, W_V, O, workspace, stream);
+}
+
+}  // extern "C"
+
+namespace cat {
+
+size_t plan_forward_ws_bytes(const cat_plan_s* plan) { return plan ? plan->fwd_ws_bytes : 0; }
+
+cat_status plan_check_forward_1d(const cat_plan_s* plan, const void* X, const void* W_A, const void* W_V,
+                                 const void* O) {
+  if (!plan) return fail(CAT_ERR_INVALID_ARG, "NULL plan");
+  if (plan->p.kind != CAT_1D) return fail(CAT_ERR_PLAN_MISMATCH, "plan is not 1D");
+  if (plan->p.B == 0) return CAT_OK;
+  return check_ptrs({X, W_A, W_V, O});
+}
+
+cat_status set_error(cat_status s, const char* msg) { return fail(s, msg); }
+
+int64_t plan_batch(const cat_plan_s* plan) { return plan->p.B; }
+
+// The 1D forward on a workspace of at least plan_forward_ws_bytes bytes,
+// arguments already checked.
+cat_status forward_1d_checked(cat_plan plan, const void* X, const void* W_A, const void* W_V, void* O, void* workspace,
+                              void* stream) {
+  cat_status st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   void* Vb = ws_at(workspace, plan->off_V);
   float* z = reinterpret_cast<float*>(ws_at(workspace, plan->off_z));
@@ -810,6 +840,10 @@ cat_status cat_forward_1d(cat_plan plan, const void* X, const void* W_A, const v
 
   return mix_from_blocked(plan, z, Vb, O, workspace, s, &mk);
 }
+
+}  // namespace cat
+
+extern "C" {
 
 cat_status cat_forward_avgkey_1d(cat_plan plan, const void* X, const void* W_Q, const void* W_K, const void* W_V,
                                  void* O, void* workspace, void* stream) {

@@ -8,6 +8,8 @@
 #include <cstddef>
 #include <cstdint>
 
+#include "../../include/cat.h"
+
 namespace cat {
 
 enum ElemType : int { ET_F32 = 0, ET_BF16 = 1 };
@@ -240,6 +242,16 @@ struct AvgKeyArgs {
 };
 size_t avgkey_part_floats(int B, int N, int D);
 hipError_t launch_avgkey(int et, const AvgKeyArgs& a, hipStream_t s, const LaunchTiming* const* t = nullptr);
+
+// Plan-level helpers of the C-ABI layer (cat_api.cpp) for entry points in
+// other translation units.
+size_t plan_forward_ws_bytes(const cat_plan_s* plan);
+int64_t plan_batch(const cat_plan_s* plan);
+cat_status plan_check_forward_1d(const cat_plan_s* plan, const void* X, const void* W_A, const void* W_V,
+                                 const void* O);
+cat_status forward_1d_checked(cat_plan_s* plan, const void* X, const void* W_A, const void* W_V, void* O,
+                              void* workspace, void* stream);
+cat_status set_error(cat_status s, const char* msg);
 
 // Raise the dynamic-LDS limit of the kernels a geometry uses (once per plan).
 hipError_t prepare_kernels(const LineGeom& g, size_t conv_lds, size_t spec_lds, size_t score_lds);

@@ -323,6 +323,23 @@ cat_status cat_forward_causal_1d(cat_plan plan, const void* X, const void* W_A, 
 cat_status cat_step_mix_causal_1d(cat_plan plan, const float* logits, const void* V, void* O, void* workspace,
                                   void* stream);
 
+/* For callers that cannot allocate device memory (code under stream
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the 1D
+ * forward of cat_forward_1d, with the same arguments minus the workspace.
+ * Its intermediates live in a fixed array of CAT_NOALLOC_SCRATCH_BYTES that
+ * the library keeps in every GPU's memory from load until the process
+ * ends; this call allocates and frees nothing.  Every call on one GPU
+ * shares that GPU's array: calls that overlap on one GPU (other streams,
+ * other threads) race, so order them.  Nothing in the array needs clearing
+ * (each call writes what it reads).  Errors: those of cat_forward_1d;
+ * CAT_ERR_UNSUPPORTED when the problem needs more than
+ * CAT_NOALLOC_SCRATCH_BYTES of intermediates (cat_plan_workspace_size
+ * bounds it; the 1D forward needs about B N D s + 8 B H L + 4 B H N
+ * bytes, s the storage bytes, more on the long path). */
+#define CAT_NOALLOC_SCRATCH_BYTES (64u << 20)
+cat_status cat_forward_1d_noalloc(cat_plan plan, const void* X, const void* W_A, const void* W_V, void* O,
+                                  void* stream);
+
 /* 2D score step: probs [B][H][N] fp32 = softmax over the grid of the scaled
  * circular cross-correlation of Q and K (both [B][N][D] fp32).  2D plans only. */
 cat_status cat_step_scores_2d(cat_plan plan, const float* Q, const float* K, float* probs,

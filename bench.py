@@ -84,6 +84,13 @@ def kernel_model(wl, L: int, ngrp: int, fused_spectrum: bool = False, direct: bo
         m["spectrum"] = dict(bytes=BH * L * 8 + spec_bytes,
                              flops=BH * (2 * fft_flops(L) + 4.0 * N), unit="valu_f32")
     m["fftconv"] = dict(bytes=2 * T * D * s + spec_bytes, flops=lines * (2 * fft_flops(L) + 6.0 * L), unit="valu_f32")
+    if wl.Hg:
+        # the matrix-core 2D conv: four dense G x G x G complex products per
+        # channel pair (4 x 4 x 2 G^3 real flops, bf16 operands); it reads V
+        # and S and writes O
+        G = wl.Hg
+        m["fftconv_matrix"] = dict(bytes=2 * T * D * s + spec_bytes, flops=lines * 4 * 4 * 2.0 * G ** 3,
+                                   unit="mfma_bf16")
     if fused_spectrum:
         cplx = 4 * 2.0 * 32 ** 3  # one 32x32x32 complex product in real flops
         m["fftconv"] = dict(bytes=2 * T * D * s + BH * N * 4, flops=lines * 4 * cplx + B * H * (d // 16) * 2 * cplx,
@@ -270,7 +277,8 @@ def dtype_label(storage: str, conv_path: str) -> str:
     projection and of the mixing; accumulation is fp32 everywhere."""
     if storage == "f32":
         return "f32 (fp32 MFMA GEMM, fp32 transforms)"
-    mix = {"fft_matrix": "fp16-operand MFMA DFT products with per-line power-of-two scaling",
+    mix = {"fft_matrix": "fp16-operand MFMA DFT products with per-line power-of-two scaling (1D), "
+                         "bf16-operand MFMA DFT-matrix products (2D)",
            "direct": "bf16 MFMA direct product (softmax weights rounded to bf16)",
            "fft_valu": "fp32 vector-ALU transforms",
            "fft_multipass": "fp32 vector-ALU transforms"}.get(conv_path, conv_path)
@@ -350,6 +358,8 @@ def run(args):
     conv_path = plan.conv_path()
     if conv_path == "direct":  # the mixing launch is the direct product, not a transform
         ktimes["directconv"] = ktimes.pop("fftconv")
+    if conv_path == "fft_matrix" and wl.Hg:  # 2D products on the matrix cores
+        ktimes["fftconv_matrix"] = ktimes.pop("fftconv")
     for k, (ms, n) in ktimes.items():
         log(f"  kernel {k:10s} {ms * 1000:9.2f} us avg over {n} launches")
 

@@ -26,6 +26,8 @@ struct cat_plan_s {
   bool mconv;        // 1D conv on the matrix cores (L = 1024, bf16, d % 16 == 0)
   bool direct;       // 1D direct circulant product on the matrix cores (bf16, N <= 256, d % 32 == 0)
   bool longn;        // 1D N beyond one workgroup's line: three passes over HBM
+  bool bconv;        // 2D square grid (32 or 96 a side), bf16: the BCCB mixing on the matrix cores
+  void* d_ftab = nullptr;  // its bf16 DFT-matrix fragments
   int logL1, logL2;  // long path: L = 2^logL1 x 2^logL2
   int cg;            // channels per group of the blocked V (2 G; 16 for mconv, 32 for direct)
   int Gs;            // lines per spectrum workgroup
@@ -70,6 +72,34 @@ cat_status hip_fail(hipError_t e, const char* what) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// fp32 -> bf16 bit pattern, round to nearest even (finite inputs).
+uint16_t bf16_rne(float f) {
+  uint32_t x;
+  std::memcpy(&x, &f, 4);
+  x += 0x7fffu + ((x >> 16) & 1u);
+  return (uint16_t)(x >> 16);
+}
+
+// The 2D matrix-core conv's DFT fragments for a side G, bf16:
+// [tile i][K step t][re, im][lane][slot s] = F[lo + 16 i][32 t + 4 grp + s % 4 + 16 (s / 4)]
+// for the tiles i < G / 32 (the kernel derives the others),
+// F[j][k] = exp(-2 pi i j k / G), lo = lane % 16, grp = lane / 16.
+void bconv_host_table(int G, std::vector<uint16_t>& tab) {
+  const int NH = G / 32, KS = G / 32;
+  tab.assign(bconv_table_halfs(G), 0);
+  const double two_pi = 6.283185307179586476925286766559;
+  size_t o = 0;
+  for (int i = 0; i < NH; ++i)
+    for (int t = 0; t < KS; ++t)
+      for (int plane = 0; plane < 2; ++plane)
+        for (int lane = 0; lane < 64; ++lane)
+          for (int sl = 0; sl < 8; ++sl) {
+            const int j = lane % 16 + 16 * i, k = 32 * t + 4 * (lane / 16) + sl % 4 + 16 * (sl / 4);
+            const double ang = two_pi * (double)(((long)j * k) % G) / (double)G;
+            tab[o++] = bf16_rne(plane == 0 ? (float)std::cos(ang) : (float)(-std::sin(ang)));
+          }
+}
 
 size_t up256(size_t v) { return (v + 255) & ~size_t(255); }
 
@@ -228,9 +258,11 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
     pl->direct = !force_fft && p->kind == CAT_1D && p->dtype == CAT_BF16 && p->N <= 256 && d % 32 == 0;
     pl->mconv = !longn && !pl->direct && !force_valu && p->kind == CAT_1D && p->dtype == CAT_BF16 &&
                 g.L1 * g.L2 == 1024 && d % 16 == 0;
+    pl->bconv = !force_valu && p->kind == CAT_BCCB_2D && p->dtype == CAT_BF16 && p->Hg == p->Wg &&
+                bconv_supported((int)p->Hg) && d % 8 == 0;
     pl->G = G;
     pl->ng = d2 / G;
-    pl->cg = pl->direct ? 32 : pl->mconv ? 16 : 2 * G;
+    pl->cg = pl->direct ? 32 : pl->mconv ? 16 : pl->bconv ? 2 : 2 * G;
     if (pl->mconv) pl->ng = (int)d / 16;
     if (pl->direct) pl->ng = (int)d / 32;
   }
@@ -353,9 +385,22 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
       return hip_fail(e, "hipMemcpy(twiddles)");
     }
   }
+  if (pl->bconv) {
+    std::vector<uint16_t> tab;
+    bconv_host_table((int)p->Hg, tab);
+    hipError_t e = hipMalloc(&pl->d_ftab, tab.size() * sizeof(uint16_t));
+    if (e == hipSuccess) e = hipMemcpy(pl->d_ftab, tab.data(), tab.size() * sizeof(uint16_t), hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+      if (pl->d_ftab) (void)hipFree(pl->d_ftab);
+      if (pl->d_tw) (void)hipFree(pl->d_tw);
+      delete pl;
+      return hip_fail(e, "DFT table upload");
+    }
+  }
   hipError_t e = longn ? hipSuccess : prepare_kernels(g, (size_t)G * line_bytes, spectrum_lds_bytes(g, Gs), 2 * line_bytes);
   if (e != hipSuccess) {
     if (pl->d_tw) (void)hipFree(pl->d_tw);
+    if (pl->d_ftab) (void)hipFree(pl->d_ftab);
     delete pl;
     return hip_fail(e, "hipFuncSetAttribute");
   }
@@ -369,6 +414,7 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
       if (pl->fork_ev) (void)hipEventDestroy(pl->fork_ev);
       if (pl->side) (void)hipStreamDestroy(pl->side);
       if (pl->d_tw) (void)hipFree(pl->d_tw);
+      if (pl->d_ftab) (void)hipFree(pl->d_ftab);
       delete pl;
       return hip_fail(se, "stream / event creation");
     }
@@ -382,6 +428,7 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
 cat_status cat_plan_destroy(cat_plan plan) {
   if (plan == nullptr) return CAT_OK;
   if (plan->d_tw) (void)hipFree(plan->d_tw);
+  if (plan->d_ftab) (void)hipFree(plan->d_ftab);
   free_events(plan);
   if (plan->join_ev) (void)hipEventDestroy(plan->join_ev);
   if (plan->fork_ev) (void)hipEventDestroy(plan->fork_ev);
@@ -448,7 +495,7 @@ cat_status cat_plan_conv_path(cat_plan plan, int* path) {
   if (!plan || !path) return fail(CAT_ERR_INVALID_ARG, "NULL argument");
   *path = plan->longn ? CAT_PATH_FFT_MULTIPASS
          : plan->direct ? CAT_PATH_DIRECT
-         : plan->mconv  ? CAT_PATH_FFT_MATRIX
+         : (plan->mconv || plan->bconv) ? CAT_PATH_FFT_MATRIX
                         : CAT_PATH_FFT_VALU;
   return CAT_OK;
 }
@@ -505,6 +552,7 @@ SpecArgs spec_base(const cat_plan_s* pl, void* ws) {
   a.N = (int)pl->p.N;
   a.scale = 1.0f;
   a.G = pl->Gs;
+  a.transpose = pl->bconv ? 1 : 0;  // the 2D matrix-core conv reads S with kc contiguous
   return a;
 }
 
@@ -554,9 +602,24 @@ hipError_t run_long_1d(const cat_plan_s* pl, const float* logits, const void* Vb
                          reinterpret_cast<float2*>(ws_at(ws, pl->off_A)), O, s, ts);
 }
 
-// The 1D conv: on the matrix cores where the plan chose that path.
+// The conv of a plan's path (1D: matrix-core FFT, direct product or vector
+// FFT; 2D: matrix-core or vector FFT) from V in the plan's blocked layout.
 hipError_t run_conv_1d(const cat_plan_s* pl, const ConvArgs& ca, hipStream_t s, const LaunchTiming* t = nullptr) {
   if (pl->direct) return launch_dconv(pl->et, ca, s, t);
+  if (pl->bconv) {
+    BconvArgs b{};
+    b.V = ca.V;
+    b.spec = ca.spec;
+    b.table = pl->d_ftab;
+    b.O = ca.O;
+    b.BH = ca.B * ca.H;
+    b.npair = ca.d / 2;
+    b.H = ca.H;
+    b.D = ca.D;
+    b.d = ca.d;
+    b.num_cu = pl->num_cu;
+    return launch_bconv(b, (int)pl->p.Hg, s, t);
+  }
   return pl->mconv ? launch_mconv(ca, s, t) : launch_conv(pl->geom, pl->et, ca, s, t);
 }
 
@@ -962,7 +1025,7 @@ cat_status cat_forward_cat_2d(cat_plan plan, const void* X, const void* W_A, con
   if (e != hipSuccess) return hip_fail(e, "spectrum launch");
   if ((st = check_sync(plan, "spectrum")) != CAT_OK) return st;
   ConvArgs ca = conv_base(plan, Vb, sa.spec, O);
-  e = launch_conv(plan->geom, plan->et, ca, s, mk.at(3));
+  e = run_conv_1d(plan, ca, s, mk.at(3));
   if (e != hipSuccess) return hip_fail(e, "fft-conv launch");
   return check_sync(plan, "fft-conv");
 }
@@ -986,7 +1049,7 @@ cat_status cat_forward_bccb_2d(cat_plan plan, const void* X, const void* W_Q, co
   ga.nseg = 3;
   ga.seg[0] = seg(W_Q, Qb, D, 1, OUT_BLOCKED, 2);
   ga.seg[1] = seg(W_K, Kb, D, 1, OUT_BLOCKED, 2);
-  ga.seg[2] = seg(W_V, Vb, D, 0, OUT_BLOCKED, 2 * plan->G);
+  ga.seg[2] = seg(W_V, Vb, D, 0, OUT_BLOCKED, plan->cg);
   hipError_t e = launch_gemm(plan->et, ga, s, mk.at(0));
   if (e != hipSuccess) return hip_fail(e, "projection launch");
   if ((st = check_sync(plan, "projection")) != CAT_OK) return st;
@@ -1019,7 +1082,7 @@ cat_status cat_forward_bccb_2d(cat_plan plan, const void* X, const void* W_Q, co
   if ((st = check_sync(plan, "spectrum")) != CAT_OK) return st;
 
   ConvArgs ca = conv_base(plan, Vb, sa.spec, O);
-  e = launch_conv(plan->geom, plan->et, ca, s, mk.at(3));
+  e = run_conv_1d(plan, ca, s, mk.at(3));
   if (e != hipSuccess) return hip_fail(e, "fft-conv launch");
   return check_sync(plan, "fft-conv");
 }

@@ -116,6 +116,7 @@ struct SpecArgs {
   int BH, N;
   float scale;
   int G, log2G;  // lines per workgroup
+  int transpose;  // 2D only: write spec[bh][k2 + L2 k1] (k2 contiguous) instead of k1 + L1 k2
 };
 
 // Fused forward transform . Hadamard . inverse transform of one group of
@@ -222,6 +223,23 @@ hipError_t launch_longconv(int et, const LongArgs& a, const float* logits, const
 hipError_t launch_psum(const float2* part, float2* out, int BH, int ngrp, int L, hipStream_t s,
                        const LaunchTiming* t = nullptr);
 hipError_t launch_relayout(const RelayoutArgs& a, hipStream_t s, const LaunchTiming* t = nullptr);
+// 2D BCCB mixing on the matrix cores (cat_bconv.hip): square grids of side
+// G = 32 or 96, bf16 storage, d % 8 == 0.  V BLOCKED with 2-channel groups;
+// spec in the transposed order [BH][kr][kc] (kc contiguous), 1/N included;
+// table of the plan's bf16 DFT fragments (bconv_table_halfs(G) entries); O
+// [B][N][D].
+struct BconvArgs {
+  const void* V;
+  const float2* spec;
+  const void* table;
+  void* O;
+  int BH, npair, H, D, d;
+  int num_cu;
+};
+bool bconv_supported(int G);
+size_t bconv_table_halfs(int G);
+hipError_t launch_bconv(const BconvArgs& a, int G, hipStream_t s, const LaunchTiming* t = nullptr);
+
 // Logits of the averaged-key variant (cat_variants.hip):
 //   z[b][h][n] = X[b][n] . (W_Q[:, head h] kbar[b]_h) * scale,
 //   kbar[b] = (token mean of X[b]) W_K.

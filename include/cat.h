@@ -35,10 +35,10 @@
  * Storage dtype (CAT_F32 or CAT_BF16) is the same for X, the weights and O;
  * accumulation is fp32 throughout (bf16 inputs are widened exactly, O is
  * rounded to nearest even).  Two bf16 paths multiply in lower precision:
- * CAT_PATH_FFT_MATRIX runs its DFT products on fp16 operands (each line
- * scaled by a power of two) and CAT_PATH_DIRECT rounds the softmax weights
- * to bf16 for its products; CAT_CONV=valu (see cat_plan_conv_path) keeps
- * every product in fp32.  X, the weights, O and the workspace must be 16-byte
+ * CAT_PATH_FFT_MATRIX runs its DFT products on fp16 operands (1D, each line
+ * scaled by a power of two) or bf16 operands (2D), and CAT_PATH_DIRECT
+ * rounds the softmax weights to bf16 for its products; CAT_CONV=valu (see
+ * cat_plan_conv_path) keeps every product in fp32.  X, the weights, O and the workspace must be 16-byte
  * aligned; O must not overlap X, the weights or the workspace.
  *
  * Calls
@@ -131,11 +131,15 @@ cat_status cat_plan_geometry(cat_plan plan, int64_t* L, int64_t* L1, int64_t* L2
 
 /* How the plan evaluates the circulant mixing (diagnostic).  *path:
  *   CAT_PATH_FFT_VALU   (0) transforms on the vector ALU, with a separate
- *                           softmax-spectrum launch (every 2D plan; 1D when
- *                           no other path applies);
+ *                           softmax-spectrum launch (2D and 1D plans that
+ *                           no other path takes);
  *   CAT_PATH_FFT_MATRIX (1) 1D, L = 1024, bf16: radix-32 DFT passes on the
  *                           matrix cores, softmax spectrum computed in the
- *                           same launch;
+ *                           same launch; 2D, square grids of 32 or 96 a
+ *                           side, bf16, d a multiple of 8: each 1D DFT pass
+ *                           over the grid is one dense DFT-matrix product on
+ *                           the matrix cores (bf16 operands, fp32
+ *                           accumulation);
  *   CAT_PATH_DIRECT     (2) 1D, bf16, N <= 256, d a multiple of 32: the product
  *                           circ(z*_h) V_h formed directly on the matrix
  *                           cores, softmax in the same launch (CAT, "Key
@@ -148,7 +152,7 @@ cat_status cat_plan_geometry(cat_plan plan, int64_t* L, int64_t* L1, int64_t* L2
  *                           "Key designs: FFT-accelerated computation";
  *                           the page names N > 10^4 as where it should pay).
  * The environment variable CAT_CONV=fft (at plan creation) excludes path 2,
- * CAT_CONV=valu paths 1 and 2.  Errors: CAT_ERR_INVALID_ARG for a NULL plan
+ * CAT_CONV=valu paths 1 and 2 (in 1D and 2D).  Errors: CAT_ERR_INVALID_ARG for a NULL plan
  * or NULL path. */
 #define CAT_PATH_FFT_VALU 0
 #define CAT_PATH_FFT_MATRIX 1

@@ -528,7 +528,7 @@ def test_scores_2d(cat, Hg, Wg):
 
 
 @pytest.mark.parametrize("Hg,Wg,dtype", [(g[0], g[1], "f32") for g in GRIDS] +
-                         [(12, 12, "bf16"), (32, 32, "f32"), (96, 96, "f32"), (96, 96, "bf16")])
+                         [(12, 12, "bf16"), (32, 32, "f32"), (32, 32, "bf16"), (96, 96, "f32"), (96, 96, "bf16")])
 def test_mix_2d(cat, Hg, Wg, dtype):
     say("mix_2d", Hg, Wg, dtype)
     import torch
@@ -545,10 +545,37 @@ def test_mix_2d(cat, Hg, Wg, dtype):
     assert_parity(O, ref, dtype, "O")
 
 
+@pytest.mark.parametrize("G", [32, 96])
+@pytest.mark.parametrize("case", ["normal", "uniform", "onehot", "tiny", "huge"])
+def test_mix_2d_matrix(cat, G, case):
+    """The 2D mixing on the matrix cores (bf16, square grids of 32 and 96):
+    ordinary logits, uniform logits (the filter is a constant: every output
+    is the grid mean), a near one-hot filter (a cyclic shift of the grid),
+    and value scales 1e-4 and 3e4 (the per-grid power-of-two scaling)."""
+    say("mix_2d_matrix", G, case)
+    import torch
+    B, D, H = (1, 64, 2) if G == 96 else (2, 64, 2)
+    N = G * G
+    rng = np.random.default_rng(G + len(case))
+    logits = (rng.standard_normal((B, H, N)) * 2).astype(np.float32)
+    if case == "uniform":
+        logits[:] = 0.25
+    elif case == "onehot":
+        logits[:, :, 5 * G + 7] = 40.0
+    vs = {"tiny": 1e-4, "huge": 3e4}.get(case, 1.0)
+    V = (rng.standard_normal((B, N, D)) * vs).astype(np.float32)
+    V = W.bf16_bits_to_f32(W.round_bf16_bits(V)).reshape(V.shape)
+    plan = cat.cat_plan_create("2d", "bf16", B, N, D, H, G, G)
+    assert plan.conv_path() == "fft_matrix"
+    O = to_np(cat.cat_step_mix(plan, torch.from_numpy(logits).cuda(), to_dev(V, "bf16")))
+    ref = oracle.bccb_2d(oracle.softmax(logits).reshape(B, H, G, G), V)
+    assert_parity(O, ref, "bf16", "O")
+
+
 @pytest.mark.parametrize("B,Hg,Wg,D,H,dtype,ss", [(1, 3, 4, 16, 2, "f32", 1.0), (2, 8, 8, 32, 2, "f32", 0.3),
                                                   (2, 12, 12, 48, 3, "bf16", 0.3), (1, 6, 8, 64, 1, "f32", 1.0),
                                                   (2, 16, 16, 64, 4, "bf16", 0.2), (2, 8, 8, 24, 4, "f32", 0.5),
-                                                  (1, 12, 12, 24, 2, "bf16", 0.3)])
+                                                  (1, 12, 12, 24, 2, "bf16", 0.3), (2, 32, 32, 64, 2, "bf16", 0.3)])
 def test_forward_2d_small(cat, B, Hg, Wg, D, H, dtype, ss):
     say("forward_2d", B, Hg, Wg, D, H, dtype, ss)
     import torch

@@ -87,29 +87,28 @@ __device__ __forceinline__ raw8 xr8(const raw8& x, uint32_t m) { return make_uin
 constexpr uint32_t NEG = 0x80008000u;  // every slot negated
 constexpr uint32_t ODD = 0x80000000u;  // odd slots (high halves) negated
 
-// acc += data (A operand, rows kept) x constant (B).  CONJ conjugates the
-// constant; FLIP applies the (-1)^k of DFT rows j + G/2 (on the data).
-template <bool CONJ, bool FLIP>
-__device__ __forceinline__ void mulA(const CX& d, const CX& k, CT& acc) {
-  const uint32_t f = FLIP ? ODD : 0u;
-  const raw8 dr = xr8(d.re, f), di = xr8(d.im, f);
-  if (CONJ) {  // (dr + i di)(kr - i ki) = dr kr + di ki + i (di kr - dr ki)
-    const raw8 ndr = xr8(d.re, f ^ NEG);
-    acc.re = mm(di, k.im, mm(dr, k.re, acc.re));
-    acc.im = mm(ndr, k.im, mm(di, k.re, acc.im));
-  } else {  // (dr + i di)(kr + i ki) = dr kr - di ki + i (dr ki + di kr)
-    const raw8 ndi = xr8(d.im, f ^ NEG);
-    acc.re = mm(ndi, k.im, mm(dr, k.re, acc.re));
-    acc.im = mm(di, k.re, mm(dr, k.im, acc.im));
-  }
+// A constant fragment with its negated imaginary part alongside.
+struct KX {
+  raw8 re, im, nim;
+};
+__device__ __forceinline__ KX kx(const raw8& re, const raw8& im) { return KX{re, im, xr8(im, NEG)}; }
+// The odd-slot flip of a data operand: (-1)^k on the data stands for the
+// upper-half DFT tile (rows j + G / 2) of the constant it meets.
+__device__ __forceinline__ CX flip(const CX& d) { return CX{xr8(d.re, ODD), xr8(d.im, ODD)}; }
+
+// acc += data (A operand, rows kept) x constant (B):
+//   (dr + i di)(kr + i ki)          = dr kr + di (-ki) + i (dr ki + di kr)
+//   (dr + i di)(kr - i ki) (CONJ)   = dr kr + di ki + i (dr (-ki) + di kr)
+template <bool CONJ>
+__device__ __forceinline__ void mulA(const CX& d, const KX& k, CT& acc) {
+  acc.re = mm(d.im, CONJ ? k.im : k.nim, mm(d.re, k.re, acc.re));
+  acc.im = mm(d.im, k.re, mm(d.re, CONJ ? k.nim : k.im, acc.im));
 }
-// acc += constant (A) x data (B operand, columns kept), constant not conjugated.
-template <bool FLIP>
-__device__ __forceinline__ void mulB(const CX& k, const CX& d, CT& acc) {
-  const uint32_t f = FLIP ? ODD : 0u;
-  const raw8 dr = xr8(d.re, f), di = xr8(d.im, f), ndi = xr8(d.im, f ^ NEG);
-  acc.re = mm(k.im, ndi, mm(k.re, dr, acc.re));
-  acc.im = mm(k.im, dr, mm(k.re, di, acc.im));
+// acc += constant (A) x data (B operand, columns kept), same forms.
+template <bool CONJ>
+__device__ __forceinline__ void mulB(const KX& k, const CX& d, CT& acc) {
+  acc.re = mm(CONJ ? k.im : k.nim, d.im, mm(k.re, d.re, acc.re));
+  acc.im = mm(CONJ ? k.nim : k.im, d.re, mm(k.re, d.im, acc.im));
 }
 // K operand whose slot v + 4 y takes value v of tile y, rounded to bf16.
 __device__ __forceinline__ CX stack(const CT& t0, const CT& t1) {
@@ -160,14 +159,13 @@ __global__ __launch_bounds__(BT) void bconv_kernel(BconvArgs a) {
   // DFT fragments kf[i][t] for i < NH: lane (lo, grp), slot s ->
   // F[lo + 16 i][32 t + 4 grp + s % 4 + 16 (s / 4)]; tile i + NH is tile i
   // times (-1)^k, k having the parity of s.
-  CX kf[NH][KS];
+  KX kf[NH][KS];
 #pragma unroll
   for (int i = 0; i < NH; ++i)
 #pragma unroll
     for (int t = 0; t < KS; ++t) {
       const uint4* src = reinterpret_cast<const uint4*>(a.table) + ((size_t)(i * KS + t) * 2) * 64 + lane;
-      kf[i][t].re = src[0];
-      kf[i][t].im = src[64];
+      kf[i][t] = kx(src[0], src[64]);
     }
 
   const int qpb = a.npair / 4;  // quads of pairs per (b, h)
@@ -204,13 +202,16 @@ __global__ __launch_bounds__(BT) void bconv_kernel(BconvArgs a) {
           x[t].im = make_uint4(hi2(w0.x, w0.y), hi2(w0.z, w0.w), hi2(w1.x, w1.y), hi2(w1.z, w1.w));
         }
         if (ri + 1 < NT) fetch((ri + 1) & 1, ri + 1);
+        CX xf[KS];
+#pragma unroll
+        for (int t = 0; t < KS; ++t) xf[t] = flip(x[t]);
 #pragma unroll
         for (int kt = 0; kt < NT; ++kt) {
           CT d1 = zero_ct();
 #pragma unroll
           for (int t = 0; t < KS; ++t) {
-            if (kt < NH) mulA<false, false>(x[t], kf[kt][t], d1);
-            else mulA<false, true>(x[t], kf[kt - NH][t], d1);
+            if (kt < NH) mulA<false>(x[t], kf[kt][t], d1);
+            else mulA<false>(xf[t], kf[kt - NH][t], d1);
           }
           // rows r = 16 ri + 4 grp + v, col kc = 16 kt + lo -> es[kc][r .. r + 3]
           const int o = (16 * kt + lo) * PITCH + 16 * ri + 4 * grp;
@@ -247,6 +248,9 @@ __global__ __launch_bounds__(BT) void bconv_kernel(BconvArgs a) {
       }
       // pass 2 (rows kr = 16 ki + 4 grp + v, cols kc), two kr tiles at a
       // time, each times the spectrum and stacked into pass 3's operand
+      CX yf[KS];
+#pragma unroll
+      for (int t = 0; t < KS; ++t) yf[t] = flip(y[t]);
       CX z[KS];
 #pragma unroll
       for (int tt = 0; tt < KS; ++tt) {
@@ -258,7 +262,7 @@ __global__ __launch_bounds__(BT) void bconv_kernel(BconvArgs a) {
 #pragma unroll
           for (int t = 0; t < KS; ++t) {
             if (ki < NH) mulB<false>(kf[ki][t], y[t], d2[u]);
-            else mulB<true>(kf[ki - NH][t], y[t], d2[u]);
+            else mulB<false>(kf[ki - NH][t], yf[t], d2[u]);
           }
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
@@ -271,23 +275,23 @@ __global__ __launch_bounds__(BT) void bconv_kernel(BconvArgs a) {
         z[tt] = stack(d2[0], d2[1]);
         __builtin_amdgcn_sched_barrier(0);
       }
-      // pass 3: D3[i] rows kc = 16 kt + 4 grp + v, cols r' = 16 i + lo ->
-      // es[kc][r'] (the band's rows, already read above)
+      // pass 3 (data as B): D3[i] rows r' = 16 i + 4 grp + v, cols kc = 16 kt + lo
+      // -> es[kc][r' .. r' + 3] (the band's rows, already read above)
+      CX zf[KS];
+#pragma unroll
+      for (int t = 0; t < KS; ++t) zf[t] = flip(z[t]);
 #pragma unroll
       for (int i = 0; i < NT; ++i) {
         CT d3 = zero_ct();
 #pragma unroll
         for (int t = 0; t < KS; ++t) {
-          if (i < NH) mulA<true, false>(z[t], kf[i][t], d3);
-          else mulA<true, true>(z[t], kf[i - NH][t], d3);
+          if (i < NH) mulB<true>(kf[i][t], z[t], d3);
+          else mulB<true>(kf[i - NH][t], zf[t], d3);
         }
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int o = (16 * kt + 4 * grp + v) * PITCH + 16 * i + lo;
-          const uint32_t pk = pack_bf16x2(d3.re[v], d3.im[v]);
-          e[o] = (uint16_t)(pk & 0xffffu);
-          e[PLANE + o] = (uint16_t)(pk >> 16);
-        }
+        const int o = (16 * kt + lo) * PITCH + 16 * i + 4 * grp;
+        *reinterpret_cast<uint2*>(e + o) = make_uint2(pack_bf16x2(d3.re[0], d3.re[1]), pack_bf16x2(d3.re[2], d3.re[3]));
+        *reinterpret_cast<uint2*>(e + PLANE + o) =
+            make_uint2(pack_bf16x2(d3.im[0], d3.im[1]), pack_bf16x2(d3.im[2], d3.im[3]));
       }
     }
     __syncthreads();
@@ -299,7 +303,7 @@ __global__ __launch_bounds__(BT) void bconv_kernel(BconvArgs a) {
       uint4* ob = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.O) + (size_t)b * N * a.D +
                                            (size_t)h * a.d + 8 * pq);
       const int Dq = a.D / 8;  // 16-byte chunks per token row of O
-      CX kc[2][KS];
+      KX kc[2][KS];
       auto fetch_kc = [&](const int buf, int ct) {
         // column tile ct's constant (runtime index, (-1)^k of the upper half applied)
         const int c0 = ct < NH ? ct : ct - NH;
@@ -307,8 +311,7 @@ __global__ __launch_bounds__(BT) void bconv_kernel(BconvArgs a) {
 #pragma unroll
         for (int t = 0; t < KS; ++t) {
           const uint4* src = reinterpret_cast<const uint4*>(a.table) + ((size_t)(c0 * KS + t) * 2) * 64 + lane;
-          kc[buf][t].re = xr8(src[0], fl);
-          kc[buf][t].im = xr8(src[64], fl);
+          kc[buf][t] = kx(xr8(src[0], fl), xr8(src[64], fl));
         }
       };
       auto unit = [&](int u, auto bufc) {
@@ -329,7 +332,7 @@ __global__ __launch_bounds__(BT) void bconv_kernel(BconvArgs a) {
             CX x;
             x.re = make_uint4(r0.x, r0.y, r1.x, r1.y);
             x.im = make_uint4(i0.x, i0.y, i1.x, i1.y);
-            mulA<true, false>(x, kc[cur][t], d4);
+            mulA<true>(x, kc[cur][t], d4);
           }
 #pragma unroll
           for (int v = 0; v < 4; ++v) wv[v][pp] = pack_bf16x2(d4.re[v], d4.im[v]);

@@ -46,6 +46,7 @@ struct cat_plan_s {
   size_t fwd_ws_bytes;  // workspace bytes the 1D forward itself touches (a prefix of the layout)
   bool debug_sync;
   int tile_n;        // forced GEMM tile width (0: the GEMM chooses)
+  int tile_m;        // forced GEMM tile rows (0: the GEMM chooses)
   int num_cu;        // compute units of the device current at plan creation
   // per-launch timing slots: ev[slot][launch][start/stop], kind[slot][launch]
   static constexpr int kSlots = 256, kMaxL = 32, kMaxK = 4;
@@ -280,6 +281,9 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
   const char* tn = std::getenv("CAT_GEMM_TILE_N");
   pl->tile_n = tn ? std::atoi(tn) : 0;
   if (pl->tile_n != 96 && pl->tile_n != 128 && pl->tile_n != 192) pl->tile_n = 0;
+  const char* tm = std::getenv("CAT_GEMM_TILE_M");
+  pl->tile_m = tm ? std::atoi(tm) : 0;
+  if (pl->tile_m != 128 && pl->tile_m != 256) pl->tile_m = 0;
 
   const size_t BND = (size_t)p->B * p->N * p->D;
   const size_t BH = (size_t)p->B * p->H;
@@ -530,6 +534,7 @@ GemmArgs gemm_base(const cat_plan_s* pl, const void* X) {
   a.d = pl->d;
   a.num_cu = pl->num_cu;
   a.tile_n = pl->tile_n;
+  a.tile_m = pl->tile_m;
   return a;
 }
 

@@ -9,8 +9,10 @@
 // write it.  One launch covers up to three column segments, each written in
 // the layout its consumer reads.
 //
-// Tiling: 128 x BN output tile (BN = 96, 128 or 192) per 256-thread workgroup (4
-// waves, 2 x 2), each wave a 64 x BN/2 block of 16 x 16 MFMA tiles.  K is
+// Tiling: BM x BN output tile (BM = 128 or 256, BN = 96, 128 or 192) per
+// workgroup of 2 BM threads (BM / 64 x 2 waves), each wave a 64 x BN/2 block
+// of 16 x 16 MFMA tiles; 256-row tiles (one workgroup per compute unit) halve
+// the W tile traffic per output and are used at 192 columns.  K is
 // walked in tiles of 128 bytes of an X row (64 bf16 or 32 fp32 values), i.e.
 // eight 16-byte chunks; a chunk is what one lane feeds the MFMA:
 //   bf16: 8 values -> v_mfma_f32_16x16x32_bf16 (fp32 accumulate)
@@ -36,12 +38,13 @@
 //
 // Score projection (1D): z = X W_A has only one column per head (at most
 // 32), far too narrow for a tile of its own.  It is folded into the output
-// tiles of the first segment: the first min(8, column tiles) tiles of a row
-// panel share its eight 16-row blocks, and the wave that owns a block
+// tiles of the first segment: the first min(BM / 16, column tiles) tiles of a
+// row panel share its BM / 16 16-row blocks, and the wave that owns a block
 // multiplies the X fragments it already holds for the main product by W_A^T
-// fragments (16 heads per MFMA block, one or two blocks) loaded from global
-// memory a K tile ahead.  X is therefore read once for both products; z
-// leaves head-major ([B][H][N] fp32) from registers.
+// fragments (16 heads per MFMA block, one or two blocks).  The K tile's W_A
+// rows (BK nz contiguous values) are staged in LDS with the X and W tiles and
+// read transposed like a W fragment.  X is therefore read once for both
+// products; z leaves head-major ([B][H][N] fp32) from registers.
 #include "cat_common.hpp"
 #include "cat_internal.hpp"
 
@@ -52,7 +55,6 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4;
 
 namespace {
 
-constexpr int BM = 128, NTHR = 256;
 constexpr int ZMAX = 32;   // score-projection columns (heads) one launch covers
 constexpr int ROWB = 128;  // bytes of one X row of a K tile
 
@@ -81,6 +83,7 @@ __device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds) {
 }
 #pragma clang diagnostic pop
 __device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void wait_vmem_4() { asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); }
 
 // acc += A^T B over one 16-byte chunk (A, B: 16 rows x chunk each; the
 // result's column index follows B's rows).
@@ -127,15 +130,21 @@ __device__ __forceinline__ size_t out_index(const GemmSeg& s, const GemmArgs& a,
   return (((size_t)(b * a.H + h) * ng + g) * a.Ntok + tok) * s.cg + j;
 }
 
-// ZB: 16-head blocks of the score projection (0: none, at most 2).
-template <int ET, int BN, int ZB>
-__global__ __launch_bounds__(NTHR, 2) void gemm_xw_kernel(GemmArgs a) {
+// ZB: 16-head blocks of the score projection (0: none, at most 2).  BM: tile
+// rows, 128 (256 threads, two workgroups per compute unit) or 256 (512
+// threads, one workgroup per compute unit).  ZTR: bf16 W_A fragments come
+// from transposing LDS reads (needs nz % 4 == 0).
+template <int ET, int BN, int ZB, int BM, bool ZTR = false>
+__global__ __launch_bounds__(2 * BM, 256 / BM) void gemm_xw_kernel(GemmArgs a) {
+  constexpr int NTHR = 2 * BM;  // 64-row wave blocks, two per row of waves
   using C = GemmCfg<ET>;
   constexpr int VE = C::VE, BK = C::BK, ESZ = C::ESZ;
   constexpr int PB = BN * ESZ;                  // bytes of one W row of the tile
   constexpr int CPRB = PB / 16;                 // 16-byte chunks per W row
-  constexpr int STAGE = BM * ROWB + BK * PB;  // one LDS stage: X rows, W rows
+  constexpr int ZT = ZB * BK * 16 * ESZ;        // W_A rows of the tile, room for 16 ZB heads
+  constexpr int STAGE = BM * ROWB + BK * PB + ZT;  // one LDS stage: X rows, W rows, W_A rows
   constexpr int SMEM = 2 * STAGE;
+  static_assert(ZT / 16 <= NTHR, "one W_A chunk per thread");
   constexpr int BCH = BK * CPRB / NTHR;         // W chunks per thread
   constexpr int TN = BN / 32;                   // 16-column MFMA blocks per wave
   static_assert(BCH * NTHR == BK * CPRB && TN * 32 == BN, "tile width");
@@ -159,14 +168,14 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_xw_kernel(GemmArgs a) {
   const int m0 = rt * BM, n0 = ct * BN;
   const int M = a.M, K = a.K, ncols = sg.ncols;
 
-  // Score projection (first segment only): the first nct <= 8 column tiles
-  // of a row panel share its eight 16-row blocks, block rb going to column
-  // tile rb % nct and, inside it, to wave (rb / 4, rb % 2).  A wave thus
-  // handles blocks 4 wm + wn + 2 ii, ii = 0, 1, of its own X rows.  The
-  // W_A^T fragments come straight from global memory (W_A is a few KB and
-  // stays cached), a K tile ahead of their use.
+  // Score projection (first segment only): the first nct <= BM / 16 column
+  // tiles of a row panel share its BM / 16 16-row blocks, block rb going to
+  // column tile rb % nct and, inside it, to wave (rb / 4, rb % 2).  A wave
+  // thus handles blocks 4 wm + wn + 2 ii, ii = 0, 1, of its own X rows.  The
+  // W_A rows of each K tile ride along in the LDS stage (they are contiguous
+  // in memory: BK nz values).
   const int nz = a.nz;
-  const int nct = a.seg[0].ntiles < 8 ? a.seg[0].ntiles : 8;
+  const int nct = a.seg[0].ntiles < BM / 16 ? a.seg[0].ntiles : BM / 16;
   const bool zon = ZB > 0 && si == 0 && ct < nct;
   bool zrb[2];
 #pragma unroll
@@ -180,7 +189,7 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_xw_kernel(GemmArgs a) {
   const elem_t* asrc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int r = (tid >> 3) + 32 * i;
+    const int r = (tid >> 3) + (NTHR / 8) * i;
     const int am = m0 + r < M ? m0 + r : M - 1;
     asrc[i] = reinterpret_cast<const elem_t*>(a.X) + (size_t)am * K + kch;
   }
@@ -200,6 +209,12 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_xw_kernel(GemmArgs a) {
     bsrc[i] = reinterpret_cast<const elem_t*>(sg.W) + (size_t)k * ncols + col;
   }
   const uint32_t lds0 = lds_addr(smem) + (uint32_t)wave * 64 * 16;
+  // W_A tile: 16-byte chunk c = tid of the K tile's BK nz contiguous values
+  // (8 nz chunks), read by the first 2 ZB waves; lanes past the last chunk
+  // repeat it (into the padding of the stage's W_A room).
+  const int zchunks = ZB > 0 ? 8 * nz : 0;
+  const bool zdma = zon && wave < 2 * ZB;
+  const char* zsrc = reinterpret_cast<const char*>(a.Wz) + 16 * (size_t)(tid < zchunks ? tid : zchunks - 1);
 
   // Stage tile kt into LDS stage st.
   auto issue = [&](int kt, int st) {
@@ -210,6 +225,7 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_xw_kernel(GemmArgs a) {
       for (int i = 0; i < 4; ++i) lds_dma16(asrc[i] + k0, base + i * NTHR * 16);
 #pragma unroll
       for (int i = 0; i < BCH; ++i) lds_dma16(bsrc[i] + (size_t)k0 * ncols, base + BM * ROWB + i * NTHR * 16);
+      if (ZB > 0 && zdma) lds_dma16(zsrc + (size_t)k0 * nz * ESZ, base + BM * ROWB + BK * PB);
     } else {
       // K tail: X chunks and W rows at or beyond K are zero
       const bool ok = k0 + kch < K;
@@ -231,6 +247,16 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_xw_kernel(GemmArgs a) {
       for (int i = 0; i < 4; ++i) dst[i * NTHR] = va[i];
 #pragma unroll
       for (int i = 0; i < BCH; ++i) dst[BM * 8 + i * NTHR] = vb[i];
+      if (ZB > 0 && zon && tid < ZT / 16) {  // W_A values of rows at or beyond K (and the padding) are zero
+        const elem_t* wz = reinterpret_cast<const elem_t*>(a.Wz) + (size_t)k0 * nz;
+        elem_t e[VE];
+#pragma unroll
+        for (int j = 0; j < VE; ++j) {
+          const int f = VE * tid + j;
+          e[j] = tid < zchunks && k0 + f / nz < K ? wz[f] : elem_t(0);
+        }
+        reinterpret_cast<uint4*>(smem + st * STAGE + BM * ROWB + BK * PB)[tid] = *reinterpret_cast<const uint4*>(e);
+      }
     }
   };
 
@@ -297,30 +323,49 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_xw_kernel(GemmArgs a) {
       for (int j = 0; j < TN; ++j) acc[i][j] = mfma_chunk<ET>(bf[j], af[i], acc[i][j]);
   };
 
-  // W_A^T fragments of K tile kt, [buf][zb][kc] (buf = kt % 2): lane (lrow,
-  // lgrp) holds head 16 zb + lrow (clamped to nz - 1; such heads are never
-  // stored) at the K positions of its X fragments; K positions at or beyond K
-  // read zero.
+  // W_A^T fragment of K step kc for heads 16 zb ..: lane (lrow, lgrp) holds
+  // head 16 zb + lrow at the K positions of its X fragments, read from the
+  // stage's W_A rows [BK][nz] (row pitch nz values).  bf16 with nz % 4 == 0:
+  // two transposing reads, the lanes of a group addressing 4 rows x 4 head
+  // quads exactly as for a W fragment (heads past nz read the next row's
+  // values or the zero padding; their results are never stored); otherwise
+  // one read per K value.  Heads past nz are clamped in the per-value reads.
   constexpr int ZA = ZB > 0 ? ZB : 1;  // register arrays need a size
-  uint4 zw[2][ZA][2];
-  auto zload = [&](int kt, int buf) {
-    const elem_t* wa = reinterpret_cast<const elem_t*>(a.Wz);
+  const int zp = nz * ESZ;             // bytes per W_A row
+  auto zfrag = [&](int st, int zb, int kc) -> uint4 {
+    const char* zt = smem + st * STAGE + BM * ROWB + BK * PB;
+    if constexpr (ET == ET_BF16) {
+      if constexpr (ZTR) {
+        typedef short v4s __attribute__((ext_vector_type(4)));
+        typedef __attribute__((address_space(3))) v4s lds_v4s;
+        uint2 part[2];
 #pragma unroll
-    for (int zb = 0; zb < ZB; ++zb) {
-      const int h0 = 16 * zb + lrow;
-      const int h = h0 < nz ? h0 : nz - 1;
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-        const int kb = kt * BK + (kc * 4 + lgrp) * VE;
-        elem_t e[VE];
-#pragma unroll
-        for (int u = 0; u < VE; ++u) {
-          const int k = kb + u < K ? kb + u : K - 1;
-          const elem_t v = wa[(size_t)k * nz + h];
-          e[u] = kb + u < K ? v : elem_t(0);
+        for (int hlf = 0; hlf < 2; ++hlf) {
+          const int k = kc * 32 + 8 * lgrp + 4 * hlf + (lrow >> 2);
+          const char* ptr = zt + k * zp + 32 * zb + 8 * (lrow & 3);
+          const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4s*)(const __attribute__((address_space(3))) char*)ptr);
+          part[hlf] = *reinterpret_cast<const uint2*>(&r);
         }
-        zw[buf][zb][kc] = *reinterpret_cast<const uint4*>(e);
+        return make_uint4(part[0].x, part[0].y, part[1].x, part[1].y);
+      } else {
+        const int h0 = 16 * zb + lrow, h = h0 < nz ? h0 : nz - 1;
+        uint32_t w[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int k = kc * 32 + 8 * lgrp + 2 * u;
+          const uint32_t lo = *reinterpret_cast<const uint16_t*>(zt + k * zp + 2 * h);
+          const uint32_t hi = *reinterpret_cast<const uint16_t*>(zt + (k + 1) * zp + 2 * h);
+          w[u] = lo | (hi << 16);
+        }
+        return make_uint4(w[0], w[1], w[2], w[3]);
       }
+    } else {
+      const int h0 = 16 * zb + lrow, h = h0 < nz ? h0 : nz - 1;
+      uint32_t w[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) w[u] = *reinterpret_cast<const uint32_t*>(zt + (kc * 16 + 4 * lgrp + u) * zp + 4 * h);
+      return make_uint4(w[0], w[1], w[2], w[3]);
     }
   };
   floatx4 zacc[2][ZA];  // [ii][zb]
@@ -328,38 +373,44 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_xw_kernel(GemmArgs a) {
   for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
     for (int zb = 0; zb < ZA; ++zb) zacc[ii][zb] = floatx4{0.f, 0.f, 0.f, 0.f};
-  auto zmma = [&](int kc, const uint4 (&af)[4], int buf) {
-    if (ZB == 0 || !zwave) return;
+  // The X fragment of block ii is af[wn + 2 ii]; wn is uniform, so the two
+  // cases are separate branches rather than per-lane selects.
+  auto zmma_wn = [&](int kc, const uint4 (&af)[4], int st, auto wn_tag) {
+    constexpr int WN = decltype(wn_tag)::value;
 #pragma unroll
-    for (int ii = 0; ii < 2; ++ii) {
-      if (zrb[ii]) {
-        const uint4 xa = wn ? af[1 + 2 * ii] : af[2 * ii];  // no dynamic register indexing
+    for (int zb = 0; zb < ZB; ++zb) {
+      const uint4 wf = zfrag(st, zb, kc);
 #pragma unroll
-        for (int zb = 0; zb < ZB; ++zb) zacc[ii][zb] = mfma_chunk<ET>(zw[buf][zb][kc], xa, zacc[ii][zb]);
-      }
+      for (int ii = 0; ii < 2; ++ii)
+        if (zrb[ii]) zacc[ii][zb] = mfma_chunk<ET>(wf, af[WN + 2 * ii], zacc[ii][zb]);
     }
+  };
+  auto zmma = [&](int kc, const uint4 (&af)[4], int st) {
+    if (ZB == 0 || !zwave) return;
+    if (wn)
+      zmma_wn(kc, af, st, std::integral_constant<int, 1>{});
+    else
+      zmma_wn(kc, af, st, std::integral_constant<int, 0>{});
   };
 
   // Tile kt lives in stage kt % 2.  At the top of step kt every wave has its
   // own DMA of tile kt complete and, after the barrier, all of them have
-  // finished multiplying tile kt - 1, whose stage then receives tile kt + 1.
-  // Two workgroups share a compute unit, so one's LDS reads overlap the
-  // other's MFMAs.  The W_A^T fragments are double-buffered in registers:
-  // those of tile kt + 1 are requested right after the barrier of step kt,
-  // before its MFMAs, so their global-load latency hides behind a whole step.
-  // The loop is unrolled by two so that stage and buffer indices are
-  // compile-time constants.
+  // finished multiplying tile kt - 1, whose stage then receives tile kt + 1,
+  // whose DMA thus runs under the MFMAs of tile kt.  The loop is unrolled by
+  // two so that stage indices are compile-time constants.
   const int nk = (K + BK - 1) / BK;
   issue(0, 0);
-  if (ZB > 0 && zwave) zload(0, 0);
-  // L2 warm-up: the column tiles of one row panel (consecutive workgroups on
-  // one XCD) together touch every 64-byte sector of the panel's X rows once,
-  // so that the staging loads of the later K tiles hit L2 rather than HBM.
+  // L2 warm-up, where a row panel is read by many column tiles: those tiles
+  // (consecutive workgroups on one XCD) together touch every 64-byte sector
+  // of the panel's X rows once, right after the first tile's DMA, so that
+  // the DMAs of the later K tiles hit L2 rather than all missing at once.
   // Four loads per thread cover panels of up to 4 x 256 x (column tiles)
-  // sectors; the values only feed a test that never passes.
+  // sectors; step 0 waits for the first tile only (the warm-up loads were
+  // issued after it), and the values feed a test that never passes.
   constexpr int WARM = 4;
-  uint32_t wv[WARM];
-  {
+  const bool warm = BN != 192 && a.warm;
+  uint32_t wv[WARM] = {0u, 0u, 0u, 0u};
+  if (warm) {
     const int rows = M - m0 < BM ? M - m0 : BM;
     const uint32_t spr = (uint32_t)(K * ESZ + 63) / 64;  // sectors per row
     const uint32_t nsec = (uint32_t)rows * spr;
@@ -375,21 +426,11 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_xw_kernel(GemmArgs a) {
   uint4 af[4], bf[TN];
   auto step = [&](int kt, auto parity) {
     constexpr int st = decltype(parity)::value;
-    wait_vmem_all();
+    if (kt == 0 && warm)
+      wait_vmem_4();
+    else
+      wait_vmem_all();
     __syncthreads();
-    if (ZB > 0 && zwave) {
-      // The fragments of tile kt are complete (the wait above); tying them to
-      // this point makes the compiler's own wait for them land here, before
-      // the loads of the next tile are issued, instead of at their first use.
-#pragma unroll
-      for (int zb = 0; zb < ZA; ++zb)
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc) {
-          const uint4 v = zw[st][zb][kc];
-          asm volatile("" ::"v"(v.x), "v"(v.y), "v"(v.z), "v"(v.w));
-        }
-      if (kt + 1 < nk) zload(kt + 1, st ^ 1);
-    }
     if (kt + 1 < nk) issue(kt + 1, st ^ 1);
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
@@ -402,7 +443,7 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_xw_kernel(GemmArgs a) {
     step(kt, std::integral_constant<int, 0>{});
     if (kt + 1 < nk) step(kt + 1, std::integral_constant<int, 1>{});
   }
-  if (((wv[0] ^ wv[1]) + (wv[2] ^ wv[3])) == 0x9E3779B9u && M < 0)  // keeps the warm-up loads
+  if (warm && ((wv[0] ^ wv[1]) + (wv[2] ^ wv[3])) == 0x9E3779B9u && M < 0)  // keeps the warm-up loads
     reinterpret_cast<float*>(sg.out)[0] = 0.f;
 
   // Result layout (16 x 16 MFMA, A = W rows, B = X rows): lane (lrow, lgrp)
@@ -516,15 +557,14 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_xw_kernel(GemmArgs a) {
   }
 }
 
-// Output tile width: 192, 128 or 96 columns.  Two workgroups fit a compute
-// unit, so the grid runs in rounds of 2 x CUs workgroups; the estimated time
-// is rounds x (BN + 48) (a tile costs its columns plus a fixed part), and the
-// cheapest width is taken.  192-column tiles are for 2-byte operands and
-// 2-byte outputs that take the staged epilogue only (the LDS holds two stages
-// of an fp32 W tile of that width, or an fp32 output tile, only barely or not).
-// 192-wide tiles: 2-byte operands, at most 16 score-projection heads (more
-// would not fit the registers), and every segment takes the staged epilogue
-// with 2-byte output.
+// Output tile width: 192, 128 or 96 columns.  Two 128-row workgroups fit a
+// compute unit, so the grid runs in rounds of 2 x CUs workgroups; the
+// estimated time is rounds x (BN + 48) (a tile costs its columns plus a fixed
+// part), and the cheapest width is taken.  192-column tiles are for 2-byte
+// operands and 2-byte outputs that take the staged epilogue only (the LDS
+// holds two stages of an fp32 W tile of that width, or an fp32 output tile,
+// only barely or not), and for at most 16 score-projection heads (more would
+// not fit the registers).
 bool wide_ok(int et, const GemmArgs& a) {
   bool ok = et != ET_F32 && a.nz <= 16;
   for (int s = 0; s < a.nseg; ++s) {
@@ -535,17 +575,22 @@ bool wide_ok(int et, const GemmArgs& a) {
   return ok;
 }
 
+long col_tiles(const GemmArgs& a, int bn) {
+  long t = 0;
+  for (int s = 0; s < a.nseg; ++s) t += (a.seg[s].ncols + bn - 1) / bn;
+  return t;
+}
+
 int choose_tile_n(int et, const GemmArgs& a) {
   const long cus = a.num_cu > 0 ? a.num_cu : 256;
-  const long rowtiles = (a.M + BM - 1) / BM;
+  const long rowtiles = (a.M + 127) / 128;
   const long slots = 2 * cus;
   int best = 128;
   long best_cost = -1;
   const bool stage2 = wide_ok(et, a);
   for (int bn : {192, 128, 96}) {
     if (bn == 192 && !stage2) continue;
-    long tiles = 0;
-    for (int s = 0; s < a.nseg; ++s) tiles += rowtiles * ((a.seg[s].ncols + bn - 1) / bn);
+    const long tiles = rowtiles * col_tiles(a, bn);
     const long cost = ((tiles + slots - 1) / slots) * (bn + 48);
     if (best_cost < 0 || cost < best_cost) {
       best_cost = cost;
@@ -555,7 +600,22 @@ int choose_tile_n(int et, const GemmArgs& a) {
   return best;
 }
 
-template <int BN>
+// 256-row tiles (one 512-thread workgroup per compute unit) halve the W tile
+// traffic per output; they exist for 2-byte operands at 128 or 192 columns
+// and are taken at 192 columns (at 128 they measured slower) when they need
+// no more rounds than 128-row tiles and give every compute unit a tile.
+bool tall_ok(int et, int bn) { return et != ET_F32 && (bn == 128 || bn == 192); }
+
+int choose_tile_m(int et, const GemmArgs& a, int bn) {
+  if (!tall_ok(et, bn) || bn != 192) return 128;
+  const long cus = a.num_cu > 0 ? a.num_cu : 256;
+  const long ct = col_tiles(a, bn);
+  const long t128 = (a.M + 127) / 128 * ct, t256 = (a.M + 255) / 256 * ct;
+  const long r128 = (t128 + 2 * cus - 1) / (2 * cus), r256 = (t256 + cus - 1) / cus;
+  return t256 >= cus && r256 <= r128 ? 256 : 128;
+}
+
+template <int BN, int BM>
 hipError_t launch_gemm_bn(int et, GemmArgs& a, hipStream_t stream, const LaunchTiming* t) {
   a.ncoltiles = 0;
   for (int s = 0; s < a.nseg; ++s) {
@@ -563,20 +623,34 @@ hipError_t launch_gemm_bn(int et, GemmArgs& a, hipStream_t stream, const LaunchT
     a.ncoltiles += a.seg[s].ntiles;
   }
   const int rowtiles = (a.M + BM - 1) / BM;
-  const dim3 grid((unsigned)(rowtiles * a.ncoltiles)), block(NTHR);
+  const dim3 grid((unsigned)(rowtiles * a.ncoltiles)), block(2 * BM);
+  a.warm = a.ncoltiles > 8 ? 1 : 0;  // the L2 warm-up measured faster at 9 column tiles, slower at 4 and 8
   const int zb = (a.nz + 15) / 16;
-  if constexpr (BN == 192) {  // (never with more than 16 heads)
-    if (zb == 0) return launch_k(gemm_xw_kernel<ET_BF16, BN, 0>, grid, block, 0, stream, t, a);
-    return launch_k(gemm_xw_kernel<ET_BF16, BN, 1>, grid, block, 0, stream, t, a);
-  } else {
-    if (et == ET_F32) {
-      if (zb == 0) return launch_k(gemm_xw_kernel<ET_F32, BN, 0>, grid, block, 0, stream, t, a);
-      if (zb == 1) return launch_k(gemm_xw_kernel<ET_F32, BN, 1>, grid, block, 0, stream, t, a);
-      return launch_k(gemm_xw_kernel<ET_F32, BN, 2>, grid, block, 0, stream, t, a);
+  const bool tr = a.nz % 4 == 0;
+  if (et == ET_F32) {
+    if constexpr (BN == 192 || BM == 256) {  // 2-byte operands only
+      return hipErrorInvalidValue;
+    } else {
+      if (zb == 0) return launch_k(gemm_xw_kernel<ET_F32, BN, 0, BM>, grid, block, 0, stream, t, a);
+      if (zb == 1) return launch_k(gemm_xw_kernel<ET_F32, BN, 1, BM>, grid, block, 0, stream, t, a);
+      return launch_k(gemm_xw_kernel<ET_F32, BN, 2, BM>, grid, block, 0, stream, t, a);
     }
-    if (zb == 0) return launch_k(gemm_xw_kernel<ET_BF16, BN, 0>, grid, block, 0, stream, t, a);
-    if (zb == 1) return launch_k(gemm_xw_kernel<ET_BF16, BN, 1>, grid, block, 0, stream, t, a);
-    return launch_k(gemm_xw_kernel<ET_BF16, BN, 2>, grid, block, 0, stream, t, a);
+  }
+  if (zb == 0) return launch_k(gemm_xw_kernel<ET_BF16, BN, 0, BM>, grid, block, 0, stream, t, a);
+  // 128 x 192 tiles never carry the score projection, 256 x 192 ones at most
+  // 16 heads
+  if constexpr (BN == 192 && BM == 128) {
+    return hipErrorInvalidValue;
+  } else {
+    if (zb == 1)
+      return tr ? launch_k(gemm_xw_kernel<ET_BF16, BN, 1, BM, true>, grid, block, 0, stream, t, a)
+                : launch_k(gemm_xw_kernel<ET_BF16, BN, 1, BM, false>, grid, block, 0, stream, t, a);
+    if constexpr (BN == 192) {
+      return hipErrorInvalidValue;
+    } else {
+      return tr ? launch_k(gemm_xw_kernel<ET_BF16, BN, 2, BM, true>, grid, block, 0, stream, t, a)
+                : launch_k(gemm_xw_kernel<ET_BF16, BN, 2, BM, false>, grid, block, 0, stream, t, a);
+    }
   }
 }
 
@@ -596,9 +670,19 @@ hipError_t launch_gemm(int et, GemmArgs a, hipStream_t stream, const LaunchTimin
   }
   int bn = a.tile_n ? a.tile_n : choose_tile_n(et, a);
   if (bn == 192 && !wide_ok(et, a)) bn = choose_tile_n(et, a);
-  if (bn == 96) return launch_gemm_bn<96>(et, a, stream, t);
-  if (bn == 128) return launch_gemm_bn<128>(et, a, stream, t);
-  if (bn == 192) return launch_gemm_bn<192>(et, a, stream, t);
+  int bm = a.tile_m ? a.tile_m : choose_tile_m(et, a, bn);
+  if (bm == 256 && !tall_ok(et, bn)) bm = 128;
+  // with W_A rows in every stage, two 128 x 192 workgroups no longer fit a
+  // compute unit's LDS
+  if (bn == 192 && bm == 128 && a.nz > 0) bn = 128;
+  if (bm == 256) {
+    if (bn == 128) return launch_gemm_bn<128, 256>(et, a, stream, t);
+    if (bn == 192) return launch_gemm_bn<192, 256>(et, a, stream, t);
+    return hipErrorInvalidValue;
+  }
+  if (bn == 96) return launch_gemm_bn<96, 128>(et, a, stream, t);
+  if (bn == 128) return launch_gemm_bn<128, 128>(et, a, stream, t);
+  if (bn == 192) return launch_gemm_bn<192, 128>(et, a, stream, t);
   return hipErrorInvalidValue;
 }
 

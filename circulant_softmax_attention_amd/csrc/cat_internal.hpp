@@ -86,10 +86,12 @@ struct GemmArgs {
   float* z;
   int nz;
   int tile_n;  // output tile width (96, 128 or 192); 0 lets the launcher choose
+  int tile_m;  // output tile rows (128 or 256); 0 lets the launcher choose
   FastDiv fd_nz;  // filled by the launcher
   int num_cu;  // compute units of the device (0: assume 256)
   // filled by the launcher
   int ncoltiles;
+  int warm;  // 1: the GEMM warms L2 with each row panel's X first
   FastDiv fd_ntok, fd_d;
   GemmSeg seg[3];
 };

@@ -64,11 +64,13 @@
  * failure.  Setting the environment variable CAT_DEBUG_SYNC=1 makes every
  * launch synchronise and check for asynchronous errors.
  *
- * Tuning: the projection GEMM picks its output tile width (96, 128 or 192
- * columns) from the problem; CAT_GEMM_TILE_N=96|128|192, read when a plan is
- * created, forces one for that plan's calls (192 only where the GEMM's staged
- * 2-byte epilogue applies; elsewhere the choice falls back to the default).
- * It changes speed, never results beyond rounding order.
+ * Tuning: the projection GEMM picks its output tile (128 or 256 rows by 96,
+ * 128 or 192 columns) from the problem; CAT_GEMM_TILE_N=96|128|192 and
+ * CAT_GEMM_TILE_M=128|256, read when a plan is created, force a width or a
+ * height for that plan's calls (192 columns only where the GEMM's staged
+ * 2-byte epilogue applies, 256 rows only with 2-byte operands and 128 or 192
+ * columns; elsewhere the choice falls back to an allowed one).  They change
+ * speed, never results beyond rounding order.
  */
 #ifndef CAT_H_
 #define CAT_H_

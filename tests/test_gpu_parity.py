@@ -66,16 +66,22 @@ def test_project_1d(cat, B, N, D, H, dtype):
     assert_parity(to_np(z), oracle.scores_1d(inp.X, inp.W_A), "f32", "z")
 
 
+@pytest.mark.parametrize("tile_m", [128, 256])
 @pytest.mark.parametrize("tile_n", [96, 128, 192])
 @pytest.mark.parametrize("B,N,D,H,dtype", [(2, 300, 264, 12, "bf16"), (1, 200, 200, 25, "bf16"),
+                                           (2, 300, 264, 6, "bf16"), (1, 520, 256, 16, "bf16"),
                                            (3, 130, 136, 17, "f32")])
-def test_project_tile_widths(cat, monkeypatch, tile_n, B, N, D, H, dtype):
-    """Every output tile width of the projection GEMM (forced through the
-    tuning variable), with ragged rows, a K tail, several column tiles and
-    one or two 16-head blocks of the score projection.  192-wide tiles do not
-    apply to fp32 operands; the launcher then falls back to its own choice."""
-    say("project_tile", tile_n, B, N, D, H, dtype)
+def test_project_tile_widths(cat, monkeypatch, tile_m, tile_n, B, N, D, H, dtype):
+    """Every output tile shape of the projection GEMM (forced through the
+    tuning variables), with ragged rows, a K tail, several column tiles and
+    one or two 16-head blocks of the score projection, whose W_A rows are
+    read transposed (heads a multiple of 4) or one value at a time.  Shapes a
+    case does not allow (192 columns or 256 rows with fp32 operands, 96
+    columns with 256 rows, 128 x 192 with the score projection) fall back to
+    an allowed one."""
+    say("project_tile", tile_m, tile_n, B, N, D, H, dtype)
     monkeypatch.setenv("CAT_GEMM_TILE_N", str(tile_n))
+    monkeypatch.setenv("CAT_GEMM_TILE_M", str(tile_m))
     inp = rng_inputs(17, B, N, D, H, dtype)
     plan = cat.cat_plan_create("1d", dtype, B, N, D, H)
     V, z = cat.cat_step_project(plan, to_dev(inp.X, dtype), to_dev(inp.W_A, dtype), to_dev(inp.W_V, dtype))
@@ -85,12 +91,14 @@ def test_project_tile_widths(cat, monkeypatch, tile_n, B, N, D, H, dtype):
     assert_parity(to_np(z), oracle.scores_1d(inp.X, inp.W_A), "f32", "z")
 
 
+@pytest.mark.parametrize("tile_m", [128, 256])
 @pytest.mark.parametrize("tile_n", [96, 128, 192])
-def test_forward_1d_tile_widths(cat, monkeypatch, tile_n):
-    """The whole 1D path (blocked value layout) at every GEMM tile width."""
+def test_forward_1d_tile_widths(cat, monkeypatch, tile_m, tile_n):
+    """The whole 1D path (blocked value layout) at every GEMM tile shape."""
     B, N, D, H, dtype = 2, 160, 384, 6, "bf16"
-    say("forward_tile", tile_n, B, N, D, H, dtype)
+    say("forward_tile", tile_m, tile_n, B, N, D, H, dtype)
     monkeypatch.setenv("CAT_GEMM_TILE_N", str(tile_n))
+    monkeypatch.setenv("CAT_GEMM_TILE_M", str(tile_m))
     inp = rng_inputs(19, B, N, D, H, dtype)
     plan = cat.cat_plan_create("1d", dtype, B, N, D, H)
     O = cat.cat_forward_1d(plan, to_dev(inp.X, dtype), to_dev(inp.W_A, dtype), to_dev(inp.W_V, dtype))

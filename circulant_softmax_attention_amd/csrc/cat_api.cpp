@@ -42,6 +42,8 @@ struct cat_plan_s {
   hipStream_t side = nullptr;
   hipEvent_t fork_ev = nullptr, join_ev = nullptr;
   size_t off_A, off_zc, off_Az;  // long path scratch
+  size_t off_A2;                 // long path: the second values transform of the score gradient
+  int Kp;                        // B N rounded up to 8: the padded K of the weight-gradient product
   size_t off_xpart, off_kbar, off_weff;  // averaged-key logits scratch (1D)
   size_t fwd_ws_bytes;  // workspace bytes the 1D forward itself touches (a prefix of the layout)
   bool debug_sync;
@@ -296,31 +298,8 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
   if (p->kind == CAT_1D) {
     pl->off_z = off;
     off = up256(off + BH * p->N * sizeof(float));
-    pl->off_Q = pl->off_K = pl->off_part = pl->off_psum = 0;
+    pl->off_Q = pl->off_K = pl->off_part = pl->off_psum = pl->off_A2 = 0;
     pl->fwd_ws_bytes = off;  // V, spectrum, logits (the long path adds its scratch below)
-    if (!longn) {
-      // the mixing backward: V in the blocked layout, the score-gradient
-      // partials and their sum
-      pl->off_Q = off;
-      off = up256(off + BND * pl->esz);
-      pl->off_part = off;
-      off = up256(off + BH * pl->ngrp * pl->L * sizeof(float2));
-      pl->off_psum = off;
-      off = up256(off + BH * pl->L * sizeof(float2));
-      // the whole backward: V and z recomputed, dV and dz, W_V^T, dX in
-      // fp32, X^T, dz token-major (padded to Hp heads) and dW_A padded
-      const size_t Dz = (size_t)p->D, BN = (size_t)p->B * p->N;
-      pl->Hp = (int)((p->H + 7) / 8 * 8);
-      const size_t sizes[9] = {BH * p->N * sizeof(float), BND * pl->esz, BND * pl->esz, BH * p->N * sizeof(float),
-                               Dz * Dz * pl->esz, BND * sizeof(float), BND * pl->esz,
-                               BN * pl->Hp * pl->esz, Dz * pl->Hp * pl->esz};
-      size_t* offs[9] = {&pl->off_bz, &pl->off_bV, &pl->off_bdV, &pl->off_bdz, &pl->off_bWt,
-                         &pl->off_bdXf, &pl->off_bXt, &pl->off_bP, &pl->off_bdW};
-      for (int i = 0; i < 9; ++i) {
-        *offs[i] = off;
-        off = up256(off + sizes[i]);
-      }
-    }
     if (longn) {
       pl->off_A = off;
       off = up256(off + BH * (size_t)d2 * pl->L * sizeof(float2));
@@ -329,6 +308,38 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
       pl->off_Az = off;
       off = up256(off + BH * pl->L * sizeof(float2));
       pl->fwd_ws_bytes = off;
+    }
+    // the mixing backward: V in the blocked layout, then the score-gradient
+    // partials and their sum (single-workgroup lines) or the second values
+    // transform (the long path, whose cross-spectrum line reuses Az and
+    // whose correlation line reuses zc)
+    pl->off_Q = off;
+    off = up256(off + BND * pl->esz);
+    if (!longn) {
+      pl->off_part = off;
+      off = up256(off + BH * pl->ngrp * pl->L * sizeof(float2));
+      pl->off_psum = off;
+      off = up256(off + BH * pl->L * sizeof(float2));
+    } else {
+      pl->off_A2 = off;
+      off = up256(off + BH * (size_t)d2 * pl->L * sizeof(float2));
+    }
+    // the whole backward: V and z recomputed, dV and dz, W_V^T, dX in fp32,
+    // X^T (B N padded to Kp columns), dz token-major (padded to Hp heads) and
+    // dW_A padded
+    {
+      const size_t Dz = (size_t)p->D, BN = (size_t)p->B * p->N;
+      pl->Hp = (int)((p->H + 7) / 8 * 8);
+      pl->Kp = (int)((BN + 7) / 8 * 8);
+      const size_t sizes[9] = {BH * p->N * sizeof(float), BND * pl->esz, BND * pl->esz, BH * p->N * sizeof(float),
+                               Dz * Dz * pl->esz, BND * sizeof(float), Dz * (size_t)pl->Kp * pl->esz,
+                               BN * pl->Hp * pl->esz, Dz * pl->Hp * pl->esz};
+      size_t* offs[9] = {&pl->off_bz, &pl->off_bV, &pl->off_bdV, &pl->off_bdz, &pl->off_bWt,
+                         &pl->off_bdXf, &pl->off_bXt, &pl->off_bP, &pl->off_bdW};
+      for (int i = 0; i < 9; ++i) {
+        *offs[i] = off;
+        off = up256(off + sizes[i]);
+      }
     }
     // the averaged-key logits: column-sum partials, mean key, score weights
     pl->off_xpart = off;
@@ -410,7 +421,7 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
   }
 
 
-  if (p->kind == CAT_1D && !longn) {
+  if (p->kind == CAT_1D) {  // the backward's weight-gradient branch
     hipError_t se = hipStreamCreateWithFlags(&pl->side, hipStreamNonBlocking);
     if (se == hipSuccess) se = hipEventCreateWithFlags(&pl->fork_ev, hipEventDisableTiming);
     if (se == hipSuccess) se = hipEventCreateWithFlags(&pl->join_ev, hipEventDisableTiming);
@@ -699,6 +710,17 @@ cat_status mix_backward_core(cat_plan plan, const float* logits, const void* V, 
   ra.d = plan->d;
   ra.cg = plan->cg;
   if ((e = launch_relayout(ra, s, mk_at(mk, 4))) != hipSuccess) return hip_fail(e, "relayout launch");
+  if (plan->longn) {
+    // the cross-correlation spectra of every pair of a head summed before
+    // one inverse transform (three passes), then dlogits
+    e = launch_long_scoregrad(plan->et, long_base(plan), logits, dOb, Vb,
+                              reinterpret_cast<float2*>(ws_at(workspace, plan->off_A)),
+                              reinterpret_cast<float2*>(ws_at(workspace, plan->off_A2)),
+                              reinterpret_cast<float2*>(ws_at(workspace, plan->off_Az)),
+                              reinterpret_cast<float*>(ws_at(workspace, plan->off_zc)), dlogits, s, mk_at(mk, 5));
+    if (e != hipSuccess) return hip_fail(e, "long score-gradient launch");
+    return check_sync(plan, "mixing backward");
+  }
   ScoreArgs sc{};
   sc.Q = dOb;
   sc.K = Vb;
@@ -741,12 +763,13 @@ cat_status backward_branches(cat_plan plan, const void* X, const void* W_A, cons
   void* bXt = ws_at(workspace, plan->off_bXt);
   void* bdzt = ws_at(workspace, plan->off_bP);
   void* bdWA = ws_at(workspace, plan->off_bdW);
-  if ((e = launch_transpose(et, X, bXt, B * N, D, sw)) != hipSuccess) return hip_fail(e, "transpose launch");
+  if ((e = launch_transpose(et, X, bXt, B * N, D, plan->Kp, sw)) != hipSuccess) return hip_fail(e, "transpose launch");
   if ((e = launch_pack_grads(et, nullptr, bdz, bdzt, B, N, 0, H, plan->Hp, sw)) != hipSuccess)
     return hip_fail(e, "pack launch");
   GemmArgs gw = gemm_base(plan, bXt);
   gw.M = D;
   gw.K = B * N;
+  gw.ldx = plan->Kp;  // X^T rows padded to 16-byte multiples (zero past B N)
   gw.nseg = 2;
   gw.seg[0] = seg(bdV, dW_V, D, 0, OUT_ROWMAJOR, 1);
   gw.seg[1] = seg(bdzt, bdWA, plan->Hp, 0, OUT_ROWMAJOR, 1);
@@ -755,7 +778,7 @@ cat_status backward_branches(cat_plan plan, const void* X, const void* W_A, cons
   // dX = dV W_V^T (fp32), then + dz^T W_A^T in the storage dtype
   void* bWt = ws_at(workspace, plan->off_bWt);
   float* bdXf = reinterpret_cast<float*>(ws_at(workspace, plan->off_bdXf));
-  if ((e = launch_transpose(et, W_V, bWt, D, D, s)) != hipSuccess) return hip_fail(e, "transpose launch");
+  if ((e = launch_transpose(et, W_V, bWt, D, D, D, s)) != hipSuccess) return hip_fail(e, "transpose launch");
   GemmArgs gx = gemm_base(plan, bdV);
   gx.nseg = 1;
   gx.seg[0] = seg(bWt, bdXf, D, 1, OUT_ROWMAJOR, 1);
@@ -1158,8 +1181,6 @@ cat_status cat_step_mix_backward_1d(cat_plan plan, const float* logits, const vo
   if (plan->p.B == 0) return CAT_OK;
   cat_status st = check_ptrs({logits, V, dO, dlogits, dV, workspace});
   if (st != CAT_OK) return st;
-  if (plan->longn)
-    return fail(CAT_ERR_UNSUPPORTED, "the mixing backward covers single-workgroup lines (not the multi-pass path)");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   KernelMark mk(plan);
   return mix_backward_core(plan, logits, V, dO, dlogits, dV, workspace, s, &mk);
@@ -1169,14 +1190,18 @@ cat_status cat_backward_1d(cat_plan plan, const void* X, const void* W_A, const 
                            void* dW_A, void* dW_V, void* workspace, void* stream) {
   if (!plan) return fail(CAT_ERR_INVALID_ARG, "NULL plan");
   if (plan->p.kind != CAT_1D) return fail(CAT_ERR_PLAN_MISMATCH, "plan is not 1D");
-  cat_status st = check_ptrs({X, W_A, W_V, dO, dX, dW_A, dW_V, workspace});
-  if (st != CAT_OK) return st;
-  if (plan->longn)
-    return fail(CAT_ERR_UNSUPPORTED, "the backward covers single-workgroup lines (not the multi-pass path)");
-  const int B = (int)plan->p.B, N = (int)plan->p.N, D = (int)plan->p.D, H = (int)plan->p.H;
-  if (B == 0 || (B * N) % 8 != 0)
-    return fail(CAT_ERR_UNSUPPORTED, "the weight gradients need B*N >= 8 and a multiple of 8 (X^T rows in 16-byte chunks)");
+  const int B = (int)plan->p.B, D = (int)plan->p.D, H = (int)plan->p.H;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  cat_status st;
+  if (B == 0) {
+    // an empty batch: the weight gradients are empty sums
+    if ((st = check_ptrs({dW_A, dW_V})) != CAT_OK) return st;
+    hipError_t e = launch_zero(dW_A, (size_t)D * H * plan->esz, s);
+    if (e == hipSuccess) e = launch_zero(dW_V, (size_t)D * D * plan->esz, s);
+    if (e != hipSuccess) return hip_fail(e, "zero launch");
+    return check_sync(plan, "backward");
+  }
+  if ((st = check_ptrs({X, W_A, W_V, dO, dX, dW_A, dW_V, workspace})) != CAT_OK) return st;
   const int et = plan->et;
   void* bV = ws_at(workspace, plan->off_bV);
   float* bz = reinterpret_cast<float*>(ws_at(workspace, plan->off_bz));

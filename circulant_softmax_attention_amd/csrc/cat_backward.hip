@@ -29,23 +29,24 @@ __device__ __forceinline__ void st_elem(void* p, size_t i, float v) {
     reinterpret_cast<uint16_t*>(p)[i] = to_bf16(v);
 }
 
-// dst [C][R] = src [R][C]^T, storage dtype, 32 x 32 tiles through LDS (one
-// workgroup per tile, 1D grid of tiles).
+// dst [C][ldd] = src [R][C]^T, storage dtype, with dst columns R .. ldd - 1
+// zero; 32 x 32 tiles through LDS (one workgroup per tile, 1D grid of tiles
+// over ldd x C).
 template <int ET>
 __global__ __launch_bounds__(256) void transpose_kernel(const void* __restrict__ src, void* __restrict__ dst, int R,
-                                                        int C) {
+                                                        int C, int ldd) {
   __shared__ float tile[32][33];
   const int tcs = (C + 31) / 32;
   const int tr = blockIdx.x / tcs, tc = blockIdx.x - tr * tcs;
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
   for (int k = ty; k < 32; k += 8) {
     const int r = tr * 32 + k, c = tc * 32 + tx;
-    if (r < R && c < C) tile[k][tx] = ld_elem<ET>(src, (size_t)r * C + c);
+    if (c < C) tile[k][tx] = r < R ? ld_elem<ET>(src, (size_t)r * C + c) : 0.f;
   }
   __syncthreads();
   for (int k = ty; k < 32; k += 8) {
     const int c = tc * 32 + k, r = tr * 32 + tx;
-    if (r < R && c < C) st_elem<ET>(dst, (size_t)c * R + r, tile[tx][k]);
+    if (r < ldd && c < C) st_elem<ET>(dst, (size_t)c * ldd + r, tile[tx][k]);
   }
 }
 
@@ -119,14 +120,26 @@ __global__ __launch_bounds__(256) void take_cols_kernel(const void* __restrict__
 
 unsigned blocks_for(size_t n) { return (unsigned)((n + 255) / 256); }
 
+// Zero n bytes at p (16-byte aligned): 16-byte stores, then the byte tail.
+__global__ __launch_bounds__(256) void zero_kernel(unsigned char* __restrict__ p, size_t n) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (16 * i + 16 <= n) {
+    reinterpret_cast<uint4*>(p)[i] = make_uint4(0u, 0u, 0u, 0u);
+  } else {
+    for (size_t b = 16 * i; b < n; ++b) p[b] = 0;
+  }
+}
+
 }  // namespace
 
-hipError_t launch_transpose(int et, const void* src, void* dst, int R, int C, hipStream_t s, const LaunchTiming* t) {
-  if (R < 1 || C < 1) return hipErrorInvalidValue;
-  const size_t tiles = (size_t)((R + 31) / 32) * ((C + 31) / 32);
+hipError_t launch_transpose(int et, const void* src, void* dst, int R, int C, int ldd, hipStream_t s,
+                            const LaunchTiming* t) {
+  if (R < 1 || C < 1 || ldd < R) return hipErrorInvalidValue;
+  const size_t tiles = (size_t)((ldd + 31) / 32) * ((C + 31) / 32);
   if (tiles > 0x7fffffffu) return hipErrorInvalidValue;
-  return et == ET_F32 ? launch_k(transpose_kernel<ET_F32>, dim3((unsigned)tiles), dim3(256), 0, s, t, src, dst, R, C)
-                      : launch_k(transpose_kernel<ET_BF16>, dim3((unsigned)tiles), dim3(256), 0, s, t, src, dst, R, C);
+  return et == ET_F32 ? launch_k(transpose_kernel<ET_F32>, dim3((unsigned)tiles), dim3(256), 0, s, t, src, dst, R, C, ldd)
+                      : launch_k(transpose_kernel<ET_BF16>, dim3((unsigned)tiles), dim3(256), 0, s, t, src, dst, R, C,
+                                 ldd);
 }
 
 hipError_t launch_pack_grads(int et, const void* dV, const float* dz, void* P, int B, int N, int D, int H, int Hp,
@@ -146,6 +159,13 @@ hipError_t launch_rank_heads_add(int et, const float* dXf, const float* dz, cons
              ? launch_k(rank_heads_add_kernel<ET_F32>, dim3((unsigned)nb), dim3(256), 0, s, t, dXf, dz, W_A, dX, B, N, D, H)
              : launch_k(rank_heads_add_kernel<ET_BF16>, dim3((unsigned)nb), dim3(256), 0, s, t, dXf, dz, W_A, dX, B, N, D,
                         H);
+}
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s, const LaunchTiming* t) {
+  if (bytes == 0) return hipSuccess;
+  const size_t nb = blocks_for((bytes + 15) / 16);
+  if (nb > 0x7fffffffu) return hipErrorInvalidValue;
+  return launch_k(zero_kernel, dim3((unsigned)nb), dim3(256), 0, s, t, reinterpret_cast<unsigned char*>(p), bytes);
 }
 
 hipError_t launch_take_cols(int et, const void* src, void* dst, int R, int Cs, int Cd, hipStream_t s,

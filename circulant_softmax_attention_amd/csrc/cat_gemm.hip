@@ -167,6 +167,7 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void gemm_xw_kernel(GemmArgs a) {
   const GemmSeg sg = a.seg[si];
   const int m0 = rt * BM, n0 = ct * BN;
   const int M = a.M, K = a.K, ncols = sg.ncols;
+  const int ldx = a.ldx > 0 ? a.ldx : K;  // X row pitch (elements)
 
   // Score projection (first segment only): the first nct <= BM / 16 column
   // tiles of a row panel share its BM / 16 16-row blocks, block rb going to
@@ -191,7 +192,7 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void gemm_xw_kernel(GemmArgs a) {
   for (int i = 0; i < 4; ++i) {
     const int r = (tid >> 3) + (NTHR / 8) * i;
     const int am = m0 + r < M ? m0 + r : M - 1;
-    asrc[i] = reinterpret_cast<const elem_t*>(a.X) + (size_t)am * K + kch;
+    asrc[i] = reinterpret_cast<const elem_t*>(a.X) + (size_t)am * ldx + kch;
   }
   // W tile, K-major as W is stored: slot s = tid + 256 i is K row s / CPRB,
   // position s % CPRB, and holds column chunk (position - rot(row)) mod CPRB.
@@ -414,13 +415,13 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void gemm_xw_kernel(GemmArgs a) {
     const int rows = M - m0 < BM ? M - m0 : BM;
     const uint32_t spr = (uint32_t)(K * ESZ + 63) / 64;  // sectors per row
     const uint32_t nsec = (uint32_t)rows * spr;
-    const char* xb = reinterpret_cast<const char*>(a.X) + (size_t)m0 * K * ESZ;
+    const char* xb = reinterpret_cast<const char*>(a.X) + (size_t)m0 * ldx * ESZ;
 #pragma unroll
     for (int u = 0; u < WARM; ++u) {
       uint32_t sidx = (uint32_t)ctg + (uint32_t)a.ncoltiles * (uint32_t)(tid + NTHR * u);
       sidx = sidx < nsec ? sidx : nsec - 1;
       const uint32_t r = sidx / spr, c = sidx - r * spr;
-      wv[u] = *reinterpret_cast<const uint32_t*>(xb + (size_t)r * K * ESZ + (size_t)c * 64);
+      wv[u] = *reinterpret_cast<const uint32_t*>(xb + (size_t)r * ldx * ESZ + (size_t)c * 64);
     }
   }
   uint4 af[4], bf[TN];
@@ -661,6 +662,7 @@ hipError_t launch_gemm(int et, GemmArgs a, hipStream_t stream, const LaunchTimin
   a.fd_d = make_fastdiv((uint32_t)a.d);
   a.fd_nz = make_fastdiv((uint32_t)(a.nz > 0 ? a.nz : 1));
   if (a.nz < 0 || a.nz > ZMAX || (a.nz > 0 && (a.Wz == nullptr || a.z == nullptr))) return hipErrorInvalidValue;
+  if (a.ldx != 0 && (a.ldx < a.K || a.ldx % (et == ET_F32 ? 4 : 8) != 0)) return hipErrorInvalidValue;
   for (int s = 0; s < a.nseg; ++s)
     if (a.seg[s].ncols % (et == ET_F32 ? 4 : 8) != 0) return hipErrorInvalidValue;  // whole 16-byte column chunks
   for (int s = 0; s < a.nseg; ++s) {

@@ -76,8 +76,9 @@ struct GemmSeg {
 };
 
 struct GemmArgs {
-  const void* X;  // [M][K] row-major
+  const void* X;  // [M][K] row-major, rows ldx elements apart
   int M, K;
+  int ldx;  // X row pitch in elements, a multiple of 16 bytes (0: K)
   int Ntok, H, d;
   int nseg;
   // optional score projection (1D): z [M / Ntok][nz][Ntok] fp32 = X . Wz,
@@ -186,16 +187,19 @@ hipError_t launch_dconv(int et, const ConvArgs& a, hipStream_t s, const LaunchTi
 hipError_t launch_score_partial(const LineGeom& g, const ScoreArgs& a, hipStream_t s,
                                 const LaunchTiming* t = nullptr);
 // Projection-gradient helpers of the CAT backward (cat_backward.hip), storage
-// dtype et: dst [C][R] = src [R][C]^T; P [B N][D + Hp] = [dV | dz token-major
-// | 0] (Hp >= H; D = 0: the dz block alone, dV unused); dX = dXf + dz^T W_A^T
-// (W_A [D][H], H <= 32);
+// dtype et: dst [C][ldd] = src [R][C]^T with columns R .. ldd - 1 zero;
+// P [B N][D + Hp] = [dV | dz token-major | 0] (Hp >= H; D = 0: the dz block
+// alone, dV unused); dX = dXf + dz^T W_A^T (W_A [D][H], H <= 32);
 // dst [R][Cd] = the first Cd columns of src [R][Cs].
-hipError_t launch_transpose(int et, const void* src, void* dst, int R, int C, hipStream_t s,
+hipError_t launch_transpose(int et, const void* src, void* dst, int R, int C, int ldd, hipStream_t s,
                             const LaunchTiming* t = nullptr);
 hipError_t launch_pack_grads(int et, const void* dV, const float* dz, void* P, int B, int N, int D, int H, int Hp,
                              hipStream_t s, const LaunchTiming* t = nullptr);
 hipError_t launch_rank_heads_add(int et, const float* dXf, const float* dz, const void* W_A, void* dX, int B, int N,
                                  int D, int H, hipStream_t s, const LaunchTiming* t = nullptr);
+// Zero `bytes` bytes at p (16-byte aligned) with a kernel (no memset node in
+// captured graphs).
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s, const LaunchTiming* t = nullptr);
 hipError_t launch_take_cols(int et, const void* src, void* dst, int R, int Cs, int Cd, hipStream_t s,
                             const LaunchTiming* t = nullptr);
 // zr[bh][k] = z[bh][(N - k) mod N] for BH lines of N fp32 values.
@@ -220,6 +224,19 @@ struct LongArgs {
 // fp32 scratch, O [B][N][D]).  t: six timing slots or null.
 hipError_t launch_longconv(int et, const LongArgs& a, const float* logits, const void* V, float2* zc, float2* Az,
                            float2* S, float2* A, void* O, hipStream_t s, const LaunchTiming* const* t = nullptr);
+// The score gradient of the long path (mixing backward): with dOb and Vb in
+// the blocked layout of the values (2 pb-channel groups),
+//   dz*[bh][k] = sum over the head's channels c and tokens i of
+//                dO_c[i] V_c[(i - k) mod N]
+// as the real part of IDFT_L(sum over pairs of DFT(dO pair) conj DFT(V pair))
+// / L (folded onto mod N on a padded circle), then
+//   dlogits = z* (dz* - <z*, dz*>),  z* = softmax(logits).
+// Ad, Av: [BH d/2][L] complex fp32 scratch; R: [BH][L] complex fp32
+// scratch; c: [BH][L] fp32 scratch; dlogits [BH][N] fp32.  t: one timing
+// slot for every launch, or null.
+hipError_t launch_long_scoregrad(int et, const LongArgs& a, const float* logits, const void* dOb, const void* Vb,
+                                 float2* Ad, float2* Av, float2* R, float* c, float* dlogits, hipStream_t s,
+                                 const LaunchTiming* t = nullptr);
 // 2D: out[bh][k] = sum over g of part[bh][g][k] (partials [BH][ngrp][L],
 // out [BH][L], complex fp32; summed in order g = 0, 1, ..).
 hipError_t launch_psum(const float2* part, float2* out, int BH, int ngrp, int L, hipStream_t s,

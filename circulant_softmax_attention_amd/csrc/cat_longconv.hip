@@ -521,6 +521,179 @@ __global__ __launch_bounds__(LTHR) void col_inv_kernel(LongArgs a, int PB, const
   }
 }
 
+
+// ---- score gradient (mixing backward).  The circular cross-correlation
+// of two complex lines p, q is IDFT(DFT(p) conj DFT(q)) / L:
+//   r[m] = sum_i p[i] conj(q[i - m]),
+// and with p = a + i b, q = c + i d (two real channels each) its real part
+// is sum_i a[i] c[i - m] + b[i] d[i - m], the correlation summed over both
+// channels of the pair.  Summing the products over every pair of a head
+// before one inverse transform gives the head's dz* line.
+//
+// Row pass: RB rows k1 of head bh per workgroup, all pair blocks in turn:
+// the forward DFT over n2 of the rows of Ad (kept) and of Av, the products
+// Ad conj(Av) summed over the pairs into acc, and at the end the inverse DFT
+// over k2 of the RB summed rows:  R[bh][k1][n2].
+__global__ __launch_bounds__(LTHR) void row_xcorr_kernel(LongArgs a, int PB, const float2* __restrict__ Ad,
+                                                         const float2* __restrict__ Av, float2* __restrict__ R) {
+  __shared__ float2 buf[2][LPAD];
+  __shared__ float2 keep[LPAD];
+  __shared__ float2 acc[LBUF];
+  __shared__ float2 tws[LMAXM];
+  const int L1 = 1 << a.logL1, L2 = 1 << a.logL2, L = L1 * L2;
+  const int RB = LBUF / (PB * L2) < L1 ? LBUF / (PB * L2) : L1, Rn = RB * PB;
+  const int nblk = L1 / RB;
+  const int bh = blockIdx.x / nblk, k10 = (blockIdx.x - bh * nblk) * RB;
+  const int groups = a.pairs / PB;
+  const int P2 = L2 + 1, RL = L2 * PB;
+  for (int q = threadIdx.x; q < RB * L2; q += LTHR) acc[q] = make_float2(0.f, 0.f);
+  stage_twiddles(tws, a.logL2, a.tw, a.logL1 + a.logL2);
+  for (int g = 0; g < groups; ++g) {
+    const size_t base = (((size_t)bh * groups + g) * L + (size_t)k10 * L2) * PB;  // RB contiguous rows
+    for (int q = threadIdx.x; q < RB * RL; q += LTHR) {
+      const int rr = q / RL, rem = q - rr * RL, n2 = rem / PB, j = rem - n2 * PB;
+      buf[0][(rr * PB + j) * P2 + n2] = Ad[base + q];
+    }
+    const float2* X = lds_fft<false>(buf[0], buf[1], L2, a.logL2, Rn, tws);
+    for (int q = threadIdx.x; q < Rn * L2; q += LTHR) {
+      const int r = q >> a.logL2, k2 = q & (L2 - 1);
+      keep[r * P2 + k2] = X[r * P2 + k2];
+    }
+    __syncthreads();  // X (possibly buf[0]) is consumed before buf[0] is refilled
+    for (int q = threadIdx.x; q < RB * RL; q += LTHR) {
+      const int rr = q / RL, rem = q - rr * RL, n2 = rem / PB, j = rem - n2 * PB;
+      buf[0][(rr * PB + j) * P2 + n2] = Av[base + q];
+    }
+    const float2* Y = lds_fft<false>(buf[0], buf[1], L2, a.logL2, Rn, tws);
+    for (int q = threadIdx.x; q < RB * L2; q += LTHR) {
+      const int rr = q >> a.logL2, k2 = q & (L2 - 1);
+      float2 sum = acc[q];
+      for (int j = 0; j < PB; ++j) {
+        const int i = (rr * PB + j) * P2 + k2;
+        sum.x += keep[i].x * Y[i].x + keep[i].y * Y[i].y;
+        sum.y += keep[i].y * Y[i].x - keep[i].x * Y[i].y;
+      }
+      acc[q] = sum;
+    }
+    __syncthreads();  // keep and the buffers are reused by the next block
+  }
+  for (int q = threadIdx.x; q < RB * L2; q += LTHR) {
+    const int rr = q >> a.logL2, k2 = q & (L2 - 1);
+    buf[0][rr * P2 + k2] = acc[q];
+  }
+  const float2* Bv = lds_fft<true>(buf[0], buf[1], L2, a.logL2, RB, tws);
+  const size_t obase = (size_t)bh * L + (size_t)k10 * L2;
+  for (int q = threadIdx.x; q < RB * L2; q += LTHR) {
+    const int rr = q >> a.logL2, n2 = q & (L2 - 1);
+    R[obase + q] = Bv[rr * P2 + n2];
+  }
+}
+
+// Inverse column pass of the summed line: c[bh][n1 L2 + n2] = Re(IDFT_L1
+// over k1 of R[bh][k1][n2] conj W_L^(k1 n2)) / L, CB columns per workgroup.
+__global__ __launch_bounds__(LTHR) void col_inv_corr_kernel(LongArgs a, const float2* __restrict__ R,
+                                                            float* __restrict__ c) {
+  __shared__ float2 buf[2][LPAD];
+  __shared__ float2 tws[LMAXM];
+  const int L1 = 1 << a.logL1, L2 = 1 << a.logL2, L = L1 * L2;
+  const int CB = LBUF / L1 < L2 ? LBUF / L1 : L2;
+  const int nblk = L2 / CB;
+  const int bh = blockIdx.x / nblk, n20 = (blockIdx.x - bh * nblk) * CB;
+  const size_t gbase = (size_t)bh * L;
+  for (int q = threadIdx.x; q < CB * L1; q += LTHR) {
+    const int k1 = q / CB, r = q - k1 * CB;
+    const int n2 = n20 + r;
+    buf[0][r * (L1 + 1) + k1] = cmul2(R[gbase + (size_t)k1 * L2 + n2], conj2(a.tw[(k1 * n2) & (L - 1)]));
+  }
+  stage_twiddles(tws, a.logL1, a.tw, a.logL1 + a.logL2);
+  const float2* U = lds_fft<true>(buf[0], buf[1], L1, a.logL1, CB, tws);
+  const float sc = 1.f / (float)L;
+  for (int q = threadIdx.x; q < CB * L1; q += LTHR) {
+    const int n1 = q / CB, r = q - n1 * CB;
+    c[gbase + (size_t)n1 * L2 + n20 + r] = U[r * (L1 + 1) + n1].x * sc;
+  }
+}
+
+// dlogits[bh][k] = z*[k] (g[k] - sum_m z*[m] g[m]) with z* = softmax of the
+// line's logits and g[k] = c[k] (+ c[L - N + k] for 0 < k < N on a padded
+// circle: lags that wrap mod N land there).  One 1024-thread workgroup per
+// line; four passes over the line (max, sum, dot, write).
+constexpr int GTHR = 1024;
+__device__ __forceinline__ float block_reduce(float x, bool is_max, float* red) {
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float p = __shfl_xor(x, o, 64);
+    x = is_max ? fmaxf(x, p) : x + p;
+  }
+  __syncthreads();  // red is free
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  float r = red[0];
+  for (int w = 1; w < GTHR / 64; ++w) r = is_max ? fmaxf(r, red[w]) : r + red[w];
+  return r;
+}
+__global__ __launch_bounds__(GTHR) void logits_grad_long_kernel(const float* __restrict__ z, const float* __restrict__ c,
+                                                                float* __restrict__ dz, int N, int L) {
+  __shared__ float red[GTHR / 64];
+  const int bh = blockIdx.x;
+  const float* zl = z + (size_t)bh * N;
+  const float* cl = c + (size_t)bh * L;
+  const bool wrap = N != L;
+  float m = -INFINITY;
+  for (int k = threadIdx.x; k < N; k += GTHR) m = fmaxf(m, zl[k]);
+  m = block_reduce(m, true, red);
+  float se = 0.f;
+  for (int k = threadIdx.x; k < N; k += GTHR) se += __expf(zl[k] - m);
+  const float inv = 1.f / block_reduce(se, false, red);
+  auto grad = [&](int k) { return cl[k] + (wrap && k > 0 ? cl[L - N + k] : 0.f); };
+  float dot = 0.f;
+  for (int k = threadIdx.x; k < N; k += GTHR) dot += __expf(zl[k] - m) * inv * grad(k);
+  dot = block_reduce(dot, false, red);
+  for (int k = threadIdx.x; k < N; k += GTHR) {
+    const float p = __expf(zl[k] - m) * inv;
+    dz[(size_t)bh * N + k] = p * (grad(k) - dot);
+  }
+}
+
+// The value column pass (forward): src BLOCKED values -> A, PB pairs per
+// block; register kernels when L1 is 64 or 256.
+hipError_t launch_col_values(int et, const LongArgs& a, const void* src, float2* A, hipStream_t s,
+                             const LaunchTiming* t) {
+  const int L1 = 1 << a.logL1, L2 = 1 << a.logL2, L = L1 * L2, PB = a.pb;
+  const bool wrap = a.N != L;
+  const long blocks = (long)a.BH * (a.pairs / PB);
+  const float2* nosm = nullptr;
+  const int mc = L1 == 256 ? 16 : L1 == 64 ? 8 : 0;
+  auto col = [&](auto plain, auto wrapped, unsigned grid, unsigned threads) {
+    return wrap ? launch_k(wrapped, dim3(grid), dim3(threads), 0, s, t, a, PB, src, A, nosm)
+                : launch_k(plain, dim3(grid), dim3(threads), 0, s, t, a, PB, src, A, nosm);
+  };
+  if (mc) {
+    const unsigned cv = (unsigned)(blocks * (L2 / ((128 / mc) / PB)));
+    if (mc == 16)
+      return et == ET_F32 ? col(col_reg_kernel<ET_F32, 16, false>, col_reg_kernel<ET_F32, 16, true>, cv, 128)
+                          : col(col_reg_kernel<ET_BF16, 16, false>, col_reg_kernel<ET_BF16, 16, true>, cv, 128);
+    return et == ET_F32 ? col(col_reg_kernel<ET_F32, 8, false>, col_reg_kernel<ET_F32, 8, true>, cv, 128)
+                        : col(col_reg_kernel<ET_BF16, 8, false>, col_reg_kernel<ET_BF16, 8, true>, cv, 128);
+  }
+  const int cb = LBUF / (PB * L1) < L2 ? LBUF / (PB * L1) : L2;
+  const unsigned colb = (unsigned)(blocks * (L2 / cb));
+  return et == ET_F32 ? col(col_fwd_kernel<ET_F32, false>, col_fwd_kernel<ET_F32, true>, colb, LTHR)
+                      : col(col_fwd_kernel<ET_BF16, false>, col_fwd_kernel<ET_BF16, true>, colb, LTHR);
+}
+
+// Shape checks shared by the long launchers.
+bool long_shape_ok(const LongArgs& a) {
+  const int L1 = 1 << a.logL1, L2 = 1 << a.logL2, L = L1 * L2, N = a.N, PB = a.pb;
+  if (a.logL1 < 1 || a.logL2 < 1 || L1 > LMAXM || L2 > LMAXM || a.pairs < 1 || a.BH < 1) return false;
+  if (PB < 1 || PB > 8 || (PB & (PB - 1)) != 0 || a.pairs % PB != 0) return false;
+  const int cb1 = LBUF / L1 < L2 ? LBUF / L1 : L2, rb1 = LBUF / L2 < L1 ? LBUF / L2 : L1;
+  const int cb = LBUF / (PB * L1) < L2 ? LBUF / (PB * L1) : L2, rb = LBUF / (PB * L2) < L1 ? LBUF / (PB * L2) : L1;
+  if (cb < 1 || rb < 1 || cb1 > 64 || rb1 > 64 || cb * PB > 64 || rb * PB > 64) return false;
+  if (N < 1 || (N != L && 2 * N - 1 > L) || smc_chunks(N) > 64) return false;
+  const long blocks = (long)a.BH * (a.pairs / PB);
+  return blocks * (L2 / cb) <= 0x7fffffffL && blocks * (L1 / rb) <= 0x7fffffffL;
+}
+
 }  // namespace
 
 hipError_t launch_longconv(int et, const LongArgs& a, const float* logits, const void* V, float2* zc, float2* Az,
@@ -618,6 +791,26 @@ hipError_t launch_longconv(int et, const LongArgs& a, const float* logits, const
   if (et == ET_F32)
     return launch_k(col_inv_kernel<ET_F32>, dim3((unsigned)colb), dim3(LTHR), 0, s, t[5], a, PB, (const float2*)A, O);
   return launch_k(col_inv_kernel<ET_BF16>, dim3((unsigned)colb), dim3(LTHR), 0, s, t[5], a, PB, (const float2*)A, O);
+}
+
+hipError_t launch_long_scoregrad(int et, const LongArgs& a, const float* logits, const void* dOb, const void* Vb,
+                                 float2* Ad, float2* Av, float2* R, float* c, float* dlogits, hipStream_t s,
+                                 const LaunchTiming* t) {
+  if (!long_shape_ok(a)) return hipErrorInvalidValue;
+  const int L1 = 1 << a.logL1, L2 = 1 << a.logL2, L = L1 * L2;
+  hipError_t e = launch_col_values(et, a, dOb, Ad, s, t);
+  if (e != hipSuccess) return e;
+  if ((e = launch_col_values(et, a, Vb, Av, s, t)) != hipSuccess) return e;
+  const int rb = LBUF / (a.pb * L2) < L1 ? LBUF / (a.pb * L2) : L1;
+  const int cb1 = LBUF / L1 < L2 ? LBUF / L1 : L2;
+  if ((e = launch_k(row_xcorr_kernel, dim3((unsigned)((long)a.BH * (L1 / rb))), dim3(LTHR), 0, s, t, a, a.pb,
+                    (const float2*)Ad, (const float2*)Av, R)) != hipSuccess)
+    return e;
+  if ((e = launch_k(col_inv_corr_kernel, dim3((unsigned)((long)a.BH * (L2 / cb1))), dim3(LTHR), 0, s, t, a,
+                    (const float2*)R, c)) != hipSuccess)
+    return e;
+  return launch_k(logits_grad_long_kernel, dim3((unsigned)a.BH), dim3(GTHR), 0, s, t, logits, (const float*)c, dlogits,
+                  a.N, L);
 }
 
 }  // namespace cat

@@ -370,11 +370,15 @@ def test_mix_backward_1d_workload_full_size(cat):
 @pytest.mark.parametrize("B,N,D,H,dtype,path", [
     (2, 64, 64, 4, "f32", "fft_valu"), (1, 128, 128, 2, "bf16", "direct"), (2, 1024, 128, 2, "bf16", "fft_matrix"),
     (1, 200, 96, 3, "f32", "fft_valu"), (4, 6, 16, 2, "f32", "fft_valu"), (1, 8, 64, 32, "bf16", "fft_valu"),
-    (2, 512, 96, 12, "bf16", "fft_valu"), (8, 1000, 64, 4, "f32", "fft_valu"), (2, 4096, 32, 2, "f32", "fft_valu")])
+    (2, 512, 96, 12, "bf16", "fft_valu"), (8, 1000, 64, 4, "f32", "fft_valu"), (2, 4096, 32, 2, "f32", "fft_valu"),
+    (1, 197, 64, 2, "f32", "fft_valu"), (3, 61, 48, 3, "bf16", "fft_valu"), (1, 1, 16, 2, "f32", "fft_valu"),
+    (1, 8192, 32, 2, "f32", "fft_multipass"), (1, 3000, 16, 1, "bf16", "fft_multipass")])
 def test_backward_1d(cat, B, N, D, H, dtype, path):
     """Gradients of the whole 1D forward (dX, dW_A, dW_V) against the oracle's
     chain rule; the mixing runs on the plan's path, the products on the
-    projection GEMM."""
+    projection GEMM.  B N = 197, 183 and 1 are not multiples of 8: X^T rows
+    are padded with zeros to 16-byte multiples; N = 8192 and 3000 run the
+    three-pass path (L = N, and L = 8192 >= 2N - 1)."""
     say("backward_1d", B, N, D, H, dtype, path)
     import torch
     inp = rng_inputs(31, B, N, D, H, dtype)
@@ -410,27 +414,53 @@ def check_weight_grads(ref, X, got, dtype):
             assert m <= bar, f"{name}: max_abs={m:.3e} > bar {bar:.3e} (K={K})"
 
 
-def test_backward_1d_rejections(cat):
-    """B N not a multiple of 8 (X^T rows would not be whole 16-byte chunks)
-    and the multi-pass path are rejected before any launch."""
+def test_backward_1d_empty_batch(cat):
+    """B = 0: the weight gradients are empty sums, written as zeros."""
     import torch
-    for (B, N, D, H) in [(1, 197, 64, 2), (1, 8192, 16, 2)]:
-        plan = cat.cat_plan_create("1d", "f32", B, N, D, H)
-        z = torch.zeros((B, N, D), device="cuda")
-        with pytest.raises(cat.CatError) as e:
-            cat.cat_backward_1d(plan, z, torch.zeros((D, H), device="cuda"), torch.zeros((D, D), device="cuda"), z)
-        assert e.value.status == -2
+    for dtype in ("f32", "bf16"):
+        plan = cat.cat_plan_create("1d", dtype, 0, 64, 32, 2)
+        dt = torch.float32 if dtype == "f32" else torch.bfloat16
+        X = torch.empty((0, 64, 32), dtype=dt, device="cuda")
+        dX, dWA, dWV = cat.cat_backward_1d(plan, X, torch.ones((32, 2), dtype=dt, device="cuda"),
+                                           torch.ones((32, 32), dtype=dt, device="cuda"), X,
+                                           workspace=torch.empty(256, dtype=torch.uint8, device="cuda"))
+        torch.cuda.synchronize()
+        assert dX.shape == (0, 64, 32)
+        assert torch.count_nonzero(dWA).item() == 0 and torch.count_nonzero(dWV).item() == 0
+
+
+@pytest.mark.parametrize("B,N,D,H,dtype", [(1, 8192, 16, 2, "f32"), (2, 5000, 16, 2, "bf16"), (1, 2500, 32, 1, "f32"),
+                                           (1, 16384, 8, 1, "bf16")])
+def test_mix_backward_1d_long(cat, B, N, D, H, dtype):
+    """The mixing backward on the three-pass path: dV as the forward mixing
+    with reversed logits, dlogits from the cross-correlation spectra of every
+    pair of a head summed before one inverse transform (L = N for N = 8192
+    and 16384; on the L >= 2N - 1 circle, folded onto mod-N lags, for 5000
+    and 2500), against the oracle's direct sums."""
+    say("mix_backward_long", B, N, D, H, dtype)
+    import torch
+    rng = np.random.default_rng(N + 7 * D)
+    logits = (rng.standard_normal((B, H, N)) * 2).astype(np.float32)
+    V = rng.standard_normal((B, N, D)).astype(np.float32)
+    dO = rng.standard_normal((B, N, D)).astype(np.float32)
+    if dtype == "bf16":
+        V = W.bf16_bits_to_f32(W.round_bf16_bits(V)).reshape(V.shape)
+        dO = W.bf16_bits_to_f32(W.round_bf16_bits(dO)).reshape(dO.shape)
+    plan = cat.cat_plan_create("1d", dtype, B, N, D, H)
+    assert plan.conv_path() == "fft_multipass"
+    dlogits, dV = cat.cat_step_mix_backward_1d(plan, torch.from_numpy(logits).cuda(), to_dev(V, dtype),
+                                               to_dev(dO, dtype))
+    torch.cuda.synchronize()
+    ref = oracle.mix_backward_1d(logits, V, dO)
+    assert_parity(to_np(dV), ref["dV"], dtype, "dV")
+    got = to_np(dlogits)
+    assert_parity(got, ref["dz"], "f32", "dlogits")
+    assert np.all(np.abs(got.sum(axis=-1)) <= 1e-5 * np.abs(got).sum(axis=-1) + 1e-7)
 
 
 def test_mix_backward_1d_rejections(cat):
-    """The multi-pass path has no backward yet; 2D plans are the wrong kind."""
+    """2D plans are the wrong kind for the 1D mixing backward."""
     import torch
-    plan = cat.cat_plan_create("1d", "f32", 1, 8192, 8, 2)
-    z = torch.zeros((1, 2, 8192), device="cuda")
-    V = torch.zeros((1, 8192, 8), device="cuda")
-    with pytest.raises(cat.CatError) as e:
-        cat.cat_step_mix_backward_1d(plan, z, V, V)
-    assert e.value.status == -2
     p2 = cat.cat_plan_create("2d", "f32", 1, 64, 16, 2, Hg=8, Wg=8)
     with pytest.raises(cat.CatError) as e:
         cat.cat_step_mix_backward_1d(p2, torch.zeros((1, 2, 64), device="cuda"), torch.zeros((1, 64, 16), device="cuda"),

@@ -247,14 +247,18 @@ cat_status cat_step_mix(cat_plan plan, const float* logits, const void* V, void*
  *                      of the reversed logits, on the plan's mixing path);
  *   dz*[b][h][k]     = sum over the head's channels c and tokens i of
  *                      dO[b][i][c] V[b][(i - k) mod N][c]
- *                      (a cross-correlation, by FFT on the plan's circle);
+ *                      (a cross-correlation, by FFT on the plan's circle;
+ *                      on CAT_PATH_FFT_MULTIPASS the cross-spectra of a
+ *                      head's channel pairs are summed before one
+ *                      three-pass inverse transform, and lags that wrap
+ *                      mod N are folded back on a padded circle);
  *   dlogits[b][h][k] = z*[k] (dz*[k] - sum_m z*[m] dz*[m]).
  * logits [B][H][N] fp32 (the forward's z), V and dO [B][N][D] storage
  * dtype (all caller-owned device memory, read only); dlogits [B][H][N] fp32
  * and dV [B][N][D] storage dtype are written.  dV in bf16 is rounded from
  * fp32; dlogits is computed in fp32 from the stored V and dO.  workspace:
- * cat_plan_workspace_size bytes.  Errors: CAT_ERR_PLAN_MISMATCH for a 2D
- * plan; CAT_ERR_UNSUPPORTED for plans on CAT_PATH_FFT_MULTIPASS;
+ * cat_plan_workspace_size bytes.  Every 1D length of the forward is
+ * supported.  Errors: CAT_ERR_PLAN_MISMATCH for a 2D plan;
  * CAT_ERR_INVALID_ARG for NULL or misaligned pointers. */
 cat_status cat_step_mix_backward_1d(cat_plan plan, const float* logits, const void* V, const void* dO,
                                     float* dlogits, void* dV, void* workspace, void* stream);
@@ -269,8 +273,10 @@ cat_status cat_step_mix_backward_1d(cat_plan plan, const float* logits, const vo
  * with V and z recomputed from X.  The products run on the projection
  * GEMM (fp32 accumulation; dX is accumulated in fp32 and rounded once; dV
  * and dz enter the weight products rounded to the storage dtype).
- * Errors: CAT_ERR_PLAN_MISMATCH for a 2D plan; CAT_ERR_UNSUPPORTED on the
- * multi-pass path and unless B N is a positive multiple of 8;
+ * Every 1D length and batch of the forward is supported (X^T is staged with
+ * its B N columns padded with zeros to a multiple of 8); B = 0 writes zero
+ * weight gradients (dX is empty; X, W_A, W_V, dO, dX and workspace are not
+ * read and may be NULL).  Errors: CAT_ERR_PLAN_MISMATCH for a 2D plan;
  * CAT_ERR_INVALID_ARG for NULL or misaligned pointers.  Streams: the
  * weight-gradient branch runs on a stream the plan owns (default priority),
  * forked from `stream` by an event after the mixing backward and joined

@@ -14,6 +14,10 @@
 
 using namespace cat;
 
+// Output tile width of the backward's weight-gradient product (fp32
+// split-K slabs).
+constexpr int kDwTileN = 128;
+
 struct cat_plan_s {
   cat_problem p;
   int d;
@@ -35,15 +39,16 @@ struct cat_plan_s {
   float2* d_tw;      // 1D inter-pass twiddles, L entries (null in 2D)
   size_t off_V, off_z, off_Q, off_K, off_part, off_psum, off_spec, ws_bytes;
   // the CAT backward's projection gradients (1D single-workgroup lines)
-  size_t off_bz, off_bV, off_bdV, off_bdz, off_bWt, off_bdXf, off_bXt, off_bP, off_bdW;
+  size_t off_bz, off_bV, off_bdV, off_bdz, off_bWt, off_bXt, off_bP, off_bdW;
   int Hp;  // heads padded to a whole 16-byte column chunk
   // the backward's weight-gradient branch runs on a plan-owned stream
   // (default priority), forked from and joined back to the caller's stream
   hipStream_t side = nullptr;
-  hipEvent_t fork_ev = nullptr, join_ev = nullptr;
+  hipEvent_t fork_ev = nullptr, join_ev = nullptr, pack_ev = nullptr;
   size_t off_A, off_zc, off_Az;  // long path scratch
   size_t off_A2;                 // long path: the second values transform of the score gradient
   int Kp;                        // B N rounded up to 8: the padded K of the weight-gradient product
+  int ksplit_dw, kchunk_dw;      // split K of the weight-gradient product: slices, K positions per slice
   size_t off_xpart, off_kbar, off_weff;  // averaged-key logits scratch (1D)
   size_t fwd_ws_bytes;  // workspace bytes the 1D forward itself touches (a prefix of the layout)
   bool debug_sync;
@@ -287,6 +292,12 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
   pl->tile_m = tm ? std::atoi(tm) : 0;
   if (pl->tile_m != 128 && pl->tile_m != 256) pl->tile_m = 0;
 
+  {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      n = 0;
+    pl->num_cu = n;
+  }
   const size_t BND = (size_t)p->B * p->N * p->D;
   const size_t BH = (size_t)p->B * p->H;
   size_t off = 0;
@@ -324,19 +335,36 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
       pl->off_A2 = off;
       off = up256(off + BH * (size_t)d2 * pl->L * sizeof(float2));
     }
-    // the whole backward: V and z recomputed, dV and dz, W_V^T, dX in fp32,
-    // X^T (B N padded to Kp columns), dz token-major (padded to Hp heads) and
-    // dW_A padded
+    // the whole backward: V and z recomputed, dV and dz, [W_V^T ; W_A^T ; 0],
+    // X^T (B N padded to Kp columns), P = [dV | dz^T | 0] (dz padded to Hp
+    // heads) and the split-K partial products of [dW_V | dW_A | 0] (fp32)
     {
       const size_t Dz = (size_t)p->D, BN = (size_t)p->B * p->N;
       pl->Hp = (int)((p->H + 7) / 8 * 8);
       pl->Kp = (int)((BN + 7) / 8 * 8);
-      const size_t sizes[9] = {BH * p->N * sizeof(float), BND * pl->esz, BND * pl->esz, BH * p->N * sizeof(float),
-                               Dz * Dz * pl->esz, BND * sizeof(float), Dz * (size_t)pl->Kp * pl->esz,
-                               BN * pl->Hp * pl->esz, Dz * pl->Hp * pl->esz};
-      size_t* offs[9] = {&pl->off_bz, &pl->off_bV, &pl->off_bdV, &pl->off_bdz, &pl->off_bWt,
-                         &pl->off_bdXf, &pl->off_bXt, &pl->off_bP, &pl->off_bdW};
-      for (int i = 0; i < 9; ++i) {
+      // K = B N is long and the output only D x (D + Hp): slices of K fill
+      // one round of two workgroups per compute unit with kDwTileN-wide
+      // tiles (at least 512 K positions per slice, a multiple of the K tile)
+      {
+        const long cus = pl->num_cu > 0 ? pl->num_cu : 256;
+        const long tiles = ((long)p->D + 127) / 128 * (((long)p->D + pl->Hp + kDwTileN - 1) / kDwTileN);
+        const long kt = pl->esz == 4 ? 32 : 64;
+        long S = 2 * cus / tiles;
+        const long smax = (long)BN / 512;
+        S = S < smax ? S : smax;
+        S = S < 1 ? 1 : S;
+        long kc = ((long)BN + S - 1) / S;
+        kc = kc < 1 ? kt : (kc + kt - 1) / kt * kt;  // (an empty batch: one slice of one K tile)
+        pl->kchunk_dw = (int)kc;
+        pl->ksplit_dw = BN == 0 ? 1 : (int)(((long)BN + kc - 1) / kc);
+      }
+      const size_t sizes[8] = {BH * p->N * sizeof(float), BND * pl->esz, BND * pl->esz, BH * p->N * sizeof(float),
+                               (Dz + pl->Hp) * Dz * pl->esz, Dz * (size_t)pl->Kp * pl->esz,
+                               BN * (Dz + pl->Hp) * pl->esz,
+                               (size_t)pl->ksplit_dw * Dz * (Dz + pl->Hp) * sizeof(float)};
+      size_t* offs[8] = {&pl->off_bz, &pl->off_bV, &pl->off_bdV, &pl->off_bdz, &pl->off_bWt,
+                         &pl->off_bXt, &pl->off_bP, &pl->off_bdW};
+      for (int i = 0; i < 8; ++i) {
         *offs[i] = off;
         off = up256(off + sizes[i]);
       }
@@ -363,14 +391,8 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
   }
   pl->ws_bytes = off;
 
-  // device tables and kernel attributes (first HIP calls)
+  // device tables and kernel attributes
   pl->d_tw = nullptr;
-  {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      n = 0;
-    pl->num_cu = n;
-  }
   if (g.twiddled) {
     std::vector<float2> tw((size_t)pl->L);
     const double two_pi = 6.283185307179586476925286766559;
@@ -425,7 +447,9 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
     hipError_t se = hipStreamCreateWithFlags(&pl->side, hipStreamNonBlocking);
     if (se == hipSuccess) se = hipEventCreateWithFlags(&pl->fork_ev, hipEventDisableTiming);
     if (se == hipSuccess) se = hipEventCreateWithFlags(&pl->join_ev, hipEventDisableTiming);
+    if (se == hipSuccess) se = hipEventCreateWithFlags(&pl->pack_ev, hipEventDisableTiming);
     if (se != hipSuccess) {
+      if (pl->join_ev) (void)hipEventDestroy(pl->join_ev);
       if (pl->fork_ev) (void)hipEventDestroy(pl->fork_ev);
       if (pl->side) (void)hipStreamDestroy(pl->side);
       if (pl->d_tw) (void)hipFree(pl->d_tw);
@@ -445,6 +469,7 @@ cat_status cat_plan_destroy(cat_plan plan) {
   if (plan->d_tw) (void)hipFree(plan->d_tw);
   if (plan->d_ftab) (void)hipFree(plan->d_ftab);
   free_events(plan);
+  if (plan->pack_ev) (void)hipEventDestroy(plan->pack_ev);
   if (plan->join_ev) (void)hipEventDestroy(plan->join_ev);
   if (plan->fork_ev) (void)hipEventDestroy(plan->fork_ev);
   if (plan->side) (void)hipStreamDestroy(plan->side);
@@ -748,43 +773,73 @@ cat_status mix_backward_core(cat_plan plan, const float* logits, const void* V, 
   return check_sync(plan, "mixing backward");
 }
 
-// The two branches of the whole backward after the mixing backward: dW_V
-// and dW_A on the plan's side stream (already forked from `s`), dX on `s`.
+// The whole backward after the fork (the plan's side stream already waits
+// for `s`).  With P = [dV | dz^T | 0] [B N][D + Hp] (storage dtype):
+//   side stream: X^T (needs only X, so it runs beside the projection and
+//                the mixing backward), then, once P is packed,
+//                [dW_V | dW_A | 0] = X^T P with K split into slices whose
+//                fp32 partial products are summed in order;
+//   `s`:         V and z recomputed, the mixing backward (dV, dz), P, then
+//                dX = P [W_V^T ; W_A^T ; 0] (K = D + Hp), written in the
+//                storage dtype from fp32 accumulators.
 // Returns the first failure; the caller joins the side stream either way.
-cat_status backward_branches(cat_plan plan, const void* X, const void* W_A, const void* W_V, void* dX, void* dW_A,
-                             void* dW_V, void* workspace, hipStream_t s, void* bdV, float* bdz) {
-  const int B = (int)plan->p.B, N = (int)plan->p.N, D = (int)plan->p.D, H = (int)plan->p.H;
+cat_status backward_body(cat_plan plan, const void* X, const void* W_A, const void* W_V, const void* dO, void* dX,
+                         void* dW_A, void* dW_V, void* workspace, hipStream_t s, KernelMark* mk) {
+  const int B = (int)plan->p.B, N = (int)plan->p.N, D = (int)plan->p.D, H = (int)plan->p.H, Hp = plan->Hp;
   const int et = plan->et;
   hipError_t e;
-  // dW_V = X^T dV and dW_A = X^T dz^T as two output segments of one
-  // product (X^T the shared row operand, K = B N); dW_A's padded columns
-  // are dropped afterwards
+  cat_status st;
   hipStream_t sw = plan->side;
   void* bXt = ws_at(workspace, plan->off_bXt);
-  void* bdzt = ws_at(workspace, plan->off_bP);
-  void* bdWA = ws_at(workspace, plan->off_bdW);
   if ((e = launch_transpose(et, X, bXt, B * N, D, plan->Kp, sw)) != hipSuccess) return hip_fail(e, "transpose launch");
-  if ((e = launch_pack_grads(et, nullptr, bdz, bdzt, B, N, 0, H, plan->Hp, sw)) != hipSuccess)
-    return hip_fail(e, "pack launch");
+
+  // the forward's V (row-major) and logits
+  void* bV = ws_at(workspace, plan->off_bV);
+  float* bz = reinterpret_cast<float*>(ws_at(workspace, plan->off_bz));
+  void* bdV = ws_at(workspace, plan->off_bdV);
+  float* bdz = reinterpret_cast<float*>(ws_at(workspace, plan->off_bdz));
+  GemmArgs ga = gemm_base(plan, X);
+  ga.nseg = 1;
+  ga.seg[0] = seg(W_V, bV, D, 0, OUT_ROWMAJOR, 1);
+  ga.Wz = W_A;
+  ga.z = bz;
+  ga.nz = H;
+  if ((e = launch_gemm(et, ga, s, mk->at(0))) != hipSuccess) return hip_fail(e, "projection launch");
+  // dlogits (fp32) and dV
+  if ((st = mix_backward_core(plan, bz, bV, dO, bdz, bdV, workspace, s, mk)) != CAT_OK) return st;
+  void* P = ws_at(workspace, plan->off_bP);
+  if ((e = launch_pack_grads(et, bdV, bdz, P, B, N, D, H, Hp, s)) != hipSuccess) return hip_fail(e, "pack launch");
+  if ((e = hipEventRecord(plan->pack_ev, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  if ((e = hipStreamWaitEvent(sw, plan->pack_ev, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+
+  // weight gradients (side stream)
+  const int S = plan->ksplit_dw;
+  float* pW = reinterpret_cast<float*>(ws_at(workspace, plan->off_bdW));  // [S][D][D + Hp] fp32
   GemmArgs gw = gemm_base(plan, bXt);
   gw.M = D;
   gw.K = B * N;
   gw.ldx = plan->Kp;  // X^T rows padded to 16-byte multiples (zero past B N)
-  gw.nseg = 2;
-  gw.seg[0] = seg(bdV, dW_V, D, 0, OUT_ROWMAJOR, 1);
-  gw.seg[1] = seg(bdzt, bdWA, plan->Hp, 0, OUT_ROWMAJOR, 1);
+  gw.ksplit = S;      // slices of K, each writing fp32 partial products
+  gw.kchunk = plan->kchunk_dw;
+  gw.tile_n = plan->tile_n ? plan->tile_n : kDwTileN;
+  gw.nseg = 1;
+  gw.seg[0] = seg(P, pW, D + Hp, 1, OUT_ROWMAJOR, 1);
   if ((e = launch_gemm(et, gw, sw)) != hipSuccess) return hip_fail(e, "dW launch");
-  if ((e = launch_take_cols(et, bdWA, dW_A, D, plan->Hp, H, sw)) != hipSuccess) return hip_fail(e, "dW_A copy launch");
-  // dX = dV W_V^T (fp32), then + dz^T W_A^T in the storage dtype
-  void* bWt = ws_at(workspace, plan->off_bWt);
-  float* bdXf = reinterpret_cast<float*>(ws_at(workspace, plan->off_bdXf));
-  if ((e = launch_transpose(et, W_V, bWt, D, D, D, s)) != hipSuccess) return hip_fail(e, "transpose launch");
-  GemmArgs gx = gemm_base(plan, bdV);
+  if ((e = launch_sum_slices(et, pW, dW_V, dW_A, S, D, D + Hp, D, H, sw)) != hipSuccess)
+    return hip_fail(e, "dW sum launch");
+
+  // dX (s): Wc = [W_V^T ; W_A^T ; 0] [D + Hp][D]
+  char* Wc = reinterpret_cast<char*>(ws_at(workspace, plan->off_bWt));
+  if ((e = launch_transpose(et, W_V, Wc, D, D, D, s)) != hipSuccess) return hip_fail(e, "transpose launch");
+  if ((e = launch_transpose(et, W_A, Wc + (size_t)D * D * plan->esz, D, H, D, s)) != hipSuccess)
+    return hip_fail(e, "transpose launch");
+  if ((e = launch_zero(Wc + (size_t)(D + H) * D * plan->esz, (size_t)(Hp - H) * D * plan->esz, s)) != hipSuccess)
+    return hip_fail(e, "zero launch");
+  GemmArgs gx = gemm_base(plan, P);
+  gx.K = D + Hp;
   gx.nseg = 1;
-  gx.seg[0] = seg(bWt, bdXf, D, 1, OUT_ROWMAJOR, 1);
+  gx.seg[0] = seg(Wc, dX, D, 0, OUT_ROWMAJOR, 1);
   if ((e = launch_gemm(et, gx, s)) != hipSuccess) return hip_fail(e, "dX launch");
-  if ((e = launch_rank_heads_add(et, bdXf, bdz, W_A, dX, B, N, D, H, s)) != hipSuccess)
-    return hip_fail(e, "dX heads launch");
   return CAT_OK;
 }
 
@@ -1202,32 +1257,14 @@ cat_status cat_backward_1d(cat_plan plan, const void* X, const void* W_A, const 
     return check_sync(plan, "backward");
   }
   if ((st = check_ptrs({X, W_A, W_V, dO, dX, dW_A, dW_V, workspace})) != CAT_OK) return st;
-  const int et = plan->et;
-  void* bV = ws_at(workspace, plan->off_bV);
-  float* bz = reinterpret_cast<float*>(ws_at(workspace, plan->off_bz));
-  void* bdV = ws_at(workspace, plan->off_bdV);
-  float* bdz = reinterpret_cast<float*>(ws_at(workspace, plan->off_bdz));
   KernelMark mk(plan);
-
-  // the forward's V (row-major) and logits
-  GemmArgs ga = gemm_base(plan, X);
-  ga.nseg = 1;
-  ga.seg[0] = seg(W_V, bV, D, 0, OUT_ROWMAJOR, 1);
-  ga.Wz = W_A;
-  ga.z = bz;
-  ga.nz = H;
-  hipError_t e = launch_gemm(et, ga, s, mk.at(0));
-  if (e != hipSuccess) return hip_fail(e, "projection launch");
-  // dlogits (fp32) and dV
-  if ((st = mix_backward_core(plan, bz, bV, dO, bdz, bdV, workspace, s, &mk)) != CAT_OK) return st;
-  // the weight gradients (the longer branch, enqueued first) run on the
-  // plan's side stream beside dX
+  hipError_t e;
   if ((e = hipEventRecord(plan->fork_ev, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   if ((e = hipStreamWaitEvent(plan->side, plan->fork_ev, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
   // From here on every exit joins the side stream back into `s`, so no
   // work of this call can still be queued on it once the caller reuses
   // the outputs or the workspace.
-  st = backward_branches(plan, X, W_A, W_V, dX, dW_A, dW_V, workspace, s, bdV, bdz);
+  st = backward_body(plan, X, W_A, W_V, dO, dX, dW_A, dW_V, workspace, s, &mk);
   const cat_status jst = join_side(plan, s);
   if (st != CAT_OK) return st;
   if (jst != CAT_OK) return jst;

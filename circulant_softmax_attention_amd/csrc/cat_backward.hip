@@ -1,11 +1,12 @@
-// cat_backward.hip -- layout and elementwise kernels of the CAT backward's
-// projection gradients.  With V = X W_V and z_h = X W_A[:, h] (CAT:
+// cat_backward.hip -- layout kernels of the CAT backward's projection
+// gradients.  With V = X W_V and z_h = X W_A[:, h] (CAT:
 // Circular-Convolutional Attention for Sub-Quadratic Transformers, "Method
 // details / Overall framework"), the chain rule gives
-//   dX = dV W_V^T + dz^T W_A^T,  dW_V = X^T dV,  dW_A = X^T dz^T;
-// the products run on the projection GEMM (dW_V and dW_A as two output
-// segments of one launch sharing the row operand X^T), and these kernels
-// supply its operands and the rank-H term.
+//   dX = dV W_V^T + dz^T W_A^T,  dW_V = X^T dV,  dW_A = X^T dz^T,
+// i.e. with P = [dV | dz^T] two products on the projection GEMM:
+//   [dW_V | dW_A] = X^T P  (K = B N, split into slices summed afterwards),
+//   dX = P [W_V^T ; W_A^T]  (K = D + H);
+// these kernels build the operands (transposes, P) and sum the slices.
 #include "cat_common.hpp"
 #include "cat_internal.hpp"
 
@@ -50,75 +51,59 @@ __global__ __launch_bounds__(256) void transpose_kernel(const void* __restrict__
   }
 }
 
-// P [B N][D + Hp] (storage dtype) = [dV | dz token-major | 0]: the column
-// operand of the product X^T P = [dW_V | dW_A | 0].
+// P [B N][D + Hp] (storage dtype) = [dV | dz token-major | 0]: one thread
+// per 16-byte chunk of P (D and Hp are multiples of 8, so a chunk lies
+// wholly in the dV part or wholly in the dz part).
 template <int ET>
 __global__ __launch_bounds__(256) void pack_grads_kernel(const void* __restrict__ dV, const float* __restrict__ dz,
                                                          void* __restrict__ P, int B, int N, int D, int H, int Hp) {
-  const int W = D + Hp;
+  constexpr int VE = ET == ET_F32 ? 4 : 8;
+  const int W = D + Hp, cpr = W / VE;
   const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (size_t)B * N * W) return;
-  const size_t m = idx / W;
-  const int col = (int)(idx - m * W);
-  float v;
-  if (col < D) {
-    v = ld_elem<ET>(dV, m * D + col);
+  const size_t M = (size_t)B * N;
+  if (idx >= M * cpr) return;
+  const size_t m = idx / cpr;
+  const int c0 = (int)(idx - m * cpr) * VE;
+  uint4 v;
+  if (c0 < D) {
+    v = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(dV) + (m * D + c0) * (ET == ET_F32 ? 4 : 2));
   } else {
-    const int h = col - D;
     const int b = (int)(m / N), n = (int)(m - (size_t)b * N);
-    v = h < H ? dz[((size_t)b * H + h) * N + n] : 0.f;
-  }
-  st_elem<ET>(P, idx, v);
-}
-
-// dX[m][c] = dXf[m][c] + sum_h dz[b][h][n] W_A[c][h]  (m = b N + n, H <= 32),
-// in the storage dtype.  A workgroup takes RB token rows: their dz values
-// go to LDS (zero past H), each thread keeps its column's W_A row in
-// registers and walks the rows, so dXf and dX move in coalesced rows.
-constexpr int RB = 16;
-template <int ET>
-__global__ __launch_bounds__(256) void rank_heads_add_kernel(const float* __restrict__ dXf, const float* __restrict__ dz,
-                                                             const void* __restrict__ W_A, void* __restrict__ dX,
-                                                             int B, int N, int D, int H) {
-  __shared__ float dzs[RB][33];
-  const int M = B * N, m0 = blockIdx.x * RB;
-  const int rows = M - m0 < RB ? M - m0 : RB;
-  for (int i = threadIdx.x; i < RB * 32; i += 256) {
-    const int r = i >> 5, h = i & 31;
-    float v = 0.f;
-    if (r < rows && h < H) {
-      const int m = m0 + r, b = m / N, n = m - b * N;
-      v = dz[((size_t)b * H + h) * N + n];
-    }
-    dzs[r][h] = v;
-  }
-  __syncthreads();
-  for (int c = threadIdx.x; c < D; c += 256) {
-    float w[32];
+    float f[VE];
 #pragma unroll
-    for (int h = 0; h < 32; ++h) w[h] = h < H ? ld_elem<ET>(W_A, (size_t)c * H + h) : 0.f;
-    for (int r = 0; r < rows; ++r) {
-      const size_t i = (size_t)(m0 + r) * D + c;
-      float acc = dXf[i];
-#pragma unroll
-      for (int h = 0; h < 32; ++h) acc = fmaf(dzs[r][h], w[h], acc);
-      st_elem<ET>(dX, i, acc);
+    for (int e = 0; e < VE; ++e) {
+      const int h = c0 - D + e;
+      f[e] = h < H ? dz[((size_t)b * H + h) * N + n] : 0.f;
     }
+    if constexpr (ET == ET_F32)
+      v = make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3]));
+    else
+      v = make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
   }
-}
-
-// dst [R][Cd] = the first Cd columns of src [R][Cs], storage dtype.
-template <int ET>
-__global__ __launch_bounds__(256) void take_cols_kernel(const void* __restrict__ src, void* __restrict__ dst, int R,
-                                                        int Cs, int Cd) {
-  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (size_t)R * Cd) return;
-  const size_t r = idx / Cd;
-  const int c = (int)(idx - r * Cd);
-  st_elem<ET>(dst, idx, ld_elem<ET>(src, r * Cs + c));
+  reinterpret_cast<uint4*>(P)[idx] = v;
 }
 
 unsigned blocks_for(size_t n) { return (unsigned)((n + 255) / 256); }
+
+// The split-K partial products summed: over s = 0, 1, .. S - 1 in order,
+// src [S][R][Cs] fp32; columns 0 .. C1 - 1 go to dst1 [R][C1] and columns
+// C1 .. C1 + C2 - 1 to dst2 [R][C2] (storage dtype).
+template <int ET>
+__global__ __launch_bounds__(256) void sum_slices_kernel(const float* __restrict__ src, void* __restrict__ dst1,
+                                                         void* __restrict__ dst2, int S, int R, int Cs, int C1, int C2) {
+  const int C = C1 + C2;
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (size_t)R * C) return;
+  const size_t r = idx / C;
+  const int c = (int)(idx - r * C);
+  const size_t slab = (size_t)R * Cs;
+  float acc = 0.f;
+  for (int k = 0; k < S; ++k) acc += src[k * slab + r * Cs + c];
+  if (c < C1)
+    st_elem<ET>(dst1, r * C1 + c, acc);
+  else
+    st_elem<ET>(dst2, r * C2 + (c - C1), acc);
+}
 
 // Zero n bytes at p (16-byte aligned): 16-byte stores, then the byte tail.
 __global__ __launch_bounds__(256) void zero_kernel(unsigned char* __restrict__ p, size_t n) {
@@ -144,21 +129,21 @@ hipError_t launch_transpose(int et, const void* src, void* dst, int R, int C, in
 
 hipError_t launch_pack_grads(int et, const void* dV, const float* dz, void* P, int B, int N, int D, int H, int Hp,
                              hipStream_t s, const LaunchTiming* t) {
-  const size_t n = (size_t)B * N * (D + Hp);
-  if (n == 0 || Hp < H || blocks_for(n) > 0x7fffffffu) return hipErrorInvalidValue;
+  const size_t n = (size_t)B * N * ((D + Hp) / (et == ET_F32 ? 4 : 8));  // 16-byte chunks
+  if (n == 0 || Hp < H || D % 8 != 0 || Hp % 8 != 0 || blocks_for(n) > 0x7fffffffu) return hipErrorInvalidValue;
   return et == ET_F32
              ? launch_k(pack_grads_kernel<ET_F32>, dim3(blocks_for(n)), dim3(256), 0, s, t, dV, dz, P, B, N, D, H, Hp)
              : launch_k(pack_grads_kernel<ET_BF16>, dim3(blocks_for(n)), dim3(256), 0, s, t, dV, dz, P, B, N, D, H, Hp);
 }
 
-hipError_t launch_rank_heads_add(int et, const float* dXf, const float* dz, const void* W_A, void* dX, int B, int N,
-                                 int D, int H, hipStream_t s, const LaunchTiming* t) {
-  const size_t nb = ((size_t)B * N + RB - 1) / RB;
-  if (nb == 0 || H > 32 || nb > 0x7fffffffu) return hipErrorInvalidValue;
-  return et == ET_F32
-             ? launch_k(rank_heads_add_kernel<ET_F32>, dim3((unsigned)nb), dim3(256), 0, s, t, dXf, dz, W_A, dX, B, N, D, H)
-             : launch_k(rank_heads_add_kernel<ET_BF16>, dim3((unsigned)nb), dim3(256), 0, s, t, dXf, dz, W_A, dX, B, N, D,
-                        H);
+hipError_t launch_sum_slices(int et, const float* src, void* dst1, void* dst2, int S, int R, int Cs, int C1, int C2,
+                             hipStream_t s, const LaunchTiming* t) {
+  const size_t n = (size_t)R * (C1 + C2);
+  if (n == 0 || S < 1 || C1 + C2 > Cs || blocks_for(n) > 0x7fffffffu) return hipErrorInvalidValue;
+  return et == ET_F32 ? launch_k(sum_slices_kernel<ET_F32>, dim3(blocks_for(n)), dim3(256), 0, s, t, src, dst1, dst2, S,
+                                 R, Cs, C1, C2)
+                      : launch_k(sum_slices_kernel<ET_BF16>, dim3(blocks_for(n)), dim3(256), 0, s, t, src, dst1, dst2,
+                                 S, R, Cs, C1, C2);
 }
 
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s, const LaunchTiming* t) {
@@ -166,14 +151,6 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t s, const LaunchTiming*
   const size_t nb = blocks_for((bytes + 15) / 16);
   if (nb > 0x7fffffffu) return hipErrorInvalidValue;
   return launch_k(zero_kernel, dim3((unsigned)nb), dim3(256), 0, s, t, reinterpret_cast<unsigned char*>(p), bytes);
-}
-
-hipError_t launch_take_cols(int et, const void* src, void* dst, int R, int Cs, int Cd, hipStream_t s,
-                            const LaunchTiming* t) {
-  const size_t n = (size_t)R * Cd;
-  if (n == 0 || Cd > Cs || blocks_for(n) > 0x7fffffffu) return hipErrorInvalidValue;
-  return et == ET_F32 ? launch_k(take_cols_kernel<ET_F32>, dim3(blocks_for(n)), dim3(256), 0, s, t, src, dst, R, Cs, Cd)
-                      : launch_k(take_cols_kernel<ET_BF16>, dim3(blocks_for(n)), dim3(256), 0, s, t, src, dst, R, Cs, Cd);
 }
 
 }  // namespace cat

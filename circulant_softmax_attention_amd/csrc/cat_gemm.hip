@@ -164,10 +164,15 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void gemm_xw_kernel(GemmArgs a) {
     ct -= a.seg[si].ntiles;
     ++si;
   }
-  const GemmSeg sg = a.seg[si];
+  GemmSeg sg = a.seg[si];
   const int m0 = rt * BM, n0 = ct * BN;
-  const int M = a.M, K = a.K, ncols = sg.ncols;
-  const int ldx = a.ldx > 0 ? a.ldx : K;  // X row pitch (elements)
+  // split K: slice blockIdx.y covers K positions kbase .. kbase + K - 1 and
+  // writes its fp32 partial products to its own [M][ncols] slab of out
+  const int kbase = (int)blockIdx.y * a.kchunk;
+  const int M = a.M, K = a.K - kbase < a.kchunk ? a.K - kbase : a.kchunk, ncols = sg.ncols;
+  const int ldx = a.ldx > 0 ? a.ldx : a.K;  // X row pitch (elements)
+  if (blockIdx.y > 0)
+    sg.out = reinterpret_cast<char*>(sg.out) + (size_t)blockIdx.y * M * ncols * (ET == ET_F32 || sg.out_f32 ? 4 : ESZ);
 
   // Score projection (first segment only): the first nct <= BM / 16 column
   // tiles of a row panel share its BM / 16 16-row blocks, block rb going to
@@ -192,7 +197,7 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void gemm_xw_kernel(GemmArgs a) {
   for (int i = 0; i < 4; ++i) {
     const int r = (tid >> 3) + (NTHR / 8) * i;
     const int am = m0 + r < M ? m0 + r : M - 1;
-    asrc[i] = reinterpret_cast<const elem_t*>(a.X) + (size_t)am * ldx + kch;
+    asrc[i] = reinterpret_cast<const elem_t*>(a.X) + (size_t)am * ldx + kbase + kch;
   }
   // W tile, K-major as W is stored: slot s = tid + 256 i is K row s / CPRB,
   // position s % CPRB, and holds column chunk (position - rot(row)) mod CPRB.
@@ -207,7 +212,7 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void gemm_xw_kernel(GemmArgs a) {
     int col = n0 + c * VE;
     col = col + VE <= ncols ? col : ncols - VE;
     brow[i] = k;
-    bsrc[i] = reinterpret_cast<const elem_t*>(sg.W) + (size_t)k * ncols + col;
+    bsrc[i] = reinterpret_cast<const elem_t*>(sg.W) + (size_t)(kbase + k) * ncols + col;
   }
   const uint32_t lds0 = lds_addr(smem) + (uint32_t)wave * 64 * 16;
   // W_A tile: 16-byte chunk c = tid of the K tile's BK nz contiguous values
@@ -415,7 +420,7 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void gemm_xw_kernel(GemmArgs a) {
     const int rows = M - m0 < BM ? M - m0 : BM;
     const uint32_t spr = (uint32_t)(K * ESZ + 63) / 64;  // sectors per row
     const uint32_t nsec = (uint32_t)rows * spr;
-    const char* xb = reinterpret_cast<const char*>(a.X) + (size_t)m0 * ldx * ESZ;
+    const char* xb = reinterpret_cast<const char*>(a.X) + ((size_t)m0 * ldx + kbase) * ESZ;
 #pragma unroll
     for (int u = 0; u < WARM; ++u) {
       uint32_t sidx = (uint32_t)ctg + (uint32_t)a.ncoltiles * (uint32_t)(tid + NTHR * u);
@@ -624,7 +629,7 @@ hipError_t launch_gemm_bn(int et, GemmArgs& a, hipStream_t stream, const LaunchT
     a.ncoltiles += a.seg[s].ntiles;
   }
   const int rowtiles = (a.M + BM - 1) / BM;
-  const dim3 grid((unsigned)(rowtiles * a.ncoltiles)), block(2 * BM);
+  const dim3 grid((unsigned)(rowtiles * a.ncoltiles), (unsigned)a.ksplit), block(2 * BM);
   a.warm = a.ncoltiles > 8 ? 1 : 0;  // the L2 warm-up measured faster at 9 column tiles, slower at 4 and 8
   const int zb = (a.nz + 15) / 16;
   const bool tr = a.nz % 4 == 0;
@@ -663,6 +668,19 @@ hipError_t launch_gemm(int et, GemmArgs a, hipStream_t stream, const LaunchTimin
   a.fd_nz = make_fastdiv((uint32_t)(a.nz > 0 ? a.nz : 1));
   if (a.nz < 0 || a.nz > ZMAX || (a.nz > 0 && (a.Wz == nullptr || a.z == nullptr))) return hipErrorInvalidValue;
   if (a.ldx != 0 && (a.ldx < a.K || a.ldx % (et == ET_F32 ? 4 : 8) != 0)) return hipErrorInvalidValue;
+  // split K: slices of kchunk (a multiple of the K tile) K positions, each
+  // writing fp32 row-major partial products; no score projection
+  if (a.ksplit <= 1) {
+    a.ksplit = 1;
+    a.kchunk = a.K;
+  } else {
+    const int bk = et == ET_F32 ? 32 : 64;
+    if (a.nz != 0 || a.kchunk < bk || a.kchunk % bk != 0 || (long)(a.ksplit - 1) * a.kchunk >= a.K ||
+        (long)a.ksplit * a.kchunk < a.K || a.ksplit > 65535)
+      return hipErrorInvalidValue;
+    for (int s = 0; s < a.nseg; ++s)
+      if (a.seg[s].layout != OUT_ROWMAJOR || !a.seg[s].out_f32) return hipErrorInvalidValue;
+  }
   for (int s = 0; s < a.nseg; ++s)
     if (a.seg[s].ncols % (et == ET_F32 ? 4 : 8) != 0) return hipErrorInvalidValue;  // whole 16-byte column chunks
   for (int s = 0; s < a.nseg; ++s) {

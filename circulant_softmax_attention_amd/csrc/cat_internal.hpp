@@ -79,6 +79,10 @@ struct GemmArgs {
   const void* X;  // [M][K] row-major, rows ldx elements apart
   int M, K;
   int ldx;  // X row pitch in elements, a multiple of 16 bytes (0: K)
+  // split K (ksplit > 1): slice s takes K positions s kchunk .. and writes
+  // segment outputs (row-major fp32 only) at out + s M ncols; no score
+  // projection.  ksplit <= 1: one slice.
+  int ksplit, kchunk;
   int Ntok, H, d;
   int nseg;
   // optional score projection (1D): z [M / Ntok][nz][Ntok] fp32 = X . Wz,
@@ -188,20 +192,20 @@ hipError_t launch_score_partial(const LineGeom& g, const ScoreArgs& a, hipStream
                                 const LaunchTiming* t = nullptr);
 // Projection-gradient helpers of the CAT backward (cat_backward.hip), storage
 // dtype et: dst [C][ldd] = src [R][C]^T with columns R .. ldd - 1 zero;
-// P [B N][D + Hp] = [dV | dz token-major | 0] (Hp >= H; D = 0: the dz block
-// alone, dV unused); dX = dXf + dz^T W_A^T (W_A [D][H], H <= 32);
-// dst [R][Cd] = the first Cd columns of src [R][Cs].
+// P [B N][D + Hp] = [dV | dz token-major | 0] (Hp >= H; D and Hp multiples
+// of 8).
 hipError_t launch_transpose(int et, const void* src, void* dst, int R, int C, int ldd, hipStream_t s,
                             const LaunchTiming* t = nullptr);
 hipError_t launch_pack_grads(int et, const void* dV, const float* dz, void* P, int B, int N, int D, int H, int Hp,
                              hipStream_t s, const LaunchTiming* t = nullptr);
-hipError_t launch_rank_heads_add(int et, const float* dXf, const float* dz, const void* W_A, void* dX, int B, int N,
-                                 int D, int H, hipStream_t s, const LaunchTiming* t = nullptr);
+// The sum of the S slabs of src [S][R][Cs] fp32, slabs added in order:
+// columns 0 .. C1 - 1 to dst1 [R][C1], C1 .. C1 + C2 - 1 to dst2 [R][C2]
+// (storage dtype).
+hipError_t launch_sum_slices(int et, const float* src, void* dst1, void* dst2, int S, int R, int Cs, int C1, int C2,
+                             hipStream_t s, const LaunchTiming* t = nullptr);
 // Zero `bytes` bytes at p (16-byte aligned) with a kernel (no memset node in
 // captured graphs).
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s, const LaunchTiming* t = nullptr);
-hipError_t launch_take_cols(int et, const void* src, void* dst, int R, int Cs, int Cd, hipStream_t s,
-                            const LaunchTiming* t = nullptr);
 // zr[bh][k] = z[bh][(N - k) mod N] for BH lines of N fp32 values.
 hipError_t launch_reverse_lines(const float* z, float* zr, int BH, int N, hipStream_t s,
                                 const LaunchTiming* t = nullptr);

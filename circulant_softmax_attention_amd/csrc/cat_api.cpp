@@ -195,8 +195,13 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
   const int64_t d = p->D / p->H;
   if (d % 2 != 0) return fail(CAT_ERR_INVALID_ARG, "head width d = D/H must be even");
   if (p->D % 8 != 0) return fail(CAT_ERR_INVALID_ARG, "D must be a multiple of 8");
-  if (p->B * p->N * p->D >= (int64_t(1) << 31) || p->B * p->H > (int64_t(1) << 24))
-    return fail(CAT_ERR_UNSUPPORTED, "problem too large (B*N*D must be < 2^31)");
+  {
+    // B N D < 2^31 and B H <= 2^24, tested without forming an overflowing product
+    const int64_t lim = (int64_t(1) << 31) - 1;
+    const bool big = p->N > lim || p->D > lim || p->N * p->D > lim || p->B > lim / (p->N * p->D) ||
+                     p->B > (int64_t(1) << 24) / p->H;
+    if (big) return fail(CAT_ERR_UNSUPPORTED, "problem too large (B*N*D must be < 2^31)");
+  }
 
   if (p->kind == CAT_1D && p->H > 32)
     return fail(CAT_ERR_UNSUPPORTED, "1D supports at most 32 heads (score projection fused into the GEMM)");

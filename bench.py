@@ -311,11 +311,18 @@ def run(args):
         return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dt).cuda()
 
     cat2d = args.variant == "cat2d"
+    avgkey, causal = args.variant == "avgkey", args.variant == "causal"
     if cat2d and wl.kind != "2d":
         raise SystemExit("--variant cat2d runs on 2D workloads")
+    if (avgkey or causal) and wl.kind != "1d":
+        raise SystemExit(f"--variant {args.variant} runs on 1D workloads")
     if wl.kind == "1d":
         plan = cat.cat_plan_create("1d", wl.dtype, wl.B, wl.N, wl.D, wl.H)
         weights = [dev(inp.W_A), dev(inp.W_V)]
+        if avgkey:
+            # the averaged-key variant's W_Q and W_K by the workload's weight recipe (seeded)
+            W_Q, W_K = W.extra_square_weights(wl, 2)
+            weights = [dev(W_Q), dev(W_K), dev(inp.W_V)]
     else:
         plan = cat.cat_plan_create("2d", wl.dtype, wl.B, wl.N, wl.D, wl.H, wl.Hg, wl.Wg)
         weights = [dev(inp.W_Q), dev(inp.W_K), dev(inp.W_V)]
@@ -334,7 +341,8 @@ def run(args):
     WS = [cat.alloc_workspace(plan) for _ in range(nsets)]
     log(f"transform {L} = {L1} x {L2}; {nsets} buffer sets of {set_bytes / 2**20:.1f} MiB")
 
-    fwd = cat.cat_forward_1d if wl.kind == "1d" else cat.cat_forward_cat_2d if cat2d else cat.cat_forward_bccb_2d
+    fwd = (cat.cat_forward_avgkey_1d if avgkey else cat.cat_forward_causal_1d if causal
+           else cat.cat_forward_1d if wl.kind == "1d" else cat.cat_forward_cat_2d if cat2d else cat.cat_forward_bccb_2d)
 
     def step(i):
         k = i % nsets
@@ -360,7 +368,9 @@ def run(args):
     ktimes = cat.cat_plan_kernel_times(plan)
     cat.cat_plan_set_timing(plan, False)
     conv_path = plan.conv_path()
-    if conv_path == "direct":  # the mixing launch is the direct product, not a transform
+    if causal:  # the causal direct product in the mixing slot
+        ktimes["causalconv"] = ktimes.pop("fftconv")
+    elif conv_path == "direct":  # the mixing launch is the direct product, not a transform
         ktimes["directconv"] = ktimes.pop("fftconv")
     if conv_path == "fft_matrix" and wl.Hg:  # 2D products on the matrix cores
         ktimes["fftconv_matrix"] = ktimes.pop("fftconv")
@@ -374,6 +384,20 @@ def run(args):
     model = kernel_model(dataclasses.replace(wl, kind="1d") if cat2d else wl, L, ngrp,
                          fused_spectrum=fused and conv_path == "fft_matrix",
                          direct=conv_path == "direct", multipass=conv_path == "fft_multipass")
+    T, s_ = wl.B * wl.N, (4 if wl.dtype == "f32" else 2)
+    if avgkey:
+        # V alone from the GEMM; the logits from four small launches (column
+        # sums of X, the mean key, the per-head score weights, X . w):
+        # X read twice, W_Q and W_K once, z written
+        model["project"] = dict(bytes=2 * T * wl.D * s_ + wl.D * wl.D * s_, flops=2.0 * T * wl.D * wl.D,
+                                unit=model["project"]["unit"])
+        model["avgkey_logits"] = dict(bytes=2 * T * wl.D * s_ + 2 * wl.D * wl.D * s_ + wl.B * wl.H * wl.N * 4,
+                                      flops=T * wl.D + 4.0 * wl.B * wl.D * wl.D + 2.0 * T * wl.D * wl.H, unit="valu_f32")
+    if causal:
+        # the masked direct product: N (N + 1) / 2 kept lags per (batch, head), 2 d flops each
+        model["causalconv"] = dict(bytes=2 * T * wl.D * s_ + wl.B * wl.H * wl.N * 4,
+                                   flops=1.0 * wl.B * wl.H * wl.N * (wl.N + 1) * wl.d,
+                                   unit="mfma_bf16" if s_ == 2 else "mfma_f32")
     kernels = {}
     ktimes = {k: v for k, v in ktimes.items() if v[1] > 0}  # kernels this path launched
     for k, (ms, n) in ktimes.items():
@@ -401,7 +425,7 @@ def run(args):
                     frac=round(achieved / peak, 4), traffic=measured_traffic(dom, wl.name, kd["launches_per_call"]),
                     hbm_frac=kd["hbm_frac"], compute_frac=kd["compute_frac"], us=kd["us"])
 
-    if wl.kind == "1d" and conv_path in ("fft_matrix", "direct") and not cat2d:
+    if wl.kind == "1d" and conv_path in ("fft_matrix", "direct") and args.variant is None:
         # the same mixing on the fp32 vector-ALU transforms (CAT_CONV=valu),
         # its kernels timed over K forward calls of a plan that takes them
         # (one buffer set; reported beside the step, not part of it)
@@ -445,7 +469,7 @@ def run(args):
         roofline["frac_of_copy"] = round(roofline["achieved"] / copy_gbs, 4)
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not (avgkey or causal):
         log("cpu baseline (oracle) ...")
         cpu = cpu_baseline(wl, inp, args.cpu_seconds, W_A=W_A if cat2d else None)
         log("cpu baseline:", cpu)
@@ -454,7 +478,8 @@ def run(args):
     value = tokens / (ms_per_step / 1000.0)
     line = {
         "metric": "circulant-attention tokens/s at N=1024,D=768; % of HBM roofline (1 GPU)"
-        if wl.name == W.HEADLINE else f"CAT-scored 2D tokens/s ({wl.name})" if cat2d
+        if wl.name == W.HEADLINE and args.variant is None else f"CAT-scored 2D tokens/s ({wl.name})" if cat2d
+        else f"averaged-key CAT tokens/s ({wl.name})" if avgkey else f"causal CAT tokens/s ({wl.name})" if causal
         else f"circulant-attention tokens/s ({wl.name})",
         "value": round(value, 1),
         "unit": "tokens/s",
@@ -468,7 +493,8 @@ def run(args):
         "vs_baseline": None,
         "dtype": dtype_label(wl.dtype, conv_path),
         "data": "synthetic (seeded PCG64: X~N(0,1), W~N(0,1/D))",
-        "config": {"workload": wl.name, "kind": "2d-cat-scored" if cat2d else wl.kind, "B": wl.B, "N": wl.N, "D": wl.D, "H": wl.H,
+        "config": {"workload": wl.name, "kind": "2d-cat-scored" if cat2d else f"1d-{args.variant}" if args.variant else wl.kind,
+                   "B": wl.B, "N": wl.N, "D": wl.D, "H": wl.H,
                    "grid": [wl.Hg, wl.Wg] if wl.kind == "2d" else None, "storage": wl.dtype,
                    "transform": [L, L1, L2], "mixing": conv_path, "global_batch": wl.B, "seq_len": wl.N, "parallelism": "none"},
         "e2e_hbm_frac": round(((2 * tokens * wl.D * esz) + sum(w.numel() * esz for w in weights))
@@ -649,8 +675,10 @@ def main():
     ap.add_argument("--workload", default=None, help="workload name (default: the N=1024, D=768 one)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--variant", choices=["cat2d"], default=None,
-                    help="cat2d: the CAT-scored 2D variant (cat_forward_cat_2d) on a 2D workload")
+    ap.add_argument("--variant", choices=["cat2d", "avgkey", "causal"], default=None,
+                    help="cat2d: the CAT-scored 2D variant (cat_forward_cat_2d) on a 2D workload; avgkey: the "
+                         "averaged-key variant (cat_forward_avgkey_1d), causal: causal CAT (cat_forward_causal_1d), "
+                         "on a 1D workload")
     ap.add_argument("--backward", nargs="?", const="mix", choices=["mix", "full"], default=None,
                     help="time a 1D backward instead of the forward: mix = cat_step_mix_backward_1d, "
                          "full = cat_backward_1d (dX, dW_A, dW_V)")

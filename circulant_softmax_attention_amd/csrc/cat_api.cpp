@@ -913,7 +913,7 @@ cat_status avgkey_logits(cat_plan plan, const void* X, const void* W_Q, const vo
   a.D = (int)plan->p.D;
   a.H = (int)plan->p.H;
   a.scale = 1.0f / std::sqrt((float)plan->d);
-  const LaunchTiming* ts[4] = {mk_at(mk, 8), mk_at(mk, 8), mk_at(mk, 8), mk_at(mk, 8)};
+  const LaunchTiming* ts[5] = {mk_at(mk, 8), mk_at(mk, 8), mk_at(mk, 8), mk_at(mk, 8), mk_at(mk, 8)};
   hipError_t e = launch_avgkey(plan->et, a, s, ts);
   if (e != hipSuccess) return hip_fail(e, "averaged-key logits launch");
   return check_sync(plan, "averaged-key logits");

@@ -26,14 +26,14 @@ struct cat_plan_s {
   LineGeom geom;
   int L;
   int G;             // complex lines per transform workgroup
-  int ng;            // line groups per head (d / 2 / G)
+  int ng;            // line groups per head (d / 2 / G; mconv: 8-channel groups, d / 8)
   bool mconv;        // 1D conv on the matrix cores (L = 1024, bf16, d % 16 == 0)
   bool direct;       // 1D direct circulant product on the matrix cores (bf16, N <= 256, d % 32 == 0)
   bool longn;        // 1D N beyond one workgroup's line: three passes over HBM
   bool bconv;        // 2D square grid (32 or 96 a side), bf16: the BCCB mixing on the matrix cores
-  void* d_ftab = nullptr;  // its bf16 DFT-matrix fragments
+  void* d_ftab = nullptr;  // bconv: its bf16 DFT-matrix fragments; mconv: its fp16 constant table
   int logL1, logL2;  // long path: L = 2^logL1 x 2^logL2
-  int cg;            // channels per group of the blocked V (2 G; 16 for mconv, 32 for direct)
+  int cg;            // channels per group of the blocked V (2 G; 8 for mconv, 32 for direct, 2 for bconv)
   int Gs;            // lines per spectrum workgroup
   int npair, ngrp, ppg;  // 2D score partials
   float2* d_tw;      // 1D inter-pass twiddles, L entries (null in 2D)
@@ -107,6 +107,27 @@ void bconv_host_table(int G, std::vector<uint16_t>& tab) {
             const double ang = two_pi * (double)(((long)j * k) % G) / (double)G;
             tab[o++] = bf16_rne(plane == 0 ? (float)std::cos(ang) : (float)(-std::sin(ang)));
           }
+}
+
+// The 1D matrix-core conv's constants (layout: mconv_table_halfs), fp16
+// rounded to nearest from double.
+void mconv_host_table(std::vector<uint16_t>& tab) {
+  tab.assign(mconv_table_halfs(), 0);
+  const double two_pi = 6.283185307179586476925286766559;
+  for (int q = 0; q < 8; ++q)
+    for (int lane = 0; lane < 64; ++lane)
+      for (int sl = 0; sl < 8; ++sl) {
+        const int x = (q >> 1) & 1, part = q & 1;
+        const int j = lane % 16 + 16 * x, k = 4 * (lane / 16) + sl % 4 + 16 * (sl / 4);
+        const bool twiddle = q >= 4;
+        const int L = twiddle ? 1024 : 32;
+        const double ang = two_pi * (double)(((long)j * k) % L) / (double)L;
+        const double v = (part == 0 ? std::cos(ang) : -std::sin(ang)) / (twiddle ? 32.0 : 1.0);
+        const _Float16 hv = (_Float16)v;
+        uint16_t u;
+        std::memcpy(&u, &hv, 2);
+        tab[((size_t)q * 64 + lane) * 8 + sl] = u;
+      }
 }
 
 size_t up256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -275,8 +296,8 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
                 bconv_supported((int)p->Hg) && d % 8 == 0;
     pl->G = G;
     pl->ng = d2 / G;
-    pl->cg = pl->direct ? 32 : pl->mconv ? 16 : pl->bconv ? 2 : 2 * G;
-    if (pl->mconv) pl->ng = (int)d / 16;
+    pl->cg = pl->direct ? 32 : pl->mconv ? 8 : pl->bconv ? 2 : 2 * G;
+    if (pl->mconv) pl->ng = (int)d / 8;
     if (pl->direct) pl->ng = (int)d / 32;
   }
   int Gs = 1;
@@ -427,9 +448,10 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
       return hip_fail(e, "hipMemcpy(twiddles)");
     }
   }
-  if (pl->bconv) {
+  if (pl->bconv || pl->mconv) {
     std::vector<uint16_t> tab;
-    bconv_host_table((int)p->Hg, tab);
+    if (pl->bconv) bconv_host_table((int)p->Hg, tab);
+    else mconv_host_table(tab);
     hipError_t e = hipMalloc(&pl->d_ftab, tab.size() * sizeof(uint16_t));
     if (e == hipSuccess) e = hipMemcpy(pl->d_ftab, tab.data(), tab.size() * sizeof(uint16_t), hipMemcpyHostToDevice);
     if (e != hipSuccess) {
@@ -615,6 +637,7 @@ ConvArgs conv_base(const cat_plan_s* pl, const void* Vblk, const float2* spec, v
   a.d = pl->d;
   a.G = pl->G;
   a.ng = pl->ng;
+  a.mtab = pl->mconv ? pl->d_ftab : nullptr;
   return a;
 }
 

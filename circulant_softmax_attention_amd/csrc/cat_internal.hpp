@@ -132,9 +132,10 @@ struct SpecArgs {
 struct ConvArgs {
   const void* V;      // BLOCKED [B][H][ng][N][2G], element type et
   const float2* spec; // [BH][L]
-  const float* logits;  // matrix-core conv only: when set, [BH][N] fp32 logits whose
-                        // softmax spectrum the conv computes itself (spec unused)
+  const float* logits;  // matrix-core and direct convs: [BH][N] fp32 logits whose
+                        // softmax (and its spectrum) the conv computes itself (spec unused)
   const float2* tw;   // 1D inter-pass twiddles (null for 2D; unused by the matrix-core conv)
+  const void* mtab;   // 1D matrix-core conv: its per-lane constant table (mconv_table_halfs fp16 values)
   void* O;            // [B][N][D], element type et
   int B, H, D, N, d;
   int G, log2G, ng;
@@ -178,9 +179,16 @@ hipError_t launch_spectrum(const LineGeom& g, int mode, const SpecArgs& a, hipSt
                            const LaunchTiming* t = nullptr);
 hipError_t launch_conv(const LineGeom& g, int et, const ConvArgs& a, hipStream_t s, const LaunchTiming* t = nullptr);
 // 1D FFT-convolution for L = 1024 with the radix-32 passes on the matrix
-// cores (bf16 storage): V BLOCKED with 16-channel groups (a.ng = d / 16),
-// N <= 1024, d % 16 == 0.
+// cores (bf16 storage), softmax spectrum of a.logits [BH][N] included (a.spec
+// unused): V BLOCKED with 8-channel groups (a.ng = d / 8), N <= 1024,
+// d % 16 == 0, a.logits and a.mtab set.
 hipError_t launch_mconv(const ConvArgs& a, hipStream_t s, const LaunchTiming* t = nullptr);
+// The matrix-core conv's constant table: [q][lane][slot s] fp16, q = 0..7:
+// F re, F im for x = 0 (q = 0, 1) and x = 1 (q = 2, 3), then the twiddle
+// W^(j k) / 32 re, im for x = 0 (q = 4, 5) and x = 1 (q = 6, 7), with
+// j = lane % 16 + 16 x, k = 4 (lane / 16) + s % 4 + 16 (s / 4),
+// F[j][k] = exp(-2 pi i (j k mod 32) / 32), W = exp(-2 pi i / 1024).
+constexpr size_t mconv_table_halfs() { return 8 * 64 * 8; }
 // 1D circulant mixing for N <= 256 as the direct product circ(z*) V on the
 // matrix cores, softmax of a.logits [BH][N] included: bf16 storage only
 // (et == ET_BF16), V BLOCKED with 32-channel groups (a.ng = d / 32),

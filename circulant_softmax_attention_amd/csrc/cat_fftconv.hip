@@ -104,6 +104,7 @@ hipError_t launch_score_partial(const LineGeom& g, const ScoreArgs& a, hipStream
   ScoreFn fn = e ? (a.et == ET_F32 ? e->score : e->score_bf16) : nullptr;
   if (!fn || a.cg < 2 || a.cg % 2 != 0 || a.npair % (a.cg / 2) != 0) return hipErrorInvalidValue;
   if (!g.twiddled && (a.et != ET_F32 || a.cg != 2)) return hipErrorInvalidValue;  // 2D reads fp32 pair lines
+  if (!g.twiddled && g.L1 == 96 && g.L2 == 96) return launch_score96(a, s, t);
   const size_t lds = 2 * line_lds_bytes(g);
   return launch_k(fn, dim3(a.BH * a.ngrp), dim3(2 * e->T), lds, s, t, a);
 }

@@ -198,6 +198,10 @@ hipError_t launch_dconv(int et, const ConvArgs& a, hipStream_t s, const LaunchTi
                         bool causal = false);
 hipError_t launch_score_partial(const LineGeom& g, const ScoreArgs& a, hipStream_t s,
                                 const LaunchTiming* t = nullptr);
+// The same partials on the 96 x 96 grid (cat_score96.hip): fp32 pair lines
+// (et == ET_F32, cg == 2), a.N == 9216, a.ngrp == ceil(npair / ppg); a.tw
+// unused.  launch_score_partial routes the 96 x 96 grid here.
+hipError_t launch_score96(const ScoreArgs& a, hipStream_t s, const LaunchTiming* t = nullptr);
 // Projection-gradient helpers of the CAT backward (cat_backward.hip), storage
 // dtype et: dst [C][ldd] = src [R][C]^T with columns R .. ldd - 1 zero;
 // P [B N][D + Hp] = [dV | dz token-major | 0] (Hp >= H; D and Hp multiples

@@ -565,6 +565,25 @@ def test_scores_2d(cat, Hg, Wg):
     assert_parity(probs, ref, "f32", "a*")
 
 
+@pytest.mark.parametrize("D,H", [(24, 4), (40, 4), (8, 4), (64, 1)])
+def test_scores_2d_96_pair_groups(cat, D, H):
+    """The 96 x 96 score kernel groups a head's channel pairs two to a
+    workgroup; an odd pair count (d = 6 or 10: 3 or 5 pairs) leaves one
+    group of a single pair, d = 2 a head of one pair, d = 64 the workload's
+    32 pairs."""
+    say("scores_2d_96_groups", D, H)
+    import torch
+    B, G = 1, 96
+    rng = np.random.default_rng(D * 10 + H)
+    Q = (rng.standard_normal((B, G * G, D)) * 0.5).astype(np.float32)
+    K = (rng.standard_normal((B, G * G, D)) * 0.5).astype(np.float32)
+    plan = cat.cat_plan_create("2d", "f32", B, G * G, D, H, G, G)
+    probs = to_np(cat.cat_step_scores_2d(plan, torch.from_numpy(Q).cuda(), torch.from_numpy(K).cuda()))
+    a = oracle.scores_bccb_2d(Q, K, G, G, H)
+    ref = oracle.softmax(a.reshape(B, H, -1))
+    assert_parity(probs, ref, "f32", "a*")
+
+
 @pytest.mark.parametrize("Hg,Wg,dtype", [(g[0], g[1], "f32") for g in GRIDS] +
                          [(12, 12, "bf16"), (32, 32, "f32"), (32, 32, "bf16"), (96, 96, "f32"), (96, 96, "bf16")])
 def test_mix_2d(cat, Hg, Wg, dtype):

@@ -30,19 +30,25 @@
 // lane group g stands for index 4 g + (s mod 4) + 16 (s / 4) within a K step
 // of 32, the order a result's rows come in; the constant operands use the
 // same order.  Signs live on the data operands: the constant fragments are
-// used as stored, and the (-1)^k that separates DFT rows j and j + G/2
-// becomes a sign flip of the data's odd K slots.
+// used as stored (real and imaginary parts only), each data operand carries
+// the negated part its products need (-im for the forward transform, -re
+// for the inverse), and the (-1)^k that separates DFT rows j and j + G/2
+// becomes a sign flip of the data's odd K slots, applied in place once the
+// lower-half tiles are done.
 //
-// Work split: a workgroup of four waves takes four channel pairs of one head
-// (8 channels).  Wave w carries pair w through passes 1-3 in an LDS buffer
-// of its own: pass 1 streams the pair's block from memory once, row tile by
-// row tile, and writes D1 kc-major (rows kc, 16-column bands = kc tiles);
-// passes 2-3 then take one band at a time, reading its D1 rows and writing
-// the band's D3 rows in their place.  Pass 4 contracts kc, so it waits for
-// all four buffers and is split by output tiles: its D3 operand (kc in the K
-// slots, one r' per lane) comes from transposing LDS reads of the kc-major
-// buffer, and each lane produces one token for all four pairs, a 16-byte
-// store of 8 channels per token into O [B][N][D].
+// Work split: a workgroup of eight waves takes four channel pairs of one
+// head (8 channels); waves w and w + 4 carry pair w through passes 1-3 in
+// the pair's LDS buffer.  Pass 1 streams the pair's block from memory once,
+// row tile by row tile (the two waves take alternate row tiles), and writes
+// D1 kc-major (rows kc, 16-column bands = kc tiles); passes 2-3 then take
+// one band at a time (alternate bands per wave), reading its D1 rows and
+// writing the band's D3 rows in their place.  Pass 4 contracts kc, so it
+// waits for all four buffers and is split by output tiles over the eight
+// waves: its D3 operand (kc in the K slots, one r' per lane) comes from
+// transposing LDS reads of the kc-major buffer, and each lane produces one
+// token for all four pairs, a 16-byte store of 8 channels per token into O
+// [B][N][D].  Two waves per SIMD hide each other's LDS and memory waits;
+// the constant fragments (real and imaginary parts) stay in registers.
 //
 // Layouts: V BLOCKED with 2-channel groups ([B][H][d/2][N][2], one pair's
 // grid contiguous); S [BH][kr][kc] complex fp32 with kc contiguous; the DFT
@@ -58,7 +64,7 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4;
 
 namespace {
 
-constexpr int BT = 256;  // four waves, four channel pairs
+constexpr int BT = 512;  // eight waves, four channel pairs
 
 template <int G>
 struct BC {
@@ -72,7 +78,12 @@ struct BC {
 
 // 8 values (one K-slot run) of one part as raw bits.
 typedef uint4 raw8;
-struct CX {  // complex operand: re, im
+// A data operand: real and imaginary parts and the negated part its products
+// take (-im in the forward transform, -re in the inverse).
+struct CX {
+  raw8 re, im, n;
+};
+struct KF {  // a constant fragment
   raw8 re, im;
 };
 struct CT {
@@ -87,46 +98,49 @@ __device__ __forceinline__ raw8 xr8(const raw8& x, uint32_t m) { return make_uin
 constexpr uint32_t NEG = 0x80008000u;  // every slot negated
 constexpr uint32_t ODD = 0x80000000u;  // odd slots (high halves) negated
 
-// A constant fragment with its negated imaginary part alongside.
-struct KX {
-  raw8 re, im, nim;
-};
-__device__ __forceinline__ KX kx(const raw8& re, const raw8& im) { return KX{re, im, xr8(im, NEG)}; }
-// The odd-slot flip of a data operand: (-1)^k on the data stands for the
-// upper-half DFT tile (rows j + G / 2) of the constant it meets.
-__device__ __forceinline__ CX flip(const CX& d) { return CX{xr8(d.re, ODD), xr8(d.im, ODD)}; }
+// Forward data operand from its parts; the inverse one.
+__device__ __forceinline__ CX fwd(const raw8& re, const raw8& im) { return CX{re, im, xr8(im, NEG)}; }
+__device__ __forceinline__ CX inv(const raw8& re, const raw8& im) { return CX{re, im, xr8(re, NEG)}; }
+// The odd-slot flip, in place: (-1)^k on the data stands for the upper-half
+// DFT tile (rows j + G / 2) of the constant it meets.
+__device__ __forceinline__ void flip(CX& d) {
+  d.re = xr8(d.re, ODD);
+  d.im = xr8(d.im, ODD);
+  d.n = xr8(d.n, ODD);
+}
 
 // acc += data (A operand, rows kept) x constant (B):
-//   (dr + i di)(kr + i ki)          = dr kr + di (-ki) + i (dr ki + di kr)
-//   (dr + i di)(kr - i ki) (CONJ)   = dr kr + di ki + i (dr (-ki) + di kr)
-template <bool CONJ>
-__device__ __forceinline__ void mulA(const CX& d, const KX& k, CT& acc) {
-  acc.re = mm(d.im, CONJ ? k.im : k.nim, mm(d.re, k.re, acc.re));
-  acc.im = mm(d.im, k.re, mm(d.re, CONJ ? k.nim : k.im, acc.im));
+//   forward (n = -di):  (dr + i di)(kr + i ki) = dr kr + (-di) ki + i (dr ki + di kr)
+//   inverse (n = -dr):  (dr + i di)(kr - i ki) = dr kr + di ki + i (di kr + (-dr) ki)
+__device__ __forceinline__ void mulA_f(const CX& d, const KF& k, CT& acc) {
+  acc.re = mm(d.n, k.im, mm(d.re, k.re, acc.re));
+  acc.im = mm(d.im, k.re, mm(d.re, k.im, acc.im));
+}
+__device__ __forceinline__ void mulA_i(const CX& d, const KF& k, CT& acc) {
+  acc.re = mm(d.im, k.im, mm(d.re, k.re, acc.re));
+  acc.im = mm(d.n, k.im, mm(d.im, k.re, acc.im));
 }
 // acc += constant (A) x data (B operand, columns kept), same forms.
-template <bool CONJ>
-__device__ __forceinline__ void mulB(const KX& k, const CX& d, CT& acc) {
-  acc.re = mm(CONJ ? k.im : k.nim, d.im, mm(k.re, d.re, acc.re));
-  acc.im = mm(CONJ ? k.nim : k.im, d.re, mm(k.re, d.im, acc.im));
+__device__ __forceinline__ void mulB_f(const KF& k, const CX& d, CT& acc) {
+  acc.re = mm(k.im, d.n, mm(k.re, d.re, acc.re));
+  acc.im = mm(k.im, d.re, mm(k.re, d.im, acc.im));
 }
-// K operand whose slot v + 4 y takes value v of tile y, rounded to bf16.
-__device__ __forceinline__ CX stack(const CT& t0, const CT& t1) {
-  CX r;
-  r.re = make_uint4(pack_bf16x2(t0.re[0], t0.re[1]), pack_bf16x2(t0.re[2], t0.re[3]), pack_bf16x2(t1.re[0], t1.re[1]),
+__device__ __forceinline__ void mulB_i(const KF& k, const CX& d, CT& acc) {
+  acc.re = mm(k.im, d.im, mm(k.re, d.re, acc.re));
+  acc.im = mm(k.im, d.n, mm(k.re, d.im, acc.im));
+}
+// Parts of a K operand whose slot v + 4 y takes value v of tile y, rounded to bf16.
+__device__ __forceinline__ raw8 stack_re(const CT& t0, const CT& t1) {
+  return make_uint4(pack_bf16x2(t0.re[0], t0.re[1]), pack_bf16x2(t0.re[2], t0.re[3]), pack_bf16x2(t1.re[0], t1.re[1]),
                     pack_bf16x2(t1.re[2], t1.re[3]));
-  r.im = make_uint4(pack_bf16x2(t0.im[0], t0.im[1]), pack_bf16x2(t0.im[2], t0.im[3]), pack_bf16x2(t1.im[0], t1.im[1]),
+}
+__device__ __forceinline__ raw8 stack_im(const CT& t0, const CT& t1) {
+  return make_uint4(pack_bf16x2(t0.im[0], t0.im[1]), pack_bf16x2(t0.im[2], t0.im[3]), pack_bf16x2(t1.im[0], t1.im[1]),
                     pack_bf16x2(t1.im[2], t1.im[3]));
-  return r;
 }
 // Two pair words (re | im << 16 each) -> the low halves and the high halves.
 __device__ __forceinline__ uint32_t lo2(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
 __device__ __forceinline__ uint32_t hi2(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
-// LDS position of index x (0 <= x < G) along a K-contracted row: the 8 slots
-// of lane group g in K step t sit at 32 t + 8 g + 0 .. 7.
-__device__ __forceinline__ int kpos(int x) {
-  return (x & ~31) + 8 * ((x >> 2) & 3) + 4 * ((x >> 4) & 1) + (x & 3);
-}
 __device__ __forceinline__ CT zero_ct() {
   CT c;
   c.re = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -144,6 +158,10 @@ __device__ __forceinline__ uint2 ds_tr(const uint16_t* p) {
   return __builtin_bit_cast(uint2, r);
 }
 
+// Work units: a.nfull quads (four pairs, 16-byte stores of 8 channels per
+// token), then a.nhalf half-quads (two pairs, 8-byte stores) that continue
+// the order (b, h, pair) after the quads; the workgroups stride over each
+// list.  A unit of NPW pairs has 8 / NPW waves per pair.
 template <int G>
 __global__ __launch_bounds__(BT) void bconv_kernel(BconvArgs a) {
   using P = BC<G>;
@@ -159,29 +177,33 @@ __global__ __launch_bounds__(BT) void bconv_kernel(BconvArgs a) {
   // DFT fragments kf[i][t] for i < NH: lane (lo, grp), slot s ->
   // F[lo + 16 i][32 t + 4 grp + s % 4 + 16 (s / 4)]; tile i + NH is tile i
   // times (-1)^k, k having the parity of s.
-  KX kf[NH][KS];
+  KF kf[NH][KS];
 #pragma unroll
   for (int i = 0; i < NH; ++i)
 #pragma unroll
     for (int t = 0; t < KS; ++t) {
       const uint4* src = reinterpret_cast<const uint4*>(a.table) + ((size_t)(i * KS + t) * 2) * 64 + lane;
-      kf[i][t] = kx(src[0], src[64]);
+      kf[i][t] = KF{src[0], src[64]};
     }
 
-  const int qpb = a.npair / 4;  // quads of pairs per (b, h)
-  const int nquads = a.BH * qpb;
-  const int q0 = xcd_remap(blockIdx.x, gridDim.x);
-  for (int q = q0; q < nquads; q += gridDim.x) {
-    const int bh = q / qpb, pq = q - bh * qpb;
+  const int uq0 = xcd_remap(blockIdx.x, gridDim.x);
+  auto run_units = [&](auto npw, int u0, int nu) {
+  constexpr int NPW = decltype(npw)::value;
+  constexpr int WPP = 8 / NPW;                    // waves per pair
+  const int pw = wave % NPW, half = wave / NPW;  // the wave's pair, and which of its waves
+  const int upb = a.npair / NPW;                 // units per (b, h)
+  for (int uq = uq0; uq < nu; uq += gridDim.x) {
+    const int q = u0 + uq;
+    const int bh = q / upb, pq = q - bh * upb;  // unit pq: pairs NPW pq ..
     const int b = bh / a.H, h = bh - b * a.H;
     const float2* spec = a.spec + (size_t)bh * N;
-    uint16_t* e = es[wave];
+    uint16_t* e = es[pw];
 
-    // ---- pass 1 (wave w, pair 4 pq + w): row tile by row tile, the pair's
-    // words streamed from memory once (two row tiles in flight), D1 of all
-    // kc tiles written to LDS
+    // ---- pass 1 (pair NPW pq + pw, row tiles half, half + WPP, ...): the
+    // pair's words streamed from memory once (two row tiles in flight), D1
+    // of all kc tiles written to LDS
     {
-      const uint32_t* vp = reinterpret_cast<const uint32_t*>(a.V) + ((size_t)bh * a.npair + 4 * pq + wave) * N;
+      const uint32_t* vp = reinterpret_cast<const uint32_t*>(a.V) + ((size_t)bh * a.npair + NPW * pq + pw) * N;
       uint4 w[2][KS][2];
       auto fetch = [&](int slot, int ri) {
 #pragma unroll
@@ -191,28 +213,29 @@ __global__ __launch_bounds__(BT) void bconv_kernel(BconvArgs a) {
           w[slot][t][1] = *reinterpret_cast<const uint4*>(row + 16);  // c + 16
         }
       };
-      fetch(0, 0);
+      constexpr int NJ = (NT + WPP - 1) / WPP;
+      if (half < NT) fetch(0, half);
 #pragma unroll
-      for (int ri = 0; ri < NT; ++ri) {
+      for (int j = 0; j < NJ; ++j) {
+        const int ri = half + WPP * j;
+        if (ri >= NT) break;  // uniform across the wave
         CX x[KS];
 #pragma unroll
         for (int t = 0; t < KS; ++t) {
-          const uint4 w0 = w[ri & 1][t][0], w1 = w[ri & 1][t][1];
-          x[t].re = make_uint4(lo2(w0.x, w0.y), lo2(w0.z, w0.w), lo2(w1.x, w1.y), lo2(w1.z, w1.w));
-          x[t].im = make_uint4(hi2(w0.x, w0.y), hi2(w0.z, w0.w), hi2(w1.x, w1.y), hi2(w1.z, w1.w));
+          const uint4 w0 = w[j & 1][t][0], w1 = w[j & 1][t][1];
+          x[t] = fwd(make_uint4(lo2(w0.x, w0.y), lo2(w0.z, w0.w), lo2(w1.x, w1.y), lo2(w1.z, w1.w)),
+                     make_uint4(hi2(w0.x, w0.y), hi2(w0.z, w0.w), hi2(w1.x, w1.y), hi2(w1.z, w1.w)));
         }
-        if (ri + 1 < NT) fetch((ri + 1) & 1, ri + 1);
-        CX xf[KS];
-#pragma unroll
-        for (int t = 0; t < KS; ++t) xf[t] = flip(x[t]);
+        if (j + 1 < NJ && ri + WPP < NT) fetch((j + 1) & 1, ri + WPP);
 #pragma unroll
         for (int kt = 0; kt < NT; ++kt) {
+          if (kt == NH) {
+#pragma unroll
+            for (int t = 0; t < KS; ++t) flip(x[t]);
+          }
           CT d1 = zero_ct();
 #pragma unroll
-          for (int t = 0; t < KS; ++t) {
-            if (kt < NH) mulA<false>(x[t], kf[kt][t], d1);
-            else mulA<false>(xf[t], kf[kt - NH][t], d1);
-          }
+          for (int t = 0; t < KS; ++t) mulA_f(x[t], kf[kt < NH ? kt : kt - NH][t], d1);
           // rows r = 16 ri + 4 grp + v, col kc = 16 kt + lo -> es[kc][r .. r + 3]
           const int o = (16 * kt + lo) * PITCH + 16 * ri + 4 * grp;
           *reinterpret_cast<uint2*>(e + o) = make_uint2(pack_bf16x2(d1.re[0], d1.re[1]), pack_bf16x2(d1.re[2], d1.re[3]));
@@ -222,19 +245,12 @@ __global__ __launch_bounds__(BT) void bconv_kernel(BconvArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    __syncthreads();  // both waves' row tiles of each pair
 
-    // ---- passes 2-3, one kc band at a time (band kt: rows 16 kt .. 16 kt + 15)
+    // ---- passes 2-3, one kc band at a time (band kt: rows 16 kt .. 16 kt +
+    // 15), every WPP-th band per wave
 #pragma unroll 1
-    for (int kt = 0; kt < NT; ++kt) {
-      // the spectrum of this band, S[kr][kc], kr = 16 ki + 4 grp + v, kc = 16 kt + lo
-      float2 sv[NT][4];
-      {
-        const float2* sk = spec + 16 * kt + lo;
-#pragma unroll
-        for (int ki = 0; ki < NT; ++ki)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) sv[ki][v] = sk[(size_t)(16 * ki + 4 * grp + v) * G];
-      }
+    for (int kt = half; kt < NT; kt += WPP) {
       // pass 2 operand: D1[r slots][kc lanes] from the band's rows
       CX y[KS];
 #pragma unroll
@@ -243,51 +259,53 @@ __global__ __launch_bounds__(BT) void bconv_kernel(BconvArgs a) {
         const uint2 r0 = *reinterpret_cast<const uint2*>(e + o), r1 = *reinterpret_cast<const uint2*>(e + o + 16);
         const uint2 i0 = *reinterpret_cast<const uint2*>(e + PLANE + o),
                     i1 = *reinterpret_cast<const uint2*>(e + PLANE + o + 16);
-        y[t].re = make_uint4(r0.x, r0.y, r1.x, r1.y);
-        y[t].im = make_uint4(i0.x, i0.y, i1.x, i1.y);
+        y[t] = fwd(make_uint4(r0.x, r0.y, r1.x, r1.y), make_uint4(i0.x, i0.y, i1.x, i1.y));
       }
-      // pass 2 (rows kr = 16 ki + 4 grp + v, cols kc), two kr tiles at a
-      // time, each times the spectrum and stacked into pass 3's operand
-      CX yf[KS];
+      // pass 2 (rows kr = 16 ki + 4 grp + v, cols kc), each kr tile times the
+      // spectrum S[kr][kc] (kc = 16 kt + lo), two tiles stacked into pass 3's
+      // operand
+      const float2* sk = spec + 16 * kt + lo + (size_t)(4 * grp) * G;
+      raw8 zre[KS], zim[KS];
+      CT dprev;
 #pragma unroll
-      for (int t = 0; t < KS; ++t) yf[t] = flip(y[t]);
-      CX z[KS];
+      for (int ki = 0; ki < NT; ++ki) {
+        float2 sv[4];
 #pragma unroll
-      for (int tt = 0; tt < KS; ++tt) {
-        CT d2[2];
+        for (int v = 0; v < 4; ++v) sv[v] = sk[(size_t)(16 * ki + v) * G];
+        if (ki == NH) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int ki = 2 * tt + u;
-          d2[u] = zero_ct();
-#pragma unroll
-          for (int t = 0; t < KS; ++t) {
-            if (ki < NH) mulB<false>(kf[ki][t], y[t], d2[u]);
-            else mulB<false>(kf[ki - NH][t], yf[t], d2[u]);
-          }
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const float xr = d2[u].re[v], xi = d2[u].im[v];
-            const float2 sp = sv[ki][v];
-            d2[u].re[v] = fmaf(xr, sp.x, -xi * sp.y);
-            d2[u].im[v] = fmaf(xr, sp.y, xi * sp.x);
-          }
+          for (int t = 0; t < KS; ++t) flip(y[t]);
         }
-        z[tt] = stack(d2[0], d2[1]);
-        __builtin_amdgcn_sched_barrier(0);
+        CT d2 = zero_ct();
+#pragma unroll
+        for (int t = 0; t < KS; ++t) mulB_f(kf[ki < NH ? ki : ki - NH][t], y[t], d2);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float xr = d2.re[v], xi = d2.im[v];
+          d2.re[v] = fmaf(xr, sv[v].x, -xi * sv[v].y);
+          d2.im[v] = fmaf(xr, sv[v].y, xi * sv[v].x);
+        }
+        if (ki & 1) {
+          zre[ki / 2] = stack_re(dprev, d2);
+          zim[ki / 2] = stack_im(dprev, d2);
+        } else {
+          dprev = d2;
+        }
       }
       // pass 3 (data as B): D3[i] rows r' = 16 i + 4 grp + v, cols kc = 16 kt + lo
       // -> es[kc][r' .. r' + 3] (the band's rows, already read above)
-      CX zf[KS];
+      CX z[KS];
 #pragma unroll
-      for (int t = 0; t < KS; ++t) zf[t] = flip(z[t]);
+      for (int t = 0; t < KS; ++t) z[t] = inv(zre[t], zim[t]);
 #pragma unroll
       for (int i = 0; i < NT; ++i) {
+        if (i == NH) {
+#pragma unroll
+          for (int t = 0; t < KS; ++t) flip(z[t]);
+        }
         CT d3 = zero_ct();
 #pragma unroll
-        for (int t = 0; t < KS; ++t) {
-          if (i < NH) mulB<true>(kf[i][t], z[t], d3);
-          else mulB<true>(kf[i - NH][t], zf[t], d3);
-        }
+        for (int t = 0; t < KS; ++t) mulB_i(kf[i < NH ? i : i - NH][t], z[t], d3);
         const int o = (16 * kt + lo) * PITCH + 16 * i + 4 * grp;
         *reinterpret_cast<uint2*>(e + o) = make_uint2(pack_bf16x2(d3.re[0], d3.re[1]), pack_bf16x2(d3.re[2], d3.re[3]));
         *reinterpret_cast<uint2*>(e + PLANE + o) =
@@ -296,62 +314,60 @@ __global__ __launch_bounds__(BT) void bconv_kernel(BconvArgs a) {
     }
     __syncthreads();
 
-    // ---- pass 4: output tiles (rt, ct) of all four pairs; wave w takes the
-    // tiles w, w + 4, ...  D4 rows r' = 16 rt + 4 grp + v, cols c' = 16 ct + lo.
+    // ---- pass 4: output tiles (rt, ct) of the unit's pairs; wave w takes
+    // the tiles w, w + 8, ...  D4 rows r' = 16 rt + 4 grp + v, cols c' = 16 ct + lo.
     // Operand: D3[r' lanes][kc slots] by transposing reads of the kc-major planes.
     {
-      uint4* ob = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.O) + (size_t)b * N * a.D +
-                                           (size_t)h * a.d + 8 * pq);
-      const int Dq = a.D / 8;  // 16-byte chunks per token row of O
-      KX kc[2][KS];
-      auto fetch_kc = [&](const int buf, int ct) {
-        // column tile ct's constant (runtime index, (-1)^k of the upper half applied)
-        const int c0 = ct < NH ? ct : ct - NH;
-        const uint32_t fl = ct < NH ? 0u : ODD;
-#pragma unroll
-        for (int t = 0; t < KS; ++t) {
-          const uint4* src = reinterpret_cast<const uint4*>(a.table) + ((size_t)(c0 * KS + t) * 2) * 64 + lane;
-          kc[buf][t] = kx(xr8(src[0], fl), xr8(src[64], fl));
-        }
-      };
-      auto unit = [&](int u, auto bufc) {
-        constexpr int cur = decltype(bufc)::value;
-        const int rt = u / NT, ct = u - rt * NT;
-        if (u + 4 < NT * NT) fetch_kc(cur ^ 1, (u + 4) % NT);
-        uint32_t wv[4][4];  // [v][pair]
-#pragma unroll
-        for (int pp = 0; pp < 4; ++pp) {
-          CT d4 = zero_ct();
-#pragma unroll
-          for (int t = 0; t < KS; ++t) {
-            // slots 0..3: kc = 32 t + 4 grp + 0..3; slots 4..7: kc + 16;
-            // lane lo addresses row kc0 + lo / 4, columns 16 rt + 4 (lo % 4) ..
-            const int o = (32 * t + 4 * grp + (lo >> 2)) * PITCH + 16 * rt + 4 * (lo & 3);
-            const uint2 r0 = ds_tr(es[pp] + o), r1 = ds_tr(es[pp] + o + 16 * PITCH);
-            const uint2 i0 = ds_tr(es[pp] + PLANE + o), i1 = ds_tr(es[pp] + PLANE + o + 16 * PITCH);
-            CX x;
-            x.re = make_uint4(r0.x, r0.y, r1.x, r1.y);
-            x.im = make_uint4(i0.x, i0.y, i1.x, i1.y);
-            mulA<true>(x, kc[cur][t], d4);
-          }
-#pragma unroll
-          for (int v = 0; v < 4; ++v) wv[v][pp] = pack_bf16x2(d4.re[v], d4.im[v]);
-        }
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int n = (16 * rt + 4 * grp + v) * G + 16 * ct + lo;
-          ob[(size_t)n * Dq] = make_uint4(wv[v][0], wv[v][1], wv[v][2], wv[v][3]);
-        }
-      };
-      fetch_kc(0, wave % NT);
+      uint16_t* ob = reinterpret_cast<uint16_t*>(a.O) + (size_t)b * N * a.D + (size_t)h * a.d + 2 * NPW * pq;
 #pragma unroll 1
       for (int u = wave; u < NT * NT; u += 8) {
-        unit(u, std::integral_constant<int, 0>{});
-        if (u + 4 < NT * NT) unit(u + 4, std::integral_constant<int, 1>{});
+        const int rt = u / NT, ct = u - rt * NT;
+        // column tile ct's constant: one of the fragments in registers,
+        // chosen by a wave-uniform branch (a runtime index would send the
+        // fragments to scratch), (-1)^k of the upper half applied
+        const int c0 = ct < NH ? ct : ct - NH;
+        const uint32_t fl = ct < NH ? 0u : ODD;
+        auto tile = [&](const KF* kc) {
+          uint32_t wv[4][NPW];  // [v][pair]
+#pragma unroll
+          for (int pp = 0; pp < NPW; ++pp) {
+            CT d4 = zero_ct();
+#pragma unroll
+            for (int t = 0; t < KS; ++t) {
+              // slots 0..3: kc = 32 t + 4 grp + 0..3; slots 4..7: kc + 16;
+              // lane lo addresses row kc0 + lo / 4, columns 16 rt + 4 (lo % 4) ..
+              const int o = (32 * t + 4 * grp + (lo >> 2)) * PITCH + 16 * rt + 4 * (lo & 3);
+              const uint2 r0 = ds_tr(es[pp] + o), r1 = ds_tr(es[pp] + o + 16 * PITCH);
+              const uint2 i0 = ds_tr(es[pp] + PLANE + o), i1 = ds_tr(es[pp] + PLANE + o + 16 * PITCH);
+              mulA_i(inv(make_uint4(r0.x, r0.y, r1.x, r1.y), make_uint4(i0.x, i0.y, i1.x, i1.y)), kc[t], d4);
+            }
+#pragma unroll
+            for (int v = 0; v < 4; ++v) wv[v][pp] = pack_bf16x2(d4.re[v], d4.im[v]);
+          }
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int n = (16 * rt + 4 * grp + v) * G + 16 * ct + lo;
+            if constexpr (NPW == 4)
+              *reinterpret_cast<uint4*>(ob + (size_t)n * a.D) = make_uint4(wv[v][0], wv[v][1], wv[v][2], wv[v][3]);
+            else
+              *reinterpret_cast<uint2*>(ob + (size_t)n * a.D) = make_uint2(wv[v][0], wv[v][1]);
+          }
+        };
+        sfor<0, NH>([&](auto C) {
+          if (c0 == decltype(C)::value) {
+            KF kc[KS];
+#pragma unroll
+            for (int t = 0; t < KS; ++t) kc[t] = KF{xr8(kf[decltype(C)::value][t].re, fl), xr8(kf[decltype(C)::value][t].im, fl)};
+            tile(kc);
+          }
+        });
       }
     }
-    __syncthreads();  // es is rewritten by the next quad
+    __syncthreads();  // es is rewritten by the next unit
   }
+  };
+  run_units(std::integral_constant<int, 4>{}, 0, a.nfull);
+  run_units(std::integral_constant<int, 2>{}, 2 * a.nfull, a.nhalf);
 }
 
 }  // namespace
@@ -360,17 +376,25 @@ bool bconv_supported(int G) { return G == 32 || G == 96; }
 
 size_t bconv_table_halfs(int G) { return (size_t)(G / 32) * (G / 32) * 2 * 64 * 8; }
 
-hipError_t launch_bconv(const BconvArgs& a, int G, hipStream_t s, const LaunchTiming* t) {
-  if (!bconv_supported(G) || a.d % 8 != 0 || a.npair != a.d / 2 || a.BH < 1 || a.table == nullptr || a.D % 8 != 0)
+hipError_t launch_bconv(const BconvArgs& a0, int G, hipStream_t s, const LaunchTiming* t) {
+  if (!bconv_supported(G) || a0.d % 8 != 0 || a0.npair != a0.d / 2 || a0.BH < 1 || a0.table == nullptr ||
+      a0.D % 8 != 0)
     return hipErrorInvalidValue;
-  const long quads = (long)a.BH * (a.npair / 4);
-  if (quads > 0x7fffffffL) return hipErrorInvalidValue;
-  // one workgroup per compute unit (four pairs' D3 planes fill its LDS),
-  // each looping over quads; a multiple of 8 keeps the XCD-aware order
-  long nb = a.num_cu > 0 ? a.num_cu : 256;
-  if (nb > quads) nb = quads;
-  if (G == 96) return launch_k(bconv_kernel<96>, dim3((unsigned)nb), dim3(BT), 0, s, t, a);
-  return launch_k(bconv_kernel<32>, dim3((unsigned)nb), dim3(BT), 0, s, t, a);
+  const long quads = (long)a0.BH * (a0.npair / 4);
+  if (2 * quads > 0x7fffffffL) return hipErrorInvalidValue;
+  // One workgroup per compute unit (four pairs' planes fill its LDS), each
+  // looping over quads.  When the last round of quads would fill at most
+  // half the compute units, those quads go as half-quads (two pairs each)
+  // over all of them instead, so no compute unit idles through a whole
+  // round.
+  const long ncu = a0.num_cu > 0 ? a0.num_cu : 256;
+  const long rem = quads % ncu;
+  BconvArgs a = a0;
+  a.nfull = (int)((rem > 0 && 2 * rem <= ncu) ? quads - rem : quads);
+  a.nhalf = (int)(2 * (quads - a.nfull));
+  long nb = a.nfull > a.nhalf ? a.nfull : a.nhalf;
+  if (nb > ncu) nb = ncu;
+  return launch_k(G == 96 ? bconv_kernel<96> : bconv_kernel<32>, dim3((unsigned)nb), dim3(BT), 0, s, t, a);
 }
 
 }  // namespace cat

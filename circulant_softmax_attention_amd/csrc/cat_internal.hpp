@@ -270,6 +270,7 @@ struct BconvArgs {
   void* O;
   int BH, npair, H, D, d;
   int num_cu;
+  int nfull, nhalf;  // quads, then half-quads (set by launch_bconv)
 };
 bool bconv_supported(int G);
 size_t bconv_table_halfs(int G);

@@ -77,6 +77,7 @@ hipError_t prepare_kernels(const LineGeom& g, size_t conv_lds, size_t spec_lds, 
 
 hipError_t launch_spectrum(const LineGeom& g, int mode, const SpecArgs& a, hipStream_t s, const LaunchTiming* t) {
   const Entry* e = find_entry(g);
+  if (mode == 1 && !g.twiddled && g.L1 == 96 && g.L2 == 96) return launch_spec96(a, s, t);
   SpecFn fn = e ? (mode == 0 ? e->spec0 : mode == 1 ? e->spec1 : e->spec2) : nullptr;
   if (!fn) return hipErrorInvalidValue;
   SpecArgs aa = a;

@@ -202,6 +202,11 @@ hipError_t launch_score_partial(const LineGeom& g, const ScoreArgs& a, hipStream
 // (et == ET_F32, cg == 2), a.N == 9216, a.ngrp == ceil(npair / ppg); a.tw
 // unused.  launch_score_partial routes the 96 x 96 grid here.
 hipError_t launch_score96(const ScoreArgs& a, hipStream_t s, const LaunchTiming* t = nullptr);
+// The scores-mode spectrum (logits = Re IFFT2 of the summed partials times
+// a.scale, softmax, FFT2 / N) on the 96 x 96 grid (cat_score96.hip): a.N ==
+// 9216, a.partial with a.ngrp partials per (batch, head); a.logits, a.tw
+// and a.G unused.  launch_spectrum routes mode 1 on the 96 x 96 grid here.
+hipError_t launch_spec96(const SpecArgs& a, hipStream_t s, const LaunchTiming* t = nullptr);
 // Projection-gradient helpers of the CAT backward (cat_backward.hip), storage
 // dtype et: dst [C][ldd] = src [R][C]^T with columns R .. ldd - 1 zero;
 // P [B N][D + Hp] = [dV | dz token-major | 0] (Hp >= H; D and Hp multiples

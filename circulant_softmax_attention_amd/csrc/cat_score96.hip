@@ -196,9 +196,130 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(3, 3))) vo
 }
 
 
+// ------------------------------------------------------------ softmax spectrum
+// The filter spectrum of one (batch, head) from its summed score spectrum,
+// on the 96 x 96 grid: the scores are a = Re IFFT2(S) / sqrt(d) (S the sum
+// of a.ngrp partials), a* = softmax over the grid, and the spectrum is
+// FFT2(a*) / 9216 -- the same quantities the generic spectrum kernel forms
+// in its scores mode.  The inverse transform runs the forward 96-point DFTs
+// on conj(S): the result is conj of the inverse, whose real part is the
+// same.  Workgroup: one (batch, head), the lanes of the score kernel, the
+// grid through the exchange tile four times (inverse, and forward in both
+// directions), block reductions for the softmax through LDS.
+__global__ __launch_bounds__(NTHR) void spec96_kernel(SpecArgs a) {
+  extern __shared__ __attribute__((aligned(16))) float2 tile[];  // [96][PITCH], then 8 floats
+  float* red = reinterpret_cast<float*>(tile + GS * PITCH);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h0 = (lane >> 4) & 1, h1 = lane >> 5, h = h0 + 2 * h1;
+  const int col = 16 * wave + (lane & 15);
+  const int bh = blockIdx.x;
+
+  LaneTw lt;
+  lt.h1 = h1 != 0;
+  {
+    constexpr ct::cs c8 = ct::cossin_2pi(8, GS), c12 = ct::cossin_2pi(12, GS), c20 = ct::cossin_2pi(20, GS);
+    constexpr ct::cs c24 = ct::cossin_2pi(24, GS), c36 = ct::cossin_2pi(36, GS);
+    const cf w12 = cfm((float)c12.c, (float)-c12.s);
+    lt.w8 = h0 ? (h1 ? cfm((float)c20.c, (float)-c20.s) : cfm((float)c8.c, (float)-c8.s)) : (h1 ? w12 : cfm(1.f, 0.f));
+    lt.w24 = h0 ? (h1 ? cfm((float)c36.c, (float)-c36.s) : cfm((float)c24.c, (float)-c24.s)) : (h1 ? w12 : cfm(1.f, 0.f));
+  }
+  float2* wbase8 = tile + (12 * h1 + 8 * h0) * PITCH + col;
+  float2* wbase24 = tile + (12 * h1 + 24 * h0) * PITCH + col;
+  const float2* rbase = tile + col * PITCH + h;
+  // register r of a transform's output <-> index KB[r] + 12 h1 + KD[r] h0 along
+  // its axis; the lane's column (or row) is col
+  auto exchange = [&](cf* x) {
+    __syncthreads();  // every lane is done with the tile
+    sfor<0, NR>([&](auto R) {
+      constexpr int r = decltype(R)::value;
+      float2* q = (KD[r] == 8 ? wbase8 : wbase24) + KB[r] * PITCH;
+      *q = make_float2(x[r].x, x[r].y);
+    });
+    __syncthreads();
+    sfor<0, NR>([&](auto M) {
+      constexpr int m = decltype(M)::value;
+      const float2 v = rbase[4 * m];
+      x[m] = cfm(v.x, v.y);
+    });
+  };
+  auto block_reduce = [&](float v, bool is_max) {
+    for (int o = 32; o > 0; o >>= 1) {
+      const float u = __shfl_xor(v, o);
+      v = is_max ? fmaxf(v, u) : v + u;
+    }
+    __syncthreads();  // red is free
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    float r = red[0];
+    for (int w = 1; w < NTHR / 64; ++w) r = is_max ? fmaxf(r, red[w]) : r + red[w];
+    return r;
+  };
+
+  // S[k1 = col][k2 = 4 m + h], conjugated
+  cf x[NR];
+  sfor<0, NR>([&](auto M) { x[decltype(M)::value] = cfm(0.f, 0.f); });
+  for (int g = 0; g < a.ngrp; ++g) {
+    const float2* src = a.partial + ((size_t)bh * a.ngrp + g) * NPOS + col + GS * h;
+    sfor<0, NR>([&](auto M) {
+      constexpr int m = decltype(M)::value;
+      const float2 v = src[4 * m * GS];
+      x[m] = x[m] + cfm(v.x, v.y);
+    });
+  }
+  sfor<0, NR>([&](auto M) { x[decltype(M)::value].y = -x[decltype(M)::value].y; });
+  dft96(x, lt);  // over k2: row k1 = col, register r -> n2
+  exchange(x);   // row n2 = col, register m -> k1 = 4 m + h
+  dft96(x, lt);  // over k1: register r -> n1, column n2 = col
+
+  // scores and their softmax over the grid
+  const float ls = a.scale / (float)NPOS;
+  float v[NR];
+  float mx = -INFINITY;
+  sfor<0, NR>([&](auto R) {
+    constexpr int r = decltype(R)::value;
+    v[r] = x[r].x * ls;
+    mx = fmaxf(mx, v[r]);
+  });
+  mx = block_reduce(mx, true);
+  float sum = 0.f;
+  sfor<0, NR>([&](auto R) {
+    constexpr int r = decltype(R)::value;
+    v[r] = expf(v[r] - mx);
+    sum += v[r];
+  });
+  sum = block_reduce(sum, false);
+  const float inv_s = 1.0f / sum;
+  if (a.probs != nullptr) {
+    // position n1 96 + n2, n1 = KB[r] + 12 h1 + KD[r] h0, n2 = col
+    float* pb = a.probs + (size_t)bh * NPOS + col + GS * 12 * h1;
+    sfor<0, NR>([&](auto R) {
+      constexpr int r = decltype(R)::value;
+      pb[GS * (KB[r] + KD[r] * h0)] = v[r] * inv_s;
+    });
+  }
+  // FFT2(a*) / 9216: a*[n1][n2] sits at row n1 = index of r, column n2 = col
+  const float sc = inv_s / (float)NPOS;
+  sfor<0, NR>([&](auto R) { x[decltype(R)::value] = cfm(v[decltype(R)::value] * sc, 0.f); });
+  exchange(x);   // row n1 = col, register m -> n2 = 4 m + h
+  dft96(x, lt);  // over n2: register r -> k2
+  exchange(x);   // row k2 = col, register m -> n1 = 4 m + h
+  dft96(x, lt);  // over n1: register r -> k1, k2 = col
+  float2* dst = a.spec + (size_t)bh * NPOS;
+  sfor<0, NR>([&](auto R) {
+    constexpr int r = decltype(R)::value;
+    const int k1 = KB[r] + 12 * h1 + KD[r] * h0;
+    dst[a.transpose ? col + GS * k1 : k1 + GS * col] = make_float2(x[r].x, x[r].y);
+  });
+}
+
 }  // namespace
 
 size_t score96_lds_bytes() { return (size_t)GS * PITCH * sizeof(float2); }
+
+hipError_t launch_spec96(const SpecArgs& a, hipStream_t s, const LaunchTiming* t) {
+  if (a.N != NPOS || a.partial == nullptr || a.ngrp < 1 || a.BH < 1) return hipErrorInvalidValue;
+  return launch_k(spec96_kernel, dim3((unsigned)a.BH), dim3(NTHR), score96_lds_bytes() + 8 * sizeof(float), s, t, a);
+}
 
 hipError_t launch_score96(const ScoreArgs& a, hipStream_t s, const LaunchTiming* t) {
   if (a.N != NPOS || a.et != ET_F32 || a.cg != 2 || a.ppg != 2 || a.BH < 1 || a.npair < 1 ||

@@ -121,7 +121,7 @@ KERNEL_SOURCES = {
 }
 KERNEL_SOURCES["directconv"] = ["circulant_softmax_attention_amd/csrc/cat_dconv.hip",
                                  "circulant_softmax_attention_amd/csrc/cat_common.hpp"]
-KERNEL_SOURCES["spectrum"] = KERNEL_SOURCES["fftconv"]
+KERNEL_SOURCES["spectrum"] = KERNEL_SOURCES["fftconv"] + ["circulant_softmax_attention_amd/csrc/cat_score96.hip"]
 KERNEL_SOURCES["scores"] = ["circulant_softmax_attention_amd/csrc/cat_score96.hip",
                             "circulant_softmax_attention_amd/csrc/cat_fftconv.hpp",
                             "circulant_softmax_attention_amd/csrc/cat_fft.hpp",

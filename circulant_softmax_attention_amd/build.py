@@ -30,7 +30,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", os.path.
 # asking the backend for MFMAs that write VGPRs directly saves a copy of each
 # result out of the accumulation registers.
 FILE_FLAGS = {"cat_mconv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
-SOURCES = ["cat_inst_2d_96.hip", "cat_inst_1d_large.hip", "cat_inst_1d_mid.hip", "cat_inst_2d_small.hip",
+SOURCES = ["cat_inst_2d_96.hip", "cat_inst_2d_vit.hip", "cat_inst_1d_large.hip", "cat_inst_1d_mid.hip", "cat_inst_2d_small.hip",
            "cat_inst_1d_small.hip", "cat_gemm.hip", "cat_mconv.hip", "cat_dconv.hip", "cat_longconv.hip", "cat_fftconv.hip", "cat_backward.hip", "cat_variants.hip", "cat_noalloc.hip", "cat_bconv.hip", "cat_score96.hip",
            "cat_api.cpp"]
 

@@ -284,7 +284,9 @@ cat_status cat_plan_create(cat_plan* out, const cat_problem* p) {
   if (longn)
     while (G < 8 && d2 % (2 * G) == 0) G *= 2;
   else
-    while (G < 8 && d2 % (2 * G) == 0 && (2 * G) * T <= 256 && (2 * G) * line_bytes <= lds_cap) G *= 2;
+    // (split DFTs pair lanes of one line: one line per workgroup)
+    while (line_split(g) == 1 && G < 8 && d2 % (2 * G) == 0 && (2 * G) * T <= 256 && (2 * G) * line_bytes <= lds_cap)
+      G *= 2;
   {
     const char* cv = std::getenv("CAT_CONV");
     const bool force_valu = cv && std::strcmp(cv, "valu") == 0;

@@ -11,7 +11,8 @@
 //     in registers, natural order in and out, fully unrolled.  Forward uses
 //     W = exp(-2 pi i / N); INV uses the conjugate and is NOT scaled by 1/N.
 //     Composite N is split Cooley-Tukey style into radix 3, 2, 4 and 8 steps
-//     whose twiddles are compile-time constants.
+//     whose twiddles are compile-time constants; 7 is a direct
+//     symmetric-pair DFT (so 7, 14, 28 and 56 are lengths too).
 //   * compile-time cos/sin of 2 pi k / n in double precision (Taylor series
 //     after an exact octant reduction), rounded once to float.
 //
@@ -129,7 +130,7 @@ CAT_HD cf twiddle(cf a) {
 
 // ------------------------------------------------------------ DFTs
 constexpr int pick_radix(int n) {
-  return (n % 3 == 0) ? 3 : (n == 8) ? 2 : (n == 16) ? 4 : (n % 8 == 0) ? 8 : (n % 4 == 0) ? 4 : 2;
+  return (n % 3 == 0) ? 3 : (n % 7 == 0 && n != 7) ? 7 : (n == 8) ? 2 : (n == 16) ? 4 : (n % 8 == 0) ? 8 : (n % 4 == 0) ? 4 : 2;
 }
 
 template <int N, bool INV>
@@ -161,6 +162,38 @@ struct Dft<3, INV> {
     // forward: X1 = t2 - i h d, X2 = t2 + i h d; inverse swaps the signs
     x[1] = cfm(fmaf(sg * h, d.y, t2.x), fmaf(-sg * h, d.x, t2.y));
     x[2] = cfm(fmaf(-sg * h, d.y, t2.x), fmaf(sg * h, d.x, t2.y));
+  }
+};
+
+// Length 7 (prime): with a_j = x[j] + x[7 - j] and b_j = x[j] - x[7 - j]
+// (j = 1..3), X[0] = x[0] + sum a_j and, for k = 1..3,
+//   X[k] = A_k - i B_k,  X[7 - k] = A_k + i B_k   (forward; INV swaps them)
+// with A_k = x[0] + sum_j a_j cos(2 pi j k / 7), B_k = sum_j b_j sin(2 pi j k / 7).
+template <bool INV>
+struct Dft<7, INV> {
+  CAT_HD static void run(cf* x) {
+    cf a[3], b[3];
+    sfor<1, 4>([&](auto J) {
+      constexpr int j = decltype(J)::value;
+      a[j - 1] = x[j] + x[7 - j];
+      b[j - 1] = x[j] - x[7 - j];
+    });
+    const cf x0 = x[0];
+    x[0] = x0 + a[0] + a[1] + a[2];
+    sfor<1, 4>([&](auto K) {
+      constexpr int k = decltype(K)::value;
+      cf A = x0, Bs = cfm(0.f, 0.f);
+      sfor<1, 4>([&](auto J) {
+        constexpr int j = decltype(J)::value;
+        constexpr ct::cs w = ct::cossin_2pi((long)j * k, 7);
+        constexpr float c = (float)w.c, sn = (float)w.s;
+        A = cfm(fmaf(a[j - 1].x, c, A.x), fmaf(a[j - 1].y, c, A.y));
+        Bs = cfm(fmaf(b[j - 1].x, sn, Bs.x), fmaf(b[j - 1].y, sn, Bs.y));
+      });
+      const cf mib = cfm(Bs.y, -Bs.x);  // -i B
+      x[k] = INV ? A - mib : A + mib;
+      x[7 - k] = INV ? A + mib : A - mib;
+    });
   }
 };
 

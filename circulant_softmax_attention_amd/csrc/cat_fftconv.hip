@@ -9,6 +9,7 @@ const Entry* entries_1d_mid(int* n);
 const Entry* entries_1d_large(int* n);
 const Entry* entries_2d_small(int* n);
 const Entry* entries_2d_96(int* n);
+const Entry* entries_2d_vit(int* n);
 
 namespace {
 
@@ -19,7 +20,7 @@ using kern::SpecFn;
 const Entry* find_entry(const LineGeom& g) {
   using Getter = const Entry* (*)(int*);
   static const Getter getters[] = {entries_1d_small, entries_1d_mid, entries_1d_large, entries_2d_small,
-                                   entries_2d_96};
+                                   entries_2d_96,    entries_2d_vit};
   for (Getter get : getters) {
     int n = 0;
     const Entry* e = get(&n);
@@ -55,6 +56,11 @@ size_t spectrum_lds_bytes(const LineGeom& g, int G) {
 int line_threads(const LineGeom& g) {
   const Entry* e = find_entry(g);
   return e ? e->T : 0;
+}
+
+int line_split(const LineGeom& g) {
+  const Entry* e = find_entry(g);
+  return e ? e->S : 0;
 }
 
 hipError_t prepare_kernels(const LineGeom& g, size_t conv_lds, size_t spec_lds, size_t score_lds) {

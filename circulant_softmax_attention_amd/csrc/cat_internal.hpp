@@ -170,6 +170,9 @@ bool geom_supported(const LineGeom& g);
 // LDS bytes of one transform line and the threads per line.
 size_t line_lds_bytes(const LineGeom& g);
 int line_threads(const LineGeom& g);
+// Threads per DFT of a geometry (2 for split grids, whose lines take one
+// workgroup each), 0 if unsupported.
+int line_split(const LineGeom& g);
 // LDS bytes of a spectrum workgroup of G lines (lines, reduction scratch).
 size_t spectrum_lds_bytes(const LineGeom& g, int G);
 

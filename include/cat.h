@@ -106,7 +106,8 @@ typedef enum { CAT_1D = 0, CAT_BCCB_2D = 1 } cat_kind;
  *       and the softmaxed scores periodically extended); a power-of-two N
  *       beyond 4096, and any other N beyond 2048, by three passes over HBM
  *       (see cat_plan_conv_path);
- *   2D: grids 1x1, 2x3, 3x4, 4x4, 6x8, 8x8, 12x12, 16x16, 32x32, 96x96. */
+ *   2D: grids 1x1, 2x3, 3x4, 4x4, 6x8, 8x8, 12x12, 16x16, 32x32, 96x96, and the
+ *       vision-transformer patch grids 7x7, 14x14, 24x24, 28x28, 48x48. */
 typedef struct {
   int32_t kind;  /* cat_kind */
   int32_t dtype; /* cat_dtype */

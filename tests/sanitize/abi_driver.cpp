@@ -89,7 +89,7 @@ int main() {
   }
   const cat_problem unsupported[] = {
       prob(CAT_1D, CAT_F32, 1, 131072, 32, 2),   prob(CAT_1D, CAT_F32, 1, 40000, 32, 2),
-      prob(CAT_1D, CAT_F32, 1, 64, 512, 64),     prob(CAT_BCCB_2D, CAT_F32, 1, 196, 32, 2, 14, 14),
+      prob(CAT_1D, CAT_F32, 1, 64, 512, 64),     prob(CAT_BCCB_2D, CAT_F32, 1, 100, 32, 2, 10, 10),
       prob(CAT_1D, CAT_BF16, 1 << 20, 1024, 4096, 32), prob(CAT_1D, CAT_F32, int64_t(1) << 40, int64_t(1) << 30, 64, 2),
       prob(CAT_1D, CAT_F32, int64_t(1) << 62, 4, 16, 2),
   };

@@ -548,9 +548,11 @@ def test_determinism_1d(cat):
 
 # ------------------------------------------------------------------ 2D
 GRIDS = [(1, 1), (2, 3), (3, 4), (4, 4), (6, 8), (8, 8), (12, 12), (16, 16)]
+# patch grids of common vision-transformer resolutions (7 = a radix-7 DFT)
+VIT_GRIDS = [(7, 7), (14, 14), (24, 24), (28, 28), (48, 48)]
 
 
-@pytest.mark.parametrize("Hg,Wg", GRIDS + [(32, 32), (96, 96)])
+@pytest.mark.parametrize("Hg,Wg", GRIDS + VIT_GRIDS + [(32, 32), (96, 96)])
 def test_scores_2d(cat, Hg, Wg):
     say("scores_2d", Hg, Wg)
     import torch
@@ -565,15 +567,15 @@ def test_scores_2d(cat, Hg, Wg):
     assert_parity(probs, ref, "f32", "a*")
 
 
-@pytest.mark.parametrize("D,H", [(24, 4), (40, 4), (8, 4), (64, 1)])
-def test_scores_2d_96_pair_groups(cat, D, H):
-    """The 96 x 96 score kernel groups a head's channel pairs two to a
-    workgroup; an odd pair count (d = 6 or 10: 3 or 5 pairs) leaves one
-    group of a single pair, d = 2 a head of one pair, d = 64 the workload's
-    32 pairs."""
-    say("scores_2d_96_groups", D, H)
+@pytest.mark.parametrize("B,D,H", [(1, 24, 4), (1, 40, 4), (1, 8, 4), (1, 64, 1), (3, 64, 1), (1, 48, 3)])
+def test_scores_2d_96_pair_groups(cat, B, D, H):
+    """The 96 x 96 score kernel takes a head's channel pairs two to a
+    workgroup: d = 6 and 10 (3 and 5 pairs) leave a last group of one pair,
+    d = 2 a head of one pair; d = 64 is the workload's 32 pairs, for one and
+    three heads; d = 16 gives 8 pairs for each of three heads."""
+    say("scores_2d_96_groups", B, D, H)
     import torch
-    B, G = 1, 96
+    G = 96
     rng = np.random.default_rng(D * 10 + H)
     Q = (rng.standard_normal((B, G * G, D)) * 0.5).astype(np.float32)
     K = (rng.standard_normal((B, G * G, D)) * 0.5).astype(np.float32)
@@ -584,8 +586,9 @@ def test_scores_2d_96_pair_groups(cat, D, H):
     assert_parity(probs, ref, "f32", "a*")
 
 
-@pytest.mark.parametrize("Hg,Wg,dtype", [(g[0], g[1], "f32") for g in GRIDS] +
-                         [(12, 12, "bf16"), (32, 32, "f32"), (32, 32, "bf16"), (96, 96, "f32"), (96, 96, "bf16")])
+@pytest.mark.parametrize("Hg,Wg,dtype", [(g[0], g[1], "f32") for g in GRIDS + VIT_GRIDS] +
+                         [(12, 12, "bf16"), (14, 14, "bf16"), (24, 24, "bf16"), (32, 32, "f32"), (32, 32, "bf16"),
+                          (96, 96, "f32"), (96, 96, "bf16")])
 def test_mix_2d(cat, Hg, Wg, dtype):
     say("mix_2d", Hg, Wg, dtype)
     import torch
@@ -632,7 +635,10 @@ def test_mix_2d_matrix(cat, G, case):
 @pytest.mark.parametrize("B,Hg,Wg,D,H,dtype,ss", [(1, 3, 4, 16, 2, "f32", 1.0), (2, 8, 8, 32, 2, "f32", 0.3),
                                                   (2, 12, 12, 48, 3, "bf16", 0.3), (1, 6, 8, 64, 1, "f32", 1.0),
                                                   (2, 16, 16, 64, 4, "bf16", 0.2), (2, 8, 8, 24, 4, "f32", 0.5),
-                                                  (1, 12, 12, 24, 2, "bf16", 0.3), (2, 32, 32, 64, 2, "bf16", 0.3)])
+                                                  (1, 12, 12, 24, 2, "bf16", 0.3), (2, 32, 32, 64, 2, "bf16", 0.3),
+                                                  (2, 14, 14, 64, 2, "bf16", 0.3), (1, 7, 7, 32, 2, "f32", 0.5),
+                                                  (1, 24, 24, 64, 2, "bf16", 0.3), (1, 28, 28, 32, 2, "f32", 0.3),
+                                                  (1, 48, 48, 64, 2, "bf16", 0.2)])
 def test_forward_2d_small(cat, B, Hg, Wg, D, H, dtype, ss):
     say("forward_2d", B, Hg, Wg, D, H, dtype, ss)
     import torch
@@ -646,7 +652,8 @@ def test_forward_2d_small(cat, B, Hg, Wg, D, H, dtype, ss):
 
 @pytest.mark.parametrize("B,Hg,Wg,D,H,dtype", [
     (2, 8, 8, 64, 4, "f32"), (1, 12, 12, 48, 3, "bf16"), (2, 2, 3, 16, 2, "f32"), (1, 16, 16, 32, 2, "bf16"),
-    (1, 6, 8, 24, 2, "f32"), (1, 1, 1, 16, 2, "f32"), (1, 32, 32, 64, 2, "f32"), (1, 96, 96, 64, 2, "bf16")])
+    (1, 6, 8, 24, 2, "f32"), (1, 1, 1, 16, 2, "f32"), (1, 32, 32, 64, 2, "f32"), (1, 96, 96, 64, 2, "bf16"),
+    (1, 14, 14, 64, 2, "bf16"), (1, 7, 7, 32, 2, "f32")])
 def test_forward_cat_2d(cat, B, Hg, Wg, D, H, dtype):
     """The CAT-scored 2D variant (X W_A scores, softmax over the grid, BCCB
     mixing) against the oracle, on grids from 1 x 1 to 96 x 96."""

@@ -638,7 +638,8 @@ def test_mix_2d_matrix(cat, G, case):
                                                   (1, 12, 12, 24, 2, "bf16", 0.3), (2, 32, 32, 64, 2, "bf16", 0.3),
                                                   (2, 14, 14, 64, 2, "bf16", 0.3), (1, 7, 7, 32, 2, "f32", 0.5),
                                                   (1, 24, 24, 64, 2, "bf16", 0.3), (1, 28, 28, 32, 2, "f32", 0.3),
-                                                  (1, 48, 48, 64, 2, "bf16", 0.2)])
+                                                  (1, 48, 48, 64, 2, "bf16", 0.2), (1, 96, 96, 16, 2, "f32", 0.3),
+                                                  (1, 96, 96, 16, 2, "bf16", 0.3)])
 def test_forward_2d_small(cat, B, Hg, Wg, D, H, dtype, ss):
     say("forward_2d", B, Hg, Wg, D, H, dtype, ss)
     import torch

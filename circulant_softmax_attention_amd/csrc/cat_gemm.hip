@@ -134,7 +134,7 @@ __device__ __forceinline__ size_t out_index(const GemmSeg& s, const GemmArgs& a,
 // rows, 128 (256 threads, two workgroups per compute unit) or 256 (512
 // threads, one workgroup per compute unit).  ZTR: bf16 W_A fragments come
 // from transposing LDS reads (needs nz % 4 == 0).
-template <int ET, int BN, int ZB, int BM, bool ZTR = false>
+template <int ET, int BN, int ZB, int BM, bool ZTR = false, bool KT = true>
 __global__ __launch_bounds__(2 * BM, 256 / BM) void gemm_xw_kernel(GemmArgs a) {
   constexpr int NTHR = 2 * BM;  // 64-row wave blocks, two per row of waves
   using C = GemmCfg<ET>;
@@ -222,10 +222,17 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void gemm_xw_kernel(GemmArgs a) {
   const bool zdma = zon && wave < 2 * ZB;
   const char* zsrc = reinterpret_cast<const char*>(a.Wz) + 16 * (size_t)(tid < zchunks ? tid : zchunks - 1);
 
-  // Stage tile kt into LDS stage st.
+  // K order: the workgroups that share a W tile (one column tile, the
+  // neighbouring row panels on an XCD) or an X tile (one row panel) start at
+  // different K tiles, so that at any moment they ask for different lines.
+  const int nk = (K + BK - 1) / BK;
+  const int koff = rt % nk;
+  auto kmap = [&](int kt) { return kt + koff < nk ? kt + koff : kt + koff - nk; };
+
+  // Stage the kt-th K tile (in this workgroup's order) into LDS stage st.
   auto issue = [&](int kt, int st) {
-    const int k0 = kt * BK;
-    if (k0 + BK <= K) {
+    const int k0 = kmap(kt) * BK;
+    if (!KT || k0 + BK <= K) {
       const uint32_t base = lds0 + (uint32_t)(st * STAGE);
 #pragma unroll
       for (int i = 0; i < 4; ++i) lds_dma16(asrc[i] + k0, base + i * NTHR * 16);
@@ -404,7 +411,7 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void gemm_xw_kernel(GemmArgs a) {
   // finished multiplying tile kt - 1, whose stage then receives tile kt + 1,
   // whose DMA thus runs under the MFMAs of tile kt.  The loop is unrolled by
   // two so that stage indices are compile-time constants.
-  const int nk = (K + BK - 1) / BK;
+  const bool warm = BN != 192 && a.warm;
   issue(0, 0);
   // L2 warm-up, where a row panel is read by many column tiles: those tiles
   // (consecutive workgroups on one XCD) together touch every 64-byte sector
@@ -414,7 +421,6 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void gemm_xw_kernel(GemmArgs a) {
   // sectors; step 0 waits for the first tile only (the warm-up loads were
   // issued after it), and the values feed a test that never passes.
   constexpr int WARM = 4;
-  const bool warm = BN != 192 && a.warm;
   uint32_t wv[WARM] = {0u, 0u, 0u, 0u};
   if (warm) {
     const int rows = M - m0 < BM ? M - m0 : BM;
@@ -438,11 +444,24 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void gemm_xw_kernel(GemmArgs a) {
       wait_vmem_all();
     __syncthreads();
     if (kt + 1 < nk) issue(kt + 1, st ^ 1);
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-      read_frags(st, kc, af, bf);
+    if constexpr (!KT) {
+      // both K chunks' fragments are requested before the first MFMA, so
+      // the second chunk's LDS reads run under the first chunk's products
+      // (the kernels with a K tail have no registers for this)
+      uint4 af1[4], bf1[TN];
+      read_frags(st, 0, af, bf);
+      read_frags(st, 1, af1, bf1);
       mma(af, bf);
-      zmma(kc, af, st);
+      zmma(0, af, st);
+      mma(af1, bf1);
+      zmma(1, af1, st);
+    } else {
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        read_frags(st, kc, af, bf);
+        mma(af, bf);
+        zmma(kc, af, st);
+      }
     }
   };
   for (int kt = 0; kt < nk; kt += 2) {
@@ -642,22 +661,31 @@ hipError_t launch_gemm_bn(int et, GemmArgs& a, hipStream_t stream, const LaunchT
       return launch_k(gemm_xw_kernel<ET_F32, BN, 2, BM>, grid, block, 0, stream, t, a);
     }
   }
-  if (zb == 0) return launch_k(gemm_xw_kernel<ET_BF16, BN, 0, BM>, grid, block, 0, stream, t, a);
-  // 128 x 192 tiles never carry the score projection, 256 x 192 ones at most
-  // 16 heads
-  if constexpr (BN == 192 && BM == 128) {
-    return hipErrorInvalidValue;
-  } else {
-    if (zb == 1)
-      return tr ? launch_k(gemm_xw_kernel<ET_BF16, BN, 1, BM, true>, grid, block, 0, stream, t, a)
-                : launch_k(gemm_xw_kernel<ET_BF16, BN, 1, BM, false>, grid, block, 0, stream, t, a);
-    if constexpr (BN == 192) {
+  // KT = false: every K slice is whole K tiles, so the kernel carries no
+  // tail path (and none of the registers it would hold)
+  auto bf16 = [&](auto kt_tag) -> hipError_t {
+    constexpr bool KT = decltype(kt_tag)::value;
+    if (zb == 0) return launch_k(gemm_xw_kernel<ET_BF16, BN, 0, BM, false, KT>, grid, block, 0, stream, t, a);
+    // 128 x 192 tiles never carry the score projection, 256 x 192 ones at
+    // most 16 heads
+    if constexpr (BN == 192 && BM == 128) {
       return hipErrorInvalidValue;
     } else {
-      return tr ? launch_k(gemm_xw_kernel<ET_BF16, BN, 2, BM, true>, grid, block, 0, stream, t, a)
-                : launch_k(gemm_xw_kernel<ET_BF16, BN, 2, BM, false>, grid, block, 0, stream, t, a);
+      if (zb == 1)
+        return tr ? launch_k(gemm_xw_kernel<ET_BF16, BN, 1, BM, true, KT>, grid, block, 0, stream, t, a)
+                  : launch_k(gemm_xw_kernel<ET_BF16, BN, 1, BM, false, KT>, grid, block, 0, stream, t, a);
+      if constexpr (BN == 192) {
+        return hipErrorInvalidValue;
+      } else {
+        return tr ? launch_k(gemm_xw_kernel<ET_BF16, BN, 2, BM, true, KT>, grid, block, 0, stream, t, a)
+                  : launch_k(gemm_xw_kernel<ET_BF16, BN, 2, BM, false, KT>, grid, block, 0, stream, t, a);
+      }
     }
+  };
+  if constexpr (BM == 256) {
+    if (a.K % 64 == 0) return bf16(std::false_type{});
   }
+  return bf16(std::true_type{});
 }
 
 }  // namespace

@@ -332,11 +332,22 @@ __device__ __forceinline__ void reg_fft(cf* x, int t, float2* xl, const float2* 
   Dft<MS, INV>::run(x);
 }
 
+// The values' intermediate A between the passes: complex fp32 (float2), or,
+// for bf16 storage on the all-register path, a bf16 pair (real part in the
+// low half) that halves the passes' traffic.  Arithmetic stays fp32.
+__device__ __forceinline__ float2 lda(const float2* p, size_t i) { return p[i]; }
+__device__ __forceinline__ float2 lda(const uint32_t* p, size_t i) {
+  const uint32_t w = p[i];
+  return make_float2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
+}
+__device__ __forceinline__ void sta(float2* p, size_t i, float2 v) { p[i] = v; }
+__device__ __forceinline__ void sta(uint32_t* p, size_t i, float2 v) { p[i] = pack_bf16x2(v.x, v.y); }
+
 // ---- row pass on registers (L2 = MS^2), 128 threads: R = 128 / MS lines
 // (rows x pairs) per workgroup, lane r = tid % R of each line fastest so a
 // wave's loads and stores are contiguous.  MODE as row_kernel.
-template <int MODE, int MS>
-__global__ __launch_bounds__(128) void row_reg_kernel(LongArgs a, int PB, float2* __restrict__ A,
+template <int MODE, int MS, class AT = float2>
+__global__ __launch_bounds__(128) void row_reg_kernel(LongArgs a, int PB, AT* __restrict__ A,
                                                       float2* __restrict__ S) {
   constexpr int M = MS * MS, R = 128 / MS, TP = MS * (MS + 1);
   __shared__ float2 xb[R * TP];
@@ -352,7 +363,7 @@ __global__ __launch_bounds__(128) void row_reg_kernel(LongArgs a, int PB, float2
   cf x[MS];
 #pragma unroll
   for (int ma = 0; ma < MS; ++ma) {
-    const float2 v = A[base + ((size_t)rr * M + ma * MS + t) * PB + j];
+    const float2 v = lda(A, base + ((size_t)rr * M + ma * MS + t) * PB + j);
     x[ma] = cfm(v.x, v.y);
   }
   __syncthreads();  // twiddles in LDS
@@ -370,7 +381,7 @@ __global__ __launch_bounds__(128) void row_reg_kernel(LongArgs a, int PB, float2
     reg_fft<MS, true>(x, t, xl, twm);
 #pragma unroll
     for (int nb = 0; nb < MS; ++nb)
-      A[base + ((size_t)rr * M + t + MS * nb) * PB + j] = make_float2(x[nb].x, x[nb].y);
+      sta(A, base + ((size_t)rr * M + t + MS * nb) * PB + j, make_float2(x[nb].x, x[nb].y));
   }
 }
 
@@ -379,9 +390,9 @@ __global__ __launch_bounds__(128) void row_reg_kernel(LongArgs a, int PB, float2
 // Forward: SET as col_fwd_kernel.  Lane t of line r = c PB + j holds
 // x[(ma MS + t) L2 + n20 + c][j] in register ma; after the transform it
 // holds k1 = t + MS kb in register kb.
-template <int SET, int MS, bool WRAP>
+template <int SET, int MS, bool WRAP, class AT = float2>
 __global__ __launch_bounds__(128) void col_reg_kernel(LongArgs a, int PB, const void* __restrict__ src,
-                                                      float2* __restrict__ A, const float2* __restrict__ smpart) {
+                                                      AT* __restrict__ A, const float2* __restrict__ smpart) {
   constexpr int M = MS * MS, R = 128 / MS, TP = MS * (MS + 1);
   __shared__ float2 xb[R * TP];
   __shared__ float2 twm[M];
@@ -434,15 +445,15 @@ __global__ __launch_bounds__(128) void col_reg_kernel(LongArgs a, int PB, const 
     const int k1 = t + MS * kb;
     const float2 w = a.tw[(k1 * n2) & (L - 1)];
     const cf y = cmul(x[kb], cfm(w.x, w.y));
-    A[gbase + ((size_t)k1 * L2 + n20) * PB + r] = make_float2(y.x, y.y);
+    sta(A, gbase + ((size_t)k1 * L2 + n20) * PB + r, make_float2(y.x, y.y));
   }
 }
 
 // Inverse column pass on registers: lane t of line r holds
 // A[k1][n2][j] conj W_L^(k1 n2) for k1 = ma MS + t in register ma; after the
 // inverse transform it holds n1 = t + MS nb in register nb, written to O.
-template <int DET, int MS>
-__global__ __launch_bounds__(128) void col_inv_reg_kernel(LongArgs a, int PB, const float2* __restrict__ A,
+template <int DET, int MS, class AT = float2>
+__global__ __launch_bounds__(128) void col_inv_reg_kernel(LongArgs a, int PB, const AT* __restrict__ A,
                                                           void* __restrict__ O) {
   constexpr int M = MS * MS, R = 128 / MS, TP = MS * (MS + 1);
   __shared__ float2 xb[R * TP];
@@ -460,7 +471,7 @@ __global__ __launch_bounds__(128) void col_inv_reg_kernel(LongArgs a, int PB, co
 #pragma unroll
   for (int ma = 0; ma < MS; ++ma) {
     const int k1 = ma * MS + t;
-    const float2 v = A[gbase + ((size_t)k1 * L2 + n20) * PB + r];
+    const float2 v = lda(A, gbase + ((size_t)k1 * L2 + n20) * PB + r);
     const float2 w = a.tw[(k1 * n2) & (L - 1)];
     x[ma] = cmulc(cfm(v.x, v.y), cfm(w.x, w.y));
   }
@@ -720,7 +731,7 @@ hipError_t launch_longconv(int et, const LongArgs& a, const float* logits, const
   // column passes on registers when L1 is a square of 8 or 16 (C = 128 / sqrt(L1) lines per workgroup)
   const bool wrap = N != L;
   auto col = [&](auto plain, auto wrapped, unsigned grid, unsigned threads, const LaunchTiming* tt, int pb,
-                 const void* src, float2* dst, const float2* sm) {
+                 const void* src, auto* dst, const float2* sm) {
     return wrap ? launch_k(wrapped, dim3(grid), dim3(threads), 0, s, tt, a, pb, src, dst, sm)
                 : launch_k(plain, dim3(grid), dim3(threads), 0, s, tt, a, pb, src, dst, sm);
   };
@@ -755,6 +766,28 @@ hipError_t launch_longconv(int et, const LongArgs& a, const float* logits, const
   // the mixing, PB pairs per block
   const unsigned cv = mc ? (unsigned)(blocks * (L2 / (cl / PB))) : 0;
   const float2* nosm = nullptr;
+  if (et == ET_BF16 && mc && ms) {
+    // bf16 storage with both passes on registers: bf16-pair intermediates
+    uint32_t* Ah = reinterpret_cast<uint32_t*>(A);
+    const long rv = blocks * (L1 / (rl / PB));
+    if (mc == 16)
+      e = col(col_reg_kernel<ET_BF16, 16, false, uint32_t>, col_reg_kernel<ET_BF16, 16, true, uint32_t>, cv, 128, t[3], PB,
+              V, Ah, nosm);
+    else
+      e = col(col_reg_kernel<ET_BF16, 8, false, uint32_t>, col_reg_kernel<ET_BF16, 8, true, uint32_t>, cv, 128, t[3], PB, V,
+              Ah, nosm);
+    if (e != hipSuccess) return e;
+    if (ms == 16)
+      e = launch_k(row_reg_kernel<1, 16, uint32_t>, dim3((unsigned)rv), dim3(128), 0, s, t[4], a, PB, Ah, S);
+    else
+      e = launch_k(row_reg_kernel<1, 8, uint32_t>, dim3((unsigned)rv), dim3(128), 0, s, t[4], a, PB, Ah, S);
+    if (e != hipSuccess) return e;
+    if (mc == 16)
+      return launch_k(col_inv_reg_kernel<ET_BF16, 16, uint32_t>, dim3((unsigned)cv), dim3(128), 0, s, t[5], a, PB,
+                      (const uint32_t*)Ah, O);
+    return launch_k(col_inv_reg_kernel<ET_BF16, 8, uint32_t>, dim3((unsigned)cv), dim3(128), 0, s, t[5], a, PB,
+                    (const uint32_t*)Ah, O);
+  }
   if (mc == 16)
     e = et == ET_F32 ? col(col_reg_kernel<ET_F32, 16, false>, col_reg_kernel<ET_F32, 16, true>, cv, 128, t[3], PB, V, A, nosm)
                      : col(col_reg_kernel<ET_BF16, 16, false>, col_reg_kernel<ET_BF16, 16, true>, cv, 128, t[3], PB, V, A,

@@ -390,10 +390,10 @@ __global__ __launch_bounds__(128) void row_reg_kernel(LongArgs a, int PB, AT* __
 // Forward: SET as col_fwd_kernel.  Lane t of line r = c PB + j holds
 // x[(ma MS + t) L2 + n20 + c][j] in register ma; after the transform it
 // holds k1 = t + MS kb in register kb.
-template <int SET, int MS, bool WRAP, class AT = float2>
-__global__ __launch_bounds__(128) void col_reg_kernel(LongArgs a, int PB, const void* __restrict__ src,
-                                                      AT* __restrict__ A, const float2* __restrict__ smpart) {
-  constexpr int M = MS * MS, R = 128 / MS, TP = MS * (MS + 1);
+template <int SET, int MS, bool WRAP, class AT = float2, int NT = 128>
+__global__ __launch_bounds__(NT) void col_reg_kernel(LongArgs a, int PB, const void* __restrict__ src,
+                                                     AT* __restrict__ A, const float2* __restrict__ smpart) {
+  constexpr int M = MS * MS, R = NT / MS, TP = MS * (MS + 1);
   __shared__ float2 xb[R * TP];
   __shared__ float2 twm[M];
   __shared__ float2 msum;
@@ -404,7 +404,7 @@ __global__ __launch_bounds__(128) void col_reg_kernel(LongArgs a, int PB, const 
   const size_t gbase = (size_t)gl * L * PB;
   const int r = threadIdx.x % R, t = threadIdx.x / R;
   const int c = r / PB;
-  for (int e = threadIdx.x; e < M; e += 128) twm[e] = a.tw[e * (L / M)];
+  for (int e = threadIdx.x; e < M; e += NT) twm[e] = a.tw[e * (L / M)];
   if constexpr (SET == 2) {
     const int nc = smc_chunks(a.N);
     if (threadIdx.x < 64) {
@@ -452,10 +452,10 @@ __global__ __launch_bounds__(128) void col_reg_kernel(LongArgs a, int PB, const 
 // Inverse column pass on registers: lane t of line r holds
 // A[k1][n2][j] conj W_L^(k1 n2) for k1 = ma MS + t in register ma; after the
 // inverse transform it holds n1 = t + MS nb in register nb, written to O.
-template <int DET, int MS, class AT = float2>
-__global__ __launch_bounds__(128) void col_inv_reg_kernel(LongArgs a, int PB, const AT* __restrict__ A,
-                                                          void* __restrict__ O) {
-  constexpr int M = MS * MS, R = 128 / MS, TP = MS * (MS + 1);
+template <int DET, int MS, class AT = float2, int NT = 128>
+__global__ __launch_bounds__(NT) void col_inv_reg_kernel(LongArgs a, int PB, const AT* __restrict__ A,
+                                                         void* __restrict__ O) {
+  constexpr int M = MS * MS, R = NT / MS, TP = MS * (MS + 1);
   __shared__ float2 xb[R * TP];
   __shared__ float2 twm[M];
   const int L2 = 1 << a.logL2, L = M * L2;
@@ -466,7 +466,7 @@ __global__ __launch_bounds__(128) void col_inv_reg_kernel(LongArgs a, int PB, co
   const int r = threadIdx.x % R, t = threadIdx.x / R;
   const int c = r / PB, j = r - c * PB;
   const int n2 = n20 + c;
-  for (int e = threadIdx.x; e < M; e += 128) twm[e] = a.tw[e * (L / M)];
+  for (int e = threadIdx.x; e < M; e += NT) twm[e] = a.tw[e * (L / M)];
   cf x[MS];
 #pragma unroll
   for (int ma = 0; ma < MS; ++ma) {
@@ -767,15 +767,18 @@ hipError_t launch_longconv(int et, const LongArgs& a, const float* logits, const
   const unsigned cv = mc ? (unsigned)(blocks * (L2 / (cl / PB))) : 0;
   const float2* nosm = nullptr;
   if (et == ET_BF16 && mc && ms) {
-    // bf16 storage with both passes on registers: bf16-pair intermediates
+    // bf16 storage with both passes on registers: bf16-pair intermediates,
+    // and 256-thread column workgroups (2 x 128 / sqrt(L1) lines, so that a
+    // point's lines form runs of at least 64 bytes in V and A when PB = 8)
     uint32_t* Ah = reinterpret_cast<uint32_t*>(A);
     const long rv = blocks * (L1 / (rl / PB));
+    const unsigned cv2 = (unsigned)(blocks * (L2 / ((256 / mc) / PB)));
     if (mc == 16)
-      e = col(col_reg_kernel<ET_BF16, 16, false, uint32_t>, col_reg_kernel<ET_BF16, 16, true, uint32_t>, cv, 128, t[3], PB,
-              V, Ah, nosm);
+      e = col(col_reg_kernel<ET_BF16, 16, false, uint32_t, 256>, col_reg_kernel<ET_BF16, 16, true, uint32_t, 256>, cv2, 256,
+              t[3], PB, V, Ah, nosm);
     else
-      e = col(col_reg_kernel<ET_BF16, 8, false, uint32_t>, col_reg_kernel<ET_BF16, 8, true, uint32_t>, cv, 128, t[3], PB, V,
-              Ah, nosm);
+      e = col(col_reg_kernel<ET_BF16, 8, false, uint32_t, 256>, col_reg_kernel<ET_BF16, 8, true, uint32_t, 256>, cv2, 256,
+              t[3], PB, V, Ah, nosm);
     if (e != hipSuccess) return e;
     if (ms == 16)
       e = launch_k(row_reg_kernel<1, 16, uint32_t>, dim3((unsigned)rv), dim3(128), 0, s, t[4], a, PB, Ah, S);
@@ -783,9 +786,9 @@ hipError_t launch_longconv(int et, const LongArgs& a, const float* logits, const
       e = launch_k(row_reg_kernel<1, 8, uint32_t>, dim3((unsigned)rv), dim3(128), 0, s, t[4], a, PB, Ah, S);
     if (e != hipSuccess) return e;
     if (mc == 16)
-      return launch_k(col_inv_reg_kernel<ET_BF16, 16, uint32_t>, dim3((unsigned)cv), dim3(128), 0, s, t[5], a, PB,
+      return launch_k(col_inv_reg_kernel<ET_BF16, 16, uint32_t, 256>, dim3(cv2), dim3(256), 0, s, t[5], a, PB,
                       (const uint32_t*)Ah, O);
-    return launch_k(col_inv_reg_kernel<ET_BF16, 8, uint32_t>, dim3((unsigned)cv), dim3(128), 0, s, t[5], a, PB,
+    return launch_k(col_inv_reg_kernel<ET_BF16, 8, uint32_t, 256>, dim3(cv2), dim3(256), 0, s, t[5], a, PB,
                     (const uint32_t*)Ah, O);
   }
   if (mc == 16)

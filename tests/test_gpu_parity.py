@@ -234,14 +234,15 @@ def test_conv_path_choice(cat, N, D, H, dtype, path):
     (1, 8192, 8, 2, "f32", 2.0), (1, 8192, 8, 2, "bf16", 2.0), (2, 16384, 24, 3, "f32", 3.0),
     (1, 16384, 8, 1, "f32", 0.0), (1, 16384, 8, 1, "bf16", 40.0), (1, 32768, 8, 1, "f32", 2.0),
     (1, 65536, 8, 2, "f32", 2.0), (1, 65536, 8, 1, "bf16", 2.0), (1, 65536, 16, 1, "bf16", 40.0),
-    (1, 65536, 32, 2, "bf16", 0.0),
+    (1, 65536, 32, 2, "bf16", 0.0), (1, 65536, 24, 4, "bf16", 2.0), (1, 65536, 8, 2, "bf16", 2.0),
     (1, 8192, 24, 4, "f32", 2.0), (2, 8192, 24, 2, "bf16", 2.0)])
 def test_mix_1d_long(cat, B, N, D, H, dtype, lscale):
     """Power-of-two N beyond one workgroup's line: column, row and inverse
     column passes over HBM.  Cases span N = 2^13 .. 2^16 (square and 2:1
     splits), uniform scores (lscale 0), a near one-hot softmax (lscale 40),
     and pair blocks of 1, 2, 4 and 8 channel pairs (d = 6, 12, 8, 16); at
-    N = 2^16 with bf16 storage the passes keep bf16-pair intermediates; beyond
+    N = 2^16 with bf16 storage the passes keep bf16-pair intermediates and
+    the column passes take 16, 8, 4 or 2 columns a workgroup; beyond
     16384 x 16384 x 24 multiply-adds the oracle checks 1024 sampled rows."""
     say("mix_1d_long", B, N, D, H, dtype, lscale)
     import torch

@@ -332,6 +332,19 @@ __device__ __forceinline__ void reg_fft(cf* x, int t, float2* xl, const float2* 
   Dft<MS, INV>::run(x);
 }
 
+// Pitch (complex values) of one line's LDS tile in a workgroup of R lines,
+// lane r = tid % R of each line fastest: at least MS (MS + 1), and congruent
+// to 32 / R modulo 32 (1 when R >= 32).  The 32 lanes of a half-wave (R
+// lines, 32 / R consecutive t) then fall on 32 distinct 8-byte bank pairs,
+// both where the tile is written (index r TP + ka (MS + 1) + t) and where
+// it is read transposed (index r TP + t (MS + 1) + mb).  With the bare
+// MS (MS + 1) the lines' tiles started on one or two bank pairs.
+template <int MS, int R>
+constexpr int tile_pitch() {
+  constexpr int base = MS * (MS + 1), want = R >= 32 ? 1 : 32 / R;
+  return base + ((want - base) % 32 + 32) % 32;
+}
+
 // The values' intermediate A between the passes: complex fp32 (float2), or,
 // for bf16 storage on the all-register path, a bf16 pair (real part in the
 // low half) that halves the passes' traffic.  Arithmetic stays fp32.
@@ -349,7 +362,7 @@ __device__ __forceinline__ void sta(uint32_t* p, size_t i, float2 v) { p[i] = pa
 template <int MODE, int MS, class AT = float2>
 __global__ __launch_bounds__(128) void row_reg_kernel(LongArgs a, int PB, AT* __restrict__ A,
                                                       float2* __restrict__ S) {
-  constexpr int M = MS * MS, R = 128 / MS, TP = MS * (MS + 1);
+  constexpr int M = MS * MS, R = 128 / MS, TP = tile_pitch<MS, R>();
   __shared__ float2 xb[R * TP];
   __shared__ float2 twm[M];
   const int L1 = 1 << a.logL1, L = L1 * M;
@@ -393,7 +406,7 @@ __global__ __launch_bounds__(128) void row_reg_kernel(LongArgs a, int PB, AT* __
 template <int SET, int MS, bool WRAP, class AT = float2, int NT = 128>
 __global__ __launch_bounds__(NT) void col_reg_kernel(LongArgs a, int PB, const void* __restrict__ src,
                                                      AT* __restrict__ A, const float2* __restrict__ smpart) {
-  constexpr int M = MS * MS, R = NT / MS, TP = MS * (MS + 1);
+  constexpr int M = MS * MS, R = NT / MS, TP = tile_pitch<MS, R>();
   __shared__ float2 xb[R * TP];
   __shared__ float2 twm[M];
   __shared__ float2 msum;
@@ -455,7 +468,7 @@ __global__ __launch_bounds__(NT) void col_reg_kernel(LongArgs a, int PB, const v
 template <int DET, int MS, class AT = float2, int NT = 128>
 __global__ __launch_bounds__(NT) void col_inv_reg_kernel(LongArgs a, int PB, const AT* __restrict__ A,
                                                          void* __restrict__ O) {
-  constexpr int M = MS * MS, R = NT / MS, TP = MS * (MS + 1);
+  constexpr int M = MS * MS, R = NT / MS, TP = tile_pitch<MS, R>();
   __shared__ float2 xb[R * TP];
   __shared__ float2 twm[M];
   const int L2 = 1 << a.logL2, L = M * L2;

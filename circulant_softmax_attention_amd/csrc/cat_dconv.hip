@@ -73,7 +73,10 @@ constexpr int VE = 16 / ESZ;               // values per 16-byte run (and R copi
 constexpr int KS = 4 * VE;                 // j per MFMA step: 4 lane groups x VE
 constexpr int VTP = (DNMAX + VE) * ESZ;    // bytes per Vt row (16-byte multiple)
 constexpr int VT_BYTES = DCG * VTP;
-constexpr int OS_BYTES = DNMAX * DCG * ESZ;  // O staging [Ip][32]
+constexpr int OP = DCG * ESZ + 16;          // O staging row pitch: 80 bytes, so the 8-byte
+                                            // writes of a half-wave (16 rows x 2) hit 32
+                                            // distinct bank pairs (64 bytes: 4-way)
+constexpr int OS_BYTES = DNMAX * OP;        // O staging [Ip][32], padded rows
 constexpr int TILE_BYTES = VT_BYTES > OS_BYTES ? VT_BYTES : OS_BYTES;
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
@@ -181,9 +184,11 @@ __global__ __launch_bounds__(DTHR) void dconv_kernel(ConvArgs a) {
   // ---- shifted copies of R: rc[s][p] = R[p + s - RB] = z*[(N - (p + s - RB)) mod N],
   // VE entries (one 16-byte run) per item: one modulo, then the index steps
   // down by one per entry, wrapping at 0.  Causal: R[t] = e[N - t] for
-  // 1 <= t <= N and zero elsewhere (no wrap).
+  // 1 <= t <= N and zero elsewhere (no wrap).  The copy index s runs
+  // fastest over the lanes, so neighbouring lanes read neighbouring logits
+  // (p0 + s steps by one), free of LDS bank conflicts.
   for (int e = tid; e < VE * (RP / VE); e += DTHR) {
-    const int s = e / (RP / VE), p0 = (e - s * (RP / VE)) * VE;
+    const int s = e & (VE - 1), p0 = (e / VE) * VE;
     float v[VE];
     if (CAUSAL) {
 #pragma unroll
@@ -249,7 +254,6 @@ __global__ __launch_bounds__(DTHR) void dconv_kernel(ConvArgs a) {
   __syncthreads();  // every wave is done with Vt
 
   // ---- O tile [Ip][32] in LDS: lane holds token 16 tb + lrow, channels 16 cb + 4 lgrp + v
-  constexpr int OP = DCG * ESZ;  // bytes per O row
 #pragma unroll
   for (int t = 0; t < TBW; ++t) {
     const int tb = wave + 4 * t;
@@ -267,7 +271,7 @@ __global__ __launch_bounds__(DTHR) void dconv_kernel(ConvArgs a) {
   __syncthreads();
   // ---- rows i < N -> O[b][i][h d + 32 g ..], 16-byte runs
   {
-    constexpr int CPR = OP / 16;
+    constexpr int CPR = DCG * ESZ / 16;  // 16-byte runs per O row
     char* ob = reinterpret_cast<char*>(a.O) + ((size_t)b * N * a.D + (size_t)h * a.d + (size_t)g * DCG) * ESZ;
     for (int u = tid; u < N * CPR; u += DTHR) {
       const int i = u / CPR, c = u - i * CPR;

@@ -286,7 +286,8 @@ def dtype_label(storage: str, conv_path: str) -> str:
                          "bf16-operand MFMA DFT-matrix products (2D)",
            "direct": "bf16 MFMA direct product (softmax weights rounded to bf16)",
            "fft_valu": "fp32 vector-ALU transforms",
-           "fft_multipass": "fp32 vector-ALU transforms"}.get(conv_path, conv_path)
+           "fft_multipass": "fp32 vector-ALU transforms, bf16-pair intermediates between the passes "
+                            "where both sides are 64 or 256 points"}.get(conv_path, conv_path)
     return f"bf16 storage; bf16 MFMA GEMM; {mix}; fp32 accumulate"
 
 

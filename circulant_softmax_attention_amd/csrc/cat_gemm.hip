@@ -273,6 +273,39 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void gemm_xw_kernel(GemmArgs a) {
     }
   };
 
+  // Whole-tile kernels (512 threads): the DMA slots of wave + 4 (thread
+  // tid + 256) as well, for waves 0-3, which issue both (see step)
+  const elem_t* bsrc2[BCH];
+#pragma unroll
+  for (int i = 0; i < BCH; ++i) {
+    const int s_ = tid + 256 + NTHR * i, k = s_ / CPRB, pos = s_ - k * CPRB;
+    const int c = (pos + CPRB - wrot<ET, BN>(k) % CPRB) % CPRB;
+    int col = n0 + c * VE;
+    col = col + VE <= ncols ? col : ncols - VE;
+    bsrc2[i] = reinterpret_cast<const elem_t*>(sg.W) + (size_t)(kbase + k) * ncols + col;
+  }
+  const elem_t* asrc2[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = ((tid + 256) >> 3) + (NTHR / 8) * i;
+    const int am = m0 + r < M ? m0 + r : M - 1;
+    asrc2[i] = reinterpret_cast<const elem_t*>(a.X) + (size_t)am * ldx + kbase + kch;
+  }
+  auto issue2 = [&](int kt, int st) {
+    const int k0 = kmap(kt) * BK;
+    const uint32_t base = lds0 + (uint32_t)(st * STAGE);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lds_dma16(asrc[i] + k0, base + i * NTHR * 16);
+      lds_dma16(asrc2[i] + k0, base + 4096 + i * NTHR * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < BCH; ++i) {
+      lds_dma16(bsrc[i] + (size_t)k0 * ncols, base + BM * ROWB + i * NTHR * 16);
+      lds_dma16(bsrc2[i] + (size_t)k0 * ncols, base + 4096 + BM * ROWB + i * NTHR * 16);
+    }
+    if (ZB > 0 && zdma) lds_dma16(zsrc + (size_t)k0 * nz * ESZ, base + BM * ROWB + BK * PB);
+  };
   const int lrow = lane & 15, lgrp = lane >> 4;
   const int sw = (lrow >> 1) & 7;  // (row / 2) % 8 of every X fragment row this lane reads
   floatx4 acc[4][TN];
@@ -443,19 +476,23 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void gemm_xw_kernel(GemmArgs a) {
     else
       wait_vmem_all();
     __syncthreads();
-    if (kt + 1 < nk) issue(kt + 1, st ^ 1);
     if constexpr (!KT) {
-      // both K chunks' fragments are requested before the first MFMA, so
-      // the second chunk's LDS reads run under the first chunk's products
-      // (the kernels with a K tail have no registers for this)
-      uint4 af1[4], bf1[TN];
-      read_frags(st, 0, af, bf);
-      read_frags(st, 1, af1, bf1);
-      mma(af, bf);
-      zmma(0, af, st);
-      mma(af1, bf1);
-      zmma(1, af1, st);
+      // Waves 0-3 issue the next tile's DMA for themselves and for waves
+      // 4-7, which go straight to their products.  A wave waits at a DMA
+      // instruction until the address unit takes it, and the unit takes a
+      // compute unit's requests one by one; with every wave issuing its own
+      // share, the waves queued last started their products up to 1 us late.
+      // (The kernels with a K tail keep every wave issuing its own share.)
+      static_assert(NTHR == 512, "whole-tile kernels are the 256-row, 512-thread ones");
+      if (kt + 1 < nk && wave < 4) issue2(kt + 1, st ^ 1);
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        read_frags(st, kc, af, bf);
+        mma(af, bf);
+        zmma(kc, af, st);
+      }
     } else {
+      if (kt + 1 < nk) issue(kt + 1, st ^ 1);
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) {
         read_frags(st, kc, af, bf);
